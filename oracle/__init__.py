@@ -1,0 +1,160 @@
+"""fp64 CPU oracle for the selective scan (S6) and its decode step.
+
+TEST INFRASTRUCTURE ONLY: tests, the smoke check and the bench's CPU-baseline
+leg may import this package; the product path never does. It shares no code
+with the HIP library. The arithmetic lives in ``ssm_oracle.c`` (plain C,
+float64, libm ``exp``, token loop in order); this module only compiles it with
+gcc, upcasts stored inputs exactly to float64 and calls it through ctypes.
+
+Parity is pinned by ``tests/test_oracle_pins.py`` against facts the pages fix
+(worked step example, LTI convolution, geometric closed form, delta limits,
+brute-force semiseparable sum, scalar-A masked form, step/scan composition)
+and by ``tests/test_oracle_mutants.py`` (each planted mistake fails a pin).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "ssm_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def build(src: str = SRC, out: str = LIB, force: bool = False) -> str:
+    """Compile the oracle with gcc -O2 -fopenmp (no fast-math)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes handle on one compiled oracle library."""
+
+    def __init__(self, lib_path: Optional[str] = None):
+        path = lib_path or build()
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        i64, ci = ctypes.c_int64, ctypes.c_int
+        self.lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [_DP] * 10 + [ci]
+        self.lib.oracle_scan.restype = ci
+        self.lib.oracle_step.argtypes = [i64, i64, i64] + [_DP] * 9 + [ci]
+        self.lib.oracle_step.restype = ci
+        self.lib.oracle_threads.argtypes = [ci]
+        self.lib.oracle_threads.restype = ci
+
+    def threads(self, nthreads: int = 0) -> int:
+        return int(self.lib.oracle_threads(nthreads))
+
+    # -- float64 entry points ------------------------------------------------
+    def scan64(self, x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None,
+               want_state: bool = True, nthreads: int = 0):
+        """All arguments float64 arrays (see ssm_oracle.c for shapes).
+        Returns (y, state_out or None)."""
+        x = _c64(x)
+        batch, L, D = x.shape
+        A = _c64(A)
+        N = A.shape[1]
+        delta, Bt, Ct = _c64(delta), _c64(Bt), _c64(Ct)
+        assert delta.shape == x.shape and A.shape == (D, N)
+        assert Bt.shape == (batch, L, N) and Ct.shape == (batch, L, N)
+        Dskip = None if Dskip is None else _c64(Dskip)
+        z = None if z is None else _c64(z)
+        state_in = None if state_in is None else _c64(state_in)
+        if z is not None:
+            assert z.shape == x.shape
+        if state_in is not None:
+            assert state_in.shape == (batch, D, N)
+        y = np.empty((batch, L, D), dtype=np.float64)
+        st = np.empty((batch, D, N), dtype=np.float64) if want_state else None
+        rc = self.lib.oracle_scan(batch, L, D, N, _p(x), _p(delta), _p(A), _p(Bt), _p(Ct),
+                                  _p(Dskip), _p(z), _p(state_in), _p(st), _p(y), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_scan rejected sizes")
+        return y, st
+
+    def step64(self, x, delta, A, Bt, Ct, Dskip, z, state, nthreads: int = 0):
+        """One decode step; `state` (batch, D, N) float64 is updated in place. Returns y."""
+        x = _c64(x)
+        batch, D = x.shape
+        A = _c64(A)
+        N = A.shape[1]
+        assert state.dtype == np.float64 and state.flags.c_contiguous and state.shape == (batch, D, N)
+        delta, Bt, Ct = _c64(delta), _c64(Bt), _c64(Ct)
+        Dskip = None if Dskip is None else _c64(Dskip)
+        z = None if z is None else _c64(z)
+        y = np.empty((batch, D), dtype=np.float64)
+        rc = self.lib.oracle_step(batch, D, N, _p(x), _p(delta), _p(A), _p(Bt), _p(Ct),
+                                  _p(Dskip), _p(z), _p(state), _p(y), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_step rejected sizes")
+        return y
+
+    # -- stored-dtype entry points -------------------------------------------
+    def scan(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
+        """Scan on stored inputs (float32 arrays, or bfloat16 bit patterns as uint16).
+        A, Dskip and state_in are float32. Returns float64 (y, state_out)."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.scan64(up(inp["x"]), up(inp["delta"]), upcast(inp["A"], "f32"), up(inp["Bt"]),
+                           up(inp["Ct"]), None if inp.get("Dskip") is None else upcast(inp["Dskip"], "f32"),
+                           up(inp.get("z")),
+                           None if inp.get("state_in") is None else upcast(inp["state_in"], "f32"),
+                           nthreads=nthreads)
+
+    def step(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
+             nthreads: int = 0):
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.step64(up(tok["x"]), up(tok["delta"]), upcast(A, "f32"), up(tok["Bt"]),
+                           up(tok["Ct"]), None if Dskip is None else upcast(Dskip, "f32"),
+                           up(tok.get("z")), state64, nthreads=nthreads)
+
+
+def upcast(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of a stored array: float32, or bfloat16 bits (uint16)."""
+    if dtype == "f32" or a.dtype == np.float32:
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        assert a.dtype == np.uint16
+        return (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _c64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.cast(None, _DP)
+    return a.ctypes.data_as(_DP)
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``ssm_oracle.c`` (compiled on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def timed_scan(inp, dtype, nthreads: int = 0):
+    """Run the scan and return (y, state_out, seconds, threads_used)."""
+    o = get()
+    t = time.perf_counter()
+    y, st = o.scan(inp, dtype, nthreads)
+    return y, st, time.perf_counter() - t, o.threads(nthreads)

@@ -1,0 +1,148 @@
+/*
+ * Plain fp64 CPU oracle for the selective scan (S6) and its decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only tests, the smoke check and the bench's CPU
+ * baseline may call this code. It shares nothing with the HIP path: no
+ * kernels, headers, helpers or constants.
+ *
+ * What it computes, per (batch row b, channel d), strictly in token order:
+ *
+ *   h[n] = state_in[b,d,n]  (or 0)                               initial state
+ *   for t = 0 .. L-1:
+ *     dA[n]  = exp(delta[b,t,d] * A[d,n])                        A-bar, exp-Euler rule
+ *     dBx[n] = delta[b,t,d] * Bt[b,t,n] * x[b,t,d]               B-bar = delta*B
+ *     h[n]   = dA[n] * h[n] + dBx[n]                             recurrence
+ *     y      = sum_n Ct[b,t,n] * h[n]  (+ Dskip[d] * x[b,t,d])    readout, skip
+ *     y      = y * z * sigmoid(z)      (when z is given)         silu gate
+ *     out[b,t,d] = y
+ *   state_out[b,d,:] = h
+ *
+ * Sources (the web pages on Mamba this method comes from):
+ *  - discretisation A-bar = exp(delta*A) and the first-order input rule
+ *    B-bar = delta*B: "Notas sobre Mamba", section "Preliminares" (the remark
+ *    after the discrete recurrence) and section "Recorrência trapezoidal"
+ *    (the exponential-Euler update); the Mamba-2/SSD production blog post,
+ *    section "Como o Mamba-1 alcançou complexidade linear" (the two S6
+ *    equations, with the D skip).
+ *  - time-varying recurrence and readout y_t = C_t^T h_t with the readout
+ *    taken on the updated state: "Notas sobre Mamba", section "O mecanismo
+ *    de seleção (S6)".
+ *  - the silu(z) gate multiplying the SSM output: "Notas sobre Mamba",
+ *    section "O bloco Mamba" (flowchart); silu(z) = z * sigmoid(z).
+ *  - the single-token step on a stored state: the blog post's
+ *    SelectiveSSM.forward_step listing (taken as a description of what is
+ *    computed) and "Notas sobre Mamba", section "Preliminares" (recurrent
+ *    mode with a constant-size state).
+ *
+ * Everything is float64 and uses libm exp(); no fast-math, no reordering of
+ * the token loop. OpenMP only splits independent (b, d) rows across threads.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define IDX3(a, b, c, B_, C_) (((int64_t)(a) * (B_) + (b)) * (C_) + (c))
+
+/* Returns the number of threads the parallel loops will use. */
+int oracle_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) return nthreads;
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/*
+ * Full selective scan over L tokens.
+ *   x, delta, z, y : (batch, L, D)   z may be NULL (no gate)
+ *   A              : (D, N)
+ *   Bt, Ct         : (batch, L, N)
+ *   Dskip          : (D) or NULL (no skip term)
+ *   state_in       : (batch, D, N) or NULL (zero state)
+ *   state_out      : (batch, D, N) or NULL
+ * Returns 0, or -1 on a bad size.
+ */
+int oracle_scan(int64_t batch, int64_t L, int64_t D, int64_t N,
+                const double *x, const double *delta, const double *A,
+                const double *Bt, const double *Ct, const double *Dskip,
+                const double *z, const double *state_in, double *state_out,
+                double *y, int nthreads)
+{
+    if (batch < 0 || L < 0 || D < 0 || N < 1 || N > 4096) return -1;
+    int64_t rows = batch * D;
+    int nt = oracle_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / D, d = r % D;
+        double h[4096];
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = state_in ? state_in[IDX3(b, d, n, D, N)] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double dt = delta[IDX3(b, t, d, L, D)];
+            double u = x[IDX3(b, t, d, L, D)];
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double dA = exp(dt * A[d * N + n]);
+                double dBx = dt * Bt[IDX3(b, t, n, L, N)] * u;
+                h[n] = dA * h[n] + dBx;
+                acc += Ct[IDX3(b, t, n, L, N)] * h[n];
+            }
+            if (Dskip) acc += Dskip[d] * u;
+            if (z) {
+                double g = z[IDX3(b, t, d, L, D)];
+                acc *= g / (1.0 + exp(-g));
+            }
+            y[IDX3(b, t, d, L, D)] = acc;
+        }
+        if (state_out)
+            for (int64_t n = 0; n < N; ++n) state_out[IDX3(b, d, n, D, N)] = h[n];
+    }
+    return 0;
+}
+
+/*
+ * One decode step: the loop body above with a single token, on a stored state
+ * that is updated in place.
+ *   x, delta, z, y : (batch, D)       z may be NULL
+ *   A              : (D, N)
+ *   Bt, Ct         : (batch, N)
+ *   Dskip          : (D) or NULL
+ *   state          : (batch, D, N)    read and overwritten
+ */
+int oracle_step(int64_t batch, int64_t D, int64_t N,
+                const double *x, const double *delta, const double *A,
+                const double *Bt, const double *Ct, const double *Dskip,
+                const double *z, double *state, double *y, int nthreads)
+{
+    if (batch < 0 || D < 0 || N < 1) return -1;
+    int64_t rows = batch * D;
+    int nt = oracle_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / D, d = r % D;
+        double dt = delta[r];
+        double u = x[r];
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double *hn = &state[r * N + n];
+            double dA = exp(dt * A[d * N + n]);
+            double dBx = dt * Bt[b * N + n] * u;
+            *hn = dA * *hn + dBx;
+            acc += Ct[b * N + n] * *hn;
+        }
+        if (Dskip) acc += Dskip[d] * u;
+        if (z) {
+            double g = z[r];
+            acc *= g / (1.0 + exp(-g));
+        }
+        y[r] = acc;
+    }
+    return 0;
+}

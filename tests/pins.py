@@ -1,0 +1,312 @@
+"""Checks that pin the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees. They are run on the real oracle by
+``test_oracle_pins.py`` and on deliberately broken copies of it by
+``test_oracle_mutants.py`` (every planted mistake must trip at least one pin).
+
+None of these checks re-types the oracle's loop: each compares it with an
+independent statement of the same result (a printed worked example, a closed
+form, numpy's convolution, an explicit matrix, the masked-matmul dual form,
+an invariant).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(v) for v in line.split()])
+    return rows
+
+
+def _rand_problem(rng, batch, L, D, N, gate=True, skip=True, state=True, s4d=False):
+    A = (-(np.arange(N) + 1.0))[None, :].repeat(D, 0) if s4d else -np.exp(rng.normal(size=(D, N)))
+    p = dict(
+        x=rng.normal(size=(batch, L, D)),
+        delta=np.exp(rng.uniform(np.log(1e-3), np.log(0.5), size=(batch, L, D))),
+        A=A,
+        Bt=rng.normal(size=(batch, L, N)),
+        Ct=rng.normal(size=(batch, L, N)),
+        Dskip=rng.uniform(0.5, 1.5, size=D) if skip else None,
+        z=rng.normal(size=(batch, L, D)) if gate else None,
+        state_in=rng.normal(size=(batch, D, N)) if state else None,
+    )
+    return p
+
+
+def _scan(o, p, **kw):
+    return o.scan64(p["x"], p["delta"], p["A"], p["Bt"], p["Ct"], p.get("Dskip"), p.get("z"),
+                    p.get("state_in"), **kw)
+
+
+# --- P4: the printed single-step example ------------------------------------
+def pin_step_example(o):
+    """Worked example: A=-1, B=1, h=1, x=1; delta=5 forgets, delta=0.01 holds."""
+    for dt, abar, bbar, hnew in _golden_rows("selective_step_example.txt"):
+        N = 4
+        A = -np.ones((1, N))
+        ones = np.ones((1, 1, N))
+        # full step: new state
+        _, st = o.scan64(np.ones((1, 1, 1)), np.full((1, 1, 1), dt), A, ones, ones, state_in=ones)
+        assert np.all(np.round(st, 4) == hnew), (dt, st)
+        # exact value of the same quantity: exp(-dt) + dt
+        assert abs(st[0, 0, 0] - (math.exp(-dt) + dt)) <= 1e-15 * (1 + dt), st
+        # A-bar alone: B = 0 leaves h = A-bar * 1
+        _, st0 = o.scan64(np.ones((1, 1, 1)), np.full((1, 1, 1), dt), A, 0 * ones, ones, state_in=ones)
+        assert np.all(np.round(st0, 4) == abar), (dt, st0)
+        # B-bar alone: h = 0 before the step gives h = B-bar * x
+        _, stb = o.scan64(np.ones((1, 1, 1)), np.full((1, 1, 1), dt), A, ones, ones, state_in=0 * ones)
+        assert np.all(np.round(stb, 4) == bbar), (dt, stb)
+        # the same example through the single-token decode step
+        h = np.ones((1, 1, N))
+        y = o.step64(np.ones((1, 1)), np.full((1, 1), dt), A, np.ones((1, N)), np.ones((1, N)), None, None, h)
+        assert np.all(np.round(h, 4) == hnew), (dt, h)
+        assert abs(h[0, 0, 0] - (math.exp(-dt) + dt)) <= 1e-15 * (1 + dt), h
+        assert abs(y[0, 0] - N * h[0, 0, 0]) <= 1e-14 * N * (1 + dt), y
+
+
+# --- P1: time-invariant case equals convolution ------------------------------
+def _conv_reference(A_diag, Bbar, C, x, dt):
+    abar = np.exp(dt * A_diag)
+    L = len(x)
+    K = np.array([C @ (abar ** k * Bbar) for k in range(L)])
+    return np.convolve(x, K)[:L]
+
+
+def pin_lti_convolution(o):
+    """Constant delta, B, C and no skip, gate or initial state: y = K * x."""
+    seed, N, L, dt, printed = _golden_rows("lti_convolution_demo.txt")[0]
+    rng = np.random.default_rng(int(seed))
+    N, L = int(N), int(L)
+    A = -np.exp(rng.normal(size=N))
+    B, C = rng.normal(size=N), rng.normal(size=N)
+    x = rng.normal(size=L)
+    abar = np.exp(dt * A)
+    Bbar = (abar - 1.0) / A * B               # the demo's zero-order-hold B-bar
+    # Feed B-bar through the exp-Euler input rule: delta * (Bbar / delta) = Bbar.
+    y, _ = o.scan64(x[None, :, None], np.full((1, L, 1), dt), A[None, :],
+                    np.broadcast_to(Bbar / dt, (1, L, N)), np.broadcast_to(C, (1, L, N)))
+    ref = _conv_reference(A, Bbar, C, x, dt)
+    err = np.abs(y[0, :, 0] - ref).max()
+    # the page printed `printed` for its own float64 run; this oracle gives 1.67e-16
+    assert err <= 10 * printed, err
+    # several channels, random constant delta per channel, S4D-real A, B-bar = delta*B
+    rng = np.random.default_rng(10)
+    D, N, L = 5, 16, 200
+    A = (-(np.arange(N) + 1.0))[None, :].repeat(D, 0)
+    dts = np.exp(rng.uniform(np.log(1e-3), np.log(0.3), size=D))
+    B, C = rng.normal(size=N), rng.normal(size=N)
+    x = rng.normal(size=(L, D))
+    y, _ = o.scan64(x[None], np.broadcast_to(dts, (1, L, D)), A,
+                    np.broadcast_to(B, (1, L, N)), np.broadcast_to(C, (1, L, N)))
+    for d in range(D):
+        ref = _conv_reference(A[d], dts[d] * B, C, x[:, d], dts[d])
+        assert np.allclose(y[0, :, d], ref, rtol=1e-12, atol=1e-12), d
+
+
+# --- P2: N = 1 geometric closed form -----------------------------------------
+def pin_geometric(o):
+    """N=1, constant delta/B/C, x = 1: h_t = a^(t+1) h0 + b (1 - a^(t+1)) / (1 - a)."""
+    for dt, Aval, Bv, Cv, Dv, h0 in [(0.05, -1.0, 0.7, -1.3, 0.9, 0.4), (0.3, -2.5, -1.1, 0.6, 1.2, -2.0),
+                                     (1e-3, -0.5, 2.0, 1.0, 0.0, 3.0)]:
+        L = 300
+        y, st = o.scan64(np.ones((1, L, 1)), np.full((1, L, 1), dt), np.array([[Aval]]),
+                         np.full((1, L, 1), Bv), np.full((1, L, 1), Cv), np.array([Dv]),
+                         state_in=np.array([[[h0]]]))
+        a, b = math.exp(dt * Aval), dt * Bv
+        t = np.arange(1, L + 1, dtype=np.float64)
+        h = a ** t * h0 + b * (1 - a ** t) / (1 - a)
+        assert np.allclose(y[0, :, 0], Cv * h + Dv, rtol=1e-11, atol=1e-12)
+        assert abs(st[0, 0, 0] - h[-1]) <= 1e-11 * max(1, abs(h[-1]))
+
+
+# --- P3: delta limits ---------------------------------------------------------
+def pin_delta_limits(o):
+    """delta = 0 keeps the state bit for bit; a huge delta resets it to delta*B*x."""
+    rng = np.random.default_rng(3)
+    p = _rand_problem(rng, 2, 40, 3, 16)
+    p["delta"] = np.zeros_like(p["delta"])
+    y, st = _scan(o, p)
+    assert np.array_equal(st, p["state_in"])
+    gate = p["z"] / (1 + np.exp(-p["z"]))
+    for b in range(2):
+        ref = (np.einsum("tn,dn->td", p["Ct"][b], p["state_in"][b]) + p["Dskip"] * p["x"][b]) * gate[b]
+        assert np.allclose(y[b], ref, rtol=1e-13, atol=1e-13)
+    # huge delta: A-bar underflows, the new state is delta * B * x
+    p = _rand_problem(rng, 1, 5, 4, 8, s4d=True)
+    p["delta"] = np.full_like(p["delta"], 60.0)
+    _, st = _scan(o, p)
+    ref = 60.0 * p["Bt"][0, -1][None, :] * p["x"][0, -1][:, None]
+    assert np.allclose(st[0], ref, rtol=1e-14, atol=0)
+    # small delta holds: 0.01 * |A| << 1, state moves by O(delta)
+    p = _rand_problem(rng, 1, 1, 4, 8, s4d=True, gate=False, skip=False)
+    p["delta"] = np.full_like(p["delta"], 1e-6)
+    _, st = _scan(o, p)
+    assert np.allclose(st, p["state_in"], rtol=1e-4, atol=1e-4)
+
+
+# --- P5: brute-force semiseparable sum ---------------------------------------
+def pin_semiseparable(o):
+    """y_j = sum_{i<=j} C_j^T (prod_{k=i+1..j} Abar_k) Bbar_i x_i + C_j^T (prod_{k<=j} Abar_k) h_-1."""
+    rng = np.random.default_rng(5)
+    for L in range(1, 9):
+        p = _rand_problem(rng, 2, L, 3, 5, gate=False, skip=False)
+        y, st = _scan(o, p)
+        for b in range(2):
+            for d in range(3):
+                abar = np.exp(p["delta"][b, :, d, None] * p["A"][d][None, :])        # (L, N)
+                bbar = p["delta"][b, :, d, None] * p["Bt"][b]                       # (L, N)
+                for j in range(L):
+                    tot = 0.0
+                    for i in range(j + 1):
+                        prod = np.ones(5)
+                        for k in range(i + 1, j + 1):
+                            prod = prod * abar[k]
+                        tot += float(np.sum(p["Ct"][b, j] * prod * bbar[i])) * p["x"][b, i, d]
+                    prod = np.ones(5)
+                    for k in range(0, j + 1):
+                        prod = prod * abar[k]
+                    tot += float(np.sum(p["Ct"][b, j] * prod * p["state_in"][b, d]))
+                    assert abs(y[b, j, d] - tot) <= 1e-12 * (1 + abs(tot)), (L, b, d, j)
+                # final state, the same sums without C
+                hend = np.zeros(5)
+                for i in range(L):
+                    prod = np.ones(5)
+                    for k in range(i + 1, L):
+                        prod = prod * abar[k]
+                    hend += prod * bbar[i] * p["x"][b, i, d]
+                prod = np.ones(5)
+                for k in range(L):
+                    prod = prod * abar[k]
+                hend += prod * p["state_in"][b, d]
+                assert np.allclose(st[b, d], hend, rtol=1e-12, atol=1e-13)
+
+
+# --- P7: scalar transition equals the masked (quadratic) dual form -----------
+def pin_scalar_a_dual(o):
+    """A[d, :] constant: y = (Lmask o C B^T) X, as in the SSD check."""
+    seed, L, N, P, printed = _golden_rows("ssd_dual_demo.txt")[0]
+    rng = np.random.default_rng(int(seed))
+    L, N, P = int(L), int(N), int(P)
+    a = rng.uniform(0.85, 0.99, size=L)
+    B, C = rng.normal(size=(L, N)), rng.normal(size=(L, N))
+    X = rng.normal(size=(L, P))
+    # quadratic form written from the definition: Lmask_ji = prod_{k=i+1..j} a_k
+    Lmask = np.zeros((L, L))
+    for j in range(L):
+        for i in range(j + 1):
+            Lmask[j, i] = np.prod(a[i + 1:j + 1])
+    Yq = (Lmask * (C @ B.T)) @ X
+    # the same recurrence through the S6 oracle: a_t = exp(delta_t * (-1)),
+    # input term delta_t * (B_t / delta_t) * x_t = B_t x_t, channels = P columns.
+    dt = -np.log(a)
+    y, _ = o.scan64(X[None], np.broadcast_to(dt[:, None], (1, L, P)), -np.ones((P, N)),
+                    (B / dt[:, None])[None], C[None])
+    err = np.abs(y[0] - Yq).max()
+    assert err <= 10 * printed, err  # this oracle: 1.07e-14 against the printed 9.44e-15
+    # longer random case, per-channel scalar A and random delta
+    rng = np.random.default_rng(7)
+    L, N, D = 256, 16, 4
+    Ad = -np.exp(rng.normal(size=D))
+    delta = np.exp(rng.uniform(np.log(1e-3), np.log(0.2), size=(L, D)))
+    B, C = rng.normal(size=(L, N)), rng.normal(size=(L, N))
+    x = rng.normal(size=(L, D))
+    y, _ = o.scan64(x[None], delta[None], np.repeat(Ad[:, None], N, 1), B[None], C[None])
+    for d in range(D):
+        cum = np.cumsum(delta[:, d] * Ad[d])               # log of prod_{k<=j} a_k
+        Lmask = np.tril(np.exp(cum[:, None] - cum[None, :]))
+        ref = (Lmask * (C @ B.T)) @ (delta[:, d] * x[:, d])
+        assert np.allclose(y[0, :, d], ref, rtol=1e-10, atol=1e-10), d
+
+
+# --- P6: composition of steps and of scans -----------------------------------
+def pin_composition(o):
+    """A fold of single steps equals the scan; scan(L) = scan(L1) then scan(L-L1)."""
+    rng = np.random.default_rng(6)
+    p = _rand_problem(rng, 2, 37, 5, 16, s4d=True)
+    y, st = _scan(o, p)
+    state = p["state_in"].copy()
+    for t in range(37):
+        yt = o.step64(p["x"][:, t], p["delta"][:, t], p["A"], p["Bt"][:, t], p["Ct"][:, t],
+                      p["Dskip"], p["z"][:, t], state)
+        assert np.array_equal(yt, y[:, t]), t
+    assert np.array_equal(state, st)
+    for L1 in (0, 1, 17, 36, 37):
+        q1 = {k: (v[:, :L1] if k in ("x", "delta", "Bt", "Ct", "z") else v) for k, v in p.items()}
+        q2 = {k: (v[:, L1:] if k in ("x", "delta", "Bt", "Ct", "z") else v) for k, v in p.items()}
+        y1, s1 = _scan(o, q1)
+        q2["state_in"] = s1
+        y2, s2 = _scan(o, q2)
+        assert np.array_equal(np.concatenate([y1, y2], 1), y), L1
+        assert np.array_equal(s2, st), L1
+
+
+# --- P8: skip, gate, linearity, causality ------------------------------------
+def pin_skip_gate(o):
+    """B=0 and h0=0 gives y = D x exactly; z = 0 gives 0; the gate is silu(z)."""
+    import torch
+    rng = np.random.default_rng(8)
+    p = _rand_problem(rng, 2, 30, 6, 16, gate=False, state=False)
+    p["Bt"] = np.zeros_like(p["Bt"])
+    y, st = _scan(o, p)
+    assert np.array_equal(y, p["Dskip"] * p["x"])
+    assert not st.any()
+    # the gate multiplies (C.h + D.x): with B = 0, y = D x silu(z)
+    p["z"] = rng.normal(size=p["x"].shape) * 3
+    y, _ = _scan(o, p)
+    silu = torch.nn.functional.silu(torch.from_numpy(p["z"])).numpy()
+    assert np.allclose(y, p["Dskip"] * p["x"] * silu, rtol=1e-14, atol=1e-15)
+    p["z"] = np.zeros_like(p["z"])
+    p["Bt"] = rng.normal(size=p["Bt"].shape)
+    y, _ = _scan(o, p)
+    assert not y.any()
+    # no skip term: x enters only through B
+    p = _rand_problem(rng, 1, 10, 3, 8, gate=False, skip=False, state=False)
+    p["Bt"] = np.zeros_like(p["Bt"])
+    y, _ = _scan(o, p)
+    assert not y.any()
+
+
+def pin_linearity_causality(o):
+    """Gate off: y is linear in (x, h0); nothing at t > t0 changes y[:t0+1]."""
+    rng = np.random.default_rng(9)
+    p = _rand_problem(rng, 2, 50, 4, 16, gate=False)
+    q = dict(p)
+    q["x"] = rng.normal(size=p["x"].shape)
+    q["state_in"] = rng.normal(size=p["state_in"].shape)
+    a, b = 0.7, -1.9
+    r = dict(p)
+    r["x"] = a * p["x"] + b * q["x"]
+    r["state_in"] = a * p["state_in"] + b * q["state_in"]
+    yp, sp = _scan(o, p)
+    yq, sq = _scan(o, q)
+    yr, sr = _scan(o, r)
+    assert np.allclose(yr, a * yp + b * yq, rtol=1e-11, atol=1e-11)
+    assert np.allclose(sr, a * sp + b * sq, rtol=1e-11, atol=1e-11)
+    # causality
+    p = _rand_problem(rng, 2, 50, 4, 16)
+    y0, _ = _scan(o, p)
+    t0 = 20
+    for k in ("x", "delta", "Bt", "Ct", "z"):
+        pk = dict(p)
+        pk[k] = p[k].copy()
+        pk[k][:, t0 + 1:] = pk[k][:, t0 + 1:] * 1.5 + 0.25
+        yk, _ = _scan(o, pk)
+        assert np.array_equal(yk[:, :t0 + 1], y0[:, :t0 + 1]), k
+        assert not np.array_equal(yk[:, t0 + 1:], y0[:, t0 + 1:]), k
+
+
+ALL_PINS = [pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
+            pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
+            pin_linearity_causality]

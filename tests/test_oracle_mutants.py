@@ -1,0 +1,65 @@
+"""Plant one mistake at a time in a copy of the oracle; some pin must fail.
+
+This is how the pins are shown to be sharp enough: a dropped term, a wrong
+sign, a wrong index or a transposed operand in the oracle each trips at
+least one of them. Mutants are built from the oracle's C source in a
+temporary directory with gcc; the real oracle is never modified.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+SRC = open(oracle.SRC).read()
+
+# (name, text to replace, replacement); each is applied to every occurrence.
+MUTANTS = [
+    ("update_sign", "h[n] = dA * h[n] + dBx;", "h[n] = dA * h[n] - dBx;"),
+    ("step_update_sign", "*hn = dA * *hn + dBx;", "*hn = dA * *hn - dBx;"),
+    ("exp_sign", "double dA = exp(dt * A[d * N + n]);", "double dA = exp(-dt * A[d * N + n]);"),
+    ("drop_delta_in_B", "double dBx = dt * Bt[IDX3(b, t, n, L, N)] * u;",
+     "double dBx = Bt[IDX3(b, t, n, L, N)] * u;"),
+    ("zoh_like_B", "double dBx = dt * Bt[IDX3(b, t, n, L, N)] * u;",
+     "double dBx = (dA - 1.0) / A[d * N + n] * Bt[IDX3(b, t, n, L, N)] * u;"),
+    ("readout_before_update",
+     "                h[n] = dA * h[n] + dBx;\n                acc += Ct[IDX3(b, t, n, L, N)] * h[n];",
+     "                acc += Ct[IDX3(b, t, n, L, N)] * h[n];\n                h[n] = dA * h[n] + dBx;"),
+    ("readout_uses_B", "acc += Ct[IDX3(b, t, n, L, N)] * h[n];", "acc += Bt[IDX3(b, t, n, L, N)] * h[n];"),
+    ("drop_skip", "if (Dskip) acc += Dskip[d] * u;", "if (0) acc += Dskip[d] * u;"),
+    ("skip_outside_gate",
+     "            if (Dskip) acc += Dskip[d] * u;\n            if (z) {\n                double g = z[IDX3(b, t, d, L, D)];\n                acc *= g / (1.0 + exp(-g));\n            }",
+     "            if (z) {\n                double g = z[IDX3(b, t, d, L, D)];\n                acc *= g / (1.0 + exp(-g));\n            }\n            if (Dskip) acc += Dskip[d] * u;"),
+    ("gate_sigmoid_only", "acc *= g / (1.0 + exp(-g));", "acc *= 1.0 / (1.0 + exp(-g));"),
+    ("gate_sign", "acc *= g / (1.0 + exp(-g));", "acc *= g / (1.0 + exp(g));"),
+    ("ignore_state_in", "h[n] = state_in ? state_in[IDX3(b, d, n, D, N)] : 0.0;", "h[n] = 0.0;"),
+    ("A_transposed", "exp(dt * A[d * N + n])", "exp(dt * A[(n * D + d) % (D * N)])"),
+    ("B_indexed_by_channel", "Bt[IDX3(b, t, n, L, N)] * u", "Bt[IDX3(b, t, d % N, L, N)] * u"),
+    ("delta_previous_token", "double dt = delta[IDX3(b, t, d, L, D)];",
+     "double dt = delta[IDX3(b, (t > 0 ? t - 1 : 0), d, L, D)];"),
+    ("x_neighbour_channel", "double u = x[IDX3(b, t, d, L, D)];", "double u = x[IDX3(b, t, (d + 1) % D, L, D)];"),
+    ("C_previous_token", "acc += Ct[IDX3(b, t, n, L, N)] * h[n];",
+     "acc += Ct[IDX3(b, (t > 0 ? t - 1 : 0), n, L, N)] * h[n];"),
+    ("last_state_component_dropped", "for (int64_t n = 0; n < N; ++n) state_out[IDX3(b, d, n, D, N)] = h[n];",
+     "for (int64_t n = 0; n + 1 < N; ++n) state_out[IDX3(b, d, n, D, N)] = h[n];"),
+    ("batch_row_mixup", "int64_t b = r / D, d = r % D;\n        double h[4096];",
+     "int64_t b = 0, d = r % D;\n        double h[4096];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    assert old in SRC, "mutation site not found: " + name
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(old, new))
+    lib = oracle.build(str(src), str(tmp_path / "libmutant.so"), force=True)
+    o = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, FloatingPointError, ValueError) as e:  # a pin tripped
+            failed.append(pin.__name__)
+    assert failed, "no pin caught mutant " + name

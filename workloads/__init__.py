@@ -1,0 +1,269 @@
+"""Seeded synthetic inputs for the selective scan (S6) and its decode step.
+
+This module is shared by the tests, the bench and the oracle checks. It only
+draws random numbers and stores them in the storage dtypes; it holds none of
+the scan's arithmetic. Every tensor is drawn in float64 and stored once in its
+storage dtype: float32 (round to nearest even) or bfloat16 (float64 -> float32
+-> bfloat16, each round to nearest even). bfloat16 arrays are numpy ``uint16``
+arrays that hold the raw bit patterns.
+
+Shapes (D fastest everywhere):
+  x, delta, z, y : (batch, L, D)       activation dtype
+  A              : (D, N)              float32
+  Bt, Ct         : (batch, L, N)       activation dtype
+  Dskip          : (D,)                float32
+  state          : (batch, D, N)       float32
+
+Distributions follow the workloads described for the Mamba selective scan
+(Mamba notes, "O mecanismo de seleção (S6)"; Mamba encyclopedia entry,
+"como funciona"): A = -exp(A_log) with the S4D-real choice A[d, n] = -(n+1);
+delta = softplus(0.5*eps + dt_bias) where dt_bias is the inverse softplus of a
+per-channel dt drawn log-uniform in [1e-3, 1e-1]; x, z, Bt, Ct ~ N(0, 1);
+Dskip = 1 or U(0.5, 1.5). delta is handed to the scan after the softplus.
+
+Random streams: ``numpy.random.default_rng(SeedSequence(seed, spawn_key=key))``
+with one key per (tensor kind, batch row, token chunk of 65536). Generation is
+therefore chunked and restartable, and any token range can be regenerated
+without the rest of the sequence.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
+    "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
+    "storage_to_f64", "scan_bytes", "step_bytes",
+]
+
+DTYPES = ("f32", "bf16")
+_CHUNK = 65536  # tokens per random stream
+
+# stream keys (tensor kinds)
+_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE = range(8)
+
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    """One selective-scan workload: sizes, dtype and which optional parts are on."""
+    name: str
+    batch: int
+    L: int
+    D: int
+    N: int = 16
+    dtype: str = "f32"          # activation dtype of x, delta, z, Bt, Ct, y
+    gate: bool = True           # silu(z) gate on
+    dskip: str = "uniform"      # "one", "uniform" or "none"
+    state_in: Optional[float] = None  # std of the carried-in state, None = zero state
+    seed: int = 0
+
+    @property
+    def elems(self) -> int:
+        return self.batch * self.L * self.D * self.N
+
+
+@dataclasses.dataclass(frozen=True)
+class StepConfig:
+    """A decode workload: `steps` consecutive single-token updates of a batch of states."""
+    name: str
+    batch: int
+    D: int
+    N: int = 16
+    dtype: str = "bf16"
+    gate: bool = True
+    dskip: str = "uniform"
+    state_std: float = 1.0
+    steps: int = 1000
+    seed: int = 4
+
+    @property
+    def elems_per_step(self) -> int:
+        return self.batch * self.D * self.N
+
+
+# The five workloads, in order: tiny fp32; small-model layer fp32; large-model
+# layer bf16; million-token context bf16 with a carried-in state; decode step.
+SCAN_CONFIGS: Dict[str, ScanConfig] = {
+    "c0": ScanConfig("c0_tiny_f32", 1, 256, 64, 16, "f32", gate=False, dskip="one", seed=0),
+    "c1": ScanConfig("c1_small_layer_f32", 2, 2048, 1536, 16, "f32", gate=True, dskip="uniform", seed=1),
+    "c2": ScanConfig("c2_large_layer_bf16", 8, 4096, 5120, 16, "bf16", gate=True, dskip="uniform", seed=2),
+    "c3": ScanConfig("c3_million_token_bf16", 1, 1048576, 1536, 16, "bf16", gate=True, dskip="uniform",
+                     state_in=0.1, seed=3),
+}
+STEP_CONFIG = StepConfig("c4_decode_step_bf16", 256, 5120, 16, "bf16", gate=True, dskip="uniform",
+                         state_std=1.0, steps=1000, seed=4)
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=tuple(int(k) for k in key)))
+
+
+def bf16_bits_from_f64(a: np.ndarray) -> np.ndarray:
+    """float64 -> float32 (RNE) -> bfloat16 (RNE), returned as uint16 bit patterns."""
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    rounding = ((u >> 16) & 1) + 0x7FFF
+    out = ((u + rounding) >> 16).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of a stored tensor (float32, or bfloat16 bits) to float64."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        u = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return u.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _store(a64: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return a64.astype(np.float32)
+    if dtype == "bf16":
+        return bf16_bits_from_f64(a64)
+    raise ValueError(dtype)
+
+
+def _softplus(u: np.ndarray) -> np.ndarray:
+    return np.maximum(u, 0.0) + np.log1p(np.exp(-np.abs(u)))
+
+
+def _channel_params(seed: int, D: int, N: int, dskip: str):
+    """A (D, N) float32, dt_bias (D,) float64, Dskip (D,) float32 or None."""
+    A = np.broadcast_to(-(np.arange(N, dtype=np.float64) + 1.0), (D, N)).astype(np.float32).copy()
+    dt = np.exp(_rng(seed, _K_DT).uniform(math.log(1e-3), math.log(1e-1), size=D))
+    dt_bias = dt + np.log(-np.expm1(-dt))  # inverse softplus
+    if dskip == "one":
+        Dskip = np.ones(D, dtype=np.float32)
+    elif dskip == "uniform":
+        Dskip = _rng(seed, _K_D).uniform(0.5, 1.5, size=D).astype(np.float32)
+    elif dskip == "none":
+        Dskip = None
+    else:
+        raise ValueError(dskip)
+    return A, dt_bias, Dskip
+
+
+def _token_block(seed: int, kind: int, b: int, t0: int, t1: int, width: int) -> np.ndarray:
+    """N(0,1) float64 block of shape (t1-t0, width) from the per-chunk streams."""
+    out = np.empty((t1 - t0, width), dtype=np.float64)
+    if t1 == t0:
+        return out
+    for c in range(t0 // _CHUNK, (t1 - 1) // _CHUNK + 1):
+        cs = c * _CHUNK
+        lo, hi = max(t0, cs), min(t1, cs + _CHUNK)
+        # A stream's draws are a fixed sequence: drawing the first (hi - cs)
+        # rows gives the same rows as drawing the whole chunk.
+        block = _rng(seed, kind, b, c).standard_normal((hi - cs, width))
+        out[lo - t0:hi - t0] = block[lo - cs:]
+    return out
+
+
+def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
+                channels: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Inputs of `cfg` for tokens [t0, t1) (default: all), in storage dtypes.
+
+    `channels` selects a subset of the D channels for x, delta, z, A and Dskip
+    (used to check sampled channels of very large workloads); Bt and Ct are
+    shared by all channels and always returned whole. state_in is returned
+    for every batch row and the selected channels when the workload has one.
+    The values do not depend on how the token range is split.
+    """
+    if t1 is None:
+        t1 = cfg.L
+    assert 0 <= t0 <= t1 <= cfg.L
+    A, dt_bias, Dskip = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
+    sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
+    T = t1 - t0
+    act = cfg.dtype
+    x = np.empty((cfg.batch, T, len(sel)), dtype=np.float32 if act == "f32" else np.uint16)
+    dl = np.empty_like(x)
+    z = np.empty_like(x) if cfg.gate else None
+    Bt = np.empty((cfg.batch, T, cfg.N), dtype=x.dtype)
+    Ct = np.empty_like(Bt)
+    for b in range(cfg.batch):
+        eps = _token_block(cfg.seed, _K_DNOISE, b, t0, t1, cfg.D)[:, sel]
+        dl[b] = _store(_softplus(0.5 * eps + dt_bias[sel][None, :]), act)
+        x[b] = _store(_token_block(cfg.seed, _K_X, b, t0, t1, cfg.D)[:, sel], act)
+        if z is not None:
+            z[b] = _store(_token_block(cfg.seed, _K_Z, b, t0, t1, cfg.D)[:, sel], act)
+        Bt[b] = _store(_token_block(cfg.seed, _K_B, b, t0, t1, cfg.N), act)
+        Ct[b] = _store(_token_block(cfg.seed, _K_C, b, t0, t1, cfg.N), act)
+    out = {"x": x, "delta": dl, "z": z, "A": np.ascontiguousarray(A[sel]), "Bt": Bt, "Ct": Ct,
+           "Dskip": None if Dskip is None else np.ascontiguousarray(Dskip[sel]), "state_in": None}
+    if cfg.state_in is not None:
+        st = _rng(cfg.seed, _K_STATE).standard_normal((cfg.batch, cfg.D, cfg.N)) * cfg.state_in
+        out["state_in"] = np.ascontiguousarray(st[:, sel, :].astype(np.float32))
+    return out
+
+
+def step_inputs(cfg: StepConfig, channels: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Per-workload tensors of a decode run: A, Dskip and the initial state."""
+    A, _dt_bias, Dskip = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
+    sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
+    st = _rng(cfg.seed, _K_STATE).standard_normal((cfg.batch, cfg.D, cfg.N)) * cfg.state_std
+    return {"A": np.ascontiguousarray(A[sel]),
+            "Dskip": None if Dskip is None else np.ascontiguousarray(Dskip[sel]),
+            "state": np.ascontiguousarray(st[:, sel, :].astype(np.float32))}
+
+
+def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray] = None
+                      ) -> Dict[str, np.ndarray]:
+    """Inputs of decode step `step`: x, delta, z (batch, D) and Bt, Ct (batch, N)."""
+    _A, dt_bias, _D = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
+    sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
+    act = cfg.dtype
+    key = 1000 + step
+    eps = _rng(cfg.seed, _K_DNOISE, key).standard_normal((cfg.batch, cfg.D))[:, sel]
+    out = {
+        "delta": _store(_softplus(0.5 * eps + dt_bias[sel][None, :]), act),
+        "x": _store(_rng(cfg.seed, _K_X, key).standard_normal((cfg.batch, cfg.D))[:, sel], act),
+        "z": _store(_rng(cfg.seed, _K_Z, key).standard_normal((cfg.batch, cfg.D))[:, sel], act)
+        if cfg.gate else None,
+        "Bt": _store(_rng(cfg.seed, _K_B, key).standard_normal((cfg.batch, cfg.N)), act),
+        "Ct": _store(_rng(cfg.seed, _K_C, key).standard_normal((cfg.batch, cfg.N)), act),
+    }
+    for k in ("delta", "x", "z"):
+        if out[k] is not None:
+            out[k] = np.ascontiguousarray(out[k])
+    return out
+
+
+def _esize(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+def scan_bytes(cfg: ScanConfig, state_out: bool = False) -> int:
+    """Bytes the scan must move: x, delta, (z) read and y written once per (b,t,d);
+    Bt, Ct once per token; A, Dskip once; state_in / state_out when used.
+    The (batch, L, D, N) expanded state is never counted: it is never stored."""
+    e = _esize(cfg.dtype)
+    btd = cfg.batch * cfg.L * cfg.D
+    n = btd * e * (3 + (1 if cfg.gate else 0))
+    n += 2 * cfg.batch * cfg.L * cfg.N * e
+    n += cfg.D * cfg.N * 4 + (cfg.D * 4 if cfg.dskip != "none" else 0)
+    if cfg.state_in is not None:
+        n += cfg.batch * cfg.D * cfg.N * 4
+    if state_out:
+        n += cfg.batch * cfg.D * cfg.N * 4
+    return n
+
+
+def step_bytes(cfg: StepConfig) -> int:
+    """Bytes one decode step must move: the state read and written, x, delta,
+    (z) read and y written per (b,d), Bt and Ct per sequence, A and Dskip."""
+    e = _esize(cfg.dtype)
+    bd = cfg.batch * cfg.D
+    n = 2 * bd * cfg.N * 4
+    n += bd * e * (3 + (1 if cfg.gate else 0))
+    n += 2 * cfg.batch * cfg.N * e
+    n += cfg.D * cfg.N * 4 + (cfg.D * 4 if cfg.dskip != "none" else 0)
+    return n
