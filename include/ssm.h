@@ -1,0 +1,135 @@
+/*
+ * ssm.h - C ABI of the MI355X (gfx950) selective-scan library (libssm.so).
+ *
+ * The library computes the Mamba-1 selective state-space layer (S6): the
+ * full forward scan over a sequence and the single-token recurrent decode
+ * step, with hand-written HIP kernels. Definitions, in the pages' notation
+ * (Delta = delta, B_t = Bt, C_t = Ct, D = Dskip):
+ *
+ *   dA[t,n]  = exp(delta[t] * A[n])            (A-bar, exponential rule)
+ *   dBx[t,n] = delta[t] * Bt[t,n] * x[t]       (B-bar = Delta * B_t)
+ *   h[t,n]   = dA[t,n] * h[t-1,n] + dBx[t,n]   (h[-1] = carried-in state or 0)
+ *   y[t]     = (sum_n Ct[t,n] * h[t,n] + Dskip * x[t]) * silu(z[t])
+ *   silu(z)  = z / (1 + exp(-z))
+ *
+ * per (batch row b, channel d). Sources: "Notas sobre Mamba"
+ * (rodolfoviana.com.br), sections "Preliminares" (discretisation and the
+ * first-order input rule B-bar = Delta*B), "O mecanismo de seleção (S6)"
+ * (input-dependent B_t, C_t, Delta_t and the time-varying recurrence),
+ * "A varredura paralela ciente do hardware" (the recurrence as an
+ * associative scan over (A-bar_t, B-bar_t x_t) pairs, kept on chip, only y
+ * written back), "O bloco Mamba" (the silu(z) gate); the blog post "Mamba-2
+ * e State Space Duality (SSD)" (produtoramaxvision.com.br), section "Como o
+ * Mamba-1 alcançou complexidade linear" (the S6 equations with the D skip and
+ * the one-token forward_step on a stored state).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers (hipMalloc'd or equivalent), owned by the
+ *    caller. The library allocates nothing, keeps no per-call state and may
+ *    be called from several host threads.
+ *  - Tensors are dense, row-major, in the shapes listed; D (channels) is the
+ *    fastest axis of x, delta, z and y; N is the fastest axis of Bt, Ct, A
+ *    and the state. Every base pointer must be 16-byte aligned.
+ *  - dtype selects the storage type of the activations x, delta, z, Bt, Ct
+ *    and y: SSM_F32 (float) or SSM_BF16 (bfloat16). A, Dskip and the state
+ *    are always float. All arithmetic is float32; bfloat16 outputs are
+ *    rounded to nearest even.
+ *  - N (state size) must be 1, 2, 4, 8 or 16.
+ *  - delta is the step AFTER the softplus (the pages apply softplus to a
+ *    projection plus bias before the scan).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise the host. Arguments are checked on the
+ *    host before any HIP call; a failed check returns a negative status and
+ *    launches nothing. SSM_ERR_HIP reports a failed launch; faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - NaN or Inf inputs are not special-cased and propagate.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Activation storage types. */
+#define SSM_F32 0
+#define SSM_BF16 1
+
+/* Status codes. */
+#define SSM_OK 0
+#define SSM_ERR_NULL (-1)        /* a required pointer is NULL */
+#define SSM_ERR_SHAPE (-2)       /* a size is negative or the tensor sizes overflow */
+#define SSM_ERR_DTYPE (-3)       /* dtype is neither SSM_F32 nor SSM_BF16 */
+#define SSM_ERR_UNSUPPORTED (-4) /* N is not 1, 2, 4, 8 or 16 */
+#define SSM_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned */
+#define SSM_ERR_WORKSPACE (-6)   /* workspace is NULL or smaller than required */
+#define SSM_ERR_HIP (-7)         /* a HIP launch or device query failed */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *ssm_status_string(int status);
+
+/* Library version string (static storage). */
+const char *ssm_version(void);
+
+/*
+ * Scratch bytes ssm_scan_fwd needs for these sizes (0 when none). The
+ * workspace holds per-chunk summaries of long sequences (the end state of
+ * each chunk from a zero start and the chunk's summed delta); its contents on
+ * entry do not matter and are overwritten. Returns 0 for invalid sizes.
+ */
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
+
+/*
+ * Selective scan forward over L tokens.
+ *
+ *   x, delta      (batch, L, D)  dtype      input and step (post-softplus)
+ *   A             (D, N)         float      diagonal state matrix (negative)
+ *   Bt, Ct        (batch, L, N)  dtype      per-token input / output vectors,
+ *                                           shared by all D channels
+ *   Dskip         (D)            float      skip weight; NULL = no skip term
+ *   z             (batch, L, D)  dtype      gate input; NULL = no gate
+ *   state_in      (batch, D, N)  float      carried-in state; NULL = zeros
+ *   state_out     (batch, D, N)  float      state after token L-1; NULL = not
+ *                                           written; may equal state_in
+ *   y             (batch, L, D)  dtype      output (written)
+ *   workspace     ssm_scan_workspace_bytes() bytes of device memory, or NULL
+ *                 when that size is 0
+ *
+ * y must not overlap any input. batch, L or D equal to 0 is valid: nothing is
+ * computed, except that state_out (if given) receives state_in or zeros when
+ * L is 0. The (batch, L, D, N) expanded state is never written to memory.
+ */
+int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A,
+                 const void *Bt, const void *Ct, const float *Dskip,
+                 const void *z, const float *state_in, float *state_out,
+                 void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for `batch` sequences (one token each), updating
+ * the state in place.
+ *
+ *   x, delta      (batch, D)     dtype
+ *   A             (D, N)         float
+ *   Bt, Ct        (batch, N)     dtype
+ *   Dskip         (D)            float      NULL = no skip term
+ *   z             (batch, D)     dtype      NULL = no gate
+ *   state         (batch, D, N)  float      read, then overwritten with the
+ *                                           new state
+ *   y             (batch, D)     dtype      output (written)
+ *
+ * Equivalent to ssm_scan_fwd with L = 1 and state_in = state_out = state.
+ */
+int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
+             const void *x, const void *delta, const float *A,
+             const void *Bt, const void *Ct, const float *Dskip,
+             const void *z, float *state, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

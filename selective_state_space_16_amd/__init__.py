@@ -1,0 +1,168 @@
+"""Python binding of libssm.so, the gfx950 selective-scan (S6) library.
+
+Argument marshalling only: every step of the scan and of the decode step runs
+in the HIP kernels behind the C ABI declared in ``include/ssm.h``. PyTorch
+supplies device memory and the current HIP stream. There is no fallback: if
+the library is not built, or a tensor is not on the GPU, the call raises.
+
+Functions (same names as the C ABI):
+  ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None,
+               state_out=None, y=None, workspace=None) -> y
+  ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None) -> y
+  ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
+  ssm_status_string(status) -> str, ssm_version() -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step",
+    "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS",
+]
+
+SSM_F32 = 0
+SSM_BF16 = 1
+STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE",
+          -4: "SSM_ERR_UNSUPPORTED", -5: "SSM_ERR_ALIGN", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libssm.so")
+
+# The functions include/ssm.h declares.
+EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({ssm_status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    L = ctypes.CDLL(lib_path)
+    i64, vp, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.ssm_status_string.argtypes = [ci]
+    L.ssm_status_string.restype = ctypes.c_char_p
+    L.ssm_version.argtypes = []
+    L.ssm_version.restype = ctypes.c_char_p
+    L.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    L.ssm_scan_workspace_bytes.restype = sz
+    L.ssm_scan_fwd.argtypes = [i64, i64, i64, i64, ci] + [vp] * 10 + [vp, sz, vp]
+    L.ssm_scan_fwd.restype = ci
+    L.ssm_step.argtypes = [i64, i64, i64, ci] + [vp] * 9 + [vp]
+    L.ssm_step.restype = ci
+    _lib = L
+    return L
+
+
+def ssm_status_string(status: int) -> str:
+    return lib().ssm_status_string(int(status)).decode()
+
+
+def ssm_version() -> str:
+    return lib().ssm_version().decode()
+
+
+def ssm_scan_workspace_bytes(batch: int, L: int, D: int, N: int, dtype: int) -> int:
+    return int(lib().ssm_scan_workspace_bytes(batch, L, D, N, dtype))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_out=None,
+                 y=None, workspace=None, stream=None):
+    """Selective scan forward. Shapes: x, delta, z, y (batch, L, D); A (D, N);
+    Bt, Ct (batch, L, N); Dskip (D,); state_in, state_out (batch, D, N) float32.
+    Allocates y and the workspace with torch when they are not given."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and A (D, N)")
+    batch, L, D = x.shape
+    N = A.shape[1]
+    act = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    if y is None:
+        y = torch.empty_like(x)
+    ws_bytes = ssm_scan_workspace_bytes(batch, L, D, N, code)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    args = [
+        _ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(A, "A", f32, (D, N)),
+        _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
+        _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+        _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(state_out, "state_out", f32, (batch, D, N)),
+        _ptr(y, "y", act, (batch, L, D)),
+    ]
+    ws_ptr = _ptr(workspace, "workspace")
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_scan_fwd(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_scan_fwd")
+    return y
+
+
+def ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None):
+    """One decode step. Shapes: x, delta, z, y (batch, D); A (D, N); Bt, Ct
+    (batch, N); Dskip (D,); state (batch, D, N) float32, updated in place."""
+    import torch
+    if x.dim() != 2 or A.dim() != 2:
+        raise ValueError("x must be (batch, D) and A (D, N)")
+    batch, D = x.shape
+    N = A.shape[1]
+    act = x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    if y is None:
+        y = torch.empty_like(x)
+    args = [
+        _ptr(x, "x", act), _ptr(delta, "delta", act, (batch, D)), _ptr(A, "A", f32, (D, N)),
+        _ptr(Bt, "Bt", act, (batch, N)), _ptr(Ct, "Ct", act, (batch, N)),
+        _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, D)),
+        _ptr(state, "state", f32, (batch, D, N)), _ptr(y, "y", act, (batch, D)),
+    ]
+    st = lib().ssm_step(batch, D, N, code, *args, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_step")
+    return y

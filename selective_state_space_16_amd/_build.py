@@ -1,0 +1,59 @@
+"""Compile libssm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libssm.so")
+ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["ssm_scan.hip", "ssm_step.hip", "ssm_abi.cpp"]
+
+# -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-ffp-contract=fast", "-Wall", "-Wno-unused-result",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(out: str = LIB, verbose: bool = False) -> str:
+    """Compile every source into one shared library (always rebuilds)."""
+    objs = []
+    tmpdir = os.path.join(PKG, "_build")
+    os.makedirs(tmpdir, exist_ok=True)
+    cc = hipcc()
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(tmpdir, src + ".o")
+        cmd = [cc] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [cc, "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"),
+                   "-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

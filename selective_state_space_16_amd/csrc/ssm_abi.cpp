@@ -1,0 +1,145 @@
+// C ABI of libssm.so: argument checks on the host, then kernel dispatch.
+// Every check runs before any HIP call, so a rejected call launches nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ssm.h"
+#include "ssm_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 46;  // keeps every byte offset far from overflow
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
+
+// Product of non-negative sizes, or -1 when it exceeds kMaxElems.
+int64_t checked_mul(int64_t a, int64_t b) {
+    if (a == 0 || b == 0) return 0;
+    if (a > kMaxElems / b) return -1;
+    return a * b;
+}
+
+int64_t checked_mul3(int64_t a, int64_t b, int64_t c) {
+    const int64_t ab = checked_mul(a, b);
+    return ab < 0 ? -1 : checked_mul(ab, c);
+}
+
+size_t round_up256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace layout for a plan: [chunk states (batch,K,D,N) | summed deltas (batch,K,D)].
+size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc) {
+    ssm::scan_plan(batch, L, D, N, K, Lc);
+    if (*K <= 1) return 0;
+    return round_up256((size_t)batch * *K * D * N * sizeof(float)) +
+           round_up256((size_t)batch * *K * D * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssm_status_string(int status) {
+    switch (status) {
+        case SSM_OK: return "ok";
+        case SSM_ERR_NULL: return "a required pointer is NULL";
+        case SSM_ERR_SHAPE: return "a size is negative or the tensor sizes overflow";
+        case SSM_ERR_DTYPE: return "dtype must be SSM_F32 or SSM_BF16";
+        case SSM_ERR_UNSUPPORTED: return "N must be 1, 2, 4, 8 or 16";
+        case SSM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case SSM_ERR_WORKSPACE: return "workspace is missing or too small";
+        case SSM_ERR_HIP: return "a HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char *ssm_version(void) { return "ssm-gfx950 0.1"; }
+
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
+    if (batch < 0 || L < 0 || D < 0 || !supported_n(N)) return 0;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+    if (checked_mul3(batch, L, D) < 0 || checked_mul3(batch, D, N) < 0) return 0;
+    if (batch == 0 || L == 0 || D == 0) return 0;
+    int64_t K, Lc;
+    return workspace_for(batch, L, D, N, &K, &Lc);
+}
+
+int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A,
+                 const void *Bt, const void *Ct, const float *Dskip,
+                 const void *z, const float *state_in, float *state_out,
+                 void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
+    if (checked_mul3(batch, L, D) < 0 || checked_mul3(batch, L, N) < 0 || checked_mul3(batch, D, N) < 0)
+        return SSM_ERR_SHAPE;
+    if (batch == 0 || D == 0) return SSM_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (L == 0) {
+        if (!state_out) return SSM_OK;
+        if (!aligned16(state_out) || (state_in && !aligned16(state_in))) return SSM_ERR_ALIGN;
+        if (state_in == state_out) return SSM_OK;
+        return ssm::launch_state_copy(state_in, state_out, batch * D * N, s) == hipSuccess ? SSM_OK
+                                                                                          : SSM_ERR_HIP;
+    }
+    if (!x || !delta || !A || !Bt || !Ct || !y) return SSM_ERR_NULL;
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, state_out, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+
+    ssm::ScanArgs a{};
+    a.batch = batch;
+    a.L = L;
+    a.D = D;
+    a.x = x;
+    a.delta = delta;
+    a.Bt = Bt;
+    a.Ct = Ct;
+    a.z = z;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.y = y;
+    const size_t need = workspace_for(batch, L, D, N, &a.K, &a.Lc);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return SSM_ERR_ALIGN;
+        char *w = (char *)workspace;
+        a.ws_state = (float *)w;
+        a.ws_dsum = (float *)(w + round_up256((size_t)batch * a.K * D * N * sizeof(float)));
+    }
+    return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
+             const void *x, const void *delta, const float *A,
+             const void *Bt, const void *Ct, const float *Dskip,
+             const void *z, float *state, void *y, void *stream) {
+    if (batch < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
+    if (checked_mul3(batch, D, N) < 0) return SSM_ERR_SHAPE;
+    if (batch == 0 || D == 0) return SSM_OK;
+    if (!x || !delta || !A || !Bt || !Ct || !state || !y) return SSM_ERR_NULL;
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+    ssm::StepArgs a{};
+    a.batch = batch;
+    a.D = D;
+    a.x = x;
+    a.delta = delta;
+    a.Bt = Bt;
+    a.Ct = Ct;
+    a.z = z;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.state = state;
+    a.y = y;
+    return ssm::launch_step(a, (int)N, dtype, (hipStream_t)stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

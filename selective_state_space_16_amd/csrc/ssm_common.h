@@ -1,0 +1,59 @@
+// Device helpers shared by the gfx950 scan and decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Activation storage: float, or bfloat16 held as raw 16-bit patterns.
+template <int DT> struct Act;
+template <> struct Act<0> { using T = float; };
+template <> struct Act<1> { using T = uint16_t; };
+
+__device__ __forceinline__ float ld_act(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_act(const uint16_t *p, int64_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);  // exact widening
+}
+__device__ __forceinline__ void st_act(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_act(uint16_t *p, int64_t i, float v) {
+    // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even)
+    p[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Loads of data every lane of a wave shares, through the scalar cache.
+typedef const __attribute__((address_space(4))) float *cf32_ptr;
+typedef const __attribute__((address_space(4))) uint32_t *cu32_ptr;
+
+// Row of N values starting at element `off`, identical for all lanes.
+template <int N>
+__device__ __forceinline__ void ld_row_uniform(const float *base, int64_t off, float (&r)[N]) {
+    cf32_ptr p = (cf32_ptr)(base + off);
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = p[n];
+}
+template <int N>
+__device__ __forceinline__ void ld_row_uniform(const uint16_t *base, int64_t off, float (&r)[N]) {
+    if constexpr (N == 1) {
+        r[0] = ld_act(base, off);  // a single 16-bit value: plain load
+    } else {
+        cu32_ptr p = (cu32_ptr)(base + off);  // off is even when N is even
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            uint32_t w = p[k];
+            r[2 * k] = __uint_as_float(w << 16);
+            r[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
+__device__ __forceinline__ float silu(float zv) {
+    return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
+}
+
+}  // namespace ssm

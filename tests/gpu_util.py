@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: move stored inputs to the device, run the
+library through its binding, compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import selective_state_space_16_amd as ssm
+import workloads as W
+
+# Tolerances fixed for this path: float32 activations must match the float64
+# oracle to relative L2 1e-5 and max-abs 1e-4; bfloat16 activations with a
+# float32 state to relative L2 2e-2 (outputs and final state).
+TOL = {"f32": {"rel": 1e-5, "maxabs": 1e-4}, "bf16": {"rel": 2e-2, "maxabs": None}}
+
+
+def say(*a):
+    """Print and flush, so a GPU failure names the case that was running."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def to_f64(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = got - ref
+    nref = float(np.sqrt(np.sum(ref * ref)))
+    rel = float(np.sqrt(np.sum(diff * diff))) / (nref if nref > 0 else 1.0)
+    return rel, float(np.abs(diff).max()) if diff.size else 0.0
+
+
+def check(got, ref, dtype, what):
+    rel, mx = errors(got, ref)
+    tol = TOL[dtype]
+    say(f"  {what}: relL2={rel:.3e} maxabs={mx:.3e}")
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    assert rel <= tol["rel"], f"{what}: relL2 {rel:.3e} > {tol['rel']}"
+    if tol["maxabs"] is not None:
+        assert mx <= tol["maxabs"], f"{what}: maxabs {mx:.3e} > {tol['maxabs']}"
+    return rel, mx
+
+
+def gpu_scan(inp, want_state=True, state_alias=False):
+    """Run ssm_scan_fwd on stored inputs; returns (y64, state64 or None)."""
+    import torch
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    st_out = None
+    if want_state:
+        if state_alias and dev["state_in"] is not None:
+            st_out = dev["state_in"]
+        else:
+            st_out = torch.empty((dev["x"].shape[0], dev["A"].shape[0], dev["A"].shape[1]),
+                                 dtype=torch.float32, device="cuda")
+    y = ssm.ssm_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], Dskip=dev["Dskip"],
+                         z=dev["z"], state_in=dev["state_in"], state_out=st_out)
+    torch.cuda.synchronize()
+    return to_f64(y), (to_f64(st_out) if st_out is not None else None)
+
+
+def oracle_scan(inp, dtype):
+    return oracle.get().scan(inp, dtype)

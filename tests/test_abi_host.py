@@ -1,0 +1,114 @@
+"""The C ABI on the host: the library loads, exports what include/ssm.h
+declares, and rejects bad arguments before any HIP call (CPU only; no
+kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_16_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+P = 0x10000        # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10004      # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+)\s*\(", text)))
+
+
+def test_header_matches_binding():
+    assert declared_functions() == sorted(ssm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssm.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and the exported symbols are really in the dynamic symbol table
+    out = os.popen("nm -D --defined-only " + ssm.lib_path).read()
+    for name in declared_functions():
+        assert re.search(r"\sT\s" + name + r"$", out, re.M), name
+
+
+def test_status_strings_and_version():
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert ssm.ssm_status_string(code) and ssm.ssm_status_string(code) != "unknown status"
+    assert ssm.ssm_status_string(99) == "unknown status"
+    assert "gfx950" in ssm.ssm_version()
+
+
+def test_workspace_bytes():
+    assert ssm.ssm_scan_workspace_bytes(1, 256, 64, 16, ssm.SSM_F32) >= 0
+    assert ssm.ssm_scan_workspace_bytes(-1, 256, 64, 16, ssm.SSM_F32) == 0
+    assert ssm.ssm_scan_workspace_bytes(1, 256, 64, 3, ssm.SSM_F32) == 0
+    assert ssm.ssm_scan_workspace_bytes(1, 256, 64, 16, 7) == 0
+    assert ssm.ssm_scan_workspace_bytes(0, 256, 64, 16, ssm.SSM_F32) == 0
+    # long sequences are split and need chunk summaries: (N+1) floats per chunk and channel
+    w = ssm.ssm_scan_workspace_bytes(1, 1 << 20, 1536, 16, ssm.SSM_BF16)
+    assert w > 0 and w % 256 == 0
+
+
+def scan(**kw):
+    a = dict(batch=1, L=8, D=64, N=16, dtype=0, x=P, delta=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             state_in=None, state_out=None, y=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_fwd(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["delta"],
+                                  a["A"], a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state_in"],
+                                  a["state_out"], a["y"], a["ws"], a["wsb"], a["stream"])
+
+
+def step(**kw):
+    a = dict(batch=1, D=64, N=16, dtype=0, x=P, delta=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             state=P, y=P, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_step(a["batch"], a["D"], a["N"], a["dtype"], a["x"], a["delta"], a["A"],
+                              a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(L=-5), -2), (dict(D=-1), -2), (dict(N=-16), -2),
+    (dict(dtype=2), -3), (dict(N=3), -4), (dict(N=32), -4), (dict(N=0), -4),
+    (dict(x=None), -1), (dict(delta=None), -1), (dict(A=None), -1), (dict(Bt=None), -1),
+    (dict(Ct=None), -1), (dict(y=None), -1),
+    (dict(x=MIS), -5), (dict(Ct=MIS), -5), (dict(z=MIS), -5), (dict(Dskip=MIS), -5),
+    (dict(state_out=MIS), -5),
+    (dict(batch=1 << 40, L=1 << 20, D=1 << 20), -2),
+    # a long sequence needs a workspace
+    (dict(L=1 << 20, D=64), -6), (dict(L=1 << 20, D=64, ws=P, wsb=16), -6),
+])
+def test_scan_rejects(kw, code):
+    assert scan(**kw) == code
+
+
+def test_scan_empty_is_ok_without_gpu():
+    # nothing to compute: returns before any HIP call
+    assert scan(batch=0) == 0
+    assert scan(D=0) == 0
+    assert scan(L=0) == 0            # no state_out: nothing to write
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=5), -3), (dict(N=5), -4), (dict(state=None), -1),
+    (dict(y=None), -1), (dict(state=MIS), -5), (dict(Bt=MIS), -5),
+])
+def test_step_rejects(kw, code):
+    assert step(**kw) == code
+
+
+def test_step_empty_is_ok_without_gpu():
+    assert step(batch=0) == 0
+    assert step(D=0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 8)
+    A = torch.zeros(8, 16)
+    with pytest.raises((ValueError, TypeError)):
+        ssm.ssm_scan_fwd(x, x, A, torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))

@@ -1,0 +1,103 @@
+"""Invariants of the GPU path itself (needs MI355X): split-and-resume equals one
+call, a fold of decode steps equals the scan, repeated runs are bit-identical,
+delta = 0 keeps the state, in-place state, and the empty cases."""
+import numpy as np
+import pytest
+
+import selective_state_space_16_amd as ssm
+import workloads as W
+from gpu_util import check, gpu_scan, oracle_scan, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _inp(L=900, D=96, dtype="f32", state=0.4, seed=80, batch=2):
+    return W.scan_inputs(W.ScanConfig("comp", batch, L, D, 16, dtype, gate=True, dskip="uniform",
+                                      state_in=state, seed=seed))
+
+
+def _slice(inp, t0, t1):
+    return {k: (v[:, t0:t1] if k in ("x", "delta", "z", "Bt", "Ct") and v is not None else v)
+            for k, v in inp.items()}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L1", [1, 64, 333, 899])
+def test_split_and_resume(dtype, L1):
+    """scan(L) == scan(L1) then scan(L - L1) from the first call's state."""
+    say(f"case split dtype={dtype} L1={L1}")
+    inp = _inp(dtype=dtype)
+    y, st = gpu_scan(inp)
+    a = _slice(inp, 0, L1)
+    y1, s1 = gpu_scan(a)
+    b = _slice(inp, L1, inp["x"].shape[1])
+    b["state_in"] = s1.astype(np.float32)
+    y2, s2 = gpu_scan(b)
+    check(np.concatenate([y1, y2], 1), y, dtype, "y split vs whole")
+    check(s2, st, dtype, "state split vs whole")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_fold_equals_scan(dtype):
+    import torch
+    say(f"case fold dtype={dtype}")
+    inp = _inp(L=200, D=70, dtype=dtype)
+    y, st = gpu_scan(inp)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    state = dev["state_in"].clone()
+    ys = []
+    for t in range(200):
+        yt = ssm.ssm_step(dev["x"][:, t].contiguous(), dev["delta"][:, t].contiguous(), dev["A"],
+                          dev["Bt"][:, t].contiguous(), dev["Ct"][:, t].contiguous(), state,
+                          Dskip=dev["Dskip"], z=dev["z"][:, t].contiguous())
+        ys.append(to_f64(yt))
+    torch.cuda.synchronize()
+    check(np.stack(ys, 1), y, dtype, "fold of steps vs scan (y)")
+    check(to_f64(state), st, dtype, "fold of steps vs scan (state)")
+
+
+@pytest.mark.parametrize("cfg", ["c0", "c1"])
+def test_bitwise_deterministic(cfg):
+    say(f"case determinism {cfg}")
+    inp = W.scan_inputs(W.SCAN_CONFIGS[cfg])
+    y1, _ = gpu_scan(inp, want_state=False)
+    y2, _ = gpu_scan(inp, want_state=False)
+    assert np.array_equal(y1, y2)
+
+
+def test_zero_delta_keeps_state_bitwise():
+    say("case delta = 0")
+    inp = _inp(L=1000, D=64, state=1.0)
+    inp["delta"] = np.zeros_like(inp["delta"])
+    y, st = gpu_scan(inp)
+    assert np.array_equal(st, inp["state_in"].astype(np.float64))
+    yr, _ = oracle_scan(inp, "f32")
+    check(y, yr, "f32", "y with delta = 0")
+
+
+def test_state_in_place():
+    say("case state_out aliases state_in")
+    inp = _inp(L=500, D=80)
+    y, st = gpu_scan(inp)
+    y2, st2 = gpu_scan(inp, state_alias=True)
+    assert np.array_equal(y, y2) and np.array_equal(st, st2)
+
+
+def test_empty_and_zero_length():
+    import torch
+    say("case empty")
+    A = torch.full((64, 16), -1.0, device="cuda")
+    x = torch.zeros((0, 5, 64), device="cuda")
+    Bt = torch.zeros((0, 5, 16), device="cuda")
+    ssm.ssm_scan_fwd(x, x, A, Bt, Bt)
+    # L = 0: state_out receives state_in (or zeros)
+    x = torch.zeros((2, 0, 64), device="cuda")
+    Bt = torch.zeros((2, 0, 16), device="cuda")
+    sin = torch.randn((2, 64, 16), device="cuda")
+    sout = torch.full((2, 64, 16), 7.0, device="cuda")
+    ssm.ssm_scan_fwd(x, x, A, Bt, Bt, state_in=sin, state_out=sout)
+    torch.cuda.synchronize()
+    assert torch.equal(sin, sout)
+    ssm.ssm_scan_fwd(x, x, A, Bt, Bt, state_out=sout)
+    torch.cuda.synchronize()
+    assert not sout.any()

@@ -22,9 +22,14 @@ per-channel dt drawn log-uniform in [1e-3, 1e-1]; x, z, Bt, Ct ~ N(0, 1);
 Dskip = 1 or U(0.5, 1.5). delta is handed to the scan after the softplus.
 
 Random streams: ``numpy.random.default_rng(SeedSequence(seed, spawn_key=key))``
-with one key per (tensor kind, batch row, token chunk of 65536). Generation is
-therefore chunked and restartable, and any token range can be regenerated
-without the rest of the sequence.
+with one key per (tensor kind, batch row, token chunk of 65536, block of 64
+channels). Generation is therefore chunked and restartable: any token range
+or channel subset can be regenerated without the rest of the tensor.
+
+``fill_scan_device`` / ``fill_step_device`` draw tensors of the same
+distributions with torch on the GPU; they fill the channels of very large
+workloads that a test computes but does not compare, so that only the
+compared channels need the (slower) numpy streams.
 """
 from __future__ import annotations
 
@@ -35,13 +40,14 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
+    "fill_scan_device", "fill_step_device", "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
     "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
     "storage_to_f64", "scan_bytes", "step_bytes",
 ]
 
 DTYPES = ("f32", "bf16")
 _CHUNK = 65536  # tokens per random stream
+_CBLK = 64      # channels per random stream
 
 # stream keys (tensor kinds)
 _K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE = range(8)
@@ -152,18 +158,25 @@ def _channel_params(seed: int, D: int, N: int, dskip: str):
     return A, dt_bias, Dskip
 
 
-def _token_block(seed: int, kind: int, b: int, t0: int, t1: int, width: int) -> np.ndarray:
-    """N(0,1) float64 block of shape (t1-t0, width) from the per-chunk streams."""
-    out = np.empty((t1 - t0, width), dtype=np.float64)
-    if t1 == t0:
+def _token_block(seed: int, kind: int, b: int, t0: int, t1: int, width: int,
+                 cols: Optional[np.ndarray] = None) -> np.ndarray:
+    """N(0,1) float64 block of shape (t1-t0, len(cols)) from the per-(chunk,
+    channel block) streams; `cols` defaults to all `width` columns."""
+    cols = np.arange(width) if cols is None else np.asarray(cols)
+    out = np.empty((t1 - t0, len(cols)), dtype=np.float64)
+    if t1 == t0 or len(cols) == 0:
         return out
+    blocks = np.unique(cols // _CBLK)
     for c in range(t0 // _CHUNK, (t1 - 1) // _CHUNK + 1):
         cs = c * _CHUNK
         lo, hi = max(t0, cs), min(t1, cs + _CHUNK)
-        # A stream's draws are a fixed sequence: drawing the first (hi - cs)
-        # rows gives the same rows as drawing the whole chunk.
-        block = _rng(seed, kind, b, c).standard_normal((hi - cs, width))
-        out[lo - t0:hi - t0] = block[lo - cs:]
+        for blk in blocks:
+            w = min(_CBLK, width - blk * _CBLK)
+            # A stream's draws are a fixed sequence: drawing the first (hi - cs)
+            # rows gives the same rows as drawing the whole chunk.
+            block = _rng(seed, kind, b, c, blk).standard_normal((hi - cs, w))
+            sel = np.nonzero(cols // _CBLK == blk)[0]
+            out[lo - t0:hi - t0, sel] = block[lo - cs:, cols[sel] - blk * _CBLK]
     return out
 
 
@@ -190,11 +203,11 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     Bt = np.empty((cfg.batch, T, cfg.N), dtype=x.dtype)
     Ct = np.empty_like(Bt)
     for b in range(cfg.batch):
-        eps = _token_block(cfg.seed, _K_DNOISE, b, t0, t1, cfg.D)[:, sel]
+        eps = _token_block(cfg.seed, _K_DNOISE, b, t0, t1, cfg.D, sel)
         dl[b] = _store(_softplus(0.5 * eps + dt_bias[sel][None, :]), act)
-        x[b] = _store(_token_block(cfg.seed, _K_X, b, t0, t1, cfg.D)[:, sel], act)
+        x[b] = _store(_token_block(cfg.seed, _K_X, b, t0, t1, cfg.D, sel), act)
         if z is not None:
-            z[b] = _store(_token_block(cfg.seed, _K_Z, b, t0, t1, cfg.D)[:, sel], act)
+            z[b] = _store(_token_block(cfg.seed, _K_Z, b, t0, t1, cfg.D, sel), act)
         Bt[b] = _store(_token_block(cfg.seed, _K_B, b, t0, t1, cfg.N), act)
         Ct[b] = _store(_token_block(cfg.seed, _K_C, b, t0, t1, cfg.N), act)
     out = {"x": x, "delta": dl, "z": z, "A": np.ascontiguousarray(A[sel]), "Bt": Bt, "Ct": Ct,
@@ -221,20 +234,66 @@ def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray]
     _A, dt_bias, _D = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
     sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
     act = cfg.dtype
-    key = 1000 + step
-    eps = _rng(cfg.seed, _K_DNOISE, key).standard_normal((cfg.batch, cfg.D))[:, sel]
+    key = 1000 + step  # step s draws "batch row" 1000+s, one token per sequence
+
+    def chan(kind):  # (batch, len(sel)): the batch axis plays the token axis
+        return _token_block(cfg.seed, kind, key, 0, cfg.batch, cfg.D, sel)
+
     out = {
-        "delta": _store(_softplus(0.5 * eps + dt_bias[sel][None, :]), act),
-        "x": _store(_rng(cfg.seed, _K_X, key).standard_normal((cfg.batch, cfg.D))[:, sel], act),
-        "z": _store(_rng(cfg.seed, _K_Z, key).standard_normal((cfg.batch, cfg.D))[:, sel], act)
-        if cfg.gate else None,
-        "Bt": _store(_rng(cfg.seed, _K_B, key).standard_normal((cfg.batch, cfg.N)), act),
-        "Ct": _store(_rng(cfg.seed, _K_C, key).standard_normal((cfg.batch, cfg.N)), act),
+        "delta": _store(_softplus(0.5 * chan(_K_DNOISE) + dt_bias[sel][None, :]), act),
+        "x": _store(chan(_K_X), act),
+        "z": _store(chan(_K_Z), act) if cfg.gate else None,
+        "Bt": _store(_token_block(cfg.seed, _K_B, key, 0, cfg.batch, cfg.N), act),
+        "Ct": _store(_token_block(cfg.seed, _K_C, key, 0, cfg.batch, cfg.N), act),
     }
-    for k in ("delta", "x", "z"):
-        if out[k] is not None:
-            out[k] = np.ascontiguousarray(out[k])
     return out
+
+
+def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345):
+    """torch tensors of the full workload `cfg` on `device`, same distributions
+    as scan_inputs but drawn with torch (values differ from the numpy streams).
+    Returns x, delta, z (or None) and Bt, Ct; A, Dskip and state_in come from
+    scan_inputs(cfg, 0, 0)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    _A, dt_bias, _D = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
+    bias = torch.tensor(dt_bias, dtype=torch.float32, device=device)
+    shape = (cfg.batch, cfg.L, cfg.D)
+
+    def normal(shp):
+        return torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+
+    eps = normal(shape)
+    delta = torch.nn.functional.softplus(eps.mul_(0.5).add_(bias)).to(act)
+    del eps
+    out = {"delta": delta, "x": normal(shape).to(act),
+           "z": normal(shape).to(act) if cfg.gate else None,
+           "Bt": normal((cfg.batch, cfg.L, cfg.N)).to(act), "Ct": normal((cfg.batch, cfg.L, cfg.N)).to(act)}
+    return out
+
+
+def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321):
+    """torch tensors for `steps` decode steps on `device` (same distributions as
+    step_token_inputs, drawn with torch): x, delta, z of shape (steps, batch, D)
+    and Bt, Ct of shape (steps, batch, N)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    _A, dt_bias, _D = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
+    bias = torch.tensor(dt_bias, dtype=torch.float32, device=device)
+    shape = (steps, cfg.batch, cfg.D)
+
+    def normal(shp):
+        return torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+
+    eps = normal(shape)
+    delta = torch.nn.functional.softplus(eps.mul_(0.5).add_(bias)).to(act)
+    del eps
+    return {"delta": delta, "x": normal(shape).to(act), "z": normal(shape).to(act) if cfg.gate else None,
+            "Bt": normal((steps, cfg.batch, cfg.N)).to(act), "Ct": normal((steps, cfg.batch, cfg.N)).to(act)}
 
 
 def _esize(dtype: str) -> int:
