@@ -95,7 +95,7 @@ def bench_scan(args, name):
         sets.append(W.fill_scan_device(cfg, "cuda", seed=1000 + len(sets)))
     ys = [torch.empty_like(s["x"]) for s in sets]
     ws_bytes = ssm.ssm_scan_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N, 0 if cfg.dtype == "f32" else 1)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = ssm.new_workspace(ws_bytes)
     st_out = torch.empty((cfg.batch, cfg.D, cfg.N), dtype=torch.float32, device="cuda") \
         if cfg.state_in is not None else None
     stream = torch.cuda.current_stream()
@@ -179,7 +179,7 @@ def bench_step(args):
         import oracle
         o = oracle.get()
         sel = np.arange(0, cfg.D, 16)  # a bounded sample: every 16th channel
-        st64 = base["state"][:, sel].astype(np.float64)
+        st64 = np.ascontiguousarray(base["state"][:, sel], dtype=np.float64)
         reps, tot = 0, 0.0
         while reps == 0 or (tot < args.cpu_seconds and reps < cfg.steps):
             tk = W.step_token_inputs(cfg, reps, channels=sel)

@@ -75,10 +75,17 @@ const char *ssm_status_string(int status);
 const char *ssm_version(void);
 
 /*
- * Scratch bytes ssm_scan_fwd needs for these sizes (0 when none). The
- * workspace holds per-chunk summaries of long sequences (the end state of
- * each chunk from a zero start and the chunk's summed delta); its contents on
- * entry do not matter and are overwritten. Returns 0 for invalid sizes.
+ * Scratch bytes ssm_scan_fwd needs for these sizes (0 when none). Sequences
+ * longer than one chunk are scanned by many workgroups at once; the workspace
+ * is where each chunk publishes its summary (the end state from a zero start
+ * and its summed delta) and its final state for the chunks after it, each
+ * with a flag word.
+ *
+ * The workspace must be zero-filled before its first use. After that it may
+ * be reused by later calls of any size without clearing, as long as nothing
+ * else writes to it in between; each call marks its flags with a new value.
+ * Calls that share a workspace must not run at the same time. Returns 0 for
+ * invalid sizes.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
 

@@ -20,7 +20,8 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step",
-    "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS",
+    "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
+    "workspace_error",
 ]
 
 SSM_F32 = 0
@@ -79,6 +80,20 @@ def ssm_scan_workspace_bytes(batch: int, L: int, D: int, N: int, dtype: int) -> 
     return int(lib().ssm_scan_workspace_bytes(batch, L, D, N, dtype))
 
 
+def new_workspace(nbytes: int, device="cuda"):
+    """A scan workspace: zero-filled before first use, reusable across calls."""
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def workspace_error(workspace) -> int:
+    """Nonzero when a cross-workgroup wait of a scan that used this workspace
+    timed out (reads the workspace header; synchronises)."""
+    if workspace is None or workspace.numel() < 4:
+        return 0
+    return int(workspace[:4].view(__import__("torch").int32).item())
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.float32:
@@ -127,7 +142,7 @@ def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_o
         y = torch.empty_like(x)
     ws_bytes = ssm_scan_workspace_bytes(batch, L, D, N, code)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        workspace = new_workspace(ws_bytes, x.device)
     args = [
         _ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(A, "A", f32, (D, N)),
         _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),

@@ -2,6 +2,10 @@
 // Every check runs before any HIP call, so a rejected call launches nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
 
 #include "../../include/ssm.h"
 #include "ssm_internal.h"
@@ -28,12 +32,42 @@ int64_t checked_mul3(int64_t a, int64_t b, int64_t c) {
 
 size_t round_up256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace layout for a plan: [chunk states (batch,K,D,N) | summed deltas (batch,K,D)].
-size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc) {
+// Workspace of the chunked three-launch scan: [chunk states (batch,K,D,N) | summed deltas (batch,K,D)].
+size_t twopass_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc) {
     ssm::scan_plan(batch, L, D, N, K, Lc);
     if (*K <= 1) return 0;
     return round_up256((size_t)batch * *K * D * N * sizeof(float)) +
            round_up256((size_t)batch * *K * D * sizeof(float));
+}
+
+// Workspace of the single-pass look-back scan (0 when the sequence is one chunk).
+size_t lb_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, ssm::LbPlan *p) {
+    if (!ssm::lb_plan(batch, L, D, N, p)) return 0;
+    return p->K > 1 ? p->bytes : 0;
+}
+
+// The three-launch scan is kept for comparison: SSM_SCAN_IMPL=twopass.
+bool use_twopass() {
+    const char *e = getenv("SSM_SCAN_IMPL");
+    return e && strcmp(e, "twopass") == 0;
+}
+
+size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    int64_t K, Lc;
+    ssm::LbPlan p;
+    const size_t a = twopass_workspace(batch, L, D, N, &K, &Lc);
+    const size_t b = lb_workspace(batch, L, D, N, &p);
+    return a > b ? a : b;
+}
+
+// Distinct nonzero value per call; marks the words a call publishes in the workspace.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{0};
+    uint32_t e;
+    do {
+        e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (e == 0);
+    return e;
 }
 
 }  // namespace
@@ -61,8 +95,7 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, 
     if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
     if (checked_mul3(batch, L, D) < 0 || checked_mul3(batch, D, N) < 0) return 0;
     if (batch == 0 || L == 0 || D == 0) return 0;
-    int64_t K, Lc;
-    return workspace_for(batch, L, D, N, &K, &Lc);
+    return workspace_for(batch, L, D, N);
 }
 
 int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
@@ -89,7 +122,36 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
 
-    ssm::ScanArgs a{};
+    const size_t need = workspace_for(batch, L, D, N);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return SSM_ERR_ALIGN;
+    }
+    if (use_twopass()) {
+        ssm::ScanArgs a{};
+        a.batch = batch;
+        a.L = L;
+        a.D = D;
+        a.x = x;
+        a.delta = delta;
+        a.Bt = Bt;
+        a.Ct = Ct;
+        a.z = z;
+        a.A = A;
+        a.Dskip = Dskip;
+        a.state_in = state_in;
+        a.state_out = state_out;
+        a.y = y;
+        if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
+            char *w = (char *)workspace;
+            a.ws_state = (float *)w;
+            a.ws_dsum = (float *)(w + round_up256((size_t)batch * a.K * D * N * sizeof(float)));
+        }
+        return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+    ssm::LbPlan p;
+    const size_t lbw = lb_workspace(batch, L, D, N, &p);
+    ssm::LbArgs a{};
     a.batch = batch;
     a.L = L;
     a.D = D;
@@ -103,15 +165,21 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.state_in = state_in;
     a.state_out = state_out;
     a.y = y;
-    const size_t need = workspace_for(batch, L, D, N, &a.K, &a.Lc);
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return SSM_ERR_ALIGN;
+    a.K = p.K;
+    a.ncols = p.ncols;
+    a.ncols_pad = p.ncols_pad;
+    a.nbd = p.nbd;
+    a.epoch = next_epoch();
+    if (lbw > 0) {
         char *w = (char *)workspace;
-        a.ws_state = (float *)w;
-        a.ws_dsum = (float *)(w + round_up256((size_t)batch * a.K * D * N * sizeof(float)));
+        a.error = (uint32_t *)w;
+        a.agg_s = (float *)(w + p.off_agg_s);
+        a.agg_d = (float *)(w + p.off_agg_d);
+        a.incl = (float *)(w + p.off_incl);
+        a.agg_flag = (uint32_t *)(w + p.off_agg_flag);
+        a.incl_flag = (uint32_t *)(w + p.off_incl_flag);
     }
-    return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    return ssm::launch_scan_lb(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,

@@ -20,6 +20,29 @@ struct ScanArgs {
     int64_t Lc;        // tokens per chunk (the last chunk may be shorter)
 };
 
+// Single-pass scan with a decoupled look-back between chunks.
+struct LbArgs {
+    int64_t batch, L, D;
+    const void *x, *delta, *Bt, *Ct, *z;
+    const float *A, *Dskip, *state_in;
+    float *state_out;
+    void *y;
+    int64_t K;          // chunks per sequence
+    int64_t ncols;      // batch rows x channel blocks
+    int64_t ncols_pad;  // ncols rounded up to a multiple of the XCD count
+    int64_t nbd;        // channel blocks per batch row
+    uint32_t epoch;     // value that marks this call's published words
+    uint32_t *error;    // set when a look-back wait timed out
+    float *agg_s, *agg_d, *incl;
+    uint32_t *agg_flag, *incl_flag;
+};
+
+// Geometry and workspace layout of the look-back scan for one problem size.
+struct LbPlan {
+    int64_t cpw, nl, nbd, ncols, ncols_pad, K, chunk;
+    size_t off_agg_s, off_agg_d, off_incl, off_agg_flag, off_incl_flag, bytes;
+};
+
 struct StepArgs {
     int64_t batch, D;
     const void *x, *delta, *Bt, *Ct, *z;
@@ -31,7 +54,10 @@ struct StepArgs {
 // Sequence split used for a scan of these sizes (deterministic).
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);
 
+bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, LbPlan *p);
+
 // Launchers; return hipSuccess or the launch error.
+hipError_t launch_scan_lb(const LbArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepArgs &a, int N, int dtype, hipStream_t s);

@@ -64,9 +64,13 @@ def gpu_scan(inp, want_state=True, state_alias=False):
         else:
             st_out = torch.empty((dev["x"].shape[0], dev["A"].shape[0], dev["A"].shape[1]),
                                  dtype=torch.float32, device="cuda")
+    batch, L, D = dev["x"].shape
+    ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(batch, L, D, dev["A"].shape[1],
+                                                        0 if dev["x"].dtype == torch.float32 else 1))
     y = ssm.ssm_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], Dskip=dev["Dskip"],
-                         z=dev["z"], state_in=dev["state_in"], state_out=st_out)
+                         z=dev["z"], state_in=dev["state_in"], state_out=st_out, workspace=ws)
     torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
 
 

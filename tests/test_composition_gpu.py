@@ -101,3 +101,34 @@ def test_empty_and_zero_length():
     ssm.ssm_scan_fwd(x, x, A, Bt, Bt, state_out=sout)
     torch.cuda.synchronize()
     assert not sout.any()
+
+
+def test_lookback_many_chunks_one_column():
+    """One channel block and thousands of chunks: long chains of cross-workgroup
+    carries (every chunk depends on all earlier ones)."""
+    say("case look-back stress: 1 x 200000 x 16")
+    inp = _inp(L=200_000, D=16, dtype="f32", state=0.5, seed=81, batch=1)
+    y, st = gpu_scan(inp)
+    yr, sr = oracle_scan(inp, "f32")
+    check(y, yr, "f32", "y")
+    check(st, sr, "f32", "state_out")
+
+
+def test_workspace_reuse_across_sizes():
+    """A workspace reused by calls of different sizes without clearing."""
+    import torch
+    say("case workspace reuse")
+    big = _inp(L=5000, D=96, seed=82)
+    small = _inp(L=700, D=40, seed=83)
+    nbytes = max(ssm.ssm_scan_workspace_bytes(2, 5000, 96, 16, 0), ssm.ssm_scan_workspace_bytes(2, 700, 40, 16, 0))
+    ws = ssm.new_workspace(nbytes)
+    for inp in (big, small, big, small):
+        dev = {k: to_dev(v) for k, v in inp.items()}
+        st = torch.empty_like(dev["state_in"])
+        y = ssm.ssm_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], Dskip=dev["Dskip"],
+                             z=dev["z"], state_in=dev["state_in"], state_out=st, workspace=ws)
+        torch.cuda.synchronize()
+        assert ssm.workspace_error(ws) == 0
+        yr, sr = oracle_scan(inp, "f32")
+        check(to_f64(y), yr, "f32", "y")
+        check(to_f64(st), sr, "f32", "state_out")

@@ -138,7 +138,7 @@ def test_c4_decode_1000_steps_sampled():
         ys[s] = y[:, sel_t].float()
     torch.cuda.synchronize()
     o = oracle.get()
-    st64 = base["state"][:, sel].astype(np.float64)
+    st64 = np.ascontiguousarray(base["state"][:, sel], dtype=np.float64)
     yref = np.empty((steps, cfg.batch, len(sel)))
     for s in range(steps):
         yref[s] = o.step(toks[s], base["A"][sel], base["Dskip"][sel], st64, cfg.dtype)
