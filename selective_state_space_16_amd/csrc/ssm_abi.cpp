@@ -32,31 +32,40 @@ int64_t checked_mul3(int64_t a, int64_t b, int64_t c) {
 
 size_t round_up256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace of the chunked three-launch scan: [chunk states (batch,K,D,N) | summed deltas (batch,K,D)].
+// Both scans keep a 256-byte header at the start of the workspace (the first
+// word reports a timed-out look-back wait).
+constexpr size_t kHeader = 256;
+
+// Workspace of the chunked three-launch scan:
+// [header | chunk states (batch,K,D,N) | summed deltas (batch,K,D)].
 size_t twopass_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc) {
     ssm::scan_plan(batch, L, D, N, K, Lc);
     if (*K <= 1) return 0;
-    return round_up256((size_t)batch * *K * D * N * sizeof(float)) +
+    return kHeader + round_up256((size_t)batch * *K * D * N * sizeof(float)) +
            round_up256((size_t)batch * *K * D * sizeof(float));
 }
 
 // Workspace of the single-pass look-back scan (0 when the sequence is one chunk).
-size_t lb_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, ssm::LbPlan *p) {
-    if (!ssm::lb_plan(batch, L, D, N, p)) return 0;
+size_t lb_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, ssm::LbPlan *p) {
+    if (!ssm::lb_plan(batch, L, D, N, dtype, p)) return 0;
     return p->K > 1 ? p->bytes : 0;
 }
 
-// The three-launch scan is kept for comparison: SSM_SCAN_IMPL=twopass.
-bool use_twopass() {
+// The single-pass scan reads 16-byte pieces of channel rows; shapes whose
+// rows are not whole pieces take the three-launch scan, which can also be
+// forced with SSM_SCAN_IMPL=twopass (for comparison).
+bool use_twopass(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     const char *e = getenv("SSM_SCAN_IMPL");
-    return e && strcmp(e, "twopass") == 0;
+    if (e && strcmp(e, "twopass") == 0) return true;
+    ssm::LbPlan p;
+    return !ssm::lb_plan(batch, L, D, N, dtype, &p) || !p.supported;
 }
 
-size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N) {
+size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     int64_t K, Lc;
     ssm::LbPlan p;
     const size_t a = twopass_workspace(batch, L, D, N, &K, &Lc);
-    const size_t b = lb_workspace(batch, L, D, N, &p);
+    const size_t b = lb_workspace(batch, L, D, N, dtype, &p);
     return a > b ? a : b;
 }
 
@@ -95,7 +104,7 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, 
     if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
     if (checked_mul3(batch, L, D) < 0 || checked_mul3(batch, D, N) < 0) return 0;
     if (batch == 0 || L == 0 || D == 0) return 0;
-    return workspace_for(batch, L, D, N);
+    return workspace_for(batch, L, D, N, dtype);
 }
 
 int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
@@ -122,12 +131,12 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
 
-    const size_t need = workspace_for(batch, L, D, N);
+    const size_t need = workspace_for(batch, L, D, N, dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SSM_ERR_ALIGN;
     }
-    if (use_twopass()) {
+    if (use_twopass(batch, L, D, N, dtype)) {
         ssm::ScanArgs a{};
         a.batch = batch;
         a.L = L;
@@ -143,14 +152,14 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.state_out = state_out;
         a.y = y;
         if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
-            char *w = (char *)workspace;
+            char *w = (char *)workspace + kHeader;
             a.ws_state = (float *)w;
             a.ws_dsum = (float *)(w + round_up256((size_t)batch * a.K * D * N * sizeof(float)));
         }
         return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
     ssm::LbPlan p;
-    const size_t lbw = lb_workspace(batch, L, D, N, &p);
+    const size_t lbw = lb_workspace(batch, L, D, N, dtype, &p);
     ssm::LbArgs a{};
     a.batch = batch;
     a.L = L;
@@ -166,18 +175,15 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.state_out = state_out;
     a.y = y;
     a.K = p.K;
-    a.ncols = p.ncols;
-    a.ncols_pad = p.ncols_pad;
-    a.nbd = p.nbd;
+    a.nicol = p.nicol;
     a.epoch = next_epoch();
     if (lbw > 0) {
         char *w = (char *)workspace;
         a.error = (uint32_t *)w;
+        a.incl = (uint64_t *)(w + p.off_incl);
         a.agg_s = (float *)(w + p.off_agg_s);
         a.agg_d = (float *)(w + p.off_agg_d);
-        a.incl = (float *)(w + p.off_incl);
         a.agg_flag = (uint32_t *)(w + p.off_agg_flag);
-        a.incl_flag = (uint32_t *)(w + p.off_incl_flag);
     }
     return ssm::launch_scan_lb(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

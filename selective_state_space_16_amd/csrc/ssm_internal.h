@@ -28,19 +28,19 @@ struct LbArgs {
     float *state_out;
     void *y;
     int64_t K;          // chunks per sequence
-    int64_t ncols;      // batch rows x channel blocks
-    int64_t ncols_pad;  // ncols rounded up to a multiple of the XCD count
-    int64_t nbd;        // channel blocks per batch row
+    int64_t nicol;      // item columns (batch rows x channel blocks)
     uint32_t epoch;     // value that marks this call's published words
     uint32_t *error;    // set when a look-back wait timed out
-    float *agg_s, *agg_d, *incl;
-    uint32_t *agg_flag, *incl_flag;
+    uint64_t *incl;     // per item: inclusive end state, epoch-tagged words
+    float *agg_s, *agg_d;
+    uint32_t *agg_flag;
 };
 
 // Geometry and workspace layout of the look-back scan for one problem size.
 struct LbPlan {
-    int64_t cpw, nl, nbd, ncols, ncols_pad, K, chunk;
-    size_t off_agg_s, off_agg_d, off_incl, off_agg_flag, off_incl_flag, bytes;
+    int64_t nl, nicol, K, chunk, vec;
+    bool supported;     // shape meets the tile-load requirements
+    size_t off_incl, off_agg_s, off_agg_d, off_agg_flag, bytes;
 };
 
 struct StepArgs {
@@ -54,7 +54,7 @@ struct StepArgs {
 // Sequence split used for a scan of these sizes (deterministic).
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);
 
-bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, LbPlan *p);
+bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, LbPlan *p);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_scan_lb(const LbArgs &a, int N, int dtype, hipStream_t s);

@@ -1,42 +1,49 @@
-// Single-pass selective scan (S6) forward for gfx950: register-resident chunk
-// scan with a decoupled look-back between workgroups.
+// Single-pass selective scan (S6) forward for gfx950: persistent workgroups,
+// register-resident chunk scans, and a decoupled look-back between chunks.
 //
 // The recurrence h <- dA*h + dBx is an associative composition of affine maps
 // ("Notas sobre Mamba", section "A varredura paralela ciente do hardware":
 // the scan over (A-bar_t, B-bar_t x_t) pairs). Applying a run of tokens to a
 // state equals one pair (P, S): P = prod dA = exp(A * sum delta) and S = the
-// run's end state from a zero start. This kernel uses that at two levels:
+// run's end state from a zero start. The kernel uses this at two levels.
 //
-//  - A workgroup owns one chunk of W*T tokens of one channel block. Each wave
-//    owns T consecutive tokens of the chunk. In phase A it computes
-//    dA = exp2(delta * A*log2(e)) and dBx = delta*x*B for its tokens once and
-//    keeps them in registers, folding them into its segment's (P, S). The
-//    segments are combined through LDS.
-//  - Chunks of the same channel block pass states through global memory:
-//    every chunk publishes its aggregate (sum delta, S) as soon as phase A is
-//    done, then looks back over earlier chunks (aggregates, or an inclusive
-//    end state) to obtain its carried-in state, and publishes its own
-//    inclusive end state. Workgroups are numbered chunk-major and dispatched
-//    in order, so a chunk only ever waits on chunks dispatched before it.
-//  - Phase C rescans each wave's tokens from its carried-in state using the
-//    registers from phase A (no second exponential), reads y = C.h + D.x,
-//    applies the silu(z) gate and stores y.
+// Work items. An item is one chunk of 64 tokens of one block of CPW channels
+// (CPW = 16 for N = 16). A workgroup of 4 waves scans an item: wave w owns
+// tokens 16w..16w+15. Phase A computes dA = exp2(delta * A*log2(e)) and
+// dBx = delta*x*B once per (token, state) and keeps them in registers while
+// folding them into the wave's segment pair; the four segment pairs are
+// combined through LDS. Phase C rescans the wave's tokens from its carried-in
+// state using those registers (no second exponential) and reads out y.
 //
-// Lane layout: a wave is 4 rows of 16 lanes. A channel's N states are split
-// over NGR = N/NL rows (NL = min(N, 4) states per lane); the 16 lanes of a row
-// are 16 consecutive channels. Bt[t,:] and Ct[t,:] are the same for every
+// Between items of the same channel block the carried-in state comes from a
+// decoupled look-back: every item publishes its inclusive end state as
+// 64-bit words tagged with the call's epoch (readers validate each word, so a
+// workgroup can fetch its predecessor's state before phase A and use it
+// after). When the predecessor's state is not out yet the item publishes its
+// own aggregate (sum delta, S) so that later items can skip over it, then
+// scans back over the flags of earlier items to the nearest inclusive state
+// and replays the chain forward from it with the same arithmetic every item
+// uses for its own inclusive state; results therefore do not depend on
+// timing. Every wait is bounded: on timeout the kernel records an error word
+// in the workspace header and continues with a zero state.
+//
+// Memory. HBM rows are read in whole 128-byte lines: a workgroup loads tiles
+// of 64 tokens x TCH channels (TCH = 64 bfloat16 or 32 float channels) of x,
+// delta, z and the 64 tokens of Bt, Ct into LDS with global_load_lds (no
+// registers involved), double-buffered so that the next tile streams in while
+// the TCH/CPW items of the current tile are scanned. y is written into the
+// tile's delta area (delta is dead after phase A) and stored as whole lines.
+// Workgroups are persistent (one per slot, launched cooperatively so that all
+// are resident) and each XCD works through a contiguous range of channel
+// blocks chunk-major, so that tiles sharing lines meet in one L2.
+//
+// Lanes. A wave is 4 rows of 16 lanes. A channel's N states are split over
+// NGR = N/NL rows (NL = min(N, 4) states per lane); the 16 lanes of a row are
+// 16 consecutive channels. Bt[t,:] and Ct[t,:] are the same for every
 // channel, so a row keeps the values of its state group for 16/NL tokens in
-// one register and broadcasts them to its lanes with DPP row_newbcast. The
-// readout sum over a channel's rows uses permlane16/32 swaps, which also
-// scatter the finished tokens over the rows so that every lane finishes
-// (skip, gate, store) T/NGR of the T tokens.
-//
-// Cross-workgroup publication: data words are written with device-scope
-// stores, the wave waits for them to complete (s_waitcnt), and only then a
-// flag word carrying this call's epoch is written; readers poll the flag
-// with device-scope loads and read the data after seeing it. Every wait is
-// bounded: on timeout the kernel records an error word in the workspace
-// header and continues with a zero state.
+// one register and broadcasts them with DPP row_newbcast. The readout sum over
+// a channel's rows uses permlane16/32 swaps, which also scatter the finished
+// tokens over the rows so that each lane finishes 16/NGR of the 16 tokens.
 #include <type_traits>
 
 #include "ssm_common.h"
@@ -46,24 +53,50 @@ namespace ssm {
 
 namespace {
 
-constexpr int kSegT = 16;         // tokens per wave segment
-constexpr int kLbWaves = 4;       // waves (segments) per workgroup
-constexpr int kChunk = kSegT * kLbWaves;
-constexpr int kXcds = 8;          // XCDs of an MI355X
-constexpr long kSpinLimit = 1L << 20;   // polls before a wait gives up (about a second)
+constexpr int kSegT = 16;        // tokens per wave segment
+constexpr int kWaves = 4;        // waves (segments) per workgroup
+constexpr int kChunk = kSegT * kWaves;
+constexpr int kXcds = 8;         // XCDs of an MI355X
+constexpr long kSpinLimit = 1L << 20;  // polls before a wait gives up (about a second)
 
-template <int N>
+template <int N, int DT>
 struct Geo {
-    static constexpr int NL = N < 4 ? N : 4;     // states per lane
-    static constexpr int NGR = N / NL;           // rows per channel
-    static constexpr int SETS = 4 / NGR;         // channel sets per wave
-    static constexpr int CPW = SETS * 16;        // channels per wave
-    static constexpr int TPV = 16 / NL;          // tokens per broadcast register
-    static constexpr int BREGS = kSegT / TPV;    // broadcast registers per segment
-    static constexpr int OWN = kSegT / NGR;      // tokens each lane finishes
+    using T = typename Act<DT>::T;
+    static constexpr int NL = N < 4 ? N : 4;       // states per lane
+    static constexpr int NGR = N / NL;             // rows per channel
+    static constexpr int CPW = (4 / NGR) * 16;     // channels per wave
+    static constexpr int TPV = 16 / NL;            // tokens per broadcast register
+    static constexpr int BREGS = kSegT / TPV;      // broadcast registers per segment
+    static constexpr int OWN = kSegT / NGR;        // tokens each lane finishes
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int LINE_CH = 128 / ESZ;      // channels in a 128-byte line
+    static constexpr int TCH = CPW > LINE_CH ? CPW : LINE_CH;  // tile channels
+    static constexpr int SUBS = TCH / CPW;         // items per tile
+    static constexpr int VEC = 16 / ESZ;           // elements per 16-byte piece
 };
 
-// DPP row_newbcast: every lane of a row gets lane SRC of that row.
+template <int N, int DT>
+struct TileBuf {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    T x[kChunk][G::TCH];
+    T dl[kChunk][G::TCH];  // delta; y is written here once delta is dead
+    T z[kChunk][G::TCH];
+    T B[kChunk][N];
+    T C[kChunk][N];
+    float A[G::TCH][N];    // state matrix rows of the tile's channels
+    float Dsk[G::TCH];     // skip weights of the tile's channels
+};
+
+template <int N, int DT>
+struct Shared {
+    using G = Geo<N, DT>;
+    TileBuf<N, DT> buf[2];
+    float seg_s[kWaves][64][G::NL];  // segment end states (read only between the two item barriers)
+    float seg_d[kWaves][64];         // segment summed deltas
+    float carry[64][G::NL];          // the item's carried-in state
+};
+
 template <int SRC>
 __device__ __forceinline__ float row_bcast(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, true));
@@ -88,14 +121,6 @@ SSM_FMAC_BCAST(8) SSM_FMAC_BCAST(9) SSM_FMAC_BCAST(10) SSM_FMAC_BCAST(11)
 SSM_FMAC_BCAST(12) SSM_FMAC_BCAST(13) SSM_FMAC_BCAST(14) SSM_FMAC_BCAST(15)
 #undef SSM_FMAC_BCAST
 
-template <int I, int END, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (I < END) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, END>(f);
-    }
-}
-
 // v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b, so
 // a = [a.lo, b.lo] and b = [a.hi, b.hi]. v_permlane16_swap: the odd rows of a
 // trade places with the even rows of b. Written as inline assembly (with the
@@ -108,6 +133,14 @@ __device__ __forceinline__ void swap_odd_even_rows(float &a, float &b) {
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+template <int I, int END, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < END) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, END>(f);
+    }
+}
+
 __device__ __forceinline__ void st_dev(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -117,6 +150,12 @@ __device__ __forceinline__ float ld_dev(const float *p) {
 __device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
     return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t epoch) {
+    __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Complete this wave's stores, then raise the flag.
 __device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t epoch, int lane) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -125,262 +164,410 @@ __device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t epoch, int
     if (lane == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int N, int DT, bool GATE, bool SKIP>
-__global__ __launch_bounds__(64 * kLbWaves) void scan_lb_kernel(LbArgs a) {
-    using G = Geo<N>;
-    using T = typename Act<DT>::T;
-    constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TPV = G::TPV, BREGS = G::BREGS;
+// One 16-byte piece per lane from global memory straight into LDS at
+// lds + lane*16 (lds is the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
 
-    __shared__ float seg_s[kLbWaves][64][NL];
-    __shared__ float seg_d[kLbWaves][64];
-    __shared__ float carry_in[64][NL];
+// Issue the loads of one tile into LDS, spread over waves 1..3 (wave 0 keeps
+// its memory counter free for the look-back). Pieces past the end of the
+// sequence or of the channels are read from an in-bounds location instead;
+// their LDS slots are never used for a stored result.
+template <int N, int DT, bool GATE>
+__device__ __forceinline__ void issue_tile_loads(TileBuf<N, DT> &tb, const LbArgs &a, int64_t b, int64_t ch0,
+                                                 int64_t k, int w, int lane) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr int PPR = G::TCH / G::VEC;            // pieces per tile row
+    constexpr int ACT_PIECES = kChunk * PPR;        // pieces per activation tile (a multiple of 64)
+    constexpr int BC_PIECES = kChunk * N / G::VEC;  // pieces per Bt/Ct tile (a multiple of 64)
+    constexpr int NACT = GATE ? 3 : 2;              // x, delta (, z)
+    const int64_t D = a.D, L = a.L;
+    // activation tiles, in whole waves of 64 pieces
+    for (int base = (w - 1) * 64; base < NACT * ACT_PIECES; base += 3 * 64) {
+        const int arr = base / ACT_PIECES;
+        const int pa = base - arr * ACT_PIECES + lane;
+        const int r = pa / PPR, c = (pa % PPR) * G::VEC;
+        int64_t t = k * kChunk + r;
+        t = t < L ? t : L - 1;
+        int64_t ch = ch0 + c;
+        ch = ch + G::VEC <= D ? ch : D - G::VEC;
+        const T *src = arr == 0 ? (const T *)a.x : arr == 1 ? (const T *)a.delta : (const T *)a.z;
+        T *dst = arr == 0 ? &tb.x[0][0] : arr == 1 ? &tb.dl[0][0] : &tb.z[0][0];
+        load_lds16(src + (b * L + t) * D + ch, dst + (int64_t)(base - arr * ACT_PIECES) * G::VEC);
+    }
+    // A rows of the tile's channels (contiguous), and the skip weights
+    constexpr int A_PIECES = G::TCH * N / 4;        // 16-byte pieces of float
+    for (int base = (w - 1) * 64; base < A_PIECES; base += 3 * 64) {
+        int64_t ch = ch0 + (base + lane) * 4 / N;
+        const int c = (base + lane) * 4 % N;
+        ch = ch < D ? ch : D - 1;
+        load_lds16(a.A + ch * N + c, &tb.A[0][0] + (int64_t)base * 4);
+    }
+    if (a.Dskip && w == 3) {
+        // 4-byte pieces: lane i loads channel ch0 + i (TCH <= 64)
+        int64_t ch = ch0 + lane;
+        ch = ch < D ? ch : D - 1;
+        if (lane < G::TCH)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.Dskip + ch),
+                                             (__attribute__((address_space(3))) void *)&tb.Dsk[0], 4, 0, 0);
+    }
+    // Bt and Ct tiles: the 64 tokens are contiguous rows of N values
+    for (int base = (w - 1) * 64; base < 2 * BC_PIECES; base += 3 * 64) {
+        const int arr = base / BC_PIECES;
+        const int pq = base - arr * BC_PIECES + lane;
+        const int r = pq * G::VEC / N, c = pq * G::VEC % N;
+        int64_t t = k * kChunk + r;
+        t = t < L ? t : L - 1;
+        const T *src = arr == 0 ? (const T *)a.Bt : (const T *)a.Ct;
+        T *dst = arr == 0 ? &tb.B[0][0] : &tb.C[0][0];
+        load_lds16(src + (b * L + t) * N + c, dst + (int64_t)(base - arr * BC_PIECES) * G::VEC);
+    }
+}
+
+template <int N, int DT, bool GATE, bool SKIP>
+__global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TPV = G::TPV, BREGS = G::BREGS;
+    constexpr int TCH = G::TCH, SUBS = G::SUBS;
+
+    __shared__ Shared<N, DT> sh;
 
     const int w = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
     const int row = l >> 4, k16 = l & 15;
-    const int g = row % NGR;                 // state group of this lane
-    const int64_t D = a.D, L = a.L;
-    // Workgroups go to the 8 XCDs round-robin (block id mod 8). Each XCD gets
-    // a contiguous range of columns so that neighbouring channel blocks, which
-    // share cache lines of x, delta, z and y, meet in the same L2; within an
-    // XCD the blocks run chunk-major, so a chunk's predecessor (same column)
-    // has a smaller block id on the same XCD and is dispatched before it.
-    const int64_t bid = blockIdx.x;
-    const int64_t part = bid % kXcds, slot = bid / kXcds;
-    const int64_t cpp = a.ncols_pad / kXcds;  // columns per XCD
-    const int64_t k = slot / cpp;             // chunk
-    const int64_t col = part * cpp + slot % cpp;  // (batch row, channel block)
-    if (col >= a.ncols) return;               // padding column
-    const int64_t b = col / a.nbd;
-    const int64_t d = (col % a.nbd) * CPW + (row / NGR) * 16 + k16;
-    const bool valid = d < D;
-    const int64_t dc = valid ? d : D - 1;
-    const int64_t t0 = k * kChunk + (int64_t)w * kSegT;
+    const int g = row % NGR;           // state group of this lane
     const int nstate0 = g * NL;
+    const int64_t D = a.D, L = a.L;
 
-    float A2[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) A2[j] = a.A[dc * N + nstate0 + j] * kLog2e;
+    // Tiles: (batch row, tile column) x chunk. XCD x owns tile columns
+    // [x*tpx, (x+1)*tpx) and walks them chunk-major.
+    const int64_t ntpb = (D + TCH - 1) / TCH;          // tile columns per batch row
+    const int64_t ntcol = a.batch * ntpb;
+    const int64_t tpx = (ntcol + kXcds - 1) / kXcds;
+    const int64_t nlocal = tpx * a.K;
+    const int xcd = blockIdx.x % kXcds;
+    const int64_t gx = gridDim.x / kXcds;               // workgroups per XCD
+    const int64_t first = blockIdx.x / kXcds;
 
-    const T *xp = (const T *)a.x;
-    const T *dp = (const T *)a.delta;
-    const T *Bp = (const T *)a.Bt;
-    const T *Cp = (const T *)a.Ct;
+    auto tile_of = [&](int64_t s, int64_t &tcol, int64_t &k) {
+        k = s / tpx;
+        tcol = xcd * tpx + s % tpx;
+        return tcol < ntcol;
+    };
 
-    // Inputs of this wave's segment. Tokens past the end act as the identity
-    // map (delta = 0, x = 0) and are never stored.
-    float xv[kSegT], dv[kSegT];
-#pragma unroll
-    for (int t = 0; t < kSegT; ++t) {
-        const int64_t tt = t0 + t;
-        if (tt < L) {
-            const int64_t r = (b * L + tt) * D + dc;
-            xv[t] = ld_act(xp, r);
-            dv[t] = ld_act(dp, r);
-        } else {
-            xv[t] = 0.0f;
-            dv[t] = 0.0f;
-        }
-    }
-    float Bq[BREGS], Cq[BREGS];
-#pragma unroll
-    for (int q = 0; q < BREGS; ++q) {
-        int64_t tt = t0 + q * TPV + k16 / NL;
-        tt = tt < L ? tt : L - 1;
-        const int64_t off = (b * L + tt) * N + nstate0 + (k16 % NL);
-        Bq[q] = ld_act(Bp, off);
-        Cq[q] = ld_act(Cp, off);
+    // Prologue: the first tile.
+    int64_t s = first;
+    {
+        int64_t tcol, k;
+        if (s < nlocal && tile_of(s, tcol, k) && w > 0)
+            issue_tile_loads<N, DT, GATE>(sh.buf[0], a, tcol / ntpb, (tcol % ntpb) * TCH, k, w, l);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
-    // Start reading the predecessor's flag now (after the input loads, so that
-    // waiting for those does not wait for it); it is looked at after phase A.
-    uint32_t early_flag = 0;
-    if (w == 0 && k > 0) early_flag = ld_flag(a.incl_flag + (k - 1) * a.ncols + col);
-
-    // Phase A: discretise once, keep dA and dBx, fold the segment.
-    float dA[kSegT][NL], u[kSegT][NL], S[NL];
-    float dsum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) S[j] = 0.0f;
-    static_for<0, kSegT>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        const float dx = dv[t] * xv[t];
-        dsum += dv[t];
-        static_for<0, NL>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            dA[t][j] = fast_exp2(dv[t] * A2[j]);
-            u[t][j] = row_bcast<(t % TPV) * NL + j>(Bq[t / TPV]) * dx;
-            S[j] = __builtin_fmaf(dA[t][j], S[j], u[t][j]);
-        });
-    });
-#pragma unroll
-    for (int j = 0; j < NL; ++j) seg_s[w][l][j] = S[j];
-    seg_d[w][l] = dsum;
-    __syncthreads();
-
-    if (w == 0) {
-        // Chunk aggregate: fold the segments in order.
-        float Sagg[NL], dagg = seg_d[0][l];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) Sagg[j] = seg_s[0][l][j];
-#pragma unroll
-        for (int v = 1; v < kLbWaves; ++v) {
-            const float dd = seg_d[v][l];
-#pragma unroll
-            for (int j = 0; j < NL; ++j) Sagg[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), Sagg[j], seg_s[v][l][j]);
-            dagg += dd;
+    int it = 0;        // tile counter (LDS buffer parity)
+    for (; s < nlocal; s += gx, ++it) {
+        TileBuf<N, DT> &tb = sh.buf[it & 1];
+        int64_t tcol, k;
+        const bool real = tile_of(s, tcol, k);
+        // Stream in the next tile while this one is scanned.
+        {
+            int64_t tcol2, k2;
+            if (w > 0 && s + gx < nlocal && tile_of(s + gx, tcol2, k2))
+                issue_tile_loads<N, DT, GATE>(sh.buf[(it + 1) & 1], a, tcol2 / ntpb, (tcol2 % ntpb) * TCH, k2, w, l);
         }
-        const int64_t item = k * a.ncols + col;
-        const bool publish = k + 1 < a.K;
-        // Chunk 0 publishes only its inclusive state, right after reading
-        // state_in: the look-back never reads state_in itself, so state_out
-        // (written by the last chunk, which depends on chunk 0) may alias it.
-        if (publish && k > 0) {
+        if (real) {
+            const int64_t b = tcol / ntpb;
+            const int64_t ch0 = (tcol % ntpb) * TCH;
+            const int64_t t0 = k * kChunk + (int64_t)w * kSegT;  // first token of this wave
+#pragma unroll 1
+            for (int sub = 0; sub < SUBS; ++sub) {
+                if (ch0 + sub * CPW >= D) break;                    // no channel of this item exists
+                const int cl = sub * CPW + (row / NGR) * 16 + k16;  // channel within the tile
+                const int64_t d = ch0 + cl;
+                const bool valid = d < D;
+                const int64_t dc = valid ? d : D - 1;
+                const int64_t icol = tcol * SUBS + sub;            // item column
+                const int64_t item = k * a.nicol + icol;
+
+                float A2[NL];
 #pragma unroll
-            for (int j = 0; j < NL; ++j) st_dev(a.agg_s + item * (64 * NL) + l * NL + j, Sagg[j]);
-            st_dev(a.agg_d + item * 64 + l, dagg);
-            publish_flag(a.agg_flag + item, a.epoch, l);
-        }
-        // Carried-in state of the chunk.
-        float H[NL];
-        if (k == 0) {
-            const float *si = a.state_in ? a.state_in + (b * D + dc) * N + nstate0 : nullptr;
+                for (int j = 0; j < NL; ++j) A2[j] = tb.A[cl][nstate0 + j] * kLog2e;
+
+                // Early look-back: the predecessor's inclusive state, if it is
+                // already out; checked after phase A.
+                uint64_t early[NL] = {};
+                if (w == 0 && k > 0) {
+                    const uint64_t *src = a.incl + ((k - 1) * a.nicol + icol) * (64 * NL) + l * NL;
 #pragma unroll
-            for (int j = 0; j < NL; ++j) H[j] = si ? si[j] : 0.0f;
-        } else {
-            // Walk back to the nearest chunk whose inclusive state is out,
-            // waiting at each chunk until at least its aggregate is.
-            int64_t j0 = k - 1;
-            long spin = 0;
-            bool failed = false;
-            bool ready = __builtin_amdgcn_readfirstlane(early_flag) == a.epoch;
-            while (!ready) {
-                const int64_t it = j0 * a.ncols + col;
-                if (__builtin_amdgcn_readfirstlane(ld_flag(a.incl_flag + it)) == a.epoch) break;
-                if (__builtin_amdgcn_readfirstlane(ld_flag(a.agg_flag + it)) == a.epoch) {
-                    --j0;  // chunk 0 has no aggregate: the walk ends at an inclusive state
-                    spin = 0;
-                    continue;
+                    for (int j = 0; j < NL; ++j) early[j] = ld_tagged(src + j);
                 }
-                // give up after kSpinLimit polls, or at once when another wait already failed
-                if (++spin > kSpinLimit || (spin % 64 == 0 && __builtin_amdgcn_readfirstlane(ld_flag(a.error)) != 0)) {
-                    if (l == 0) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    failed = true;
-                    break;
+
+                // Inputs of this wave's segment from the tile. Tokens past the
+                // end act as the identity map (delta = 0, x = 0).
+                float xv[kSegT], dv[kSegT];
+#pragma unroll
+                for (int t = 0; t < kSegT; ++t) {
+                    const int tw = w * kSegT + t;
+                    const bool in = t0 + t < L;
+                    xv[t] = in ? ld_act(&tb.x[tw][0], cl) : 0.0f;
+                    dv[t] = in ? ld_act(&tb.dl[tw][0], cl) : 0.0f;
                 }
-                __builtin_amdgcn_s_sleep(2);
+                float Bq[BREGS], Cq[BREGS];
+#pragma unroll
+                for (int q = 0; q < BREGS; ++q) {
+                    const int tw = w * kSegT + q * TPV + k16 / NL;
+                    Bq[q] = ld_act(&tb.B[tw][0], nstate0 + (k16 % NL));
+                    Cq[q] = ld_act(&tb.C[tw][0], nstate0 + (k16 % NL));
+                }
+
+                // Phase A: discretise once, keep dA and dBx, fold the segment.
+                float dA[kSegT][NL], u[kSegT][NL], S[NL];
+                float dsum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < NL; ++j) S[j] = 0.0f;
+                static_for<0, kSegT>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    const float dx = dv[t] * xv[t];
+                    dsum += dv[t];
+                    static_for<0, NL>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        dA[t][j] = fast_exp2(dv[t] * A2[j]);
+                        u[t][j] = row_bcast<(t % TPV) * NL + j>(Bq[t / TPV]) * dx;
+                        S[j] = __builtin_fmaf(dA[t][j], S[j], u[t][j]);
+                    });
+                });
+#pragma unroll
+                for (int j = 0; j < NL; ++j) sh.seg_s[w][l][j] = S[j];
+                sh.seg_d[w][l] = dsum;
+                __syncthreads();
+
+                // Earlier segments of this item folded from a zero start; read
+                // between the two barriers, so the segment buffers need no copy.
+                float pre_s[NL], pre_d = 0.0f;
+#pragma unroll
+                for (int j = 0; j < NL; ++j) pre_s[j] = 0.0f;
+                for (int v = 0; v < w; ++v) {
+                    const float dd = sh.seg_d[v][l];
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) pre_s[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), pre_s[j], sh.seg_s[v][l][j]);
+                    pre_d += dd;
+                }
+
+                if (w == 0) {
+                    // Item aggregate: fold the segments in order.
+                    float Sagg[NL], dagg = sh.seg_d[0][l];
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) Sagg[j] = sh.seg_s[0][l][j];
+#pragma unroll
+                    for (int v = 1; v < kWaves; ++v) {
+                        const float dd = sh.seg_d[v][l];
+#pragma unroll
+                        for (int j = 0; j < NL; ++j)
+                            Sagg[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), Sagg[j], sh.seg_s[v][l][j]);
+                        dagg += dd;
+                    }
+                    const bool publish = k + 1 < a.K;
+                    float H[NL];
+                    if (k == 0) {
+                        const float *si = a.state_in ? a.state_in + (b * D + dc) * N + nstate0 : nullptr;
+#pragma unroll
+                        for (int j = 0; j < NL; ++j) H[j] = si ? si[j] : 0.0f;
+                    } else {
+                        bool ok = true;
+#pragma unroll
+                        for (int j = 0; j < NL; ++j) ok = ok && (uint32_t)(early[j] >> 32) == a.epoch;
+                        if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+#pragma unroll
+                            for (int j = 0; j < NL; ++j) H[j] = __uint_as_float((uint32_t)early[j]);
+                        } else {
+                            // Slow path: let later items skip this one, then
+                            // scan back to the nearest inclusive state.
+                            if (publish) {
+#pragma unroll
+                                for (int j = 0; j < NL; ++j) st_dev(a.agg_s + item * (64 * NL) + l * NL + j, Sagg[j]);
+                                st_dev(a.agg_d + item * 64 + l, dagg);
+                                publish_flag(a.agg_flag + item, a.epoch, l);
+                            }
+                            int64_t base = k - 1;  // chunk examined by lane 0
+                            int64_t j0 = -1;
+                            long spin = 0;
+                            while (true) {
+                                const int64_t jj = base - l;  // chunk examined by this lane
+                                bool inc = false, agg = false;
+                                if (jj >= 0) {
+                                    // the first word of an item's inclusive state stands for all of it;
+                                    // the replay below still checks every word it reads
+                                    inc = (uint32_t)(ld_tagged(a.incl + (jj * a.nicol + icol) * (64 * NL)) >> 32) == a.epoch;
+                                    agg = inc || ld_flag(a.agg_flag + jj * a.nicol + icol) == a.epoch;
+                                }
+                                const uint64_t m_inc = __builtin_amdgcn_ballot_w64(inc);
+                                const uint64_t m_agg = __builtin_amdgcn_ballot_w64(agg);
+                                if (m_inc) {
+                                    const int i0 = __builtin_ctzll(m_inc);
+                                    const uint64_t below = i0 == 0 ? 0 : (~0ull >> (64 - i0));
+                                    if ((m_agg & below) == below) {
+                                        j0 = base - i0;
+                                        break;
+                                    }
+                                } else if (m_agg == ~0ull) {
+                                    base -= 64;  // 64 aggregates and no inclusive state yet: look further back
+                                    spin = 0;
+                                    continue;
+                                }
+                                if (++spin > kSpinLimit ||
+                                    (spin % 64 == 0 && __builtin_amdgcn_readfirstlane(ld_flag(a.error)) != 0)) {
+                                    if (l == 0) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                    break;
+                                }
+                                __builtin_amdgcn_s_sleep(2);
+                            }
+                            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                            if (j0 < 0) {
+#pragma unroll
+                                for (int j = 0; j < NL; ++j) H[j] = 0.0f;
+                            } else {
+                                // Replay the chain forward from that state with the
+                                // arithmetic each item uses for its own inclusive state.
+                                const uint64_t *src = a.incl + (j0 * a.nicol + icol) * (64 * NL) + l * NL;
+#pragma unroll
+                                for (int j = 0; j < NL; ++j) {
+                                    uint64_t v = ld_tagged(src + j);
+                                    for (long sp = 0; (uint32_t)(v >> 32) != a.epoch && sp < kSpinLimit; ++sp)
+                                        v = ld_tagged(src + j);
+                                    H[j] = __uint_as_float((uint32_t)v);
+                                }
+                                for (int64_t jj = j0 + 1; jj < k; ++jj) {
+                                    const int64_t it2 = jj * a.nicol + icol;
+                                    const float dd = ld_dev(a.agg_d + it2 * 64 + l);
+#pragma unroll
+                                    for (int j = 0; j < NL; ++j)
+                                        H[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), H[j],
+                                                              ld_dev(a.agg_s + it2 * (64 * NL) + l * NL + j));
+                                }
+                            }
+                        }
+                    }
+                    if (publish) {
+                        uint64_t *dst = a.incl + item * (64 * NL) + l * NL;
+#pragma unroll
+                        for (int j = 0; j < NL; ++j)
+                            st_tagged(dst + j, __builtin_fmaf(fast_exp2(A2[j] * dagg), H[j], Sagg[j]), a.epoch);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) sh.carry[l][j] = H[j];
+                }
+                __syncthreads();
+
+                // This wave's carried-in state: the item's, pushed through the
+                // earlier segments (folded above, before the barrier).
+                float h[NL];
+#pragma unroll
+                for (int j = 0; j < NL; ++j) h[j] = __builtin_fmaf(fast_exp2(A2[j] * pre_d), sh.carry[l][j], pre_s[j]);
+
+                // Phase C: rescan from registers; partial readout over this lane's states.
+                float yp[kSegT];
+                static_for<0, kSegT>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    yp[t] = 0.0f;
+                    static_for<0, NL>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        h[j] = __builtin_fmaf(dA[t][j], h[j], u[t][j]);
+                        fmac_bcast<(t % TPV) * NL + j>(yp[t], Cq[t / TPV], h[j]);
+                    });
+                });
+
+                if (k == a.K - 1 && w == kWaves - 1 && a.state_out && valid) {
+                    float *so = a.state_out + (b * D + d) * N + nstate0;
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) so[j] = h[j];
+                }
+
+                // Sum the partial readouts over a channel's rows. Afterwards
+                // row r holds the finished token t = NGR*q + (r % NGR) of group q.
+                float yo[G::OWN];
+                if constexpr (NGR == 4) {
+#pragma unroll
+                    for (int q = 0; q < kSegT / 4; ++q) {
+                        float a0 = yp[4 * q + 0], a2 = yp[4 * q + 2], a1 = yp[4 * q + 1], a3 = yp[4 * q + 3];
+                        swap_halves(a0, a2);  // rows 0,1: token 0 | rows 2,3: token 2
+                        swap_halves(a1, a3);  // rows 0,1: token 1 | rows 2,3: token 3
+                        float s02 = a0 + a2, s13 = a1 + a3;
+                        swap_odd_even_rows(s02, s13);
+                        yo[q] = s02 + s13;
+                    }
+                } else if constexpr (NGR == 2) {
+#pragma unroll
+                    for (int q = 0; q < kSegT / 2; ++q) {
+                        float a0 = yp[2 * q + 0], a1 = yp[2 * q + 1];
+                        swap_odd_even_rows(a0, a1);
+                        yo[q] = a0 + a1;
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < kSegT; ++q) yo[q] = yp[q];
+                }
+
+                // Finish the owned tokens (D skip, silu gate) into the tile.
+                const float dskip = SKIP ? tb.Dsk[cl] : 0.0f;
+#pragma unroll
+                for (int q = 0; q < G::OWN; ++q) {
+                    const int t = NGR * q + g;
+                    const int tw = w * kSegT + t;
+                    const float xt = ld_act(&tb.x[tw][0], cl);
+                    float yv = yo[q];
+                    if (SKIP) yv = __builtin_fmaf(dskip, xt, yv);
+                    if (GATE) yv *= silu(ld_act(&tb.z[tw][0], cl));
+                    st_act(&tb.dl[tw][0], cl, yv);
+                }
             }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (failed) {
-#pragma unroll
-                for (int j = 0; j < NL; ++j) H[j] = 0.0f;
-            } else {
-                // Replay the chain forward from that state, chunk by chunk, with
-                // the same operations every chunk uses for its own inclusive
-                // state, so the carry does not depend on where the walk stopped.
-                const int64_t it0 = j0 * a.ncols + col;
-#pragma unroll
-                for (int j = 0; j < NL; ++j) H[j] = ld_dev(a.incl + it0 * (64 * NL) + l * NL + j);
-                for (int64_t jj = j0 + 1; jj < k; ++jj) {
-                    const int64_t it = jj * a.ncols + col;
-                    const float dd = ld_dev(a.agg_d + it * 64 + l);
-#pragma unroll
-                    for (int j = 0; j < NL; ++j)
-                        H[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), H[j], ld_dev(a.agg_s + it * (64 * NL) + l * NL + j));
+        }
+        __syncthreads();
+        // Store the finished y tile as whole lines (waves 1..3), then make sure
+        // the next tile has landed before anyone reads it.
+        if (real && w > 0) {
+            using VT = uint32_t __attribute__((ext_vector_type(4)));
+            constexpr int PPR = TCH / G::VEC;
+            const int64_t b = tcol / ntpb, ch0 = (tcol % ntpb) * TCH;
+            T *yptr = (T *)a.y;
+            for (int p = (w - 1) * 64 + l; p < kChunk * PPR; p += 3 * 64) {
+                const int r = p / PPR, c = (p % PPR) * G::VEC;
+                const int64_t t = k * kChunk + r;
+                if (t < L && ch0 + c < D) {
+                    const VT v = *(const VT *)&tb.dl[r][c];
+                    *(VT *)(yptr + (b * L + t) * D + ch0 + c) = v;
                 }
             }
         }
-        if (publish) {
-#pragma unroll
-            for (int j = 0; j < NL; ++j)
-                st_dev(a.incl + item * (64 * NL) + l * NL + j, __builtin_fmaf(fast_exp2(A2[j] * dagg), H[j], Sagg[j]));
-            publish_flag(a.incl_flag + item, a.epoch, l);
-        }
-#pragma unroll
-        for (int j = 0; j < NL; ++j) carry_in[l][j] = H[j];
-    }
-    __syncthreads();
-
-    // This wave's carried-in state: the chunk's, pushed through earlier segments.
-    float h[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) h[j] = carry_in[l][j];
-    for (int v = 0; v < w; ++v) {
-        const float dd = seg_d[v][l];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) h[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), h[j], seg_s[v][l][j]);
-    }
-
-    // Phase C: rescan from registers; partial readout over this lane's states.
-    float yp[kSegT];
-    static_for<0, kSegT>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        yp[t] = 0.0f;
-        static_for<0, NL>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            h[j] = __builtin_fmaf(dA[t][j], h[j], u[t][j]);
-            fmac_bcast<(t % TPV) * NL + j>(yp[t], Cq[t / TPV], h[j]);
-        });
-    });
-
-    if (k == a.K - 1 && w == kLbWaves - 1 && a.state_out && valid) {
-        float *so = a.state_out + (b * D + d) * N + nstate0;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) so[j] = h[j];
-    }
-
-    // Sum the partial readouts over a channel's rows. Afterwards row r holds
-    // the finished token t = NGR*q + (r % NGR) of group q.
-    float yo[G::OWN];
-    if constexpr (NGR == 4) {
-#pragma unroll
-        for (int q = 0; q < kSegT / 4; ++q) {
-            float a0 = yp[4 * q + 0], a2 = yp[4 * q + 2], a1 = yp[4 * q + 1], a3 = yp[4 * q + 3];
-            swap_halves(a0, a2);   // rows 0,1: token 0 | rows 2,3: token 2
-            swap_halves(a1, a3);   // rows 0,1: token 1 | rows 2,3: token 3
-            float s02 = a0 + a2, s13 = a1 + a3;
-            swap_odd_even_rows(s02, s13);
-            yo[q] = s02 + s13;
-        }
-    } else if constexpr (NGR == 2) {
-#pragma unroll
-        for (int q = 0; q < kSegT / 2; ++q) {
-            float a0 = yp[2 * q + 0], a1 = yp[2 * q + 1];
-            swap_odd_even_rows(a0, a1);
-            yo[q] = a0 + a1;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < kSegT; ++q) yo[q] = yp[q];
-    }
-
-    // Finish the owned tokens: D skip, silu gate, store.
-    const float dskip = SKIP ? a.Dskip[dc] : 0.0f;
-    T *yptr = (T *)a.y;
-    const T *zp = (const T *)a.z;
-#pragma unroll
-    for (int q = 0; q < G::OWN; ++q) {
-        const int t = NGR * q + g;
-        const int64_t tt = t0 + t;
-        // x of token t; t depends on the row, so select by value
-        float xt = xv[NGR * q];
-#pragma unroll
-        for (int c = 1; c < NGR; ++c) xt = (g == c) ? xv[NGR * q + c] : xt;
-        float yv = yo[q];
-        if (SKIP) yv = __builtin_fmaf(dskip, xt, yv);
-        if (tt < L && valid) {
-            const int64_t r = (b * L + tt) * D + d;
-            if (GATE) yv *= silu(ld_act(zp, r));
-            st_act(yptr, r, yv);
-        }
+        if (w > 0) __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 }
 
 template <int N, int DT, bool GATE, bool SKIP>
 hipError_t launch_lb_typed(const LbArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((scan_lb_kernel<N, DT, GATE, SKIP>), dim3((unsigned)(a.ncols_pad * a.K)), dim3(64 * kLbWaves),
-                       0, s, a);
-    return hipGetLastError();
+    auto kern = scan_lb_kernel<N, DT, GATE, SKIP>;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cus = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kWaves, 0)) != hipSuccess) return e;
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    using G = Geo<N, DT>;
+    const int64_t ntcol = a.batch * ((a.D + G::TCH - 1) / G::TCH);
+    const int64_t tpx = (ntcol + kXcds - 1) / kXcds;
+    const int64_t need = tpx * a.K * kXcds;  // one workgroup per tile is the most that helps
+    int64_t grid = (int64_t)cus * per_cu / kXcds * kXcds;
+    if (grid > need) grid = need;
+    if (grid < kXcds) grid = kXcds;
+    LbArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchCooperativeKernel((const void *)kern, dim3((unsigned)grid), dim3(64 * kWaves), params, 0, s);
 }
 
 template <int N, int DT>
@@ -397,41 +584,42 @@ hipError_t launch_lb_dtype(const LbArgs &a, int dtype, hipStream_t s) {
     return dtype == 0 ? launch_lb_flags<N, 0>(a, s) : launch_lb_flags<N, 1>(a, s);
 }
 
-template <int N>
+template <int N, int DT>
 void lb_geometry(int64_t batch, int64_t L, int64_t D, LbPlan *p) {
-    using G = Geo<N>;
-    p->cpw = G::CPW;
+    using G = Geo<N, DT>;
     p->nl = G::NL;
-    p->nbd = (D + G::CPW - 1) / G::CPW;
-    p->ncols = batch * p->nbd;
-    p->ncols_pad = (p->ncols + kXcds - 1) / kXcds * kXcds;
+    p->nicol = batch * ((D + G::TCH - 1) / G::TCH) * G::SUBS;
     p->K = (L + kChunk - 1) / kChunk;
+    p->vec = G::VEC;
 }
 
 }  // namespace
 
-bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, LbPlan *p) {
+bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, LbPlan *p) {
+    const bool bf = dtype == 1;
     switch (N) {
-        case 1: lb_geometry<1>(batch, L, D, p); break;
-        case 2: lb_geometry<2>(batch, L, D, p); break;
-        case 4: lb_geometry<4>(batch, L, D, p); break;
-        case 8: lb_geometry<8>(batch, L, D, p); break;
-        case 16: lb_geometry<16>(batch, L, D, p); break;
+        case 1: bf ? lb_geometry<1, 1>(batch, L, D, p) : lb_geometry<1, 0>(batch, L, D, p); break;
+        case 2: bf ? lb_geometry<2, 1>(batch, L, D, p) : lb_geometry<2, 0>(batch, L, D, p); break;
+        case 4: bf ? lb_geometry<4, 1>(batch, L, D, p) : lb_geometry<4, 0>(batch, L, D, p); break;
+        case 8: bf ? lb_geometry<8, 1>(batch, L, D, p) : lb_geometry<8, 0>(batch, L, D, p); break;
+        case 16: bf ? lb_geometry<16, 1>(batch, L, D, p) : lb_geometry<16, 0>(batch, L, D, p); break;
         default: return false;
     }
     p->chunk = kChunk;
-    const int64_t items = p->ncols * p->K;
-    // header | agg_s | agg_d | incl | agg_flag | incl_flag
+    // Tiles are read as 16-byte pieces: channel rows must be whole pieces and
+    // Bt/Ct rows at least one piece.
+    const int esz = bf ? 2 : 4;
+    p->supported = (D % p->vec == 0) && (N * esz >= 16);
+    const int64_t items = p->nicol * p->K;
+    // header | incl (tagged) | agg_s | agg_d | agg_flag
     size_t off = 256;
+    p->off_incl = off;
+    off += (size_t)items * 64 * p->nl * sizeof(uint64_t);
     p->off_agg_s = off;
     off += (size_t)items * 64 * p->nl * sizeof(float);
     p->off_agg_d = off;
     off += (size_t)items * 64 * sizeof(float);
-    p->off_incl = off;
-    off += (size_t)items * 64 * p->nl * sizeof(float);
     p->off_agg_flag = off;
-    off += (size_t)items * sizeof(uint32_t);
-    p->off_incl_flag = off;
     off += (size_t)items * sizeof(uint32_t);
     p->bytes = (off + 255) / 256 * 256;
     return true;
