@@ -95,6 +95,7 @@ struct Shared {
     float seg_s[kWaves][64][G::NL];  // segment end states (read only between the two item barriers)
     float seg_d[kWaves][64];         // segment summed deltas
     float carry[64][G::NL];          // the item's carried-in state
+    uint64_t early[G::NL >= 2 ? G::NL / 2 : 1][64][2];  // predecessor's inclusive state, fetched early
 };
 
 template <int SRC>
@@ -164,11 +165,41 @@ __device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t epoch, int
     if (lane == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// LDS address of a __shared__ location, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
 // One 16-byte piece per lane from global memory straight into LDS at
-// lds + lane*16 (lds is the same for the whole wave).
-__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+// lds + lane*16 (global_load_lds_dwordx4; lds is wave-uniform). Written as
+// inline assembly so that the compiler does not count these loads: it would
+// otherwise wait for all of them before LDS reads and barriers that have
+// nothing to do with them, which serialises the prefetch of the next tile
+// with the scan of the current one. No registers receive data; the caller
+// waits with vm_wait() before the data is read.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// The same for 4-byte pieces (lds + lane*4).
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// 16-byte pieces of data other workgroups write (bypasses the CU's cache).
+__device__ __forceinline__ void dma16_coherent(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(g), "s"(lds) : "memory");
+}
+// Wait until this wave's vector memory accesses (including the loads above)
+// have completed.
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() would also
+// wait for every global access the wave has in flight, which includes the
+// next tile's loads into LDS; those are meant to stay in flight across the
+// barriers of the current tile.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Issue the loads of one tile into LDS, spread over waves 1..3 (wave 0 keeps
@@ -196,7 +227,7 @@ __device__ __forceinline__ void issue_tile_loads(TileBuf<N, DT> &tb, const LbArg
         ch = ch + G::VEC <= D ? ch : D - G::VEC;
         const T *src = arr == 0 ? (const T *)a.x : arr == 1 ? (const T *)a.delta : (const T *)a.z;
         T *dst = arr == 0 ? &tb.x[0][0] : arr == 1 ? &tb.dl[0][0] : &tb.z[0][0];
-        load_lds16(src + (b * L + t) * D + ch, dst + (int64_t)(base - arr * ACT_PIECES) * G::VEC);
+        dma16(src + (b * L + t) * D + ch, lds_addr(dst + (int64_t)(base - arr * ACT_PIECES) * G::VEC));
     }
     // A rows of the tile's channels (contiguous), and the skip weights
     constexpr int A_PIECES = G::TCH * N / 4;        // 16-byte pieces of float
@@ -204,15 +235,13 @@ __device__ __forceinline__ void issue_tile_loads(TileBuf<N, DT> &tb, const LbArg
         int64_t ch = ch0 + (base + lane) * 4 / N;
         const int c = (base + lane) * 4 % N;
         ch = ch < D ? ch : D - 1;
-        load_lds16(a.A + ch * N + c, &tb.A[0][0] + (int64_t)base * 4);
+        dma16(a.A + ch * N + c, lds_addr(&tb.A[0][0] + (int64_t)base * 4));
     }
     if (a.Dskip && w == 3) {
         // 4-byte pieces: lane i loads channel ch0 + i (TCH <= 64)
         int64_t ch = ch0 + lane;
         ch = ch < D ? ch : D - 1;
-        if (lane < G::TCH)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.Dskip + ch),
-                                             (__attribute__((address_space(3))) void *)&tb.Dsk[0], 4, 0, 0);
+        if (lane < G::TCH) dma4(a.Dskip + ch, lds_addr(&tb.Dsk[0]));
     }
     // Bt and Ct tiles: the 64 tokens are contiguous rows of N values
     for (int base = (w - 1) * 64; base < 2 * BC_PIECES; base += 3 * 64) {
@@ -223,7 +252,7 @@ __device__ __forceinline__ void issue_tile_loads(TileBuf<N, DT> &tb, const LbArg
         t = t < L ? t : L - 1;
         const T *src = arr == 0 ? (const T *)a.Bt : (const T *)a.Ct;
         T *dst = arr == 0 ? &tb.B[0][0] : &tb.C[0][0];
-        load_lds16(src + (b * L + t) * N + c, dst + (int64_t)(base - arr * BC_PIECES) * G::VEC);
+        dma16(src + (b * L + t) * N + c, lds_addr(dst + (int64_t)(base - arr * BC_PIECES) * G::VEC));
     }
 }
 
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 
     __shared__ Shared<N, DT> sh;
 
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
     const int l = threadIdx.x & 63;
     const int row = l >> 4, k16 = l & 15;
     const int g = row % NGR;           // state group of this lane
@@ -265,8 +294,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
         int64_t tcol, k;
         if (s < nlocal && tile_of(s, tcol, k) && w > 0)
             issue_tile_loads<N, DT, GATE>(sh.buf[0], a, tcol / ntpb, (tcol % ntpb) * TCH, k, w, l);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        vm_wait();
+        lds_barrier();
     }
 
     int it = 0;        // tile counter (LDS buffer parity)
@@ -283,7 +312,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
         if (real) {
             const int64_t b = tcol / ntpb;
             const int64_t ch0 = (tcol % ntpb) * TCH;
-            const int64_t t0 = k * kChunk + (int64_t)w * kSegT;  // first token of this wave
+            const int64_t tail = L - k * kChunk;  // tokens of this chunk that exist
+            if (tail < kChunk) {
+                // Tokens past the end were loaded from the last token; give them
+                // delta = 0 so that they leave the state unchanged.
+                for (int i = threadIdx.x; i < (kChunk - (int)tail) * TCH; i += 64 * kWaves)
+                    tb.dl[tail + i / TCH][i % TCH] = T(0.0f);
+                lds_barrier();
+            }
 #pragma unroll 1
             for (int sub = 0; sub < SUBS; ++sub) {
                 if (ch0 + sub * CPW >= D) break;                    // no channel of this item exists
@@ -298,24 +334,29 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 #pragma unroll
                 for (int j = 0; j < NL; ++j) A2[j] = tb.A[cl][nstate0 + j] * kLog2e;
 
-                // Early look-back: the predecessor's inclusive state, if it is
-                // already out; checked after phase A.
-                uint64_t early[NL] = {};
+                // Early look-back: fetch the predecessor's inclusive state (if it
+                // is already out) into LDS; it is checked after phase A. Going
+                // through LDS keeps these loads out of the registers and waits
+                // of the other waves.
+                uint64_t early1 = 0;  // N = 1: one 8-byte word, loaded directly
                 if (w == 0 && k > 0) {
                     const uint64_t *src = a.incl + ((k - 1) * a.nicol + icol) * (64 * NL) + l * NL;
+                    if constexpr (NL >= 2) {
 #pragma unroll
-                    for (int j = 0; j < NL; ++j) early[j] = ld_tagged(src + j);
+                        for (int p = 0; p < NL / 2; ++p) dma16_coherent(src + 2 * p, lds_addr(&sh.early[p][0][0]));
+                    } else {
+                        early1 = ld_tagged(src);
+                    }
                 }
 
-                // Inputs of this wave's segment from the tile. Tokens past the
-                // end act as the identity map (delta = 0, x = 0).
+                // Inputs of this wave's segment from the tile (tokens past the
+                // end have delta = 0 there: the identity map).
                 float xv[kSegT], dv[kSegT];
 #pragma unroll
                 for (int t = 0; t < kSegT; ++t) {
                     const int tw = w * kSegT + t;
-                    const bool in = t0 + t < L;
-                    xv[t] = in ? ld_act(&tb.x[tw][0], cl) : 0.0f;
-                    dv[t] = in ? ld_act(&tb.dl[tw][0], cl) : 0.0f;
+                    xv[t] = ld_act(&tb.x[tw][0], cl);
+                    dv[t] = ld_act(&tb.dl[tw][0], cl);
                 }
                 float Bq[BREGS], Cq[BREGS];
 #pragma unroll
@@ -344,7 +385,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 #pragma unroll
                 for (int j = 0; j < NL; ++j) sh.seg_s[w][l][j] = S[j];
                 sh.seg_d[w][l] = dsum;
-                __syncthreads();
+                lds_barrier();
 
                 // Earlier segments of this item folded from a zero start; read
                 // between the two barriers, so the segment buffers need no copy.
@@ -378,6 +419,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 #pragma unroll
                         for (int j = 0; j < NL; ++j) H[j] = si ? si[j] : 0.0f;
                     } else {
+                        uint64_t early[NL];
+                        if constexpr (NL >= 2) {
+                            vm_wait();
+#pragma unroll
+                            for (int j = 0; j < NL; ++j) early[j] = sh.early[j / 2][l][j % 2];
+                        } else {
+                            early[0] = early1;
+                        }
                         bool ok = true;
 #pragma unroll
                         for (int j = 0; j < NL; ++j) ok = ok && (uint32_t)(early[j] >> 32) == a.epoch;
@@ -461,7 +510,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 #pragma unroll
                     for (int j = 0; j < NL; ++j) sh.carry[l][j] = H[j];
                 }
-                __syncthreads();
+                lds_barrier();
 
                 // This wave's carried-in state: the item's, pushed through the
                 // earlier segments (folded above, before the barrier).
@@ -526,7 +575,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // Store the finished y tile as whole lines (waves 1..3), then make sure
         // the next tile has landed before anyone reads it.
         if (real && w > 0) {
@@ -543,8 +592,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                 }
             }
         }
-        if (w > 0) __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if (w > 0) vm_wait();
+        lds_barrier();
     }
 }
 
