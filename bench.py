@@ -9,8 +9,14 @@ several input/output sets rotate so that the 256 MB Infinity Cache cannot
 hold a whole step's working set.
 
 Prints one JSON line: throughput in G(B*L*D*N)-elements/s, the roofline of
-the dominant kernel (algorithmic bytes / measured time vs 8 TB/s), and the
-fp64 oracle timed on the host cores on a bounded sample of the same workload.
+the kernel (its algorithmic work per launch over its average launch time,
+timed with events around every launch, against the MI355X peak of the unit
+that bounds it), the same launch against the HBM peak, and the fp64 oracle
+timed on the host cores on a bounded sample of the same workload.
+
+`--copy-calibration BYTES` instead runs a plain device-to-device copy of
+BYTES bytes a few times; under `rocprofv3 --pmc FETCH_SIZE` (or WRITE_SIZE) it
+gives the factor that turns those counters into HBM bytes.
 """
 from __future__ import annotations
 
@@ -25,6 +31,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+# VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one
+# fp32 instruction per lane per slot; packed fp32 is not used).
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Issue slots the recurrence needs per (b, t, d, n) element at the least:
+# delta*A (mul), exp (a transcendental, issued at half rate: 2 slots),
+# B*(delta*x) (mul), dA*h + dBx (fma), C*h accumulated (fma).
+SCAN_SLOTS_PER_ELEM = 6
+SCAN_KERNEL = "scan_lb_kernel"
+STEP_KERNEL = "step_kernel"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -70,6 +85,38 @@ def rel_l2(got, ref):
     return float(np.sqrt((d * d).sum()) / max(np.sqrt((ref * ref).sum()), 1e-300)), float(np.abs(d).max())
 
 
+def timed(steps, step, stream):
+    """Run `steps` steps back to back on `stream`. Returns (ms per step over the
+    whole region, mean ms of one launch), both from events on that stream: one
+    pair around the region and one pair around every launch (each step is a
+    single kernel launch)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of nbytes, five times: the reference for the HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE) of a profiled run."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "launches": 5}), flush=True)
+
+
 def bench_scan(args, name):
     import numpy as np
     import torch
@@ -108,18 +155,11 @@ def bench_scan(args, name):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} steps, {ms * 1e3:.2f} us/step over {len(sets)} rotating sets")
-
-    out = {"cfg": cfg, "ms": ms, "elems": cfg.elems, "bytes": W.scan_bytes(cfg, st_out is not None),
-           "dtype": cfg.dtype, "parity": None, "cpu": None}
+    ms, launch_ms = timed(args.steps, step, stream)
+    log(f"[bench] {args.steps} steps, {ms * 1e3:.2f} us/step ({launch_ms * 1e3:.2f} us/launch) "
+        f"over {len(sets)} rotating sets")
+    out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems,
+           "bytes": W.scan_bytes(cfg, st_out is not None), "dtype": cfg.dtype, "parity": None, "cpu": None}
     # parity of the timed configuration on set 0, and the CPU baseline
     if inp is not None and not args.no_cpu:
         import oracle
@@ -165,16 +205,10 @@ def bench_step(args):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for s in range(args.warmup, nsteps):
-        step(s)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} decode steps, {ms * 1e3:.2f} us/step")
-    out = {"cfg": cfg, "ms": ms, "elems": cfg.elems_per_step, "bytes": W.step_bytes(cfg), "dtype": cfg.dtype,
-           "parity": None, "cpu": None}
+    ms, launch_ms = timed(args.steps, lambda i: step(args.warmup + i), stream)
+    log(f"[bench] {args.steps} decode steps, {ms * 1e3:.2f} us/step ({launch_ms * 1e3:.2f} us/launch)")
+    out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems_per_step, "bytes": W.step_bytes(cfg),
+           "dtype": cfg.dtype, "parity": None, "cpu": None}
     if not args.no_cpu:
         import oracle
         o = oracle.get()
@@ -202,6 +236,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -214,12 +250,27 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     r = bench_step(args) if args.workload == "c4" else bench_scan(args, args.workload)
     cfg = r["cfg"]
-    ms = r["ms"]
-    gbs = r["bytes"] / (ms * 1e-3) / 1e9
+    ms, launch_ms = r["ms"], r["launch_ms"]
+    gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
+    hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+           "traffic": traffic, "kernel": STEP_KERNEL if args.workload == "c4" else SCAN_KERNEL,
+           "algorithmic_bytes_per_launch": r["bytes"], "launch_us": launch_ms * 1e3}
+    if args.workload == "c4":
+        roof = hbm
+    else:
+        # the scan needs more time at the VALU peak than at the HBM peak
+        slots = r["elems"] * SCAN_SLOTS_PER_ELEM
+        tslots = slots / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": tslots, "peak": VALU_PEAK_TSLOTS, "unit": "T VALU-slots/s",
+                "frac": tslots / VALU_PEAK_TSLOTS, "traffic": traffic, "kernel": SCAN_KERNEL,
+                "algorithmic_slots_per_launch": slots, "launch_us": launch_ms * 1e3}
     if args.workload == "c4":
         config = {"workload": cfg.name, "batch": cfg.batch, "D": cfg.D, "N": cfg.N, "dtype": cfg.dtype,
                   "gate": cfg.gate, "steps_timed": args.steps}
@@ -243,9 +294,8 @@ def main():
         "data": "synthetic (seeded; recipe in workloads/)",
         "config": config,
         "hbm_gbs_algorithmic": gbs,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "ssm_scan_fwd (all launches of one call)" if args.workload != "c4" else "ssm_step"},
+        "roofline": roof,
+        "roofline_hbm": hbm,
         "cpu_baseline": r["cpu"],
         "parity": r["parity"],
     }

@@ -15,9 +15,13 @@ ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["ssm_scan.hip", "ssm_scan_lb.hip", "ssm_step.hip", "ssm_abi.cpp"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.
+# The atomic optimizer is off: it rewrites a one-lane atomic with a returned
+# value into a wave-wide pattern that waits for the result right away, and the
+# scan's tile counter is read only at the end of a tile.
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-ffp-contract=fast", "-Wall", "-Wno-unused-result",
 ]
 

@@ -32,8 +32,9 @@ int64_t checked_mul3(int64_t a, int64_t b, int64_t c) {
 
 size_t round_up256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Both scans keep a 256-byte header at the start of the workspace (the first
-// word reports a timed-out look-back wait).
+// Both scans keep a 256-byte header at the start of the workspace: the first
+// word reports a timed-out look-back wait; bytes 64..127 hold the single-pass
+// scan's eight tile counters.
 constexpr size_t kHeader = 256;
 
 // Workspace of the chunked three-launch scan:
@@ -45,10 +46,10 @@ size_t twopass_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t
            round_up256((size_t)batch * *K * D * sizeof(float));
 }
 
-// Workspace of the single-pass look-back scan (0 when the sequence is one chunk).
+// Workspace of the single-pass look-back scan.
 size_t lb_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, ssm::LbPlan *p) {
     if (!ssm::lb_plan(batch, L, D, N, dtype, p)) return 0;
-    return p->K > 1 ? p->bytes : 0;
+    return p->bytes;
 }
 
 // The single-pass scan reads 16-byte pieces of channel rows; shapes whose
@@ -180,10 +181,9 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     if (lbw > 0) {
         char *w = (char *)workspace;
         a.error = (uint32_t *)w;
+        a.tiles = (uint64_t *)(w + 64);
         a.incl = (uint64_t *)(w + p.off_incl);
-        a.agg_s = (float *)(w + p.off_agg_s);
-        a.agg_d = (float *)(w + p.off_agg_d);
-        a.agg_flag = (uint32_t *)(w + p.off_agg_flag);
+        a.agg = (uint64_t *)(w + p.off_agg);
     }
     return ssm::launch_scan_lb(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

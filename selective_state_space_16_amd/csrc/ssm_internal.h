@@ -30,17 +30,19 @@ struct LbArgs {
     int64_t K;          // chunks per sequence
     int64_t nicol;      // item columns (batch rows x channel blocks)
     uint32_t epoch;     // value that marks this call's published words
+    int agg_early;      // every item publishes its aggregate right after phase A
     uint32_t *error;    // set when a look-back wait timed out
+    uint64_t *tiles;    // 8 tile counters (one per XCD list), (epoch << 32 | next tile) words
     uint64_t *incl;     // per item: inclusive end state, epoch-tagged words
-    float *agg_s, *agg_d;
-    uint32_t *agg_flag;
+    uint64_t *agg;      // per item: end state from a zero start and summed delta, epoch-tagged words
 };
 
 // Geometry and workspace layout of the look-back scan for one problem size.
 struct LbPlan {
     int64_t nl, nicol, K, chunk, vec;
+    int64_t tiles_per_list;  // tiles each of the 8 per-XCD lists hands out
     bool supported;     // shape meets the tile-load requirements
-    size_t off_incl, off_agg_s, off_agg_d, off_agg_flag, bytes;
+    size_t off_incl, off_agg, bytes;
 };
 
 struct StepArgs {

@@ -9,11 +9,12 @@
 //
 // Work items. An item is one chunk of 64 tokens of one block of CPW channels
 // (CPW = 16 for N = 16). A workgroup of 4 waves scans an item: wave w owns
-// tokens 16w..16w+15. Phase A computes dA = exp2(delta * A*log2(e)) and
-// dBx = delta*x*B once per (token, state) and keeps them in registers while
-// folding them into the wave's segment pair; the four segment pairs are
-// combined through LDS. Phase C rescans the wave's tokens from its carried-in
-// state using those registers (no second exponential) and reads out y.
+// tokens 16w..16w+15. Phase A computes dA = exp2(delta * A*log2(e)) once per
+// (token, state) and keeps it in registers, with delta*x per token, while
+// folding dA and dBx = B*(delta*x) into the wave's segment pair; the four
+// segment pairs are combined through LDS. Phase C rescans the wave's tokens
+// from its carried-in state using those registers (no second exponential;
+// dBx is one multiply again) and reads out y.
 //
 // Between items of the same channel block the carried-in state comes from a
 // decoupled look-back: every item publishes its inclusive end state as
@@ -33,9 +34,12 @@
 // registers involved), double-buffered so that the next tile streams in while
 // the TCH/CPW items of the current tile are scanned. y is written into the
 // tile's delta area (delta is dead after phase A) and stored as whole lines.
-// Workgroups are persistent (one per slot, launched cooperatively so that all
-// are resident) and each XCD works through a contiguous range of channel
-// blocks chunk-major, so that tiles sharing lines meet in one L2.
+// Workgroups are persistent (as many as fit at once) and take tiles from one
+// counter per XCD (the workgroup's blockIdx modulo 8): each XCD works through
+// a contiguous range of channel blocks chunk-major, so that the look-back
+// words a tile reads were written in the same L2. Tiles are handed out in that
+// order, so a workgroup only ever waits for tiles already held by running
+// workgroups: the launch is an ordinary one.
 //
 // Lanes. A wave is 4 rows of 16 lanes. A channel's N states are split over
 // NGR = N/NL rows (NL = min(N, 4) states per lane); the 16 lanes of a row are
@@ -44,6 +48,7 @@
 // one register and broadcasts them with DPP row_newbcast. The readout sum over
 // a channel's rows uses permlane16/32 swaps, which also scatter the finished
 // tokens over the rows so that each lane finishes 16/NGR of the 16 tokens.
+#include <atomic>
 #include <type_traits>
 
 #include "ssm_common.h"
@@ -58,6 +63,7 @@ constexpr int kWaves = 4;        // waves (segments) per workgroup
 constexpr int kChunk = kSegT * kWaves;
 constexpr int kXcds = 8;         // XCDs of an MI355X
 constexpr long kSpinLimit = 1L << 20;  // polls before a wait gives up (about a second)
+constexpr int kReplay = 2;       // aggregates loaded per round trip of a look-back replay
 
 template <int N, int DT>
 struct Geo {
@@ -95,8 +101,14 @@ struct Shared {
     float seg_s[kWaves][64][G::NL];  // segment end states (read only between the two item barriers)
     float seg_d[kWaves][64];         // segment summed deltas
     float carry[64][G::NL];          // the item's carried-in state
+    int64_t tiles[1];                // the next tile handed to this workgroup
     uint64_t early[G::NL >= 2 ? G::NL / 2 : 1][64][2];  // predecessor's inclusive state, fetched early
 };
+
+// Workgroups per CU the kernel is built for: two when two copies of the LDS
+// layout fit in the CU's 160 KB, else one (float tiles with N <= 4).
+template <int N, int DT>
+constexpr int min_blocks() { return 2 * sizeof(Shared<N, DT>) <= 160 * 1024 ? 2 : 1; }
 
 template <int SRC>
 __device__ __forceinline__ float row_bcast(float v) {
@@ -142,12 +154,6 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-__device__ __forceinline__ void st_dev(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
     return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -157,17 +163,48 @@ __device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t epoch) 
 __device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Complete this wave's stores, then raise the flag.
-__device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t epoch, int lane) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (lane == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// An item's segments 0..upto-1 folded from a zero start, in order: the end
+// state from a zero start and the summed delta. Every wave that needs an
+// item's aggregate (or a prefix of it) uses this, so that they agree bit for
+// bit; the look-back replay folds with the same arithmetic.
+template <int NL>
+__device__ __forceinline__ void fold_segments(const float (&seg_s)[kWaves][64][NL], const float (&seg_d)[kWaves][64],
+                                              int l, int upto, const float (&A2)[NL], float (&S)[NL], float &d) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) S[j] = 0.0f;
+    d = 0.0f;
+    for (int v = 0; v < upto; ++v) {
+        const float dd = seg_d[v][l];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) S[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), S[j], seg_s[v][l][j]);
+        d += dd;
+    }
 }
 
-// LDS address of a __shared__ location, made wave-uniform.
+// An item's aggregate as epoch-tagged words: NL state words per lane, then one
+// summed-delta word per lane.
+template <int NL>
+__device__ __forceinline__ void publish_aggregate(uint64_t *ag, int l, const float (&S)[NL], float d, uint32_t epoch) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) st_tagged(ag + l * NL + j, S[j], epoch);
+    st_tagged(ag + 64 * NL + l, d, epoch);
+}
+
+// A tagged word loaded earlier: if it is not yet this call's, load it again
+// until it is (its writer has already published the first word of the same
+// record, so this is short) or the spin limit is reached.
+__device__ __forceinline__ uint64_t recheck(uint64_t v, const uint64_t *p, uint32_t epoch) {
+    for (long sp = 0; (uint32_t)(v >> 32) != epoch && sp < kSpinLimit; ++sp) v = ld_tagged(p);
+    return v;
+}
+__device__ __forceinline__ uint64_t ld_valid(const uint64_t *p, uint32_t epoch) {
+    return recheck(ld_tagged(p), p, epoch);
+}
+
+// LDS address of a __shared__ location, made wave-uniform. A generic
+// pointer into the LDS aperture carries the LDS address in its low 32 bits.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
 // One 16-byte piece per lane from global memory straight into LDS at
@@ -256,8 +293,24 @@ __device__ __forceinline__ void issue_tile_loads(TileBuf<N, DT> &tb, const LbArg
     }
 }
 
+// Hand out `n` consecutive tiles of one XCD's list. The counter word holds
+// (epoch << 32 | next tile); the first workgroup of a call to arrive restarts
+// it at zero. Tiles are handed out in list order, so every tile a workgroup
+// waits for has already been handed to a running workgroup: no workgroup
+// needs another one to be resident, and the launch needs no co-residency.
+__device__ int64_t grab_tiles(uint64_t *ctr, uint32_t epoch, uint32_t n) {
+    uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while ((uint32_t)(v >> 32) != epoch) {
+        if (__hip_atomic_compare_exchange_strong(ctr, &v, ((uint64_t)epoch << 32) | n, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return 0;
+    }
+    // the epoch stays for the rest of the call: only the count changes now
+    return (int64_t)(uint32_t)__hip_atomic_fetch_add(ctr, (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int N, int DT, bool GATE, bool SKIP>
-__global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
+__global__ __launch_bounds__(64 * kWaves, (min_blocks<N, DT>())) void scan_lb_kernel(LbArgs a) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TPV = G::TPV, BREGS = G::BREGS;
@@ -273,14 +326,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
     const int64_t D = a.D, L = a.L;
 
     // Tiles: (batch row, tile column) x chunk. XCD x owns tile columns
-    // [x*tpx, (x+1)*tpx) and walks them chunk-major.
+    // [x*tpx, (x+1)*tpx) and hands its tiles out chunk-major.
     const int64_t ntpb = (D + TCH - 1) / TCH;          // tile columns per batch row
     const int64_t ntcol = a.batch * ntpb;
     const int64_t tpx = (ntcol + kXcds - 1) / kXcds;
     const int64_t nlocal = tpx * a.K;
     const int xcd = blockIdx.x % kXcds;
-    const int64_t gx = gridDim.x / kXcds;               // workgroups per XCD
-    const int64_t first = blockIdx.x / kXcds;
+    uint64_t *const counter = a.tiles + xcd;
 
     auto tile_of = [&](int64_t s, int64_t &tcol, int64_t &k) {
         k = s / tpx;
@@ -288,8 +340,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
         return tcol < ntcol;
     };
 
-    // Prologue: the first tile.
-    int64_t s = first;
+    // Prologue: the first tile, loaded before the loop.
+    if (w == 0 && l == 0) sh.tiles[0] = grab_tiles(counter, a.epoch, 1);
+    lds_barrier();
+    // tile indices of a list stay below 2^30 (checked when planning)
+    int64_t s = __builtin_amdgcn_readfirstlane((int)sh.tiles[0]);
     {
         int64_t tcol, k;
         if (s < nlocal && tile_of(s, tcol, k) && w > 0)
@@ -299,16 +354,33 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
     }
 
     int it = 0;        // tile counter (LDS buffer parity)
-    for (; s < nlocal; s += gx, ++it) {
+    while (s < nlocal) {
         TileBuf<N, DT> &tb = sh.buf[it & 1];
         int64_t tcol, k;
         const bool real = tile_of(s, tcol, k);
-        // Stream in the next tile while this one is scanned.
-        {
+        // Ask for the next tile now (wave 1). Wave 1 hands the answer over
+        // between the first item's two barriers; after the second, waves 1..3
+        // start loading that tile into the other buffer (free since the end of
+        // the previous tile) while this one is scanned. Tiles are thus taken
+        // one ahead and processed in the order they are handed out. The
+        // prologue has seen this call's epoch in the counter, so a 32-bit add
+        // on its low half, the tile count, is enough.
+        uint32_t nxt;  // assigned and read by wave 1, lane 0 only
+        if (w == 1 && l == 0)
+            nxt = __hip_atomic_fetch_add((uint32_t *)counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int64_t s_next = nlocal;
+        auto hand_over = [&]() {
+            if (w == 1 && l == 0) {
+                asm volatile("" : "+v"(nxt));  // read (and wait for) it here, in wave 1 only
+                sh.tiles[0] = nxt;
+            }
+        };
+        auto start_next = [&]() {
+            s_next = __builtin_amdgcn_readfirstlane((int)sh.tiles[0]);
             int64_t tcol2, k2;
-            if (w > 0 && s + gx < nlocal && tile_of(s + gx, tcol2, k2))
+            if (w > 0 && s_next < nlocal && tile_of(s_next, tcol2, k2))
                 issue_tile_loads<N, DT, GATE>(sh.buf[(it + 1) & 1], a, tcol2 / ntpb, (tcol2 % ntpb) * TCH, k2, w, l);
-        }
+        };
         if (real) {
             const int64_t b = tcol / ntpb;
             const int64_t ch0 = (tcol % ntpb) * TCH;
@@ -366,20 +438,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                     Cq[q] = ld_act(&tb.C[tw][0], nstate0 + (k16 % NL));
                 }
 
-                // Phase A: discretise once, keep dA and dBx, fold the segment.
-                float dA[kSegT][NL], u[kSegT][NL], S[NL];
+                // Phase A: discretise, keep dA (the exponentials) and delta*x,
+                // fold the segment. dBx = B*(delta*x) is one multiply and is
+                // formed again in phase C rather than held in registers.
+                float dA[kSegT][NL], dx[kSegT], S[NL];
                 float dsum = 0.0f;
 #pragma unroll
                 for (int j = 0; j < NL; ++j) S[j] = 0.0f;
                 static_for<0, kSegT>([&](auto tc) {
                     constexpr int t = decltype(tc)::value;
-                    const float dx = dv[t] * xv[t];
+                    dx[t] = dv[t] * xv[t];
                     dsum += dv[t];
                     static_for<0, NL>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
                         dA[t][j] = fast_exp2(dv[t] * A2[j]);
-                        u[t][j] = row_bcast<(t % TPV) * NL + j>(Bq[t / TPV]) * dx;
-                        S[j] = __builtin_fmaf(dA[t][j], S[j], u[t][j]);
+                        const float u = row_bcast<(t % TPV) * NL + j>(Bq[t / TPV]) * dx[t];
+                        S[j] = __builtin_fmaf(dA[t][j], S[j], u);
                     });
                 });
 #pragma unroll
@@ -389,30 +463,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 
                 // Earlier segments of this item folded from a zero start; read
                 // between the two barriers, so the segment buffers need no copy.
-                float pre_s[NL], pre_d = 0.0f;
-#pragma unroll
-                for (int j = 0; j < NL; ++j) pre_s[j] = 0.0f;
-                for (int v = 0; v < w; ++v) {
-                    const float dd = sh.seg_d[v][l];
-#pragma unroll
-                    for (int j = 0; j < NL; ++j) pre_s[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), pre_s[j], sh.seg_s[v][l][j]);
-                    pre_d += dd;
+                float pre_s[NL], pre_d;
+                fold_segments<NL>(sh.seg_s, sh.seg_d, l, w, A2, pre_s, pre_d);
+                const bool publish = k + 1 < a.K;  // a later chunk reads this item's words
+
+                // With several chunks of a column in flight at once, every item
+                // publishes its aggregate right away (wave 2), so that its
+                // successors can fold it in without waiting for its state.
+                if (a.agg_early && w == 2 && publish) {
+                    float Sagg[NL], dagg;
+                    fold_segments<NL>(sh.seg_s, sh.seg_d, l, kWaves, A2, Sagg, dagg);
+                    publish_aggregate<NL>(a.agg + item * (64 * (NL + 1)), l, Sagg, dagg, a.epoch);
                 }
 
+                if (sub == 0) hand_over();
+
                 if (w == 0) {
-                    // Item aggregate: fold the segments in order.
-                    float Sagg[NL], dagg = sh.seg_d[0][l];
-#pragma unroll
-                    for (int j = 0; j < NL; ++j) Sagg[j] = sh.seg_s[0][l][j];
-#pragma unroll
-                    for (int v = 1; v < kWaves; ++v) {
-                        const float dd = sh.seg_d[v][l];
-#pragma unroll
-                        for (int j = 0; j < NL; ++j)
-                            Sagg[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), Sagg[j], sh.seg_s[v][l][j]);
-                        dagg += dd;
-                    }
-                    const bool publish = k + 1 < a.K;
                     float H[NL];
                     if (k == 0) {
                         const float *si = a.state_in ? a.state_in + (b * D + dc) * N + nstate0 : nullptr;
@@ -434,13 +500,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
 #pragma unroll
                             for (int j = 0; j < NL; ++j) H[j] = __uint_as_float((uint32_t)early[j]);
                         } else {
-                            // Slow path: let later items skip this one, then
-                            // scan back to the nearest inclusive state.
-                            if (publish) {
-#pragma unroll
-                                for (int j = 0; j < NL; ++j) st_dev(a.agg_s + item * (64 * NL) + l * NL + j, Sagg[j]);
-                                st_dev(a.agg_d + item * 64 + l, dagg);
-                                publish_flag(a.agg_flag + item, a.epoch, l);
+                            // Slow path. Publish this item's aggregate (unless wave 2
+                            // has) so that later items can fold it in without waiting
+                            // for it, then find the nearest earlier item whose
+                            // inclusive state is out with the aggregates of all items
+                            // after it out.
+                            if (publish && !a.agg_early) {
+                                float Sagg[NL], dagg;
+                                fold_segments<NL>(sh.seg_s, sh.seg_d, l, kWaves, A2, Sagg, dagg);
+                                publish_aggregate<NL>(a.agg + item * (64 * (NL + 1)), l, Sagg, dagg, a.epoch);
                             }
                             int64_t base = k - 1;  // chunk examined by lane 0
                             int64_t j0 = -1;
@@ -449,10 +517,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                                 const int64_t jj = base - l;  // chunk examined by this lane
                                 bool inc = false, agg = false;
                                 if (jj >= 0) {
-                                    // the first word of an item's inclusive state stands for all of it;
+                                    // the first word of an item's record stands for all of it;
                                     // the replay below still checks every word it reads
-                                    inc = (uint32_t)(ld_tagged(a.incl + (jj * a.nicol + icol) * (64 * NL)) >> 32) == a.epoch;
-                                    agg = inc || ld_flag(a.agg_flag + jj * a.nicol + icol) == a.epoch;
+                                    const int64_t it2 = jj * a.nicol + icol;
+                                    inc = (uint32_t)(ld_tagged(a.incl + it2 * (64 * NL)) >> 32) == a.epoch;
+                                    agg = inc || (uint32_t)(ld_tagged(a.agg + it2 * (64 * (NL + 1))) >> 32) == a.epoch;
                                 }
                                 const uint64_t m_inc = __builtin_amdgcn_ballot_w64(inc);
                                 const uint64_t m_agg = __builtin_amdgcn_ballot_w64(agg);
@@ -475,48 +544,68 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                                 }
                                 __builtin_amdgcn_s_sleep(2);
                             }
-                            __atomic_signal_fence(__ATOMIC_SEQ_CST);
                             if (j0 < 0) {
 #pragma unroll
                                 for (int j = 0; j < NL; ++j) H[j] = 0.0f;
                             } else {
                                 // Replay the chain forward from that state with the
-                                // arithmetic each item uses for its own inclusive state.
+                                // arithmetic each item uses for its own inclusive
+                                // state, kReplay aggregates per round trip.
                                 const uint64_t *src = a.incl + (j0 * a.nicol + icol) * (64 * NL) + l * NL;
 #pragma unroll
-                                for (int j = 0; j < NL; ++j) {
-                                    uint64_t v = ld_tagged(src + j);
-                                    for (long sp = 0; (uint32_t)(v >> 32) != a.epoch && sp < kSpinLimit; ++sp)
-                                        v = ld_tagged(src + j);
-                                    H[j] = __uint_as_float((uint32_t)v);
-                                }
-                                for (int64_t jj = j0 + 1; jj < k; ++jj) {
-                                    const int64_t it2 = jj * a.nicol + icol;
-                                    const float dd = ld_dev(a.agg_d + it2 * 64 + l);
+                                for (int j = 0; j < NL; ++j) H[j] = __uint_as_float((uint32_t)ld_valid(src + j, a.epoch));
+                                for (int64_t jj = j0 + 1; jj < k; jj += kReplay) {
+                                    uint64_t sv[kReplay][NL], dv2[kReplay];
 #pragma unroll
-                                    for (int j = 0; j < NL; ++j)
-                                        H[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), H[j],
-                                                              ld_dev(a.agg_s + it2 * (64 * NL) + l * NL + j));
+                                    for (int q = 0; q < kReplay; ++q) {
+                                        if (jj + q < k) {
+                                            const uint64_t *ag = a.agg + ((jj + q) * a.nicol + icol) * (64 * (NL + 1));
+#pragma unroll
+                                            for (int j = 0; j < NL; ++j) sv[q][j] = ld_tagged(ag + l * NL + j);
+                                            dv2[q] = ld_tagged(ag + 64 * NL + l);
+                                        }
+                                    }
+#pragma unroll
+                                    for (int q = 0; q < kReplay; ++q) {
+                                        if (jj + q < k) {
+                                            const uint64_t *ag = a.agg + ((jj + q) * a.nicol + icol) * (64 * (NL + 1));
+                                            const float dd = __uint_as_float((uint32_t)recheck(dv2[q], ag + 64 * NL + l, a.epoch));
+#pragma unroll
+                                            for (int j = 0; j < NL; ++j)
+                                                H[j] = __builtin_fmaf(fast_exp2(A2[j] * dd), H[j],
+                                                                      __uint_as_float((uint32_t)recheck(sv[q][j], ag + l * NL + j, a.epoch)));
+                                        }
+                                    }
                                 }
                             }
                         }
-                    }
-                    if (publish) {
-                        uint64_t *dst = a.incl + item * (64 * NL) + l * NL;
-#pragma unroll
-                        for (int j = 0; j < NL; ++j)
-                            st_tagged(dst + j, __builtin_fmaf(fast_exp2(A2[j] * dagg), H[j], Sagg[j]), a.epoch);
                     }
 #pragma unroll
                     for (int j = 0; j < NL; ++j) sh.carry[l][j] = H[j];
                 }
                 lds_barrier();
+                if (sub == 0) start_next();
 
                 // This wave's carried-in state: the item's, pushed through the
                 // earlier segments (folded above, before the barrier).
-                float h[NL];
+                float h[NL], H[NL];
 #pragma unroll
-                for (int j = 0; j < NL; ++j) h[j] = __builtin_fmaf(fast_exp2(A2[j] * pre_d), sh.carry[l][j], pre_s[j]);
+                for (int j = 0; j < NL; ++j) {
+                    H[j] = sh.carry[l][j];
+                    h[j] = __builtin_fmaf(fast_exp2(A2[j] * pre_d), H[j], pre_s[j]);
+                }
+                // The last wave publishes the item's inclusive state (its own
+                // segment completes the aggregate in its registers); wave 0's
+                // memory queue stays free for the next item's look-back.
+                if (w == kWaves - 1 && publish) {
+                    uint64_t *dst = a.incl + item * (64 * NL) + l * NL;
+                    const float dagg = pre_d + dsum;
+#pragma unroll
+                    for (int j = 0; j < NL; ++j) {
+                        const float sagg = __builtin_fmaf(fast_exp2(A2[j] * dsum), pre_s[j], S[j]);
+                        st_tagged(dst + j, __builtin_fmaf(fast_exp2(A2[j] * dagg), H[j], sagg), a.epoch);
+                    }
+                }
 
                 // Phase C: rescan from registers; partial readout over this lane's states.
                 float yp[kSegT];
@@ -525,7 +614,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                     yp[t] = 0.0f;
                     static_for<0, NL>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
-                        h[j] = __builtin_fmaf(dA[t][j], h[j], u[t][j]);
+                        const float u = row_bcast<(t % TPV) * NL + j>(Bq[t / TPV]) * dx[t];
+                        h[j] = __builtin_fmaf(dA[t][j], h[j], u);
                         fmac_bcast<(t % TPV) * NL + j>(yp[t], Cq[t / TPV], h[j]);
                     });
                 });
@@ -575,6 +665,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
                 }
             }
         }
+        if (!real) {
+            hand_over();
+            lds_barrier();
+            start_next();
+        }
         lds_barrier();
         // Store the finished y tile as whole lines (waves 1..3), then make sure
         // the next tile has landed before anyone reads it.
@@ -594,19 +689,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void scan_lb_kernel(LbArgs a) {
         }
         if (w > 0) vm_wait();
         lds_barrier();
+        s = s_next;
+        ++it;
     }
 }
 
 template <int N, int DT, bool GATE, bool SKIP>
 hipError_t launch_lb_typed(const LbArgs &a, hipStream_t s) {
     auto kern = scan_lb_kernel<N, DT, GATE, SKIP>;
+    constexpr int kMaxDevices = 64;
+    // CU count and resident workgroups per CU, queried once per device:
+    // (cus << 32 | per_cu), 0 = not queried yet
+    static std::atomic<uint64_t> cache[kMaxDevices];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int cus = 0, per_cu = 0;
-    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kWaves, 0)) != hipSuccess) return e;
-    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    uint64_t packed = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (packed == 0) {
+        int cus = 0, per_cu = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kWaves, 0)) != hipSuccess) return e;
+        if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+        packed = (uint64_t)cus << 32 | (uint32_t)per_cu;
+        if (dev < kMaxDevices) cache[dev].store(packed, std::memory_order_relaxed);
+    }
+    const int cus = (int)(packed >> 32), per_cu = (int)(uint32_t)packed;
     using G = Geo<N, DT>;
     const int64_t ntcol = a.batch * ((a.D + G::TCH - 1) / G::TCH);
     const int64_t tpx = (ntcol + kXcds - 1) / kXcds;
@@ -615,8 +722,10 @@ hipError_t launch_lb_typed(const LbArgs &a, hipStream_t s) {
     if (grid > need) grid = need;
     if (grid < kXcds) grid = kXcds;
     LbArgs args = a;
+    // more workgroups per XCD than tile columns: chunks of a column overlap
+    args.agg_early = grid / kXcds > tpx;
     void *params[] = {&args};
-    return hipLaunchCooperativeKernel((const void *)kern, dim3((unsigned)grid), dim3(64 * kWaves), params, 0, s);
+    return hipLaunchKernel((const void *)kern, dim3((unsigned)grid), dim3(64 * kWaves), params, 0, s);
 }
 
 template <int N, int DT>
@@ -640,6 +749,7 @@ void lb_geometry(int64_t batch, int64_t L, int64_t D, LbPlan *p) {
     p->nicol = batch * ((D + G::TCH - 1) / G::TCH) * G::SUBS;
     p->K = (L + kChunk - 1) / kChunk;
     p->vec = G::VEC;
+    p->tiles_per_list = (batch * ((D + G::TCH - 1) / G::TCH) + kXcds - 1) / kXcds * p->K;
 }
 
 }  // namespace
@@ -659,17 +769,17 @@ bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, LbPlan *
     // Bt/Ct rows at least one piece.
     const int esz = bf ? 2 : 4;
     p->supported = (D % p->vec == 0) && (N * esz >= 16);
+    // tile indices of one XCD's list must fit the counters (and a 32-bit lane)
+    if (p->tiles_per_list >= (int64_t(1) << 30)) p->supported = false;
     const int64_t items = p->nicol * p->K;
-    // header | incl (tagged) | agg_s | agg_d | agg_flag
+    // header (error word, tile counters) | incl | agg, all words epoch-tagged:
+    // per item, incl holds 64 lanes x NL state words and agg 64 x NL state
+    // words followed by 64 summed-delta words
     size_t off = 256;
     p->off_incl = off;
     off += (size_t)items * 64 * p->nl * sizeof(uint64_t);
-    p->off_agg_s = off;
-    off += (size_t)items * 64 * p->nl * sizeof(float);
-    p->off_agg_d = off;
-    off += (size_t)items * 64 * sizeof(float);
-    p->off_agg_flag = off;
-    off += (size_t)items * sizeof(uint32_t);
+    p->off_agg = off;
+    off += (size_t)items * 64 * (p->nl + 1) * sizeof(uint64_t);
     p->bytes = (off + 255) / 256 * 256;
     return true;
 }
