@@ -52,22 +52,39 @@ size_t lb_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, s
     return p->bytes;
 }
 
-// The single-pass scan reads 16-byte pieces of channel rows; shapes whose
-// rows are not whole pieces take the three-launch scan, which can also be
-// forced with SSM_SCAN_IMPL=twopass (for comparison).
-bool use_twopass(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
+// Workspace of the stripe scan.
+size_t stripe_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, ssm::StripePlan *p) {
+    if (!ssm::stripe_plan(batch, L, D, N, dtype, p)) return 0;
+    return p->bytes;
+}
+
+// Which scan runs. The stripe scan reads 16-byte pieces of channel rows and
+// Bt/Ct rows; shapes it cannot take run the chunked three-launch scan.
+// SSM_SCAN_IMPL=twopass|lb|stripe picks one for comparison (if the shape
+// allows it).
+enum class Impl { kTwopass, kLb, kStripe };
+
+Impl choose_impl(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
+    ssm::StripePlan sp;
+    ssm::LbPlan lp;
+    const bool stripe_ok = ssm::stripe_plan(batch, L, D, N, dtype, &sp) && sp.supported;
+    const bool lb_ok = ssm::lb_plan(batch, L, D, N, dtype, &lp) && lp.supported;
     const char *e = getenv("SSM_SCAN_IMPL");
-    if (e && strcmp(e, "twopass") == 0) return true;
-    ssm::LbPlan p;
-    return !ssm::lb_plan(batch, L, D, N, dtype, &p) || !p.supported;
+    if (e && strcmp(e, "twopass") == 0) return Impl::kTwopass;
+    if (e && strcmp(e, "lb") == 0 && lb_ok) return Impl::kLb;
+    if (stripe_ok) return Impl::kStripe;
+    return Impl::kTwopass;
 }
 
 size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     int64_t K, Lc;
-    ssm::LbPlan p;
-    const size_t a = twopass_workspace(batch, L, D, N, &K, &Lc);
-    const size_t b = lb_workspace(batch, L, D, N, dtype, &p);
-    return a > b ? a : b;
+    ssm::LbPlan lp;
+    ssm::StripePlan sp;
+    switch (choose_impl(batch, L, D, N, dtype)) {
+        case Impl::kLb: return lb_workspace(batch, L, D, N, dtype, &lp);
+        case Impl::kStripe: return stripe_workspace(batch, L, D, N, dtype, &sp);
+        default: return twopass_workspace(batch, L, D, N, &K, &Lc);
+    }
 }
 
 // Distinct nonzero value per call; marks the words a call publishes in the workspace.
@@ -137,7 +154,38 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SSM_ERR_ALIGN;
     }
-    if (use_twopass(batch, L, D, N, dtype)) {
+    const Impl impl = choose_impl(batch, L, D, N, dtype);
+    if (impl == Impl::kStripe) {
+        ssm::StripePlan p;
+        stripe_workspace(batch, L, D, N, dtype, &p);
+        ssm::StripeArgs a{};
+        a.batch = batch;
+        a.L = L;
+        a.D = D;
+        a.x = x;
+        a.delta = delta;
+        a.Bt = Bt;
+        a.Ct = Ct;
+        a.z = z;
+        a.A = A;
+        a.Dskip = Dskip;
+        a.state_in = state_in;
+        a.state_out = state_out;
+        a.y = y;
+        a.ntpb = p.ntpb;
+        a.ncol = p.ncol;
+        a.cols_per_list = p.cols_per_list;
+        a.S = p.S;
+        a.SL = p.SL;
+        a.epoch = next_epoch();
+        char *w = (char *)workspace;
+        a.error = (uint32_t *)w;
+        a.counters = (uint32_t *)(w + 64);
+        a.incl = (uint64_t *)(w + p.off_incl);
+        a.agg = (uint64_t *)(w + p.off_agg);
+        return ssm::launch_scan_stripe(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    }
+    if (impl == Impl::kTwopass) {
         ssm::ScanArgs a{};
         a.batch = batch;
         a.L = L;
@@ -181,7 +229,7 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     if (lbw > 0) {
         char *w = (char *)workspace;
         a.error = (uint32_t *)w;
-        a.tiles = (uint64_t *)(w + 64);
+        a.tiles = (uint32_t *)(w + 64);
         a.incl = (uint64_t *)(w + p.off_incl);
         a.agg = (uint64_t *)(w + p.off_agg);
     }

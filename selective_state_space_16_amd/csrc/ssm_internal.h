@@ -32,7 +32,7 @@ struct LbArgs {
     uint32_t epoch;     // value that marks this call's published words
     int agg_early;      // every item publishes its aggregate right after phase A
     uint32_t *error;    // set when a look-back wait timed out
-    uint64_t *tiles;    // 8 tile counters (one per XCD list), (epoch << 32 | next tile) words
+    uint32_t *tiles;    // 8 tile counters (one per XCD list), zero between calls
     uint64_t *incl;     // per item: inclusive end state, epoch-tagged words
     uint64_t *agg;      // per item: end state from a zero start and summed delta, epoch-tagged words
 };
@@ -41,6 +41,31 @@ struct LbArgs {
 struct LbPlan {
     int64_t nl, nicol, K, chunk, vec;
     int64_t tiles_per_list;  // tiles each of the 8 per-XCD lists hands out
+    bool supported;     // shape meets the tile-load requirements
+    size_t off_incl, off_agg, bytes;
+};
+
+// Stripe scan: every wave walks its channels along a stripe of the sequence.
+struct StripeArgs {
+    int64_t batch, L, D;
+    const void *x, *delta, *Bt, *Ct, *z;
+    const float *A, *Dskip, *state_in;
+    float *state_out;
+    void *y;
+    int64_t ntpb;           // tile columns per batch row
+    int64_t ncol;           // tile columns
+    int64_t cols_per_list;  // tile columns per unit list
+    int64_t S;              // stripes per tile column
+    int64_t SL;             // tokens per stripe (the last one may be shorter)
+    uint32_t epoch;         // value that marks this call's published words
+    uint32_t *error;        // set when a look-back wait timed out
+    uint32_t *counters;     // 8 unit counters, zero between calls
+    uint64_t *incl;         // per (column, stripe, wave): end state, epoch-tagged words
+    uint64_t *agg;          // per (column, stripe, wave): end state from zero and summed delta
+};
+
+struct StripePlan {
+    int64_t nl, tch, tt, vec, ntpb, ncol, cols_per_list, S, SL;
     bool supported;     // shape meets the tile-load requirements
     size_t off_incl, off_agg, bytes;
 };
@@ -57,9 +82,11 @@ struct StepArgs {
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);
 
 bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, LbPlan *p);
+bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, StripePlan *p);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_scan_lb(const LbArgs &a, int N, int dtype, hipStream_t s);
+hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepArgs &a, int N, int dtype, hipStream_t s);

@@ -52,6 +52,7 @@
 #include <type_traits>
 
 #include "ssm_common.h"
+#include "ssm_device.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -62,7 +63,6 @@ constexpr int kSegT = 16;        // tokens per wave segment
 constexpr int kWaves = 4;        // waves (segments) per workgroup
 constexpr int kChunk = kSegT * kWaves;
 constexpr int kXcds = 8;         // XCDs of an MI355X
-constexpr long kSpinLimit = 1L << 20;  // polls before a wait gives up (about a second)
 constexpr int kReplay = 2;       // aggregates loaded per round trip of a look-back replay
 
 template <int N, int DT>
@@ -110,59 +110,6 @@ struct Shared {
 template <int N, int DT>
 constexpr int min_blocks() { return 2 * sizeof(Shared<N, DT>) <= 160 * 1024 ? 2 : 1; }
 
-template <int SRC>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, true));
-}
-
-// acc += (lane SRC of the row's `c`) * h, as one v_fmac_f32 with a DPP source.
-// The leading s_nop covers the DPP read-after-VALU-write hazard, which the
-// compiler does not see inside inline assembly.
-#define SSM_FMAC_BCAST(SRC)                                                                       \
-    template <>                                                                                   \
-    __device__ __forceinline__ void fmac_bcast<SRC>(float &acc, float c, float h) {               \
-        asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #SRC                    \
-                     " row_mask:0xf bank_mask:0xf"                                                \
-                     : "+v"(acc)                                                                  \
-                     : "v"(c), "v"(h));                                                           \
-    }
-template <int SRC>
-__device__ __forceinline__ void fmac_bcast(float &acc, float c, float h);
-SSM_FMAC_BCAST(0) SSM_FMAC_BCAST(1) SSM_FMAC_BCAST(2) SSM_FMAC_BCAST(3)
-SSM_FMAC_BCAST(4) SSM_FMAC_BCAST(5) SSM_FMAC_BCAST(6) SSM_FMAC_BCAST(7)
-SSM_FMAC_BCAST(8) SSM_FMAC_BCAST(9) SSM_FMAC_BCAST(10) SSM_FMAC_BCAST(11)
-SSM_FMAC_BCAST(12) SSM_FMAC_BCAST(13) SSM_FMAC_BCAST(14) SSM_FMAC_BCAST(15)
-#undef SSM_FMAC_BCAST
-
-// v_permlane32_swap: lanes 32-63 of a trade places with lanes 0-31 of b, so
-// a = [a.lo, b.lo] and b = [a.hi, b.hi]. v_permlane16_swap: the odd rows of a
-// trade places with the even rows of b. Written as inline assembly (with the
-// two wait states a VALU-written source needs) because the compiler builtin
-// returns both results in one register when they feed the same add.
-__device__ __forceinline__ void swap_halves(float &a, float &b) {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap_odd_even_rows(float &a, float &b) {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-
-template <int I, int END, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (I < END) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, END>(f);
-    }
-}
-
-__device__ __forceinline__ uint32_t ld_flag(const uint32_t *p) {
-    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t epoch) {
-    __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // An item's segments 0..upto-1 folded from a zero start, in order: the end
 // state from a zero start and the summed delta. Every wave that needs an
 // item's aggregate (or a prefix of it) uses this, so that they agree bit for
@@ -188,55 +135,6 @@ __device__ __forceinline__ void publish_aggregate(uint64_t *ag, int l, const flo
 #pragma unroll
     for (int j = 0; j < NL; ++j) st_tagged(ag + l * NL + j, S[j], epoch);
     st_tagged(ag + 64 * NL + l, d, epoch);
-}
-
-// A tagged word loaded earlier: if it is not yet this call's, load it again
-// until it is (its writer has already published the first word of the same
-// record, so this is short) or the spin limit is reached.
-__device__ __forceinline__ uint64_t recheck(uint64_t v, const uint64_t *p, uint32_t epoch) {
-    for (long sp = 0; (uint32_t)(v >> 32) != epoch && sp < kSpinLimit; ++sp) v = ld_tagged(p);
-    return v;
-}
-__device__ __forceinline__ uint64_t ld_valid(const uint64_t *p, uint32_t epoch) {
-    return recheck(ld_tagged(p), p, epoch);
-}
-
-// LDS address of a __shared__ location, made wave-uniform. A generic
-// pointer into the LDS aperture carries the LDS address in its low 32 bits.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
-// One 16-byte piece per lane from global memory straight into LDS at
-// lds + lane*16 (global_load_lds_dwordx4; lds is wave-uniform). Written as
-// inline assembly so that the compiler does not count these loads: it would
-// otherwise wait for all of them before LDS reads and barriers that have
-// nothing to do with them, which serialises the prefetch of the next tile
-// with the scan of the current one. No registers receive data; the caller
-// waits with vm_wait() before the data is read.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-// The same for 4-byte pieces (lds + lane*4).
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-// 16-byte pieces of data other workgroups write (bypasses the CU's cache).
-__device__ __forceinline__ void dma16_coherent(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(g), "s"(lds) : "memory");
-}
-// Wait until this wave's vector memory accesses (including the loads above)
-// have completed.
-__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Workgroup barrier that orders LDS accesses only. __syncthreads() would also
-// wait for every global access the wave has in flight, which includes the
-// next tile's loads into LDS; those are meant to stay in flight across the
-// barriers of the current tile.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 // Issue the loads of one tile into LDS, spread over waves 1..3 (wave 0 keeps
@@ -293,20 +191,17 @@ __device__ __forceinline__ void issue_tile_loads(TileBuf<N, DT> &tb, const LbArg
     }
 }
 
-// Hand out `n` consecutive tiles of one XCD's list. The counter word holds
-// (epoch << 32 | next tile); the first workgroup of a call to arrive restarts
-// it at zero. Tiles are handed out in list order, so every tile a workgroup
-// waits for has already been handed to a running workgroup: no workgroup
-// needs another one to be resident, and the launch needs no co-residency.
-__device__ int64_t grab_tiles(uint64_t *ctr, uint32_t epoch, uint32_t n) {
-    uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while ((uint32_t)(v >> 32) != epoch) {
-        if (__hip_atomic_compare_exchange_strong(ctr, &v, ((uint64_t)epoch << 32) | n, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            return 0;
-    }
-    // the epoch stays for the rest of the call: only the count changes now
-    return (int64_t)(uint32_t)__hip_atomic_fetch_add(ctr, (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The next tile of one XCD's list. Tiles are handed out in list order, so
+// every tile a workgroup waits for has already been handed to a running
+// workgroup: no workgroup needs another one to be resident, and the launch
+// needs no co-residency. Each workgroup takes tiles until it is handed one
+// past the end, so a call makes exactly (tiles + workgroups of the list) takes;
+// the last one puts the counter back to zero for the next call.
+__device__ __forceinline__ uint32_t take_tile(uint32_t *ctr) {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void after_take(uint32_t *ctr, uint32_t t, uint32_t last) {
+    if (t == last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int N, int DT, bool GATE, bool SKIP>
@@ -332,7 +227,8 @@ __global__ __launch_bounds__(64 * kWaves, (min_blocks<N, DT>())) void scan_lb_ke
     const int64_t tpx = (ntcol + kXcds - 1) / kXcds;
     const int64_t nlocal = tpx * a.K;
     const int xcd = blockIdx.x % kXcds;
-    uint64_t *const counter = a.tiles + xcd;
+    uint32_t *const counter = a.tiles + xcd;
+    const uint32_t last_take = (uint32_t)(nlocal + gridDim.x / kXcds - 1);
 
     auto tile_of = [&](int64_t s, int64_t &tcol, int64_t &k) {
         k = s / tpx;
@@ -341,7 +237,11 @@ __global__ __launch_bounds__(64 * kWaves, (min_blocks<N, DT>())) void scan_lb_ke
     };
 
     // Prologue: the first tile, loaded before the loop.
-    if (w == 0 && l == 0) sh.tiles[0] = grab_tiles(counter, a.epoch, 1);
+    if (w == 0 && l == 0) {
+        const uint32_t t = take_tile(counter);
+        after_take(counter, t, last_take);
+        sh.tiles[0] = t;
+    }
     lds_barrier();
     // tile indices of a list stay below 2^30 (checked when planning)
     int64_t s = __builtin_amdgcn_readfirstlane((int)sh.tiles[0]);
@@ -362,16 +262,14 @@ __global__ __launch_bounds__(64 * kWaves, (min_blocks<N, DT>())) void scan_lb_ke
         // between the first item's two barriers; after the second, waves 1..3
         // start loading that tile into the other buffer (free since the end of
         // the previous tile) while this one is scanned. Tiles are thus taken
-        // one ahead and processed in the order they are handed out. The
-        // prologue has seen this call's epoch in the counter, so a 32-bit add
-        // on its low half, the tile count, is enough.
+        // one ahead and processed in the order they are handed out.
         uint32_t nxt;  // assigned and read by wave 1, lane 0 only
-        if (w == 1 && l == 0)
-            nxt = __hip_atomic_fetch_add((uint32_t *)counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (w == 1 && l == 0) nxt = take_tile(counter);
         int64_t s_next = nlocal;
         auto hand_over = [&]() {
             if (w == 1 && l == 0) {
                 asm volatile("" : "+v"(nxt));  // read (and wait for) it here, in wave 1 only
+                after_take(counter, nxt, last_take);
                 sh.tiles[0] = nxt;
             }
         };

@@ -1,0 +1,553 @@
+// Selective scan (S6) forward for gfx950, organised by stripes.
+//
+// The recurrence h <- dA*h + dBx runs along the sequence independently for
+// every (batch row, channel, state) ("Notas sobre Mamba", section "A varredura
+// paralela ciente do hardware": an associative scan over (A-bar_t, B-bar_t
+// x_t) pairs, kept on chip, only y written back). Here a wave owns CPW
+// channels (16 for N = 16: four rows of 16 lanes, NL = 4 states per lane) and
+// walks the tokens of its stripe in order with the state in registers, so the
+// scan itself needs no communication at all: per token and state it is one
+// exponential, dA*h + B*(delta*x), and C*h accumulated into the readout.
+//
+// Work units. A workgroup of four waves covers a tile column of TCH = 4*CPW
+// channels of one batch row and a stripe of the sequence. When there are at
+// least as many tile columns as workgroup slots, a stripe is the whole
+// sequence and each unit is one pass. Otherwise every column is cut into S
+// stripes that run at the same time, and the carried-in state of a stripe is
+// found with the associative composition of affine maps: applying a run of
+// tokens to a state is the pair (P, S) with P = exp(A * sum delta) and S the
+// run's end state from a zero start. Pass 1 walks the stripe to get its own
+// (sum delta, S) and publishes it; a look-back then finds the nearest earlier
+// stripe whose end state is out and folds the pairs in between (the chain of
+// a handful of records, once per stripe); pass 2 walks the stripe again from
+// that state and writes y. Every record is a set of 64-bit words tagged with
+// the call's epoch, so a reader can validate each word without flags or
+// completion waits. The replay uses the same arithmetic each stripe uses for
+// its own end state, so results do not depend on timing.
+//
+// Memory. Tiles of TT tokens x TCH channels of x, delta (and z, for pass 2),
+// and the TT tokens of Bt (and Ct) are loaded into LDS with global_load_lds,
+// double-buffered so that the next tile streams in while this one is scanned;
+// channel rows are whole 128-byte lines (64 bfloat16 or, as two lines, 64
+// float channels). Waves 1..3 issue the loads; wave 0 writes the finished y
+// tile back as whole lines, so no wave ever waits for its own stores. A tile
+// column's A rows and skip weights live in registers.
+//
+// Scheduling. Units are handed out from one counter per list (eight lists, a
+// workgroup serves the list of its blockIdx modulo 8, i.e. its XCD; tile
+// columns are dealt to the lists round robin). Units are handed out in list
+// order with the stripes of a column in sequence order, so a stripe only ever
+// waits for stripes already held by running workgroups: the launch needs no
+// co-residency.
+#include <atomic>
+
+#include "ssm_common.h"
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kWaves = 4;   // waves per workgroup (one per channel group)
+constexpr int kLists = 8;   // unit lists (one per XCD of an MI355X)
+constexpr int kReplay = 8;  // stripe records loaded per round trip of a look-back replay
+constexpr int kSlotsPerList = 64;  // workgroups a list is planned for (2 per CU on 256 CUs)
+
+template <int N, int DT>
+struct Geo {
+    using T = typename Act<DT>::T;
+    static constexpr int NL = N < 4 ? N : 4;       // states per lane
+    static constexpr int NGR = N / NL;             // rows per channel
+    static constexpr int CPW = (4 / NGR) * 16;     // channels per wave
+    static constexpr int TCH = kWaves * CPW;       // channels per tile column
+    static constexpr int TPV = 16 / NL;            // tokens per broadcast register
+    static constexpr int GROUP = TPV > 8 ? TPV : 8;  // tokens per register group
+    static constexpr int BREGS = GROUP / TPV;      // broadcast registers per group
+    static constexpr int OWN = GROUP / NGR;        // tokens of a group each lane finishes
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int VEC = 16 / ESZ;           // elements per 16-byte piece
+    // tokens per tile: three activation tiles of at most 24 KB
+    static constexpr int TT_RAW = 8192 / (TCH * ESZ);
+    static constexpr int TT = TT_RAW < 16 ? 16 : (TT_RAW > 64 ? 64 : TT_RAW);
+    static constexpr int PPR = TCH / VEC;           // pieces per tile row
+    static constexpr int ACT_PIECES = TT * PPR;     // pieces per activation tile (a multiple of 64)
+    static constexpr int BC_PIECES = TT * N / VEC;  // pieces per Bt/Ct tile
+    static constexpr int BC_SLOTS = (BC_PIECES + 63) / 64 * 64;
+    static_assert(ACT_PIECES % 64 == 0, "activation tiles are loaded in whole waves of pieces");
+};
+
+template <int N, int DT>
+struct TileBuf {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    T x[G::TT][G::TCH];
+    T dl[G::TT][G::TCH];  // delta; pass 2 writes y here once a token's delta is used
+    T z[G::TT][G::TCH];
+    T B[G::BC_SLOTS * G::VEC];  // Bt rows of the tile's tokens (padded to whole waves of pieces)
+    T C[G::BC_SLOTS * G::VEC];
+};
+
+template <int N, int DT>
+struct Shared {
+    TileBuf<N, DT> buf[2];
+    int unit;  // the unit handed to this workgroup
+};
+
+template <int N, int DT>
+constexpr int stripe_min_blocks() { return 2 * sizeof(Shared<N, DT>) <= 160 * 1024 ? 2 : 1; }
+
+// An activation element of an LDS tile row, widened to float. A bfloat16 is
+// read as the 32-bit word holding it and its neighbour, and moved into the
+// high half of the result with one byte permute (`sel` depends only on the
+// element's parity): the loads then go straight to their own registers.
+__device__ __forceinline__ float lds_act(const float *row, int i, uint32_t) { return row[i]; }
+__device__ __forceinline__ float lds_act(const uint16_t *row, int i, uint32_t sel) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(row)[i >> 1];
+    return __uint_as_float(__builtin_amdgcn_perm(w, w, sel));
+}
+// Byte selector of lds_act for an element of this parity: bytes 1,0 (even) or
+// 3,2 (odd) of the word into bytes 3,2 of the result, zeros below.
+__device__ __forceinline__ uint32_t half_sel(int i) { return (i & 1) ? 0x03020c0cu : 0x01000c0cu; }
+
+__device__ __forceinline__ uint32_t take_unit(uint32_t *ctr) {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Load tile `tile` of the stripe (tokens t0 + tile*TT ...) of tile column
+// (b, ch0) into LDS, spread over waves 1..3. Pass 1 needs x, delta and Bt;
+// pass 2 also z and Ct. Pieces past the end of the sequence or of the
+// channels are read from an in-bounds location instead; the tokens are given
+// delta = 0 afterwards and the channels are never stored.
+template <int N, int DT, bool GATE, int PASS>
+__device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
+                                          int w, int lane) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr int NACT = (PASS == 2 && GATE) ? 3 : 2;
+    constexpr int NBC = PASS == 2 ? 2 : 1;
+    const int64_t D = a.D, L = a.L;
+    for (int base = (w - 1) * 64; base < NACT * G::ACT_PIECES; base += 3 * 64) {
+        const int arr = base / G::ACT_PIECES;
+        const int pa = base - arr * G::ACT_PIECES + lane;
+        const int r = pa / G::PPR, c = (pa % G::PPR) * G::VEC;
+        int64_t t = tt0 + r;
+        t = t < L ? t : L - 1;
+        int64_t ch = ch0 + c;
+        ch = ch + G::VEC <= D ? ch : D - G::VEC;
+        const T *src = arr == 0 ? (const T *)a.x : arr == 1 ? (const T *)a.delta : (const T *)a.z;
+        T *dst = arr == 0 ? &tb.x[0][0] : arr == 1 ? &tb.dl[0][0] : &tb.z[0][0];
+        dma16(src + (b * L + t) * D + ch, lds_addr(dst + (int64_t)(base - arr * G::ACT_PIECES) * G::VEC));
+    }
+    for (int base = (w - 1) * 64; base < NBC * G::BC_SLOTS; base += 3 * 64) {
+        const int arr = base / G::BC_SLOTS;
+        int pq = base - arr * G::BC_SLOTS + lane;
+        pq = pq < G::BC_PIECES ? pq : G::BC_PIECES - 1;  // padding slots repeat the last piece
+        const int r = pq * G::VEC / N, c = pq * G::VEC % N;
+        int64_t t = tt0 + r;
+        t = t < L ? t : L - 1;
+        const T *src = arr == 0 ? (const T *)a.Bt : (const T *)a.Ct;
+        T *dst = arr == 0 ? tb.B : tb.C;
+        dma16(src + (b * L + t) * N + c, lds_addr(dst + (int64_t)(base - arr * G::BC_SLOTS) * G::VEC));
+    }
+}
+
+// One stripe record: NL state words per lane (and, for an aggregate, one
+// summed-delta word per lane), epoch-tagged.
+template <int NL>
+__device__ __forceinline__ void publish_state(uint64_t *rec, int l, const float (&S)[NL], uint32_t epoch) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) st_tagged(rec + l * NL + j, S[j], epoch);
+}
+
+template <int N, int DT, bool GATE, bool SKIP>
+__global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void scan_stripe_kernel(StripeArgs a) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TCH = G::TCH, TPV = G::TPV, BREGS = G::BREGS;
+    constexpr int TT = G::TT, GROUP = G::GROUP;
+
+    __shared__ Shared<N, DT> sh;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
+    const int l = threadIdx.x & 63;
+    const int row = l >> 4, k16 = l & 15;
+    const int g = row % NGR;                            // state group of this lane
+    const int nstate0 = g * NL;
+    const int cl = w * CPW + (row / NGR) * 16 + k16;    // channel within the tile column
+    const uint32_t sel_ch = half_sel(cl);                 // lds_act selectors: this lane's channel
+    const uint32_t sel_st = half_sel(k16 % NL);           // and its Bt/Ct element (nstate0 is even)
+    const int64_t D = a.D, L = a.L;
+    const int64_t S = a.S, SL = a.SL;
+
+    const int list = blockIdx.x % kLists;
+    uint32_t *const counter = a.counters + list;
+    const uint32_t units = (uint32_t)(a.cols_per_list * S);
+    // every workgroup takes units until it is handed one past the end, so a
+    // call makes exactly (units + workgroups of the list) takes; the last one
+    // puts the counter back to zero for the next call
+    const uint32_t last_take = units + gridDim.x / kLists - 1;
+
+    while (true) {
+        if (w == 0 && l == 0) {
+            const uint32_t u = take_unit(counter);
+            if (u == last_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sh.unit = (int)u;
+        }
+        lds_barrier();
+        const uint32_t u = (uint32_t)__builtin_amdgcn_readfirstlane(sh.unit);
+        if (u >= units) break;
+        const int64_t col = list + (int64_t)kLists * (u / S);  // tile column
+        const int64_t j = u % S;                                // stripe
+        if (col >= a.ncol) {
+            lds_barrier();  // sh.unit is rewritten at the top
+            continue;
+        }
+        const int64_t b = col / a.ntpb;
+        const int64_t ch0 = (col % a.ntpb) * TCH;
+        const int64_t d = ch0 + cl;
+        const bool valid = d < D;
+        const int64_t dc = valid ? d : D - 1;
+        const int64_t t0 = j * SL;
+        const int64_t t1 = t0 + SL < L ? t0 + SL : L;
+        const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
+        const bool has_next = j + 1 < S;  // a later stripe needs this one's end state
+
+        float A2[NL];
+#pragma unroll
+        for (int q = 0; q < NL; ++q) A2[q] = a.A[dc * N + nstate0 + q] * kLog2e;
+        const float dskip = SKIP ? a.Dskip[dc] : 0.0f;
+        const int64_t rec = ((col * S + j) * kWaves + w);  // this wave's records
+
+        // Walk the stripe's tiles: PASS 1 folds (dA, dBx) from a zero start,
+        // PASS 2 runs the recurrence from h and writes y.
+        float h[NL];
+        auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
+            constexpr int PASS = decltype(pass_c)::value;
+            if (w > 0) load_tile<N, DT, GATE, PASS>(sh.buf[0], a, b, ch0, t0, w, l);
+            if (w > 0) vm_wait();
+            lds_barrier();
+            for (int i = 0; i < ntiles; ++i) {
+                TileBuf<N, DT> &tb = sh.buf[i & 1];
+                const int64_t tt0 = t0 + (int64_t)i * TT;
+                if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l);
+                const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
+                if (tail < TT) {
+                    // tokens past the end were loaded from the last token; give
+                    // them delta = 0 so that they leave the state unchanged
+                    for (int q = threadIdx.x; q < (TT - (int)tail) * TCH; q += 64 * kWaves)
+                        tb.dl[tail + q / TCH][q % TCH] = T(0.0f);
+                    lds_barrier();
+                }
+#pragma unroll 1
+                for (int tg = 0; tg < TT; tg += GROUP) {
+                    float xv[GROUP], dv[GROUP];
+#pragma unroll
+                    for (int t = 0; t < GROUP; ++t) {
+                        xv[t] = lds_act(&tb.x[tg + t][0], cl, sel_ch);
+                        dv[t] = lds_act(&tb.dl[tg + t][0], cl, sel_ch);
+                    }
+                    float Bq[BREGS], Cq[BREGS], xo[G::OWN], zo[G::OWN];
+#pragma unroll
+                    for (int q = 0; q < BREGS; ++q) {
+                        const int tw = tg + q * TPV + k16 / NL;
+                        Bq[q] = lds_act(&tb.B[tw * N], nstate0 + (k16 % NL), sel_st);
+                        if constexpr (PASS == 2) Cq[q] = lds_act(&tb.C[tw * N], nstate0 + (k16 % NL), sel_st);
+                    }
+                    if constexpr (PASS == 2) {
+                        // x and z of the tokens this lane finishes (token NGR*q + g of the group)
+#pragma unroll
+                        for (int q = 0; q < G::OWN; ++q) {
+                            const int tw = tg + NGR * q + g;
+                            xo[q] = SKIP ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
+                            zo[q] = GATE ? lds_act(&tb.z[tw][0], cl, sel_ch) : 0.0f;
+                        }
+                    }
+                    if constexpr (PASS == 1) {
+                        static_for<0, GROUP>([&](auto tc) {
+                            constexpr int t = decltype(tc)::value;
+                            const float dx = dv[t] * xv[t];
+                            dsum += dv[t];
+                            static_for<0, NL>([&](auto jc) {
+                                constexpr int q = decltype(jc)::value;
+                                const float dA = fast_exp2(dv[t] * A2[q]);
+                                st[q] = __builtin_fmaf(dA, st[q], row_bcast<(t % TPV) * NL + q>(Bq[t / TPV]) * dx);
+                            });
+                        });
+                    } else {
+                        float yp[GROUP];
+                        static_for<0, GROUP>([&](auto tc) {
+                            constexpr int t = decltype(tc)::value;
+                            const float dx = dv[t] * xv[t];
+                            yp[t] = 0.0f;
+                            static_for<0, NL>([&](auto jc) {
+                                constexpr int q = decltype(jc)::value;
+                                const float dA = fast_exp2(dv[t] * A2[q]);
+                                st[q] = __builtin_fmaf(dA, st[q], row_bcast<(t % TPV) * NL + q>(Bq[t / TPV]) * dx);
+                            });
+                            fmac_row<NL, (t % TPV) * NL>(yp[t], Cq[t / TPV], st);
+                        });
+                        // Sum the partial readouts over a channel's rows; afterwards
+                        // row r holds the finished token NGR*q + (r % NGR) of group q.
+                        float yo[G::OWN];
+                        if constexpr (NGR == 4) {
+#pragma unroll
+                            for (int q = 0; q < GROUP / 4; ++q) {
+                                float a0 = yp[4 * q + 0], a2 = yp[4 * q + 2], a1 = yp[4 * q + 1], a3 = yp[4 * q + 3];
+                                swap_halves(a0, a2);  // rows 0,1: token 0 | rows 2,3: token 2
+                                swap_halves(a1, a3);  // rows 0,1: token 1 | rows 2,3: token 3
+                                float s02 = a0 + a2, s13 = a1 + a3;
+                                swap_odd_even_rows(s02, s13);
+                                yo[q] = s02 + s13;
+                            }
+                        } else if constexpr (NGR == 2) {
+#pragma unroll
+                            for (int q = 0; q < GROUP / 2; ++q) {
+                                float a0 = yp[2 * q + 0], a1 = yp[2 * q + 1];
+                                swap_odd_even_rows(a0, a1);
+                                yo[q] = a0 + a1;
+                            }
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < GROUP; ++q) yo[q] = yp[q];
+                        }
+                        // Finish the owned tokens (D skip, silu gate) into the tile.
+#pragma unroll
+                        for (int q = 0; q < G::OWN; ++q) {
+                            const int tw = tg + NGR * q + g;
+                            float yv = yo[q];
+                            if (SKIP) yv = __builtin_fmaf(dskip, xo[q], yv);
+                            if (GATE) yv *= silu(zo[q]);
+                            st_act(&tb.dl[tw][0], cl, yv);
+                        }
+                    }
+                }
+                if constexpr (PASS == 2) {
+                    lds_barrier();
+                    // wave 0 writes the finished y tile back as whole lines
+                    if (w == 0) {
+                        using VT = uint32_t __attribute__((ext_vector_type(4)));
+                        T *yptr = (T *)a.y;
+                        for (int p = l; p < G::ACT_PIECES; p += 64) {
+                            const int r = p / G::PPR, c = (p % G::PPR) * G::VEC;
+                            if (r < tail && ch0 + c < D) {
+                                const VT v = *(const VT *)&tb.dl[r][c];
+                                *(VT *)(yptr + (b * L + tt0 + r) * D + ch0 + c) = v;
+                            }
+                        }
+                    }
+                }
+                if (w > 0) vm_wait();  // the next tile has landed
+                lds_barrier();
+            }
+        };
+
+        float agg[NL], dagg = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NL; ++q) agg[q] = 0.0f;
+        if (has_next && j > 0) {
+            walk(std::integral_constant<int, 1>{}, agg, dagg);
+            uint64_t *ar = a.agg + rec * (64 * (NL + 1));
+            publish_state<NL>(ar, l, agg, a.epoch);
+            st_tagged(ar + 64 * NL + l, dagg, a.epoch);
+        } else if (has_next) {
+            walk(std::integral_constant<int, 1>{}, agg, dagg);  // stripe 0: its end state goes out directly
+        }
+
+        // Carried-in state of this stripe.
+        if (j == 0) {
+            const float *si = a.state_in ? a.state_in + (b * D + dc) * N + nstate0 : nullptr;
+#pragma unroll
+            for (int q = 0; q < NL; ++q) h[q] = si ? si[q] : 0.0f;
+        } else {
+            // Look back over the earlier stripes of this column: the nearest
+            // one whose end state is out, with the aggregates of all stripes
+            // after it out.
+            int64_t j0 = -1;
+            long spin = 0;
+            while (true) {
+                const int64_t jj = j - 1 - l;  // stripe examined by this lane
+                bool inc = false, ag = false;
+                if (jj >= 0) {
+                    // the first word of a record stands for all of it; the
+                    // replay below still checks every word it reads
+                    const int64_t r2 = (col * S + jj) * kWaves + w;
+                    inc = (uint32_t)(ld_tagged(a.incl + r2 * (64 * NL)) >> 32) == a.epoch;
+                    ag = inc || (uint32_t)(ld_tagged(a.agg + r2 * (64 * (NL + 1))) >> 32) == a.epoch;
+                }
+                const uint64_t m_inc = __builtin_amdgcn_ballot_w64(inc);
+                const uint64_t m_agg = __builtin_amdgcn_ballot_w64(ag);
+                if (m_inc) {
+                    const int i0 = __builtin_ctzll(m_inc);
+                    const uint64_t below = i0 == 0 ? 0 : (~0ull >> (64 - i0));
+                    if ((m_agg & below) == below) {
+                        j0 = j - 1 - i0;
+                        break;
+                    }
+                }
+                if (++spin > kSpinLimit ||
+                    (spin % 64 == 0 && __builtin_amdgcn_readfirstlane(ld_flag(a.error)) != 0)) {
+                    if (l == 0) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+            if (j0 < 0) {
+#pragma unroll
+                for (int q = 0; q < NL; ++q) h[q] = 0.0f;
+            } else {
+                // Replay forward from that state with the arithmetic each
+                // stripe uses for its own end state, kReplay records per
+                // round trip.
+                const uint64_t *src = a.incl + ((col * S + j0) * kWaves + w) * (64 * NL) + l * NL;
+#pragma unroll
+                for (int q = 0; q < NL; ++q) h[q] = __uint_as_float((uint32_t)ld_valid(src + q, a.epoch));
+                for (int64_t jj = j0 + 1; jj < j; jj += kReplay) {
+                    uint64_t sv[kReplay][NL], dv2[kReplay];
+#pragma unroll
+                    for (int r = 0; r < kReplay; ++r) {
+                        if (jj + r < j) {
+                            const uint64_t *ar = a.agg + ((col * S + jj + r) * kWaves + w) * (64 * (NL + 1));
+#pragma unroll
+                            for (int q = 0; q < NL; ++q) sv[r][q] = ld_tagged(ar + l * NL + q);
+                            dv2[r] = ld_tagged(ar + 64 * NL + l);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < kReplay; ++r) {
+                        if (jj + r < j) {
+                            const uint64_t *ar = a.agg + ((col * S + jj + r) * kWaves + w) * (64 * (NL + 1));
+                            const float dd = __uint_as_float((uint32_t)recheck(dv2[r], ar + 64 * NL + l, a.epoch));
+#pragma unroll
+                            for (int q = 0; q < NL; ++q)
+                                h[q] = __builtin_fmaf(fast_exp2(A2[q] * dd), h[q],
+                                                      __uint_as_float((uint32_t)recheck(sv[r][q], ar + l * NL + q, a.epoch)));
+                        }
+                    }
+                }
+            }
+        }
+        if (has_next) {
+            // this stripe's end state, for the stripes after it
+            float e[NL];
+#pragma unroll
+            for (int q = 0; q < NL; ++q) e[q] = __builtin_fmaf(fast_exp2(A2[q] * dagg), h[q], agg[q]);
+            publish_state<NL>(a.incl + rec * (64 * NL), l, e, a.epoch);
+        }
+
+        float unused = 0.0f;
+        walk(std::integral_constant<int, 2>{}, h, unused);
+        if (!has_next && a.state_out && valid) {
+            float *so = a.state_out + (b * D + d) * N + nstate0;
+#pragma unroll
+            for (int q = 0; q < NL; ++q) so[q] = h[q];
+        }
+    }
+}
+
+template <int N, int DT, bool GATE, bool SKIP>
+hipError_t launch_stripe_typed(const StripeArgs &a, hipStream_t s) {
+    auto kern = scan_stripe_kernel<N, DT, GATE, SKIP>;
+    constexpr int kMaxDevices = 64;
+    // CU count and resident workgroups per CU, queried once per device:
+    // (cus << 32 | per_cu), 0 = not queried yet
+    static std::atomic<uint64_t> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    uint64_t packed = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (packed == 0) {
+        int cus = 0, per_cu = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kWaves, 0)) != hipSuccess) return e;
+        if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+        packed = (uint64_t)cus << 32 | (uint32_t)per_cu;
+        if (dev < kMaxDevices) cache[dev].store(packed, std::memory_order_relaxed);
+    }
+    const int cus = (int)(packed >> 32), per_cu = (int)(uint32_t)packed;
+    int64_t per_list = (int64_t)cus * per_cu / kLists;
+    const int64_t units = a.cols_per_list * a.S;
+    if (per_list > units) per_list = units;
+    if (per_list < 1) per_list = 1;
+    StripeArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel((const void *)kern, dim3((unsigned)(per_list * kLists)), dim3(64 * kWaves), params, 0, s);
+}
+
+template <int N, int DT>
+hipError_t launch_stripe_flags(const StripeArgs &a, hipStream_t s) {
+    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
+    if (gate && skip) return launch_stripe_typed<N, DT, true, true>(a, s);
+    if (gate) return launch_stripe_typed<N, DT, true, false>(a, s);
+    if (skip) return launch_stripe_typed<N, DT, false, true>(a, s);
+    return launch_stripe_typed<N, DT, false, false>(a, s);
+}
+
+template <int N>
+hipError_t launch_stripe_dtype(const StripeArgs &a, int dtype, hipStream_t s) {
+    return dtype == 0 ? launch_stripe_flags<N, 0>(a, s) : launch_stripe_flags<N, 1>(a, s);
+}
+
+template <int N, int DT>
+void stripe_geometry(int64_t batch, int64_t L, int64_t D, StripePlan *p) {
+    using G = Geo<N, DT>;
+    p->nl = G::NL;
+    p->tch = G::TCH;
+    p->tt = G::TT;
+    p->vec = G::VEC;
+    p->ntpb = (D + G::TCH - 1) / G::TCH;
+    p->ncol = batch * p->ntpb;
+    p->cols_per_list = (p->ncol + kLists - 1) / kLists;
+    // stripes per column: enough units to fill the planned workgroup slots
+    const int64_t tiles = (L + G::TT - 1) / G::TT;
+    int64_t S = kSlotsPerList / (p->cols_per_list > 0 ? p->cols_per_list : 1);
+    if (S > 64) S = 64;  // the look-back examines at most 64 earlier stripes at once
+    if (S > tiles) S = tiles;
+    if (S < 1) S = 1;
+    const int64_t tiles_per_stripe = (tiles + S - 1) / S;
+    p->SL = tiles_per_stripe * G::TT;
+    p->S = tiles > 0 ? (tiles + tiles_per_stripe - 1) / tiles_per_stripe : 1;
+}
+
+}  // namespace
+
+bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, StripePlan *p) {
+    const bool bf = dtype == 1;
+    switch (N) {
+        case 1: bf ? stripe_geometry<1, 1>(batch, L, D, p) : stripe_geometry<1, 0>(batch, L, D, p); break;
+        case 2: bf ? stripe_geometry<2, 1>(batch, L, D, p) : stripe_geometry<2, 0>(batch, L, D, p); break;
+        case 4: bf ? stripe_geometry<4, 1>(batch, L, D, p) : stripe_geometry<4, 0>(batch, L, D, p); break;
+        case 8: bf ? stripe_geometry<8, 1>(batch, L, D, p) : stripe_geometry<8, 0>(batch, L, D, p); break;
+        case 16: bf ? stripe_geometry<16, 1>(batch, L, D, p) : stripe_geometry<16, 0>(batch, L, D, p); break;
+        default: return false;
+    }
+    // Tiles are read as 16-byte pieces: channel rows must be whole pieces
+    // (and at least one), and Bt/Ct rows at least one piece.
+    const int esz = bf ? 2 : 4;
+    p->supported = (D % p->vec == 0) && (D >= p->vec) && (N * esz >= 16) &&
+                   (p->cols_per_list * p->S < (int64_t(1) << 30));
+    // header (error word, unit counters) | incl | agg: per record 64 lanes x
+    // NL end-state words, and 64 x NL state words followed by 64 summed-delta
+    // words; one record per (tile column, stripe, wave)
+    const int64_t recs = p->S > 1 ? p->ncol * p->S * kWaves : 0;
+    size_t off = 256;
+    p->off_incl = off;
+    off += (size_t)recs * 64 * p->nl * sizeof(uint64_t);
+    p->off_agg = off;
+    off += (size_t)recs * 64 * (p->nl + 1) * sizeof(uint64_t);
+    p->bytes = (off + 255) / 256 * 256;
+    return true;
+}
+
+hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s) {
+    switch (N) {
+        case 1: return launch_stripe_dtype<1>(a, dtype, s);
+        case 2: return launch_stripe_dtype<2>(a, dtype, s);
+        case 4: return launch_stripe_dtype<4>(a, dtype, s);
+        case 8: return launch_stripe_dtype<8>(a, dtype, s);
+        case 16: return launch_stripe_dtype<16>(a, dtype, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssm
