@@ -175,6 +175,7 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.ntpb = p.ntpb;
         a.ncol = p.ncol;
         a.cols_per_list = p.cols_per_list;
+        a.n_whole = p.n_whole;
         a.S = p.S;
         a.SL = p.SL;
         a.epoch = next_epoch();

@@ -55,7 +55,8 @@ struct StripeArgs {
     int64_t ntpb;           // tile columns per batch row
     int64_t ncol;           // tile columns
     int64_t cols_per_list;  // tile columns per unit list
-    int64_t S;              // stripes per tile column
+    int64_t n_whole;        // columns per list run as one whole-sequence unit each
+    int64_t S;              // stripes per remaining column
     int64_t SL;             // tokens per stripe (the last one may be shorter)
     uint32_t epoch;         // value that marks this call's published words
     uint32_t *error;        // set when a look-back wait timed out
@@ -65,7 +66,7 @@ struct StripeArgs {
 };
 
 struct StripePlan {
-    int64_t nl, tch, tt, vec, ntpb, ncol, cols_per_list, S, SL;
+    int64_t nl, tch, tt, vec, ntpb, ncol, cols_per_list, n_whole, S, SL;
     bool supported;     // shape meets the tile-load requirements
     size_t off_incl, off_agg, bytes;
 };

@@ -178,11 +178,11 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
     const uint32_t sel_ch = half_sel(cl);                 // lds_act selectors: this lane's channel
     const uint32_t sel_st = half_sel(k16 % NL);           // and its Bt/Ct element (nstate0 is even)
     const int64_t D = a.D, L = a.L;
-    const int64_t S = a.S, SL = a.SL;
+    const int64_t n_whole = a.n_whole, n_split = a.cols_per_list - a.n_whole;
 
     const int list = blockIdx.x % kLists;
     uint32_t *const counter = a.counters + list;
-    const uint32_t units = (uint32_t)(a.cols_per_list * S);
+    const uint32_t units = (uint32_t)(n_whole + n_split * a.S);
     // every workgroup takes units until it is handed one past the end, so a
     // call makes exactly (units + workgroups of the list) takes; the last one
     // puts the counter back to zero for the next call
@@ -197,8 +197,14 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         lds_barrier();
         const uint32_t u = (uint32_t)__builtin_amdgcn_readfirstlane(sh.unit);
         if (u >= units) break;
-        const int64_t col = list + (int64_t)kLists * (u / S);  // tile column
-        const int64_t j = u % S;                                // stripe
+        // The list's first n_whole columns are whole-sequence units; each of
+        // the others is cut into S stripes (which fill the last round).
+        const bool whole = u < n_whole;
+        const int64_t S = whole ? 1 : a.S;
+        const int64_t SL = whole ? L : a.SL;
+        const int64_t cs = whole ? 0 : (u - n_whole) / S;       // split column index
+        const int64_t j = whole ? 0 : (u - n_whole) % S;        // stripe
+        const int64_t col = list + (int64_t)kLists * (whole ? u : n_whole + cs);  // tile column
         if (col >= a.ncol) {
             lds_barrier();  // sh.unit is rewritten at the top
             continue;
@@ -217,19 +223,50 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
 #pragma unroll
         for (int q = 0; q < NL; ++q) A2[q] = a.A[dc * N + nstate0 + q] * kLog2e;
         const float dskip = SKIP ? a.Dskip[dc] : 0.0f;
-        const int64_t rec = ((col * S + j) * kWaves + w);  // this wave's records
+        // records of stripe jj of this column, for this wave
+        const int64_t rec0 = ((int64_t)list * n_split + cs) * S;
+        auto rec_of = [&](int64_t jj) { return (rec0 + jj) * kWaves + w; };
+        const int64_t rec = rec_of(j);
 
         // Walk the stripe's tiles: PASS 1 folds (dA, dBx) from a zero start,
         // PASS 2 runs the recurrence from h and writes y.
         float h[NL];
-        auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
+        // The finished y of tile i (pass 2): every wave writes a share of it back
+        // as whole lines from the tile's delta area.
+        auto store_y = [&](const TileBuf<N, DT> &tb, int i) {
+            using VT = uint32_t __attribute__((ext_vector_type(4)));
+            const int64_t tt0 = t0 + (int64_t)i * TT;
+            const int64_t rows = t1 - tt0;  // tokens of the tile inside the stripe
+            T *yptr = (T *)a.y;
+#pragma unroll
+            for (int p = threadIdx.x; p < G::ACT_PIECES; p += 64 * kWaves) {
+                const int r = p / G::PPR, c = (p % G::PPR) * G::VEC;
+                if (r < rows && ch0 + c < D) {
+                    const VT v = *(const VT *)&tb.dl[r][c];
+                    *(VT *)(yptr + (b * L + tt0 + r) * D + ch0 + c) = v;
+                }
+            }
+        };
+        // First tile of a pass, loaded ahead (before the look-back, for pass 2).
+        auto prefetch = [&](auto pass_c) {
             constexpr int PASS = decltype(pass_c)::value;
             if (w > 0) load_tile<N, DT, GATE, PASS>(sh.buf[0], a, b, ch0, t0, w, l);
-            if (w > 0) vm_wait();
+        };
+        auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
+            constexpr int PASS = decltype(pass_c)::value;
+            if (w > 0) vm_wait();  // the first tile (prefetch) has landed
             lds_barrier();
             for (int i = 0; i < ntiles; ++i) {
                 TileBuf<N, DT> &tb = sh.buf[i & 1];
                 const int64_t tt0 = t0 + (int64_t)i * TT;
+                if constexpr (PASS == 2) {
+                    // y of the previous tile goes out now, so that the stores
+                    // complete behind this tile's scan; its buffer is loaded next
+                    if (i > 0) {
+                        store_y(sh.buf[(i - 1) & 1], i - 1);
+                        lds_barrier();
+                    }
+                }
                 if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l);
                 const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
                 if (tail < TT) {
@@ -322,37 +359,26 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         }
                     }
                 }
-                if constexpr (PASS == 2) {
-                    lds_barrier();
-                    // wave 0 writes the finished y tile back as whole lines
-                    if (w == 0) {
-                        using VT = uint32_t __attribute__((ext_vector_type(4)));
-                        T *yptr = (T *)a.y;
-                        for (int p = l; p < G::ACT_PIECES; p += 64) {
-                            const int r = p / G::PPR, c = (p % G::PPR) * G::VEC;
-                            if (r < tail && ch0 + c < D) {
-                                const VT v = *(const VT *)&tb.dl[r][c];
-                                *(VT *)(yptr + (b * L + tt0 + r) * D + ch0 + c) = v;
-                            }
-                        }
-                    }
-                }
-                if (w > 0) vm_wait();  // the next tile has landed
+                vm_wait();  // the next tile has landed (and this wave's earlier y stores are out)
                 lds_barrier();
             }
+            if constexpr (PASS == 2) store_y(sh.buf[(ntiles - 1) & 1], ntiles - 1);
         };
 
         float agg[NL], dagg = 0.0f;
 #pragma unroll
         for (int q = 0; q < NL; ++q) agg[q] = 0.0f;
         if (has_next && j > 0) {
+            prefetch(std::integral_constant<int, 1>{});
             walk(std::integral_constant<int, 1>{}, agg, dagg);
             uint64_t *ar = a.agg + rec * (64 * (NL + 1));
             publish_state<NL>(ar, l, agg, a.epoch);
             st_tagged(ar + 64 * NL + l, dagg, a.epoch);
         } else if (has_next) {
+            prefetch(std::integral_constant<int, 1>{});
             walk(std::integral_constant<int, 1>{}, agg, dagg);  // stripe 0: its end state goes out directly
         }
+        prefetch(std::integral_constant<int, 2>{});  // lands during the look-back
 
         // Carried-in state of this stripe.
         if (j == 0) {
@@ -371,7 +397,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                 if (jj >= 0) {
                     // the first word of a record stands for all of it; the
                     // replay below still checks every word it reads
-                    const int64_t r2 = (col * S + jj) * kWaves + w;
+                    const int64_t r2 = rec_of(jj);
                     inc = (uint32_t)(ld_tagged(a.incl + r2 * (64 * NL)) >> 32) == a.epoch;
                     ag = inc || (uint32_t)(ld_tagged(a.agg + r2 * (64 * (NL + 1))) >> 32) == a.epoch;
                 }
@@ -399,7 +425,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                 // Replay forward from that state with the arithmetic each
                 // stripe uses for its own end state, kReplay records per
                 // round trip.
-                const uint64_t *src = a.incl + ((col * S + j0) * kWaves + w) * (64 * NL) + l * NL;
+                const uint64_t *src = a.incl + rec_of(j0) * (64 * NL) + l * NL;
 #pragma unroll
                 for (int q = 0; q < NL; ++q) h[q] = __uint_as_float((uint32_t)ld_valid(src + q, a.epoch));
                 for (int64_t jj = j0 + 1; jj < j; jj += kReplay) {
@@ -407,7 +433,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
 #pragma unroll
                     for (int r = 0; r < kReplay; ++r) {
                         if (jj + r < j) {
-                            const uint64_t *ar = a.agg + ((col * S + jj + r) * kWaves + w) * (64 * (NL + 1));
+                            const uint64_t *ar = a.agg + rec_of(jj + r) * (64 * (NL + 1));
 #pragma unroll
                             for (int q = 0; q < NL; ++q) sv[r][q] = ld_tagged(ar + l * NL + q);
                             dv2[r] = ld_tagged(ar + 64 * NL + l);
@@ -416,7 +442,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
 #pragma unroll
                     for (int r = 0; r < kReplay; ++r) {
                         if (jj + r < j) {
-                            const uint64_t *ar = a.agg + ((col * S + jj + r) * kWaves + w) * (64 * (NL + 1));
+                            const uint64_t *ar = a.agg + rec_of(jj + r) * (64 * (NL + 1));
                             const float dd = __uint_as_float((uint32_t)recheck(dv2[r], ar + 64 * NL + l, a.epoch));
 #pragma unroll
                             for (int q = 0; q < NL; ++q)
@@ -466,7 +492,7 @@ hipError_t launch_stripe_typed(const StripeArgs &a, hipStream_t s) {
     }
     const int cus = (int)(packed >> 32), per_cu = (int)(uint32_t)packed;
     int64_t per_list = (int64_t)cus * per_cu / kLists;
-    const int64_t units = a.cols_per_list * a.S;
+    const int64_t units = a.n_whole + (a.cols_per_list - a.n_whole) * a.S;
     if (per_list > units) per_list = units;
     if (per_list < 1) per_list = 1;
     StripeArgs args = a;
@@ -498,15 +524,21 @@ void stripe_geometry(int64_t batch, int64_t L, int64_t D, StripePlan *p) {
     p->ntpb = (D + G::TCH - 1) / G::TCH;
     p->ncol = batch * p->ntpb;
     p->cols_per_list = (p->ncol + kLists - 1) / kLists;
-    // stripes per column: enough units to fill the planned workgroup slots
+    // Columns that fill whole rounds of the planned workgroup slots run as
+    // whole-sequence units; the rest are cut into S stripes each, so that
+    // the last round is full too.
+    const int64_t C = p->cols_per_list;
     const int64_t tiles = (L + G::TT - 1) / G::TT;
-    int64_t S = kSlotsPerList / (p->cols_per_list > 0 ? p->cols_per_list : 1);
+    const int64_t rem = C >= kSlotsPerList ? C % kSlotsPerList : C;
+    int64_t S = rem > 0 ? kSlotsPerList / rem : 1;
     if (S > 64) S = 64;  // the look-back examines at most 64 earlier stripes at once
     if (S > tiles) S = tiles;
     if (S < 1) S = 1;
     const int64_t tiles_per_stripe = (tiles + S - 1) / S;
+    S = tiles > 0 ? (tiles + tiles_per_stripe - 1) / tiles_per_stripe : 1;
     p->SL = tiles_per_stripe * G::TT;
-    p->S = tiles > 0 ? (tiles + tiles_per_stripe - 1) / tiles_per_stripe : 1;
+    p->S = S;
+    p->n_whole = S > 1 ? C - rem : C;
 }
 
 }  // namespace
@@ -526,10 +558,11 @@ bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, Stri
     const int esz = bf ? 2 : 4;
     p->supported = (D % p->vec == 0) && (D >= p->vec) && (N * esz >= 16) &&
                    (p->cols_per_list * p->S < (int64_t(1) << 30));
+    const int64_t n_split = p->cols_per_list - p->n_whole;
     // header (error word, unit counters) | incl | agg: per record 64 lanes x
     // NL end-state words, and 64 x NL state words followed by 64 summed-delta
     // words; one record per (tile column, stripe, wave)
-    const int64_t recs = p->S > 1 ? p->ncol * p->S * kWaves : 0;
+    const int64_t recs = p->S > 1 ? kLists * n_split * p->S * kWaves : 0;
     size_t off = 256;
     p->off_incl = off;
     off += (size_t)recs * 64 * p->nl * sizeof(uint64_t);
