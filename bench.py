@@ -38,7 +38,7 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 # delta*A (mul), exp (a transcendental, issued at half rate: 2 slots),
 # B*(delta*x) (mul), dA*h + dBx (fma), C*h accumulated (fma).
 SCAN_SLOTS_PER_ELEM = 6
-SCAN_KERNEL = "scan_lb_kernel"
+SCAN_KERNEL = "scan_stripe_kernel"
 STEP_KERNEL = "step_kernel"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 

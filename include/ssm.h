@@ -25,8 +25,10 @@
  *
  * Conventions for every entry point:
  *  - Pointers are device pointers (hipMalloc'd or equivalent), owned by the
- *    caller. The library allocates nothing, keeps no per-call state and may
- *    be called from several host threads.
+ *    caller. The library allocates nothing and may be called from several
+ *    host threads; its only state is a process-wide call counter (it marks the
+ *    words a call publishes in the workspace) and, per device, the CU count
+ *    and resident workgroups of each kernel, queried once.
  *  - Tensors are dense, row-major, in the shapes listed; D (channels) is the
  *    fastest axis of x, delta, z and y; N is the fastest axis of Bt, Ct, A
  *    and the state. Every base pointer must be 16-byte aligned.
@@ -75,15 +77,16 @@ const char *ssm_status_string(int status);
 const char *ssm_version(void);
 
 /*
- * Scratch bytes ssm_scan_fwd needs for these sizes (0 when none). Sequences
- * longer than one chunk are scanned by many workgroups at once; the workspace
- * is where each chunk publishes its summary (the end state from a zero start
- * and its summed delta) and its final state for the chunks after it, each
- * with a flag word.
+ * Scratch bytes ssm_scan_fwd needs for these sizes (0 when none). The
+ * workspace holds the counters that hand work to the workgroups and, when a
+ * sequence is cut into stripes scanned at the same time, each stripe's
+ * summary (its end state from a zero start and its summed delta) and its end
+ * state for the stripes after it, as words tagged with the call.
  *
  * The workspace must be zero-filled before its first use. After that it may
  * be reused by later calls of any size without clearing, as long as nothing
- * else writes to it in between; each call marks its flags with a new value.
+ * else writes to it in between: each call tags its words with a new value and
+ * leaves its counters at zero.
  * Calls that share a workspace must not run at the same time. Returns 0 for
  * invalid sizes.
  */

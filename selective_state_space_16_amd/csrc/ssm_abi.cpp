@@ -33,8 +33,8 @@ int64_t checked_mul3(int64_t a, int64_t b, int64_t c) {
 size_t round_up256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Both scans keep a 256-byte header at the start of the workspace: the first
-// word reports a timed-out look-back wait; bytes 64..127 hold the single-pass
-// scan's eight tile counters.
+// word reports a timed-out wait for another workgroup's words; bytes 64..95
+// hold the stripe scan's eight unit counters.
 constexpr size_t kHeader = 256;
 
 // Workspace of the chunked three-launch scan:
@@ -46,12 +46,6 @@ size_t twopass_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t
            round_up256((size_t)batch * *K * D * sizeof(float));
 }
 
-// Workspace of the single-pass look-back scan.
-size_t lb_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, ssm::LbPlan *p) {
-    if (!ssm::lb_plan(batch, L, D, N, dtype, p)) return 0;
-    return p->bytes;
-}
-
 // Workspace of the stripe scan.
 size_t stripe_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, ssm::StripePlan *p) {
     if (!ssm::stripe_plan(batch, L, D, N, dtype, p)) return 0;
@@ -59,32 +53,23 @@ size_t stripe_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, int dtyp
 }
 
 // Which scan runs. The stripe scan reads 16-byte pieces of channel rows and
-// Bt/Ct rows; shapes it cannot take run the chunked three-launch scan.
-// SSM_SCAN_IMPL=twopass|lb|stripe picks one for comparison (if the shape
-// allows it).
-enum class Impl { kTwopass, kLb, kStripe };
+// Bt/Ct rows; shapes it cannot take run the chunked three-launch scan, which
+// SSM_SCAN_IMPL=twopass also selects (for comparison).
+enum class Impl { kTwopass, kStripe };
 
 Impl choose_impl(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     ssm::StripePlan sp;
-    ssm::LbPlan lp;
     const bool stripe_ok = ssm::stripe_plan(batch, L, D, N, dtype, &sp) && sp.supported;
-    const bool lb_ok = ssm::lb_plan(batch, L, D, N, dtype, &lp) && lp.supported;
     const char *e = getenv("SSM_SCAN_IMPL");
     if (e && strcmp(e, "twopass") == 0) return Impl::kTwopass;
-    if (e && strcmp(e, "lb") == 0 && lb_ok) return Impl::kLb;
-    if (stripe_ok) return Impl::kStripe;
-    return Impl::kTwopass;
+    return stripe_ok ? Impl::kStripe : Impl::kTwopass;
 }
 
 size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     int64_t K, Lc;
-    ssm::LbPlan lp;
     ssm::StripePlan sp;
-    switch (choose_impl(batch, L, D, N, dtype)) {
-        case Impl::kLb: return lb_workspace(batch, L, D, N, dtype, &lp);
-        case Impl::kStripe: return stripe_workspace(batch, L, D, N, dtype, &sp);
-        default: return twopass_workspace(batch, L, D, N, &K, &Lc);
-    }
+    return choose_impl(batch, L, D, N, dtype) == Impl::kStripe ? stripe_workspace(batch, L, D, N, dtype, &sp)
+                                                               : twopass_workspace(batch, L, D, N, &K, &Lc);
 }
 
 // Distinct nonzero value per call; marks the words a call publishes in the workspace.
@@ -186,31 +171,7 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.agg = (uint64_t *)(w + p.off_agg);
         return ssm::launch_scan_stripe(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
     }
-    if (impl == Impl::kTwopass) {
-        ssm::ScanArgs a{};
-        a.batch = batch;
-        a.L = L;
-        a.D = D;
-        a.x = x;
-        a.delta = delta;
-        a.Bt = Bt;
-        a.Ct = Ct;
-        a.z = z;
-        a.A = A;
-        a.Dskip = Dskip;
-        a.state_in = state_in;
-        a.state_out = state_out;
-        a.y = y;
-        if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
-            char *w = (char *)workspace + kHeader;
-            a.ws_state = (float *)w;
-            a.ws_dsum = (float *)(w + round_up256((size_t)batch * a.K * D * N * sizeof(float)));
-        }
-        return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
-    }
-    ssm::LbPlan p;
-    const size_t lbw = lb_workspace(batch, L, D, N, dtype, &p);
-    ssm::LbArgs a{};
+    ssm::ScanArgs a{};
     a.batch = batch;
     a.L = L;
     a.D = D;
@@ -224,17 +185,12 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.state_in = state_in;
     a.state_out = state_out;
     a.y = y;
-    a.K = p.K;
-    a.nicol = p.nicol;
-    a.epoch = next_epoch();
-    if (lbw > 0) {
-        char *w = (char *)workspace;
-        a.error = (uint32_t *)w;
-        a.tiles = (uint32_t *)(w + 64);
-        a.incl = (uint64_t *)(w + p.off_incl);
-        a.agg = (uint64_t *)(w + p.off_agg);
+    if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
+        char *w = (char *)workspace + kHeader;
+        a.ws_state = (float *)w;
+        a.ws_dsum = (float *)(w + round_up256((size_t)batch * a.K * D * N * sizeof(float)));
     }
-    return ssm::launch_scan_lb(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,

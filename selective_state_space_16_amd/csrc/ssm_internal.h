@@ -20,31 +20,6 @@ struct ScanArgs {
     int64_t Lc;        // tokens per chunk (the last chunk may be shorter)
 };
 
-// Single-pass scan with a decoupled look-back between chunks.
-struct LbArgs {
-    int64_t batch, L, D;
-    const void *x, *delta, *Bt, *Ct, *z;
-    const float *A, *Dskip, *state_in;
-    float *state_out;
-    void *y;
-    int64_t K;          // chunks per sequence
-    int64_t nicol;      // item columns (batch rows x channel blocks)
-    uint32_t epoch;     // value that marks this call's published words
-    int agg_early;      // every item publishes its aggregate right after phase A
-    uint32_t *error;    // set when a look-back wait timed out
-    uint32_t *tiles;    // 8 tile counters (one per XCD list), zero between calls
-    uint64_t *incl;     // per item: inclusive end state, epoch-tagged words
-    uint64_t *agg;      // per item: end state from a zero start and summed delta, epoch-tagged words
-};
-
-// Geometry and workspace layout of the look-back scan for one problem size.
-struct LbPlan {
-    int64_t nl, nicol, K, chunk, vec;
-    int64_t tiles_per_list;  // tiles each of the 8 per-XCD lists hands out
-    bool supported;     // shape meets the tile-load requirements
-    size_t off_incl, off_agg, bytes;
-};
-
 // Stripe scan: every wave walks its channels along a stripe of the sequence.
 struct StripeArgs {
     int64_t batch, L, D;
@@ -82,11 +57,9 @@ struct StepArgs {
 // Sequence split used for a scan of these sizes (deterministic).
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);
 
-bool lb_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, LbPlan *p);
 bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, StripePlan *p);
 
 // Launchers; return hipSuccess or the launch error.
-hipError_t launch_scan_lb(const LbArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
