@@ -110,6 +110,53 @@ __device__ __forceinline__ float lds_act(const uint16_t *row, int i, uint32_t se
 // 3,2 (odd) of the word into bytes 3,2 of the result, zeros below.
 __device__ __forceinline__ uint32_t half_sel(int i) { return (i & 1) ? 0x03020c0cu : 0x01000c0cu; }
 
+// bfloat16 reads of an LDS tile straight into the high half of a register
+// whose low half is zero (it last held a value read this way, or 0.0f): the
+// register then holds the exact float, with no VALU work (the compiler does
+// not form these loads itself). Each block waits for its own loads, so no
+// register is read while its load is in flight. `a` and `b` are per-lane LDS
+// byte addresses; value k is read at a + k*STRIDE.
+template <int STRIDE>
+__device__ __forceinline__ void lds_bf16_8x2(float (&va)[8], float (&vb)[8], uint32_t a, uint32_t b) {
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %16 offset:%18\n\tds_read_u16_d16_hi %1, %16 offset:%19\n\t"
+        "ds_read_u16_d16_hi %2, %16 offset:%20\n\tds_read_u16_d16_hi %3, %16 offset:%21\n\t"
+        "ds_read_u16_d16_hi %4, %16 offset:%22\n\tds_read_u16_d16_hi %5, %16 offset:%23\n\t"
+        "ds_read_u16_d16_hi %6, %16 offset:%24\n\tds_read_u16_d16_hi %7, %16 offset:%25\n\t"
+        "ds_read_u16_d16_hi %8, %17 offset:%18\n\tds_read_u16_d16_hi %9, %17 offset:%19\n\t"
+        "ds_read_u16_d16_hi %10, %17 offset:%20\n\tds_read_u16_d16_hi %11, %17 offset:%21\n\t"
+        "ds_read_u16_d16_hi %12, %17 offset:%22\n\tds_read_u16_d16_hi %13, %17 offset:%23\n\t"
+        "ds_read_u16_d16_hi %14, %17 offset:%24\n\tds_read_u16_d16_hi %15, %17 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]),
+          "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]), "+v"(vb[4]), "+v"(vb[5]), "+v"(vb[6]), "+v"(vb[7])
+        : "v"(a), "v"(b), "i"(0), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE),
+          "i"(6 * STRIDE), "i"(7 * STRIDE)
+        : "memory");
+}
+// Two values from each of up to four addresses (value k at addr + k*STRIDE):
+// pairs from `a` and `b` with stride SA, pairs from `c` and `d` with stride SC.
+template <int SA, int SC>
+__device__ __forceinline__ void lds_bf16_2x4(float (&va)[2], float (&vb)[2], float (&vc)[2], float (&vd)[2],
+                                             uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %8 offset:0\n\tds_read_u16_d16_hi %1, %8 offset:%12\n\t"
+        "ds_read_u16_d16_hi %2, %9 offset:0\n\tds_read_u16_d16_hi %3, %9 offset:%12\n\t"
+        "ds_read_u16_d16_hi %4, %10 offset:0\n\tds_read_u16_d16_hi %5, %10 offset:%13\n\t"
+        "ds_read_u16_d16_hi %6, %11 offset:0\n\tds_read_u16_d16_hi %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(va[0]), "+v"(va[1]), "+v"(vb[0]), "+v"(vb[1]), "+v"(vc[0]), "+v"(vc[1]), "+v"(vd[0]), "+v"(vd[1])
+        : "v"(a), "v"(b), "v"(c), "v"(d), "i"(SA), "i"(SC)
+        : "memory");
+}
+template <int SA>
+__device__ __forceinline__ void lds_bf16_2(float (&va)[2], uint32_t a) {
+    asm volatile("ds_read_u16_d16_hi %0, %2 offset:0\n\tds_read_u16_d16_hi %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                 : "+v"(va[0]), "+v"(va[1])
+                 : "v"(a), "i"(SA)
+                 : "memory");
+}
+
 __device__ __forceinline__ uint32_t take_unit(uint32_t *ctr) {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -254,6 +301,16 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         };
         auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
             constexpr int PASS = decltype(pass_c)::value;
+            // bfloat16 groups of 8 tokens with two broadcast registers and two
+            // finished tokens per lane take the high-half loads
+            constexpr bool kHiLoads = DT == 1 && GROUP == 8 && BREGS == 2 && G::OWN == 2;
+            float xv[GROUP], dv[GROUP], Bq[BREGS], Cq[BREGS], xo[G::OWN], zo[G::OWN];
+#pragma unroll
+            for (int t = 0; t < GROUP; ++t) xv[t] = dv[t] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < BREGS; ++q) Bq[q] = Cq[q] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < G::OWN; ++q) xo[q] = zo[q] = 0.0f;
             if (w > 0) vm_wait();  // the first tile (prefetch) has landed
             lds_barrier();
             for (int i = 0; i < ntiles; ++i) {
@@ -278,26 +335,40 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                 }
 #pragma unroll 1
                 for (int tg = 0; tg < TT; tg += GROUP) {
-                    float xv[GROUP], dv[GROUP];
+                    if constexpr (kHiLoads) {
+                        // bfloat16: loads into the high halves of the registers
+                        // that held the previous group's values
+                        constexpr int ROWB = TCH * 2, BCB = N * 2;
+                        lds_bf16_8x2<ROWB>(xv, dv, (uint32_t)(uintptr_t)&tb.x[tg][cl], (uint32_t)(uintptr_t)&tb.dl[tg][cl]);
+                        const uint32_t bq = (uint32_t)(uintptr_t)&tb.B[(tg + k16 / NL) * N + nstate0 + (k16 % NL)];
+                        const uint32_t cq = (uint32_t)(uintptr_t)&tb.C[(tg + k16 / NL) * N + nstate0 + (k16 % NL)];
+                        if constexpr (PASS == 2) {
+                            const uint32_t xa = (uint32_t)(uintptr_t)&tb.x[tg + g][cl];
+                            const uint32_t za = (uint32_t)(uintptr_t)&tb.z[tg + g][cl];
+                            lds_bf16_2x4<TPV * BCB, NGR * ROWB>(Bq, Cq, xo, zo, bq, cq, xa, za);
+                        } else {
+                            lds_bf16_2<TPV * BCB>(Bq, bq);
+                        }
+                    } else {
 #pragma unroll
-                    for (int t = 0; t < GROUP; ++t) {
-                        xv[t] = lds_act(&tb.x[tg + t][0], cl, sel_ch);
-                        dv[t] = lds_act(&tb.dl[tg + t][0], cl, sel_ch);
-                    }
-                    float Bq[BREGS], Cq[BREGS], xo[G::OWN], zo[G::OWN];
+                        for (int t = 0; t < GROUP; ++t) {
+                            xv[t] = lds_act(&tb.x[tg + t][0], cl, sel_ch);
+                            dv[t] = lds_act(&tb.dl[tg + t][0], cl, sel_ch);
+                        }
 #pragma unroll
-                    for (int q = 0; q < BREGS; ++q) {
-                        const int tw = tg + q * TPV + k16 / NL;
-                        Bq[q] = lds_act(&tb.B[tw * N], nstate0 + (k16 % NL), sel_st);
-                        if constexpr (PASS == 2) Cq[q] = lds_act(&tb.C[tw * N], nstate0 + (k16 % NL), sel_st);
-                    }
-                    if constexpr (PASS == 2) {
-                        // x and z of the tokens this lane finishes (token NGR*q + g of the group)
+                        for (int q = 0; q < BREGS; ++q) {
+                            const int tw = tg + q * TPV + k16 / NL;
+                            Bq[q] = lds_act(&tb.B[tw * N], nstate0 + (k16 % NL), sel_st);
+                            if constexpr (PASS == 2) Cq[q] = lds_act(&tb.C[tw * N], nstate0 + (k16 % NL), sel_st);
+                        }
+                        if constexpr (PASS == 2) {
+                            // x and z of the tokens this lane finishes (token NGR*q + g of the group)
 #pragma unroll
-                        for (int q = 0; q < G::OWN; ++q) {
-                            const int tw = tg + NGR * q + g;
-                            xo[q] = SKIP ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
-                            zo[q] = GATE ? lds_act(&tb.z[tw][0], cl, sel_ch) : 0.0f;
+                            for (int q = 0; q < G::OWN; ++q) {
+                                const int tw = tg + NGR * q + g;
+                                xo[q] = SKIP ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
+                                zo[q] = GATE ? lds_act(&tb.z[tw][0], cl, sel_ch) : 0.0f;
+                            }
                         }
                     }
                     if constexpr (PASS == 1) {
