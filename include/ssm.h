@@ -87,8 +87,10 @@ const char *ssm_version(void);
  * be reused by later calls of any size without clearing, as long as nothing
  * else writes to it in between: each call tags its words with a new value and
  * leaves its counters at zero.
- * Calls that share a workspace must not run at the same time. Returns 0 for
- * invalid sizes.
+ * Calls that share a workspace must not run at the same time. The tag is
+ * fixed when a call is issued, so a scan that uses a workspace must not be
+ * captured into a HIP graph and replayed: a replay would reuse the tag.
+ * Returns 0 for invalid sizes.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
 
@@ -132,6 +134,8 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
  *   y             (batch, D)     dtype      output (written)
  *
  * Equivalent to ssm_scan_fwd with L = 1 and state_in = state_out = state.
+ * Uses no workspace and keeps nothing between calls, so a sequence of steps
+ * may be captured into a HIP graph and replayed.
  */
 int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
              const void *x, const void *delta, const float *A,

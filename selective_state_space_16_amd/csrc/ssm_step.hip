@@ -2,13 +2,18 @@
 //
 // The step reads and rewrites the whole (batch, D, N) float state, so it is
 // bound by memory traffic ("Notas sobre Mamba", section "Formulação MIMO":
-// decode cost is governed by the state read and written each token). Each
-// lane owns NPL = min(N, 4) consecutive state values of one channel and
-// moves them as one 16-byte access; LPC = N / NPL lanes share a channel, so a
-// wave covers 64 / LPC channels of one batch row and its state accesses are
-// one contiguous span. The partial readouts of a channel's lanes are summed
-// with DPP quad permutes; the first lane of the group finishes the channel
-// (D skip, silu gate) and stores y.
+// decode cost is governed by the state read and written each token).
+//
+// A wave serves 64 consecutive channels of kRows batch rows. Their state is
+// one contiguous span of 64 * N floats per row, read and written as LPC = N /
+// NPL wave-wide 16-byte accesses (NPL = min(N, 4) floats per lane): in access
+// q, lane l holds states n0 = (l % LPC) * NPL .. + NPL of channel
+// q * (64 / LPC) + l / LPC. The per-channel inputs (x, delta, z) and the output
+// y move as one 64-lane access per row, lane l owning channel l; the lanes
+// that work on a channel fetch its x and delta from lane l with ds_bpermute,
+// and the channel's readout, summed over its LPC lanes with DPP quad
+// permutes, comes back the same way. A is read once for the kRows rows, and
+// every load of a row group is issued before the first use.
 #include "ssm_common.h"
 #include "ssm_internal.h"
 
@@ -17,6 +22,10 @@ namespace ssm {
 namespace {
 
 constexpr int kStepBlock = 256;
+constexpr int kWaveCh = 64;  // channels per wave
+constexpr int kBlockCh = kWaveCh * (kStepBlock / 64);
+constexpr int kRows = 2;  // batch rows per lane
+constexpr unsigned kMaxGridY = 65535;
 
 template <int NPL> struct Vec;
 template <> struct Vec<1> { using T = float; };
@@ -35,8 +44,31 @@ __device__ __forceinline__ void st_vec(float *p, const float (&r)[NPL]) {
     *(typename Vec<NPL>::T *)p = v;
 }
 
+// NPL consecutive B or C values as one access. bfloat16 rows are kept as raw
+// 16-bit patterns until use.
+template <int NPL> struct Raw16;
+template <> struct Raw16<1> { using T = uint16_t; };
+template <> struct Raw16<2> { using T = uint32_t; };
+template <> struct Raw16<4> { using T = uint2; };
+
+template <int NPL, int DT> struct BcRaw {
+    using T = typename Vec<NPL>::T;
+    static __device__ __forceinline__ T load(const float *p) { return *(const T *)p; }
+    static __device__ __forceinline__ void widen(const T &v, float (&r)[NPL]) { __builtin_memcpy(r, &v, sizeof(v)); }
+};
+template <int NPL> struct BcRaw<NPL, 1> {
+    using T = typename Raw16<NPL>::T;
+    static __device__ __forceinline__ T load(const uint16_t *p) { return *(const T *)p; }
+    static __device__ __forceinline__ void widen(const T &v, float (&r)[NPL]) {
+        uint16_t u[NPL];
+        __builtin_memcpy(u, &v, sizeof(v));
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) r[j] = __uint_as_float((uint32_t)u[j] << 16);
+    }
+};
+
 // Sum over the LPC lanes of a group (LPC in {1, 2, 4}; groups are aligned quads
-// or pairs inside a quad).
+// or pairs inside a quad); every lane of the group gets the sum.
 template <int LPC>
 __device__ __forceinline__ float group_sum(float v) {
     if constexpr (LPC >= 2)  // quad_perm [1,0,3,2]
@@ -46,59 +78,117 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Value of v in lane `src` of the wave.
+__device__ __forceinline__ float from_lane(int src, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src * 4, __builtin_bit_cast(int, v)));
+}
+
+// Grid: x = block of kBlockCh channels, y = group of kRows batch rows
+// (strided by gridDim.y when the groups outnumber kMaxGridY).
 template <int N, int DT, bool GATE, bool SKIP>
 __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
     using T = typename Act<DT>::T;
     constexpr int NPL = N < 4 ? N : 4;
-    constexpr int LPC = N / NPL;
-    constexpr int CPB = kStepBlock / LPC;  // channels per block
+    constexpr int LPC = N / NPL;        // lanes per channel = accesses per row
+    constexpr int CPA = kWaveCh / LPC;  // channels per access
+    using BC = BcRaw<NPL, DT>;
     const int64_t D = a.D;
-    const int64_t nblk = (D + CPB - 1) / CPB;  // flat grid: block id = b * nblk + channel block
-    const int64_t b = blockIdx.x / nblk;
-    const int tid = threadIdx.x;
-    const int64_t d = (int64_t)(blockIdx.x % nblk) * CPB + tid / LPC;
-    const int sub = tid % LPC;
-    const bool valid = d < D;
-    const int64_t dc = valid ? d : D - 1;
-    const int n0 = sub * NPL;
-
+    const int l = threadIdx.x & 63;
+    const int64_t cw = (int64_t)blockIdx.x * kBlockCh + (threadIdx.x >> 6) * kWaveCh;  // wave's first channel
+    const int n0 = (l % LPC) * NPL;
+    // Channel of this lane in access q, clamped into range for loads.
+    int64_t chq[LPC];
+    bool okq[LPC];
+#pragma unroll
+    for (int q = 0; q < LPC; ++q) {
+        const int64_t c = cw + q * CPA + l / LPC;
+        okq[q] = c < D;
+        chq[q] = c < D ? c : D - 1;
+    }
+    const bool own_ok = cw + l < D;
+    const int64_t own = own_ok ? cw + l : D - 1;  // channel whose x, delta, z and y this lane moves
     const T *xp = (const T *)a.x;
     const T *dp = (const T *)a.delta;
     const T *Bp = (const T *)a.Bt;
     const T *Cp = (const T *)a.Ct;
-    const int64_t row = b * D + dc;
-    const float dt = ld_act(dp, row);
-    const float xv = ld_act(xp, row);
+    const int64_t groups = (a.batch + kRows - 1) / kRows;
 
-    float h[NPL], A2[NPL], Bv[NPL], Cv[NPL];
-    float *sp = a.state + row * N + n0;
-    ld_vec<NPL>(sp, h);
-    ld_vec<NPL>(a.A + dc * N + n0, A2);
+    float A2[LPC][NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        Bv[j] = ld_act(Bp, b * N + n0 + j);
-        Cv[j] = ld_act(Cp, b * N + n0 + j);
-    }
-    const float dx = dt * xv;
-    float acc = 0.0f;
+    for (int q = 0; q < LPC; ++q) ld_vec<NPL>(a.A + chq[q] * N + n0, A2[q]);
+    const float ds = SKIP ? a.Dskip[own] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        h[j] = __builtin_fmaf(fast_exp2(dt * (A2[j] * kLog2e)), h[j], dx * Bv[j]);
-        acc = __builtin_fmaf(Cv[j], h[j], acc);
+    for (int q = 0; q < LPC; ++q)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) A2[q][j] *= kLog2e;
+
+    for (int64_t g = blockIdx.y; g < groups; g += gridDim.y) {
+        int64_t bc[kRows];
+        bool bok[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int64_t b = g * kRows + r;
+            bok[r] = b < a.batch;
+            bc[r] = bok[r] ? b : a.batch - 1;
+        }
+        float h[kRows][LPC][NPL], xo[kRows], dto[kRows], zo[kRows];
+        typename BC::T braw[kRows], craw[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+#pragma unroll
+            for (int q = 0; q < LPC; ++q) ld_vec<NPL>(a.state + (bc[r] * D + chq[q]) * N + n0, h[r][q]);
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int64_t row = bc[r] * D + own;
+            xo[r] = ld_act(xp, row);
+            dto[r] = ld_act(dp, row);
+            if (GATE) zo[r] = ld_act((const T *)a.z, row);
+            braw[r] = BC::load(Bp + bc[r] * N + n0);
+            craw[r] = BC::load(Cp + bc[r] * N + n0);
+        }
+
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            float Bv[NPL], Cv[NPL], acc[LPC];
+            BC::widen(braw[r], Bv);
+            BC::widen(craw[r], Cv);
+#pragma unroll
+            for (int q = 0; q < LPC; ++q) {
+                const int src = q * CPA + l / LPC;
+                const float dt = LPC == 1 ? dto[r] : from_lane(src, dto[r]);
+                const float xv = LPC == 1 ? xo[r] : from_lane(src, xo[r]);
+                const float dx = dt * xv;
+                float s = 0.0f;
+#pragma unroll
+                for (int j = 0; j < NPL; ++j) {
+                    h[r][q][j] = __builtin_fmaf(fast_exp2(dt * A2[q][j]), h[r][q][j], dx * Bv[j]);
+                    s = __builtin_fmaf(Cv[j], h[r][q][j], s);
+                }
+                if (bok[r] && okq[q]) st_vec<NPL>(a.state + (bc[r] * D + chq[q]) * N + n0, h[r][q]);
+                acc[q] = group_sum<LPC>(s);
+            }
+            // Channel l's sum sits in access l / CPA, lane (l % CPA) * LPC.
+            float v = acc[0];
+            if constexpr (LPC > 1) {
+                const int src = (l % CPA) * LPC;
+#pragma unroll
+                for (int q = 0; q < LPC; ++q) {
+                    const float t = from_lane(src, acc[q]);
+                    v = l / CPA == q ? t : v;
+                }
+            }
+            if (SKIP) v = __builtin_fmaf(ds, xo[r], v);
+            if (GATE) v *= silu(zo[r]);
+            if (bok[r] && own_ok) st_act((T *)a.y, bc[r] * D + own, v);
+        }
     }
-    if (valid) st_vec<NPL>(sp, h);
-    acc = group_sum<LPC>(acc);
-    if (!valid || sub != 0) return;
-    if (SKIP) acc = __builtin_fmaf(a.Dskip[d], xv, acc);
-    if (GATE) acc *= silu(ld_act((const T *)a.z, row));
-    st_act((T *)a.y, row, acc);
 }
 
 template <int N, int DT, bool GATE, bool SKIP>
 hipError_t launch_step_typed(const StepArgs &a, hipStream_t s) {
-    constexpr int NPL = N < 4 ? N : 4;
-    constexpr int CPB = kStepBlock / (N / NPL);
-    const dim3 grid((unsigned)((a.D + CPB - 1) / CPB * a.batch));
+    const int64_t groups = (a.batch + kRows - 1) / kRows;
+    if ((a.D + kBlockCh - 1) / kBlockCh > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.D + kBlockCh - 1) / kBlockCh), (unsigned)(groups < kMaxGridY ? groups : kMaxGridY));
     hipLaunchKernelGGL((step_kernel<N, DT, GATE, SKIP>), grid, dim3(kStepBlock), 0, s, a);
     return hipGetLastError();
 }

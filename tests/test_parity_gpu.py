@@ -171,3 +171,28 @@ def test_step_every_output(N, dtype, D):
         torch.cuda.synchronize()
         check(to_f64(y), yr, dtype, f"y step {s}")
     check(to_f64(state), st64, dtype, "state")
+
+
+def test_step_more_row_groups_than_grid_rows():
+    """Decode step with more batch-row groups than one launch row of blocks can
+    hold (the kernel strides over them): batch 140001 (odd), D 3, N 2, fp32."""
+    import torch
+    import oracle
+    import selective_state_space_16_amd as ssm
+    cfg = W.StepConfig("step_tall", 140001, 3, 2, "f32", gate=True, dskip="uniform",
+                       state_std=1.0, steps=2, seed=91)
+    say(f"case {cfg}")
+    base = W.step_inputs(cfg)
+    state = to_dev(base["state"])
+    A = to_dev(base["A"])
+    Dskip = to_dev(base["Dskip"])
+    st64 = base["state"].astype(np.float64)
+    o = oracle.get()
+    for s in range(cfg.steps):
+        tk = W.step_token_inputs(cfg, s)
+        y = ssm.ssm_step(to_dev(tk["x"]), to_dev(tk["delta"]), A, to_dev(tk["Bt"]), to_dev(tk["Ct"]), state,
+                         Dskip=Dskip, z=to_dev(tk["z"]))
+        yr = o.step(tk, base["A"], base["Dskip"], st64, "f32")
+        torch.cuda.synchronize()
+        check(to_f64(y), yr, "f32", f"y step {s}")
+    check(to_f64(state), st64, "f32", "state")
