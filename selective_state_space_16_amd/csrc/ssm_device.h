@@ -18,49 +18,31 @@ __device__ __forceinline__ float row_bcast(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xF, 0xF, true));
 }
 
-// acc += (lane SRC of the row's `c`) * h, as one v_fmac_f32 with a DPP source.
-// The leading s_nop covers the DPP read-after-VALU-write hazard, which the
-// compiler does not see inside inline assembly.
-#define SSM_FMAC_BCAST(SRC)                                                                       \
-    template <>                                                                                   \
-    __device__ __forceinline__ void fmac_bcast<SRC>(float &acc, float c, float h) {               \
-        asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #SRC                    \
-                     " row_mask:0xf bank_mask:0xf"                                                \
-                     : "+v"(acc)                                                                  \
-                     : "v"(c), "v"(h));                                                           \
-    }
-template <int SRC>
-__device__ __forceinline__ void fmac_bcast(float &acc, float c, float h);
-SSM_FMAC_BCAST(0) SSM_FMAC_BCAST(1) SSM_FMAC_BCAST(2) SSM_FMAC_BCAST(3)
-SSM_FMAC_BCAST(4) SSM_FMAC_BCAST(5) SSM_FMAC_BCAST(6) SSM_FMAC_BCAST(7)
-SSM_FMAC_BCAST(8) SSM_FMAC_BCAST(9) SSM_FMAC_BCAST(10) SSM_FMAC_BCAST(11)
-SSM_FMAC_BCAST(12) SSM_FMAC_BCAST(13) SSM_FMAC_BCAST(14) SSM_FMAC_BCAST(15)
-#undef SSM_FMAC_BCAST
-
-// acc += sum over j < NL of (lane S0+j of the row's `c`) * h[j]: NL v_fmac_f32
-// with DPP sources behind one pair of wait states (only `c` is read through
-// DPP, so the NL instructions share them; h[j] are plain operands).
+// acc = sum over j < NL of (lane S0+j of the row's `c`) * h[j]: one
+// v_mul_f32 and NL-1 v_fmac_f32, all with DPP sources, behind one pair of wait
+// states (only `c` is read through DPP, so the NL instructions share them;
+// h[j] are plain operands).
 template <int NL, int S0>
-__device__ __forceinline__ void fmac_row(float &acc, float c, const float (&h)[NL]) {
+__device__ __forceinline__ void dot_row(float &acc, float c, const float (&h)[NL]) {
     if constexpr (NL == 4) {
         asm volatile("s_nop 1"
-                     "\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%6 row_mask:0xf bank_mask:0xf"
+                     "\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:%6 row_mask:0xf bank_mask:0xf"
                      "\n\tv_fmac_f32_dpp %0, %1, %3 row_newbcast:%7 row_mask:0xf bank_mask:0xf"
                      "\n\tv_fmac_f32_dpp %0, %1, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf"
                      "\n\tv_fmac_f32_dpp %0, %1, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
-                     : "+v"(acc)
+                     : "=&v"(acc)
                      : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "i"(S0), "i"(S0 + 1), "i"(S0 + 2),
                        "i"(S0 + 3));
     } else if constexpr (NL == 2) {
         asm volatile("s_nop 1"
-                     "\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%4 row_mask:0xf bank_mask:0xf"
+                     "\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:%4 row_mask:0xf bank_mask:0xf"
                      "\n\tv_fmac_f32_dpp %0, %1, %3 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
-                     : "+v"(acc)
+                     : "=&v"(acc)
                      : "v"(c), "v"(h[0]), "v"(h[1]), "i"(S0), "i"(S0 + 1));
     } else {
         static_assert(NL == 1, "1, 2 or 4 states per lane");
-        asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                     : "+v"(acc)
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "=&v"(acc)
                      : "v"(c), "v"(h[0]), "i"(S0));
     }
 }

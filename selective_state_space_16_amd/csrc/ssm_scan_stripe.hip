@@ -40,6 +40,7 @@
 // waits for stripes already held by running workgroups: the launch needs no
 // co-residency.
 #include <atomic>
+#include <cstddef>
 
 #include "ssm_common.h"
 #include "ssm_device.h"
@@ -114,46 +115,54 @@ __device__ __forceinline__ uint32_t half_sel(int i) { return (i & 1) ? 0x03020c0
 // whose low half is zero (it last held a value read this way, or 0.0f): the
 // register then holds the exact float, with no VALU work (the compiler does
 // not form these loads itself). Each block waits for its own loads, so no
-// register is read while its load is in flight. `a` and `b` are per-lane LDS
-// byte addresses; value k is read at a + k*STRIDE.
-template <int STRIDE>
-__device__ __forceinline__ void lds_bf16_8x2(float (&va)[8], float (&vb)[8], uint32_t a, uint32_t b) {
+// register is read while its load is in flight. Addresses are a per-lane LDS
+// byte address plus immediate offsets, so a fully unrolled walk over a tile
+// needs no address arithmetic.
+//
+// Eight values of each of two arrays: value k at base + OA + k*STRIDE and at
+// base + OB + k*STRIDE.
+template <int STRIDE, int OA, int OB>
+__device__ __forceinline__ void lds_bf16_8x2(float (&va)[8], float (&vb)[8], uint32_t base) {
     asm volatile(
-        "ds_read_u16_d16_hi %0, %16 offset:%18\n\tds_read_u16_d16_hi %1, %16 offset:%19\n\t"
-        "ds_read_u16_d16_hi %2, %16 offset:%20\n\tds_read_u16_d16_hi %3, %16 offset:%21\n\t"
-        "ds_read_u16_d16_hi %4, %16 offset:%22\n\tds_read_u16_d16_hi %5, %16 offset:%23\n\t"
-        "ds_read_u16_d16_hi %6, %16 offset:%24\n\tds_read_u16_d16_hi %7, %16 offset:%25\n\t"
-        "ds_read_u16_d16_hi %8, %17 offset:%18\n\tds_read_u16_d16_hi %9, %17 offset:%19\n\t"
-        "ds_read_u16_d16_hi %10, %17 offset:%20\n\tds_read_u16_d16_hi %11, %17 offset:%21\n\t"
-        "ds_read_u16_d16_hi %12, %17 offset:%22\n\tds_read_u16_d16_hi %13, %17 offset:%23\n\t"
-        "ds_read_u16_d16_hi %14, %17 offset:%24\n\tds_read_u16_d16_hi %15, %17 offset:%25\n\t"
+        "ds_read_u16_d16_hi %0, %16 offset:%17\n\tds_read_u16_d16_hi %1, %16 offset:%18\n\t"
+        "ds_read_u16_d16_hi %2, %16 offset:%19\n\tds_read_u16_d16_hi %3, %16 offset:%20\n\t"
+        "ds_read_u16_d16_hi %4, %16 offset:%21\n\tds_read_u16_d16_hi %5, %16 offset:%22\n\t"
+        "ds_read_u16_d16_hi %6, %16 offset:%23\n\tds_read_u16_d16_hi %7, %16 offset:%24\n\t"
+        "ds_read_u16_d16_hi %8, %16 offset:%25\n\tds_read_u16_d16_hi %9, %16 offset:%26\n\t"
+        "ds_read_u16_d16_hi %10, %16 offset:%27\n\tds_read_u16_d16_hi %11, %16 offset:%28\n\t"
+        "ds_read_u16_d16_hi %12, %16 offset:%29\n\tds_read_u16_d16_hi %13, %16 offset:%30\n\t"
+        "ds_read_u16_d16_hi %14, %16 offset:%31\n\tds_read_u16_d16_hi %15, %16 offset:%32\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]),
           "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]), "+v"(vb[4]), "+v"(vb[5]), "+v"(vb[6]), "+v"(vb[7])
-        : "v"(a), "v"(b), "i"(0), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE),
-          "i"(6 * STRIDE), "i"(7 * STRIDE)
+        : "v"(base), "i"(OA), "i"(OA + STRIDE), "i"(OA + 2 * STRIDE), "i"(OA + 3 * STRIDE), "i"(OA + 4 * STRIDE),
+          "i"(OA + 5 * STRIDE), "i"(OA + 6 * STRIDE), "i"(OA + 7 * STRIDE), "i"(OB), "i"(OB + STRIDE),
+          "i"(OB + 2 * STRIDE), "i"(OB + 3 * STRIDE), "i"(OB + 4 * STRIDE), "i"(OB + 5 * STRIDE),
+          "i"(OB + 6 * STRIDE), "i"(OB + 7 * STRIDE)
         : "memory");
 }
-// Two values from each of up to four addresses (value k at addr + k*STRIDE):
-// pairs from `a` and `b` with stride SA, pairs from `c` and `d` with stride SC.
-template <int SA, int SC>
+// Two values of each of four arrays: a at ab + OA + {0, SA}, b at ab + OB +
+// {0, SA}, c at cd + OC + {0, SC}, d at cd + OD + {0, SC}.
+template <int SA, int SC, int OA, int OB, int OC, int OD>
 __device__ __forceinline__ void lds_bf16_2x4(float (&va)[2], float (&vb)[2], float (&vc)[2], float (&vd)[2],
-                                             uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+                                             uint32_t ab, uint32_t cd) {
     asm volatile(
-        "ds_read_u16_d16_hi %0, %8 offset:0\n\tds_read_u16_d16_hi %1, %8 offset:%12\n\t"
-        "ds_read_u16_d16_hi %2, %9 offset:0\n\tds_read_u16_d16_hi %3, %9 offset:%12\n\t"
-        "ds_read_u16_d16_hi %4, %10 offset:0\n\tds_read_u16_d16_hi %5, %10 offset:%13\n\t"
-        "ds_read_u16_d16_hi %6, %11 offset:0\n\tds_read_u16_d16_hi %7, %11 offset:%13\n\t"
+        "ds_read_u16_d16_hi %0, %8 offset:%10\n\tds_read_u16_d16_hi %1, %8 offset:%11\n\t"
+        "ds_read_u16_d16_hi %2, %8 offset:%12\n\tds_read_u16_d16_hi %3, %8 offset:%13\n\t"
+        "ds_read_u16_d16_hi %4, %9 offset:%14\n\tds_read_u16_d16_hi %5, %9 offset:%15\n\t"
+        "ds_read_u16_d16_hi %6, %9 offset:%16\n\tds_read_u16_d16_hi %7, %9 offset:%17\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "+v"(va[0]), "+v"(va[1]), "+v"(vb[0]), "+v"(vb[1]), "+v"(vc[0]), "+v"(vc[1]), "+v"(vd[0]), "+v"(vd[1])
-        : "v"(a), "v"(b), "v"(c), "v"(d), "i"(SA), "i"(SC)
+        : "v"(ab), "v"(cd), "i"(OA), "i"(OA + SA), "i"(OB), "i"(OB + SA), "i"(OC), "i"(OC + SC), "i"(OD),
+          "i"(OD + SC)
         : "memory");
 }
-template <int SA>
+// Two values of one array, at a + OA + {0, SA}.
+template <int SA, int OA>
 __device__ __forceinline__ void lds_bf16_2(float (&va)[2], uint32_t a) {
-    asm volatile("ds_read_u16_d16_hi %0, %2 offset:0\n\tds_read_u16_d16_hi %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+    asm volatile("ds_read_u16_d16_hi %0, %2 offset:%3\n\tds_read_u16_d16_hi %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
                  : "+v"(va[0]), "+v"(va[1])
-                 : "v"(a), "i"(SA)
+                 : "v"(a), "i"(OA), "i"(OA + SA)
                  : "memory");
 }
 
@@ -333,21 +342,26 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         tb.dl[tail + q / TCH][q % TCH] = T(0.0f);
                     lds_barrier();
                 }
-#pragma unroll 1
-                for (int tg = 0; tg < TT; tg += GROUP) {
+                // per-lane LDS byte addresses in this tile: the lane's channel
+                // column, its Bt/Ct element and its first owned token's row
+                using TB = TileBuf<N, DT>;
+                constexpr int ROWB = TCH * G::ESZ, BCB = N * G::ESZ;
+                constexpr int OFF_DL = offsetof(TB, dl), OFF_Z = offsetof(TB, z);
+                constexpr int OFF_B = offsetof(TB, B), OFF_C = offsetof(TB, C);
+                const uint32_t a_ch = lds_addr(&tb) + cl * G::ESZ;
+                const uint32_t a_bc = lds_addr(&tb) + OFF_B + ((k16 / NL) * N + nstate0 + (k16 % NL)) * G::ESZ;
+                const uint32_t a_own = a_ch + g * ROWB;
+                static_for<0, TT / GROUP>([&](auto gc) {
+                    constexpr int tg = decltype(gc)::value * GROUP;
                     if constexpr (kHiLoads) {
                         // bfloat16: loads into the high halves of the registers
                         // that held the previous group's values
-                        constexpr int ROWB = TCH * 2, BCB = N * 2;
-                        lds_bf16_8x2<ROWB>(xv, dv, (uint32_t)(uintptr_t)&tb.x[tg][cl], (uint32_t)(uintptr_t)&tb.dl[tg][cl]);
-                        const uint32_t bq = (uint32_t)(uintptr_t)&tb.B[(tg + k16 / NL) * N + nstate0 + (k16 % NL)];
-                        const uint32_t cq = (uint32_t)(uintptr_t)&tb.C[(tg + k16 / NL) * N + nstate0 + (k16 % NL)];
+                        lds_bf16_8x2<ROWB, tg * ROWB, OFF_DL + tg * ROWB>(xv, dv, a_ch);
                         if constexpr (PASS == 2) {
-                            const uint32_t xa = (uint32_t)(uintptr_t)&tb.x[tg + g][cl];
-                            const uint32_t za = (uint32_t)(uintptr_t)&tb.z[tg + g][cl];
-                            lds_bf16_2x4<TPV * BCB, NGR * ROWB>(Bq, Cq, xo, zo, bq, cq, xa, za);
+                            lds_bf16_2x4<TPV * BCB, NGR * ROWB, tg * BCB, OFF_C - OFF_B + tg * BCB, tg * ROWB,
+                                         OFF_Z + tg * ROWB>(Bq, Cq, xo, zo, a_bc, a_own);
                         } else {
-                            lds_bf16_2<TPV * BCB>(Bq, bq);
+                            lds_bf16_2<TPV * BCB, tg * BCB>(Bq, a_bc);
                         }
                     } else {
 #pragma unroll
@@ -387,13 +401,12 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         static_for<0, GROUP>([&](auto tc) {
                             constexpr int t = decltype(tc)::value;
                             const float dx = dv[t] * xv[t];
-                            yp[t] = 0.0f;
                             static_for<0, NL>([&](auto jc) {
                                 constexpr int q = decltype(jc)::value;
                                 const float dA = fast_exp2(dv[t] * A2[q]);
                                 st[q] = __builtin_fmaf(dA, st[q], row_bcast<(t % TPV) * NL + q>(Bq[t / TPV]) * dx);
                             });
-                            fmac_row<NL, (t % TPV) * NL>(yp[t], Cq[t / TPV], st);
+                            dot_row<NL, (t % TPV) * NL>(yp[t], Cq[t / TPV], st);
                         });
                         // Sum the partial readouts over a channel's rows; afterwards
                         // row r holds the finished token NGR*q + (r % NGR) of group q.
@@ -429,7 +442,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                             st_act(&tb.dl[tw][0], cl, yv);
                         }
                     }
-                }
+                });
                 vm_wait();  // the next tile has landed (and this wave's earlier y stores are out)
                 lds_barrier();
             }
