@@ -103,13 +103,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
-// The same for 4-byte pieces (lds + lane*4).
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-// 16-byte pieces of data other workgroups write (bypasses the CU's cache).
-__device__ __forceinline__ void dma16_coherent(const void *g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(g), "s"(lds) : "memory");
+// The same with a wave-uniform base address (SGPRs) and a per-lane 32-bit
+// byte offset: no per-lane address arithmetic.
+__device__ __forceinline__ void dma16_s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
 }
 // Wait until this wave's vector memory accesses (including the loads above)
 // have completed.

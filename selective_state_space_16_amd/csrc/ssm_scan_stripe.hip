@@ -170,19 +170,50 @@ __device__ __forceinline__ uint32_t take_unit(uint32_t *ctr) {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Load tile `tile` of the stripe (tokens t0 + tile*TT ...) of tile column
-// (b, ch0) into LDS, spread over waves 1..3. Pass 1 needs x, delta and Bt;
-// pass 2 also z and Ct. Pieces past the end of the sequence or of the
-// channels are read from an in-bounds location instead; the tokens are given
-// delta = 0 afterwards and the channels are never stored.
-template <int N, int DT, bool GATE, int PASS>
-__device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
-                                          int w, int lane) {
+// Load the tile of TT tokens starting at tt0 of tile column (b, ch0) into
+// LDS, spread over waves 1..3. Pass 1 needs x, delta and Bt; pass 2 also z
+// and Ct. Each wave moves slots of 64 16-byte pieces; a slot of an activation
+// array covers whole tile rows, so a piece's address is a wave-uniform row
+// address (SGPRs) plus the lane's offset within the slot, `act_off`, which is
+// the same for every tile of a unit. Only the last tile of a sequence, whose
+// rows may run past L, takes the per-piece path: pieces past the end of the
+// sequence are read from the last token instead, and the tokens are given
+// delta = 0 afterwards. Channels past D (a last, partial column) are read
+// from the last whole piece of the row and never stored.
+template <int N, int DT, bool GATE, int PASS, int WV>
+__device__ __forceinline__ void load_tile_w(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
+                                            int lane, uint32_t act_off) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     constexpr int NACT = (PASS == 2 && GATE) ? 3 : 2;
     constexpr int NBC = PASS == 2 ? 2 : 1;
+    using TB = TileBuf<N, DT>;
     const int64_t D = a.D, L = a.L;
+    if (tt0 + G::TT <= L) {
+        const uint32_t rowb = (uint32_t)(D * G::ESZ);
+        const int64_t off = ((b * L + tt0) * D + ch0) * G::ESZ;
+        const uint32_t lds_tb = lds_addr(&tb);
+        // the wave's slots: pieces (WV - 1) * 64 + 192 * k
+        static_for<0, (NACT * G::ACT_PIECES - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
+            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
+            constexpr int arr = base / G::ACT_PIECES;
+            constexpr int pa0 = base - arr * G::ACT_PIECES;  // first piece of the slot
+            const void *p = arr == 0 ? a.x : arr == 1 ? a.delta : a.z;
+            constexpr int dst = (arr == 0 ? offsetof(TB, x) : arr == 1 ? offsetof(TB, dl) : offsetof(TB, z)) + pa0 * 16;
+            dma16_s((const char *)p + off + (uint64_t)(pa0 / G::PPR) * rowb, act_off, lds_tb + dst);
+        });
+        const int64_t boff = (b * L + tt0) * N * G::ESZ;
+        static_for<0, (NBC * G::BC_SLOTS - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
+            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
+            constexpr int arr = base / G::BC_SLOTS;
+            constexpr int pq0 = base - arr * G::BC_SLOTS;
+            const int pq = pq0 + lane < G::BC_PIECES ? pq0 + lane : G::BC_PIECES - 1;  // padding repeats the last piece
+            constexpr int dst = (arr == 0 ? offsetof(TB, B) : offsetof(TB, C)) + pq0 * 16;
+            dma16_s((const char *)(arr == 0 ? a.Bt : a.Ct) + boff, (uint32_t)pq * 16, lds_tb + dst);
+        });
+        return;
+    }
+    const int w = WV;
     for (int base = (w - 1) * 64; base < NACT * G::ACT_PIECES; base += 3 * 64) {
         const int arr = base / G::ACT_PIECES;
         const int pa = base - arr * G::ACT_PIECES + lane;
@@ -206,6 +237,14 @@ __device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &
         T *dst = arr == 0 ? tb.B : tb.C;
         dma16(src + (b * L + t) * N + c, lds_addr(dst + (int64_t)(base - arr * G::BC_SLOTS) * G::VEC));
     }
+}
+
+template <int N, int DT, bool GATE, int PASS>
+__device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
+                                          int w, int lane, uint32_t act_off) {
+    if (w == 1) load_tile_w<N, DT, GATE, PASS, 1>(tb, a, b, ch0, tt0, lane, act_off);
+    else if (w == 2) load_tile_w<N, DT, GATE, PASS, 2>(tb, a, b, ch0, tt0, lane, act_off);
+    else load_tile_w<N, DT, GATE, PASS, 3>(tb, a, b, ch0, tt0, lane, act_off);
 }
 
 // One stripe record: NL state words per lane (and, for an aggregate, one
@@ -269,6 +308,10 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         const int64_t ch0 = (col % a.ntpb) * TCH;
         const int64_t d = ch0 + cl;
         const bool valid = d < D;
+        // this lane's byte offset within an activation slot of a tile (see load_tile)
+        int64_t lane_ch = ch0 + (l % G::PPR) * G::VEC;
+        lane_ch = lane_ch + G::VEC <= D ? lane_ch : D - G::VEC;
+        const uint32_t act_off = (uint32_t)((l / G::PPR) * D + (lane_ch - ch0)) * G::ESZ;
         const int64_t dc = valid ? d : D - 1;
         const int64_t t0 = j * SL;
         const int64_t t1 = t0 + SL < L ? t0 + SL : L;
@@ -306,7 +349,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         // First tile of a pass, loaded ahead (before the look-back, for pass 2).
         auto prefetch = [&](auto pass_c) {
             constexpr int PASS = decltype(pass_c)::value;
-            if (w > 0) load_tile<N, DT, GATE, PASS>(sh.buf[0], a, b, ch0, t0, w, l);
+            if (w > 0) load_tile<N, DT, GATE, PASS>(sh.buf[0], a, b, ch0, t0, w, l, act_off);
         };
         auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
             constexpr int PASS = decltype(pass_c)::value;
@@ -333,7 +376,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         lds_barrier();
                     }
                 }
-                if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l);
+                if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l, act_off);
                 const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
                 if (tail < TT) {
                     // tokens past the end were loaded from the last token; give
