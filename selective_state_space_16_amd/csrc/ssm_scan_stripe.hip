@@ -52,7 +52,7 @@ namespace {
 
 constexpr int kWaves = 4;   // waves per workgroup (one per channel group)
 constexpr int kLists = 8;   // unit lists (one per XCD of an MI355X)
-constexpr int kReplay = 8;  // stripe records loaded per round trip of a look-back replay
+constexpr int kReplay = 4;  // stripe records loaded per round trip of a look-back replay
 constexpr int kSlotsPerList = 64;  // workgroups a list is planned for (2 per CU on 256 CUs)
 
 template <int N, int DT>
