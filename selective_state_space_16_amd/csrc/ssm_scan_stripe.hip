@@ -248,11 +248,12 @@ __device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &
 }
 
 // One stripe record: NL state words per lane (and, for an aggregate, one
-// summed-delta word per lane), epoch-tagged.
+// summed-delta word per lane), epoch-tagged. Word j of lane l sits at j*64 + l,
+// so each store instruction of a wave writes 512 contiguous bytes.
 template <int NL>
 __device__ __forceinline__ void publish_state(uint64_t *rec, int l, const float (&S)[NL], uint32_t epoch) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) st_tagged(rec + l * NL + j, S[j], epoch);
+    for (int j = 0; j < NL; ++j) st_tagged(rec + j * 64 + l, S[j], epoch);
 }
 
 template <int N, int DT, bool GATE, bool SKIP>
@@ -552,9 +553,9 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                 // Replay forward from that state with the arithmetic each
                 // stripe uses for its own end state, kReplay records per
                 // round trip.
-                const uint64_t *src = a.incl + rec_of(j0) * (64 * NL) + l * NL;
+                const uint64_t *src = a.incl + rec_of(j0) * (64 * NL) + l;
 #pragma unroll
-                for (int q = 0; q < NL; ++q) h[q] = __uint_as_float((uint32_t)ld_valid(src + q, a.epoch));
+                for (int q = 0; q < NL; ++q) h[q] = __uint_as_float((uint32_t)ld_valid(src + q * 64, a.epoch));
                 for (int64_t jj = j0 + 1; jj < j; jj += kReplay) {
                     uint64_t sv[kReplay][NL], dv2[kReplay];
 #pragma unroll
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         if (jj + r < j) {
                             const uint64_t *ar = a.agg + rec_of(jj + r) * (64 * (NL + 1));
 #pragma unroll
-                            for (int q = 0; q < NL; ++q) sv[r][q] = ld_tagged(ar + l * NL + q);
+                            for (int q = 0; q < NL; ++q) sv[r][q] = ld_tagged(ar + q * 64 + l);
                             dv2[r] = ld_tagged(ar + 64 * NL + l);
                         }
                     }
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
 #pragma unroll
                             for (int q = 0; q < NL; ++q)
                                 h[q] = __builtin_fmaf(fast_exp2(A2[q] * dd), h[q],
-                                                      __uint_as_float((uint32_t)recheck(sv[r][q], ar + l * NL + q, a.epoch)));
+                                                      __uint_as_float((uint32_t)recheck(sv[r][q], ar + q * 64 + l, a.epoch)));
                         }
                     }
                 }
