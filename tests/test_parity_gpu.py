@@ -52,6 +52,21 @@ def test_ragged_channels(D):
     _run_full(_cfg(f"D{D}", 3, 300, D, 16, "f32", gate=True, state_in=0.3, seed=50))
 
 
+@pytest.mark.parametrize("L", [1, 7, 65, 1000, 4097])
+def test_ragged_lengths_bf16(L):
+    """bfloat16 tiles of 64 tokens: the last tile of a sequence runs past L."""
+    _run_full(_cfg(f"L{L}b", 1, L, 96, 16, "bf16", gate=True, state_in=0.3, seed=41))
+
+
+@pytest.mark.parametrize("D,dtype", [(4, "f32"), (68, "f32"), (132, "f32"), (8, "bf16"), (56, "bf16"),
+                                     (72, "bf16"), (200, "bf16"), (264, "bf16")])
+def test_partial_channel_columns(D, dtype):
+    """Widths that are whole 16-byte pieces but not whole 64-channel tile
+    columns: the last column's loads clamp to the row and its extra channels
+    are never stored."""
+    _run_full(_cfg(f"D{D}{dtype}", 2, 777, D, 16, dtype, gate=True, state_in=0.3, seed=51))
+
+
 @pytest.mark.parametrize("gate,dskip,state", [(False, "none", None), (True, "none", None),
                                               (False, "uniform", 1.0), (True, "one", 0.1)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
