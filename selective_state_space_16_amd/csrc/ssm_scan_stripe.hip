@@ -82,11 +82,13 @@ template <int N, int DT>
 struct TileBuf {
     using G = Geo<N, DT>;
     using T = typename G::T;
-    T x[G::TT][G::TCH];
-    T dl[G::TT][G::TCH];  // delta; pass 2 writes y here once a token's delta is used
-    T z[G::TT][G::TCH];
-    T B[G::BC_SLOTS * G::VEC];  // Bt rows of the tile's tokens (padded to whole waves of pieces)
-    T C[G::BC_SLOTS * G::VEC];
+    // 16-byte aligned: pieces land here as whole 16-byte writes and y is read
+    // back as 16-byte reads
+    alignas(16) T x[G::TT][G::TCH];
+    alignas(16) T dl[G::TT][G::TCH];  // delta; pass 2 writes y here once a token's delta is used
+    alignas(16) T z[G::TT][G::TCH];
+    alignas(16) T B[G::BC_SLOTS * G::VEC];  // Bt rows of the tile's tokens (padded to whole waves of pieces)
+    alignas(16) T C[G::BC_SLOTS * G::VEC];
 };
 
 template <int N, int DT>
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
             for (int p = threadIdx.x; p < G::ACT_PIECES; p += 64 * kWaves) {
                 const int r = p / G::PPR, c = (p % G::PPR) * G::VEC;
                 if (r < rows && ch0 + c < D) {
-                    const VT v = *(const VT *)&tb.dl[r][c];
+                    const VT v = *(const VT *)__builtin_assume_aligned(&tb.dl[r][c], 16);
                     *(VT *)(yptr + (b * L + tt0 + r) * D + ch0 + c) = v;
                 }
             }
