@@ -54,6 +54,8 @@ class Oracle:
         self.lib.oracle_step.restype = ci
         self.lib.oracle_threads.argtypes = [ci]
         self.lib.oracle_threads.restype = ci
+        self.lib.oracle_softplus_bias.argtypes = [i64, i64, _DP, _DP, _DP]
+        self.lib.oracle_softplus_bias.restype = ci
 
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.oracle_threads(nthreads))
@@ -102,6 +104,19 @@ class Oracle:
             raise ValueError("oracle_step rejected sizes")
         return y
 
+    def softplus_bias64(self, raw, bias=None):
+        """softplus(raw + bias[d]) over the last axis (D) of a float64 array."""
+        raw = _c64(raw)
+        D = raw.shape[-1]
+        rows = raw.size // D if D else 0
+        bias = None if bias is None else _c64(bias)
+        if bias is not None:
+            assert bias.shape == (D,)
+        out = np.empty_like(raw)
+        if self.lib.oracle_softplus_bias(rows, D, _p(raw), _p(bias), _p(out)) != 0:
+            raise ValueError("oracle_softplus_bias rejected sizes")
+        return out
+
     # -- stored-dtype entry points -------------------------------------------
     def scan(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
         """Scan on stored inputs (float32 arrays, or bfloat16 bit patterns as uint16).
@@ -112,6 +127,28 @@ class Oracle:
                            up(inp.get("z")),
                            None if inp.get("state_in") is None else upcast(inp["state_in"], "f32"),
                            nthreads=nthreads)
+
+    def scan_dt(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
+        """Scan whose step size is given before its activation: inp["delta_raw"]
+        (stored dtype) and inp["dt_bias"] (D,) float32 or None."""
+        bias = None if inp.get("dt_bias") is None else upcast(inp["dt_bias"], "f32")
+        d64 = self.softplus_bias64(upcast(inp["delta_raw"], dtype), bias)
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.scan64(up(inp["x"]), d64, upcast(inp["A"], "f32"), up(inp["Bt"]),
+                           up(inp["Ct"]), None if inp.get("Dskip") is None else upcast(inp["Dskip"], "f32"),
+                           up(inp.get("z")),
+                           None if inp.get("state_in") is None else upcast(inp["state_in"], "f32"),
+                           nthreads=nthreads)
+
+    def step_dt(self, tok: Dict[str, np.ndarray], A, Dskip, dt_bias, state64: np.ndarray, dtype: str,
+                nthreads: int = 0):
+        """Decode step with tok["delta_raw"] and dt_bias (D,) float32 or None."""
+        bias = None if dt_bias is None else upcast(dt_bias, "f32")
+        d64 = self.softplus_bias64(upcast(tok["delta_raw"], dtype), bias)
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.step64(up(tok["x"]), d64, upcast(A, "f32"), up(tok["Bt"]),
+                           up(tok["Ct"]), None if Dskip is None else upcast(Dskip, "f32"),
+                           up(tok.get("z")), state64, nthreads=nthreads)
 
     def step(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
              nthreads: int = 0):

@@ -34,8 +34,17 @@
  *    computed) and "Notas sobre Mamba", section "Preliminares" (recurrent
  *    mode with a constant-size state).
  *
- * Everything is float64 and uses libm exp(); no fast-math, no reordering of
- * the token loop. OpenMP only splits independent (b, d) rows across threads.
+ * The step size may also be given before its activation: delta is then
+ * softplus(delta_raw + dt_bias[d]), the pre-activation being a per-token
+ * projection and dt_bias a per-channel parameter ("Notas sobre Mamba",
+ * section "O mecanismo de seleção (S6)": delta_t as the softplus of a linear
+ * map of x_t plus a bias; the blog post's forward_step listing applies the
+ * same softplus to its projected delta). oracle_softplus_bias computes that
+ * activation; the scan and the step then run on its result unchanged.
+ *
+ * Everything is float64 and uses libm exp()/log1p(); no fast-math, no
+ * reordering of the token loop. OpenMP only splits independent (b, d) rows
+ * across threads.
  */
 #include <math.h>
 #include <stddef.h>
@@ -103,6 +112,22 @@ int oracle_scan(int64_t batch, int64_t L, int64_t D, int64_t N,
         if (state_out)
             for (int64_t n = 0; n < N; ++n) state_out[IDX3(b, d, n, D, N)] = h[n];
     }
+    return 0;
+}
+
+/*
+ * Step-size activation: out[r, d] = softplus(raw[r, d] + bias[d]) for the
+ * `rows` rows of D channels of a (rows, D) array; bias may be NULL (zero).
+ * softplus(u) = log(1 + exp(u)), evaluated as max(u, 0) + log1p(exp(-|u|)).
+ */
+int oracle_softplus_bias(int64_t rows, int64_t D, const double *raw, const double *bias, double *out)
+{
+    if (rows < 0 || D < 0) return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d) {
+            double u = raw[r * D + d] + (bias ? bias[d] : 0.0);
+            out[r * D + d] = (u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u)));
+        }
     return 0;
 }
 

@@ -307,6 +307,36 @@ def pin_linearity_causality(o):
         assert not np.array_equal(yk[:, t0 + 1:], y0[:, t0 + 1:]), k
 
 
-ALL_PINS = [pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
+def pin_softplus_activation(o):
+    """Step-size activation delta = softplus(raw + dt_bias[d]) ("Notas sobre
+    Mamba", section "O mecanismo de seleção (S6)"): against closed forms, the
+    identity softplus(u) - softplus(-u) = u, numpy's logaddexp(0, u), the
+    per-channel broadcast of the bias, and a scan on that activated delta."""
+    ln2 = math.log(2.0)
+    assert abs(o.softplus_bias64(np.zeros((1, 1)))[0, 0] - ln2) <= 1e-16
+    u = np.concatenate([np.linspace(-60, 60, 241), [-700.0, -36.5, -1e-9, 1e-9, 36.5, 700.0]])[None, :]
+    sp = o.softplus_bias64(u)
+    ref = np.logaddexp(0.0, u)
+    assert np.all(np.abs(sp - ref) <= 4e-16 * np.maximum(np.abs(ref), 1e-300) + 1e-300), "softplus vs logaddexp"
+    assert np.allclose(sp - o.softplus_bias64(-u), u, rtol=0, atol=1e-13), "softplus(u) - softplus(-u) = u"
+    assert abs(o.softplus_bias64(np.array([[-50.0]]))[0, 0] / math.exp(-50.0) - 1.0) < 1e-15, "left tail exp(u)"
+    rng = np.random.default_rng(7)
+    raw = rng.normal(size=(6, 11)) * 3.0
+    bias = rng.normal(size=11)
+    got = o.softplus_bias64(raw, bias)
+    assert np.allclose(got, np.logaddexp(0.0, raw + bias[None, :]), rtol=1e-15, atol=0), "bias per channel"
+    # a scan on the activated step equals the scan with delta given directly
+    p = _rand_problem(rng, 2, 9, 5, 4)
+    draw = rng.normal(size=p["x"].shape) * 0.5
+    db = np.log(np.expm1(np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=5))))  # inverse softplus of dt
+    d_act = o.softplus_bias64(draw, db)
+    assert np.allclose(d_act, np.logaddexp(0.0, draw + db[None, None, :]), rtol=1e-15, atol=0)
+    q = dict(p, delta=np.logaddexp(0.0, draw + db[None, None, :]))
+    y1, s1 = _scan(o, dict(p, delta=d_act))
+    y2, s2 = _scan(o, q)
+    assert np.allclose(y1, y2, rtol=1e-13, atol=1e-14) and np.allclose(s1, s2, rtol=1e-13, atol=1e-14)
+
+
+ALL_PINS = [pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
             pin_linearity_causality]

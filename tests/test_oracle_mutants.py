@@ -46,6 +46,11 @@ MUTANTS = [
      "for (int64_t n = 0; n + 1 < N; ++n) state_out[IDX3(b, d, n, D, N)] = h[n];"),
     ("batch_row_mixup", "int64_t b = r / D, d = r % D;\n        double h[4096];",
      "int64_t b = 0, d = r % D;\n        double h[4096];"),
+    ("softplus_drops_bias", "double u = raw[r * D + d] + (bias ? bias[d] : 0.0);", "double u = raw[r * D + d];"),
+    ("softplus_bias_by_row", "(bias ? bias[d] : 0.0)", "(bias ? bias[r % D] : 0.0)"),
+    ("softplus_log_not_log1p", "log1p(exp(-fabs(u)))", "log(1.0 + exp(-fabs(u)))"),
+    ("softplus_relu_only", "(u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u)))", "(u > 0.0 ? u : 0.0)"),
+    ("softplus_tail_sign", "log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
 ]
 
 

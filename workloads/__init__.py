@@ -181,7 +181,7 @@ def _token_block(seed: int, kind: int, b: int, t0: int, t1: int, width: int,
 
 
 def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
-                channels: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                channels: Optional[np.ndarray] = None, raw_delta: bool = False) -> Dict[str, np.ndarray]:
     """Inputs of `cfg` for tokens [t0, t1) (default: all), in storage dtypes.
 
     `channels` selects a subset of the D channels for x, delta, z, A and Dskip
@@ -189,6 +189,10 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     shared by all channels and always returned whole. state_in is returned
     for every batch row and the selected channels when the workload has one.
     The values do not depend on how the token range is split.
+
+    With raw_delta, the step size is also returned before its activation:
+    delta_raw = 0.5*eps in the storage dtype and dt_bias (D,) float32, the two
+    terms whose softplus is delta.
     """
     if t1 is None:
         t1 = cfg.L
@@ -202,9 +206,12 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     z = np.empty_like(x) if cfg.gate else None
     Bt = np.empty((cfg.batch, T, cfg.N), dtype=x.dtype)
     Ct = np.empty_like(Bt)
+    draw = np.empty_like(x) if raw_delta else None
     for b in range(cfg.batch):
         eps = _token_block(cfg.seed, _K_DNOISE, b, t0, t1, cfg.D, sel)
         dl[b] = _store(_softplus(0.5 * eps + dt_bias[sel][None, :]), act)
+        if draw is not None:
+            draw[b] = _store(0.5 * eps, act)
         x[b] = _store(_token_block(cfg.seed, _K_X, b, t0, t1, cfg.D, sel), act)
         if z is not None:
             z[b] = _store(_token_block(cfg.seed, _K_Z, b, t0, t1, cfg.D, sel), act)
@@ -215,22 +222,28 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     if cfg.state_in is not None:
         st = _rng(cfg.seed, _K_STATE).standard_normal((cfg.batch, cfg.D, cfg.N)) * cfg.state_in
         out["state_in"] = np.ascontiguousarray(st[:, sel, :].astype(np.float32))
+    if draw is not None:
+        out["delta_raw"] = draw
+        out["dt_bias"] = np.ascontiguousarray(dt_bias[sel].astype(np.float32))
     return out
 
 
 def step_inputs(cfg: StepConfig, channels: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Per-workload tensors of a decode run: A, Dskip and the initial state."""
-    A, _dt_bias, Dskip = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
+    """Per-workload tensors of a decode run: A, Dskip, dt_bias (float32) and
+    the initial state."""
+    A, dt_bias, Dskip = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
     sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
     st = _rng(cfg.seed, _K_STATE).standard_normal((cfg.batch, cfg.D, cfg.N)) * cfg.state_std
     return {"A": np.ascontiguousarray(A[sel]),
             "Dskip": None if Dskip is None else np.ascontiguousarray(Dskip[sel]),
+            "dt_bias": np.ascontiguousarray(dt_bias[sel].astype(np.float32)),
             "state": np.ascontiguousarray(st[:, sel, :].astype(np.float32))}
 
 
-def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray] = None
-                      ) -> Dict[str, np.ndarray]:
-    """Inputs of decode step `step`: x, delta, z (batch, D) and Bt, Ct (batch, N)."""
+def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray] = None,
+                      raw_delta: bool = False) -> Dict[str, np.ndarray]:
+    """Inputs of decode step `step`: x, delta, z (batch, D) and Bt, Ct (batch, N);
+    with raw_delta also delta_raw = 0.5*eps (delta is its softplus plus dt_bias)."""
     _A, dt_bias, _D = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
     sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
     act = cfg.dtype
@@ -239,17 +252,20 @@ def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray]
     def chan(kind):  # (batch, len(sel)): the batch axis plays the token axis
         return _token_block(cfg.seed, kind, key, 0, cfg.batch, cfg.D, sel)
 
+    eps = chan(_K_DNOISE)
     out = {
-        "delta": _store(_softplus(0.5 * chan(_K_DNOISE) + dt_bias[sel][None, :]), act),
+        "delta": _store(_softplus(0.5 * eps + dt_bias[sel][None, :]), act),
         "x": _store(chan(_K_X), act),
         "z": _store(chan(_K_Z), act) if cfg.gate else None,
         "Bt": _store(_token_block(cfg.seed, _K_B, key, 0, cfg.batch, cfg.N), act),
         "Ct": _store(_token_block(cfg.seed, _K_C, key, 0, cfg.batch, cfg.N), act),
     }
+    if raw_delta:
+        out["delta_raw"] = _store(0.5 * eps, act)
     return out
 
 
-def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345):
+def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345, raw_delta: bool = False):
     """torch tensors of the full workload `cfg` on `device`, same distributions
     as scan_inputs but drawn with torch (values differ from the numpy streams).
     Returns x, delta, z (or None) and Bt, Ct; A, Dskip and state_in come from
@@ -265,16 +281,21 @@ def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345):
     def normal(shp):
         return torch.randn(shp, generator=g, device=device, dtype=torch.float32)
 
-    eps = normal(shape)
-    delta = torch.nn.functional.softplus(eps.mul_(0.5).add_(bias)).to(act)
+    eps = normal(shape).mul_(0.5)
+    if raw_delta:  # delta before its activation, and the bias
+        delta, extra = eps.to(act), {"delta_raw": None, "dt_bias": bias}
+    else:
+        delta, extra = torch.nn.functional.softplus(eps.add_(bias)).to(act), {}
     del eps
     out = {"delta": delta, "x": normal(shape).to(act),
            "z": normal(shape).to(act) if cfg.gate else None,
            "Bt": normal((cfg.batch, cfg.L, cfg.N)).to(act), "Ct": normal((cfg.batch, cfg.L, cfg.N)).to(act)}
+    if raw_delta:
+        out["delta_raw"], out["dt_bias"] = out.pop("delta"), extra["dt_bias"]
     return out
 
 
-def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321):
+def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321, raw_delta: bool = False):
     """torch tensors for `steps` decode steps on `device` (same distributions as
     step_token_inputs, drawn with torch): x, delta, z of shape (steps, batch, D)
     and Bt, Ct of shape (steps, batch, N)."""
@@ -289,8 +310,12 @@ def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321):
     def normal(shp):
         return torch.randn(shp, generator=g, device=device, dtype=torch.float32)
 
-    eps = normal(shape)
-    delta = torch.nn.functional.softplus(eps.mul_(0.5).add_(bias)).to(act)
+    eps = normal(shape).mul_(0.5)
+    if raw_delta:  # delta before its activation; the bias is step_inputs' dt_bias
+        return {"delta_raw": eps.to(act), "x": normal(shape).to(act),
+                "z": normal(shape).to(act) if cfg.gate else None,
+                "Bt": normal((steps, cfg.batch, cfg.N)).to(act), "Ct": normal((steps, cfg.batch, cfg.N)).to(act)}
+    delta = torch.nn.functional.softplus(eps.add_(bias)).to(act)
     del eps
     return {"delta": delta, "x": normal(shape).to(act), "z": normal(shape).to(act) if cfg.gate else None,
             "Bt": normal((steps, cfg.batch, cfg.N)).to(act), "Ct": normal((steps, cfg.batch, cfg.N)).to(act)}
