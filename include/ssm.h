@@ -38,7 +38,8 @@
  *    rounded to nearest even.
  *  - N (state size) must be 1, 2, 4, 8 or 16.
  *  - delta is the step AFTER the softplus (the pages apply softplus to a
- *    projection plus bias before the scan).
+ *    projection plus bias before the scan). The *_dt entry points take the
+ *    step before it and apply softplus(delta_raw + dt_bias) themselves.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronise the host. Arguments are checked on the
  *    host before any HIP call; a failed check returns a negative status and
@@ -121,6 +122,27 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                  void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssm_scan_fwd with the step size given before its activation: the scan uses
+ * delta = softplus(delta_raw + dt_bias[d]), softplus(u) = log(1 + exp(u)).
+ * The pages make the step size the softplus of a projection of the input plus
+ * a bias ("Notas sobre Mamba", section "O mecanismo de seleção (S6)");
+ * delta_raw is that projection, computed upstream, and dt_bias the bias.
+ *
+ *   delta_raw     (batch, L, D)  dtype      step size before the activation
+ *   dt_bias       (D)            float      per-channel bias; NULL = zero
+ *
+ * Every other argument, the workspace and the status codes are those of
+ * ssm_scan_fwd. The activation is computed in float32 once per (token,
+ * channel). For bfloat16 activations the result is held as bfloat16 (round
+ * to nearest even), the precision of a delta handed over already activated.
+ */
+int ssm_scan_fwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                    const void *x, const void *delta_raw, const float *dt_bias, const float *A,
+                    const void *Bt, const void *Ct, const float *Dskip,
+                    const void *z, const float *state_in, float *state_out,
+                    void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for `batch` sequences (one token each), updating
  * the state in place.
  *
@@ -141,6 +163,18 @@ int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
              const void *x, const void *delta, const float *A,
              const void *Bt, const void *Ct, const float *Dskip,
              const void *z, float *state, void *y, void *stream);
+
+/*
+ * ssm_step with the step size given before its activation, as in
+ * ssm_scan_fwd_dt: delta = softplus(delta_raw + dt_bias[d]) in float32.
+ *
+ *   delta_raw     (batch, D)     dtype
+ *   dt_bias       (D)            float      NULL = zero
+ */
+int ssm_step_dt(int64_t batch, int64_t D, int64_t N, int dtype,
+                const void *x, const void *delta_raw, const float *dt_bias, const float *A,
+                const void *Bt, const void *Ct, const float *Dskip,
+                const void *z, float *state, void *y, void *stream);
 
 #ifdef __cplusplus
 }

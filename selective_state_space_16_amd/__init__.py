@@ -9,6 +9,8 @@ Functions (same names as the C ABI):
   ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None,
                state_out=None, y=None, workspace=None) -> y
   ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None) -> y
+  ssm_scan_fwd_dt / ssm_step_dt: the same with delta_raw and dt_bias in place
+      of delta; the kernels use softplus(delta_raw + dt_bias) as the step size
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
 """
@@ -19,7 +21,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step",
+    "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
     "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
@@ -33,7 +35,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libssm.so")
 
 # The functions include/ssm.h declares.
-EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step")
+EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
+           "ssm_scan_fwd_dt", "ssm_step_dt")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -64,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd.restype = ci
     L.ssm_step.argtypes = [i64, i64, i64, ci] + [vp] * 9 + [vp]
     L.ssm_step.restype = ci
+    L.ssm_scan_fwd_dt.argtypes = [i64, i64, i64, i64, ci] + [vp] * 11 + [vp, sz, vp]
+    L.ssm_scan_fwd_dt.restype = ci
+    L.ssm_step_dt.argtypes = [i64, i64, i64, ci] + [vp] * 10 + [vp]
+    L.ssm_step_dt.restype = ci
     _lib = L
     return L
 
@@ -125,11 +132,7 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_out=None,
-                 y=None, workspace=None, stream=None):
-    """Selective scan forward. Shapes: x, delta, z, y (batch, L, D); A (D, N);
-    Bt, Ct (batch, L, N); Dskip (D,); state_in, state_out (batch, D, N) float32.
-    Allocates y and the workspace with torch when they are not given."""
+def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream):
     import torch
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, D) and A (D, N)")
@@ -143,8 +146,12 @@ def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_o
     ws_bytes = ssm_scan_workspace_bytes(batch, L, D, N, code)
     if workspace is None and ws_bytes > 0:
         workspace = new_workspace(ws_bytes, x.device)
-    args = [
-        _ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(A, "A", f32, (D, N)),
+    dname = "delta_raw" if name == "ssm_scan_fwd_dt" else "delta"
+    args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, L, D))]
+    if name == "ssm_scan_fwd_dt":
+        args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
+    args += [
+        _ptr(A, "A", f32, (D, N)),
         _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
         _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
         _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(state_out, "state_out", f32, (batch, D, N)),
@@ -152,15 +159,30 @@ def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_o
     ]
     ws_ptr = _ptr(workspace, "workspace")
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ssm_scan_fwd(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
+    st = getattr(lib(), name)(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
     if st != 0:
-        raise SSMError(st, "ssm_scan_fwd")
+        raise SSMError(st, name)
     return y
 
 
-def ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None):
-    """One decode step. Shapes: x, delta, z, y (batch, D); A (D, N); Bt, Ct
-    (batch, N); Dskip (D,); state (batch, D, N) float32, updated in place."""
+def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_out=None,
+                 y=None, workspace=None, stream=None):
+    """Selective scan forward. Shapes: x, delta, z, y (batch, L, D); A (D, N);
+    Bt, Ct (batch, L, N); Dskip (D,); state_in, state_out (batch, D, N) float32.
+    Allocates y and the workspace with torch when they are not given."""
+    return _scan("ssm_scan_fwd", x, delta, None, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream)
+
+
+def ssm_scan_fwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_out=None,
+                    y=None, workspace=None, stream=None):
+    """ssm_scan_fwd with the step size before its activation: the kernel uses
+    softplus(delta_raw + dt_bias). delta_raw (batch, L, D); dt_bias (D,) float32
+    or None (zero)."""
+    return _scan("ssm_scan_fwd_dt", x, delta_raw, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y,
+                 workspace, stream)
+
+
+def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream):
     import torch
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, D) and A (D, N)")
@@ -171,13 +193,28 @@ def ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None
     f32 = torch.float32
     if y is None:
         y = torch.empty_like(x)
-    args = [
-        _ptr(x, "x", act), _ptr(delta, "delta", act, (batch, D)), _ptr(A, "A", f32, (D, N)),
+    dname = "delta_raw" if name == "ssm_step_dt" else "delta"
+    args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, D))]
+    if name == "ssm_step_dt":
+        args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
+    args += [
+        _ptr(A, "A", f32, (D, N)),
         _ptr(Bt, "Bt", act, (batch, N)), _ptr(Ct, "Ct", act, (batch, N)),
         _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, D)),
         _ptr(state, "state", f32, (batch, D, N)), _ptr(y, "y", act, (batch, D)),
     ]
-    st = lib().ssm_step(batch, D, N, code, *args, _stream(stream))
+    st = getattr(lib(), name)(batch, D, N, code, *args, _stream(stream))
     if st != 0:
-        raise SSMError(st, "ssm_step")
+        raise SSMError(st, name)
     return y
+
+
+def ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None):
+    """One decode step. Shapes: x, delta, z, y (batch, D); A (D, N); Bt, Ct
+    (batch, N); Dskip (D,); state (batch, D, N) float32, updated in place."""
+    return _step("ssm_step", x, delta, None, A, Bt, Ct, state, Dskip, z, y, stream)
+
+
+def ssm_step_dt(x, delta_raw, dt_bias, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None):
+    """ssm_step with the step size before its activation (see ssm_scan_fwd_dt)."""
+    return _step("ssm_step_dt", x, delta_raw, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream)

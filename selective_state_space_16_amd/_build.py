@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm.so")
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["ssm_scan.hip", "ssm_scan_stripe.hip", "ssm_step.hip", "ssm_abi.cpp"]
+SOURCES = ["ssm_scan_stripe_act.hip", "ssm_scan_stripe.hip", "ssm_scan.hip", "ssm_step.hip", "ssm_abi.cpp"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.
 # The atomic optimizer is off: it rewrites a one-lane atomic with a returned
@@ -34,12 +34,14 @@ def hipcc() -> str:
 
 
 def build(out: str = LIB, verbose: bool = False) -> str:
-    """Compile every source into one shared library (always rebuilds)."""
-    objs = []
+    """Compile every source into one shared library (always rebuilds). The
+    sources compile in parallel; the two tiled-scan files take the longest."""
+    from concurrent.futures import ThreadPoolExecutor
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
     cc = hipcc()
-    for src in SOURCES:
+
+    def compile_one(src):
         path = os.path.join(CSRC, src)
         obj = os.path.join(tmpdir, src + ".o")
         cmd = [cc] + HIP_FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
@@ -49,7 +51,10 @@ def build(out: str = LIB, verbose: bool = False) -> str:
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:

@@ -110,11 +110,11 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, 
     return workspace_for(batch, L, D, N, dtype);
 }
 
-int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
-                 const void *x, const void *delta, const float *A,
-                 const void *Bt, const void *Ct, const float *Dskip,
-                 const void *z, const float *state_in, float *state_out,
-                 void *y, void *workspace, size_t workspace_bytes, void *stream) {
+static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                    const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
+                    const void *Bt, const void *Ct, const float *Dskip,
+                    const void *z, const float *state_in, float *state_out,
+                    void *y, void *workspace, size_t workspace_bytes, void *stream) {
     if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
@@ -130,7 +130,7 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                                                                                           : SSM_ERR_HIP;
     }
     if (!x || !delta || !A || !Bt || !Ct || !y) return SSM_ERR_NULL;
-    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, state_out, y};
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, state_out, y, dt_bias};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
 
@@ -156,6 +156,8 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.Dskip = Dskip;
         a.state_in = state_in;
         a.state_out = state_out;
+        a.dt_bias = dt_bias;
+        a.delta_softplus = softplus;
         a.y = y;
         a.ntpb = p.ntpb;
         a.ncol = p.ncol;
@@ -183,6 +185,8 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.A = A;
     a.Dskip = Dskip;
     a.state_in = state_in;
+    a.dt_bias = dt_bias;
+    a.delta_softplus = softplus;
     a.state_out = state_out;
     a.y = y;
     if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
@@ -193,17 +197,17 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     return ssm::launch_scan(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
-             const void *x, const void *delta, const float *A,
-             const void *Bt, const void *Ct, const float *Dskip,
-             const void *z, float *state, void *y, void *stream) {
+static int step(int64_t batch, int64_t D, int64_t N, int dtype,
+                const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
+                const void *Bt, const void *Ct, const float *Dskip,
+                const void *z, float *state, void *y, void *stream) {
     if (batch < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
     if (checked_mul3(batch, D, N) < 0) return SSM_ERR_SHAPE;
     if (batch == 0 || D == 0) return SSM_OK;
     if (!x || !delta || !A || !Bt || !Ct || !state || !y) return SSM_ERR_NULL;
-    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y};
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y, dt_bias};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
     ssm::StepArgs a{};
@@ -218,7 +222,41 @@ int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
     a.Dskip = Dskip;
     a.state = state;
     a.y = y;
+    a.dt_bias = dt_bias;
+    a.delta_softplus = softplus;
     return ssm::launch_step(a, (int)N, dtype, (hipStream_t)stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A,
+                 const void *Bt, const void *Ct, const float *Dskip,
+                 const void *z, const float *state_in, float *state_out,
+                 void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    return scan_fwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, state_out, y,
+                    workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                    const void *x, const void *delta_raw, const float *dt_bias, const float *A,
+                    const void *Bt, const void *Ct, const float *Dskip,
+                    const void *z, const float *state_in, float *state_out,
+                    void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    return scan_fwd(batch, L, D, N, dtype, x, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state_in, state_out, y,
+                    workspace, workspace_bytes, stream);
+}
+
+int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
+             const void *x, const void *delta, const float *A,
+             const void *Bt, const void *Ct, const float *Dskip,
+             const void *z, float *state, void *y, void *stream) {
+    return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream);
+}
+
+int ssm_step_dt(int64_t batch, int64_t D, int64_t N, int dtype,
+                const void *x, const void *delta_raw, const float *dt_bias, const float *A,
+                const void *Bt, const void *Ct, const float *Dskip,
+                const void *z, float *state, void *y, void *stream) {
+    return step(batch, D, N, dtype, x, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state, y, stream);
 }
 
 }  // extern "C"

@@ -51,6 +51,29 @@ __device__ __forceinline__ void ld_row_uniform(const uint16_t *base, int64_t off
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(u) = log(1 + exp(u)) = max(u, 0) + log1p(exp(-|u|)). With
+// e = exp(-|u|) in (0, 1] and w = 1 + e rounded to float, log1p(e) is taken as
+// log(w) * e / (w - 1), or e when w == 1: the correction of D. Goldberg, "What
+// every computer scientist should know about floating-point arithmetic"
+// (ACM Computing Surveys, 1991), theorem 4, which keeps log1p accurate for
+// small e where log(1 + e) alone would lose it.
+__device__ __forceinline__ float softplus(float u) {
+    const float e = fast_exp2(-__builtin_fabsf(u) * kLog2e);
+    const float w = 1.0f + e;
+    const float l = w == 1.0f ? e : __builtin_amdgcn_logf(w) * kLn2 * (e * __builtin_amdgcn_rcpf(w - 1.0f));
+    return __builtin_fmaxf(u, 0.0f) + l;
+}
+
+// A value as the activation dtype holds it: unchanged for float, rounded to
+// the nearest bfloat16 (ties to even) for bfloat16.
+template <int DT>
+__device__ __forceinline__ float act_round(float v) {
+    if constexpr (DT == 0) return v;
+    else return (float)(__bf16)v;
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
 __device__ __forceinline__ float silu(float zv) {
     return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));

@@ -12,6 +12,8 @@ struct ScanArgs {
     int64_t batch, L, D;
     const void *x, *delta, *Bt, *Ct, *z;
     const float *A, *Dskip, *state_in;
+    const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
+    int delta_softplus;    // delta holds the raw step size: use softplus(delta + dt_bias)
     float *state_out;
     void *y;
     float *ws_state;   // (batch, K, D, N) chunk end states, then carried-in states
@@ -25,6 +27,8 @@ struct StripeArgs {
     int64_t batch, L, D;
     const void *x, *delta, *Bt, *Ct, *z;
     const float *A, *Dskip, *state_in;
+    const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
+    int delta_softplus;    // delta holds the raw step size: use softplus(delta + dt_bias)
     float *state_out;
     void *y;
     int64_t ntpb;           // tile columns per batch row
@@ -50,6 +54,8 @@ struct StepArgs {
     int64_t batch, D;
     const void *x, *delta, *Bt, *Ct, *z;
     const float *A, *Dskip;
+    const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
+    int delta_softplus;    // delta holds the raw step size: use softplus(delta + dt_bias)
     float *state;
     void *y;
 };
@@ -61,6 +67,8 @@ bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, Stri
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s);
+// The instances for a delta given before its activation (called by launch_scan_stripe).
+hipError_t launch_scan_stripe_act(const StripeArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepArgs &a, int N, int dtype, hipStream_t s);

@@ -72,12 +72,14 @@ __global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a) {
     const T *Cp = (const T *)a.Ct;
     T *yp = (T *)a.y;
     const float dskip = (SKIP && MODE == kFinal) ? a.Dskip[dc] : 0.0f;
+    const float dtb = a.dt_bias ? a.dt_bias[dc] : 0.0f;  // bias of a raw step size
 
     float dsum = 0.0f;
 #pragma unroll 4
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t row = (b * L + t) * D + dc;
-        const float dt = ld_act(dp, row);
+        float dt = ld_act(dp, row);
+        if (a.delta_softplus) dt = act_round<DT>(softplus(dt + dtb));
         const float xv = ld_act(xp, row);
         float Bv[N];
         ld_row_uniform<N>(Bp, (b * L + t) * N, Bv);

@@ -1,0 +1,752 @@
+// Selective scan (S6) forward for gfx950, organised by stripes: the kernel and
+// its launch, included by the two files that instantiate it (a delta given
+// after, and before, its activation).
+//
+// The recurrence h <- dA*h + dBx runs along the sequence independently for
+// every (batch row, channel, state) ("Notas sobre Mamba", section "A varredura
+// paralela ciente do hardware": an associative scan over (A-bar_t, B-bar_t
+// x_t) pairs, kept on chip, only y written back). Here a wave owns CPW
+// channels (16 for N = 16: four rows of 16 lanes, NL = 4 states per lane) and
+// walks the tokens of its stripe in order with the state in registers, so the
+// scan itself needs no communication at all: per token and state it is one
+// exponential, dA*h + B*(delta*x), and C*h accumulated into the readout.
+//
+// Work units. A workgroup of four waves covers a tile column of TCH = 4*CPW
+// channels of one batch row and a stripe of the sequence. When there are at
+// least as many tile columns as workgroup slots, a stripe is the whole
+// sequence and each unit is one pass. Otherwise every column is cut into S
+// stripes that run at the same time, and the carried-in state of a stripe is
+// found with the associative composition of affine maps: applying a run of
+// tokens to a state is the pair (P, S) with P = exp(A * sum delta) and S the
+// run's end state from a zero start. Pass 1 walks the stripe to get its own
+// (sum delta, S) and publishes it; a look-back then finds the nearest earlier
+// stripe whose end state is out and folds the pairs in between (the chain of
+// a handful of records, once per stripe); pass 2 walks the stripe again from
+// that state and writes y. Every record is a set of 64-bit words tagged with
+// the call's epoch, so a reader can validate each word without flags or
+// completion waits. The replay uses the same arithmetic each stripe uses for
+// its own end state, so results do not depend on timing.
+//
+// Memory. Tiles of TT tokens x TCH channels of x, delta (and z, for pass 2),
+// and the TT tokens of Bt (and Ct) are loaded into LDS with global_load_lds,
+// double-buffered so that the next tile streams in while this one is scanned;
+// channel rows are whole 128-byte lines (64 bfloat16 or, as two lines, 64
+// float channels). Waves 1..3 issue the loads; wave 0 writes the finished y
+// tile back as whole lines, so no wave ever waits for its own stores. A tile
+// column's A rows and skip weights live in registers.
+//
+// Scheduling. Units are handed out from one counter per list (eight lists, a
+// workgroup serves the list of its blockIdx modulo 8, i.e. its XCD; tile
+// columns are dealt to the lists round robin). Units are handed out in list
+// order with the stripes of a column in sequence order, so a stripe only ever
+// waits for stripes already held by running workgroups: the launch needs no
+// co-residency.
+#pragma once
+
+#include <atomic>
+#include <cstddef>
+
+#include "ssm_common.h"
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kWaves = 4;   // waves per workgroup (one per channel group)
+constexpr int kLists = 8;   // unit lists (one per XCD of an MI355X)
+constexpr int kReplay = 4;  // stripe records loaded per round trip of a look-back replay
+constexpr int kSlotsPerList = 64;  // workgroups a list is planned for (2 per CU on 256 CUs)
+
+template <int N, int DT>
+struct Geo {
+    using T = typename Act<DT>::T;
+    static constexpr int NL = N < 4 ? N : 4;       // states per lane
+    static constexpr int NGR = N / NL;             // rows per channel
+    static constexpr int CPW = (4 / NGR) * 16;     // channels per wave
+    static constexpr int TCH = kWaves * CPW;       // channels per tile column
+    static constexpr int TPV = 16 / NL;            // tokens per broadcast register
+    static constexpr int GROUP = TPV > 8 ? TPV : 8;  // tokens per register group
+    static constexpr int BREGS = GROUP / TPV;      // broadcast registers per group
+    static constexpr int OWN = GROUP / NGR;        // tokens of a group each lane finishes
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int VEC = 16 / ESZ;           // elements per 16-byte piece
+    // tokens per tile: three activation tiles of at most 24 KB
+    static constexpr int TT_RAW = 8192 / (TCH * ESZ);
+    static constexpr int TT = TT_RAW < 16 ? 16 : (TT_RAW > 64 ? 64 : TT_RAW);
+    static constexpr int PPR = TCH / VEC;           // pieces per tile row
+    static constexpr int ACT_PIECES = TT * PPR;     // pieces per activation tile (a multiple of 64)
+    static constexpr int BC_PIECES = TT * N / VEC;  // pieces per Bt/Ct tile
+    static constexpr int BC_SLOTS = (BC_PIECES + 63) / 64 * 64;
+    static_assert(ACT_PIECES % 64 == 0, "activation tiles are loaded in whole waves of pieces");
+};
+
+template <int N, int DT>
+struct TileBuf {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    // 16-byte aligned: pieces land here as whole 16-byte writes and y is read
+    // back as 16-byte reads
+    alignas(16) T x[G::TT][G::TCH];
+    alignas(16) T dl[G::TT][G::TCH];  // delta; pass 2 writes y here once a token's delta is used
+    alignas(16) T z[G::TT][G::TCH];
+    alignas(16) T B[G::BC_SLOTS * G::VEC];  // Bt rows of the tile's tokens (padded to whole waves of pieces)
+    alignas(16) T C[G::BC_SLOTS * G::VEC];
+};
+
+template <int N, int DT>
+struct Shared {
+    TileBuf<N, DT> buf[2];
+    int unit;  // the unit handed to this workgroup
+};
+
+template <int N, int DT>
+constexpr int stripe_min_blocks() { return 2 * sizeof(Shared<N, DT>) <= 160 * 1024 ? 2 : 1; }
+
+// An activation element of an LDS tile row, widened to float. A bfloat16 is
+// read as the 32-bit word holding it and its neighbour, and moved into the
+// high half of the result with one byte permute (`sel` depends only on the
+// element's parity): the loads then go straight to their own registers.
+__device__ __forceinline__ float lds_act(const float *row, int i, uint32_t) { return row[i]; }
+__device__ __forceinline__ float lds_act(const uint16_t *row, int i, uint32_t sel) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(row)[i >> 1];
+    return __uint_as_float(__builtin_amdgcn_perm(w, w, sel));
+}
+// Byte selector of lds_act for an element of this parity: bytes 1,0 (even) or
+// 3,2 (odd) of the word into bytes 3,2 of the result, zeros below.
+__device__ __forceinline__ uint32_t half_sel(int i) { return (i & 1) ? 0x03020c0cu : 0x01000c0cu; }
+
+// bfloat16 reads of an LDS tile straight into the high half of a register
+// whose low half is zero (it last held a value read this way, or 0.0f): the
+// register then holds the exact float, with no VALU work (the compiler does
+// not form these loads itself). Each block waits for its own loads, so no
+// register is read while its load is in flight. Addresses are a per-lane LDS
+// byte address plus immediate offsets, so a fully unrolled walk over a tile
+// needs no address arithmetic.
+//
+// Eight values of each of two arrays: value k at base + OA + k*STRIDE and at
+// base + OB + k*STRIDE.
+template <int STRIDE, int OA, int OB>
+__device__ __forceinline__ void lds_bf16_8x2(float (&va)[8], float (&vb)[8], uint32_t base) {
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %16 offset:%17\n\tds_read_u16_d16_hi %1, %16 offset:%18\n\t"
+        "ds_read_u16_d16_hi %2, %16 offset:%19\n\tds_read_u16_d16_hi %3, %16 offset:%20\n\t"
+        "ds_read_u16_d16_hi %4, %16 offset:%21\n\tds_read_u16_d16_hi %5, %16 offset:%22\n\t"
+        "ds_read_u16_d16_hi %6, %16 offset:%23\n\tds_read_u16_d16_hi %7, %16 offset:%24\n\t"
+        "ds_read_u16_d16_hi %8, %16 offset:%25\n\tds_read_u16_d16_hi %9, %16 offset:%26\n\t"
+        "ds_read_u16_d16_hi %10, %16 offset:%27\n\tds_read_u16_d16_hi %11, %16 offset:%28\n\t"
+        "ds_read_u16_d16_hi %12, %16 offset:%29\n\tds_read_u16_d16_hi %13, %16 offset:%30\n\t"
+        "ds_read_u16_d16_hi %14, %16 offset:%31\n\tds_read_u16_d16_hi %15, %16 offset:%32\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]),
+          "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]), "+v"(vb[4]), "+v"(vb[5]), "+v"(vb[6]), "+v"(vb[7])
+        : "v"(base), "i"(OA), "i"(OA + STRIDE), "i"(OA + 2 * STRIDE), "i"(OA + 3 * STRIDE), "i"(OA + 4 * STRIDE),
+          "i"(OA + 5 * STRIDE), "i"(OA + 6 * STRIDE), "i"(OA + 7 * STRIDE), "i"(OB), "i"(OB + STRIDE),
+          "i"(OB + 2 * STRIDE), "i"(OB + 3 * STRIDE), "i"(OB + 4 * STRIDE), "i"(OB + 5 * STRIDE),
+          "i"(OB + 6 * STRIDE), "i"(OB + 7 * STRIDE)
+        : "memory");
+}
+// Two values of each of four arrays: a at ab + OA + {0, SA}, b at ab + OB +
+// {0, SA}, c at cd + OC + {0, SC}, d at cd + OD + {0, SC}.
+template <int SA, int SC, int OA, int OB, int OC, int OD>
+__device__ __forceinline__ void lds_bf16_2x4(float (&va)[2], float (&vb)[2], float (&vc)[2], float (&vd)[2],
+                                             uint32_t ab, uint32_t cd) {
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %8 offset:%10\n\tds_read_u16_d16_hi %1, %8 offset:%11\n\t"
+        "ds_read_u16_d16_hi %2, %8 offset:%12\n\tds_read_u16_d16_hi %3, %8 offset:%13\n\t"
+        "ds_read_u16_d16_hi %4, %9 offset:%14\n\tds_read_u16_d16_hi %5, %9 offset:%15\n\t"
+        "ds_read_u16_d16_hi %6, %9 offset:%16\n\tds_read_u16_d16_hi %7, %9 offset:%17\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(va[0]), "+v"(va[1]), "+v"(vb[0]), "+v"(vb[1]), "+v"(vc[0]), "+v"(vc[1]), "+v"(vd[0]), "+v"(vd[1])
+        : "v"(ab), "v"(cd), "i"(OA), "i"(OA + SA), "i"(OB), "i"(OB + SA), "i"(OC), "i"(OC + SC), "i"(OD),
+          "i"(OD + SC)
+        : "memory");
+}
+// Two values of one array, at a + OA + {0, SA}.
+template <int SA, int OA>
+__device__ __forceinline__ void lds_bf16_2(float (&va)[2], uint32_t a) {
+    asm volatile("ds_read_u16_d16_hi %0, %2 offset:%3\n\tds_read_u16_d16_hi %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+                 : "+v"(va[0]), "+v"(va[1])
+                 : "v"(a), "i"(OA), "i"(OA + SA)
+                 : "memory");
+}
+
+// An empty volatile statement that reads and rewrites `st` and `x`: every
+// computation of those values comes before it and every use after it, and it
+// stays in order with the other volatile statements (the tile loads).
+template <int NL>
+__device__ __forceinline__ void order_point(float (&st)[NL], float &x) {
+    if constexpr (NL == 4) asm volatile("" : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]), "+v"(x));
+    else if constexpr (NL == 2) asm volatile("" : "+v"(st[0]), "+v"(st[1]), "+v"(x));
+    else asm volatile("" : "+v"(st[0]), "+v"(x));
+}
+
+__device__ __forceinline__ uint32_t take_unit(uint32_t *ctr) {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Load the tile of TT tokens starting at tt0 of tile column (b, ch0) into
+// LDS, spread over waves 1..3. Pass 1 needs x, delta and Bt; pass 2 also z
+// and Ct. Each wave moves slots of 64 16-byte pieces; a slot of an activation
+// array covers whole tile rows, so a piece's address is a wave-uniform row
+// address (SGPRs) plus the lane's offset within the slot, `act_off`, which is
+// the same for every tile of a unit. Only the last tile of a sequence, whose
+// rows may run past L, takes the per-piece path: pieces past the end of the
+// sequence are read from the last token instead, and the tokens are given
+// delta = 0 afterwards. Channels past D (a last, partial column) are read
+// from the last whole piece of the row and never stored.
+template <int N, int DT, bool GATE, int PASS, int WV>
+__device__ __forceinline__ void load_tile_w(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
+                                            int lane, uint32_t act_off) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr int NACT = (PASS == 2 && GATE) ? 3 : 2;
+    constexpr int NBC = PASS == 2 ? 2 : 1;
+    using TB = TileBuf<N, DT>;
+    const int64_t D = a.D, L = a.L;
+    if (tt0 + G::TT <= L) {
+        const uint32_t rowb = (uint32_t)(D * G::ESZ);
+        const int64_t off = ((b * L + tt0) * D + ch0) * G::ESZ;
+        const uint32_t lds_tb = lds_addr(&tb);
+        // the wave's slots: pieces (WV - 1) * 64 + 192 * k
+        static_for<0, (NACT * G::ACT_PIECES - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
+            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
+            constexpr int arr = base / G::ACT_PIECES;
+            constexpr int pa0 = base - arr * G::ACT_PIECES;  // first piece of the slot
+            const void *p = arr == 0 ? a.x : arr == 1 ? a.delta : a.z;
+            constexpr int dst = (arr == 0 ? offsetof(TB, x) : arr == 1 ? offsetof(TB, dl) : offsetof(TB, z)) + pa0 * 16;
+            dma16_s((const char *)p + off + (uint64_t)(pa0 / G::PPR) * rowb, act_off, lds_tb + dst);
+        });
+        const int64_t boff = (b * L + tt0) * N * G::ESZ;
+        static_for<0, (NBC * G::BC_SLOTS - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
+            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
+            constexpr int arr = base / G::BC_SLOTS;
+            constexpr int pq0 = base - arr * G::BC_SLOTS;
+            const int pq = pq0 + lane < G::BC_PIECES ? pq0 + lane : G::BC_PIECES - 1;  // padding repeats the last piece
+            constexpr int dst = (arr == 0 ? offsetof(TB, B) : offsetof(TB, C)) + pq0 * 16;
+            dma16_s((const char *)(arr == 0 ? a.Bt : a.Ct) + boff, (uint32_t)pq * 16, lds_tb + dst);
+        });
+        return;
+    }
+    const int w = WV;
+    for (int base = (w - 1) * 64; base < NACT * G::ACT_PIECES; base += 3 * 64) {
+        const int arr = base / G::ACT_PIECES;
+        const int pa = base - arr * G::ACT_PIECES + lane;
+        const int r = pa / G::PPR, c = (pa % G::PPR) * G::VEC;
+        int64_t t = tt0 + r;
+        t = t < L ? t : L - 1;
+        int64_t ch = ch0 + c;
+        ch = ch + G::VEC <= D ? ch : D - G::VEC;
+        const T *src = arr == 0 ? (const T *)a.x : arr == 1 ? (const T *)a.delta : (const T *)a.z;
+        T *dst = arr == 0 ? &tb.x[0][0] : arr == 1 ? &tb.dl[0][0] : &tb.z[0][0];
+        dma16(src + (b * L + t) * D + ch, lds_addr(dst + (int64_t)(base - arr * G::ACT_PIECES) * G::VEC));
+    }
+    for (int base = (w - 1) * 64; base < NBC * G::BC_SLOTS; base += 3 * 64) {
+        const int arr = base / G::BC_SLOTS;
+        int pq = base - arr * G::BC_SLOTS + lane;
+        pq = pq < G::BC_PIECES ? pq : G::BC_PIECES - 1;  // padding slots repeat the last piece
+        const int r = pq * G::VEC / N, c = pq * G::VEC % N;
+        int64_t t = tt0 + r;
+        t = t < L ? t : L - 1;
+        const T *src = arr == 0 ? (const T *)a.Bt : (const T *)a.Ct;
+        T *dst = arr == 0 ? tb.B : tb.C;
+        dma16(src + (b * L + t) * N + c, lds_addr(dst + (int64_t)(base - arr * G::BC_SLOTS) * G::VEC));
+    }
+}
+
+template <int N, int DT, bool GATE, int PASS>
+__device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
+                                          int w, int lane, uint32_t act_off) {
+    if (w == 1) load_tile_w<N, DT, GATE, PASS, 1>(tb, a, b, ch0, tt0, lane, act_off);
+    else if (w == 2) load_tile_w<N, DT, GATE, PASS, 2>(tb, a, b, ch0, tt0, lane, act_off);
+    else load_tile_w<N, DT, GATE, PASS, 3>(tb, a, b, ch0, tt0, lane, act_off);
+}
+
+// Step-size activation for a raw step: each loading wave applies
+// softplus(delta + dt_bias) to the delta pieces it loaded itself, once its
+// loads have landed and before the tile barrier, so every (token, channel)
+// is activated once. `dtb` holds the bias of the lane's VEC channels (the
+// lane's piece column is the same in every slot).
+template <int N, int DT>
+__device__ __forceinline__ void activate_delta(TileBuf<N, DT> &tb, int w, int lane, const float (&dtb)[Geo<N, DT>::VEC]) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    using VT = uint32_t __attribute__((ext_vector_type(4)));
+    // the wave's slots are pieces (w - 1) * 64 + 192 * k; those of the delta
+    // tile lie in [ACT_PIECES, 2 * ACT_PIECES)
+#pragma unroll 1
+    for (int base = (w - 1) * 64; base < 2 * G::ACT_PIECES; base += 3 * 64) {
+        if (base < G::ACT_PIECES) continue;
+        T *p = &tb.dl[0][0] + (int64_t)(base - G::ACT_PIECES + lane) * G::VEC;
+        VT v = *(const VT *)__builtin_assume_aligned(p, 16);
+        T e[G::VEC];
+        __builtin_memcpy(e, &v, sizeof(v));
+#pragma unroll
+        for (int k = 0; k < G::VEC; ++k) {
+            const float f = softplus(ld_act(e, k) + dtb[k]);
+            if constexpr (DT == 0) e[k] = f;
+            else e[k] = __builtin_bit_cast(uint16_t, (__bf16)f);
+        }
+        __builtin_memcpy(&v, e, sizeof(v));
+        *(VT *)__builtin_assume_aligned(p, 16) = v;
+    }
+}
+
+// One stripe record: NL state words per lane (and, for an aggregate, one
+// summed-delta word per lane), epoch-tagged. Word j of lane l sits at j*64 + l,
+// so each store instruction of a wave writes 512 contiguous bytes.
+template <int NL>
+__device__ __forceinline__ void publish_state(uint64_t *rec, int l, const float (&S)[NL], uint32_t epoch) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) st_tagged(rec + j * 64 + l, S[j], epoch);
+}
+
+// SP: delta holds the step size before its activation (softplus(delta +
+// dt_bias), applied to each tile as it lands); a separate instance, so that
+// the kernels for an activated delta carry none of that code.
+template <int N, int DT, bool GATE, bool SKIP, bool SP>
+__global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void scan_stripe_kernel(StripeArgs a) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TCH = G::TCH, TPV = G::TPV, BREGS = G::BREGS;
+    constexpr int TT = G::TT, GROUP = G::GROUP;
+
+    __shared__ Shared<N, DT> sh;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
+    const int l = threadIdx.x & 63;
+    const int row = l >> 4, k16 = l & 15;
+    const int g = row % NGR;                            // state group of this lane
+    const int nstate0 = g * NL;
+    const int cl = w * CPW + (row / NGR) * 16 + k16;    // channel within the tile column
+    const uint32_t sel_ch = half_sel(cl);                 // lds_act selectors: this lane's channel
+    const uint32_t sel_st = half_sel(k16 % NL);           // and its Bt/Ct element (nstate0 is even)
+    const int64_t D = a.D, L = a.L;
+    const int64_t n_whole = a.n_whole, n_split = a.cols_per_list - a.n_whole;
+
+    const int list = blockIdx.x % kLists;
+    uint32_t *const counter = a.counters + list;
+    const uint32_t units = (uint32_t)(n_whole + n_split * a.S);
+    // every workgroup takes units until it is handed one past the end, so a
+    // call makes exactly (units + workgroups of the list) takes; the last one
+    // puts the counter back to zero for the next call
+    const uint32_t last_take = units + gridDim.x / kLists - 1;
+
+    while (true) {
+        if (w == 0 && l == 0) {
+            const uint32_t u = take_unit(counter);
+            if (u == last_take) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sh.unit = (int)u;
+        }
+        lds_barrier();
+        const uint32_t u = (uint32_t)__builtin_amdgcn_readfirstlane(sh.unit);
+        if (u >= units) break;
+        // The list's first n_whole columns are whole-sequence units; each of
+        // the others is cut into S stripes (which fill the last round).
+        const bool whole = u < n_whole;
+        const int64_t S = whole ? 1 : a.S;
+        const int64_t SL = whole ? L : a.SL;
+        const int64_t cs = whole ? 0 : (u - n_whole) / S;       // split column index
+        const int64_t j = whole ? 0 : (u - n_whole) % S;        // stripe
+        const int64_t col = list + (int64_t)kLists * (whole ? u : n_whole + cs);  // tile column
+        if (col >= a.ncol) {
+            lds_barrier();  // sh.unit is rewritten at the top
+            continue;
+        }
+        const int64_t b = col / a.ntpb;
+        const int64_t ch0 = (col % a.ntpb) * TCH;
+        const int64_t d = ch0 + cl;
+        const bool valid = d < D;
+        // this lane's byte offset within an activation slot of a tile (see load_tile)
+        int64_t lane_ch = ch0 + (l % G::PPR) * G::VEC;
+        lane_ch = lane_ch + G::VEC <= D ? lane_ch : D - G::VEC;
+        const uint32_t act_off = (uint32_t)((l / G::PPR) * D + (lane_ch - ch0)) * G::ESZ;
+        // bias of the raw step size for the channels of this lane's pieces
+        float dtb[G::VEC];
+#pragma unroll
+        for (int k = 0; k < G::VEC; ++k) dtb[k] = (SP && a.dt_bias) ? a.dt_bias[lane_ch + k] : 0.0f;
+        const int64_t dc = valid ? d : D - 1;
+        const int64_t t0 = j * SL;
+        const int64_t t1 = t0 + SL < L ? t0 + SL : L;
+        const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
+        const bool has_next = j + 1 < S;  // a later stripe needs this one's end state
+
+        float A2[NL];
+#pragma unroll
+        for (int q = 0; q < NL; ++q) A2[q] = a.A[dc * N + nstate0 + q] * kLog2e;
+        const float dskip = SKIP ? a.Dskip[dc] : 0.0f;
+        // records of stripe jj of this column, for this wave
+        const int64_t rec0 = ((int64_t)list * n_split + cs) * S;
+        auto rec_of = [&](int64_t jj) { return (rec0 + jj) * kWaves + w; };
+        const int64_t rec = rec_of(j);
+
+        // Walk the stripe's tiles: PASS 1 folds (dA, dBx) from a zero start,
+        // PASS 2 runs the recurrence from h and writes y.
+        float h[NL];
+        // The finished y of tile i (pass 2): every wave writes a share of it back
+        // as whole lines from the tile's delta area.
+        auto store_y = [&](const TileBuf<N, DT> &tb, int i) {
+            using VT = uint32_t __attribute__((ext_vector_type(4)));
+            const int64_t tt0 = t0 + (int64_t)i * TT;
+            const int64_t rows = t1 - tt0;  // tokens of the tile inside the stripe
+            T *yptr = (T *)a.y;
+#pragma unroll
+            for (int p = threadIdx.x; p < G::ACT_PIECES; p += 64 * kWaves) {
+                const int r = p / G::PPR, c = (p % G::PPR) * G::VEC;
+                if (r < rows && ch0 + c < D) {
+                    const VT v = *(const VT *)__builtin_assume_aligned(&tb.dl[r][c], 16);
+                    *(VT *)(yptr + (b * L + tt0 + r) * D + ch0 + c) = v;
+                }
+            }
+        };
+        // First tile of a pass, loaded ahead (before the look-back, for pass 2).
+        auto prefetch = [&](auto pass_c) {
+            constexpr int PASS = decltype(pass_c)::value;
+            if (w > 0) load_tile<N, DT, GATE, PASS>(sh.buf[0], a, b, ch0, t0, w, l, act_off);
+        };
+        auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
+            constexpr int PASS = decltype(pass_c)::value;
+            // bfloat16 groups of 8 tokens with two broadcast registers and two
+            // finished tokens per lane take the high-half loads
+            constexpr bool kHiLoads = DT == 1 && GROUP == 8 && BREGS == 2 && G::OWN == 2;
+            float xv[GROUP], dv[GROUP], Bq[BREGS], Cq[BREGS], xo[G::OWN], zo[G::OWN];
+#pragma unroll
+            for (int t = 0; t < GROUP; ++t) xv[t] = dv[t] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < BREGS; ++q) Bq[q] = Cq[q] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < G::OWN; ++q) xo[q] = zo[q] = 0.0f;
+            if (w > 0) vm_wait();  // the first tile (prefetch) has landed
+            if constexpr (SP) {
+                if (w > 0) activate_delta(sh.buf[0], w, l, dtb);
+            }
+            lds_barrier();
+            for (int i = 0; i < ntiles; ++i) {
+                TileBuf<N, DT> &tb = sh.buf[i & 1];
+                const int64_t tt0 = t0 + (int64_t)i * TT;
+                if constexpr (PASS == 2) {
+                    // y of the previous tile goes out now, so that the stores
+                    // complete behind this tile's scan; its buffer is loaded next
+                    if (i > 0) {
+                        store_y(sh.buf[(i - 1) & 1], i - 1);
+                        lds_barrier();
+                    }
+                }
+                if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l, act_off);
+                const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
+                if (tail < TT) {
+                    // tokens past the end were loaded from the last token; give
+                    // them delta = 0 so that they leave the state unchanged
+                    for (int q = threadIdx.x; q < (TT - (int)tail) * TCH; q += 64 * kWaves)
+                        tb.dl[tail + q / TCH][q % TCH] = T(0.0f);
+                    lds_barrier();
+                }
+                // per-lane LDS byte addresses in this tile: the lane's channel
+                // column, its Bt/Ct element and its first owned token's row
+                using TB = TileBuf<N, DT>;
+                constexpr int ROWB = TCH * G::ESZ, BCB = N * G::ESZ;
+                constexpr int OFF_DL = offsetof(TB, dl), OFF_Z = offsetof(TB, z);
+                constexpr int OFF_B = offsetof(TB, B), OFF_C = offsetof(TB, C);
+                const uint32_t a_ch = lds_addr(&tb) + cl * G::ESZ;
+                const uint32_t a_bc = lds_addr(&tb) + OFF_B + ((k16 / NL) * N + nstate0 + (k16 % NL)) * G::ESZ;
+                const uint32_t a_own = a_ch + g * ROWB;
+                static_for<0, TT / GROUP>([&](auto gc) {
+                    constexpr int tg = decltype(gc)::value * GROUP;
+                    // Keep the groups in order: the previous group's state
+                    // and summed delta pass through here before this group's
+                    // loads are issued, so the compiler cannot hoist the
+                    // loads of later groups above earlier arithmetic (which
+                    // would keep every group's values live at once). The
+                    // activation code of SP made the compiler do that.
+                    if constexpr (SP) order_point<NL>(st, dsum);
+                    if constexpr (kHiLoads) {
+                        // bfloat16: loads into the high halves of the registers
+                        // that held the previous group's values
+                        lds_bf16_8x2<ROWB, tg * ROWB, OFF_DL + tg * ROWB>(xv, dv, a_ch);
+                        if constexpr (PASS == 2) {
+                            lds_bf16_2x4<TPV * BCB, NGR * ROWB, tg * BCB, OFF_C - OFF_B + tg * BCB, tg * ROWB,
+                                         OFF_Z + tg * ROWB>(Bq, Cq, xo, zo, a_bc, a_own);
+                        } else {
+                            lds_bf16_2<TPV * BCB, tg * BCB>(Bq, a_bc);
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < GROUP; ++t) {
+                            xv[t] = lds_act(&tb.x[tg + t][0], cl, sel_ch);
+                            dv[t] = lds_act(&tb.dl[tg + t][0], cl, sel_ch);
+                        }
+#pragma unroll
+                        for (int q = 0; q < BREGS; ++q) {
+                            const int tw = tg + q * TPV + k16 / NL;
+                            Bq[q] = lds_act(&tb.B[tw * N], nstate0 + (k16 % NL), sel_st);
+                            if constexpr (PASS == 2) Cq[q] = lds_act(&tb.C[tw * N], nstate0 + (k16 % NL), sel_st);
+                        }
+                        if constexpr (PASS == 2) {
+                            // x and z of the tokens this lane finishes (token NGR*q + g of the group)
+#pragma unroll
+                            for (int q = 0; q < G::OWN; ++q) {
+                                const int tw = tg + NGR * q + g;
+                                xo[q] = SKIP ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
+                                zo[q] = GATE ? lds_act(&tb.z[tw][0], cl, sel_ch) : 0.0f;
+                            }
+                        }
+                    }
+                    if constexpr (PASS == 1) {
+                        static_for<0, GROUP>([&](auto tc) {
+                            constexpr int t = decltype(tc)::value;
+                            const float dx = dv[t] * xv[t];
+                            dsum += dv[t];
+                            static_for<0, NL>([&](auto jc) {
+                                constexpr int q = decltype(jc)::value;
+                                const float dA = fast_exp2(dv[t] * A2[q]);
+                                st[q] = __builtin_fmaf(dA, st[q], row_bcast<(t % TPV) * NL + q>(Bq[t / TPV]) * dx);
+                            });
+                        });
+                    } else {
+                        float yp[GROUP];
+                        static_for<0, GROUP>([&](auto tc) {
+                            constexpr int t = decltype(tc)::value;
+                            const float dx = dv[t] * xv[t];
+                            static_for<0, NL>([&](auto jc) {
+                                constexpr int q = decltype(jc)::value;
+                                const float dA = fast_exp2(dv[t] * A2[q]);
+                                st[q] = __builtin_fmaf(dA, st[q], row_bcast<(t % TPV) * NL + q>(Bq[t / TPV]) * dx);
+                            });
+                            dot_row<NL, (t % TPV) * NL>(yp[t], Cq[t / TPV], st);
+                        });
+                        // Sum the partial readouts over a channel's rows; afterwards
+                        // row r holds the finished token NGR*q + (r % NGR) of group q.
+                        float yo[G::OWN];
+                        if constexpr (NGR == 4) {
+#pragma unroll
+                            for (int q = 0; q < GROUP / 4; ++q) {
+                                float a0 = yp[4 * q + 0], a2 = yp[4 * q + 2], a1 = yp[4 * q + 1], a3 = yp[4 * q + 3];
+                                swap_halves(a0, a2);  // rows 0,1: token 0 | rows 2,3: token 2
+                                swap_halves(a1, a3);  // rows 0,1: token 1 | rows 2,3: token 3
+                                float s02 = a0 + a2, s13 = a1 + a3;
+                                swap_odd_even_rows(s02, s13);
+                                yo[q] = s02 + s13;
+                            }
+                        } else if constexpr (NGR == 2) {
+#pragma unroll
+                            for (int q = 0; q < GROUP / 2; ++q) {
+                                float a0 = yp[2 * q + 0], a1 = yp[2 * q + 1];
+                                swap_odd_even_rows(a0, a1);
+                                yo[q] = a0 + a1;
+                            }
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < GROUP; ++q) yo[q] = yp[q];
+                        }
+                        // Finish the owned tokens (D skip, silu gate) into the tile.
+#pragma unroll
+                        for (int q = 0; q < G::OWN; ++q) {
+                            const int tw = tg + NGR * q + g;
+                            float yv = yo[q];
+                            if (SKIP) yv = __builtin_fmaf(dskip, xo[q], yv);
+                            if (GATE) yv *= silu(zo[q]);
+                            st_act(&tb.dl[tw][0], cl, yv);
+                        }
+                    }
+                });
+                vm_wait();  // the next tile has landed (and this wave's earlier y stores are out)
+                if constexpr (SP) {
+                    if (w > 0 && i + 1 < ntiles) activate_delta(sh.buf[(i + 1) & 1], w, l, dtb);
+                }
+                lds_barrier();
+            }
+            if constexpr (PASS == 2) store_y(sh.buf[(ntiles - 1) & 1], ntiles - 1);
+        };
+
+        float agg[NL], dagg = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NL; ++q) agg[q] = 0.0f;
+        if (has_next && j > 0) {
+            prefetch(std::integral_constant<int, 1>{});
+            walk(std::integral_constant<int, 1>{}, agg, dagg);
+            uint64_t *ar = a.agg + rec * (64 * (NL + 1));
+            publish_state<NL>(ar, l, agg, a.epoch);
+            st_tagged(ar + 64 * NL + l, dagg, a.epoch);
+        } else if (has_next) {
+            prefetch(std::integral_constant<int, 1>{});
+            walk(std::integral_constant<int, 1>{}, agg, dagg);  // stripe 0: its end state goes out directly
+        }
+        prefetch(std::integral_constant<int, 2>{});  // lands during the look-back
+
+        // Carried-in state of this stripe.
+        if (j == 0) {
+            const float *si = a.state_in ? a.state_in + (b * D + dc) * N + nstate0 : nullptr;
+#pragma unroll
+            for (int q = 0; q < NL; ++q) h[q] = si ? si[q] : 0.0f;
+        } else {
+            // Look back over the earlier stripes of this column: the nearest
+            // one whose end state is out, with the aggregates of all stripes
+            // after it out.
+            int64_t j0 = -1;
+            long spin = 0;
+            while (true) {
+                const int64_t jj = j - 1 - l;  // stripe examined by this lane
+                bool inc = false, ag = false;
+                if (jj >= 0) {
+                    // the first word of a record stands for all of it; the
+                    // replay below still checks every word it reads
+                    const int64_t r2 = rec_of(jj);
+                    inc = (uint32_t)(ld_tagged(a.incl + r2 * (64 * NL)) >> 32) == a.epoch;
+                    ag = inc || (uint32_t)(ld_tagged(a.agg + r2 * (64 * (NL + 1))) >> 32) == a.epoch;
+                }
+                const uint64_t m_inc = __builtin_amdgcn_ballot_w64(inc);
+                const uint64_t m_agg = __builtin_amdgcn_ballot_w64(ag);
+                if (m_inc) {
+                    const int i0 = __builtin_ctzll(m_inc);
+                    const uint64_t below = i0 == 0 ? 0 : (~0ull >> (64 - i0));
+                    if ((m_agg & below) == below) {
+                        j0 = j - 1 - i0;
+                        break;
+                    }
+                }
+                if (++spin > kSpinLimit ||
+                    (spin % 64 == 0 && __builtin_amdgcn_readfirstlane(ld_flag(a.error)) != 0)) {
+                    if (l == 0) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+            if (j0 < 0) {
+#pragma unroll
+                for (int q = 0; q < NL; ++q) h[q] = 0.0f;
+            } else {
+                // Replay forward from that state with the arithmetic each
+                // stripe uses for its own end state, kReplay records per
+                // round trip.
+                const uint64_t *src = a.incl + rec_of(j0) * (64 * NL) + l;
+#pragma unroll
+                for (int q = 0; q < NL; ++q) h[q] = __uint_as_float((uint32_t)ld_valid(src + q * 64, a.epoch));
+                for (int64_t jj = j0 + 1; jj < j; jj += kReplay) {
+                    uint64_t sv[kReplay][NL], dv2[kReplay];
+#pragma unroll
+                    for (int r = 0; r < kReplay; ++r) {
+                        if (jj + r < j) {
+                            const uint64_t *ar = a.agg + rec_of(jj + r) * (64 * (NL + 1));
+#pragma unroll
+                            for (int q = 0; q < NL; ++q) sv[r][q] = ld_tagged(ar + q * 64 + l);
+                            dv2[r] = ld_tagged(ar + 64 * NL + l);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < kReplay; ++r) {
+                        if (jj + r < j) {
+                            const uint64_t *ar = a.agg + rec_of(jj + r) * (64 * (NL + 1));
+                            const float dd = __uint_as_float((uint32_t)recheck(dv2[r], ar + 64 * NL + l, a.epoch));
+#pragma unroll
+                            for (int q = 0; q < NL; ++q)
+                                h[q] = __builtin_fmaf(fast_exp2(A2[q] * dd), h[q],
+                                                      __uint_as_float((uint32_t)recheck(sv[r][q], ar + q * 64 + l, a.epoch)));
+                        }
+                    }
+                }
+            }
+        }
+        if (has_next) {
+            // this stripe's end state, for the stripes after it
+            float e[NL];
+#pragma unroll
+            for (int q = 0; q < NL; ++q) e[q] = __builtin_fmaf(fast_exp2(A2[q] * dagg), h[q], agg[q]);
+            publish_state<NL>(a.incl + rec * (64 * NL), l, e, a.epoch);
+        }
+
+        float unused = 0.0f;
+        walk(std::integral_constant<int, 2>{}, h, unused);
+        if (!has_next && a.state_out && valid) {
+            float *so = a.state_out + (b * D + d) * N + nstate0;
+#pragma unroll
+            for (int q = 0; q < NL; ++q) so[q] = h[q];
+        }
+    }
+}
+
+template <int N, int DT, bool GATE, bool SKIP, bool SP>
+hipError_t launch_stripe_typed(const StripeArgs &a, hipStream_t s) {
+    auto kern = scan_stripe_kernel<N, DT, GATE, SKIP, SP>;
+    constexpr int kMaxDevices = 64;
+    // CU count and resident workgroups per CU, queried once per device:
+    // (cus << 32 | per_cu), 0 = not queried yet
+    static std::atomic<uint64_t> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    uint64_t packed = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (packed == 0) {
+        int cus = 0, per_cu = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kWaves, 0)) != hipSuccess) return e;
+        if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+        packed = (uint64_t)cus << 32 | (uint32_t)per_cu;
+        if (dev < kMaxDevices) cache[dev].store(packed, std::memory_order_relaxed);
+    }
+    const int cus = (int)(packed >> 32), per_cu = (int)(uint32_t)packed;
+    int64_t per_list = (int64_t)cus * per_cu / kLists;
+    const int64_t units = a.n_whole + (a.cols_per_list - a.n_whole) * a.S;
+    if (per_list > units) per_list = units;
+    if (per_list < 1) per_list = 1;
+    StripeArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel((const void *)kern, dim3((unsigned)(per_list * kLists)), dim3(64 * kWaves), params, 0, s);
+}
+
+template <int N, int DT, bool SP>
+hipError_t launch_stripe_flags(const StripeArgs &a, hipStream_t s) {
+    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
+    if (gate && skip) return launch_stripe_typed<N, DT, true, true, SP>(a, s);
+    if (gate) return launch_stripe_typed<N, DT, true, false, SP>(a, s);
+    if (skip) return launch_stripe_typed<N, DT, false, true, SP>(a, s);
+    return launch_stripe_typed<N, DT, false, false, SP>(a, s);
+}
+
+template <int N, bool SP>
+hipError_t launch_stripe_dtype(const StripeArgs &a, int dtype, hipStream_t s) {
+    return dtype == 0 ? launch_stripe_flags<N, 0, SP>(a, s) : launch_stripe_flags<N, 1, SP>(a, s);
+}
+
+template <bool SP>
+hipError_t launch_stripe_n(const StripeArgs &a, int N, int dtype, hipStream_t s) {
+    switch (N) {
+        case 1: return launch_stripe_dtype<1, SP>(a, dtype, s);
+        case 2: return launch_stripe_dtype<2, SP>(a, dtype, s);
+        case 4: return launch_stripe_dtype<4, SP>(a, dtype, s);
+        case 8: return launch_stripe_dtype<8, SP>(a, dtype, s);
+        case 16: return launch_stripe_dtype<16, SP>(a, dtype, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int N, int DT>
+void stripe_geometry(int64_t batch, int64_t L, int64_t D, StripePlan *p) {
+    using G = Geo<N, DT>;
+    p->nl = G::NL;
+    p->tch = G::TCH;
+    p->tt = G::TT;
+    p->vec = G::VEC;
+    p->ntpb = (D + G::TCH - 1) / G::TCH;
+    p->ncol = batch * p->ntpb;
+    p->cols_per_list = (p->ncol + kLists - 1) / kLists;
+    // Columns that fill whole rounds of the planned workgroup slots run as
+    // whole-sequence units; the rest are cut into S stripes each, so that
+    // the last round is full too.
+    const int64_t C = p->cols_per_list;
+    const int64_t tiles = (L + G::TT - 1) / G::TT;
+    const int64_t rem = C >= kSlotsPerList ? C % kSlotsPerList : C;
+    int64_t S = rem > 0 ? kSlotsPerList / rem : 1;
+    if (S > 64) S = 64;  // the look-back examines at most 64 earlier stripes at once
+    if (S > tiles) S = tiles;
+    if (S < 1) S = 1;
+    const int64_t tiles_per_stripe = (tiles + S - 1) / S;
+    S = tiles > 0 ? (tiles + tiles_per_stripe - 1) / tiles_per_stripe : 1;
+    p->SL = tiles_per_stripe * G::TT;
+    p->S = S;
+    p->n_whole = S > 1 ? C - rem : C;
+}
+
+}  // namespace
+
+}  // namespace ssm

@@ -84,8 +84,9 @@ __device__ __forceinline__ float from_lane(int src, float v) {
 }
 
 // Grid: x = block of kBlockCh channels, y = group of kRows batch rows
-// (strided by gridDim.y when the groups outnumber kMaxGridY).
-template <int N, int DT, bool GATE, bool SKIP>
+// (strided by gridDim.y when the groups outnumber kMaxGridY). SP: delta holds
+// the step size before its activation, softplus(delta + dt_bias).
+template <int N, int DT, bool GATE, bool SKIP, bool SP>
 __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
     using T = typename Act<DT>::T;
     constexpr int NPL = N < 4 ? N : 4;
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int q = 0; q < LPC; ++q) ld_vec<NPL>(a.A + chq[q] * N + n0, A2[q]);
     const float ds = SKIP ? a.Dskip[own] : 0.0f;
+    const float dtb = (SP && a.dt_bias) ? a.dt_bias[own] : 0.0f;  // bias of a raw step size
 #pragma unroll
     for (int q = 0; q < LPC; ++q)
 #pragma unroll
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
             const int64_t row = bc[r] * D + own;
             xo[r] = ld_act(xp, row);
             dto[r] = ld_act(dp, row);
+            if constexpr (SP) dto[r] = act_round<DT>(softplus(dto[r] + dtb));
             if (GATE) zo[r] = ld_act((const T *)a.z, row);
             braw[r] = BC::load(Bp + bc[r] * N + n0);
             craw[r] = BC::load(Cp + bc[r] * N + n0);
@@ -184,22 +187,28 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
     }
 }
 
-template <int N, int DT, bool GATE, bool SKIP>
+template <int N, int DT, bool GATE, bool SKIP, bool SP>
 hipError_t launch_step_typed(const StepArgs &a, hipStream_t s) {
     const int64_t groups = (a.batch + kRows - 1) / kRows;
     if ((a.D + kBlockCh - 1) / kBlockCh > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((a.D + kBlockCh - 1) / kBlockCh), (unsigned)(groups < kMaxGridY ? groups : kMaxGridY));
-    hipLaunchKernelGGL((step_kernel<N, DT, GATE, SKIP>), grid, dim3(kStepBlock), 0, s, a);
+    hipLaunchKernelGGL((step_kernel<N, DT, GATE, SKIP, SP>), grid, dim3(kStepBlock), 0, s, a);
     return hipGetLastError();
 }
 
 template <int N, int DT>
 hipError_t launch_step_flags(const StepArgs &a, hipStream_t s) {
     const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
-    if (gate && skip) return launch_step_typed<N, DT, true, true>(a, s);
-    if (gate) return launch_step_typed<N, DT, true, false>(a, s);
-    if (skip) return launch_step_typed<N, DT, false, true>(a, s);
-    return launch_step_typed<N, DT, false, false>(a, s);
+    if (a.delta_softplus) {
+        if (gate && skip) return launch_step_typed<N, DT, true, true, true>(a, s);
+        if (gate) return launch_step_typed<N, DT, true, false, true>(a, s);
+        if (skip) return launch_step_typed<N, DT, false, true, true>(a, s);
+        return launch_step_typed<N, DT, false, false, true>(a, s);
+    }
+    if (gate && skip) return launch_step_typed<N, DT, true, true, false>(a, s);
+    if (gate) return launch_step_typed<N, DT, true, false, false>(a, s);
+    if (skip) return launch_step_typed<N, DT, false, true, false>(a, s);
+    return launch_step_typed<N, DT, false, false, false>(a, s);
 }
 
 template <int N>

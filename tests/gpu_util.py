@@ -76,3 +76,21 @@ def gpu_scan(inp, want_state=True, state_alias=False):
 
 def oracle_scan(inp, dtype):
     return oracle.get().scan(inp, dtype)
+
+
+def gpu_scan_dt(inp, dt_bias=True):
+    """Run ssm_scan_fwd_dt on stored inputs (inp["delta_raw"], inp["dt_bias"]);
+    returns (y64, state64). With dt_bias=False the bias argument is NULL."""
+    import torch
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    batch, L, D = dev["x"].shape
+    N = dev["A"].shape[1]
+    st_out = torch.empty((batch, D, N), dtype=torch.float32, device="cuda")
+    ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(batch, L, D, N,
+                                                        0 if dev["x"].dtype == torch.float32 else 1))
+    y = ssm.ssm_scan_fwd_dt(dev["x"], dev["delta_raw"], dev["dt_bias"] if dt_bias else None, dev["A"], dev["Bt"],
+                            dev["Ct"], Dskip=dev["Dskip"], z=dev["z"], state_in=dev["state_in"], state_out=st_out,
+                            workspace=ws)
+    torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
+    return to_f64(y), to_f64(st_out)

@@ -112,3 +112,42 @@ def test_binding_refuses_cpu_tensors():
     A = torch.zeros(8, 16)
     with pytest.raises((ValueError, TypeError)):
         ssm.ssm_scan_fwd(x, x, A, torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
+
+
+def scan_dt(**kw):
+    a = dict(batch=1, L=8, D=64, N=16, dtype=0, x=P, delta_raw=P, dt_bias=None, A=P, Bt=P, Ct=P, Dskip=None,
+             z=None, state_in=None, state_out=None, y=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_fwd_dt(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["delta_raw"],
+                                     a["dt_bias"], a["A"], a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state_in"],
+                                     a["state_out"], a["y"], a["ws"], a["wsb"], a["stream"])
+
+
+def step_dt(**kw):
+    a = dict(batch=1, D=64, N=16, dtype=0, x=P, delta_raw=P, dt_bias=None, A=P, Bt=P, Ct=P, Dskip=None,
+             z=None, state=P, y=P, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_step_dt(a["batch"], a["D"], a["N"], a["dtype"], a["x"], a["delta_raw"], a["dt_bias"],
+                                 a["A"], a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=3), -4), (dict(delta_raw=None), -1),
+    (dict(y=None), -1), (dict(dt_bias=MIS), -5), (dict(x=MIS), -5),
+    (dict(L=1 << 20, D=64), -6),
+])
+def test_scan_dt_rejects(kw, code):
+    assert scan_dt(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=5), -4), (dict(delta_raw=None), -1),
+    (dict(state=None), -1), (dict(dt_bias=MIS), -5),
+])
+def test_step_dt_rejects(kw, code):
+    assert step_dt(**kw) == code
+
+
+def test_dt_entry_points_empty_ok_without_gpu():
+    assert scan_dt(batch=0) == 0 and scan_dt(D=0) == 0
+    assert step_dt(batch=0) == 0 and step_dt(D=0) == 0
