@@ -131,19 +131,21 @@ def bench_scan(args, name):
     log(f"[bench] workload {cfg}")
     t0 = time.time()
     # set 0: the seeded numpy streams (checked against the oracle below)
-    inp = W.scan_inputs(cfg) if name != "c3" else None
+    sp = args.softplus  # delta handed over before its activation
+    inp = W.scan_inputs(cfg, raw_delta=sp) if name != "c3" else None
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
     whole = W.scan_inputs(cfg, 0, 0)
     A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
     st_in = to_dev(whole["state_in"])
     sets = []
     if inp is not None:
-        sets.append({k: to_dev(inp[k]) for k in ("x", "delta", "z", "Bt", "Ct")})
+        keys = ("x", "delta_raw", "dt_bias", "z", "Bt", "Ct") if sp else ("x", "delta", "z", "Bt", "Ct")
+        sets.append({k: to_dev(inp[k]) for k in keys})
     # further sets: same distributions, drawn on the GPU
     per_set = W.scan_bytes(cfg)
     nsets = max(1, min(args.rotate, int(60e9 // max(per_set, 1))))
     while len(sets) < nsets:
-        sets.append(W.fill_scan_device(cfg, "cuda", seed=1000 + len(sets)))
+        sets.append(W.fill_scan_device(cfg, "cuda", seed=1000 + len(sets), raw_delta=sp))
     ys = [torch.empty_like(s["x"]) for s in sets]
     ws_bytes = ssm.ssm_scan_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N, 0 if cfg.dtype == "f32" else 1)
     ws = ssm.new_workspace(ws_bytes)
@@ -153,8 +155,12 @@ def bench_scan(args, name):
 
     def step(i):
         s = sets[i % len(sets)]
-        ssm.ssm_scan_fwd(s["x"], s["delta"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"], state_in=st_in,
-                         state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
+        if sp:
+            ssm.ssm_scan_fwd_dt(s["x"], s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"],
+                                state_in=st_in, state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
+        else:
+            ssm.ssm_scan_fwd(s["x"], s["delta"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"], state_in=st_in,
+                             state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -163,7 +169,8 @@ def bench_scan(args, name):
     log(f"[bench] {args.steps} steps, {ms * 1e3:.2f} us/step ({launch_ms * 1e3:.2f} us/launch) "
         f"over {len(sets)} rotating sets")
     out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems,
-           "bytes": W.scan_bytes(cfg, st_out is not None), "dtype": cfg.dtype, "parity": None, "cpu": None}
+           "bytes": W.scan_bytes(cfg, st_out is not None) + (cfg.D * 4 if sp else 0), "dtype": cfg.dtype,
+           "parity": None, "cpu": None}
     # parity of the timed configuration on set 0, and the CPU baseline
     if inp is not None and not args.no_cpu:
         import oracle
@@ -175,7 +182,7 @@ def bench_scan(args, name):
         reps, tot, yr = 0, 0.0, None
         while reps == 0 or tot < args.cpu_seconds:
             t = time.perf_counter()
-            yr, _ = o.scan(inp, cfg.dtype)
+            yr, _ = o.scan_dt(inp, cfg.dtype) if sp else o.scan(inp, cfg.dtype)
             tot += time.perf_counter() - t
             reps += 1
         rel, mx = rel_l2(y0, yr)
@@ -198,13 +205,19 @@ def bench_step(args):
     base = W.step_inputs(cfg)
     state = to_dev(base["state"])
     A, Dskip = to_dev(base["A"]), to_dev(base["Dskip"])
-    fill = W.fill_step_device(cfg, nsteps, "cuda")
+    sp = args.softplus  # delta handed over before its activation
+    fill = W.fill_step_device(cfg, nsteps, "cuda", raw_delta=sp)
+    bias = to_dev(base["dt_bias"])
     y = torch.empty((cfg.batch, cfg.D), dtype=fill["x"].dtype, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(s):
-        ssm.ssm_step(fill["x"][s], fill["delta"][s], A, fill["Bt"][s], fill["Ct"][s], state, Dskip=Dskip,
-                     z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
+        if sp:
+            ssm.ssm_step_dt(fill["x"][s], fill["delta_raw"][s], bias, A, fill["Bt"][s], fill["Ct"][s], state,
+                            Dskip=Dskip, z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
+        else:
+            ssm.ssm_step(fill["x"][s], fill["delta"][s], A, fill["Bt"][s], fill["Ct"][s], state, Dskip=Dskip,
+                         z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
 
     # A decode loop is launch-bound from Python (the binding's argument checks
     # take about as long as the kernel), so the K timed steps are captured once
@@ -229,7 +242,8 @@ def bench_step(args):
     launch_ms = ms  # one launch per step, back to back inside the graph
     log(f"[bench] {args.steps} decode steps from a graph, {ms * 1e3:.2f} us/step "
         f"(eager launches from Python: {eager_ms * 1e3:.2f} us/step)")
-    out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems_per_step, "bytes": W.step_bytes(cfg),
+    out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems_per_step,
+           "bytes": W.step_bytes(cfg) + (cfg.D * 4 if sp else 0),
            "dtype": cfg.dtype, "parity": None, "cpu": None}
     if not args.no_cpu:
         import oracle
@@ -238,9 +252,12 @@ def bench_step(args):
         st64 = np.ascontiguousarray(base["state"][:, sel], dtype=np.float64)
         reps, tot = 0, 0.0
         while reps == 0 or (tot < args.cpu_seconds and reps < cfg.steps):
-            tk = W.step_token_inputs(cfg, reps, channels=sel)
+            tk = W.step_token_inputs(cfg, reps, channels=sel, raw_delta=sp)
             t = time.perf_counter()
-            o.step(tk, base["A"][sel], base["Dskip"][sel], st64, cfg.dtype)
+            if sp:
+                o.step_dt(tk, base["A"][sel], base["Dskip"][sel], base["dt_bias"][sel], st64, cfg.dtype)
+            else:
+                o.step(tk, base["A"][sel], base["Dskip"][sel], st64, cfg.dtype)
             tot += time.perf_counter() - t
             reps += 1
         out["cpu"] = {"value": cfg.batch * len(sel) * cfg.N * reps / tot / 1e9, "unit": "G(B*D*N)-elem/s",
@@ -258,6 +275,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--softplus", action="store_true",
+                    help="hand delta over before its activation (ssm_scan_fwd_dt / ssm_step_dt)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -280,7 +299,7 @@ def main():
     cfg = r["cfg"]
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = None if args.softplus else measured_traffic(args.workload)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": STEP_KERNEL if args.workload == "c4" else SCAN_KERNEL,
            "algorithmic_bytes_per_launch": r["bytes"], "launch_us": launch_ms * 1e3}
@@ -296,10 +315,14 @@ def main():
     if args.workload == "c4":
         config = {"workload": cfg.name, "batch": cfg.batch, "D": cfg.D, "N": cfg.N, "dtype": cfg.dtype,
                   "gate": cfg.gate, "steps_timed": args.steps}
+        if args.softplus:
+            config["delta"] = "raw: softplus(delta_raw + dt_bias) in the kernel"
         metric = "decode-step G(B*D*N)-elem/s"
     else:
         config = {"workload": cfg.name, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                   "dtype": cfg.dtype, "gate": cfg.gate, "state_in": cfg.state_in is not None}
+        if args.softplus:
+            config["delta"] = "raw: softplus(delta_raw + dt_bias) in the kernel"
         metric = "selective-scan G(B*L*D*N)-elem/s"
     line = {
         "metric": metric,

@@ -54,16 +54,18 @@ __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_ex
 constexpr float kLn2 = 0.6931471805599453f;
 
 // softplus(u) = log(1 + exp(u)) = max(u, 0) + log1p(exp(-|u|)). With
-// e = exp(-|u|) in (0, 1] and w = 1 + e rounded to float, log1p(e) is taken as
-// log(w) * e / (w - 1), or e when w == 1: the correction of D. Goldberg, "What
-// every computer scientist should know about floating-point arithmetic"
-// (ACM Computing Surveys, 1991), theorem 4, which keeps log1p accurate for
-// small e where log(1 + e) alone would lose it.
+// e = exp(-|u|) in (0, 1] and w = 1 + e rounded to float, w - 1 is exact
+// (Sterbenz) and so is r = e - (w - 1), the rounding error of the sum. Then
+// log1p(e) = log(w) + log(1 + r / w), and since |r| <= 2^-24 the second term
+// differs from r by at most |r| (w - 1) / w + r^2, which is under one ulp of
+// log1p(e) (as log1p(e) >= e / (1 + e)). This is the compensated-sum form of
+// log1p (the rounding error of 1 + e fed back to first order): it needs no
+// division, and gives e when w == 1.
 __device__ __forceinline__ float softplus(float u) {
     const float e = fast_exp2(-__builtin_fabsf(u) * kLog2e);
     const float w = 1.0f + e;
-    const float l = w == 1.0f ? e : __builtin_amdgcn_logf(w) * kLn2 * (e * __builtin_amdgcn_rcpf(w - 1.0f));
-    return __builtin_fmaxf(u, 0.0f) + l;
+    const float r = e - (w - 1.0f);
+    return __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, __builtin_fmaxf(u, 0.0f) + r);
 }
 
 // A value as the activation dtype holds it: unchanged for float, rounded to

@@ -263,22 +263,22 @@ __device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &
     else load_tile_w<N, DT, GATE, PASS, 3>(tb, a, b, ch0, tt0, lane, act_off);
 }
 
-// Step-size activation for a raw step: each loading wave applies
-// softplus(delta + dt_bias) to the delta pieces it loaded itself, once its
-// loads have landed and before the tile barrier, so every (token, channel)
-// is activated once. `dtb` holds the bias of the lane's VEC channels (the
-// lane's piece column is the same in every slot).
+// Step-size activation for a raw step: once a tile has landed, the
+// workgroup's threads share its delta pieces (piece p goes to thread
+// p mod 256) and replace each value by softplus(delta + dt_bias), so every
+// (token, channel) is activated once. A thread's pieces all sit in the same
+// piece column (256 is a multiple of the pieces per row), so `dtb` holds the
+// bias of its VEC channels.
 template <int N, int DT>
-__device__ __forceinline__ void activate_delta(TileBuf<N, DT> &tb, int w, int lane, const float (&dtb)[Geo<N, DT>::VEC]) {
+__device__ __forceinline__ void activate_delta(TileBuf<N, DT> &tb, const float (&dtb)[Geo<N, DT>::VEC]) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     using VT = uint32_t __attribute__((ext_vector_type(4)));
-    // the wave's slots are pieces (w - 1) * 64 + 192 * k; those of the delta
-    // tile lie in [ACT_PIECES, 2 * ACT_PIECES)
-#pragma unroll 1
-    for (int base = (w - 1) * 64; base < 2 * G::ACT_PIECES; base += 3 * 64) {
-        if (base < G::ACT_PIECES) continue;
-        T *p = &tb.dl[0][0] + (int64_t)(base - G::ACT_PIECES + lane) * G::VEC;
+    static_assert((64 * kWaves) % G::PPR == 0, "a thread's pieces share one column");
+    static_assert(G::ACT_PIECES % (64 * kWaves) == 0, "every thread has the same number of pieces");
+#pragma unroll
+    for (int k0 = 0; k0 < G::ACT_PIECES / (64 * kWaves); ++k0) {
+        T *p = &tb.dl[0][0] + (int64_t)(threadIdx.x + k0 * 64 * kWaves) * G::VEC;
         VT v = *(const VT *)__builtin_assume_aligned(p, 16);
         T e[G::VEC];
         __builtin_memcpy(e, &v, sizeof(v));
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         int64_t lane_ch = ch0 + (l % G::PPR) * G::VEC;
         lane_ch = lane_ch + G::VEC <= D ? lane_ch : D - G::VEC;
         const uint32_t act_off = (uint32_t)((l / G::PPR) * D + (lane_ch - ch0)) * G::ESZ;
-        // bias of the raw step size for the channels of this lane's pieces
+        // bias of the raw step size for the channels of this thread's delta pieces
         float dtb[G::VEC];
 #pragma unroll
         for (int k = 0; k < G::VEC; ++k) dtb[k] = (SP && a.dt_bias) ? a.dt_bias[lane_ch + k] : 0.0f;
@@ -418,9 +418,6 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
 #pragma unroll
             for (int q = 0; q < G::OWN; ++q) xo[q] = zo[q] = 0.0f;
             if (w > 0) vm_wait();  // the first tile (prefetch) has landed
-            if constexpr (SP) {
-                if (w > 0) activate_delta(sh.buf[0], w, l, dtb);
-            }
             lds_barrier();
             for (int i = 0; i < ntiles; ++i) {
                 TileBuf<N, DT> &tb = sh.buf[i & 1];
@@ -428,11 +425,10 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                 if constexpr (PASS == 2) {
                     // y of the previous tile goes out now, so that the stores
                     // complete behind this tile's scan; its buffer is loaded next
-                    if (i > 0) {
-                        store_y(sh.buf[(i - 1) & 1], i - 1);
-                        lds_barrier();
-                    }
+                    if (i > 0) store_y(sh.buf[(i - 1) & 1], i - 1);
                 }
+                if constexpr (SP) activate_delta(tb, dtb);  // this tile has landed for every wave
+                if (SP || (PASS == 2 && i > 0)) lds_barrier();
                 if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l, act_off);
                 const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
                 if (tail < TT) {
@@ -551,9 +547,6 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                     }
                 });
                 vm_wait();  // the next tile has landed (and this wave's earlier y stores are out)
-                if constexpr (SP) {
-                    if (w > 0 && i + 1 < ntiles) activate_delta(sh.buf[(i + 1) & 1], w, l, dtb);
-                }
                 lds_barrier();
             }
             if constexpr (PASS == 2) store_y(sh.buf[(ntiles - 1) & 1], ntiles - 1);

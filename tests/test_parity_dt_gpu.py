@@ -108,3 +108,85 @@ def test_step_dt_fold_equals_scan_dt(dtype):
     torch.cuda.synchronize()
     check(np.stack(ys, 1), y, dtype, "fold of steps vs scan (y)")
     check(to_f64(state), st, dtype, "fold of steps vs scan (state)")
+
+
+# -- the activation on its own ------------------------------------------------
+# With a zero carried-in state, x = 1, Bt = 1, Ct = (1, 0, ..., 0), no skip
+# term and no gate, the first state of a channel after a token is exactly its
+# activated step size, and so is y; A = -2e38 (A log2(e) still finite) makes
+# dA = 0 in the scan for every step size the sweep gives (the smallest,
+# softplus(-80) ~ 1.8e-35, still sends delta A below -5000), so no earlier
+# token leaks in (the step starts from a zero state anyway). This reads
+# the kernels' softplus(delta_raw + dt_bias) value by value.
+
+def _act_raw(shape, dtype, seed):
+    """Raw step sizes whose activated argument u = raw + bias sweeps the range a
+    projection can give, with fine sweeps where exp(-|u|) falls below the
+    float32 rounding of 1 + e and around u = 0."""
+    rng = np.random.default_rng(seed)
+    D = shape[-1]
+    bias = rng.uniform(-1.0, 1.0, D).astype(np.float32)
+    n = int(np.prod(shape))
+    parts = [np.linspace(-80.0, 40.0, n // 4), np.linspace(-19.0, -13.0, n // 4),
+             np.linspace(-1.0, 1.0, n // 4)]
+    parts.append(rng.normal(-4.0, 3.0, n - sum(len(p) for p in parts)))
+    u = np.concatenate(parts)
+    rng.shuffle(u)
+    raw = W._store(u.reshape(shape) - bias.astype(np.float64), dtype)
+    return raw, bias
+
+
+def _act_check(got, raw, bias, dtype):
+    """got: float64 copy of the kernel's activated step sizes."""
+    raw64 = W.storage_to_f64(raw, dtype)
+    ref = oracle.get().softplus_bias64(raw64, bias.astype(np.float64))
+    u = raw64 + bias.astype(np.float64)
+    # float32 evaluation: u = raw + bias rounds (relative error |u| 2^-24 in
+    # exp(u)), exp and log cost a few ulps
+    tol = (8.0 + 4.0 * np.abs(u)) * 2.0 ** -24 * np.abs(ref)
+    # bfloat16: the value is then rounded to 8 significant bits, half an ulp
+    half = 0.5 * 2.0 ** (np.floor(np.log2(np.abs(ref))) - 7) if dtype == "bf16" else 0.0 * ref
+    excess = np.abs(got - ref) - half  # error beyond the storage rounding
+    worst = int(np.argmax(excess / tol))
+    say(f"  activation: max (err - storage rounding)/tol {excess.flat[worst] / tol.flat[worst]:.3f} at "
+        f"u={u.flat[worst]:.6g} (got {got.flat[worst]:.9g}, ref {ref.flat[worst]:.9g}); "
+        f"max rel err {np.max(np.abs(got - ref) / ref):.3e}")
+    assert np.all(excess <= tol), "activated step sizes beyond the float32 error bound"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [96, 128])
+def test_scan_dt_activation_values(dtype, D):
+    import torch
+    import selective_state_space_16_amd as ssm
+    batch, L, N = 2, 700, 16
+    say(f"case scan activation values batch={batch} L={L} D={D} N={N} {dtype}")
+    raw, bias = _act_raw((batch, L, D), dtype, seed=D)
+    one = W._store(np.ones((batch, L, D)), dtype)
+    Bt = W._store(np.ones((batch, L, N)), dtype)
+    Ct = W._store(np.eye(N)[0][None, None, :].repeat(L, 1).repeat(batch, 0), dtype)
+    A = np.full((D, N), -2e38, np.float32)
+    dev = [to_dev(v) for v in (one, raw, bias, A, Bt, Ct)]
+    ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(batch, L, D, N, 0 if dtype == "f32" else 1))
+    y = ssm.ssm_scan_fwd_dt(*dev, workspace=ws)
+    torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0
+    _act_check(to_f64(y), raw, bias, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_dt_activation_values(dtype):
+    import torch
+    import selective_state_space_16_amd as ssm
+    batch, D, N = 64, 4096, 16
+    say(f"case step activation values batch={batch} D={D} N={N} {dtype}")
+    raw, bias = _act_raw((batch, D), dtype, seed=7)
+    one = W._store(np.ones((batch, D)), dtype)
+    Bt = W._store(np.ones((batch, N)), dtype)
+    Ct = W._store(np.eye(N)[0][None, :].repeat(batch, 0), dtype)
+    A = np.full((D, N), -1.0, np.float32)
+    state = torch.zeros((batch, D, N), dtype=torch.float32, device="cuda")
+    y = ssm.ssm_step_dt(to_dev(one), to_dev(raw), to_dev(bias), to_dev(A), to_dev(Bt), to_dev(Ct), state)
+    torch.cuda.synchronize()
+    _act_check(to_f64(y), raw, bias, dtype)
+    _act_check(to_f64(state[:, :, 0]), raw, bias, dtype)
