@@ -8,8 +8,11 @@ gcc, upcasts stored inputs exactly to float64 and calls it through ctypes.
 
 Parity is pinned by ``tests/test_oracle_pins.py`` against facts the pages fix
 (worked step example, LTI convolution, geometric closed form, delta limits,
-brute-force semiseparable sum, scalar-A masked form, step/scan composition)
-and by ``tests/test_oracle_mutants.py`` (each planted mistake fails a pin).
+brute-force semiseparable sum, scalar-A masked form, step/scan composition;
+for the exponential-trapezoidal variant the pages' seeded comparison with the
+Euler rule, the classic trapezoidal convolution, second-order convergence on
+an ODE with a closed-form solution, an unrolled sum and resumption) and by
+``tests/test_oracle_mutants.py`` (each planted mistake fails a pin).
 """
 from __future__ import annotations
 
@@ -56,6 +59,10 @@ class Oracle:
         self.lib.oracle_threads.restype = ci
         self.lib.oracle_softplus_bias.argtypes = [i64, i64, _DP, _DP, _DP]
         self.lib.oracle_softplus_bias.restype = ci
+        self.lib.oracle_scan_trap.argtypes = [i64, i64, i64, i64] + [_DP] * 13 + [ci]
+        self.lib.oracle_scan_trap.restype = ci
+        self.lib.oracle_step_trap.argtypes = [i64, i64, i64] + [_DP] * 12 + [ci]
+        self.lib.oracle_step_trap.restype = ci
 
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.oracle_threads(nthreads))
@@ -104,6 +111,51 @@ class Oracle:
             raise ValueError("oracle_step rejected sizes")
         return y
 
+    def scan_trap64(self, x, delta, lam, A, Bt, Ct, Dskip=None, z=None, x_prev=None, B_prev=None,
+                    state_in=None, want_state: bool = True, nthreads: int = 0):
+        """Exponential-trapezoidal scan; lam has x's shape, x_prev (batch, D) and
+        B_prev (batch, N) are the token before the first (None = none).
+        All arrays float64. Returns (y, state_out or None)."""
+        x = _c64(x)
+        batch, L, D = x.shape
+        A = _c64(A)
+        N = A.shape[1]
+        delta, lam, Bt, Ct = _c64(delta), _c64(lam), _c64(Bt), _c64(Ct)
+        assert delta.shape == x.shape and lam.shape == x.shape and A.shape == (D, N)
+        assert Bt.shape == (batch, L, N) and Ct.shape == (batch, L, N)
+        opt = lambda a, shape: None if a is None else _c64(a).reshape(shape)
+        Dskip, z = opt(Dskip, (D,)), opt(z, x.shape)
+        x_prev, B_prev = opt(x_prev, (batch, D)), opt(B_prev, (batch, N))
+        state_in = opt(state_in, (batch, D, N))
+        y = np.empty((batch, L, D), dtype=np.float64)
+        st = np.empty((batch, D, N), dtype=np.float64) if want_state else None
+        rc = self.lib.oracle_scan_trap(batch, L, D, N, _p(x), _p(delta), _p(lam), _p(A), _p(Bt), _p(Ct),
+                                       _p(Dskip), _p(z), _p(x_prev), _p(B_prev), _p(state_in), _p(st),
+                                       _p(y), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_scan_trap rejected sizes")
+        return y, st
+
+    def step_trap64(self, x, delta, lam, A, Bt, Ct, Dskip, z, x_prev, B_prev, state, nthreads: int = 0):
+        """One exponential-trapezoidal decode step; `state` (batch, D, N) float64
+        is updated in place. Returns y."""
+        x = _c64(x)
+        batch, D = x.shape
+        A = _c64(A)
+        N = A.shape[1]
+        assert state.dtype == np.float64 and state.flags.c_contiguous and state.shape == (batch, D, N)
+        delta, lam, Bt, Ct = _c64(delta), _c64(lam), _c64(Bt), _c64(Ct)
+        assert lam.shape == x.shape
+        opt = lambda a, shape: None if a is None else _c64(a).reshape(shape)
+        Dskip, z = opt(Dskip, (D,)), opt(z, x.shape)
+        x_prev, B_prev = opt(x_prev, (batch, D)), opt(B_prev, (batch, N))
+        y = np.empty((batch, D), dtype=np.float64)
+        rc = self.lib.oracle_step_trap(batch, D, N, _p(x), _p(delta), _p(lam), _p(A), _p(Bt), _p(Ct),
+                                       _p(Dskip), _p(z), _p(x_prev), _p(B_prev), _p(state), _p(y), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_step_trap rejected sizes")
+        return y
+
     def softplus_bias64(self, raw, bias=None):
         """softplus(raw + bias[d]) over the last axis (D) of a float64 array."""
         raw = _c64(raw)
@@ -149,6 +201,26 @@ class Oracle:
         return self.step64(up(tok["x"]), d64, upcast(A, "f32"), up(tok["Bt"]),
                            up(tok["Ct"]), None if Dskip is None else upcast(Dskip, "f32"),
                            up(tok.get("z")), state64, nthreads=nthreads)
+
+    def scan_trap(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
+        """Exponential-trapezoidal scan on stored inputs: inp["lam"] (stored dtype)
+        and optional inp["x_prev"], inp["B_prev"] (stored dtype)."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.scan_trap64(up(inp["x"]), up(inp["delta"]), up(inp["lam"]), upcast(inp["A"], "f32"),
+                                up(inp["Bt"]), up(inp["Ct"]),
+                                None if inp.get("Dskip") is None else upcast(inp["Dskip"], "f32"),
+                                up(inp.get("z")), up(inp.get("x_prev")), up(inp.get("B_prev")),
+                                None if inp.get("state_in") is None else upcast(inp["state_in"], "f32"),
+                                nthreads=nthreads)
+
+    def step_trap(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
+                  nthreads: int = 0):
+        """Exponential-trapezoidal decode step: tok["lam"], tok["x_prev"], tok["B_prev"]."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.step_trap64(up(tok["x"]), up(tok["delta"]), up(tok["lam"]), upcast(A, "f32"), up(tok["Bt"]),
+                                up(tok["Ct"]), None if Dskip is None else upcast(Dskip, "f32"),
+                                up(tok.get("z")), up(tok.get("x_prev")), up(tok.get("B_prev")), state64,
+                                nthreads=nthreads)
 
     def step(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
              nthreads: int = 0):

@@ -42,6 +42,13 @@
  * same softplus to its projected delta). oracle_softplus_bias computes that
  * activation; the scan and the step then run on its result unchanged.
  *
+ * The exponential-trapezoidal variant (oracle_scan_trap, oracle_step_trap)
+ * replaces the input term of the recurrence by a blend of the previous and
+ * the current token's input, with a per-token weight lam in [0, 1] ("Notas
+ * sobre Mamba", section "Recorrência trapezoidal", the generalised
+ * exponential-trapezoidal rule and its coefficients alpha, beta, gamma);
+ * lam = 1 gives the exponential-Euler scan above back.
+ *
  * Everything is float64 and uses libm exp()/log1p(); no fast-math, no
  * reordering of the token loop. OpenMP only splits independent (b, d) rows
  * across threads.
@@ -160,6 +167,108 @@ int oracle_step(int64_t batch, int64_t D, int64_t N,
             double dA = exp(dt * A[d * N + n]);
             double dBx = dt * Bt[b * N + n] * u;
             *hn = dA * *hn + dBx;
+            acc += Ct[b * N + n] * *hn;
+        }
+        if (Dskip) acc += Dskip[d] * u;
+        if (z) {
+            double g = z[r];
+            acc *= g / (1.0 + exp(-g));
+        }
+        y[r] = acc;
+    }
+    return 0;
+}
+
+/*
+ * Exponential-trapezoidal scan over L tokens. Per (b, d), with the input of
+ * token t written v_t[n] = Bt[b,t,n] * x[b,t,d]:
+ *
+ *   alpha[n] = exp(delta_t * A[d,n])
+ *   beta[n]  = (1 - lam_t) * delta_t * alpha[n]
+ *   gamma    = lam_t * delta_t
+ *   h[n]     = alpha[n] * h[n] + beta[n] * v_{t-1}[n] + gamma * v_t[n]
+ *
+ * with delta_t = delta[b,t,d] and lam_t = lam[b,t,d]. The input before token
+ * 0 is v_{-1}[n] = B_prev[b,n] * x_prev[b,d] when both are given (the last
+ * token of an earlier call on the same sequence), else 0. Readout, skip,
+ * gate and the final state are those of oracle_scan.
+ *   lam            : (batch, L, D)
+ *   x_prev         : (batch, D) or NULL
+ *   B_prev         : (batch, N) or NULL
+ */
+int oracle_scan_trap(int64_t batch, int64_t L, int64_t D, int64_t N,
+                     const double *x, const double *delta, const double *lam, const double *A,
+                     const double *Bt, const double *Ct, const double *Dskip,
+                     const double *z, const double *x_prev, const double *B_prev,
+                     const double *state_in, double *state_out, double *y, int nthreads)
+{
+    if (batch < 0 || L < 0 || D < 0 || N < 1 || N > 4096) return -1;
+    int64_t rows = batch * D;
+    int nt = oracle_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / D, d = r % D;
+        double h[4096], vprev[4096];
+        for (int64_t n = 0; n < N; ++n) {
+            h[n] = state_in ? state_in[IDX3(b, d, n, D, N)] : 0.0;
+            vprev[n] = (x_prev && B_prev) ? B_prev[b * N + n] * x_prev[b * D + d] : 0.0;
+        }
+        for (int64_t t = 0; t < L; ++t) {
+            double dt = delta[IDX3(b, t, d, L, D)];
+            double lm = lam[IDX3(b, t, d, L, D)];
+            double u = x[IDX3(b, t, d, L, D)];
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double alpha = exp(dt * A[d * N + n]);
+                double beta = (1.0 - lm) * dt * alpha;
+                double gamma = lm * dt;
+                double v = Bt[IDX3(b, t, n, L, N)] * u;
+                h[n] = alpha * h[n] + beta * vprev[n] + gamma * v;
+                vprev[n] = v;
+                acc += Ct[IDX3(b, t, n, L, N)] * h[n];
+            }
+            if (Dskip) acc += Dskip[d] * u;
+            if (z) {
+                double g = z[IDX3(b, t, d, L, D)];
+                acc *= g / (1.0 + exp(-g));
+            }
+            y[IDX3(b, t, d, L, D)] = acc;
+        }
+        if (state_out)
+            for (int64_t n = 0; n < N; ++n) state_out[IDX3(b, d, n, D, N)] = h[n];
+    }
+    return 0;
+}
+
+/*
+ * One decode step of the exponential-trapezoidal scan on a stored state,
+ * updated in place; x_prev (batch, D) and B_prev (batch, N) are the previous
+ * token's x and Bt (NULL = none, as at the start of a sequence).
+ */
+int oracle_step_trap(int64_t batch, int64_t D, int64_t N,
+                     const double *x, const double *delta, const double *lam, const double *A,
+                     const double *Bt, const double *Ct, const double *Dskip,
+                     const double *z, const double *x_prev, const double *B_prev,
+                     double *state, double *y, int nthreads)
+{
+    if (batch < 0 || D < 0 || N < 1) return -1;
+    int64_t rows = batch * D;
+    int nt = oracle_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / D, d = r % D;
+        double dt = delta[r], lm = lam[r];
+        double u = x[r];
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double *hn = &state[r * N + n];
+            double alpha = exp(dt * A[d * N + n]);
+            double beta = (1.0 - lm) * dt * alpha;
+            double gamma = lm * dt;
+            double vp = (x_prev && B_prev) ? B_prev[b * N + n] * x_prev[r] : 0.0;
+            *hn = alpha * *hn + beta * vp + gamma * Bt[b * N + n] * u;
             acc += Ct[b * N + n] * *hn;
         }
         if (Dskip) acc += Dskip[d] * u;

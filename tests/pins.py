@@ -337,6 +337,160 @@ def pin_softplus_activation(o):
     assert np.allclose(y1, y2, rtol=1e-13, atol=1e-14) and np.allclose(s1, s2, rtol=1e-13, atol=1e-14)
 
 
-ALL_PINS = [pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
+# --- the exponential-trapezoidal variant ------------------------------------
+def _trap(o, p, lam, **kw):
+    return o.scan_trap64(p["x"], p["delta"], lam, p["A"], p["Bt"], p["Ct"], p.get("Dskip"), p.get("z"),
+                         p.get("x_prev"), p.get("B_prev"), p.get("state_in"), **kw)
+
+
+def _states_one_channel(fn, N, L):
+    """h_t[n] for every t and n of a one-channel scan: one run per n with the
+    readout vector Ct = e_n, so that y_t = h_t[n] exactly."""
+    H = np.empty((L, N))
+    for n in range(N):
+        C = np.zeros((1, L, N))
+        C[0, :, n] = 1.0
+        H[:, n] = fn(C)[0][0, :, 0]
+    return H
+
+
+def pin_trap_pages_example(o):
+    """The pages' seeded comparison of the two rules ("Notas sobre Mamba",
+    section "Recorrência trapezoidal"): lambda = 1 gives the exponential-Euler
+    states back, lambda = 1/2 departs from them by the printed 1.50."""
+    for seed, L, N, lam, printed in _golden_rows("trapezoid_demo.txt"):
+        rng = np.random.default_rng(int(seed))
+        L, N = int(L), int(N)
+        A = -np.exp(rng.normal(size=N))
+        B = rng.normal(size=(L, N))
+        x = rng.normal(size=L)
+        delta = np.exp(rng.normal(size=L) * 0.3)
+        args = (x[None, :, None], delta[None, :, None])
+        euler = _states_one_channel(lambda C: o.scan64(*args, A[None, :], B[None], C), N, L)
+        trap = _states_one_channel(
+            lambda C: o.scan_trap64(*args, np.full((1, L, 1), lam), A[None, :], B[None], C), N, L)
+        err = np.abs(trap - euler).max()
+        if lam == 1.0:
+            assert err <= 10 * printed, err   # rounding order only
+        else:
+            assert abs(err - printed) < 0.005, err  # the printed three digits
+
+
+def pin_trap_lambda_one_is_euler(o):
+    """lambda = 1 removes the previous-token term: the exponential-Euler scan,
+    with every optional part and an earlier input given (which must then be
+    ignored)."""
+    rng = np.random.default_rng(31)
+    p = _rand_problem(rng, 2, 37, 5, 4)
+    p["x_prev"], p["B_prev"] = rng.normal(size=(2, 5)), rng.normal(size=(2, 4))
+    y1, s1 = _trap(o, p, np.ones_like(p["x"]))
+    y2, s2 = _scan(o, p)
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-13) and np.allclose(s1, s2, rtol=1e-12, atol=1e-13)
+
+
+def pin_trap_classic_convolution(o):
+    """Constant delta, lambda = 1/2, constant B and C, no earlier input: the
+    classic trapezoidal rule on the exponential. Unrolled, token t-k enters
+    h_t with weight delta/2 for k = 0 and delta * Abar^k for k >= 1, so y is
+    numpy's convolution of x with sum_n C_n B_n K_k[n]."""
+    rng = np.random.default_rng(12)
+    D, N, L = 3, 4, 120
+    A = -np.exp(rng.normal(size=(D, N)))
+    dts = np.exp(rng.uniform(np.log(1e-2), np.log(0.5), size=D))
+    B, C = rng.normal(size=N), rng.normal(size=N)
+    x = rng.normal(size=(L, D))
+    y, _ = o.scan_trap64(x[None], np.broadcast_to(dts, (1, L, D)), np.full((1, L, D), 0.5), A,
+                         np.broadcast_to(B, (1, L, N)), np.broadcast_to(C, (1, L, N)))
+    k = np.arange(L)[:, None]
+    for d in range(D):
+        K = dts[d] * np.exp(dts[d] * A[d])[None, :] ** k      # (L, N): delta * Abar^k
+        K[0] = dts[d] / 2.0
+        kappa = (K * (C * B)[None, :]).sum(1)
+        ref = np.convolve(x[:, d], kappa)[:L]
+        assert np.allclose(y[0, :, d], ref, rtol=1e-11, atol=1e-12), d
+
+
+def pin_trap_second_order(o):
+    """The rule integrates h' = a h + x(s) with x(s) = cos(s), h(0) = 0 at
+    second order for lambda = 1/2 (error ratio about 4 when the step halves)
+    and at first order for lambda = 1 (ratio about 2). Token t sits at time
+    (t + 1) * delta, and the input before token 0 is x(0) = 1, passed as the
+    earlier token; the exact value is h(T) = (sin T - a cos T + a e^(aT)) / (a^2 + 1)."""
+    a, T = -0.7, 4.0
+    exact = (math.sin(T) - a * math.cos(T) + a * math.exp(a * T)) / (a * a + 1.0)
+    errs = {0.5: [], 1.0: []}
+    for L in (40, 80, 160):
+        dt = T / L
+        x = np.cos(dt * (np.arange(L) + 1.0))[None, :, None]
+        ones = np.ones((1, L, 1))
+        for lam in errs:
+            y, _ = o.scan_trap64(x, ones * dt, ones * lam, np.array([[a]]), ones, ones,
+                                 x_prev=np.ones((1, 1)), B_prev=np.ones((1, 1)))
+            errs[lam].append(abs(y[0, -1, 0] - exact))
+    for lam, order in ((0.5, 4.0), (1.0, 2.0)):
+        e = errs[lam]
+        for r in (e[0] / e[1], e[1] / e[2]):
+            assert abs(r / order - 1.0) < 0.1, (lam, e)
+
+
+def pin_trap_brute_force(o):
+    """Tiny inputs against the unrolled sum: h_t = (prod_{r<=t} Abar_r) h_in +
+    sum_{s<=t} (prod_{s<r<=t} Abar_r) (gamma_s v_s + beta_s v_{s-1}), with a
+    random lambda per token and channel, an earlier input and every optional
+    part."""
+    rng = np.random.default_rng(5)
+    batch, L, D, N = 2, 6, 3, 2
+    p = _rand_problem(rng, batch, L, D, N)
+    p["x_prev"], p["B_prev"] = rng.normal(size=(batch, D)), rng.normal(size=(batch, N))
+    lam = rng.uniform(0.0, 1.0, size=(batch, L, D))
+    y, st = _trap(o, p, lam)
+    for b in range(batch):
+        for d in range(D):
+            abar = np.exp(p["delta"][b, :, d][:, None] * p["A"][d][None, :])       # (L, N)
+            v = p["Bt"][b] * p["x"][b, :, d][:, None]                                # (L, N)
+            vprev = np.vstack([p["B_prev"][b] * p["x_prev"][b, d], v[:-1]])
+            w = (lam[b, :, d] * p["delta"][b, :, d])[:, None] * v +                 ((1.0 - lam[b, :, d]) * p["delta"][b, :, d])[:, None] * abar * vprev
+            for t in range(L):
+                h = np.prod(abar[:t + 1], axis=0) * p["state_in"][b, d]
+                for s_ in range(t + 1):
+                    h = h + np.prod(abar[s_ + 1:t + 1], axis=0) * w[s_]
+                yt = (p["Ct"][b, t] * h).sum() + p["Dskip"][d] * p["x"][b, t, d]
+                g = p["z"][b, t, d]
+                yt *= g / (1.0 + math.exp(-g))
+                assert abs(y[b, t, d] - yt) <= 1e-12 * (1 + abs(yt)), (b, t, d)
+            assert np.allclose(st[b, d], h, rtol=1e-12, atol=1e-13)
+
+
+def pin_trap_composition(o):
+    """Resuming: a scan cut at token m, the second part given the first part's
+    final state and its last token as the earlier input, equals one scan; and
+    L decode steps, each given the previous token, equal the scan."""
+    rng = np.random.default_rng(8)
+    batch, L, D, N = 2, 23, 4, 3
+    p = _rand_problem(rng, batch, L, D, N)
+    p["x_prev"], p["B_prev"] = rng.normal(size=(batch, D)), rng.normal(size=(batch, N))
+    lam = rng.uniform(0.0, 1.0, size=(batch, L, D))
+    y, st = _trap(o, p, lam)
+    m = 9
+    cut = lambda a, sl: None if a is None else a[:, sl]
+    p1 = dict(p, x=p["x"][:, :m], delta=p["delta"][:, :m], Bt=p["Bt"][:, :m], Ct=p["Ct"][:, :m], z=cut(p["z"], slice(0, m)))
+    y1, s1 = _trap(o, p1, lam[:, :m])
+    p2 = dict(p, x=p["x"][:, m:], delta=p["delta"][:, m:], Bt=p["Bt"][:, m:], Ct=p["Ct"][:, m:], z=cut(p["z"], slice(m, L)),
+              state_in=s1, x_prev=p["x"][:, m - 1], B_prev=p["Bt"][:, m - 1])
+    y2, s2 = _trap(o, p2, lam[:, m:])
+    assert np.allclose(np.concatenate([y1, y2], 1), y, rtol=1e-12, atol=1e-13)
+    assert np.allclose(s2, st, rtol=1e-12, atol=1e-13)
+    state = np.ascontiguousarray(p["state_in"], dtype=np.float64).copy()
+    xp, bp = p["x_prev"], p["B_prev"]
+    for t in range(L):
+        yt = o.step_trap64(p["x"][:, t], p["delta"][:, t], lam[:, t], p["A"], p["Bt"][:, t], p["Ct"][:, t],
+                           p["Dskip"], p["z"][:, t], xp, bp, state)
+        assert np.allclose(yt, y[:, t], rtol=1e-12, atol=1e-13), t
+        xp, bp = p["x"][:, t], p["Bt"][:, t]
+    assert np.allclose(state, st, rtol=1e-12, atol=1e-13)
+
+
+ALL_PINS = [pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
+            pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
             pin_linearity_causality]

@@ -51,6 +51,21 @@ MUTANTS = [
     ("softplus_log_not_log1p", "log1p(exp(-fabs(u)))", "log(1.0 + exp(-fabs(u)))"),
     ("softplus_relu_only", "(u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u)))", "(u > 0.0 ? u : 0.0)"),
     ("softplus_tail_sign", "log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
+    ("trap_beta_without_alpha", "double beta = (1.0 - lm) * dt * alpha;", "double beta = (1.0 - lm) * dt;"),
+    ("trap_beta_weight_lam", "double beta = (1.0 - lm) * dt * alpha;", "double beta = lm * dt * alpha;"),
+    ("trap_gamma_weight_one_minus_lam", "double gamma = lm * dt;", "double gamma = (1.0 - lm) * dt;"),
+    ("trap_prev_input_never_advances", "                vprev[n] = v;\n", ""),
+    ("trap_prev_input_advanced_early",
+     "                h[n] = alpha * h[n] + beta * vprev[n] + gamma * v;\n                vprev[n] = v;\n",
+     "                vprev[n] = v;\n                h[n] = alpha * h[n] + beta * vprev[n] + gamma * v;\n"),
+    ("trap_earlier_input_ignored", "vprev[n] = (x_prev && B_prev) ? B_prev[b * N + n] * x_prev[b * D + d] : 0.0;",
+     "vprev[n] = 0.0;"),
+    ("trap_earlier_B_batch_row_0", "B_prev[b * N + n] * x_prev[b * D + d]", "B_prev[n] * x_prev[b * D + d]"),
+    ("trap_lam_previous_token", "double lm = lam[IDX3(b, t, d, L, D)];",
+     "double lm = lam[IDX3(b, t > 0 ? t - 1 : 0, d, L, D)];"),
+    ("trap_step_prev_uses_current_B", "B_prev[b * N + n] * x_prev[r]", "Bt[b * N + n] * x_prev[r]"),
+    ("trap_step_beta_without_alpha", "            double beta = (1.0 - lm) * dt * alpha;\n            double gamma = lm * dt;\n            double vp",
+     "            double beta = (1.0 - lm) * dt;\n            double gamma = lm * dt;\n            double vp"),
 ]
 
 
