@@ -132,7 +132,8 @@ def bench_scan(args, name):
     t0 = time.time()
     # set 0: the seeded numpy streams (checked against the oracle below)
     sp = args.softplus  # delta handed over before its activation
-    inp = W.scan_inputs(cfg, raw_delta=sp) if name != "c3" else None
+    tr = args.trap  # exponential-trapezoidal rule
+    inp = W.scan_inputs(cfg, raw_delta=sp, trap=tr) if name != "c3" else None
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
     whole = W.scan_inputs(cfg, 0, 0)
     A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
@@ -140,12 +141,14 @@ def bench_scan(args, name):
     sets = []
     if inp is not None:
         keys = ("x", "delta_raw", "dt_bias", "z", "Bt", "Ct") if sp else ("x", "delta", "z", "Bt", "Ct")
+        if tr:
+            keys += ("lam", "x_prev", "B_prev")
         sets.append({k: to_dev(inp[k]) for k in keys})
     # further sets: same distributions, drawn on the GPU
     per_set = W.scan_bytes(cfg)
     nsets = max(1, min(args.rotate, int(60e9 // max(per_set, 1))))
     while len(sets) < nsets:
-        sets.append(W.fill_scan_device(cfg, "cuda", seed=1000 + len(sets), raw_delta=sp))
+        sets.append(W.fill_scan_device(cfg, "cuda", seed=1000 + len(sets), raw_delta=sp, trap=tr))
     ys = [torch.empty_like(s["x"]) for s in sets]
     ws_bytes = ssm.ssm_scan_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N, 0 if cfg.dtype == "f32" else 1)
     ws = ssm.new_workspace(ws_bytes)
@@ -158,6 +161,10 @@ def bench_scan(args, name):
         if sp:
             ssm.ssm_scan_fwd_dt(s["x"], s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"],
                                 state_in=st_in, state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
+        elif tr:
+            ssm.ssm_scan_fwd_trap(s["x"], s["delta"], s["lam"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"],
+                                  x_prev=s["x_prev"], B_prev=s["B_prev"], state_in=st_in, state_out=st_out,
+                                  y=ys[i % len(sets)], workspace=ws, stream=stream)
         else:
             ssm.ssm_scan_fwd(s["x"], s["delta"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"], state_in=st_in,
                              state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
@@ -169,7 +176,8 @@ def bench_scan(args, name):
     log(f"[bench] {args.steps} steps, {ms * 1e3:.2f} us/step ({launch_ms * 1e3:.2f} us/launch) "
         f"over {len(sets)} rotating sets")
     out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems,
-           "bytes": W.scan_bytes(cfg, st_out is not None) + (cfg.D * 4 if sp else 0), "dtype": cfg.dtype,
+           "bytes": W.scan_bytes(cfg, st_out is not None) + (cfg.D * 4 if sp else 0) +
+                    (W.trap_extra_bytes(cfg) if tr else 0), "dtype": cfg.dtype,
            "parity": None, "cpu": None}
     # parity of the timed configuration on set 0, and the CPU baseline
     if inp is not None and not args.no_cpu:
@@ -182,7 +190,7 @@ def bench_scan(args, name):
         reps, tot, yr = 0, 0.0, None
         while reps == 0 or tot < args.cpu_seconds:
             t = time.perf_counter()
-            yr, _ = o.scan_dt(inp, cfg.dtype) if sp else o.scan(inp, cfg.dtype)
+            yr, _ = o.scan_dt(inp, cfg.dtype) if sp else o.scan_trap(inp, cfg.dtype) if tr else o.scan(inp, cfg.dtype)
             tot += time.perf_counter() - t
             reps += 1
         rel, mx = rel_l2(y0, yr)
@@ -206,7 +214,8 @@ def bench_step(args):
     state = to_dev(base["state"])
     A, Dskip = to_dev(base["A"]), to_dev(base["Dskip"])
     sp = args.softplus  # delta handed over before its activation
-    fill = W.fill_step_device(cfg, nsteps, "cuda", raw_delta=sp)
+    tr = args.trap  # exponential-trapezoidal rule; step s gets token s - 1 as the earlier token
+    fill = W.fill_step_device(cfg, nsteps, "cuda", raw_delta=sp, trap=tr)
     bias = to_dev(base["dt_bias"])
     y = torch.empty((cfg.batch, cfg.D), dtype=fill["x"].dtype, device="cuda")
     stream = torch.cuda.current_stream()
@@ -215,6 +224,11 @@ def bench_step(args):
         if sp:
             ssm.ssm_step_dt(fill["x"][s], fill["delta_raw"][s], bias, A, fill["Bt"][s], fill["Ct"][s], state,
                             Dskip=Dskip, z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
+        elif tr:
+            xp, bp = (fill["x"][s - 1], fill["Bt"][s - 1]) if s > 0 else (None, None)
+            ssm.ssm_step_trap(fill["x"][s], fill["delta"][s], fill["lam"][s], A, fill["Bt"][s], fill["Ct"][s], state,
+                              Dskip=Dskip, z=fill["z"][s], x_prev=xp, B_prev=bp, y=y,
+                              stream=torch.cuda.current_stream())
         else:
             ssm.ssm_step(fill["x"][s], fill["delta"][s], A, fill["Bt"][s], fill["Ct"][s], state, Dskip=Dskip,
                          z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
@@ -243,19 +257,24 @@ def bench_step(args):
     log(f"[bench] {args.steps} decode steps from a graph, {ms * 1e3:.2f} us/step "
         f"(eager launches from Python: {eager_ms * 1e3:.2f} us/step)")
     out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems_per_step,
-           "bytes": W.step_bytes(cfg) + (cfg.D * 4 if sp else 0),
+           "bytes": W.step_bytes(cfg) + (cfg.D * 4 if sp else 0) + (W.trap_step_extra_bytes(cfg) if tr else 0),
            "dtype": cfg.dtype, "parity": None, "cpu": None}
     if not args.no_cpu:
         import oracle
         o = oracle.get()
         sel = np.arange(0, cfg.D, 16)  # a bounded sample: every 16th channel
         st64 = np.ascontiguousarray(base["state"][:, sel], dtype=np.float64)
-        reps, tot = 0, 0.0
+        reps, tot, prev = 0, 0.0, None
         while reps == 0 or (tot < args.cpu_seconds and reps < cfg.steps):
-            tk = W.step_token_inputs(cfg, reps, channels=sel, raw_delta=sp)
+            tk = W.step_token_inputs(cfg, reps, channels=sel, raw_delta=sp, trap=tr)
             t = time.perf_counter()
             if sp:
                 o.step_dt(tk, base["A"][sel], base["Dskip"][sel], base["dt_bias"][sel], st64, cfg.dtype)
+            elif tr:
+                o.step_trap(dict(tk, x_prev=None if prev is None else prev["x"],
+                                 B_prev=None if prev is None else prev["Bt"]),
+                            base["A"][sel], base["Dskip"][sel], st64, cfg.dtype)
+                prev = tk
             else:
                 o.step(tk, base["A"][sel], base["Dskip"][sel], st64, cfg.dtype)
             tot += time.perf_counter() - t
@@ -277,9 +296,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--softplus", action="store_true",
                     help="hand delta over before its activation (ssm_scan_fwd_dt / ssm_step_dt)")
+    ap.add_argument("--trap", action="store_true",
+                    help="the exponential-trapezoidal rule (ssm_scan_fwd_trap / ssm_step_trap)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.softplus and args.trap:
+        ap.error("--softplus and --trap select different entry points; give one")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -299,7 +322,7 @@ def main():
     cfg = r["cfg"]
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
-    traffic = None if args.softplus else measured_traffic(args.workload)
+    traffic = None if (args.softplus or args.trap) else measured_traffic(args.workload)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": STEP_KERNEL if args.workload == "c4" else SCAN_KERNEL,
            "algorithmic_bytes_per_launch": r["bytes"], "launch_us": launch_ms * 1e3}
@@ -317,12 +340,16 @@ def main():
                   "gate": cfg.gate, "steps_timed": args.steps}
         if args.softplus:
             config["delta"] = "raw: softplus(delta_raw + dt_bias) in the kernel"
+        if args.trap:
+            config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "decode-step G(B*D*N)-elem/s"
     else:
         config = {"workload": cfg.name, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                   "dtype": cfg.dtype, "gate": cfg.gate, "state_in": cfg.state_in is not None}
         if args.softplus:
             config["delta"] = "raw: softplus(delta_raw + dt_bias) in the kernel"
+        if args.trap:
+            config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "selective-scan G(B*L*D*N)-elem/s"
     line = {
         "metric": metric,

@@ -143,6 +143,41 @@ int ssm_scan_fwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssm_scan_fwd with the exponential-trapezoidal rule of "Notas sobre Mamba",
+ * section "Recorrência trapezoidal": the input term blends the previous and
+ * the current token's input with a per-token weight lam,
+ *
+ *   h[t,n] = dA[t,n] * h[t-1,n]
+ *            + (1 - lam[t]) * delta[t] * dA[t,n] * Bt[t-1,n] * x[t-1]
+ *            + lam[t] * delta[t] * Bt[t,n] * x[t]
+ *
+ * with dA, the readout, the skip term, the gate and the state as in
+ * ssm_scan_fwd. lam = 1 everywhere gives ssm_scan_fwd's result; lam = 1/2 is
+ * the classic trapezoidal rule. lam is the weight itself (the pages take it
+ * as the sigmoid of a per-token projection, computed upstream).
+ *
+ *   lam           (batch, L, D)  dtype      weight per token and channel,
+ *                                           normally in [0, 1]
+ *   x_prev        (batch, D)     dtype      x and Bt of the token before token
+ *   B_prev        (batch, N)     dtype      0 (to resume a sequence cut after
+ *                                           an earlier call: that call's last
+ *                                           token); both NULL = no earlier
+ *                                           token (its input term is zero)
+ *
+ * Passing exactly one of x_prev and B_prev, or a NULL lam with a non-empty
+ * input, returns SSM_ERR_NULL. Every other argument, the workspace
+ * (ssm_scan_workspace_bytes) and the status codes are those of ssm_scan_fwd.
+ * A long sequence may be scanned in pieces: pass each piece the previous
+ * piece's state_out as state_in and its last token's x and Bt as x_prev and
+ * B_prev.
+ */
+int ssm_scan_fwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x, const void *delta, const void *lam, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                      const void *x_prev, const void *B_prev, const float *state_in, float *state_out,
+                      void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for `batch` sequences (one token each), updating
  * the state in place.
  *
@@ -175,6 +210,24 @@ int ssm_step_dt(int64_t batch, int64_t D, int64_t N, int dtype,
                 const void *x, const void *delta_raw, const float *dt_bias, const float *A,
                 const void *Bt, const void *Ct, const float *Dskip,
                 const void *z, float *state, void *y, void *stream);
+
+/*
+ * One decode step with the exponential-trapezoidal rule (see
+ * ssm_scan_fwd_trap). The state holds h only; the caller passes the previous
+ * token's x and Bt (the ones given to the previous step) as x_prev and
+ * B_prev, or NULL for both at the first token of a sequence.
+ *
+ *   lam           (batch, D)     dtype
+ *   x_prev        (batch, D)     dtype      NULL = no earlier token
+ *   B_prev        (batch, N)     dtype      NULL = no earlier token
+ *
+ * Equivalent to ssm_scan_fwd_trap with L = 1 and state_in = state_out =
+ * state. Arguments and status codes otherwise as in ssm_step.
+ */
+int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
+                  const void *x, const void *delta, const void *lam, const float *A,
+                  const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                  const void *x_prev, const void *B_prev, float *state, void *y, void *stream);
 
 #ifdef __cplusplus
 }

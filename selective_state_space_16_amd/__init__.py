@@ -11,6 +11,8 @@ Functions (same names as the C ABI):
   ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None) -> y
   ssm_scan_fwd_dt / ssm_step_dt: the same with delta_raw and dt_bias in place
       of delta; the kernels use softplus(delta_raw + dt_bias) as the step size
+  ssm_scan_fwd_trap / ssm_step_trap: the exponential-trapezoidal rule, with a
+      per-token weight lam and the token before the first (x_prev, B_prev)
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
 """
@@ -22,7 +24,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
+    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
 
@@ -36,7 +38,7 @@ lib_path = os.path.join(_HERE, "libssm.so")
 
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
-           "ssm_scan_fwd_dt", "ssm_step_dt")
+           "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -71,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_dt.restype = ci
     L.ssm_step_dt.argtypes = [i64, i64, i64, ci] + [vp] * 10 + [vp]
     L.ssm_step_dt.restype = ci
+    L.ssm_scan_fwd_trap.argtypes = [i64, i64, i64, i64, ci] + [vp] * 13 + [vp, sz, vp]
+    L.ssm_scan_fwd_trap.restype = ci
+    L.ssm_step_trap.argtypes = [i64, i64, i64, ci] + [vp] * 12 + [vp]
+    L.ssm_step_trap.restype = ci
     _lib = L
     return L
 
@@ -132,7 +138,8 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream):
+def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream,
+          lam=None, x_prev=None, B_prev=None):
     import torch
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, D) and A (D, N)")
@@ -150,10 +157,17 @@ def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, 
     args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, L, D))]
     if name == "ssm_scan_fwd_dt":
         args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
+    trap = name == "ssm_scan_fwd_trap"
+    if trap:
+        args.append(_ptr(lam, "lam", act, (batch, L, D)))
     args += [
         _ptr(A, "A", f32, (D, N)),
         _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
         _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+    ]
+    if trap:
+        args += [_ptr(x_prev, "x_prev", act, (batch, D)), _ptr(B_prev, "B_prev", act, (batch, N))]
+    args += [
         _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(state_out, "state_out", f32, (batch, D, N)),
         _ptr(y, "y", act, (batch, L, D)),
     ]
@@ -182,7 +196,16 @@ def ssm_scan_fwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, Dskip=None, z=None, state_
                  workspace, stream)
 
 
-def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream):
+def ssm_scan_fwd_trap(x, delta, lam, A, Bt, Ct, Dskip=None, z=None, x_prev=None, B_prev=None, state_in=None,
+                      state_out=None, y=None, workspace=None, stream=None):
+    """ssm_scan_fwd with the exponential-trapezoidal rule: lam (batch, L, D) in
+    the activation dtype; x_prev (batch, D) and B_prev (batch, N), the token
+    before the first, both or neither."""
+    return _scan("ssm_scan_fwd_trap", x, delta, None, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace,
+                 stream, lam=lam, x_prev=x_prev, B_prev=B_prev)
+
+
+def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, lam=None, x_prev=None, B_prev=None):
     import torch
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, D) and A (D, N)")
@@ -197,12 +220,17 @@ def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream):
     args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, D))]
     if name == "ssm_step_dt":
         args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
+    trap = name == "ssm_step_trap"
+    if trap:
+        args.append(_ptr(lam, "lam", act, (batch, D)))
     args += [
         _ptr(A, "A", f32, (D, N)),
         _ptr(Bt, "Bt", act, (batch, N)), _ptr(Ct, "Ct", act, (batch, N)),
         _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, D)),
-        _ptr(state, "state", f32, (batch, D, N)), _ptr(y, "y", act, (batch, D)),
     ]
+    if trap:
+        args += [_ptr(x_prev, "x_prev", act, (batch, D)), _ptr(B_prev, "B_prev", act, (batch, N))]
+    args += [_ptr(state, "state", f32, (batch, D, N)), _ptr(y, "y", act, (batch, D))]
     st = getattr(lib(), name)(batch, D, N, code, *args, _stream(stream))
     if st != 0:
         raise SSMError(st, name)
@@ -218,3 +246,12 @@ def ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None
 def ssm_step_dt(x, delta_raw, dt_bias, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None):
     """ssm_step with the step size before its activation (see ssm_scan_fwd_dt)."""
     return _step("ssm_step_dt", x, delta_raw, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream)
+
+
+def ssm_step_trap(x, delta, lam, A, Bt, Ct, state, Dskip=None, z=None, x_prev=None, B_prev=None, y=None,
+                  stream=None):
+    """One decode step with the exponential-trapezoidal rule: lam (batch, D);
+    x_prev (batch, D) and B_prev (batch, N) are the previous token's x and Bt
+    (both None at a sequence's first token)."""
+    return _step("ssm_step_trap", x, delta, None, A, Bt, Ct, state, Dskip, z, y, stream, lam=lam, x_prev=x_prev,
+                 B_prev=B_prev)

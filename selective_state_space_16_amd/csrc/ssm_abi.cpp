@@ -110,11 +110,17 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, 
     return workspace_for(batch, L, D, N, dtype);
 }
 
+// Extra inputs of the exponential-trapezoidal rule: the per-token weight and
+// the token before the first (both of x_prev and B_prev, or neither).
+struct TrapIn {
+    const void *lam = nullptr, *x_prev = nullptr, *B_prev = nullptr;
+};
+
 static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
                     const void *Bt, const void *Ct, const float *Dskip,
                     const void *z, const float *state_in, float *state_out,
-                    void *y, void *workspace, size_t workspace_bytes, void *stream) {
+                    void *y, void *workspace, size_t workspace_bytes, void *stream, TrapIn tr = {}) {
     if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
@@ -130,7 +136,8 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                                                                                           : SSM_ERR_HIP;
     }
     if (!x || !delta || !A || !Bt || !Ct || !y) return SSM_ERR_NULL;
-    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, state_out, y, dt_bias};
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, state_out, y, dt_bias, tr.lam, tr.x_prev,
+                          tr.B_prev};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
 
@@ -158,6 +165,9 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.state_out = state_out;
         a.dt_bias = dt_bias;
         a.delta_softplus = softplus;
+        a.lam = tr.lam;
+        a.x_prev = tr.x_prev;
+        a.B_prev = tr.B_prev;
         a.y = y;
         a.ntpb = p.ntpb;
         a.ncol = p.ncol;
@@ -187,6 +197,9 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.state_in = state_in;
     a.dt_bias = dt_bias;
     a.delta_softplus = softplus;
+    a.lam = tr.lam;
+    a.x_prev = tr.x_prev;
+    a.B_prev = tr.B_prev;
     a.state_out = state_out;
     a.y = y;
     if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
@@ -200,14 +213,14 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
 static int step(int64_t batch, int64_t D, int64_t N, int dtype,
                 const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
                 const void *Bt, const void *Ct, const float *Dskip,
-                const void *z, float *state, void *y, void *stream) {
+                const void *z, float *state, void *y, void *stream, TrapIn tr = {}) {
     if (batch < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
     if (checked_mul3(batch, D, N) < 0) return SSM_ERR_SHAPE;
     if (batch == 0 || D == 0) return SSM_OK;
     if (!x || !delta || !A || !Bt || !Ct || !state || !y) return SSM_ERR_NULL;
-    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y, dt_bias};
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y, dt_bias, tr.lam, tr.x_prev, tr.B_prev};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
     ssm::StepArgs a{};
@@ -224,6 +237,9 @@ static int step(int64_t batch, int64_t D, int64_t N, int dtype,
     a.y = y;
     a.dt_bias = dt_bias;
     a.delta_softplus = softplus;
+    a.lam = tr.lam;
+    a.x_prev = tr.x_prev;
+    a.B_prev = tr.B_prev;
     return ssm::launch_step(a, (int)N, dtype, (hipStream_t)stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -245,6 +261,21 @@ int ssm_scan_fwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     workspace, workspace_bytes, stream);
 }
 
+int ssm_scan_fwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x, const void *delta, const void *lam, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                      const void *x_prev, const void *B_prev, const float *state_in, float *state_out,
+                      void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!lam && batch > 0 && L > 0 && D > 0) return SSM_ERR_NULL;
+    if ((x_prev == nullptr) != (B_prev == nullptr)) return SSM_ERR_NULL;
+    TrapIn tr;
+    tr.lam = lam;
+    tr.x_prev = x_prev;
+    tr.B_prev = B_prev;
+    return scan_fwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, state_out, y,
+                    workspace, workspace_bytes, stream, tr);
+}
+
 int ssm_step(int64_t batch, int64_t D, int64_t N, int dtype,
              const void *x, const void *delta, const float *A,
              const void *Bt, const void *Ct, const float *Dskip,
@@ -257,6 +288,19 @@ int ssm_step_dt(int64_t batch, int64_t D, int64_t N, int dtype,
                 const void *Bt, const void *Ct, const float *Dskip,
                 const void *z, float *state, void *y, void *stream) {
     return step(batch, D, N, dtype, x, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state, y, stream);
+}
+
+int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
+                  const void *x, const void *delta, const void *lam, const float *A,
+                  const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                  const void *x_prev, const void *B_prev, float *state, void *y, void *stream) {
+    if (!lam && batch > 0 && D > 0) return SSM_ERR_NULL;
+    if ((x_prev == nullptr) != (B_prev == nullptr)) return SSM_ERR_NULL;
+    TrapIn tr;
+    tr.lam = lam;
+    tr.x_prev = x_prev;
+    tr.B_prev = B_prev;
+    return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
 }  // extern "C"

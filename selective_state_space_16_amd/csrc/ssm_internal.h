@@ -14,6 +14,9 @@ struct ScanArgs {
     const float *A, *Dskip, *state_in;
     const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
     int delta_softplus;    // delta holds the raw step size: use softplus(delta + dt_bias)
+    // exponential-trapezoidal rule: per-token weight lam (NULL = the Euler
+    // rule) and the token before the first (x_prev, B_prev; NULL = none)
+    const void *lam, *x_prev, *B_prev;
     float *state_out;
     void *y;
     float *ws_state;   // (batch, K, D, N) chunk end states, then carried-in states
@@ -29,6 +32,9 @@ struct StripeArgs {
     const float *A, *Dskip, *state_in;
     const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
     int delta_softplus;    // delta holds the raw step size: use softplus(delta + dt_bias)
+    // exponential-trapezoidal rule: per-token weight lam (NULL = the Euler
+    // rule) and the token before the first (x_prev, B_prev; NULL = none)
+    const void *lam, *x_prev, *B_prev;
     float *state_out;
     void *y;
     int64_t ntpb;           // tile columns per batch row
@@ -56,6 +62,9 @@ struct StepArgs {
     const float *A, *Dskip;
     const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
     int delta_softplus;    // delta holds the raw step size: use softplus(delta + dt_bias)
+    // exponential-trapezoidal rule: per-token weight lam (NULL = the Euler
+    // rule) and the token before the first (x_prev, B_prev; NULL = none)
+    const void *lam, *x_prev, *B_prev;
     float *state;
     void *y;
 };
@@ -69,6 +78,8 @@ bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, Stri
 hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s);
 // The instances for a delta given before its activation (called by launch_scan_stripe).
 hipError_t launch_scan_stripe_act(const StripeArgs &a, int N, int dtype, hipStream_t s);
+// The instances for the exponential-trapezoidal rule (called by launch_scan_stripe).
+hipError_t launch_scan_stripe_trap(const StripeArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepArgs &a, int N, int dtype, hipStream_t s);

@@ -18,6 +18,14 @@
 //   3. final:   every chunk rescans from its carried-in state, writes y, and
 //               the last chunk writes state_out.
 // With K = 1 only the final launch runs, from state_in.
+//
+// TRAP: the exponential-trapezoidal rule ("Notas sobre Mamba", section
+// "Recorrência trapezoidal"): h = a h + (1 - lam) delta a v_prev + lam delta v
+// with v = B x of this token and v_prev that of the previous one, taken as
+// h = a (h + ((1 - lam) delta x_prev) B_prev) + (lam delta x) B. The pair
+// composition is unchanged (a = exp(delta A)); a chunk's summary includes its
+// first token's term in the input of the token before it, read from memory
+// (or x_prev, B_prev for token 0).
 #include "ssm_common.h"
 #include "ssm_internal.h"
 
@@ -28,7 +36,7 @@ namespace {
 constexpr int kWave = 64;
 enum { kFinal = 0, kSummary = 1 };
 
-template <int N, int DT, int MODE, bool GATE, bool SKIP>
+template <int N, int DT, int MODE, bool GATE, bool SKIP, bool TRAP>
 __global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a) {
     using T = typename Act<DT>::T;
     const int lane = threadIdx.x;
@@ -74,6 +82,20 @@ __global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a) {
     const float dskip = (SKIP && MODE == kFinal) ? a.Dskip[dc] : 0.0f;
     const float dtb = a.dt_bias ? a.dt_bias[dc] : 0.0f;  // bias of a raw step size
 
+    // TRAP: x and Bt of the token before this one
+    float xprev = 0.0f, Bprev[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Bprev[n] = 0.0f;
+    if constexpr (TRAP) {
+        if (t0 > 0) {
+            xprev = ld_act(xp, (b * L + t0 - 1) * D + dc);
+            ld_row_uniform<N>(Bp, (b * L + t0 - 1) * N, Bprev);
+        } else if (a.x_prev) {
+            xprev = ld_act((const T *)a.x_prev, b * D + dc);
+            ld_row_uniform<N>((const T *)a.B_prev, b * N, Bprev);
+        }
+    }
+
     float dsum = 0.0f;
 #pragma unroll 4
     for (int64_t t = t0; t < t1; ++t) {
@@ -83,7 +105,18 @@ __global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a) {
         const float xv = ld_act(xp, row);
         float Bv[N];
         ld_row_uniform<N>(Bp, (b * L + t) * N, Bv);
-        const float dx = dt * xv;
+        float dx = dt * xv;
+        if constexpr (TRAP) {
+            const float lm = ld_act((const T *)a.lam, row);
+            const float px = (dt - lm * dt) * xprev;
+            dx = lm * dt * xv;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                h[n] = __builtin_fmaf(px, Bprev[n], h[n]);
+                Bprev[n] = Bv[n];
+            }
+            xprev = xv;
+        }
         if (MODE == kSummary) {
             dsum += dt;
 #pragma unroll
@@ -141,28 +174,33 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float *src, float
     if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
-template <int N, int DT, bool GATE, bool SKIP>
+template <int N, int DT, bool GATE, bool SKIP, bool TRAP>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t s) {
     const dim3 blk(kWave);
     const int64_t nb = (a.D + kWave - 1) / kWave;
     if (a.K > 1) {
-        hipLaunchKernelGGL((scan_chunk_kernel<N, DT, kSummary, GATE, SKIP>),
+        hipLaunchKernelGGL((scan_chunk_kernel<N, DT, kSummary, GATE, SKIP, TRAP>),
                            dim3((unsigned)(nb * (a.K - 1) * a.batch)), blk, 0, s, a);
         const int64_t total = a.batch * a.D * N;
         hipLaunchKernelGGL((scan_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     }
-    hipLaunchKernelGGL((scan_chunk_kernel<N, DT, kFinal, GATE, SKIP>),
+    hipLaunchKernelGGL((scan_chunk_kernel<N, DT, kFinal, GATE, SKIP, TRAP>),
                        dim3((unsigned)(nb * a.K * a.batch)), blk, 0, s, a);
     return hipGetLastError();
 }
 
+template <int N, int DT, bool TRAP>
+hipError_t launch_rule(const ScanArgs &a, hipStream_t s) {
+    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
+    if (gate && skip) return launch_typed<N, DT, true, true, TRAP>(a, s);
+    if (gate) return launch_typed<N, DT, true, false, TRAP>(a, s);
+    if (skip) return launch_typed<N, DT, false, true, TRAP>(a, s);
+    return launch_typed<N, DT, false, false, TRAP>(a, s);
+}
+
 template <int N, int DT>
 hipError_t launch_flags(const ScanArgs &a, hipStream_t s) {
-    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
-    if (gate && skip) return launch_typed<N, DT, true, true>(a, s);
-    if (gate) return launch_typed<N, DT, true, false>(a, s);
-    if (skip) return launch_typed<N, DT, false, true>(a, s);
-    return launch_typed<N, DT, false, false>(a, s);
+    return a.lam ? launch_rule<N, DT, true>(a, s) : launch_rule<N, DT, false>(a, s);
 }
 
 template <int N>

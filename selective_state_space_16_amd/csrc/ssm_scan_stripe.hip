@@ -34,8 +34,9 @@ bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, Stri
 }
 
 hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s) {
+    if (a.lam) return launch_scan_stripe_trap(a, N, dtype, s);
     if (a.delta_softplus) return launch_scan_stripe_act(a, N, dtype, s);
-    return launch_stripe_n<false>(a, N, dtype, s);
+    return launch_stripe_n<kEuler>(a, N, dtype, s);
 }
 
 }  // namespace ssm

@@ -5,7 +5,7 @@
 namespace ssm {
 
 hipError_t launch_scan_stripe_act(const StripeArgs &a, int N, int dtype, hipStream_t s) {
-    return launch_stripe_n<true>(a, N, dtype, s);
+    return launch_stripe_n<kSoftplus>(a, N, dtype, s);
 }
 
 }  // namespace ssm

@@ -82,27 +82,33 @@ struct Geo {
     static_assert(ACT_PIECES % 64 == 0, "activation tiles are loaded in whole waves of pieces");
 };
 
-template <int N, int DT>
+// TRAP: the exponential-trapezoidal rule, which also needs the weight lam of
+// each token and the delta and lam of the token after the tile.
+template <int N, int DT, bool TRAP = false>
 struct TileBuf {
     using G = Geo<N, DT>;
     using T = typename G::T;
     // 16-byte aligned: pieces land here as whole 16-byte writes and y is read
     // back as 16-byte reads
     alignas(16) T x[G::TT][G::TCH];
-    alignas(16) T dl[G::TT][G::TCH];  // delta; pass 2 writes y here once a token's delta is used
+    // delta; pass 2 writes y here once a token's delta is used. TRAP: row TT
+    // holds the token after the tile.
+    alignas(16) T dl[G::TT + (TRAP ? 1 : 0)][G::TCH];
     alignas(16) T z[G::TT][G::TCH];
     alignas(16) T B[G::BC_SLOTS * G::VEC];  // Bt rows of the tile's tokens (padded to whole waves of pieces)
     alignas(16) T C[G::BC_SLOTS * G::VEC];
+    alignas(16) T lam[TRAP ? G::TT + 1 : 1][TRAP ? G::TCH : G::VEC];  // TRAP: rows as dl (else a stub)
 };
 
-template <int N, int DT>
+template <int N, int DT, bool TRAP = false>
 struct Shared {
-    TileBuf<N, DT> buf[2];
+    TileBuf<N, DT, TRAP> buf[2];
+    float cb[TRAP ? Geo<N, DT>::TT : 1];  // TRAP, pass 2: sum_n Ct[t,n] Bt[t,n] per token of the current tile
     int unit;  // the unit handed to this workgroup
 };
 
-template <int N, int DT>
-constexpr int stripe_min_blocks() { return 2 * sizeof(Shared<N, DT>) <= 160 * 1024 ? 2 : 1; }
+template <int N, int DT, bool TRAP>
+constexpr int stripe_min_blocks() { return 2 * sizeof(Shared<N, DT, TRAP>) <= 160 * 1024 ? 2 : 1; }
 
 // An activation element of an LDS tile row, widened to float. A bfloat16 is
 // read as the 32-bit word holding it and its neighbour, and moved into the
@@ -147,6 +153,38 @@ __device__ __forceinline__ void lds_bf16_8x2(float (&va)[8], float (&vb)[8], uin
           "i"(OB + 6 * STRIDE), "i"(OB + 7 * STRIDE)
         : "memory");
 }
+// Eight values of each of three arrays, at base + OA + k*STRIDE, base + OB +
+// k*STRIDE and base + OC + k*STRIDE, and the ninth value of the second and
+// third arrays.
+template <int STRIDE, int OA, int OB, int OC>
+__device__ __forceinline__ void lds_bf16_8x3n(float (&va)[8], float (&vb)[8], float (&vc)[8], float &nb, float &nc,
+                                              uint32_t base) {
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %26 offset:%27\n\tds_read_u16_d16_hi %1, %26 offset:%28\n\tds_read_u16_d16_hi %2, %26 offset:%29\n\tds_read_u16_d16_hi %3, %26 offset:%30\n\tds_read_u16_d16_hi %4, %26 offset:%31\n\tds_read_u16_d16_hi %5, %26 offset:%32\n\tds_read_u16_d16_hi %6, %26 offset:%33\n\tds_read_u16_d16_hi %7, %26 offset:%34\n\tds_read_u16_d16_hi %8, %26 offset:%35\n\tds_read_u16_d16_hi %9, %26 offset:%36\n\tds_read_u16_d16_hi %10, %26 offset:%37\n\tds_read_u16_d16_hi %11, %26 offset:%38\n\tds_read_u16_d16_hi %12, %26 offset:%39\n\tds_read_u16_d16_hi %13, %26 offset:%40\n\tds_read_u16_d16_hi %14, %26 offset:%41\n\tds_read_u16_d16_hi %15, %26 offset:%42\n\tds_read_u16_d16_hi %16, %26 offset:%43\n\tds_read_u16_d16_hi %17, %26 offset:%44\n\tds_read_u16_d16_hi %18, %26 offset:%45\n\tds_read_u16_d16_hi %19, %26 offset:%46\n\tds_read_u16_d16_hi %20, %26 offset:%47\n\tds_read_u16_d16_hi %21, %26 offset:%48\n\tds_read_u16_d16_hi %22, %26 offset:%49\n\tds_read_u16_d16_hi %23, %26 offset:%50\n\tds_read_u16_d16_hi %24, %26 offset:%51\n\tds_read_u16_d16_hi %25, %26 offset:%52\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]),
+          "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]), "+v"(vb[4]), "+v"(vb[5]), "+v"(vb[6]), "+v"(vb[7]),
+          "+v"(vc[0]), "+v"(vc[1]), "+v"(vc[2]), "+v"(vc[3]), "+v"(vc[4]), "+v"(vc[5]), "+v"(vc[6]), "+v"(vc[7]),
+          "+v"(nb), "+v"(nc)
+        : "v"(base), "i"(OA), "i"(OA + STRIDE), "i"(OA + 2 * STRIDE), "i"(OA + 3 * STRIDE), "i"(OA + 4 * STRIDE),
+          "i"(OA + 5 * STRIDE), "i"(OA + 6 * STRIDE), "i"(OA + 7 * STRIDE), "i"(OB), "i"(OB + STRIDE),
+          "i"(OB + 2 * STRIDE), "i"(OB + 3 * STRIDE), "i"(OB + 4 * STRIDE), "i"(OB + 5 * STRIDE),
+          "i"(OB + 6 * STRIDE), "i"(OB + 7 * STRIDE), "i"(OC), "i"(OC + STRIDE), "i"(OC + 2 * STRIDE),
+          "i"(OC + 3 * STRIDE), "i"(OC + 4 * STRIDE), "i"(OC + 5 * STRIDE), "i"(OC + 6 * STRIDE),
+          "i"(OC + 7 * STRIDE), "i"(OB + 8 * STRIDE), "i"(OC + 8 * STRIDE)
+        : "memory");
+}
+// Two values of each of two arrays: a at base + OA + {0, SA}, b at base + OB + {0, SA}.
+template <int SA, int OA, int OB>
+__device__ __forceinline__ void lds_bf16_2x2(float (&va)[2], float (&vb)[2], uint32_t base) {
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %4 offset:%5\n\tds_read_u16_d16_hi %1, %4 offset:%6\n\t"
+        "ds_read_u16_d16_hi %2, %4 offset:%7\n\tds_read_u16_d16_hi %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(va[0]), "+v"(va[1]), "+v"(vb[0]), "+v"(vb[1])
+        : "v"(base), "i"(OA), "i"(OA + SA), "i"(OB), "i"(OB + SA)
+        : "memory");
+}
 // Two values of each of four arrays: a at ab + OA + {0, SA}, b at ab + OB +
 // {0, SA}, c at cd + OC + {0, SC}, d at cd + OD + {0, SC}.
 template <int SA, int SC, int OA, int OB, int OC, int OD>
@@ -186,50 +224,13 @@ __device__ __forceinline__ uint32_t take_unit(uint32_t *ctr) {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Load the tile of TT tokens starting at tt0 of tile column (b, ch0) into
-// LDS, spread over waves 1..3. Pass 1 needs x, delta and Bt; pass 2 also z
-// and Ct. Each wave moves slots of 64 16-byte pieces; a slot of an activation
-// array covers whole tile rows, so a piece's address is a wave-uniform row
-// address (SGPRs) plus the lane's offset within the slot, `act_off`, which is
-// the same for every tile of a unit. Only the last tile of a sequence, whose
-// rows may run past L, takes the per-piece path: pieces past the end of the
-// sequence are read from the last token instead, and the tokens are given
-// delta = 0 afterwards. Channels past D (a last, partial column) are read
-// from the last whole piece of the row and never stored.
-template <int N, int DT, bool GATE, int PASS, int WV>
-__device__ __forceinline__ void load_tile_w(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
-                                            int lane, uint32_t act_off) {
+// The per-piece path of load_tile_w, with addresses clamped into the sequence.
+template <int N, int DT, int NACT, int NBC, bool HAS_Z, bool TRAP>
+__device__ __forceinline__ void load_tile_clamped(TileBuf<N, DT, TRAP> &tb, const StripeArgs &a, int64_t b,
+                                                  int64_t ch0, int64_t tt0, int w, int lane) {
     using G = Geo<N, DT>;
     using T = typename G::T;
-    constexpr int NACT = (PASS == 2 && GATE) ? 3 : 2;
-    constexpr int NBC = PASS == 2 ? 2 : 1;
-    using TB = TileBuf<N, DT>;
     const int64_t D = a.D, L = a.L;
-    if (tt0 + G::TT <= L) {
-        const uint32_t rowb = (uint32_t)(D * G::ESZ);
-        const int64_t off = ((b * L + tt0) * D + ch0) * G::ESZ;
-        const uint32_t lds_tb = lds_addr(&tb);
-        // the wave's slots: pieces (WV - 1) * 64 + 192 * k
-        static_for<0, (NACT * G::ACT_PIECES - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
-            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
-            constexpr int arr = base / G::ACT_PIECES;
-            constexpr int pa0 = base - arr * G::ACT_PIECES;  // first piece of the slot
-            const void *p = arr == 0 ? a.x : arr == 1 ? a.delta : a.z;
-            constexpr int dst = (arr == 0 ? offsetof(TB, x) : arr == 1 ? offsetof(TB, dl) : offsetof(TB, z)) + pa0 * 16;
-            dma16_s((const char *)p + off + (uint64_t)(pa0 / G::PPR) * rowb, act_off, lds_tb + dst);
-        });
-        const int64_t boff = (b * L + tt0) * N * G::ESZ;
-        static_for<0, (NBC * G::BC_SLOTS - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
-            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
-            constexpr int arr = base / G::BC_SLOTS;
-            constexpr int pq0 = base - arr * G::BC_SLOTS;
-            const int pq = pq0 + lane < G::BC_PIECES ? pq0 + lane : G::BC_PIECES - 1;  // padding repeats the last piece
-            constexpr int dst = (arr == 0 ? offsetof(TB, B) : offsetof(TB, C)) + pq0 * 16;
-            dma16_s((const char *)(arr == 0 ? a.Bt : a.Ct) + boff, (uint32_t)pq * 16, lds_tb + dst);
-        });
-        return;
-    }
-    const int w = WV;
     for (int base = (w - 1) * 64; base < NACT * G::ACT_PIECES; base += 3 * 64) {
         const int arr = base / G::ACT_PIECES;
         const int pa = base - arr * G::ACT_PIECES + lane;
@@ -238,8 +239,9 @@ __device__ __forceinline__ void load_tile_w(TileBuf<N, DT> &tb, const StripeArgs
         t = t < L ? t : L - 1;
         int64_t ch = ch0 + c;
         ch = ch + G::VEC <= D ? ch : D - G::VEC;
-        const T *src = arr == 0 ? (const T *)a.x : arr == 1 ? (const T *)a.delta : (const T *)a.z;
-        T *dst = arr == 0 ? &tb.x[0][0] : arr == 1 ? &tb.dl[0][0] : &tb.z[0][0];
+        const bool is_z = arr == 2 && HAS_Z;
+        const T *src = arr == 0 ? (const T *)a.x : arr == 1 ? (const T *)a.delta : is_z ? (const T *)a.z : (const T *)a.lam;
+        T *dst = arr == 0 ? &tb.x[0][0] : arr == 1 ? &tb.dl[0][0] : is_z ? &tb.z[0][0] : &tb.lam[0][0];
         dma16(src + (b * L + t) * D + ch, lds_addr(dst + (int64_t)(base - arr * G::ACT_PIECES) * G::VEC));
     }
     for (int base = (w - 1) * 64; base < NBC * G::BC_SLOTS; base += 3 * 64) {
@@ -255,12 +257,76 @@ __device__ __forceinline__ void load_tile_w(TileBuf<N, DT> &tb, const StripeArgs
     }
 }
 
-template <int N, int DT, bool GATE, int PASS>
-__device__ __forceinline__ void load_tile(TileBuf<N, DT> &tb, const StripeArgs &a, int64_t b, int64_t ch0, int64_t tt0,
-                                          int w, int lane, uint32_t act_off) {
-    if (w == 1) load_tile_w<N, DT, GATE, PASS, 1>(tb, a, b, ch0, tt0, lane, act_off);
-    else if (w == 2) load_tile_w<N, DT, GATE, PASS, 2>(tb, a, b, ch0, tt0, lane, act_off);
-    else load_tile_w<N, DT, GATE, PASS, 3>(tb, a, b, ch0, tt0, lane, act_off);
+// Load the tile of TT tokens starting at tt0 of tile column (b, ch0) into
+// LDS, spread over waves 1..3. Pass 1 needs x, delta and Bt; pass 2 also z
+// and Ct. Each wave moves slots of 64 16-byte pieces; a slot of an activation
+// array covers whole tile rows, so a piece's address is a wave-uniform row
+// address (SGPRs) plus the lane's offset within the slot, `act_off`, which is
+// the same for every tile of a unit. Only the last tile of a sequence, whose
+// rows may run past L, takes the per-piece path: pieces past the end of the
+// sequence are read from the last token instead, and the tokens are given
+// delta = 0 afterwards. Channels past D (a last, partial column) are read
+// from the last whole piece of the row and never stored. TRAP adds lam, and
+// the delta (wave 1) and lam (wave 2) row of the token after the tile, read
+// from the last token when there is none.
+template <int N, int DT, bool GATE, int PASS, int WV, bool TRAP>
+__device__ __forceinline__ void load_tile_w(TileBuf<N, DT, TRAP> &tb, const StripeArgs &a, int64_t b, int64_t ch0,
+                                            int64_t tt0, int lane, uint32_t act_off) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    constexpr bool HAS_Z = PASS == 2 && GATE;
+    constexpr int NACT = 2 + (HAS_Z ? 1 : 0) + (TRAP ? 1 : 0);  // x, delta, [z], [lam]
+    constexpr int NBC = PASS == 2 ? 2 : 1;
+    using TB = TileBuf<N, DT, TRAP>;
+    const int64_t D = a.D, L = a.L;
+    if (tt0 + G::TT <= L) {
+        const uint32_t rowb = (uint32_t)(D * G::ESZ);
+        const int64_t off = ((b * L + tt0) * D + ch0) * G::ESZ;
+        const uint32_t lds_tb = lds_addr(&tb);
+        // the wave's slots: pieces (WV - 1) * 64 + 192 * k
+        static_for<0, (NACT * G::ACT_PIECES - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
+            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
+            constexpr int arr = base / G::ACT_PIECES;
+            constexpr int pa0 = base - arr * G::ACT_PIECES;  // first piece of the slot
+            constexpr bool is_z = arr == 2 && HAS_Z;
+            const void *p = arr == 0 ? a.x : arr == 1 ? a.delta : is_z ? a.z : a.lam;
+            constexpr int dst = (arr == 0   ? offsetof(TB, x)
+                                 : arr == 1 ? offsetof(TB, dl)
+                                 : is_z     ? offsetof(TB, z)
+                                            : offsetof(TB, lam)) +
+                                pa0 * 16;
+            dma16_s((const char *)p + off + (uint64_t)(pa0 / G::PPR) * rowb, act_off, lds_tb + dst);
+        });
+        const int64_t boff = (b * L + tt0) * N * G::ESZ;
+        static_for<0, (NBC * G::BC_SLOTS - (WV - 1) * 64 + 191) / 192>([&](auto kc) {
+            constexpr int base = (WV - 1) * 64 + 192 * decltype(kc)::value;
+            constexpr int arr = base / G::BC_SLOTS;
+            constexpr int pq0 = base - arr * G::BC_SLOTS;
+            const int pq = pq0 + lane < G::BC_PIECES ? pq0 + lane : G::BC_PIECES - 1;  // padding repeats the last piece
+            constexpr int dst = (arr == 0 ? offsetof(TB, B) : offsetof(TB, C)) + pq0 * 16;
+            dma16_s((const char *)(arr == 0 ? a.Bt : a.Ct) + boff, (uint32_t)pq * 16, lds_tb + dst);
+        });
+    } else {
+        load_tile_clamped<N, DT, NACT, NBC, HAS_Z, TRAP>(tb, a, b, ch0, tt0, WV, lane);
+    }
+    if constexpr (TRAP && (WV == 1 || WV == 2)) {
+        if (lane < G::PPR) {
+            int64_t t = tt0 + G::TT;
+            t = t < L ? t : L - 1;
+            int64_t ch = ch0 + (int64_t)lane * G::VEC;
+            ch = ch + G::VEC <= D ? ch : D - G::VEC;
+            const T *src = WV == 1 ? (const T *)a.delta : (const T *)a.lam;
+            dma16(src + (b * L + t) * D + ch, lds_addr(WV == 1 ? &tb.dl[G::TT][0] : &tb.lam[G::TT][0]));
+        }
+    }
+}
+
+template <int N, int DT, bool GATE, int PASS, bool TRAP>
+__device__ __forceinline__ void load_tile(TileBuf<N, DT, TRAP> &tb, const StripeArgs &a, int64_t b, int64_t ch0,
+                                          int64_t tt0, int w, int lane, uint32_t act_off) {
+    if (w == 1) load_tile_w<N, DT, GATE, PASS, 1, TRAP>(tb, a, b, ch0, tt0, lane, act_off);
+    else if (w == 2) load_tile_w<N, DT, GATE, PASS, 2, TRAP>(tb, a, b, ch0, tt0, lane, act_off);
+    else load_tile_w<N, DT, GATE, PASS, 3, TRAP>(tb, a, b, ch0, tt0, lane, act_off);
 }
 
 // Step-size activation for a raw step: once a tile has landed, the
@@ -302,17 +368,36 @@ __device__ __forceinline__ void publish_state(uint64_t *rec, int l, const float 
     for (int j = 0; j < NL; ++j) st_tagged(rec + j * 64 + l, S[j], epoch);
 }
 
-// SP: delta holds the step size before its activation (softplus(delta +
-// dt_bias), applied to each tile as it lands); a separate instance, so that
-// the kernels for an activated delta carry none of that code.
-template <int N, int DT, bool GATE, bool SKIP, bool SP>
-__global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void scan_stripe_kernel(StripeArgs a) {
+// What the scan computes besides the exponential-Euler recurrence on an
+// activated step size; each is a separate instance, so that the kernels for
+// the plain rule carry none of that code.
+//  kSoftplus: delta holds the step size before its activation (softplus(delta
+//    + dt_bias), applied to each tile as it lands).
+//  kTrap: the exponential-trapezoidal rule ("Notas sobre Mamba", section
+//    "Recorrência trapezoidal"): h_t = a_t h_{t-1} + mu_t a_t v_{t-1} +
+//    lam_t delta_t v_t, with a_t = exp(delta_t A), v_t = B_t x_t and mu_t =
+//    (1 - lam_t) delta_t. The kernel runs the same recurrence on
+//    k_t = h_t + mu_{t+1} v_t, which is
+//      k_t = a_t k_{t-1} + (lam_t delta_t + mu_{t+1}) v_t,
+//    the exponential-Euler form with the input weight lam_t delta_t +
+//    mu_{t+1} in place of delta_t; so a state update costs what it costs
+//    there, and stripes compose as before. Then
+//      y_t = C_t . k_t - mu_{t+1} x_t (C_t . B_t) + D x_t   (before the gate),
+//    k starts from h_in + mu_0 v_{-1}, and mu_L = 0 (no token after the call)
+//    makes the final k the final h.
+enum ScanMode { kEuler = 0, kSoftplus = 1, kTrap = 2 };
+
+template <int N, int DT, bool GATE, bool SKIP, int MODE>
+__global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTrap>())) void scan_stripe_kernel(
+    StripeArgs a) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TCH = G::TCH, TPV = G::TPV, BREGS = G::BREGS;
     constexpr int TT = G::TT, GROUP = G::GROUP;
+    constexpr bool SP = MODE == kSoftplus, TRAP = MODE == kTrap;
+    using TBT = TileBuf<N, DT, TRAP>;
 
-    __shared__ Shared<N, DT> sh;
+    __shared__ Shared<N, DT, TRAP> sh;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
     const int l = threadIdx.x & 63;
@@ -386,7 +471,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         float h[NL];
         // The finished y of tile i (pass 2): every wave writes a share of it back
         // as whole lines from the tile's delta area.
-        auto store_y = [&](const TileBuf<N, DT> &tb, int i) {
+        auto store_y = [&](const TBT &tb, int i) {
             using VT = uint32_t __attribute__((ext_vector_type(4)));
             const int64_t tt0 = t0 + (int64_t)i * TT;
             const int64_t rows = t1 - tt0;  // tokens of the tile inside the stripe
@@ -403,7 +488,17 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
         // First tile of a pass, loaded ahead (before the look-back, for pass 2).
         auto prefetch = [&](auto pass_c) {
             constexpr int PASS = decltype(pass_c)::value;
-            if (w > 0) load_tile<N, DT, GATE, PASS>(sh.buf[0], a, b, ch0, t0, w, l, act_off);
+            if (w > 0) load_tile<N, DT, GATE, PASS, TRAP>(sh.buf[0], a, b, ch0, t0, w, l, act_off);
+        };
+        // TRAP, pass 2: C_t . B_t of every token of a landed tile, into sh.cb
+        auto tile_cb = [&](const TBT &tb) {
+            if (threadIdx.x < TT) {
+                const T *Br = &tb.B[threadIdx.x * N], *Cr = &tb.C[threadIdx.x * N];
+                float cbv = 0.0f;
+#pragma unroll
+                for (int n = 0; n < N; ++n) cbv = __builtin_fmaf(lds_act(Cr, n, half_sel(n)), lds_act(Br, n, half_sel(n)), cbv);
+                sh.cb[threadIdx.x] = cbv;
+            }
         };
         auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
             constexpr int PASS = decltype(pass_c)::value;
@@ -411,8 +506,13 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
             // finished tokens per lane take the high-half loads
             constexpr bool kHiLoads = DT == 1 && GROUP == 8 && BREGS == 2 && G::OWN == 2;
             float xv[GROUP], dv[GROUP], Bq[BREGS], Cq[BREGS], xo[G::OWN], zo[G::OWN];
+            // TRAP: lam of the group's tokens, delta and lam of the token after
+            // the group, and of the token after each finished token
+            float lv[GROUP], dn = 0.0f, ln = 0.0f, dno[G::OWN], lno[G::OWN];
 #pragma unroll
-            for (int t = 0; t < GROUP; ++t) xv[t] = dv[t] = 0.0f;
+            for (int t = 0; t < GROUP; ++t) xv[t] = dv[t] = lv[t] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < G::OWN; ++q) dno[q] = lno[q] = 0.0f;
 #pragma unroll
             for (int q = 0; q < BREGS; ++q) Bq[q] = Cq[q] = 0.0f;
 #pragma unroll
@@ -420,7 +520,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
             if (w > 0) vm_wait();  // the first tile (prefetch) has landed
             lds_barrier();
             for (int i = 0; i < ntiles; ++i) {
-                TileBuf<N, DT> &tb = sh.buf[i & 1];
+                TBT &tb = sh.buf[i & 1];
                 const int64_t tt0 = t0 + (int64_t)i * TT;
                 if constexpr (PASS == 2) {
                     // y of the previous tile goes out now, so that the stores
@@ -428,21 +528,36 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                     if (i > 0) store_y(sh.buf[(i - 1) & 1], i - 1);
                 }
                 if constexpr (SP) activate_delta(tb, dtb);  // this tile has landed for every wave
-                if (SP || (PASS == 2 && i > 0)) lds_barrier();
-                if (w > 0 && i + 1 < ntiles) load_tile<N, DT, GATE, PASS>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l, act_off);
-                const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
-                if (tail < TT) {
-                    // tokens past the end were loaded from the last token; give
-                    // them delta = 0 so that they leave the state unchanged
-                    for (int q = threadIdx.x; q < (TT - (int)tail) * TCH; q += 64 * kWaves)
-                        tb.dl[tail + q / TCH][q % TCH] = T(0.0f);
-                    lds_barrier();
+                if constexpr (TRAP && PASS == 2) tile_cb(tb);
+                if (SP || (PASS == 2 && (TRAP || i > 0))) lds_barrier();
+                if (w > 0 && i + 1 < ntiles)
+                    load_tile<N, DT, GATE, PASS, TRAP>(sh.buf[(i + 1) & 1], a, b, ch0, tt0 + TT, w, l, act_off);
+                // tokens past the end were loaded from the last token; give
+                // them delta = 0 so that they leave the state unchanged
+                if constexpr (TRAP) {
+                    // The call's last tile, with the token after it: rows from
+                    // L - tt0 through TT. (Stripes are whole tiles, so any other
+                    // tile is full and its next token is real.) mu is then 0
+                    // from token L on.
+                    if (tt0 + TT >= L) {
+                        const int first = (int)(L - tt0);
+                        for (int q = threadIdx.x; q < (TT + 1 - first) * TCH; q += 64 * kWaves)
+                            tb.dl[first + q / TCH][q % TCH] = T(0.0f);
+                        lds_barrier();
+                    }
+                } else {
+                    const int64_t tail = t1 - tt0;  // tokens of this tile inside the stripe
+                    if (tail < TT) {
+                        for (int q = threadIdx.x; q < (TT - (int)tail) * TCH; q += 64 * kWaves)
+                            tb.dl[tail + q / TCH][q % TCH] = T(0.0f);
+                        lds_barrier();
+                    }
                 }
                 // per-lane LDS byte addresses in this tile: the lane's channel
                 // column, its Bt/Ct element and its first owned token's row
-                using TB = TileBuf<N, DT>;
+                using TB = TBT;
                 constexpr int ROWB = TCH * G::ESZ, BCB = N * G::ESZ;
-                constexpr int OFF_DL = offsetof(TB, dl), OFF_Z = offsetof(TB, z);
+                constexpr int OFF_DL = offsetof(TB, dl), OFF_Z = offsetof(TB, z), OFF_LAM = offsetof(TB, lam);
                 constexpr int OFF_B = offsetof(TB, B), OFF_C = offsetof(TB, C);
                 const uint32_t a_ch = lds_addr(&tb) + cl * G::ESZ;
                 const uint32_t a_bc = lds_addr(&tb) + OFF_B + ((k16 / NL) * N + nstate0 + (k16 % NL)) * G::ESZ;
@@ -459,10 +574,17 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                     if constexpr (kHiLoads) {
                         // bfloat16: loads into the high halves of the registers
                         // that held the previous group's values
-                        lds_bf16_8x2<ROWB, tg * ROWB, OFF_DL + tg * ROWB>(xv, dv, a_ch);
+                        if constexpr (TRAP)
+                            lds_bf16_8x3n<ROWB, tg * ROWB, OFF_DL + tg * ROWB, OFF_LAM + tg * ROWB>(xv, dv, lv, dn, ln,
+                                                                                                  a_ch);
+                        else
+                            lds_bf16_8x2<ROWB, tg * ROWB, OFF_DL + tg * ROWB>(xv, dv, a_ch);
                         if constexpr (PASS == 2) {
                             lds_bf16_2x4<TPV * BCB, NGR * ROWB, tg * BCB, OFF_C - OFF_B + tg * BCB, tg * ROWB,
                                          OFF_Z + tg * ROWB>(Bq, Cq, xo, zo, a_bc, a_own);
+                            if constexpr (TRAP)
+                                lds_bf16_2x2<NGR * ROWB, OFF_DL + (tg + 1) * ROWB, OFF_LAM + (tg + 1) * ROWB>(dno, lno,
+                                                                                                          a_own);
                         } else {
                             lds_bf16_2<TPV * BCB, tg * BCB>(Bq, a_bc);
                         }
@@ -471,6 +593,11 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         for (int t = 0; t < GROUP; ++t) {
                             xv[t] = lds_act(&tb.x[tg + t][0], cl, sel_ch);
                             dv[t] = lds_act(&tb.dl[tg + t][0], cl, sel_ch);
+                            if constexpr (TRAP) lv[t] = lds_act(&tb.lam[tg + t][0], cl, sel_ch);
+                        }
+                        if constexpr (TRAP) {
+                            dn = lds_act(&tb.dl[tg + GROUP][0], cl, sel_ch);
+                            ln = lds_act(&tb.lam[tg + GROUP][0], cl, sel_ch);
                         }
 #pragma unroll
                         for (int q = 0; q < BREGS; ++q) {
@@ -483,15 +610,38 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
 #pragma unroll
                             for (int q = 0; q < G::OWN; ++q) {
                                 const int tw = tg + NGR * q + g;
-                                xo[q] = SKIP ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
+                                xo[q] = (SKIP || TRAP) ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
                                 zo[q] = GATE ? lds_act(&tb.z[tw][0], cl, sel_ch) : 0.0f;
+                                if constexpr (TRAP) {
+                                    dno[q] = lds_act(&tb.dl[tw + 1][0], cl, sel_ch);
+                                    lno[q] = lds_act(&tb.lam[tw + 1][0], cl, sel_ch);
+                                }
                             }
                         }
                     }
+                    // input weight times x of token t of the group: delta x, or
+                    // for TRAP (lam delta + mu of the next token) x
+                    auto in_x = [&](auto tc) {
+                        constexpr int t = decltype(tc)::value;
+                        if constexpr (TRAP) {
+                            float dnx, lnx;
+                            if constexpr (t + 1 < GROUP) {
+                                dnx = dv[t + 1];
+                                lnx = lv[t + 1];
+                            } else {
+                                dnx = dn;
+                                lnx = ln;
+                            }
+                            const float mu = __builtin_fmaf(-lnx, dnx, dnx);
+                            return __builtin_fmaf(lv[t], dv[t], mu) * xv[t];
+                        } else {
+                            return dv[t] * xv[t];
+                        }
+                    };
                     if constexpr (PASS == 1) {
                         static_for<0, GROUP>([&](auto tc) {
                             constexpr int t = decltype(tc)::value;
-                            const float dx = dv[t] * xv[t];
+                            const float dx = in_x(tc);
                             dsum += dv[t];
                             static_for<0, NL>([&](auto jc) {
                                 constexpr int q = decltype(jc)::value;
@@ -503,7 +653,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         float yp[GROUP];
                         static_for<0, GROUP>([&](auto tc) {
                             constexpr int t = decltype(tc)::value;
-                            const float dx = dv[t] * xv[t];
+                            const float dx = in_x(tc);
                             static_for<0, NL>([&](auto jc) {
                                 constexpr int q = decltype(jc)::value;
                                 const float dA = fast_exp2(dv[t] * A2[q]);
@@ -540,6 +690,11 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
                         for (int q = 0; q < G::OWN; ++q) {
                             const int tw = tg + NGR * q + g;
                             float yv = yo[q];
+                            if constexpr (TRAP) {
+                                // h = k - mu_{t+1} v_t: subtract mu_{t+1} x_t (C_t . B_t)
+                                const float mu = __builtin_fmaf(-lno[q], dno[q], dno[q]);
+                                yv = __builtin_fmaf(-mu * xo[q], sh.cb[tw], yv);
+                            }
                             if (SKIP) yv = __builtin_fmaf(dskip, xo[q], yv);
                             if (GATE) yv *= silu(zo[q]);
                             st_act(&tb.dl[tw][0], cl, yv);
@@ -572,6 +727,17 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
             const float *si = a.state_in ? a.state_in + (b * D + dc) * N + nstate0 : nullptr;
 #pragma unroll
             for (int q = 0; q < NL; ++q) h[q] = si ? si[q] : 0.0f;
+            if constexpr (TRAP) {
+                // k starts from h_in + mu_0 v_{-1}, v_{-1} = B_prev x_prev
+                if (a.x_prev) {
+                    const int64_t r0 = b * L * D + dc;  // token 0
+                    const float d0 = ld_act((const T *)a.delta, r0), l0 = ld_act((const T *)a.lam, r0);
+                    const float px = __builtin_fmaf(-l0, d0, d0) * ld_act((const T *)a.x_prev, b * D + dc);
+#pragma unroll
+                    for (int q = 0; q < NL; ++q)
+                        h[q] = __builtin_fmaf(px, ld_act((const T *)a.B_prev, b * N + nstate0 + q), h[q]);
+                }
+            }
         } else {
             // Look back over the earlier stripes of this column: the nearest
             // one whose end state is out, with the aggregates of all stripes
@@ -658,9 +824,9 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT>())) void sca
     }
 }
 
-template <int N, int DT, bool GATE, bool SKIP, bool SP>
+template <int N, int DT, bool GATE, bool SKIP, int MODE>
 hipError_t launch_stripe_typed(const StripeArgs &a, hipStream_t s) {
-    auto kern = scan_stripe_kernel<N, DT, GATE, SKIP, SP>;
+    auto kern = scan_stripe_kernel<N, DT, GATE, SKIP, MODE>;
     constexpr int kMaxDevices = 64;
     // CU count and resident workgroups per CU, queried once per device:
     // (cus << 32 | per_cu), 0 = not queried yet
@@ -687,28 +853,28 @@ hipError_t launch_stripe_typed(const StripeArgs &a, hipStream_t s) {
     return hipLaunchKernel((const void *)kern, dim3((unsigned)(per_list * kLists)), dim3(64 * kWaves), params, 0, s);
 }
 
-template <int N, int DT, bool SP>
+template <int N, int DT, int MODE>
 hipError_t launch_stripe_flags(const StripeArgs &a, hipStream_t s) {
     const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
-    if (gate && skip) return launch_stripe_typed<N, DT, true, true, SP>(a, s);
-    if (gate) return launch_stripe_typed<N, DT, true, false, SP>(a, s);
-    if (skip) return launch_stripe_typed<N, DT, false, true, SP>(a, s);
-    return launch_stripe_typed<N, DT, false, false, SP>(a, s);
+    if (gate && skip) return launch_stripe_typed<N, DT, true, true, MODE>(a, s);
+    if (gate) return launch_stripe_typed<N, DT, true, false, MODE>(a, s);
+    if (skip) return launch_stripe_typed<N, DT, false, true, MODE>(a, s);
+    return launch_stripe_typed<N, DT, false, false, MODE>(a, s);
 }
 
-template <int N, bool SP>
+template <int N, int MODE>
 hipError_t launch_stripe_dtype(const StripeArgs &a, int dtype, hipStream_t s) {
-    return dtype == 0 ? launch_stripe_flags<N, 0, SP>(a, s) : launch_stripe_flags<N, 1, SP>(a, s);
+    return dtype == 0 ? launch_stripe_flags<N, 0, MODE>(a, s) : launch_stripe_flags<N, 1, MODE>(a, s);
 }
 
-template <bool SP>
+template <int MODE>
 hipError_t launch_stripe_n(const StripeArgs &a, int N, int dtype, hipStream_t s) {
     switch (N) {
-        case 1: return launch_stripe_dtype<1, SP>(a, dtype, s);
-        case 2: return launch_stripe_dtype<2, SP>(a, dtype, s);
-        case 4: return launch_stripe_dtype<4, SP>(a, dtype, s);
-        case 8: return launch_stripe_dtype<8, SP>(a, dtype, s);
-        case 16: return launch_stripe_dtype<16, SP>(a, dtype, s);
+        case 1: return launch_stripe_dtype<1, MODE>(a, dtype, s);
+        case 2: return launch_stripe_dtype<2, MODE>(a, dtype, s);
+        case 4: return launch_stripe_dtype<4, MODE>(a, dtype, s);
+        case 8: return launch_stripe_dtype<8, MODE>(a, dtype, s);
+        case 16: return launch_stripe_dtype<16, MODE>(a, dtype, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -83,11 +83,22 @@ __device__ __forceinline__ float from_lane(int src, float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src * 4, __builtin_bit_cast(int, v)));
 }
 
+// What the step computes besides the exponential-Euler update on an
+// activated step size.
+enum StepMode { kEuler = 0, kSoftplus = 1, kTrap = 2 };
+
 // Grid: x = block of kBlockCh channels, y = group of kRows batch rows
-// (strided by gridDim.y when the groups outnumber kMaxGridY). SP: delta holds
-// the step size before its activation, softplus(delta + dt_bias).
-template <int N, int DT, bool GATE, bool SKIP, bool SP>
+// (strided by gridDim.y when the groups outnumber kMaxGridY).
+// MODE kSoftplus: delta holds the step size before its activation,
+// softplus(delta + dt_bias). MODE kTrap: the exponential-trapezoidal rule
+// ("Notas sobre Mamba", section "Recorrência trapezoidal"),
+//   h = a h + (1 - lam) delta a v_prev + lam delta v,  a = exp(delta A),
+// with v = B x of this token and v_prev = B_prev x_prev of the previous one
+// (zero when x_prev and B_prev are not given), taken as
+//   h = a (h + ((1 - lam) delta x_prev) B_prev) + (lam delta x) B.
+template <int N, int DT, bool GATE, bool SKIP, int MODE>
 __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
+    constexpr bool SP = MODE == kSoftplus, TRAP = MODE == kTrap;
     using T = typename Act<DT>::T;
     constexpr int NPL = N < 4 ? N : 4;
     constexpr int LPC = N / NPL;        // lanes per channel = accesses per row
@@ -133,8 +144,8 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
             bok[r] = b < a.batch;
             bc[r] = bok[r] ? b : a.batch - 1;
         }
-        float h[kRows][LPC][NPL], xo[kRows], dto[kRows], zo[kRows];
-        typename BC::T braw[kRows], craw[kRows];
+        float h[kRows][LPC][NPL], xo[kRows], dto[kRows], zo[kRows], lo[kRows], xpo[kRows];
+        typename BC::T braw[kRows], craw[kRows], bpraw[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; ++r)
 #pragma unroll
@@ -148,24 +159,50 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
             if (GATE) zo[r] = ld_act((const T *)a.z, row);
             braw[r] = BC::load(Bp + bc[r] * N + n0);
             craw[r] = BC::load(Cp + bc[r] * N + n0);
+            if constexpr (TRAP) {
+                lo[r] = ld_act((const T *)a.lam, row);
+                if (a.x_prev) {
+                    xpo[r] = ld_act((const T *)a.x_prev, bc[r] * D + own);
+                    bpraw[r] = BC::load((const T *)a.B_prev + bc[r] * N + n0);
+                }
+            }
         }
 
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
-            float Bv[NPL], Cv[NPL], acc[LPC];
+            float Bv[NPL], Cv[NPL], Bpv[NPL], acc[LPC];
             BC::widen(braw[r], Bv);
             BC::widen(craw[r], Cv);
+            if constexpr (TRAP) {
+                if (a.x_prev) BC::widen(bpraw[r], Bpv);
+            }
 #pragma unroll
             for (int q = 0; q < LPC; ++q) {
                 const int src = q * CPA + l / LPC;
                 const float dt = LPC == 1 ? dto[r] : from_lane(src, dto[r]);
                 const float xv = LPC == 1 ? xo[r] : from_lane(src, xo[r]);
-                const float dx = dt * xv;
                 float s = 0.0f;
+                if constexpr (TRAP) {
+                    const float lm = LPC == 1 ? lo[r] : from_lane(src, lo[r]);
+                    const float dx = lm * dt * xv;
+                    if (a.x_prev) {
+                        const float xp = LPC == 1 ? xpo[r] : from_lane(src, xpo[r]);
+                        const float px = (dt - lm * dt) * xp;
 #pragma unroll
-                for (int j = 0; j < NPL; ++j) {
-                    h[r][q][j] = __builtin_fmaf(fast_exp2(dt * A2[q][j]), h[r][q][j], dx * Bv[j]);
-                    s = __builtin_fmaf(Cv[j], h[r][q][j], s);
+                        for (int j = 0; j < NPL; ++j) h[r][q][j] = __builtin_fmaf(px, Bpv[j], h[r][q][j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NPL; ++j) {
+                        h[r][q][j] = __builtin_fmaf(fast_exp2(dt * A2[q][j]), h[r][q][j], dx * Bv[j]);
+                        s = __builtin_fmaf(Cv[j], h[r][q][j], s);
+                    }
+                } else {
+                    const float dx = dt * xv;
+#pragma unroll
+                    for (int j = 0; j < NPL; ++j) {
+                        h[r][q][j] = __builtin_fmaf(fast_exp2(dt * A2[q][j]), h[r][q][j], dx * Bv[j]);
+                        s = __builtin_fmaf(Cv[j], h[r][q][j], s);
+                    }
                 }
                 if (bok[r] && okq[q]) st_vec<NPL>(a.state + (bc[r] * D + chq[q]) * N + n0, h[r][q]);
                 acc[q] = group_sum<LPC>(s);
@@ -187,28 +224,29 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
     }
 }
 
-template <int N, int DT, bool GATE, bool SKIP, bool SP>
+template <int N, int DT, bool GATE, bool SKIP, int MODE>
 hipError_t launch_step_typed(const StepArgs &a, hipStream_t s) {
     const int64_t groups = (a.batch + kRows - 1) / kRows;
     if ((a.D + kBlockCh - 1) / kBlockCh > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((a.D + kBlockCh - 1) / kBlockCh), (unsigned)(groups < kMaxGridY ? groups : kMaxGridY));
-    hipLaunchKernelGGL((step_kernel<N, DT, GATE, SKIP, SP>), grid, dim3(kStepBlock), 0, s, a);
+    hipLaunchKernelGGL((step_kernel<N, DT, GATE, SKIP, MODE>), grid, dim3(kStepBlock), 0, s, a);
     return hipGetLastError();
+}
+
+template <int N, int DT, int MODE>
+hipError_t launch_step_mode(const StepArgs &a, hipStream_t s) {
+    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
+    if (gate && skip) return launch_step_typed<N, DT, true, true, MODE>(a, s);
+    if (gate) return launch_step_typed<N, DT, true, false, MODE>(a, s);
+    if (skip) return launch_step_typed<N, DT, false, true, MODE>(a, s);
+    return launch_step_typed<N, DT, false, false, MODE>(a, s);
 }
 
 template <int N, int DT>
 hipError_t launch_step_flags(const StepArgs &a, hipStream_t s) {
-    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
-    if (a.delta_softplus) {
-        if (gate && skip) return launch_step_typed<N, DT, true, true, true>(a, s);
-        if (gate) return launch_step_typed<N, DT, true, false, true>(a, s);
-        if (skip) return launch_step_typed<N, DT, false, true, true>(a, s);
-        return launch_step_typed<N, DT, false, false, true>(a, s);
-    }
-    if (gate && skip) return launch_step_typed<N, DT, true, true, false>(a, s);
-    if (gate) return launch_step_typed<N, DT, true, false, false>(a, s);
-    if (skip) return launch_step_typed<N, DT, false, true, false>(a, s);
-    return launch_step_typed<N, DT, false, false, false>(a, s);
+    if (a.lam) return launch_step_mode<N, DT, kTrap>(a, s);
+    if (a.delta_softplus) return launch_step_mode<N, DT, kSoftplus>(a, s);
+    return launch_step_mode<N, DT, kEuler>(a, s);
 }
 
 template <int N>

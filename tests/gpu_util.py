@@ -94,3 +94,23 @@ def gpu_scan_dt(inp, dt_bias=True):
     torch.cuda.synchronize()
     assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
     return to_f64(y), to_f64(st_out)
+
+
+def gpu_scan_trap(inp, prev=True, want_state=True):
+    """Run ssm_scan_fwd_trap on stored inputs (inp["lam"], inp["x_prev"],
+    inp["B_prev"]); with prev=False no earlier token is passed. Returns (y64,
+    state64 or None)."""
+    import torch
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    batch, L, D = dev["x"].shape
+    N = dev["A"].shape[1]
+    st_out = torch.empty((batch, D, N), dtype=torch.float32, device="cuda") if want_state else None
+    ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(batch, L, D, N,
+                                                        0 if dev["x"].dtype == torch.float32 else 1))
+    y = ssm.ssm_scan_fwd_trap(dev["x"], dev["delta"], dev["lam"], dev["A"], dev["Bt"], dev["Ct"],
+                              Dskip=dev["Dskip"], z=dev["z"], x_prev=dev["x_prev"] if prev else None,
+                              B_prev=dev["B_prev"] if prev else None, state_in=dev["state_in"], state_out=st_out,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
+    return to_f64(y), (to_f64(st_out) if st_out is not None else None)

@@ -151,3 +151,44 @@ def test_step_dt_rejects(kw, code):
 def test_dt_entry_points_empty_ok_without_gpu():
     assert scan_dt(batch=0) == 0 and scan_dt(D=0) == 0
     assert step_dt(batch=0) == 0 and step_dt(D=0) == 0
+
+
+def scan_trap(**kw):
+    a = dict(batch=1, L=8, D=64, N=16, dtype=0, x=P, delta=P, lam=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             x_prev=None, B_prev=None, state_in=None, state_out=None, y=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_fwd_trap(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["delta"],
+                                       a["lam"], a["A"], a["Bt"], a["Ct"], a["Dskip"], a["z"], a["x_prev"],
+                                       a["B_prev"], a["state_in"], a["state_out"], a["y"], a["ws"], a["wsb"],
+                                       a["stream"])
+
+
+def step_trap(**kw):
+    a = dict(batch=1, D=64, N=16, dtype=0, x=P, delta=P, lam=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             x_prev=None, B_prev=None, state=P, y=P, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_step_trap(a["batch"], a["D"], a["N"], a["dtype"], a["x"], a["delta"], a["lam"], a["A"],
+                                   a["Bt"], a["Ct"], a["Dskip"], a["z"], a["x_prev"], a["B_prev"], a["state"],
+                                   a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=3), -4), (dict(lam=None), -1), (dict(delta=None), -1),
+    (dict(x_prev=P), -1), (dict(B_prev=P), -1), (dict(y=None), -1), (dict(lam=MIS), -5),
+    (dict(x_prev=MIS, B_prev=P), -5), (dict(x_prev=P, B_prev=MIS), -5), (dict(L=1 << 20, D=64), -6),
+])
+def test_scan_trap_rejects(kw, code):
+    assert scan_trap(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=5), -4), (dict(lam=None), -1), (dict(state=None), -1),
+    (dict(x_prev=P), -1), (dict(B_prev=P), -1), (dict(lam=MIS), -5), (dict(x_prev=MIS, B_prev=P), -5),
+])
+def test_step_trap_rejects(kw, code):
+    assert step_trap(**kw) == code
+
+
+def test_trap_entry_points_empty_ok_without_gpu():
+    assert scan_trap(batch=0) == 0 and scan_trap(D=0) == 0 and scan_trap(lam=None, L=0) == 0
+    assert step_trap(batch=0) == 0 and step_trap(D=0) == 0

@@ -20,6 +20,9 @@ Distributions follow the workloads described for the Mamba selective scan
 delta = softplus(0.5*eps + dt_bias) where dt_bias is the inverse softplus of a
 per-channel dt drawn log-uniform in [1e-3, 1e-1]; x, z, Bt, Ct ~ N(0, 1);
 Dskip = 1 or U(0.5, 1.5). delta is handed to the scan after the softplus.
+For the exponential-trapezoidal rule ("Recorrência trapezoidal"), the weight
+lam = sigmoid(u) with u ~ N(0, 1) per (b, t, d) (the sigmoid of a per-token
+projection), and the token before the first, x_prev and B_prev, ~ N(0, 1).
 
 Random streams: ``numpy.random.default_rng(SeedSequence(seed, spawn_key=key))``
 with one key per (tensor kind, batch row, token chunk of 65536, block of 64
@@ -42,7 +45,7 @@ import numpy as np
 __all__ = [
     "fill_scan_device", "fill_step_device", "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
     "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
-    "storage_to_f64", "scan_bytes", "step_bytes",
+    "storage_to_f64", "scan_bytes", "step_bytes", "trap_extra_bytes", "trap_step_extra_bytes",
 ]
 
 DTYPES = ("f32", "bf16")
@@ -50,7 +53,7 @@ _CHUNK = 65536  # tokens per random stream
 _CBLK = 64      # channels per random stream
 
 # stream keys (tensor kinds)
-_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE = range(8)
+_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE, _K_LAM, _K_XPREV, _K_BPREV = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -180,8 +183,13 @@ def _token_block(seed: int, kind: int, b: int, t0: int, t1: int, width: int,
     return out
 
 
+def _sigmoid(u: np.ndarray) -> np.ndarray:
+    return 0.5 * (1.0 + np.tanh(0.5 * u))
+
+
 def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
-                channels: Optional[np.ndarray] = None, raw_delta: bool = False) -> Dict[str, np.ndarray]:
+                channels: Optional[np.ndarray] = None, raw_delta: bool = False,
+                trap: bool = False) -> Dict[str, np.ndarray]:
     """Inputs of `cfg` for tokens [t0, t1) (default: all), in storage dtypes.
 
     `channels` selects a subset of the D channels for x, delta, z, A and Dskip
@@ -193,6 +201,11 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     With raw_delta, the step size is also returned before its activation:
     delta_raw = 0.5*eps in the storage dtype and dt_bias (D,) float32, the two
     terms whose softplus is delta.
+
+    With trap, also the exponential-trapezoidal inputs: lam (batch, T, D) and
+    the token before t0, x_prev (batch, D) and B_prev (batch, N): token t0 - 1
+    of x and Bt when t0 > 0, else draws of their own (the last token of an
+    earlier piece of the sequence).
     """
     if t1 is None:
         t1 = cfg.L
@@ -225,6 +238,19 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     if draw is not None:
         out["delta_raw"] = draw
         out["dt_bias"] = np.ascontiguousarray(dt_bias[sel].astype(np.float32))
+    if trap:
+        lam = np.empty_like(x)
+        xp = np.empty((cfg.batch, len(sel)), dtype=x.dtype)
+        bp = np.empty((cfg.batch, cfg.N), dtype=x.dtype)
+        for b in range(cfg.batch):
+            lam[b] = _store(_sigmoid(_token_block(cfg.seed, _K_LAM, b, t0, t1, cfg.D, sel)), act)
+            if t0 > 0:
+                xp[b] = _store(_token_block(cfg.seed, _K_X, b, t0 - 1, t0, cfg.D, sel)[0], act)
+                bp[b] = _store(_token_block(cfg.seed, _K_B, b, t0 - 1, t0, cfg.N)[0], act)
+            else:
+                xp[b] = _store(_token_block(cfg.seed, _K_XPREV, b, 0, 1, cfg.D, sel)[0], act)
+                bp[b] = _store(_token_block(cfg.seed, _K_BPREV, b, 0, 1, cfg.N)[0], act)
+        out["lam"], out["x_prev"], out["B_prev"] = lam, xp, bp
     return out
 
 
@@ -241,9 +267,11 @@ def step_inputs(cfg: StepConfig, channels: Optional[np.ndarray] = None) -> Dict[
 
 
 def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray] = None,
-                      raw_delta: bool = False) -> Dict[str, np.ndarray]:
+                      raw_delta: bool = False, trap: bool = False) -> Dict[str, np.ndarray]:
     """Inputs of decode step `step`: x, delta, z (batch, D) and Bt, Ct (batch, N);
-    with raw_delta also delta_raw = 0.5*eps (delta is its softplus plus dt_bias)."""
+    with raw_delta also delta_raw = 0.5*eps (delta is its softplus plus dt_bias);
+    with trap also lam (batch, D) (the previous token's x and Bt are those of
+    step - 1)."""
     _A, dt_bias, _D = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
     sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
     act = cfg.dtype
@@ -262,10 +290,12 @@ def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray]
     }
     if raw_delta:
         out["delta_raw"] = _store(0.5 * eps, act)
+    if trap:
+        out["lam"] = _store(_sigmoid(chan(_K_LAM)), act)
     return out
 
 
-def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345, raw_delta: bool = False):
+def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345, raw_delta: bool = False, trap: bool = False):
     """torch tensors of the full workload `cfg` on `device`, same distributions
     as scan_inputs but drawn with torch (values differ from the numpy streams).
     Returns x, delta, z (or None) and Bt, Ct; A, Dskip and state_in come from
@@ -292,10 +322,15 @@ def fill_scan_device(cfg: ScanConfig, device, seed: int = 12345, raw_delta: bool
            "Bt": normal((cfg.batch, cfg.L, cfg.N)).to(act), "Ct": normal((cfg.batch, cfg.L, cfg.N)).to(act)}
     if raw_delta:
         out["delta_raw"], out["dt_bias"] = out.pop("delta"), extra["dt_bias"]
+    if trap:  # lam = sigmoid(N(0,1)) and the token before the first
+        out["lam"] = torch.sigmoid(normal(shape)).to(act)
+        out["x_prev"] = normal((cfg.batch, cfg.D)).to(act)
+        out["B_prev"] = normal((cfg.batch, cfg.N)).to(act)
     return out
 
 
-def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321, raw_delta: bool = False):
+def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321, raw_delta: bool = False,
+                     trap: bool = False):
     """torch tensors for `steps` decode steps on `device` (same distributions as
     step_token_inputs, drawn with torch): x, delta, z of shape (steps, batch, D)
     and Bt, Ct of shape (steps, batch, N)."""
@@ -317,8 +352,11 @@ def fill_step_device(cfg: StepConfig, steps: int, device, seed: int = 54321, raw
                 "Bt": normal((steps, cfg.batch, cfg.N)).to(act), "Ct": normal((steps, cfg.batch, cfg.N)).to(act)}
     delta = torch.nn.functional.softplus(eps.add_(bias)).to(act)
     del eps
-    return {"delta": delta, "x": normal(shape).to(act), "z": normal(shape).to(act) if cfg.gate else None,
-            "Bt": normal((steps, cfg.batch, cfg.N)).to(act), "Ct": normal((steps, cfg.batch, cfg.N)).to(act)}
+    out = {"delta": delta, "x": normal(shape).to(act), "z": normal(shape).to(act) if cfg.gate else None,
+           "Bt": normal((steps, cfg.batch, cfg.N)).to(act), "Ct": normal((steps, cfg.batch, cfg.N)).to(act)}
+    if trap:
+        out["lam"] = torch.sigmoid(normal(shape)).to(act)
+    return out
 
 
 def _esize(dtype: str) -> int:
@@ -339,6 +377,19 @@ def scan_bytes(cfg: ScanConfig, state_out: bool = False) -> int:
     if state_out:
         n += cfg.batch * cfg.D * cfg.N * 4
     return n
+
+
+def trap_extra_bytes(cfg: ScanConfig) -> int:
+    """What the exponential-trapezoidal scan reads beyond scan_bytes: lam per
+    (b, t, d) and the earlier token, x_prev (batch, D) and B_prev (batch, N)."""
+    e = _esize(cfg.dtype)
+    return cfg.batch * cfg.L * cfg.D * e + cfg.batch * (cfg.D + cfg.N) * e
+
+
+def trap_step_extra_bytes(cfg: StepConfig) -> int:
+    """The same for one decode step: lam and x_prev (batch, D), B_prev (batch, N)."""
+    e = _esize(cfg.dtype)
+    return cfg.batch * (2 * cfg.D + cfg.N) * e
 
 
 def step_bytes(cfg: StepConfig) -> int:
