@@ -131,83 +131,139 @@ __device__ __forceinline__ uint32_t half_sel(int i) { return (i & 1) ? 0x03020c0
 // byte address plus immediate offsets, so a fully unrolled walk over a tile
 // needs no address arithmetic.
 //
-// Eight values of each of two arrays: value k at base + OA + k*STRIDE and at
-// base + OB + k*STRIDE.
-template <int STRIDE, int OA, int OB>
-__device__ __forceinline__ void lds_bf16_8x2(float (&va)[8], float (&vb)[8], uint32_t base) {
+// Pass-1 loads of one 8-token group (bfloat16, state size 16): x and delta of
+// the 8 tokens (b0 + OX / OD + k * ROWB) and the two Bt registers (b1 + OB +
+// {0, SB}), as one block with one wait.
+template <int ROWB, int OX, int OD, int SB, int OB>
+__device__ __forceinline__ void lds_bf16_p1(float (&xv)[8], float (&dv)[8], float (&bq)[2], uint32_t b0,
+                                            uint32_t b1) {
     asm volatile(
-        "ds_read_u16_d16_hi %0, %16 offset:%17\n\tds_read_u16_d16_hi %1, %16 offset:%18\n\t"
-        "ds_read_u16_d16_hi %2, %16 offset:%19\n\tds_read_u16_d16_hi %3, %16 offset:%20\n\t"
-        "ds_read_u16_d16_hi %4, %16 offset:%21\n\tds_read_u16_d16_hi %5, %16 offset:%22\n\t"
-        "ds_read_u16_d16_hi %6, %16 offset:%23\n\tds_read_u16_d16_hi %7, %16 offset:%24\n\t"
-        "ds_read_u16_d16_hi %8, %16 offset:%25\n\tds_read_u16_d16_hi %9, %16 offset:%26\n\t"
-        "ds_read_u16_d16_hi %10, %16 offset:%27\n\tds_read_u16_d16_hi %11, %16 offset:%28\n\t"
-        "ds_read_u16_d16_hi %12, %16 offset:%29\n\tds_read_u16_d16_hi %13, %16 offset:%30\n\t"
-        "ds_read_u16_d16_hi %14, %16 offset:%31\n\tds_read_u16_d16_hi %15, %16 offset:%32\n\t"
+        "ds_read_u16_d16_hi %0, %18 offset:%20\n\tds_read_u16_d16_hi %1, %18 offset:%21\n\t"
+        "ds_read_u16_d16_hi %2, %18 offset:%22\n\tds_read_u16_d16_hi %3, %18 offset:%23\n\t"
+        "ds_read_u16_d16_hi %4, %18 offset:%24\n\tds_read_u16_d16_hi %5, %18 offset:%25\n\t"
+        "ds_read_u16_d16_hi %6, %18 offset:%26\n\tds_read_u16_d16_hi %7, %18 offset:%27\n\t"
+        "ds_read_u16_d16_hi %8, %18 offset:%28\n\tds_read_u16_d16_hi %9, %18 offset:%29\n\t"
+        "ds_read_u16_d16_hi %10, %18 offset:%30\n\tds_read_u16_d16_hi %11, %18 offset:%31\n\t"
+        "ds_read_u16_d16_hi %12, %18 offset:%32\n\tds_read_u16_d16_hi %13, %18 offset:%33\n\t"
+        "ds_read_u16_d16_hi %14, %18 offset:%34\n\tds_read_u16_d16_hi %15, %18 offset:%35\n\t"
+        "ds_read_u16_d16_hi %16, %19 offset:%36\n\tds_read_u16_d16_hi %17, %19 offset:%37\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]),
-          "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]), "+v"(vb[4]), "+v"(vb[5]), "+v"(vb[6]), "+v"(vb[7])
-        : "v"(base), "i"(OA), "i"(OA + STRIDE), "i"(OA + 2 * STRIDE), "i"(OA + 3 * STRIDE), "i"(OA + 4 * STRIDE),
-          "i"(OA + 5 * STRIDE), "i"(OA + 6 * STRIDE), "i"(OA + 7 * STRIDE), "i"(OB), "i"(OB + STRIDE),
-          "i"(OB + 2 * STRIDE), "i"(OB + 3 * STRIDE), "i"(OB + 4 * STRIDE), "i"(OB + 5 * STRIDE),
-          "i"(OB + 6 * STRIDE), "i"(OB + 7 * STRIDE)
+        :"+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(dv[0]),
+         "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]), "+v"(dv[4]), "+v"(dv[5]), "+v"(dv[6]), "+v"(dv[7]), "+v"(bq[0]), "+v"(bq[1])
+        :"v"(b0), "v"(b1), "i"(OX), "i"(OX + 1 * ROWB), "i"(OX + 2 * ROWB), "i"(OX + 3 * ROWB), "i"(OX + 4 * ROWB),
+         "i"(OX + 5 * ROWB), "i"(OX + 6 * ROWB), "i"(OX + 7 * ROWB), "i"(OD), "i"(OD + 1 * ROWB), "i"(OD + 2 * ROWB),
+         "i"(OD + 3 * ROWB), "i"(OD + 4 * ROWB), "i"(OD + 5 * ROWB), "i"(OD + 6 * ROWB), "i"(OD + 7 * ROWB), "i"(OB),
+         "i"(OB + 1 * SB)
         : "memory");
 }
-// Eight values of each of three arrays, at base + OA + k*STRIDE, base + OB +
-// k*STRIDE and base + OC + k*STRIDE, and the ninth value of the second and
-// third arrays.
-template <int STRIDE, int OA, int OB, int OC>
-__device__ __forceinline__ void lds_bf16_8x3n(float (&va)[8], float (&vb)[8], float (&vc)[8], float &nb, float &nc,
-                                              uint32_t base) {
+
+// Pass-2 loads of one 8-token group: as lds_bf16_p1, plus the Ct registers
+// (b1 + OC + {0, SB}) and x and z of the two tokens this lane finishes
+// (b2 + OXO / OZO + {0, SO}).
+template <int ROWB, int OX, int OD, int SB, int OB, int OC, int SO, int OXO, int OZO>
+__device__ __forceinline__ void lds_bf16_p2(float (&xv)[8], float (&dv)[8], float (&bq)[2], float (&cq)[2],
+                                            float (&xo)[2], float (&zo)[2], uint32_t b0, uint32_t b1, uint32_t b2) {
     asm volatile(
-        "ds_read_u16_d16_hi %0, %26 offset:%27\n\tds_read_u16_d16_hi %1, %26 offset:%28\n\tds_read_u16_d16_hi %2, %26 offset:%29\n\tds_read_u16_d16_hi %3, %26 offset:%30\n\tds_read_u16_d16_hi %4, %26 offset:%31\n\tds_read_u16_d16_hi %5, %26 offset:%32\n\tds_read_u16_d16_hi %6, %26 offset:%33\n\tds_read_u16_d16_hi %7, %26 offset:%34\n\tds_read_u16_d16_hi %8, %26 offset:%35\n\tds_read_u16_d16_hi %9, %26 offset:%36\n\tds_read_u16_d16_hi %10, %26 offset:%37\n\tds_read_u16_d16_hi %11, %26 offset:%38\n\tds_read_u16_d16_hi %12, %26 offset:%39\n\tds_read_u16_d16_hi %13, %26 offset:%40\n\tds_read_u16_d16_hi %14, %26 offset:%41\n\tds_read_u16_d16_hi %15, %26 offset:%42\n\tds_read_u16_d16_hi %16, %26 offset:%43\n\tds_read_u16_d16_hi %17, %26 offset:%44\n\tds_read_u16_d16_hi %18, %26 offset:%45\n\tds_read_u16_d16_hi %19, %26 offset:%46\n\tds_read_u16_d16_hi %20, %26 offset:%47\n\tds_read_u16_d16_hi %21, %26 offset:%48\n\tds_read_u16_d16_hi %22, %26 offset:%49\n\tds_read_u16_d16_hi %23, %26 offset:%50\n\tds_read_u16_d16_hi %24, %26 offset:%51\n\tds_read_u16_d16_hi %25, %26 offset:%52\n\t"
+        "ds_read_u16_d16_hi %0, %24 offset:%27\n\tds_read_u16_d16_hi %1, %24 offset:%28\n\t"
+        "ds_read_u16_d16_hi %2, %24 offset:%29\n\tds_read_u16_d16_hi %3, %24 offset:%30\n\t"
+        "ds_read_u16_d16_hi %4, %24 offset:%31\n\tds_read_u16_d16_hi %5, %24 offset:%32\n\t"
+        "ds_read_u16_d16_hi %6, %24 offset:%33\n\tds_read_u16_d16_hi %7, %24 offset:%34\n\t"
+        "ds_read_u16_d16_hi %8, %24 offset:%35\n\tds_read_u16_d16_hi %9, %24 offset:%36\n\t"
+        "ds_read_u16_d16_hi %10, %24 offset:%37\n\tds_read_u16_d16_hi %11, %24 offset:%38\n\t"
+        "ds_read_u16_d16_hi %12, %24 offset:%39\n\tds_read_u16_d16_hi %13, %24 offset:%40\n\t"
+        "ds_read_u16_d16_hi %14, %24 offset:%41\n\tds_read_u16_d16_hi %15, %24 offset:%42\n\t"
+        "ds_read_u16_d16_hi %16, %25 offset:%43\n\tds_read_u16_d16_hi %17, %25 offset:%44\n\t"
+        "ds_read_u16_d16_hi %18, %25 offset:%45\n\tds_read_u16_d16_hi %19, %25 offset:%46\n\t"
+        "ds_read_u16_d16_hi %20, %26 offset:%47\n\tds_read_u16_d16_hi %21, %26 offset:%48\n\t"
+        "ds_read_u16_d16_hi %22, %26 offset:%49\n\tds_read_u16_d16_hi %23, %26 offset:%50\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]),
-          "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]), "+v"(vb[4]), "+v"(vb[5]), "+v"(vb[6]), "+v"(vb[7]),
-          "+v"(vc[0]), "+v"(vc[1]), "+v"(vc[2]), "+v"(vc[3]), "+v"(vc[4]), "+v"(vc[5]), "+v"(vc[6]), "+v"(vc[7]),
-          "+v"(nb), "+v"(nc)
-        : "v"(base), "i"(OA), "i"(OA + STRIDE), "i"(OA + 2 * STRIDE), "i"(OA + 3 * STRIDE), "i"(OA + 4 * STRIDE),
-          "i"(OA + 5 * STRIDE), "i"(OA + 6 * STRIDE), "i"(OA + 7 * STRIDE), "i"(OB), "i"(OB + STRIDE),
-          "i"(OB + 2 * STRIDE), "i"(OB + 3 * STRIDE), "i"(OB + 4 * STRIDE), "i"(OB + 5 * STRIDE),
-          "i"(OB + 6 * STRIDE), "i"(OB + 7 * STRIDE), "i"(OC), "i"(OC + STRIDE), "i"(OC + 2 * STRIDE),
-          "i"(OC + 3 * STRIDE), "i"(OC + 4 * STRIDE), "i"(OC + 5 * STRIDE), "i"(OC + 6 * STRIDE),
-          "i"(OC + 7 * STRIDE), "i"(OB + 8 * STRIDE), "i"(OC + 8 * STRIDE)
+        :"+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(dv[0]),
+         "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]), "+v"(dv[4]), "+v"(dv[5]), "+v"(dv[6]), "+v"(dv[7]), "+v"(bq[0]), "+v"(bq[1]),
+         "+v"(cq[0]), "+v"(cq[1]), "+v"(xo[0]), "+v"(xo[1]), "+v"(zo[0]), "+v"(zo[1])
+        :"v"(b0), "v"(b1), "v"(b2), "i"(OX), "i"(OX + 1 * ROWB), "i"(OX + 2 * ROWB), "i"(OX + 3 * ROWB), "i"(OX + 4 * ROWB),
+         "i"(OX + 5 * ROWB), "i"(OX + 6 * ROWB), "i"(OX + 7 * ROWB), "i"(OD), "i"(OD + 1 * ROWB), "i"(OD + 2 * ROWB),
+         "i"(OD + 3 * ROWB), "i"(OD + 4 * ROWB), "i"(OD + 5 * ROWB), "i"(OD + 6 * ROWB), "i"(OD + 7 * ROWB), "i"(OB),
+         "i"(OB + 1 * SB), "i"(OC), "i"(OC + 1 * SB), "i"(OXO), "i"(OXO + 1 * SO), "i"(OZO), "i"(OZO + 1 * SO)
         : "memory");
 }
-// Two values of each of two arrays: a at base + OA + {0, SA}, b at base + OB + {0, SA}.
-template <int SA, int OA, int OB>
-__device__ __forceinline__ void lds_bf16_2x2(float (&va)[2], float (&vb)[2], uint32_t base) {
+
+// Trapezoidal rule, pass 1: as lds_bf16_p1, plus lam of the 8 tokens (b0 +
+// OL + k * ROWB) and delta and lam of the token after them (b0 + OD / OL + 8 *
+// ROWB).
+template <int ROWB, int OX, int OD, int OL, int SB, int OB>
+__device__ __forceinline__ void lds_bf16_t1(float (&xv)[8], float (&dv)[8], float (&lv)[8], float &dn, float &ln,
+                                            float (&bq)[2], uint32_t b0, uint32_t b1) {
     asm volatile(
-        "ds_read_u16_d16_hi %0, %4 offset:%5\n\tds_read_u16_d16_hi %1, %4 offset:%6\n\t"
-        "ds_read_u16_d16_hi %2, %4 offset:%7\n\tds_read_u16_d16_hi %3, %4 offset:%8\n\t"
+        "ds_read_u16_d16_hi %0, %28 offset:%30\n\tds_read_u16_d16_hi %1, %28 offset:%31\n\t"
+        "ds_read_u16_d16_hi %2, %28 offset:%32\n\tds_read_u16_d16_hi %3, %28 offset:%33\n\t"
+        "ds_read_u16_d16_hi %4, %28 offset:%34\n\tds_read_u16_d16_hi %5, %28 offset:%35\n\t"
+        "ds_read_u16_d16_hi %6, %28 offset:%36\n\tds_read_u16_d16_hi %7, %28 offset:%37\n\t"
+        "ds_read_u16_d16_hi %8, %28 offset:%38\n\tds_read_u16_d16_hi %9, %28 offset:%39\n\t"
+        "ds_read_u16_d16_hi %10, %28 offset:%40\n\tds_read_u16_d16_hi %11, %28 offset:%41\n\t"
+        "ds_read_u16_d16_hi %12, %28 offset:%42\n\tds_read_u16_d16_hi %13, %28 offset:%43\n\t"
+        "ds_read_u16_d16_hi %14, %28 offset:%44\n\tds_read_u16_d16_hi %15, %28 offset:%45\n\t"
+        "ds_read_u16_d16_hi %16, %28 offset:%46\n\tds_read_u16_d16_hi %17, %28 offset:%47\n\t"
+        "ds_read_u16_d16_hi %18, %28 offset:%48\n\tds_read_u16_d16_hi %19, %28 offset:%49\n\t"
+        "ds_read_u16_d16_hi %20, %28 offset:%50\n\tds_read_u16_d16_hi %21, %28 offset:%51\n\t"
+        "ds_read_u16_d16_hi %22, %28 offset:%52\n\tds_read_u16_d16_hi %23, %28 offset:%53\n\t"
+        "ds_read_u16_d16_hi %24, %28 offset:%54\n\tds_read_u16_d16_hi %25, %28 offset:%55\n\t"
+        "ds_read_u16_d16_hi %26, %29 offset:%56\n\tds_read_u16_d16_hi %27, %29 offset:%57\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "+v"(va[0]), "+v"(va[1]), "+v"(vb[0]), "+v"(vb[1])
-        : "v"(base), "i"(OA), "i"(OA + SA), "i"(OB), "i"(OB + SA)
+        :"+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(dv[0]),
+         "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]), "+v"(dv[4]), "+v"(dv[5]), "+v"(dv[6]), "+v"(dv[7]), "+v"(lv[0]), "+v"(lv[1]),
+         "+v"(lv[2]), "+v"(lv[3]), "+v"(lv[4]), "+v"(lv[5]), "+v"(lv[6]), "+v"(lv[7]), "+v"(dn), "+v"(ln), "+v"(bq[0]),
+         "+v"(bq[1])
+        :"v"(b0), "v"(b1), "i"(OX), "i"(OX + 1 * ROWB), "i"(OX + 2 * ROWB), "i"(OX + 3 * ROWB), "i"(OX + 4 * ROWB),
+         "i"(OX + 5 * ROWB), "i"(OX + 6 * ROWB), "i"(OX + 7 * ROWB), "i"(OD), "i"(OD + 1 * ROWB), "i"(OD + 2 * ROWB),
+         "i"(OD + 3 * ROWB), "i"(OD + 4 * ROWB), "i"(OD + 5 * ROWB), "i"(OD + 6 * ROWB), "i"(OD + 7 * ROWB), "i"(OL),
+         "i"(OL + 1 * ROWB), "i"(OL + 2 * ROWB), "i"(OL + 3 * ROWB), "i"(OL + 4 * ROWB), "i"(OL + 5 * ROWB),
+         "i"(OL + 6 * ROWB), "i"(OL + 7 * ROWB), "i"(OD + 8 * ROWB), "i"(OL + 8 * ROWB), "i"(OB), "i"(OB + 1 * SB)
         : "memory");
 }
-// Two values of each of four arrays: a at ab + OA + {0, SA}, b at ab + OB +
-// {0, SA}, c at cd + OC + {0, SC}, d at cd + OD + {0, SC}.
-template <int SA, int SC, int OA, int OB, int OC, int OD>
-__device__ __forceinline__ void lds_bf16_2x4(float (&va)[2], float (&vb)[2], float (&vc)[2], float (&vd)[2],
-                                             uint32_t ab, uint32_t cd) {
+
+// Trapezoidal rule, pass 2: as lds_bf16_t1, plus the Ct registers, x and z of
+// the two finished tokens and delta and lam of the token after each (b2 +
+// OXO / OZO / ODO / OLO + {0, SO}), and the float C . B of each finished token
+// (b3 + OCB + {0, SCB}).
+template <int ROWB, int OX, int OD, int OL, int SB, int OB, int OC, int SO, int OXO, int OZO, int ODO, int OLO, int SCB, int OCB>
+__device__ __forceinline__ void lds_bf16_t2(float (&xv)[8], float (&dv)[8], float (&lv)[8], float &dn, float &ln,
+                                            float (&bq)[2], float (&cq)[2], float (&xo)[2], float (&zo)[2],
+                                            float (&dno)[2], float (&lno)[2], float (&cbo)[2], uint32_t b0,
+                                            uint32_t b1, uint32_t b2, uint32_t b3) {
     asm volatile(
-        "ds_read_u16_d16_hi %0, %8 offset:%10\n\tds_read_u16_d16_hi %1, %8 offset:%11\n\t"
-        "ds_read_u16_d16_hi %2, %8 offset:%12\n\tds_read_u16_d16_hi %3, %8 offset:%13\n\t"
-        "ds_read_u16_d16_hi %4, %9 offset:%14\n\tds_read_u16_d16_hi %5, %9 offset:%15\n\t"
-        "ds_read_u16_d16_hi %6, %9 offset:%16\n\tds_read_u16_d16_hi %7, %9 offset:%17\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "+v"(va[0]), "+v"(va[1]), "+v"(vb[0]), "+v"(vb[1]), "+v"(vc[0]), "+v"(vc[1]), "+v"(vd[0]), "+v"(vd[1])
-        : "v"(ab), "v"(cd), "i"(OA), "i"(OA + SA), "i"(OB), "i"(OB + SA), "i"(OC), "i"(OC + SC), "i"(OD),
-          "i"(OD + SC)
+        "ds_read_u16_d16_hi %0, %40 offset:%44\n\tds_read_u16_d16_hi %1, %40 offset:%45\n\t"
+        "ds_read_u16_d16_hi %2, %40 offset:%46\n\tds_read_u16_d16_hi %3, %40 offset:%47\n\t"
+        "ds_read_u16_d16_hi %4, %40 offset:%48\n\tds_read_u16_d16_hi %5, %40 offset:%49\n\t"
+        "ds_read_u16_d16_hi %6, %40 offset:%50\n\tds_read_u16_d16_hi %7, %40 offset:%51\n\t"
+        "ds_read_u16_d16_hi %8, %40 offset:%52\n\tds_read_u16_d16_hi %9, %40 offset:%53\n\t"
+        "ds_read_u16_d16_hi %10, %40 offset:%54\n\tds_read_u16_d16_hi %11, %40 offset:%55\n\t"
+        "ds_read_u16_d16_hi %12, %40 offset:%56\n\tds_read_u16_d16_hi %13, %40 offset:%57\n\t"
+        "ds_read_u16_d16_hi %14, %40 offset:%58\n\tds_read_u16_d16_hi %15, %40 offset:%59\n\t"
+        "ds_read_u16_d16_hi %16, %40 offset:%60\n\tds_read_u16_d16_hi %17, %40 offset:%61\n\t"
+        "ds_read_u16_d16_hi %18, %40 offset:%62\n\tds_read_u16_d16_hi %19, %40 offset:%63\n\t"
+        "ds_read_u16_d16_hi %20, %40 offset:%64\n\tds_read_u16_d16_hi %21, %40 offset:%65\n\t"
+        "ds_read_u16_d16_hi %22, %40 offset:%66\n\tds_read_u16_d16_hi %23, %40 offset:%67\n\t"
+        "ds_read_u16_d16_hi %24, %40 offset:%68\n\tds_read_u16_d16_hi %25, %40 offset:%69\n\t"
+        "ds_read_u16_d16_hi %26, %41 offset:%70\n\tds_read_u16_d16_hi %27, %41 offset:%71\n\t"
+        "ds_read_u16_d16_hi %28, %41 offset:%72\n\tds_read_u16_d16_hi %29, %41 offset:%73\n\t"
+        "ds_read_u16_d16_hi %30, %42 offset:%74\n\tds_read_u16_d16_hi %31, %42 offset:%75\n\t"
+        "ds_read_u16_d16_hi %32, %42 offset:%76\n\tds_read_u16_d16_hi %33, %42 offset:%77\n\t"
+        "ds_read_u16_d16_hi %34, %42 offset:%78\n\tds_read_u16_d16_hi %35, %42 offset:%79\n\t"
+        "ds_read_u16_d16_hi %36, %42 offset:%80\n\tds_read_u16_d16_hi %37, %42 offset:%81\n\t"
+        "ds_read_b32 %38, %43 offset:%82\n\tds_read_b32 %39, %43 offset:%83\n\ts_waitcnt lgkmcnt(0)"
+        :"+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]), "+v"(dv[0]),
+         "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]), "+v"(dv[4]), "+v"(dv[5]), "+v"(dv[6]), "+v"(dv[7]), "+v"(lv[0]), "+v"(lv[1]),
+         "+v"(lv[2]), "+v"(lv[3]), "+v"(lv[4]), "+v"(lv[5]), "+v"(lv[6]), "+v"(lv[7]), "+v"(dn), "+v"(ln), "+v"(bq[0]),
+         "+v"(bq[1]), "+v"(cq[0]), "+v"(cq[1]), "+v"(xo[0]), "+v"(xo[1]), "+v"(zo[0]), "+v"(zo[1]), "+v"(dno[0]),
+         "+v"(dno[1]), "+v"(lno[0]), "+v"(lno[1]), "=&v"(cbo[0]), "=&v"(cbo[1])
+        :"v"(b0), "v"(b1), "v"(b2), "v"(b3), "i"(OX), "i"(OX + 1 * ROWB), "i"(OX + 2 * ROWB), "i"(OX + 3 * ROWB),
+         "i"(OX + 4 * ROWB), "i"(OX + 5 * ROWB), "i"(OX + 6 * ROWB), "i"(OX + 7 * ROWB), "i"(OD), "i"(OD + 1 * ROWB),
+         "i"(OD + 2 * ROWB), "i"(OD + 3 * ROWB), "i"(OD + 4 * ROWB), "i"(OD + 5 * ROWB), "i"(OD + 6 * ROWB),
+         "i"(OD + 7 * ROWB), "i"(OL), "i"(OL + 1 * ROWB), "i"(OL + 2 * ROWB), "i"(OL + 3 * ROWB), "i"(OL + 4 * ROWB),
+         "i"(OL + 5 * ROWB), "i"(OL + 6 * ROWB), "i"(OL + 7 * ROWB), "i"(OD + 8 * ROWB), "i"(OL + 8 * ROWB), "i"(OB),
+         "i"(OB + 1 * SB), "i"(OC), "i"(OC + 1 * SB), "i"(OXO), "i"(OXO + 1 * SO), "i"(OZO), "i"(OZO + 1 * SO), "i"(ODO),
+         "i"(ODO + 1 * SO), "i"(OLO), "i"(OLO + 1 * SO), "i"(OCB), "i"(OCB + 1 * SCB)
         : "memory");
-}
-// Two values of one array, at a + OA + {0, SA}.
-template <int SA, int OA>
-__device__ __forceinline__ void lds_bf16_2(float (&va)[2], uint32_t a) {
-    asm volatile("ds_read_u16_d16_hi %0, %2 offset:%3\n\tds_read_u16_d16_hi %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-                 : "+v"(va[0]), "+v"(va[1])
-                 : "v"(a), "i"(OA), "i"(OA + SA)
-                 : "memory");
 }
 
 // An empty volatile statement that reads and rewrites `st` and `x`: every
@@ -508,7 +564,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             float xv[GROUP], dv[GROUP], Bq[BREGS], Cq[BREGS], xo[G::OWN], zo[G::OWN];
             // TRAP: lam of the group's tokens, delta and lam of the token after
             // the group, and of the token after each finished token
-            float lv[GROUP], dn = 0.0f, ln = 0.0f, dno[G::OWN], lno[G::OWN];
+            float lv[GROUP], dn = 0.0f, ln = 0.0f, dno[G::OWN], lno[G::OWN], cbo[G::OWN];
 #pragma unroll
             for (int t = 0; t < GROUP; ++t) xv[t] = dv[t] = lv[t] = 0.0f;
 #pragma unroll
@@ -562,6 +618,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                 const uint32_t a_ch = lds_addr(&tb) + cl * G::ESZ;
                 const uint32_t a_bc = lds_addr(&tb) + OFF_B + ((k16 / NL) * N + nstate0 + (k16 % NL)) * G::ESZ;
                 const uint32_t a_own = a_ch + g * ROWB;
+                const uint32_t a_cb = lds_addr(&sh.cb[0]) + g * 4;  // TRAP: C . B of the lane's first finished token
                 static_for<0, TT / GROUP>([&](auto gc) {
                     constexpr int tg = decltype(gc)::value * GROUP;
                     // Keep the groups in order: the previous group's state
@@ -573,21 +630,21 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                     if constexpr (SP) order_point<NL>(st, dsum);
                     if constexpr (kHiLoads) {
                         // bfloat16: loads into the high halves of the registers
-                        // that held the previous group's values
-                        if constexpr (TRAP)
-                            lds_bf16_8x3n<ROWB, tg * ROWB, OFF_DL + tg * ROWB, OFF_LAM + tg * ROWB>(xv, dv, lv, dn, ln,
-                                                                                                  a_ch);
+                        // that held the previous group's values, one wait per group
+                        constexpr int OX = tg * ROWB, OD = OFF_DL + tg * ROWB, OL = OFF_LAM + tg * ROWB;
+                        constexpr int SB = TPV * BCB, OB = tg * BCB, OC = OFF_C - OFF_B + tg * BCB;
+                        constexpr int SO = NGR * ROWB, OXO = tg * ROWB, OZO = OFF_Z + tg * ROWB;
+                        if constexpr (TRAP && PASS == 2)
+                            lds_bf16_t2<ROWB, OX, OD, OL, SB, OB, OC, SO, OXO, OZO, OFF_DL + (tg + 1) * ROWB,
+                                        OFF_LAM + (tg + 1) * ROWB, NGR * 4, tg * 4>(
+                                xv, dv, lv, dn, ln, Bq, Cq, xo, zo, dno, lno, cbo, a_ch, a_bc, a_own, a_cb);
+                        else if constexpr (TRAP)
+                            lds_bf16_t1<ROWB, OX, OD, OL, SB, OB>(xv, dv, lv, dn, ln, Bq, a_ch, a_bc);
+                        else if constexpr (PASS == 2)
+                            lds_bf16_p2<ROWB, OX, OD, SB, OB, OC, SO, OXO, OZO>(xv, dv, Bq, Cq, xo, zo, a_ch, a_bc,
+                                                                                a_own);
                         else
-                            lds_bf16_8x2<ROWB, tg * ROWB, OFF_DL + tg * ROWB>(xv, dv, a_ch);
-                        if constexpr (PASS == 2) {
-                            lds_bf16_2x4<TPV * BCB, NGR * ROWB, tg * BCB, OFF_C - OFF_B + tg * BCB, tg * ROWB,
-                                         OFF_Z + tg * ROWB>(Bq, Cq, xo, zo, a_bc, a_own);
-                            if constexpr (TRAP)
-                                lds_bf16_2x2<NGR * ROWB, OFF_DL + (tg + 1) * ROWB, OFF_LAM + (tg + 1) * ROWB>(dno, lno,
-                                                                                                          a_own);
-                        } else {
-                            lds_bf16_2<TPV * BCB, tg * BCB>(Bq, a_bc);
-                        }
+                            lds_bf16_p1<ROWB, OX, OD, SB, OB>(xv, dv, Bq, a_ch, a_bc);
                     } else {
 #pragma unroll
                         for (int t = 0; t < GROUP; ++t) {
@@ -615,6 +672,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                                 if constexpr (TRAP) {
                                     dno[q] = lds_act(&tb.dl[tw + 1][0], cl, sel_ch);
                                     lno[q] = lds_act(&tb.lam[tw + 1][0], cl, sel_ch);
+                                    cbo[q] = sh.cb[tw];
                                 }
                             }
                         }
@@ -693,7 +751,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                             if constexpr (TRAP) {
                                 // h = k - mu_{t+1} v_t: subtract mu_{t+1} x_t (C_t . B_t)
                                 const float mu = __builtin_fmaf(-lno[q], dno[q], dno[q]);
-                                yv = __builtin_fmaf(-mu * xo[q], sh.cb[tw], yv);
+                                yv = __builtin_fmaf(-mu * xo[q], cbo[q], yv);
                             }
                             if (SKIP) yv = __builtin_fmaf(dskip, xo[q], yv);
                             if (GATE) yv *= silu(zo[q]);
