@@ -546,13 +546,28 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             constexpr int PASS = decltype(pass_c)::value;
             if (w > 0) load_tile<N, DT, GATE, PASS, TRAP>(sh.buf[0], a, b, ch0, t0, w, l, act_off);
         };
-        // TRAP, pass 2: C_t . B_t of every token of a landed tile, into sh.cb
+        // TRAP, pass 2: C_t . B_t of every token of a landed tile, into sh.cb.
+        // PARTS consecutive threads share a token, SPP states each, and sum
+        // their parts with lane exchanges.
         auto tile_cb = [&](const TBT &tb) {
-            if (threadIdx.x < TT) {
+            constexpr int PARTS = 64 * kWaves / TT;
+            if constexpr (N % PARTS == 0) {
+                constexpr int SPP = N / PARTS;
+                const int t = threadIdx.x / PARTS, n0 = (threadIdx.x % PARTS) * SPP;
+                const T *Br = &tb.B[t * N], *Cr = &tb.C[t * N];
+                float cbv = 0.0f;
+#pragma unroll
+                for (int n = n0; n < n0 + SPP; ++n)
+                    cbv = __builtin_fmaf(lds_act(Cr, n, half_sel(n)), lds_act(Br, n, half_sel(n)), cbv);
+#pragma unroll
+                for (int m = 1; m < PARTS; m <<= 1) cbv += __shfl_xor(cbv, m);
+                if (n0 == 0) sh.cb[t] = cbv;
+            } else if (threadIdx.x < TT) {
                 const T *Br = &tb.B[threadIdx.x * N], *Cr = &tb.C[threadIdx.x * N];
                 float cbv = 0.0f;
 #pragma unroll
-                for (int n = 0; n < N; ++n) cbv = __builtin_fmaf(lds_act(Cr, n, half_sel(n)), lds_act(Br, n, half_sel(n)), cbv);
+                for (int n = 0; n < N; ++n)
+                    cbv = __builtin_fmaf(lds_act(Cr, n, half_sel(n)), lds_act(Br, n, half_sel(n)), cbv);
                 sh.cb[threadIdx.x] = cbv;
             }
         };
