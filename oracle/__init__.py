@@ -63,6 +63,8 @@ class Oracle:
         self.lib.oracle_scan_trap.restype = ci
         self.lib.oracle_step_trap.argtypes = [i64, i64, i64] + [_DP] * 12 + [ci]
         self.lib.oracle_step_trap.restype = ci
+        self.lib.oracle_ssd.argtypes = [i64] * 6 + [_DP] * 9 + [ci]
+        self.lib.oracle_ssd.restype = ci
 
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.oracle_threads(nthreads))
@@ -156,6 +158,26 @@ class Oracle:
             raise ValueError("oracle_step_trap rejected sizes")
         return y
 
+    def ssd64(self, x, delta, A, Bt, Ct, Dskip=None, state_in=None, want_state: bool = True, nthreads: int = 0):
+        """Mamba-2 SSD layer on float64 arrays: x (batch, L, H, P), delta (batch, L, H),
+        A (H,), Bt/Ct (batch, L, G, N), Dskip (H,), state_in (batch, H, P, N).
+        Returns (y, state_out or None)."""
+        x = _c64(x)
+        batch, L, H, P = x.shape
+        Bt, Ct = _c64(Bt), _c64(Ct)
+        G, N = Bt.shape[2], Bt.shape[3]
+        delta, A = _c64(delta), _c64(A).reshape(H)
+        assert delta.shape == (batch, L, H) and Bt.shape == (batch, L, G, N) and Ct.shape == Bt.shape
+        Dskip = None if Dskip is None else _c64(Dskip).reshape(H)
+        state_in = None if state_in is None else _c64(state_in).reshape(batch, H, P, N)
+        y = np.empty((batch, L, H, P), dtype=np.float64)
+        st = np.empty((batch, H, P, N), dtype=np.float64) if want_state else None
+        rc = self.lib.oracle_ssd(batch, L, H, P, G, N, _p(x), _p(delta), _p(A), _p(Bt), _p(Ct), _p(Dskip),
+                                 _p(state_in), _p(st), _p(y), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_ssd rejected sizes")
+        return y, st
+
     def softplus_bias64(self, raw, bias=None):
         """softplus(raw + bias[d]) over the last axis (D) of a float64 array."""
         raw = _c64(raw)
@@ -221,6 +243,14 @@ class Oracle:
                                 up(tok["Ct"]), None if Dskip is None else upcast(Dskip, "f32"),
                                 up(tok.get("z")), up(tok.get("x_prev")), up(tok.get("B_prev")), state64,
                                 nthreads=nthreads)
+
+    def ssd(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
+        """SSD layer on stored inputs (x, delta, Bt, Ct in the stored dtype; A,
+        Dskip, state_in float32)."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        return self.ssd64(up(inp["x"]), up(inp["delta"]), f32(inp["A"]), up(inp["Bt"]), up(inp["Ct"]),
+                          f32(inp.get("Dskip")), f32(inp.get("state_in")), nthreads=nthreads)
 
     def step(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
              nthreads: int = 0):

@@ -49,11 +49,19 @@
  * exponential-trapezoidal rule and its coefficients alpha, beta, gamma);
  * lam = 1 gives the exponential-Euler scan above back.
  *
+ * oracle_ssd is the Mamba-2 state space dual (SSD) layer: the same recurrence
+ * with the transition restricted to a scalar per head times the identity, so
+ * each head keeps a (P, N) state updated by an outer product ("Mamba-2 e
+ * State Space Duality (SSD)"; "Notas sobre Mamba", section "A forma dual:
+ * atenção mascarada", where the scalar transition a_t I and the recurrent
+ * form of the dual are given).
+ *
  * Everything is float64 and uses libm exp()/log1p(); no fast-math, no
  * reordering of the token loop. OpenMP only splits independent (b, d) rows
  * across threads.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #ifdef _OPENMP
@@ -277,6 +285,62 @@ int oracle_step_trap(int64_t batch, int64_t D, int64_t N,
             acc *= g / (1.0 + exp(-g));
         }
         y[r] = acc;
+    }
+    return 0;
+}
+
+/*
+ * Mamba-2 SSD layer: per (batch row b, head h), with the scalar transition
+ * a_t = exp(delta[b,t,h] * A[h]) and group g = h / (H / G) of Bt and Ct:
+ *
+ *   S[p][n] = state_in[b,h,p,n]  (or 0)
+ *   for t = 0 .. L-1:
+ *     S[p][n] = a_t * S[p][n] + delta[b,t,h] * x[b,t,h,p] * Bt[b,t,g,n]
+ *     y[b,t,h,p] = sum_n Ct[b,t,g,n] * S[p][n]  (+ Dskip[h] * x[b,t,h,p])
+ *   state_out[b,h,:,:] = S
+ *
+ *   x, y           : (batch, L, H, P)
+ *   delta          : (batch, L, H)      step after its activation
+ *   A              : (H)                one scalar per head
+ *   Bt, Ct         : (batch, L, G, N)   G groups, each shared by H / G heads
+ *   Dskip          : (H) or NULL
+ *   state_in/_out  : (batch, H, P, N) or NULL
+ * The input term is delta * B_t * x_t, the first-order rule of the S6 scan
+ * this layer restricts. Returns 0, or -1 on a bad size.
+ */
+int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+               const double *x, const double *delta, const double *A, const double *Bt, const double *Ct,
+               const double *Dskip, const double *state_in, double *state_out, double *y, int nthreads)
+{
+    if (batch < 0 || L < 0 || H < 1 || P < 1 || G < 1 || N < 1 || H % G != 0 || P * N > (1 << 20)) return -1;
+    int64_t rows = batch * H;
+    int nt = oracle_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / H, h = r % H, g = h / (H / G);
+        double *S = (double *)malloc((size_t)(P * N) * sizeof(double));
+        for (int64_t i = 0; i < P * N; ++i) S[i] = state_in ? state_in[r * P * N + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double dt = delta[(b * L + t) * H + h];
+            double a = exp(dt * A[h]);
+            const double *xt = &x[((b * L + t) * H + h) * P];
+            const double *Bg = &Bt[((b * L + t) * G + g) * N];
+            const double *Cg = &Ct[((b * L + t) * G + g) * N];
+            double *yt = &y[((b * L + t) * H + h) * P];
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    S[p * N + n] = a * S[p * N + n] + dt * xt[p] * Bg[n];
+                    acc += Cg[n] * S[p * N + n];
+                }
+                if (Dskip) acc += Dskip[h] * xt[p];
+                yt[p] = acc;
+            }
+        }
+        if (state_out)
+            for (int64_t i = 0; i < P * N; ++i) state_out[r * P * N + i] = S[i];
+        free(S);
     }
     return 0;
 }

@@ -490,7 +490,95 @@ def pin_trap_composition(o):
     assert np.allclose(state, st, rtol=1e-12, atol=1e-13)
 
 
-ALL_PINS = [pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
+# --- the Mamba-2 SSD layer -----------------------------------------------------
+def pin_ssd_pages_dual(o):
+    """The pages' check of the SSD dual ("Notas sobre Mamba", section "A forma
+    dual: atenção mascarada"): the (P, N)-state recurrence of the SSD oracle
+    equals the quadratic masked form (Lmask o C B^T) X, to the printed 9.44e-15
+    (within 10x, as the rounding order differs)."""
+    seed, L, N, P, printed = _golden_rows("ssd_dual_demo.txt")[0]
+    rng = np.random.default_rng(int(seed))
+    L, N, P = int(L), int(N), int(P)
+    a = rng.uniform(0.85, 0.99, size=L)
+    B, C = rng.normal(size=(L, N)), rng.normal(size=(L, N))
+    X = rng.normal(size=(L, P))
+    Lmask = np.zeros((L, L))
+    for j in range(L):
+        for i in range(j + 1):
+            Lmask[j, i] = np.prod(a[i + 1:j + 1])
+    Yq = (Lmask * (C @ B.T)) @ X
+    # a_t = exp(delta_t * A) with A = -1; the input term delta_t x_t B_t = X_t B_t
+    dt = -np.log(a)
+    y, _ = o.ssd64((X / dt[:, None])[None, :, None, :], dt[None, :, None], np.array([-1.0]),
+                   B[None, :, None, :], C[None, :, None, :])
+    err = np.abs(y[0, :, 0, :] - Yq).max()
+    assert err <= 10 * printed, err
+
+
+def pin_ssd_is_scalar_a_s6(o):
+    """Head dimension P = 1, one head per channel: the S6 scan with A[d, :]
+    equal to the head's scalar (the restriction the SSD layer makes), with the
+    skip term and a carried-in state."""
+    rng = np.random.default_rng(21)
+    batch, L, H, N = 2, 40, 5, 6
+    p = _rand_problem(rng, batch, L, H, N, gate=False)
+    Ah = -np.exp(rng.normal(size=H))
+    p["A"] = np.repeat(Ah[:, None], N, 1)
+    y6, s6 = _scan(o, p)
+    y, st = o.ssd64(p["x"][..., None], p["delta"], Ah, p["Bt"][:, :, None, :], p["Ct"][:, :, None, :],
+                    p["Dskip"], p["state_in"][:, :, None, :])
+    assert np.allclose(y[..., 0], y6, rtol=1e-12, atol=1e-13)
+    assert np.allclose(st[:, :, 0, :], s6, rtol=1e-12, atol=1e-13)
+
+
+def pin_ssd_brute_force(o):
+    """Tiny inputs with several heads per group against the explicit sum
+    y_t[p] = sum_{i<=t} (prod_{i<k<=t} a_k) (C_t . B_i) delta_i x_i[p]
+             + (prod_{k<=t} a_k) C_t . S0[p] + D x_t[p]."""
+    rng = np.random.default_rng(22)
+    batch, L, H, P, G, N = 2, 6, 4, 3, 2, 2
+    x = rng.normal(size=(batch, L, H, P))
+    dl = np.exp(rng.uniform(np.log(0.05), np.log(1.0), size=(batch, L, H)))
+    A = -np.exp(rng.normal(size=H))
+    B, C = rng.normal(size=(batch, L, G, N)), rng.normal(size=(batch, L, G, N))
+    Dk = rng.uniform(0.5, 1.5, size=H)
+    S0 = rng.normal(size=(batch, H, P, N))
+    y, st = o.ssd64(x, dl, A, B, C, Dk, S0)
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            a = np.exp(dl[b, :, h] * A[h])
+            for t in range(L):
+                ref = np.prod(a[:t + 1]) * (S0[b, h] @ C[b, t, g]) + Dk[h] * x[b, t, h]
+                for i in range(t + 1):
+                    ref = ref + np.prod(a[i + 1:t + 1]) * (C[b, t, g] @ B[b, i, g]) * dl[b, i, h] * x[b, i, h]
+                assert np.allclose(y[b, t, h], ref, rtol=1e-12, atol=1e-12), (b, t, h)
+            fin = np.prod(a) * S0[b, h]
+            for i in range(L):
+                fin = fin + np.prod(a[i + 1:]) * dl[b, i, h] * np.outer(x[b, i, h], B[b, i, g])
+            assert np.allclose(st[b, h], fin, rtol=1e-12, atol=1e-12)
+
+
+def pin_ssd_resume(o):
+    """A sequence cut in two, the second part started from the first part's
+    final state, equals one call."""
+    rng = np.random.default_rng(23)
+    batch, L, H, P, G, N = 2, 29, 4, 5, 2, 3
+    x = rng.normal(size=(batch, L, H, P))
+    dl = np.exp(rng.uniform(np.log(1e-3), np.log(0.5), size=(batch, L, H)))
+    A = -np.exp(rng.normal(size=H))
+    B, C = rng.normal(size=(batch, L, G, N)), rng.normal(size=(batch, L, G, N))
+    S0 = rng.normal(size=(batch, H, P, N))
+    y, st = o.ssd64(x, dl, A, B, C, None, S0)
+    m = 11
+    y1, s1 = o.ssd64(x[:, :m], dl[:, :m], A, B[:, :m], C[:, :m], None, S0)
+    y2, s2 = o.ssd64(x[:, m:], dl[:, m:], A, B[:, m:], C[:, m:], None, s1)
+    assert np.allclose(np.concatenate([y1, y2], 1), y, rtol=1e-12, atol=1e-13)
+    assert np.allclose(s2, st, rtol=1e-12, atol=1e-13)
+
+
+ALL_PINS = [pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
+            pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
             pin_linearity_causality]

@@ -63,6 +63,12 @@ MUTANTS = [
     ("trap_earlier_B_batch_row_0", "B_prev[b * N + n] * x_prev[b * D + d]", "B_prev[n] * x_prev[b * D + d]"),
     ("trap_lam_previous_token", "double lm = lam[IDX3(b, t, d, L, D)];",
      "double lm = lam[IDX3(b, t > 0 ? t - 1 : 0, d, L, D)];"),
+    ("ssd_group_modulo", "g = h / (H / G);", "g = h % G;"),
+    ("ssd_input_without_delta", "+ dt * xt[p] * Bg[n];", "+ xt[p] * Bg[n];"),
+    ("ssd_decay_of_group", "double a = exp(dt * A[h]);", "double a = exp(dt * A[g]);"),
+    ("ssd_readout_uses_B", "acc += Cg[n] * S[p * N + n];", "acc += Bg[n] * S[p * N + n];"),
+    ("ssd_state_transposed", "state_out[r * P * N + i] = S[i];", "state_out[r * P * N + i] = S[(i % P) * N + i / P];"),
+    ("ssd_skip_of_head_zero", "if (Dskip) acc += Dskip[h] * xt[p];", "if (Dskip) acc += Dskip[0] * xt[p];"),
     ("trap_step_prev_uses_current_B", "B_prev[b * N + n] * x_prev[r]", "Bt[b * N + n] * x_prev[r]"),
     ("trap_step_beta_without_alpha", "            double beta = (1.0 - lm) * dt * alpha;\n            double gamma = lm * dt;\n            double vp",
      "            double beta = (1.0 - lm) * dt;\n            double gamma = lm * dt;\n            double vp"),
