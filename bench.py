@@ -40,6 +40,8 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 SCAN_SLOTS_PER_ELEM = 6
 SCAN_KERNEL = "scan_stripe_kernel"
 STEP_KERNEL = "step_kernel"
+SSD_KERNEL = "ssd_kernel"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix-core peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -201,6 +203,86 @@ def bench_scan(args, name):
     return out
 
 
+def ssd_flops(cfg) -> int:
+    """Matrix-core flops the chunked SSD algorithm needs per launch (Q = 64):
+    per chunk and head, C B^T and M x on the lower triangle with its diagonal
+    (Q (Q + 1) / 2 entries), C H^T and the state update x^T (w o B) in full."""
+    Q = 64
+    chunks = (cfg.L + Q - 1) // Q
+    tri = Q * (Q + 1) // 2
+    per = 2 * (tri * cfg.N + tri * cfg.P + Q * cfg.N * cfg.P + cfg.P * Q * cfg.N)
+    return cfg.batch * cfg.H * chunks * per
+
+
+def bench_ssd(args):
+    import numpy as np
+    import torch
+    import selective_state_space_16_amd as ssm
+    import workloads as W
+
+    cfg = W.SSD_CONFIGS["ssd"]
+    log(f"[bench] workload {cfg}")
+    whole = W.ssd_inputs(cfg, 0, 0)
+    A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
+    per_set = W.ssd_bytes(cfg)
+    nsets = max(1, min(args.rotate, int(60e9 // max(per_set, 1))))
+    sets = [W.fill_ssd_device(cfg, "cuda", seed=2000 + k) for k in range(nsets)]
+    # set 0: sampled (batch row, head) pairs from the seeded streams, for the parity check
+    picks = [(0, 0), (cfg.batch - 1, cfg.H - 1)]
+    subs = {}
+    for b, h in picks:
+        sub = W.ssd_inputs(cfg, batches=[b], heads=[h])
+        subs[(b, h)] = sub
+        sets[0]["x"][b, :, h] = to_dev(sub["x"][0, :, 0])
+        sets[0]["delta"][b, :, h] = to_dev(sub["delta"][0, :, 0])
+        sets[0]["Bt"][b] = to_dev(sub["Bt"][0])
+        sets[0]["Ct"][b] = to_dev(sub["Ct"][0])
+    ys = [torch.empty_like(s_["x"]) for s_ in sets]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s_ = sets[i % len(sets)]
+        ssm.ssm_ssd_fwd(s_["x"], s_["delta"], A, s_["Bt"], s_["Ct"], Dskip=Dskip, y=ys[i % len(sets)], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms, launch_ms = timed(args.steps, step, stream)
+    log(f"[bench] {args.steps} steps, {ms * 1e3:.2f} us/step ({launch_ms * 1e3:.2f} us/launch) "
+        f"over {len(sets)} rotating sets")
+    out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems, "bytes": W.ssd_bytes(cfg),
+           "flops": ssd_flops(cfg), "dtype": cfg.dtype, "parity": None, "cpu": None}
+    if not args.no_cpu:
+        import oracle
+        step(0)
+        torch.cuda.synchronize()
+        o = oracle.get()
+        worst, reps, tot = 0.0, 0, 0.0
+        for (b, h), sub in subs.items():
+            t = time.perf_counter()
+            yr, _ = o.ssd(sub, cfg.dtype)
+            tot += time.perf_counter() - t
+            reps += 1
+            rel, _ = rel_l2(ys[0][b, :, h].double().cpu().numpy(), yr[0, :, 0])
+            worst = max(worst, rel)
+        out["parity"] = {"relL2_worst_sampled_head": worst, "heads": len(subs)}
+        # CPU baseline: the oracle on whole heads, about cpu_seconds of work
+        k = 0
+        while tot < args.cpu_seconds:
+            sub = W.ssd_inputs(cfg, batches=[k % cfg.batch], heads=[(7 * k) % cfg.H])
+            t = time.perf_counter()
+            o.ssd(sub, cfg.dtype)
+            tot += time.perf_counter() - t
+            reps += 1
+            k += 1
+        per_head = cfg.L * cfg.P * cfg.N
+        out["cpu"] = {"value": per_head * reps / tot / 1e9, "unit": "G(B*L*H*P*N)-elem/s", "cores": 1,
+                      "kind": "oracle",
+                      "sample": f"{reps} whole (batch row, head) sequences, {tot:.1f}s, fp64 C oracle "
+                                f"(one head per call, so one thread)"}
+    return out
+
+
 def bench_step(args):
     import numpy as np
     import torch
@@ -290,7 +372,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "ssd"])
     ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -318,16 +400,28 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    r = bench_step(args) if args.workload == "c4" else bench_scan(args, args.workload)
+    if args.workload == "ssd" and (args.softplus or args.trap):
+        ap.error("--softplus and --trap apply to the S6 scan and step")
+    if args.workload == "ssd":
+        r = bench_ssd(args)
+    else:
+        r = bench_step(args) if args.workload == "c4" else bench_scan(args, args.workload)
     cfg = r["cfg"]
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
     traffic = None if (args.softplus or args.trap) else measured_traffic(args.workload)
+    kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL}.get(args.workload, SCAN_KERNEL)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-           "traffic": traffic, "kernel": STEP_KERNEL if args.workload == "c4" else SCAN_KERNEL,
+           "traffic": traffic, "kernel": kernel,
            "algorithmic_bytes_per_launch": r["bytes"], "launch_us": launch_ms * 1e3}
-    if args.workload == "c4":
-        roof = hbm
+    mfma = None
+    if args.workload == "ssd":
+        tf = r["flops"] / (launch_ms * 1e-3) / 1e12
+        mfma = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / MFMA_BF16_PEAK_TFLOPS, "kernel": kernel, "algorithmic_flops_per_launch": r["flops"],
+                "launch_us": launch_ms * 1e3}
+    if args.workload in ("c4", "ssd"):
+        roof = hbm  # the SSD layer needs more time at the HBM peak than at the matrix-core peak
     else:
         # the scan needs more time at the VALU peak than at the HBM peak
         slots = r["elems"] * SCAN_SLOTS_PER_ELEM
@@ -335,7 +429,11 @@ def main():
         roof = {"bound": "alu", "achieved": tslots, "peak": VALU_PEAK_TSLOTS, "unit": "T VALU-slots/s",
                 "frac": tslots / VALU_PEAK_TSLOTS, "traffic": traffic, "kernel": SCAN_KERNEL,
                 "algorithmic_slots_per_launch": slots, "launch_us": launch_ms * 1e3}
-    if args.workload == "c4":
+    if args.workload == "ssd":
+        config = {"workload": cfg.name, "batch": cfg.batch, "L": cfg.L, "H": cfg.H, "P": cfg.P, "G": cfg.G,
+                  "N": cfg.N, "dtype": cfg.dtype, "chunk": 64}
+        metric = "ssd-layer G(B*L*H*P*N)-elem/s"
+    elif args.workload == "c4":
         config = {"workload": cfg.name, "batch": cfg.batch, "D": cfg.D, "N": cfg.N, "dtype": cfg.dtype,
                   "gate": cfg.gate, "steps_timed": args.steps}
         if args.softplus:
@@ -354,7 +452,7 @@ def main():
     line = {
         "metric": metric,
         "value": r["elems"] / (ms * 1e-3) / 1e9,
-        "unit": "G(B*L*D*N)-elem/s" if args.workload != "c4" else "G(B*D*N)-elem/s",
+        "unit": {"c4": "G(B*D*N)-elem/s", "ssd": "G(B*L*H*P*N)-elem/s"}.get(args.workload, "G(B*L*D*N)-elem/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -368,6 +466,7 @@ def main():
         "hbm_gbs_algorithmic": gbs,
         "roofline": roof,
         "roofline_hbm": hbm,
+        "roofline_mfma": mfma,
         "cpu_baseline": r["cpu"],
         "parity": r["parity"],
     }

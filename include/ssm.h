@@ -229,6 +229,38 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
                   const void *Bt, const void *Ct, const float *Dskip, const void *z,
                   const void *x_prev, const void *B_prev, float *state, void *y, void *stream);
 
+/*
+ * Mamba-2 state space dual (SSD) layer: the selective recurrence with the
+ * transition restricted to a scalar per head times the identity ("Notas sobre
+ * Mamba", section "A forma dual: atenção mascarada"; "Mamba-2 e State Space
+ * Duality (SSD)"). Per batch row b and head h, with group g = h / (H / G):
+ *
+ *   a[t]      = exp(delta[b,t,h] * A[h])
+ *   S[p][n]   = a[t] * S[p][n] + delta[b,t,h] * x[b,t,h,p] * Bt[b,t,g,n]
+ *   y[b,t,h,p] = sum_n Ct[b,t,g,n] * S[p][n]  (+ Dskip[h] * x[b,t,h,p])
+ *
+ * computed by chunks of 64 tokens: inside a chunk by the masked (attention-
+ * like) dual form on the matrix cores, across chunks through the state
+ * (section "O algoritmo SSD").
+ *
+ *   x, y          (batch, L, H, P)  bfloat16
+ *   delta         (batch, L, H)     bfloat16   step after its activation
+ *   A             (H)               float      negative scalar per head
+ *   Bt, Ct        (batch, L, G, N)  bfloat16   shared by the H / G heads of a group
+ *   Dskip         (H)               float      NULL = no skip term
+ *   state_in      (batch, H, P, N)  float      NULL = zeros
+ *   state_out     (batch, H, P, N)  float      NULL = not written; may equal state_in
+ *
+ * Supported: dtype SSM_BF16 (float accumulation; the chunk's masked matrix,
+ * the weighted B and the state copy that meets C are rounded to bfloat16 on
+ * the way into the matrix cores), P = 64, N = 64 or 128; anything else returns
+ * SSM_ERR_UNSUPPORTED. H must be a multiple of G (else SSM_ERR_SHAPE). Uses no
+ * workspace and keeps nothing between calls. Conventions otherwise as above.
+ */
+int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                const float *Dskip, const float *state_in, float *state_out, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

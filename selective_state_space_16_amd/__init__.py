@@ -13,6 +13,9 @@ Functions (same names as the C ABI):
       of delta; the kernels use softplus(delta_raw + dt_bias) as the step size
   ssm_scan_fwd_trap / ssm_step_trap: the exponential-trapezoidal rule, with a
       per-token weight lam and the token before the first (x_prev, B_prev)
+  ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None,
+              y=None) -> y: the Mamba-2 SSD layer (x (batch, L, H, P), Bt/Ct
+      (batch, L, G, N), bfloat16)
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
 """
@@ -24,7 +27,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
+    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
 
@@ -38,7 +41,7 @@ lib_path = os.path.join(_HERE, "libssm.so")
 
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
-           "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap")
+           "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -77,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_trap.restype = ci
     L.ssm_step_trap.argtypes = [i64, i64, i64, ci] + [vp] * 12 + [vp]
     L.ssm_step_trap.restype = ci
+    L.ssm_ssd_fwd.argtypes = [i64] * 6 + [ci] + [vp] * 9 + [vp]
+    L.ssm_ssd_fwd.restype = ci
     _lib = L
     return L
 
@@ -255,3 +260,26 @@ def ssm_step_trap(x, delta, lam, A, Bt, Ct, state, Dskip=None, z=None, x_prev=No
     (both None at a sequence's first token)."""
     return _step("ssm_step_trap", x, delta, None, A, Bt, Ct, state, Dskip, z, y, stream, lam=lam, x_prev=x_prev,
                  B_prev=B_prev)
+
+
+def ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None, y=None, stream=None):
+    """Mamba-2 SSD layer. Shapes: x, y (batch, L, H, P) and delta (batch, L, H)
+    bfloat16; A, Dskip (H,) float32; Bt, Ct (batch, L, G, N) bfloat16;
+    state_in, state_out (batch, H, P, N) float32."""
+    import torch
+    if x.dim() != 4 or Bt.dim() != 4:
+        raise ValueError("x must be (batch, L, H, P) and Bt (batch, L, G, N)")
+    batch, L, H, P = x.shape
+    G, N = Bt.shape[2], Bt.shape[3]
+    act, f32 = x.dtype, torch.float32
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, H)), _ptr(A, "A", f32, (H,)),
+            _ptr(Bt, "Bt", act, (batch, L, G, N)), _ptr(Ct, "Ct", act, (batch, L, G, N)),
+            _ptr(Dskip, "Dskip", f32, (H,)), _ptr(state_in, "state_in", f32, (batch, H, P, N)),
+            _ptr(state_out, "state_out", f32, (batch, H, P, N)), _ptr(y, "y", act, (batch, L, H, P))]
+    st = lib().ssm_ssd_fwd(batch, L, H, P, G, N, code, *args, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_ssd_fwd")
+    return y

@@ -303,4 +303,44 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
     return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
+int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                const float *Dskip, const float *state_in, float *state_out, void *y, void *stream) {
+    if (batch < 0 || L < 0 || H < 0 || P < 0 || G < 0 || N < 0) return SSM_ERR_SHAPE;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (dtype != SSM_BF16 || !ssm::ssd_supported(P, N)) return SSM_ERR_UNSUPPORTED;
+    if (H > 0 && (G < 1 || H % G != 0)) return SSM_ERR_SHAPE;
+    if (checked_mul3(batch, L, H) < 0 || checked_mul3(checked_mul(batch, L), H, P) < 0 ||
+        checked_mul3(checked_mul(batch, L), G, N) < 0 || checked_mul3(checked_mul(batch, H), P, N) < 0)
+        return SSM_ERR_SHAPE;
+    if (batch == 0 || H == 0) return SSM_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (L == 0) {
+        if (!state_out) return SSM_OK;
+        if (!aligned16(state_out) || (state_in && !aligned16(state_in))) return SSM_ERR_ALIGN;
+        if (state_in == state_out) return SSM_OK;
+        return ssm::launch_state_copy(state_in, state_out, batch * H * P * N, s) == hipSuccess ? SSM_OK
+                                                                                              : SSM_ERR_HIP;
+    }
+    if (!x || !delta || !A || !Bt || !Ct || !y) return SSM_ERR_NULL;
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, state_in, state_out, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+    ssm::SsdArgs a{};
+    a.batch = batch;
+    a.L = L;
+    a.H = H;
+    a.G = G;
+    a.x = x;
+    a.delta = delta;
+    a.Bt = Bt;
+    a.Ct = Ct;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.y = y;
+    return ssm::launch_ssd(a, (int)N, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

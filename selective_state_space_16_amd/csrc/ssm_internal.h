@@ -69,6 +69,18 @@ struct StepArgs {
     void *y;
 };
 
+// Mamba-2 SSD layer: x, y (batch, L, H, P); delta (batch, L, H); Bt, Ct
+// (batch, L, G, N); A, Dskip (H); state (batch, H, P, N); bfloat16 activations.
+struct SsdArgs {
+    int64_t batch, L, H, G;
+    const void *x, *delta, *Bt, *Ct;
+    const float *A, *Dskip, *state_in;
+    float *state_out;
+    void *y;
+};
+bool ssd_supported(int64_t P, int64_t N);
+hipError_t launch_ssd(const SsdArgs &a, int N, hipStream_t s);
+
 // Sequence split used for a scan of these sizes (deterministic).
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);
 

@@ -114,3 +114,16 @@ def gpu_scan_trap(inp, prev=True, want_state=True):
     torch.cuda.synchronize()
     assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
+
+
+def gpu_ssd(inp, want_state=True):
+    """Run ssm_ssd_fwd on stored SSD inputs; returns (y64, state64 or None)."""
+    import torch
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    batch, L, H, P = dev["x"].shape
+    N = dev["Bt"].shape[3]
+    st_out = torch.empty((batch, H, P, N), dtype=torch.float32, device="cuda") if want_state else None
+    y = ssm.ssm_ssd_fwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], Dskip=dev["Dskip"],
+                        state_in=dev["state_in"], state_out=st_out)
+    torch.cuda.synchronize()
+    return to_f64(y), (to_f64(st_out) if st_out is not None else None)

@@ -192,3 +192,25 @@ def test_step_trap_rejects(kw, code):
 def test_trap_entry_points_empty_ok_without_gpu():
     assert scan_trap(batch=0) == 0 and scan_trap(D=0) == 0 and scan_trap(lam=None, L=0) == 0
     assert step_trap(batch=0) == 0 and step_trap(D=0) == 0
+
+
+def ssd(**kw):
+    a = dict(batch=1, L=8, H=4, P=64, G=1, N=128, dtype=1, x=P, delta=P, A=P, Bt=P, Ct=P, Dskip=None,
+             state_in=None, state_out=None, y=P, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_ssd_fwd(a["batch"], a["L"], a["H"], a["P"], a["G"], a["N"], a["dtype"], a["x"], a["delta"],
+                                 a["A"], a["Bt"], a["Ct"], a["Dskip"], a["state_in"], a["state_out"], a["y"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=3), -3), (dict(dtype=0), -4), (dict(P=32), -4), (dict(N=16), -4),
+    (dict(G=3), -2), (dict(G=0), -2), (dict(x=None), -1), (dict(y=None), -1), (dict(Bt=MIS), -5),
+    (dict(state_out=MIS), -5),
+])
+def test_ssd_rejects(kw, code):
+    assert ssd(**kw) == code
+
+
+def test_ssd_empty_ok_without_gpu():
+    assert ssd(batch=0) == 0 and ssd(H=0) == 0 and ssd(L=0) == 0

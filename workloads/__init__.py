@@ -20,6 +20,9 @@ Distributions follow the workloads described for the Mamba selective scan
 delta = softplus(0.5*eps + dt_bias) where dt_bias is the inverse softplus of a
 per-channel dt drawn log-uniform in [1e-3, 1e-1]; x, z, Bt, Ct ~ N(0, 1);
 Dskip = 1 or U(0.5, 1.5). delta is handed to the scan after the softplus.
+For the Mamba-2 SSD layer (x (batch, L, H, P), Bt/Ct (batch, L, G, N)): A_h =
+-U(1, 16) per head, delta = softplus(0.5*eps + dt_bias) with dt_bias per head
+as above, x, Bt, Ct ~ N(0, 1), Dskip ~ U(0.5, 1.5), bfloat16 activations.
 For the exponential-trapezoidal rule ("Recorrência trapezoidal"), the weight
 lam = sigmoid(u) with u ~ N(0, 1) per (b, t, d) (the sigmoid of a per-token
 projection), and the token before the first, x_prev and B_prev, ~ N(0, 1).
@@ -46,6 +49,7 @@ __all__ = [
     "fill_scan_device", "fill_step_device", "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
     "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
     "storage_to_f64", "scan_bytes", "step_bytes", "trap_extra_bytes", "trap_step_extra_bytes",
+    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes",
 ]
 
 DTYPES = ("f32", "bf16")
@@ -53,7 +57,7 @@ _CHUNK = 65536  # tokens per random stream
 _CBLK = 64      # channels per random stream
 
 # stream keys (tensor kinds)
-_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE, _K_LAM, _K_XPREV, _K_BPREV = range(11)
+_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE, _K_LAM, _K_XPREV, _K_BPREV, _K_AH = range(12)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -92,6 +96,34 @@ class StepConfig:
     @property
     def elems_per_step(self) -> int:
         return self.batch * self.D * self.N
+
+
+@dataclasses.dataclass(frozen=True)
+class SsdConfig:
+    """A Mamba-2 SSD workload: x (batch, L, H, P), Bt/Ct (batch, L, G, N)."""
+    name: str
+    batch: int
+    L: int
+    H: int
+    P: int = 64
+    G: int = 1
+    N: int = 128
+    dtype: str = "bf16"
+    dskip: bool = True
+    state_in: Optional[float] = None
+    seed: int = 5
+
+    @property
+    def elems(self) -> int:
+        """State updates per launch: batch * L * H * P * N."""
+        return self.batch * self.L * self.H * self.P * self.N
+
+
+# A Mamba-2 layer with 5120 inner channels as 80 heads of 64, state size 128
+# (the pages: the SSD state can grow from 16 to 64, 128 or 256), one group.
+SSD_CONFIGS: Dict[str, SsdConfig] = {
+    "ssd": SsdConfig("ssd_mamba2_layer_bf16", 8, 4096, 80, 64, 1, 128, "bf16", dskip=True, seed=5),
+}
 
 
 # The five workloads, in order: tiny fp32; small-model layer fp32; large-model
@@ -377,6 +409,81 @@ def scan_bytes(cfg: ScanConfig, state_out: bool = False) -> int:
     if state_out:
         n += cfg.batch * cfg.D * cfg.N * 4
     return n
+
+
+def _ssd_head_params(cfg: SsdConfig):
+    """A (H,) float32, dt_bias (H,) float64, Dskip (H,) float32 or None."""
+    A = (-_rng(cfg.seed, _K_AH).uniform(1.0, 16.0, size=cfg.H)).astype(np.float32)
+    dt = np.exp(_rng(cfg.seed, _K_DT).uniform(math.log(1e-3), math.log(1e-1), size=cfg.H))
+    dt_bias = dt + np.log(-np.expm1(-dt))
+    Dskip = _rng(cfg.seed, _K_D).uniform(0.5, 1.5, size=cfg.H).astype(np.float32) if cfg.dskip else None
+    return A, dt_bias, Dskip
+
+
+def ssd_inputs(cfg: SsdConfig, t0: int = 0, t1: Optional[int] = None, batches=None, heads=None):
+    """SSD inputs of `cfg` for tokens [t0, t1), in storage dtypes; `batches`
+    and `heads` select batch rows and heads. Selected heads must share one
+    group: Bt and Ct are then that group's (G = 1). The values do not depend on
+    the selection or on how the token range is split."""
+    if t1 is None:
+        t1 = cfg.L
+    bsel = np.arange(cfg.batch) if batches is None else np.asarray(batches)
+    hsel = np.arange(cfg.H) if heads is None else np.asarray(heads)
+    A, dt_bias, Dskip = _ssd_head_params(cfg)
+    T, act = t1 - t0, cfg.dtype
+    cols = (hsel[:, None] * cfg.P + np.arange(cfg.P)[None, :]).reshape(-1)
+    groups = np.arange(cfg.G)
+    if heads is not None:
+        groups = np.unique(hsel // (cfg.H // cfg.G))
+        assert len(groups) == 1, "selected heads must share one group"
+    gcols = (groups[:, None] * cfg.N + np.arange(cfg.N)[None, :]).reshape(-1)
+    NG = len(groups)
+    x = np.empty((len(bsel), T, len(hsel), cfg.P), dtype=np.float32 if act == "f32" else np.uint16)
+    dl = np.empty((len(bsel), T, len(hsel)), dtype=x.dtype)
+    Bt = np.empty((len(bsel), T, NG, cfg.N), dtype=x.dtype)
+    Ct = np.empty_like(Bt)
+    for k, b in enumerate(bsel):
+        x[k] = _store(_token_block(cfg.seed, _K_X, b, t0, t1, cfg.H * cfg.P, cols), act).reshape(T, len(hsel), cfg.P)
+        eps = _token_block(cfg.seed, _K_DNOISE, b, t0, t1, cfg.H, hsel)
+        dl[k] = _store(_softplus(0.5 * eps + dt_bias[hsel][None, :]), act)
+        Bt[k] = _store(_token_block(cfg.seed, _K_B, b, t0, t1, cfg.G * cfg.N, gcols), act).reshape(T, NG, cfg.N)
+        Ct[k] = _store(_token_block(cfg.seed, _K_C, b, t0, t1, cfg.G * cfg.N, gcols), act).reshape(T, NG, cfg.N)
+    out = {"x": x, "delta": dl, "A": np.ascontiguousarray(A[hsel]), "Bt": Bt, "Ct": Ct,
+           "Dskip": None if Dskip is None else np.ascontiguousarray(Dskip[hsel]), "state_in": None}
+    if cfg.state_in is not None:
+        st = _rng(cfg.seed, _K_STATE).standard_normal((cfg.batch, cfg.H, cfg.P, cfg.N)) * cfg.state_in
+        out["state_in"] = np.ascontiguousarray(st[bsel][:, hsel].astype(np.float32))
+    return out
+
+
+def fill_ssd_device(cfg: SsdConfig, device, seed: int = 777):
+    """torch tensors of the full SSD workload on `device`, same distributions as
+    ssd_inputs drawn with torch: x, delta, Bt, Ct."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    _A, dt_bias, _D = _ssd_head_params(cfg)
+    bias = torch.tensor(dt_bias, dtype=torch.float32, device=device)
+
+    def normal(shp):
+        return torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+
+    return {"x": normal((cfg.batch, cfg.L, cfg.H, cfg.P)).to(act),
+            "delta": torch.nn.functional.softplus(normal((cfg.batch, cfg.L, cfg.H)).mul_(0.5).add_(bias)).to(act),
+            "Bt": normal((cfg.batch, cfg.L, cfg.G, cfg.N)).to(act),
+            "Ct": normal((cfg.batch, cfg.L, cfg.G, cfg.N)).to(act)}
+
+
+def ssd_bytes(cfg: SsdConfig, state_out: bool = False) -> int:
+    """Bytes the SSD layer must move: x read and y written per (b, t, h, p),
+    delta per (b, t, h), Bt and Ct per (b, t, g, n), A and Dskip once, the state
+    when carried in or out."""
+    e = _esize(cfg.dtype)
+    n = 2 * cfg.batch * cfg.L * cfg.H * cfg.P * e + cfg.batch * cfg.L * cfg.H * e
+    n += 2 * cfg.batch * cfg.L * cfg.G * cfg.N * e + cfg.H * 4 * (2 if cfg.dskip else 1)
+    st = cfg.batch * cfg.H * cfg.P * cfg.N * 4
+    return n + (st if cfg.state_in is not None else 0) + (st if state_out else 0)
 
 
 def trap_extra_bytes(cfg: ScanConfig) -> int:
