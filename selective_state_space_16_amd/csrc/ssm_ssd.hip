@@ -9,17 +9,24 @@
 // small matrix products, and between chunks the (P, N) state carries the rest
 // (the chunked algorithm of section "O algoritmo SSD" and of "Mamba-2 e State
 // Space Duality (SSD)", where Q is typically 64). Per chunk, with cum_j the
-// log2 decay from the chunk start through token j:
+// log2 decay from the chunk start through token j, the kernel forms the
+// transposed products
 //
-//   G      = C B^T                                  (Q x Q, K = N)
-//   M_ji   = G_ji exp2(cum_j - cum_i) delta_i,  i <= j (0 above the diagonal)
-//   y      = M x + diag(exp2(cum)) C H^T + D x      (K = Q, then K = N)
-//   H      = exp2(cum_last) H + x^T (w o B),        w_i = delta_i exp2(cum_last - cum_i)
+//   G^T      = B C^T                                      (K = N)
+//   M^T_ij   = G^T_ij exp2(cum_j - cum_i) delta_i,  i <= j  (0 below)
+//   y^T      = x^T M^T + (H C^T) diag(exp2(cum)) + D x^T  (K = Q, then K = N)
+//   H        = exp2(cum_last) H + x^T (w o B),            w_i = delta_i exp2(cum_last - cum_i)
 //
 // One workgroup of four waves walks the chunks of one (batch row, head) in
-// order. The state H (P x N float) stays in the matrix-core accumulators of
-// the waves for the whole sequence; a bfloat16 copy in LDS feeds C H^T. All
-// products are v_mfma_f32_16x16x32_bf16 with float accumulation.
+// order; wave w owns the 16 tokens 16 w .. 16 w + 15 of every chunk for y and
+// the 16 rows 16 w .. of the state. The state H (P x N float) stays in the
+// matrix-core accumulators for the whole sequence; a bfloat16 copy in LDS
+// feeds H C^T. A 16 x 16 tile of G^T comes out of the matrix core with each
+// lane holding four consecutive rows of one column, which is the operand
+// layout of the 16 x 16 x 16 product: M^T is masked and scaled in registers
+// and goes straight back in, never through LDS. The next chunk's x, B, C and
+// delta are loaded into registers while the current one is computed. Two
+// workgroup barriers per chunk.
 #include "ssm_common.h"
 #include "ssm_internal.h"
 
@@ -28,60 +35,187 @@ namespace ssm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQ = 64;   // tokens per chunk
 constexpr int kP = 64;   // head dimension
 constexpr int kThreads = 256;
 
 // LDS of one workgroup. Rows are padded by 16 bytes so that the 16 lanes that
-// read one 16-byte piece each from 16 consecutive rows hit different banks.
+// read one piece each from 16 consecutive rows hit different banks.
 template <int N>
 struct SsdShared {
     static constexpr int RN = N + 8, RQ = kQ + 8;
     alignas(16) uint16_t Cs[kQ][RN];  // C rows of the chunk
-    alignas(16) uint16_t Bs[kQ][RN];  // B rows; then M [kQ][RQ]; then y [kQ][RQ]
+    alignas(16) uint16_t Bs[kQ][RN];  // B rows
     alignas(16) uint16_t BT[N][RQ];   // w_i B[i][n], transposed
     alignas(16) uint16_t XT[kP][RQ];  // x, transposed
     alignas(16) uint16_t Hs[kP][RN];  // the state rounded to bfloat16
     float cum[kQ];                    // log2 decay from the chunk start through token j
     float dl[kQ];                     // delta
-    float w[kQ];                      // delta_i exp2(cum_last - cum_i)
 };
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *(const bf16x8 *)__builtin_assume_aligned(p, 16); }
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ s16x4 ld4(const uint16_t *p) { return *(const s16x4 *)__builtin_assume_aligned(p, 8); }
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ uint16_t to_bf16(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 __device__ __forceinline__ float from_bf16(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
-// The ten 16 x 16 tiles of the chunk's lower triangle, as (row block, column
-// block), dealt to the four waves round robin.
-__constant__ const int kLowJ[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ const int kLowI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// The chunk's global data, held in registers between its load and its LDS
+// store, as 16-byte pieces of 8 consecutive p (x) or n (Bt, Ct) of one token.
+// x and Bt pieces are stored transposed, so lane l holds token l (wave w holds
+// the pieces 8 (w + 4 k)): the 64 lanes of a transposed store then write one
+// contiguous row. Ct pieces are stored as rows: 16-byte pieces in row order.
+// The delta of token `lane` (every wave holds all 64). Tokens past L are read
+// from token L - 1 and zeroed where they are stored, so that no instruction
+// needs a loaded value before the chunk is consumed and the loads stay in
+// flight.
+template <int N>
+struct ChunkRegs {
+    static constexpr int XP = kP / 8 / 4, BP = N / 8 / 4;
+    u32x4 x[XP], b[BP], c[BP];
+    uint16_t dl;
+};
 
-// Matrix-core tile layout (16 x 16 x 32, bfloat16): the A operand row r,
-// k = 8 kk .. 8 kk + 7 sits in lane r + 16 kk; the B operand column c, the same
-// k, in lane c + 16 kk; result element e of lane l is row 4 (l / 16) + e,
-// column l % 16. So A is read from a [row][k] array and B from a [column][k]
-// array, one 16-byte piece per lane.
+// Where a thread's pieces of token 0 of a sequence sit, and how far one chunk
+// moves them (element offsets). The last, partial chunk clamps its tokens to
+// L - 1 instead.
+template <int N>
+struct ChunkAddr {
+    const uint16_t *dl, *x, *b, *c[ChunkRegs<N>::BP];
+    int64_t sdl, sx, sbc;  // per-chunk steps of delta, x and Bt/Ct
+};
+
+template <int N>
+__device__ __forceinline__ void load_chunk(ChunkRegs<N> &r, const ChunkAddr<N> &ad, const SsdArgs &a, int64_t t0,
+                                           int tid) {
+    using R = ChunkRegs<N>;
+    const int64_t L = a.L;
+    const int l = tid & 63, w = tid >> 6;
+    const int64_t c = t0 / kQ;
+    if (t0 + kQ <= L) {
+        r.dl = ad.dl[c * ad.sdl];
+#pragma unroll
+        for (int k = 0; k < R::XP; ++k) r.x[k] = *(const u32x4 *)(ad.x + c * ad.sx + 8 * (w + 4 * k));
+#pragma unroll
+        for (int k = 0; k < R::BP; ++k) r.b[k] = *(const u32x4 *)(ad.b + c * ad.sbc + 8 * (w + 4 * k));
+#pragma unroll
+        for (int k = 0; k < R::BP; ++k) r.c[k] = *(const u32x4 *)(ad.c[k] + c * ad.sbc);
+    } else {
+        // token u of this chunk, clamped, as a step from token 0 of the chunk
+        const int64_t last = L - 1 - t0;
+        const int64_t ul = l < last ? l : last;
+        r.dl = ad.dl[c * ad.sdl + (ul - l) * (ad.sdl / kQ)];
+#pragma unroll
+        for (int k = 0; k < R::XP; ++k)
+            r.x[k] = *(const u32x4 *)(ad.x + c * ad.sx + (ul - l) * (ad.sx / kQ) + 8 * (w + 4 * k));
+#pragma unroll
+        for (int k = 0; k < R::BP; ++k)
+            r.b[k] = *(const u32x4 *)(ad.b + c * ad.sbc + (ul - l) * (ad.sbc / kQ) + 8 * (w + 4 * k));
+#pragma unroll
+        for (int k = 0; k < R::BP; ++k) {
+            const int t = (tid + k * kThreads) / (N / 8);
+            const int64_t u = t < last ? t : last;
+            r.c[k] = *(const u32x4 *)(ad.c[k] + c * ad.sbc + (u - t) * (ad.sbc / kQ));
+        }
+    }
+}
+
+// An empty statement that takes the chunk registers as inputs and outputs: the
+// code that unpacks them cannot move above it, so the loads that fill them
+// stay in flight until the chunk is consumed.
+template <int N>
+__device__ __forceinline__ void pin(ChunkRegs<N> &r) {
+#pragma unroll
+    for (int k = 0; k < ChunkRegs<N>::XP; ++k) asm volatile("" : "+v"(r.x[k]));
+#pragma unroll
+    for (int k = 0; k < ChunkRegs<N>::BP; ++k) asm volatile("" : "+v"(r.b[k]), "+v"(r.c[k]));
+    uint32_t d = r.dl;
+    asm volatile("" : "+v"(d));
+    r.dl = (uint16_t)d;
+}
+
+// The products of wave W for its 16 tokens j = 16 W + lr of the chunk: the
+// G^T tiles of i blocks 0 .. W, masked and scaled into M^T in registers, and
+// y^T = x^T M^T + (H C^T) exp2(cum_j) + D x^T as four 16 x 16 tiles of p,
+// packed to bfloat16 in `yout` (tile pb: rows p = 16 pb + 4 lq .. + 3).
+// W is a compile-time constant so that the independent tiles interleave.
+template <int N, bool SKIP, int W>
+__device__ __forceinline__ void wave_products(SsdShared<N> &sh, int lr, int lq, float dsk, u32x2 (&yout)[4]) {
+    constexpr int KB = N / 32, NT = W + 1;
+    bf16x8 cf[KB];  // C rows of the wave's tokens: the B operand of G^T and of H C^T
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) cf[kb] = ld8(&sh.Cs[16 * W + lr][32 * kb + 8 * lq]);
+    const int jj = 16 * W + lr;
+    const float cum_j = sh.cum[jj];
+    f32x4 gacc[NT];
+#pragma unroll
+    for (int ib = 0; ib < NT; ++ib) gacc[ib] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ib = 0; ib < NT; ++ib) gacc[ib] = mfma32(ld8(&sh.Bs[16 * ib + lr][32 * kb + 8 * lq]), cf[kb], gacc[ib]);
+    s16x4 mt[NT];
+#pragma unroll
+    for (int ib = 0; ib < NT; ++ib)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ii = 16 * ib + 4 * lq + e;
+            float v = gacc[ib][e] * fast_exp2(cum_j - sh.cum[ii]) * sh.dl[ii];
+            if (ib == W) v = ii <= jj ? v : 0.0f;  // the diagonal tile: i <= j only
+            mt[ib][e] = (short)to_bf16(v);
+        }
+    f32x4 yd[4], yo[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) yd[pb] = yo[pb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) yo[pb] = mfma32(ld8(&sh.Hs[16 * pb + lr][32 * kb + 8 * lq]), cf[kb], yo[pb]);
+#pragma unroll
+    for (int ib = 0; ib < NT; ++ib)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) yd[pb] = mfma16(ld4(&sh.XT[16 * pb + lr][16 * ib + 4 * lq]), mt[ib], yd[pb]);
+    const float dec_j = fast_exp2(cum_j);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+        uint16_t out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = __builtin_fmaf(dec_j, yo[pb][e], yd[pb][e]);
+            if (SKIP) v = __builtin_fmaf(dsk, from_bf16(sh.XT[16 * pb + 4 * lq + e][jj]), v);
+            out[e] = to_bf16(v);
+        }
+        __builtin_memcpy(&yout[pb], out, sizeof(out));
+    }
+}
+
+// Matrix-core layouts. 16 x 16 x 32: the A operand row r, k = 8 kk .. + 7 sits
+// in lane r + 16 kk; the B operand column c, the same k, in lane c + 16 kk.
+// 16 x 16 x 16: the same with 4 k per lane (k = 4 kk .. + 3). Both: result
+// element e of lane l is row 4 (l / 16) + e, column l % 16. So A is read from a
+// [row][k] array and B from a [column][k] array.
 template <int N, bool SKIP>
 __global__ __launch_bounds__(kThreads, 2) void ssd_kernel(SsdArgs a) {
-    constexpr int NB = N / 16, RQ = kQ + 8;
+    constexpr int NB = N / 16, KB = N / 32;
     __shared__ SsdShared<N> sh;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    using R = ChunkRegs<N>;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
     const int lr = l & 15, lq = l >> 4;
     const int64_t H = a.H, L = a.L, G = a.G;
     const int64_t b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
     const float A2 = a.A[h] * kLog2e;
     const float dsk = SKIP ? a.Dskip[h] : 0.0f;
-    const uint16_t *xp = (const uint16_t *)a.x;
-    const uint16_t *dp = (const uint16_t *)a.delta;
-    const uint16_t *Bp = (const uint16_t *)a.Bt;
-    const uint16_t *Cp = (const uint16_t *)a.Ct;
     uint16_t *yp = (uint16_t *)a.y;
-    uint16_t (*Ms)[RQ] = reinterpret_cast<uint16_t (*)[RQ]>(&sh.Bs[0][0]);
 
     // The state: wave w holds rows p = 16 w + 4 lq + e, columns n = 16 nb + lr.
     f32x4 Hacc[NB];
@@ -94,132 +228,110 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_kernel(SsdArgs a) {
             sh.Hs[16 * w + 4 * lq + e][16 * nb + lr] = to_bf16(Hacc[nb][e]);
         }
 
+    ChunkAddr<N> ad;
+    ad.sdl = kQ * H;
+    ad.sx = kQ * H * kP;
+    ad.sbc = kQ * G * N;
+    ad.dl = (const uint16_t *)a.delta + (b * L + l) * H + h;
+    ad.x = (const uint16_t *)a.x + ((b * L + l) * H + h) * kP;
+    ad.b = (const uint16_t *)a.Bt + ((b * L + l) * G + g) * N;
+#pragma unroll
+    for (int k = 0; k < R::BP; ++k) {
+        const int q = tid + k * kThreads, t = q / (N / 8), n0 = (q % (N / 8)) * 8;
+        ad.c[k] = (const uint16_t *)a.Ct + ((b * L + t) * G + g) * N + n0;
+    }
+    // y of the previous chunk, stored once that chunk's successor has landed
+    // (so that waiting for the loads never waits for these stores)
+    u32x2 yout[4];
+    int64_t yt0 = -1;
+    const int64_t yrow = (b * L + 16 * w + lr) * H + h;  // this lane's token of chunk 0
+    auto store_y = [&]() {
+        if (yt0 >= 0 && yt0 + 16 * w + lr < L) {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+                *(u32x2 *)(yp + (yrow + yt0 * H) * kP + 16 * pb + 4 * lq) = yout[pb];
+        }
+    };
+    R r;
+    load_chunk<N>(r, ad, a, 0, tid);
     const int64_t nchunks = (L + kQ - 1) / kQ;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * kQ;
-        // 1. the chunk's delta, x (transposed), B and C; tokens past L are zero
-        if (w == 0) sh.dl[l] = t0 + l < L ? from_bf16(dp[(b * L + t0 + l) * H + h]) : 0.0f;
-        for (int q = tid; q < kQ * kP / 8; q += kThreads) {
-            const int t = q / (kP / 8), p0 = (q % (kP / 8)) * 8;
-            uint4 v = {0, 0, 0, 0};
-            if (t0 + t < L) v = *(const uint4 *)(xp + ((b * L + t0 + t) * H + h) * kP + p0);
-            uint16_t e[8];
-            __builtin_memcpy(e, &v, sizeof(v));
+        pin<N>(r);
+        store_y();
+        // 1. decay: an inclusive scan of delta A over the 64 tokens, in every
+        //    wave (lane = token), and the state-update weights
+        const float dl = t0 + l < L ? from_bf16(r.dl) : 0.0f;
+        float cum = dl * A2;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) sh.XT[p0 + k][t] = e[k];
+        for (int d = 1; d < 64; d <<= 1) {
+            const float u = __shfl_up(cum, d);
+            if (l >= d) cum += u;
         }
-        for (int q = tid; q < kQ * N / 8; q += kThreads) {
-            const int t = q / (N / 8), n0 = (q % (N / 8)) * 8;
-            uint4 vb = {0, 0, 0, 0}, vc = {0, 0, 0, 0};
-            if (t0 + t < L) {
-                const int64_t off = ((b * L + t0 + t) * G + g) * N + n0;
-                vb = *(const uint4 *)(Bp + off);
-                vc = *(const uint4 *)(Cp + off);
-            }
-            *(uint4 *)&sh.Bs[t][n0] = vb;
-            *(uint4 *)&sh.Cs[t][n0] = vc;
-        }
-        __syncthreads();
-        // 2. cumulative log2 decay (an inclusive scan over the 64 tokens) and
-        //    the state-update weights
+        const float cum_last = __shfl(cum, 63);
+        const float wl = dl * fast_exp2(cum_last - cum);
         if (w == 0) {
-            float v = sh.dl[l] * A2;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float u = __shfl_up(v, d);
-                if (l >= d) v += u;
-            }
-            sh.cum[l] = v;
-            sh.w[l] = sh.dl[l] * fast_exp2(__shfl(v, 63) - v);
+            sh.cum[l] = cum;
+            sh.dl[l] = dl;
         }
-        __syncthreads();
-        // 3. G = C B^T on the lower-triangle tiles, and BT = (w o B)^T
-        f32x4 Gt[3];
-        int ntiles = 0;
-        for (int k = w; k < 10; k += 4, ++ntiles) {
-            const int jb = kLowJ[k], ib = kLowI[k];
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // 2. the chunk into LDS: x and w o B transposed (lane = token), B and C
+        //    as rows
+        const bool lin = t0 + l < L;
 #pragma unroll
-            for (int kb = 0; kb < N / 32; ++kb)
-                acc = mfma(ld8(&sh.Cs[16 * jb + lr][32 * kb + 8 * lq]), ld8(&sh.Bs[16 * ib + lr][32 * kb + 8 * lq]), acc);
-            Gt[ntiles] = acc;
-        }
-        for (int q = tid; q < kQ * N / 8; q += kThreads) {
-            const int t = q / (N / 8), n0 = (q % (N / 8)) * 8;
+        for (int k = 0; k < R::XP; ++k) {
+            const int p0 = 8 * (w + 4 * k);
             uint16_t e[8];
-            __builtin_memcpy(e, &sh.Bs[t][n0], sizeof(e));
-            const float wt = sh.w[t];
+            __builtin_memcpy(e, &r.x[k], sizeof(e));
 #pragma unroll
-            for (int k = 0; k < 8; ++k) sh.BT[n0 + k][t] = to_bf16(from_bf16(e[k]) * wt);
+            for (int j = 0; j < 8; ++j) sh.XT[p0 + j][l] = lin ? e[j] : 0;
         }
-        __syncthreads();  // every read of Bs is done: its space now holds M
-        // 4. M: decay, delta and the causal mask on the wave's tiles; zeros above
-        for (int k = w, i = 0; k < 10; k += 4, ++i) {
-            const int jb = kLowJ[k], ib = kLowI[k];
-            const int ii = 16 * ib + lr;
-            const float ci = sh.cum[ii], di = sh.dl[ii];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int jj = 16 * jb + 4 * lq + e;
-                const float v = ii <= jj ? Gt[i][e] * fast_exp2(sh.cum[jj] - ci) * di : 0.0f;
-                Ms[jj][ii] = to_bf16(v);
-            }
+        for (int k = 0; k < R::BP; ++k) {
+            const int n0 = 8 * (w + 4 * k);
+            *(u32x4 *)&sh.Bs[l][n0] = lin ? r.b[k] : u32x4{0, 0, 0, 0};
+            uint16_t e[8];
+            __builtin_memcpy(e, &r.b[k], sizeof(e));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sh.BT[n0 + j][l] = to_bf16(from_bf16(e[j]) * wl);  // wl = 0 past L
         }
-        for (int q = tid; q < 6 * 256; q += kThreads) {  // the six tiles above the diagonal
-            const int tile = q / 256, r = (q % 256) / 16, cc = q % 16;
-            const int jb = tile < 3 ? 0 : tile < 5 ? 1 : 2;
-            const int ib = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
-            Ms[16 * jb + r][16 * ib + cc] = 0;
+#pragma unroll
+        for (int k = 0; k < R::BP; ++k) {
+            const int q = tid + k * kThreads, t = q / (N / 8), n0 = (q % (N / 8)) * 8;
+            *(u32x4 *)&sh.Cs[t][n0] = t0 + t < L ? r.c[k] : u32x4{0, 0, 0, 0};
         }
         __syncthreads();
-        // 5. y for the wave's 16 tokens: M x + diag(exp2(cum)) C H^T + D x
-        float yv[4][4];
-        {
-            const int jb = w;
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                f32x4 yd = {0.0f, 0.0f, 0.0f, 0.0f}, yo = {0.0f, 0.0f, 0.0f, 0.0f};
-                for (int kb = 0; kb <= jb / 2; ++kb)
-                    yd = mfma(ld8(&Ms[16 * jb + lr][32 * kb + 8 * lq]), ld8(&sh.XT[16 * pb + lr][32 * kb + 8 * lq]), yd);
-#pragma unroll
-                for (int kb = 0; kb < N / 32; ++kb)
-                    yo = mfma(ld8(&sh.Cs[16 * jb + lr][32 * kb + 8 * lq]), ld8(&sh.Hs[16 * pb + lr][32 * kb + 8 * lq]), yo);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int jj = 16 * jb + 4 * lq + e, pp = 16 * pb + lr;
-                    float v = __builtin_fmaf(fast_exp2(sh.cum[jj]), yo[e], yd[e]);
-                    if (SKIP) v = __builtin_fmaf(dsk, from_bf16(sh.XT[pp][jj]), v);
-                    yv[pb][e] = v;
-                }
-            }
+        // 3. the next chunk's loads, in flight during this chunk's products
+        if (c + 1 < nchunks) load_chunk<N>(r, ad, a, t0 + kQ, tid);
+        asm volatile("" ::: "memory");  // keeps the loads here: they are consumed next chunk
+        // 4-5. the wave's tokens: G^T, M^T, and y^T (stored at the next chunk)
+        switch (w) {
+            case 0: wave_products<N, SKIP, 0>(sh, lr, lq, dsk, yout); break;
+            case 1: wave_products<N, SKIP, 1>(sh, lr, lq, dsk, yout); break;
+            case 2: wave_products<N, SKIP, 2>(sh, lr, lq, dsk, yout); break;
+            default: wave_products<N, SKIP, 3>(sh, lr, lq, dsk, yout); break;
         }
-        __syncthreads();  // M, C and the state copy are read: y goes where M was
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ms[16 * w + 4 * lq + e][16 * pb + lr] = to_bf16(yv[pb][e]);
+        yt0 = t0;
         // 6. the state: H = exp2(cum_last) H + x^T (w o B), on the wave's 16 rows
         {
-            const float dec = fast_exp2(sh.cum[kQ - 1]);
+            const float dec = fast_exp2(cum_last);
+            bf16x8 xf[kQ / 32];
+#pragma unroll
+            for (int kb = 0; kb < kQ / 32; ++kb) xf[kb] = ld8(&sh.XT[16 * w + lr][32 * kb + 8 * lq]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 f32x4 acc = Hacc[nb] * dec;
 #pragma unroll
-                for (int kb = 0; kb < kQ / 32; ++kb)
-                    acc = mfma(ld8(&sh.XT[16 * w + lr][32 * kb + 8 * lq]), ld8(&sh.BT[16 * nb + lr][32 * kb + 8 * lq]), acc);
+                for (int kb = 0; kb < kQ / 32; ++kb) acc = mfma32(xf[kb], ld8(&sh.BT[16 * nb + lr][32 * kb + 8 * lq]), acc);
                 Hacc[nb] = acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sh.Hs[16 * w + 4 * lq + e][16 * nb + lr] = to_bf16(acc[e]);
             }
         }
-        __syncthreads();
-        // 7. y rows out, 16 bytes per thread and piece
-        for (int q = tid; q < kQ * kP / 8; q += kThreads) {
-            const int t = q / (kP / 8), p0 = (q % (kP / 8)) * 8;
-            if (t0 + t < L) *(uint4 *)(yp + ((b * L + t0 + t) * H + h) * kP + p0) = *(const uint4 *)&Ms[t][p0];
-        }
-        __syncthreads();  // the next chunk's loads overwrite the LDS
+        __syncthreads();  // every read of this chunk's LDS is done
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sh.Hs[16 * w + 4 * lq + e][16 * nb + lr] = to_bf16(Hacc[nb][e]);
     }
+    store_y();
     if (a.state_out) {
         float *so = a.state_out + (b * H + h) * (int64_t)(kP * N);
 #pragma unroll
