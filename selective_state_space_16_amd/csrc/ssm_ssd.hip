@@ -85,47 +85,37 @@ struct ChunkRegs {
     uint16_t dl;
 };
 
-// Where a thread's pieces of token 0 of a sequence sit, and how far one chunk
-// moves them (element offsets). The last, partial chunk clamps its tokens to
+// The chunk's loads: a wave-uniform base per tensor (the chunk's first token
+// in this batch row and head or group) plus a 32-bit per-lane byte offset that
+// is the same for every chunk. The last, partial chunk clamps its tokens to
 // L - 1 instead.
 template <int N>
-struct ChunkAddr {
-    const uint16_t *dl, *x, *b, *c[ChunkRegs<N>::BP];
-    int64_t sdl, sx, sbc;  // per-chunk steps of delta, x and Bt/Ct
-};
-
-template <int N>
-__device__ __forceinline__ void load_chunk(ChunkRegs<N> &r, const ChunkAddr<N> &ad, const SsdArgs &a, int64_t t0,
-                                           int tid) {
+__device__ __forceinline__ void load_chunk(ChunkRegs<N> &r, const SsdArgs &a, int64_t b, int64_t h, int64_t g,
+                                           int64_t t0, int tid) {
     using R = ChunkRegs<N>;
-    const int64_t L = a.L;
+    const int64_t L = a.L, H = a.H, G = a.G;
     const int l = tid & 63, w = tid >> 6;
-    const int64_t c = t0 / kQ;
-    if (t0 + kQ <= L) {
-        r.dl = ad.dl[c * ad.sdl];
+    const char *xb = (const char *)a.x + ((b * L + t0) * H + h) * (kP * 2);
+    const char *bb = (const char *)a.Bt + ((b * L + t0) * G + g) * (N * 2);
+    const char *cb = (const char *)a.Ct + ((b * L + t0) * G + g) * (N * 2);
+    const char *db = (const char *)a.delta + ((b * L + t0) * H + h) * 2;
+    const uint32_t xs = (uint32_t)(H * kP * 2), bs = (uint32_t)(G * N * 2), ds = (uint32_t)(H * 2);
+    const bool part = t0 + kQ > L;
+    const uint32_t last = (uint32_t)(L - 1 - t0);  // used only when part
+    // token of this lane (x, Bt, delta) and of this thread's Ct pieces
+    uint32_t ul = (uint32_t)l;
+    if (part) ul = ul < last ? ul : last;
+    r.dl = *(const uint16_t *)(db + ul * ds);
 #pragma unroll
-        for (int k = 0; k < R::XP; ++k) r.x[k] = *(const u32x4 *)(ad.x + c * ad.sx + 8 * (w + 4 * k));
+    for (int k = 0; k < R::XP; ++k) r.x[k] = *(const u32x4 *)(xb + ul * xs + 16 * (w + 4 * k));
 #pragma unroll
-        for (int k = 0; k < R::BP; ++k) r.b[k] = *(const u32x4 *)(ad.b + c * ad.sbc + 8 * (w + 4 * k));
+    for (int k = 0; k < R::BP; ++k) r.b[k] = *(const u32x4 *)(bb + ul * bs + 16 * (w + 4 * k));
+    const uint32_t cn = (uint32_t)((tid % (N / 8)) * 16);
 #pragma unroll
-        for (int k = 0; k < R::BP; ++k) r.c[k] = *(const u32x4 *)(ad.c[k] + c * ad.sbc);
-    } else {
-        // token u of this chunk, clamped, as a step from token 0 of the chunk
-        const int64_t last = L - 1 - t0;
-        const int64_t ul = l < last ? l : last;
-        r.dl = ad.dl[c * ad.sdl + (ul - l) * (ad.sdl / kQ)];
-#pragma unroll
-        for (int k = 0; k < R::XP; ++k)
-            r.x[k] = *(const u32x4 *)(ad.x + c * ad.sx + (ul - l) * (ad.sx / kQ) + 8 * (w + 4 * k));
-#pragma unroll
-        for (int k = 0; k < R::BP; ++k)
-            r.b[k] = *(const u32x4 *)(ad.b + c * ad.sbc + (ul - l) * (ad.sbc / kQ) + 8 * (w + 4 * k));
-#pragma unroll
-        for (int k = 0; k < R::BP; ++k) {
-            const int t = (tid + k * kThreads) / (N / 8);
-            const int64_t u = t < last ? t : last;
-            r.c[k] = *(const u32x4 *)(ad.c[k] + c * ad.sbc + (u - t) * (ad.sbc / kQ));
-        }
+    for (int k = 0; k < R::BP; ++k) {
+        uint32_t t = (uint32_t)((tid + k * kThreads) / (N / 8));
+        if (part) t = t < last ? t : last;
+        r.c[k] = *(const u32x4 *)(cb + t * bs + cn);
     }
 }
 
@@ -228,18 +218,6 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_kernel(SsdArgs a) {
             sh.Hs[16 * w + 4 * lq + e][16 * nb + lr] = to_bf16(Hacc[nb][e]);
         }
 
-    ChunkAddr<N> ad;
-    ad.sdl = kQ * H;
-    ad.sx = kQ * H * kP;
-    ad.sbc = kQ * G * N;
-    ad.dl = (const uint16_t *)a.delta + (b * L + l) * H + h;
-    ad.x = (const uint16_t *)a.x + ((b * L + l) * H + h) * kP;
-    ad.b = (const uint16_t *)a.Bt + ((b * L + l) * G + g) * N;
-#pragma unroll
-    for (int k = 0; k < R::BP; ++k) {
-        const int q = tid + k * kThreads, t = q / (N / 8), n0 = (q % (N / 8)) * 8;
-        ad.c[k] = (const uint16_t *)a.Ct + ((b * L + t) * G + g) * N + n0;
-    }
     // y of the previous chunk, stored once that chunk's successor has landed
     // (so that waiting for the loads never waits for these stores)
     u32x2 yout[4];
@@ -253,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_kernel(SsdArgs a) {
         }
     };
     R r;
-    load_chunk<N>(r, ad, a, 0, tid);
+    load_chunk<N>(r, a, b, h, g, 0, tid);
     const int64_t nchunks = (L + kQ - 1) / kQ;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * kQ;
@@ -301,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_kernel(SsdArgs a) {
         }
         __syncthreads();
         // 3. the next chunk's loads, in flight during this chunk's products
-        if (c + 1 < nchunks) load_chunk<N>(r, ad, a, t0 + kQ, tid);
+        if (c + 1 < nchunks) load_chunk<N>(r, a, b, h, g, t0 + kQ, tid);
         asm volatile("" ::: "memory");  // keeps the loads here: they are consumed next chunk
         // 4-5. the wave's tokens: G^T, M^T, and y^T (stored at the next chunk)
         switch (w) {
