@@ -65,6 +65,8 @@ class Oracle:
         self.lib.oracle_step_trap.restype = ci
         self.lib.oracle_ssd.argtypes = [i64] * 6 + [_DP] * 9 + [ci]
         self.lib.oracle_ssd.restype = ci
+        self.lib.oracle_scan_bwd.argtypes = [i64] * 4 + [_DP] * 18
+        self.lib.oracle_scan_bwd.restype = ci
 
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.oracle_threads(nthreads))
@@ -178,6 +180,31 @@ class Oracle:
             raise ValueError("oracle_ssd rejected sizes")
         return y, st
 
+    def scan_bwd64(self, x, delta, A, Bt, Ct, Dskip, z, state_in, dy, dstate=None):
+        """Gradient of scan64 for the loss sum(dy * y) + sum(dstate * state_out).
+        float64 arrays; returns a dict dx, ddelta, dA, dBt, dCt, dDskip (or None),
+        dz (or None), dstate_in."""
+        x = _c64(x)
+        batch, L, D = x.shape
+        A = _c64(A)
+        N = A.shape[1]
+        delta, Bt, Ct, dy = _c64(delta), _c64(Bt), _c64(Ct), _c64(dy)
+        assert delta.shape == x.shape and dy.shape == x.shape and Bt.shape == (batch, L, N) and Ct.shape == Bt.shape
+        opt = lambda a, shape: None if a is None else _c64(a).reshape(shape)
+        Dskip, z = opt(Dskip, (D,)), opt(z, x.shape)
+        state_in, dstate = opt(state_in, (batch, D, N)), opt(dstate, (batch, D, N))
+        out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty((D, N)),
+               "dBt": np.empty((batch, L, N)), "dCt": np.empty((batch, L, N)),
+               "dDskip": None if Dskip is None else np.empty(D), "dz": None if z is None else np.empty_like(x),
+               "dstate_in": np.empty((batch, D, N))}
+        rc = self.lib.oracle_scan_bwd(batch, L, D, N, _p(x), _p(delta), _p(A), _p(Bt), _p(Ct), _p(Dskip), _p(z),
+                                      _p(state_in), _p(dy), _p(dstate), _p(out["dx"]), _p(out["ddelta"]),
+                                      _p(out["dA"]), _p(out["dBt"]), _p(out["dCt"]), _p(out["dDskip"]),
+                                      _p(out["dz"]), _p(out["dstate_in"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd rejected sizes")
+        return out
+
     def softplus_bias64(self, raw, bias=None):
         """softplus(raw + bias[d]) over the last axis (D) of a float64 array."""
         raw = _c64(raw)
@@ -251,6 +278,13 @@ class Oracle:
         f32 = lambda a: None if a is None else upcast(a, "f32")
         return self.ssd64(up(inp["x"]), up(inp["delta"]), f32(inp["A"]), up(inp["Bt"]), up(inp["Ct"]),
                           f32(inp.get("Dskip")), f32(inp.get("state_in")), nthreads=nthreads)
+
+    def scan_bwd(self, inp: Dict[str, np.ndarray], dy, dstate, dtype: str):
+        """Gradient of the scan on stored inputs; dy in the stored dtype, dstate float32 or None."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        return self.scan_bwd64(up(inp["x"]), up(inp["delta"]), f32(inp["A"]), up(inp["Bt"]), up(inp["Ct"]),
+                               f32(inp.get("Dskip")), up(inp.get("z")), f32(inp.get("state_in")), up(dy), f32(dstate))
 
     def step(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
              nthreads: int = 0):

@@ -56,6 +56,12 @@
  * atenção mascarada", where the scalar transition a_t I and the recurrent
  * form of the dual are given).
  *
+ * oracle_scan_bwd is the gradient of the scan (reverse mode, by hand): the
+ * pages give the forward pass and say that the states are recomputed rather
+ * than stored for the backward ("Notas sobre Mamba", section "A varredura
+ * paralela ciente do hardware"); the gradient itself is the chain rule applied
+ * to the recurrence above, written out below.
+ *
  * Everything is float64 and uses libm exp()/log1p(); no fast-math, no
  * reordering of the token loop. OpenMP only splits independent (b, d) rows
  * across threads.
@@ -342,5 +348,92 @@ int oracle_ssd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_
             for (int64_t i = 0; i < P * N; ++i) state_out[r * P * N + i] = S[i];
         free(S);
     }
+    return 0;
+}
+
+/*
+ * Gradient of oracle_scan (all gates and options as there) for the loss
+ *   sum_{b,t,d} dy[b,t,d] * y[b,t,d]  +  sum_{b,d,n} dstate[b,d,n] * state_out[b,d,n]
+ * (dstate may be NULL = 0). Writes the gradient with respect to every input:
+ *   dx, ddelta, dz      : (batch, L, D)     (dz only when z is given)
+ *   dA                  : (D, N)
+ *   dBt, dCt            : (batch, L, N)
+ *   dDskip              : (D)              (only when Dskip is given)
+ *   dstate_in           : (batch, D, N)    (may be NULL)
+ * Per (b, d), with a_t[n] = exp(delta_t A[n]), s_t = sum_n C_t[n] h_t[n] + D x_t,
+ * g(z) = z sigmoid(z) and ds_t = dy_t g(z_t):
+ *   forward:  h_t = a_t h_{t-1} + delta_t B_t x_t          (kept for every t)
+ *   backward: G = dstate (or 0); for t = L-1 .. 0:
+ *     G[n]    += C_t[n] ds_t                  (G is now dLoss/dh_t)
+ *     dC_t[n] += ds_t h_t[n];  dD += ds_t x_t;  dx_t = ds_t D
+ *     dz_t     = dy_t s_t g'(z_t)
+ *     ddelta_t = sum_n G[n] (A[n] a_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *     dA[n]   += G[n] delta_t a_t[n] h_{t-1}[n]
+ *     dB_t[n] += G[n] delta_t x_t;  dx_t += sum_n G[n] delta_t B_t[n]
+ *     G[n]     = a_t[n] G[n]                  (dLoss/dh_{t-1} so far)
+ *   dstate_in = G.
+ * Single-threaded (dA, dB, dC and dD sum over rows). Returns 0, or -1 on a
+ * bad size or when memory runs out.
+ */
+int oracle_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N,
+                    const double *x, const double *delta, const double *A,
+                    const double *Bt, const double *Ct, const double *Dskip,
+                    const double *z, const double *state_in, const double *dy, const double *dstate,
+                    double *dx, double *ddelta, double *dA, double *dBt, double *dCt, double *dDskip,
+                    double *dz, double *dstate_in)
+{
+    if (batch < 0 || L < 0 || D < 0 || N < 1 || N > 4096) return -1;
+    double *H = (double *)malloc((size_t)((L + 1) * N) * sizeof(double));  /* H[(t + 1) N + n] = h_t */
+    if (!H) return -1;
+    for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
+    for (int64_t i = 0; i < batch * L * N; ++i) dBt[i] = dCt[i] = 0.0;
+    if (dDskip)
+        for (int64_t d = 0; d < D; ++d) dDskip[d] = 0.0;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            for (int64_t n = 0; n < N; ++n) H[n] = state_in ? state_in[IDX3(b, d, n, D, N)] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double dt = delta[IDX3(b, t, d, L, D)], u = x[IDX3(b, t, d, L, D)];
+                for (int64_t n = 0; n < N; ++n)
+                    H[(t + 1) * N + n] = exp(dt * A[d * N + n]) * H[t * N + n] + dt * Bt[IDX3(b, t, n, L, N)] * u;
+            }
+            double G[4096];
+            for (int64_t n = 0; n < N; ++n) G[n] = dstate ? dstate[IDX3(b, d, n, D, N)] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                int64_t r = IDX3(b, t, d, L, D);
+                double dt = delta[r], u = x[r];
+                double sum = 0.0;
+                for (int64_t n = 0; n < N; ++n) sum += Ct[IDX3(b, t, n, L, N)] * H[(t + 1) * N + n];
+                if (Dskip) sum += Dskip[d] * u;
+                double gate = 1.0, dgate = 0.0;
+                if (z) {
+                    double zz = z[r], sg = 1.0 / (1.0 + exp(-zz));
+                    gate = zz * sg;
+                    dgate = sg * (1.0 + zz * (1.0 - sg));
+                    dz[r] = dy[r] * sum * dgate;
+                }
+                double ds = dy[r] * gate;
+                double gx = Dskip ? ds * Dskip[d] : 0.0;
+                if (dDskip) dDskip[d] += ds * u;
+                double gd = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    int64_t bn = IDX3(b, t, n, L, N);
+                    G[n] += Ct[bn] * ds;
+                    dCt[bn] += ds * H[(t + 1) * N + n];
+                    double a = exp(dt * A[d * N + n]);
+                    double hp = H[t * N + n];
+                    gd += G[n] * (A[d * N + n] * a * hp + Bt[bn] * u);
+                    dA[d * N + n] += G[n] * dt * a * hp;
+                    dBt[bn] += G[n] * dt * u;
+                    gx += G[n] * dt * Bt[bn];
+                    G[n] *= a;
+                }
+                ddelta[r] = gd;
+                dx[r] = gx;
+            }
+            if (dstate_in)
+                for (int64_t n = 0; n < N; ++n) dstate_in[IDX3(b, d, n, D, N)] = G[n];
+        }
+    free(H);
     return 0;
 }

@@ -577,7 +577,64 @@ def pin_ssd_resume(o):
     assert np.allclose(s2, st, rtol=1e-12, atol=1e-13)
 
 
-ALL_PINS = [pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
+# --- the scan's gradient -------------------------------------------------------
+def _loss(o, p, dy, dstate):
+    y, st = _scan(o, p)
+    return float(np.sum(y * dy) + np.sum(st * dstate))
+
+
+def pin_bwd_finite_differences(o):
+    """Every gradient of the backward oracle against central differences of the
+    forward oracle's loss sum(dy * y) + sum(dstate * state_out), element by
+    element, on a tiny problem with every optional part."""
+    rng = np.random.default_rng(41)
+    batch, L, D, N = 2, 6, 3, 4
+    p = _rand_problem(rng, batch, L, D, N)
+    dy, dstate = rng.normal(size=(batch, L, D)), rng.normal(size=(batch, D, N))
+    g = o.scan_bwd64(p["x"], p["delta"], p["A"], p["Bt"], p["Ct"], p["Dskip"], p["z"], p["state_in"], dy, dstate)
+    names = {"x": "dx", "delta": "ddelta", "A": "dA", "Bt": "dBt", "Ct": "dCt", "Dskip": "dDskip", "z": "dz",
+             "state_in": "dstate_in"}
+    for k, gk in names.items():
+        base = p[k]
+        num = np.empty_like(base)
+        for i in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[i]))
+            q = dict(p)
+            q[k] = base.copy()
+            q[k][i] = base[i] + eps
+            up = _loss(o, q, dy, dstate)
+            q[k][i] = base[i] - eps
+            dn = _loss(o, q, dy, dstate)
+            num[i] = (up - dn) / (2 * eps)
+        assert np.allclose(g[gk], num, rtol=1e-6, atol=1e-7), (k, np.abs(g[gk] - num).max())
+
+
+def pin_bwd_adjoint_identities(o):
+    """y is linear in x (zero carried-in state), and, without the skip term,
+    in Bt, in Ct and in the carried-in state (x = 0 for the last): for each,
+    <dy, J v> = <J^T dy, v> exactly, which pins dx, dBt, dCt and dstate_in to
+    rounding at a larger size."""
+    rng = np.random.default_rng(42)
+    batch, L, D, N = 2, 40, 5, 6
+    p = _rand_problem(rng, batch, L, D, N, state=False)
+    dy = rng.normal(size=(batch, L, D))
+    for k, gk, skip in (("x", "dx", True), ("Bt", "dBt", False), ("Ct", "dCt", False)):
+        q = dict(p, Dskip=p["Dskip"] if skip else None)
+        g = o.scan_bwd64(q["x"], q["delta"], q["A"], q["Bt"], q["Ct"], q["Dskip"], q["z"], None, dy)
+        v = rng.normal(size=p[k].shape)
+        q[k] = v
+        y, _ = _scan(o, q)
+        lhs, rhs = float(np.sum(dy * y)), float(np.sum(g[gk] * v))
+        assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs)), (k, lhs, rhs)
+    # the carried-in state, with x = 0 (and no skip contribution then)
+    q = dict(p, x=np.zeros_like(p["x"]), state_in=rng.normal(size=(batch, D, N)))
+    g = o.scan_bwd64(q["x"], q["delta"], q["A"], q["Bt"], q["Ct"], q["Dskip"], q["z"], q["state_in"], dy)
+    y, _ = _scan(o, q)
+    lhs, rhs = float(np.sum(dy * y)), float(np.sum(g["dstate_in"] * q["state_in"]))
+    assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs)), (lhs, rhs)
+
+
+ALL_PINS = [pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
             pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,

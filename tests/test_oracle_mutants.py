@@ -63,6 +63,13 @@ MUTANTS = [
     ("trap_earlier_B_batch_row_0", "B_prev[b * N + n] * x_prev[b * D + d]", "B_prev[n] * x_prev[b * D + d]"),
     ("trap_lam_previous_token", "double lm = lam[IDX3(b, t, d, L, D)];",
      "double lm = lam[IDX3(b, t > 0 ? t - 1 : 0, d, L, D)];"),
+    ("bwd_state_grad_not_decayed", "                    G[n] *= a;\n", ""),
+    ("bwd_delta_misses_input_term", "gd += G[n] * (A[d * N + n] * a * hp + Bt[bn] * u);", "gd += G[n] * (A[d * N + n] * a * hp);"),
+    ("bwd_dA_without_delta", "dA[d * N + n] += G[n] * dt * a * hp;", "dA[d * N + n] += G[n] * a * hp;"),
+    ("bwd_dC_uses_previous_state", "dCt[bn] += ds * H[(t + 1) * N + n];", "dCt[bn] += ds * H[t * N + n];"),
+    ("bwd_gate_derivative_sigmoid_only", "dgate = sg * (1.0 + zz * (1.0 - sg));", "dgate = sg;"),
+    ("bwd_skip_grad_missing", "double gx = Dskip ? ds * Dskip[d] : 0.0;", "double gx = 0.0;"),
+    ("bwd_readout_grad_after_decay", "                    G[n] += Ct[bn] * ds;\n", ""),
     ("ssd_group_modulo", "g = h / (H / G);", "g = h % G;"),
     ("ssd_input_without_delta", "+ dt * xt[p] * Bg[n];", "+ xt[p] * Bg[n];"),
     ("ssd_decay_of_group", "double a = exp(dt * A[h]);", "double a = exp(dt * A[g]);"),
@@ -88,4 +95,5 @@ def test_mutant_is_caught(name, old, new, tmp_path):
             pin(o)
         except (AssertionError, FloatingPointError, ValueError) as e:  # a pin tripped
             failed.append(pin.__name__)
+            break
     assert failed, "no pin caught mutant " + name
