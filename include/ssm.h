@@ -261,6 +261,55 @@ int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64
                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
                 const float *Dskip, const float *state_in, float *state_out, void *y, void *stream);
 
+/*
+ * Scratch bytes ssm_scan_bwd needs for these sizes (0 for empty or invalid
+ * sizes). The gradient cuts the sequence into chunks of 32 tokens; the
+ * workspace holds, per (batch row, chunk, channel), the state and the
+ * gradient entering the chunk and the chunk's summed delta, and the partial
+ * sums of dBt, dCt (per 64 channels), dA and dDskip (per chunk). It needs no
+ * clearing: every word is written before it is read within one call. Calls
+ * that share a workspace must not run at the same time.
+ */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
+
+/*
+ * Gradient of ssm_scan_fwd (the Euler rule, delta given after its activation)
+ * for the loss sum(dy * y) + sum(dstate * state_out). The pages give the
+ * forward recurrence and recompute its states in the backward pass instead of
+ * storing them ("Notas sobre Mamba", section "A varredura paralela ciente do
+ * hardware"); the gradient is the chain rule through that recurrence. With
+ * dA_t = exp(delta_t A) and s_t = silu(z_t) (1 without a gate), the gradient
+ * of the state runs backwards,
+ *
+ *   G_t = Ct[t] * dy_t s_t + dA_{t+1} * G_{t+1},      G_{L-1} includes dstate,
+ *
+ * and every input's gradient follows from G and the recomputed states.
+ *
+ *   x, delta, A, Bt, Ct, Dskip, z, state_in   as passed to ssm_scan_fwd
+ *   dy            (batch, L, D)  dtype      gradient of y
+ *   dstate        (batch, D, N)  float      gradient of state_out; NULL = zeros
+ *   dx, ddelta    (batch, L, D)  dtype      written
+ *   dA            (D, N)         float      written (summed over batch and tokens)
+ *   dBt, dCt      (batch, L, N)  float      written (summed over channels)
+ *   dDskip        (D)            float      written when Dskip and dDskip are
+ *                                           both given; NULL = not written
+ *   dz            (batch, L, D)  dtype      written; required when z is given
+ *   dstate_in     (batch, D, N)  float      gradient of state_in (of the zero
+ *                                           start when state_in is NULL);
+ *                                           NULL = not written; may equal dstate
+ *   workspace     ssm_scan_bwd_workspace_bytes() bytes of device memory
+ *
+ * Every sum runs in a fixed order, so equal inputs give equal bits. L = 0 or
+ * batch = 0 writes zeros to dA (and dDskip) and copies dstate to dstate_in.
+ * Status codes as in ssm_scan_fwd; a missing required output is SSM_ERR_NULL.
+ */
+int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                 const float *Dskip, const void *z, const float *state_in,
+                 const void *dy, const float *dstate,
+                 void *dx, void *ddelta, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
+                 float *dstate_in, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

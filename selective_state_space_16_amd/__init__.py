@@ -16,7 +16,11 @@ Functions (same names as the C ABI):
   ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None,
               y=None) -> y: the Mamba-2 SSD layer (x (batch, L, H, P), Bt/Ct
       (batch, L, G, N), bfloat16)
+  ssm_scan_bwd(x, delta, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None,
+               dstate=None) -> dict: the gradient of ssm_scan_fwd (dx, ddelta,
+      dA, dBt, dCt, dDskip, dz, dstate_in)
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
+  ssm_scan_bwd_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
 """
 from __future__ import annotations
@@ -27,7 +31,8 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
+    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
+    "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
 
@@ -41,7 +46,8 @@ lib_path = os.path.join(_HERE, "libssm.so")
 
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
-           "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd")
+           "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -82,6 +88,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_step_trap.restype = ci
     L.ssm_ssd_fwd.argtypes = [i64] * 6 + [ci] + [vp] * 9 + [vp]
     L.ssm_ssd_fwd.restype = ci
+    L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    L.ssm_scan_bwd_workspace_bytes.restype = sz
+    L.ssm_scan_bwd.argtypes = [i64, i64, i64, i64, ci] + [vp] * 18 + [vp, sz, vp]
+    L.ssm_scan_bwd.restype = ci
     _lib = L
     return L
 
@@ -96,6 +106,10 @@ def ssm_version() -> str:
 
 def ssm_scan_workspace_bytes(batch: int, L: int, D: int, N: int, dtype: int) -> int:
     return int(lib().ssm_scan_workspace_bytes(batch, L, D, N, dtype))
+
+
+def ssm_scan_bwd_workspace_bytes(batch: int, L: int, D: int, N: int, dtype: int) -> int:
+    return int(lib().ssm_scan_bwd_workspace_bytes(batch, L, D, N, dtype))
 
 
 def new_workspace(nbytes: int, device="cuda"):
@@ -283,3 +297,47 @@ def ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None, 
     if st != 0:
         raise SSMError(st, "ssm_ssd_fwd")
     return y
+
+
+def ssm_scan_bwd(x, delta, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None, dstate=None, out=None,
+                 workspace=None, stream=None):
+    """Gradient of ssm_scan_fwd for the loss sum(dy * y) + sum(dstate * state_out).
+    Inputs as for ssm_scan_fwd; dy like x; dstate (batch, D, N) float32 or None.
+    Returns a dict: dx, ddelta, dz (like x; dz None without a gate), dA (D, N),
+    dBt, dCt (batch, L, N), dDskip (D,) or None, dstate_in (batch, D, N), all
+    float32 but the first three. `out` may hold preallocated outputs by those names."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and A (D, N)")
+    batch, L, D = x.shape
+    N = A.shape[1]
+    act, f32 = x.dtype, torch.float32
+    code = _dtype_code(x)
+    o = dict(out or {})
+    new = lambda shape, dt: torch.empty(shape, dtype=dt, device=x.device)
+    o.setdefault("dx", torch.empty_like(x))
+    o.setdefault("ddelta", torch.empty_like(x))
+    o.setdefault("dz", None if z is None else torch.empty_like(x))
+    o.setdefault("dA", new((D, N), f32))
+    o.setdefault("dBt", new((batch, L, N), f32))
+    o.setdefault("dCt", new((batch, L, N), f32))
+    o.setdefault("dDskip", None if Dskip is None else new((D,), f32))
+    o.setdefault("dstate_in", new((batch, D, N), f32))
+    ws_bytes = ssm_scan_bwd_workspace_bytes(batch, L, D, N, code)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(A, "A", f32, (D, N)),
+            _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
+            _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+            _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(dy, "dy", act, (batch, L, D)),
+            _ptr(dstate, "dstate", f32, (batch, D, N)),
+            _ptr(o["dx"], "dx", act, (batch, L, D)), _ptr(o["ddelta"], "ddelta", act, (batch, L, D)),
+            _ptr(o["dA"], "dA", f32, (D, N)), _ptr(o["dBt"], "dBt", f32, (batch, L, N)),
+            _ptr(o["dCt"], "dCt", f32, (batch, L, N)), _ptr(o["dDskip"], "dDskip", f32, (D,)),
+            _ptr(o["dz"], "dz", act, (batch, L, D)), _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
+    ws_ptr = _ptr(workspace, "workspace")
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_scan_bwd(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_scan_bwd")
+    return o

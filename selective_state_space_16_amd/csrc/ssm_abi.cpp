@@ -303,6 +303,129 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
     return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
+// Workspace of the gradient: [header | hst | dsum | gq | rsum | pdB | pdC | pdA | pdD].
+struct BwdLayout {
+    int64_t K;
+    size_t off[8], bytes;
+};
+
+static BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    BwdLayout w{};
+    w.K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
+    const int64_t nDB = ssm::bwd_channel_blocks(D, N);
+    const size_t sz[8] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
+                          (size_t)(batch * w.K * D),     (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
+                          (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D)};
+    size_t off = kHeader;
+    for (int i = 0; i < 8; ++i) {
+        w.off[i] = off;
+        off += round_up256(sz[i] * sizeof(float));
+    }
+    w.bytes = off;
+    return w;
+}
+
+// Sizes the gradient accepts: every count within kMaxElems and every flat
+// grid within 2^32 work-items.
+static bool bwd_sizes_ok(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    const int64_t K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
+    if (checked_mul3(batch, L, D) < 0 || checked_mul3(batch, L, N) < 0 || checked_mul3(batch, D, N) < 0)
+        return false;
+    const int64_t nDB = ssm::bwd_channel_blocks(D, N);
+    if (checked_mul3(checked_mul(batch, K), D, N) < 0 || checked_mul3(checked_mul(nDB, batch), L, N) < 0)
+        return false;
+    const int64_t blocks = checked_mul3(nDB, K, batch);
+    return blocks >= 0 && blocks < ((int64_t)1 << 24);
+}
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
+    if (batch <= 0 || L <= 0 || D <= 0 || !supported_n(N)) return 0;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+    if (!bwd_sizes_ok(batch, L, D, N)) return 0;
+    return bwd_layout(batch, L, D, N).bytes;
+}
+
+int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                 const float *Dskip, const void *z, const float *state_in,
+                 const void *dy, const float *dstate,
+                 void *dx, void *ddelta, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
+                 float *dstate_in, void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
+    if (!bwd_sizes_ok(batch, L, D, N)) return SSM_ERR_SHAPE;
+    if (D > 0 && !dA) return SSM_ERR_NULL;
+    if (z && !dz) return SSM_ERR_NULL;
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx, ddelta,
+                          dA, dBt, dCt, dDskip, dz, dstate_in, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (D == 0) return SSM_OK;
+    if (batch == 0 || L == 0) {
+        // nothing flows through the tokens: the parameter gradients are zero
+        // and the gradient of the entering state is that of the leaving one
+        if (ssm::launch_state_copy(nullptr, dA, D * N, s) != hipSuccess) return SSM_ERR_HIP;
+        if (Dskip && dDskip && ssm::launch_state_copy(nullptr, dDskip, D, s) != hipSuccess) return SSM_ERR_HIP;
+        if (dstate_in && dstate_in != dstate &&
+            ssm::launch_state_copy(dstate, dstate_in, batch * D * N, s) != hipSuccess)
+            return SSM_ERR_HIP;
+        return SSM_OK;
+    }
+    if (!x || !delta || !A || !Bt || !Ct || !dy || !dx || !ddelta || !dBt || !dCt) return SSM_ERR_NULL;
+    const BwdLayout w = bwd_layout(batch, L, D, N);
+    if (!workspace || workspace_bytes < w.bytes) return SSM_ERR_WORKSPACE;
+    char *ws = (char *)workspace;
+    ssm::ScanArgs f{};
+    f.batch = batch;
+    f.L = L;
+    f.D = D;
+    f.x = x;
+    f.delta = delta;
+    f.Bt = Bt;
+    f.Ct = Ct;
+    f.A = A;
+    f.state_in = state_in;
+    f.K = w.K;
+    f.Lc = ssm::kBwdChunk;
+    f.ws_state = (float *)(ws + w.off[0]);
+    f.ws_dsum = (float *)(ws + w.off[1]);
+    if (ssm::launch_scan_states(f, (int)N, dtype, s) != hipSuccess) return SSM_ERR_HIP;
+    ssm::BwdArgs a{};
+    a.batch = batch;
+    a.L = L;
+    a.D = D;
+    a.K = w.K;
+    a.x = x;
+    a.delta = delta;
+    a.Bt = Bt;
+    a.Ct = Ct;
+    a.z = z;
+    a.dy = dy;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.state_in = state_in;
+    a.dstate = dstate;
+    a.dx = dx;
+    a.ddelta = ddelta;
+    a.dz = dz;
+    a.dA = dA;
+    a.dBt = dBt;
+    a.dCt = dCt;
+    a.dDskip = Dskip ? dDskip : nullptr;
+    a.dstate_in = dstate_in;
+    a.hst = f.ws_state;
+    a.dsum = f.ws_dsum;
+    a.gq = (float *)(ws + w.off[2]);
+    a.rsum = (float *)(ws + w.off[3]);
+    a.pdB = (float *)(ws + w.off[4]);
+    a.pdC = (float *)(ws + w.off[5]);
+    a.pdA = (float *)(ws + w.off[6]);
+    a.pdD = (float *)(ws + w.off[7]);
+    return ssm::launch_scan_bwd(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
                 const float *Dskip, const float *state_in, float *state_out, void *y, void *stream) {

@@ -81,6 +81,35 @@ struct SsdArgs {
 bool ssd_supported(int64_t P, int64_t N);
 hipError_t launch_ssd(const SsdArgs &a, int N, hipStream_t s);
 
+// Gradient of the scan (Euler rule, delta after its activation). Pointers are
+// device pointers; dx, ddelta, dz in the activation dtype, the rest float.
+constexpr int64_t kBwdChunk = 32;  // tokens per chunk of the gradient
+struct BwdArgs {
+    int64_t batch, L, D, K;  // K = ceil(L / kBwdChunk) chunks
+    const void *x, *delta, *Bt, *Ct, *z, *dy;
+    const float *A, *Dskip, *state_in, *dstate;
+    void *dx, *ddelta, *dz;
+    float *dA, *dBt, *dCt, *dDskip, *dstate_in;
+    // workspace
+    float *hst;         // (batch, K, D, N) state entering each chunk
+    float *dsum;        // (batch, K, D)    summed delta per chunk
+    float *gq;          // (batch, K, D, N) gradient entering each chunk from its end
+    float *rsum;        // (batch, K, D)    summed delta per chunk (reverse pass)
+    float *pdB, *pdC;   // (bwd_channel_blocks, batch, L, N) per-block partial sums
+    float *pdA;         // (batch, K, D, N) per-chunk partial sums
+    float *pdD;         // (batch, K, D)
+};
+hipError_t launch_scan_bwd(const BwdArgs &a, int N, int dtype, hipStream_t s);
+// Channel blocks of the gradient's chunk kernel (256 lanes; two lanes per
+// channel when N = 16): the number of partials of dBt and dCt.
+inline int64_t bwd_channel_blocks(int64_t D, int64_t N) {
+    const int64_t cpb = N > 8 ? 256 / (N / 8) : 256;
+    return (D + cpb - 1) / cpb;
+}
+// Summary and carry launches of the chunked scan: the state entering every
+// chunk into a.ws_state (used by the gradient).
+hipError_t launch_scan_states(const ScanArgs &a, int N, int dtype, hipStream_t s);
+
 // Sequence split used for a scan of these sizes (deterministic).
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);
 

@@ -1,0 +1,351 @@
+// Gradient of the selective scan (S6) for gfx950.
+//
+// The loss is sum(dy * y) + sum(dstate * state_out). Per (batch row b,
+// channel d), with a_t = exp(delta_t A), h_t = a_t h_{t-1} + delta_t B_t x_t and
+// the gradient G_t = dLoss/dh_t, the chain rule gives
+//
+//   G_t = C_t ds_t + a_{t+1} G_{t+1},        ds_t = dy_t silu(z_t),
+//
+// a linear recurrence run backwards in t. The states are recomputed rather
+// than stored ("Notas sobre Mamba", section "A varredura paralela ciente do
+// hardware": the backward recomputes the intermediate states), so nothing of
+// size (batch, L, D, N) is written. The sequence is cut into chunks of 32
+// tokens:
+//   1. the forward chunk summaries and their carry give the state entering
+//      every chunk (the kernels of the forward scan, ssm_scan.hip);
+//   2. a reverse summary per chunk: G at the chunk's first token, times its
+//      a_t, from a zero gradient at the chunk's end, and the chunk's summed
+//      delta;
+//   3. a reverse carry per (b, d, n) over the chunks, from dstate at the end:
+//      the gradient entering every chunk from the tokens after it;
+//   4. per chunk, from its entering state and gradient: the states again at
+//      8-token checkpoints, then token by token backwards, every gradient.
+//      dB and dC sum over the channels: exchanges within each wave, then LDS
+//      across the block's waves, one partial per block of channels; dA and dD
+//      sum over (b, t): one partial per (b, chunk);
+//   5. the partials are summed, in a fixed order.
+#include "ssm_common.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kSub = 8;  // tokens per recomputed block
+
+// silu(z) and its derivative sigmoid(z) (1 + z (1 - sigmoid(z))).
+__device__ __forceinline__ void silu_and_grad(float z, float &g, float &dg) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * kLog2e));
+    g = z * sg;
+    dg = sg * (1.0f + z * (1.0f - sg));
+}
+
+// Sum of v[0..N) over the lanes of a wave that share bit SPAN and above
+// (SPAN = 64: the whole wave). The halving exchanges leave lane l with the
+// sum, over N lanes, of one element, named by the bits of l below log2(N);
+// the remaining exchanges add the lanes that hold the same element. Returns
+// that sum.
+template <int N, int SPAN>
+__device__ __forceinline__ float wave_sum_vec(float (&v)[N], int lane) {
+#pragma unroll
+    for (int half = N / 2, bit = 1; half >= 1; half /= 2, bit *= 2) {
+        const bool upper = (lane & bit) != 0;  // keeps the upper half of the current vector
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = upper ? v[i] : v[i + half];
+            const float keep = upper ? v[i + half] : v[i];
+            v[i] = keep + __shfl_xor(send, bit);
+        }
+    }
+    float s = v[0];
+#pragma unroll
+    for (int bit = N; bit < SPAN; bit *= 2) s += __shfl_xor(s, bit);
+    return s;
+}
+
+// The element of v that wave_sum_vec<N, SPAN> leaves in lane `lane`.
+template <int N>
+__device__ __forceinline__ int wave_sum_index(int lane) {
+    int idx = 0;
+#pragma unroll
+    for (int half = N / 2, bit = 1; half >= 1; half /= 2, bit *= 2)
+        if (lane & bit) idx += half;
+    return idx;
+}
+
+// 2. reverse summaries: per (b, chunk k >= 1, channel), G entering token t0 - 1
+// from a zero gradient at the chunk's end, and the chunk's summed delta.
+template <int N, int DT, bool GATE>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rev_summary_kernel(BwdArgs a) {
+    using T = typename Act<DT>::T;
+    const int64_t D = a.D, L = a.L, K = a.K;
+    // flat grid: block id = (b * (K - 1) + k - 1) * channel_blocks + channel_block
+    const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads, bid = blockIdx.x;
+    const int64_t d = (bid % nb) * kBwdThreads + threadIdx.x;
+    const int64_t k = (bid / nb) % (K - 1) + 1, b = bid / (nb * (K - 1));
+    const bool valid = d < D;
+    const int64_t dc = valid ? d : D - 1;
+    const int64_t t0 = k * kBwdChunk, t1 = t0 + kBwdChunk < L ? t0 + kBwdChunk : L;
+    float A2[N], G[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[dc * N + n] * kLog2e;
+        G[n] = 0.0f;
+    }
+    const T *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
+    const T *Cp = (const T *)a.Ct;
+    float dsum = 0.0f;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        const int64_t row = (b * L + t) * D + dc;
+        const float dt = ld_act(dp, row);
+        float ds = ld_act(gp, row);
+        if (GATE) {
+            float g, dg;
+            silu_and_grad(ld_act(zp, row), g, dg);
+            ds *= g;
+        }
+        float Cv[N];
+        ld_row_uniform<N>(Cp, (b * L + t) * N, Cv);
+        dsum += dt;
+#pragma unroll
+        for (int n = 0; n < N; ++n) G[n] = fast_exp2(dt * A2[n]) * __builtin_fmaf(Cv[n], ds, G[n]);
+    }
+    if (!valid) return;
+    float *dst = a.gq + ((b * K + k) * D + d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) dst[n] = G[n];
+    a.rsum[(b * K + k) * D + d] = dsum;
+}
+
+// 3. reverse carry: per (b, d, n), replace each chunk's reverse summary by the
+// gradient entering the chunk from the tokens after it; the gradient leaving
+// chunk 0 is dstate_in.
+template <int N>
+__global__ __launch_bounds__(256) void bwd_rev_carry_kernel(BwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t D = a.D, K = a.K;
+    if (i >= a.batch * D * N) return;
+    const int64_t n = i % N, d = (i / N) % D, b = i / ((int64_t)N * D);
+    const float A2 = a.A[d * N + n] * kLog2e;
+    float q = a.dstate ? a.dstate[i] : 0.0f;
+    for (int64_t k = K - 1; k >= 0; --k) {
+        float *slot = a.gq + ((b * K + k) * D + d) * N + n;
+        const float r = k > 0 ? *slot : 0.0f;
+        *slot = q;
+        if (k > 0) q = __builtin_fmaf(fast_exp2(A2 * a.rsum[(b * K + k) * D + d]), q, r);
+    }
+}
+
+// 4. the gradients of one chunk, for one batch row and a block of channels.
+// N <= 8: a lane owns a channel and its N state elements. N = 16: two lanes
+// own a channel, 8 elements each (lanes l and l + 32 of a wave), so that the
+// recomputed states of 8 tokens fit in registers; their per-channel sums meet
+// through one exchange. Bt and Ct of the chunk are staged in LDS.
+template <int N, int DT, bool GATE, bool SKIP>
+__global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
+    using T = typename Act<DT>::T;
+    constexpr int NP = N < 8 ? N : 8;        // state elements per lane
+    constexpr int R = N / NP;                // lanes per channel
+    constexpr int SPAN = 64 / R;             // channels per wave
+    constexpr int CPB = kBwdThreads / R;     // channels per block
+    constexpr int NCK = kBwdChunk / kSub;    // checkpoints per chunk
+    constexpr int NW = kBwdThreads / 64;     // waves per block
+    __shared__ float sB[kBwdChunk][N], sC[kBwdChunk][N];
+    __shared__ float ck[NCK][NP][kBwdThreads];   // state entering each block of kSub tokens
+    __shared__ float red[2][NW][kSub][N];        // per-wave sums of dCt, dBt
+    const int64_t D = a.D, L = a.L, K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = R == 1 ? 0 : lane / SPAN, cl = lane % SPAN;
+    // flat grid: block id = (b * K + k) * channel_blocks + channel_block
+    const int64_t nb = (D + CPB - 1) / CPB, bid = blockIdx.x;
+    const int64_t cb = bid % nb, k = (bid / nb) % K, b = bid / (nb * K);
+    const int64_t d = cb * CPB + w * SPAN + cl;
+    const bool valid = d < D;
+    const int64_t dc = valid ? d : D - 1;
+    const int64_t t0 = k * kBwdChunk, t1 = t0 + kBwdChunk < L ? t0 + kBwdChunk : L;
+    const int cnt_chunk = (int)(t1 - t0);
+    const T *xp = (const T *)a.x, *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
+    for (int i = tid; i < kBwdChunk * N; i += kBwdThreads) {
+        const int j = i / N, n = i % N;
+        const bool in = j < cnt_chunk;
+        const int64_t o = (b * L + t0 + (in ? j : 0)) * N + n;
+        sB[j][n] = in ? ld_act((const T *)a.Bt, o) : 0.0f;
+        sC[j][n] = in ? ld_act((const T *)a.Ct, o) : 0.0f;
+    }
+    const int n0 = r * NP;  // first state element of this lane
+    float A2[NP], h[NP], G[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        A2[i] = a.A[dc * N + n0 + i] * kLog2e;
+        h[i] = a.hst[((b * K + k) * D + dc) * N + n0 + i];
+        G[i] = a.gq[((b * K + k) * D + dc) * N + n0 + i];
+    }
+    __syncthreads();
+    // forward through the chunk, keeping the state entering each block
+    for (int j = 0; j < cnt_chunk; ++j) {
+        if (j % kSub == 0) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) ck[j / kSub][i][tid] = h[i];
+        }
+        const int64_t row = (b * L + t0 + j) * D + dc;
+        const float dt = ld_act(dp, row), dx = dt * ld_act(xp, row);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), h[i], dx * sB[j][n0 + i]);
+    }
+    float dA[NP], dD = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) dA[i] = 0.0f;
+    const float dsk = SKIP ? a.Dskip[dc] : 0.0f;
+    const int elem = n0 + wave_sum_index<NP>(cl);  // element this lane holds after the channel sums
+    const int nblk = (cnt_chunk + kSub - 1) / kSub;
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int s0 = blk * kSub;
+        const int cnt = cnt_chunk - s0 < kSub ? cnt_chunk - s0 : kSub;
+        // states of the block: hb[j] = state entering token s0 + j
+        float hb[kSub + 1][NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) hb[0][i] = ck[blk][i][tid];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            if (j < cnt) {
+                const int64_t row = (b * L + t0 + s0 + j) * D + dc;
+                const float dt = ld_act(dp, row), dx = dt * ld_act(xp, row);
+#pragma unroll
+                for (int i = 0; i < NP; ++i)
+                    hb[j + 1][i] = __builtin_fmaf(fast_exp2(dt * A2[i]), hb[j][i], dx * sB[s0 + j][n0 + i]);
+            }
+        }
+#pragma unroll
+        for (int j = kSub - 1; j >= 0; --j) {
+            if (j >= cnt) continue;
+            const int tl = s0 + j;
+            const int64_t row = (b * L + t0 + tl) * D + dc;
+            const float dt = ld_act(dp, row), xv = ld_act(xp, row), dyv = ld_act(gp, row);
+            float gate = 1.0f, dgate = 0.0f;
+            if (GATE) silu_and_grad(ld_act(zp, row), gate, dgate);
+            const float ds = valid ? dyv * gate : 0.0f;
+            float pre = 0.0f, gdt = 0.0f, gx = 0.0f, dCv[NP], dBv[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const float Cv = sC[tl][n0 + i], Bv = sB[tl][n0 + i];
+                pre = __builtin_fmaf(Cv, hb[j + 1][i], pre);
+                G[i] = __builtin_fmaf(Cv, ds, G[i]);
+                dCv[i] = ds * hb[j + 1][i];
+                const float av = fast_exp2(dt * A2[i]);
+                const float gah = G[i] * av * hb[j][i];
+                gdt = __builtin_fmaf(gah * kLn2, A2[i], __builtin_fmaf(G[i] * Bv, xv, gdt));
+                dA[i] = __builtin_fmaf(gah, dt, dA[i]);
+                dBv[i] = valid ? G[i] * dt * xv : 0.0f;
+                gx = __builtin_fmaf(G[i] * dt, Bv, gx);
+                G[i] *= av;
+            }
+            if (R == 2) {  // the other half of the channel's state elements
+                pre += __shfl_xor(pre, SPAN);
+                gdt += __shfl_xor(gdt, SPAN);
+                gx += __shfl_xor(gx, SPAN);
+            }
+            if (SKIP) {
+                pre = __builtin_fmaf(dsk, xv, pre);
+                gx = __builtin_fmaf(ds, dsk, gx);
+            }
+            dD = __builtin_fmaf(ds, xv, dD);
+            if (valid && r == 0) {
+                st_act((T *)a.dx, row, gx);
+                st_act((T *)a.ddelta, row, gdt);
+                if (GATE) st_act((T *)a.dz, row, dyv * pre * dgate);
+            }
+            const float sc = wave_sum_vec<NP, SPAN>(dCv, lane);
+            const float sb = wave_sum_vec<NP, SPAN>(dBv, lane);
+            if (cl < NP) {
+                red[0][w][j][elem] = sc;
+                red[1][w][j][elem] = sb;
+            }
+        }
+        __syncthreads();
+        // the block's sums over its channels, one partial per channel block
+        for (int i = tid; i < 2 * kSub * N; i += kBwdThreads) {
+            const int which = i / (kSub * N), j = (i / N) % kSub, n = i % N;
+            if (j < cnt) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) sum += red[which][v][j][n];
+                float *dst = which == 0 ? a.pdC : a.pdB;
+                dst[((cb * a.batch + b) * L + t0 + s0 + j) * N + n] = sum;
+            }
+        }
+        __syncthreads();
+    }
+    if (!valid) return;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) a.pdA[((b * K + k) * D + d) * N + n0 + i] = dA[i];
+    if (r == 0) a.pdD[(b * K + k) * D + d] = dD;
+    if (k == 0 && a.dstate_in) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) a.dstate_in[(b * D + d) * N + n0 + i] = G[i];
+    }
+}
+
+// 5. the sums of the partials, in a fixed order.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part, int64_t nparts, int64_t stride,
+                                                         float *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int64_t p = 0; p < nparts; ++p) s += part[p * stride + i];
+    out[i] = s;
+}
+
+template <int N, int DT, bool GATE, bool SKIP>
+hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
+    const int64_t D = a.D, K = a.K;
+    const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads;
+    if (K > 1)
+        hipLaunchKernelGGL((bwd_rev_summary_kernel<N, DT, GATE>), dim3((unsigned)(nb * (K - 1) * a.batch)),
+                           dim3(kBwdThreads), 0, s, a);
+    const int64_t total = a.batch * D * N;
+    hipLaunchKernelGGL((bwd_rev_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    const int64_t ncb = bwd_channel_blocks(D, N);
+    hipLaunchKernelGGL((bwd_chunk_kernel<N, DT, GATE, SKIP>), dim3((unsigned)(ncb * K * a.batch)),
+                       dim3(kBwdThreads), 0, s, a);
+    const int64_t nDB = ncb, bln = a.batch * a.L * N;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdB, nDB, bln,
+                       a.dBt, bln);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdC, nDB, bln,
+                       a.dCt, bln);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D * N + 255) / 256)), dim3(256), 0, s, a.pdA,
+                       a.batch * K, D * N, a.dA, D * N);
+    if (a.dDskip)
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0, s, a.pdD, a.batch * K,
+                           D, a.dDskip, D);
+    return hipGetLastError();
+}
+
+template <int N, int DT>
+hipError_t launch_bwd_flags(const BwdArgs &a, hipStream_t s) {
+    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
+    if (gate && skip) return launch_bwd_typed<N, DT, true, true>(a, s);
+    if (gate) return launch_bwd_typed<N, DT, true, false>(a, s);
+    if (skip) return launch_bwd_typed<N, DT, false, true>(a, s);
+    return launch_bwd_typed<N, DT, false, false>(a, s);
+}
+
+template <int N>
+hipError_t launch_bwd_dtype(const BwdArgs &a, int dtype, hipStream_t s) {
+    return dtype == 0 ? launch_bwd_flags<N, 0>(a, s) : launch_bwd_flags<N, 1>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdArgs &a, int N, int dtype, hipStream_t s) {
+    switch (N) {
+        case 1: return launch_bwd_dtype<1>(a, dtype, s);
+        case 2: return launch_bwd_dtype<2>(a, dtype, s);
+        case 4: return launch_bwd_dtype<4>(a, dtype, s);
+        case 8: return launch_bwd_dtype<8>(a, dtype, s);
+        case 16: return launch_bwd_dtype<16>(a, dtype, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssm

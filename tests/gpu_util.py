@@ -127,3 +127,42 @@ def gpu_ssd(inp, want_state=True):
                         state_in=dev["state_in"], state_out=st_out)
     torch.cuda.synchronize()
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
+
+
+def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False):
+    """Run ssm_scan_bwd on stored inputs and upstream gradients; returns a dict
+    of float64 arrays with the oracle's keys (dDskip/dz None when absent)."""
+    import torch
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    dy, dstate = to_dev(grads["dy"]), to_dev(grads.get("dstate"))
+    out = {}
+    if dstate_alias and dstate is not None:
+        out["dstate_in"] = dstate
+    if not want_dskip:
+        out["dDskip"] = None
+    g = ssm.ssm_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], dy, Dskip=dev["Dskip"],
+                         z=dev["z"], state_in=dev["state_in"], dstate=dstate, out=out)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else to_f64(v)) for k, v in g.items()}
+
+
+def oracle_scan_bwd(inp, grads, dtype):
+    return oracle.get().scan_bwd(inp, grads["dy"], grads.get("dstate"), dtype)
+
+
+def check_grads(got, ref, dtype, keys=None):
+    """Every gradient against the oracle's: relative L2 as for the outputs;
+    for float32, max-abs 1e-4 scaled by the largest reference magnitude (the
+    parameter gradients are sums over many tokens and channels)."""
+    for k in keys or ("dx", "ddelta", "dz", "dA", "dBt", "dCt", "dDskip", "dstate_in"):
+        if ref.get(k) is None:
+            assert got.get(k) is None, k + " written but not expected"
+            continue
+        g, r = got[k], ref[k]
+        rel, mx = errors(g, r)
+        scale = max(1.0, float(np.abs(r).max()) if r.size else 1.0)
+        say(f"  {k}: relL2={rel:.3e} maxabs={mx:.3e} (scale {scale:.3g})")
+        assert np.all(np.isfinite(g)), k + ": non-finite output"
+        assert rel <= TOL[dtype]["rel"], f"{k}: relL2 {rel:.3e} > {TOL[dtype]['rel']}"
+        if TOL[dtype]["maxabs"] is not None:
+            assert mx <= TOL[dtype]["maxabs"] * scale, f"{k}: maxabs {mx:.3e} > {TOL[dtype]['maxabs']} x {scale:.3g}"

@@ -49,7 +49,7 @@ __all__ = [
     "fill_scan_device", "fill_step_device", "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
     "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
     "storage_to_f64", "scan_bytes", "step_bytes", "trap_extra_bytes", "trap_step_extra_bytes",
-    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes",
+    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes", "grad_inputs",
 ]
 
 DTYPES = ("f32", "bf16")
@@ -57,7 +57,8 @@ _CHUNK = 65536  # tokens per random stream
 _CBLK = 64      # channels per random stream
 
 # stream keys (tensor kinds)
-_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE, _K_LAM, _K_XPREV, _K_BPREV, _K_AH = range(12)
+_K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE, _K_LAM, _K_XPREV, _K_BPREV, _K_AH, _K_DY, _K_DSTATE = \
+    range(14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -283,6 +284,24 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
                 xp[b] = _store(_token_block(cfg.seed, _K_XPREV, b, 0, 1, cfg.D, sel)[0], act)
                 bp[b] = _store(_token_block(cfg.seed, _K_BPREV, b, 0, 1, cfg.N)[0], act)
         out["lam"], out["x_prev"], out["B_prev"] = lam, xp, bp
+    return out
+
+
+def grad_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None, channels: Optional[np.ndarray] = None,
+                dstate: bool = True) -> Dict[str, np.ndarray]:
+    """Upstream gradients for the scan of `cfg` over tokens [t0, t1): dy
+    (batch, T, D) N(0,1) in the storage dtype, and dstate (batch, D, N) N(0,1)
+    float32 (None unless `dstate`). Channel selection as in scan_inputs."""
+    if t1 is None:
+        t1 = cfg.L
+    sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
+    dy = np.empty((cfg.batch, t1 - t0, len(sel)), dtype=np.float32 if cfg.dtype == "f32" else np.uint16)
+    for b in range(cfg.batch):
+        dy[b] = _store(_token_block(cfg.seed, _K_DY, b, t0, t1, cfg.D, sel), cfg.dtype)
+    out = {"dy": dy, "dstate": None}
+    if dstate:
+        st = _rng(cfg.seed, _K_DSTATE).standard_normal((cfg.batch, cfg.D, cfg.N))
+        out["dstate"] = np.ascontiguousarray(st[:, sel, :].astype(np.float32))
     return out
 
 
