@@ -38,6 +38,10 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 # delta*A (mul), exp (a transcendental, issued at half rate: 2 slots),
 # B*(delta*x) (mul), dA*h + dBx (fma), C*h accumulated (fma).
 SCAN_SLOTS_PER_ELEM = 6
+# The gradient per element at the least: the recurrence again (delta*A, exp
+# at 2 slots, B*(delta*x), fma) and the reverse step (G += C*ds, ds*h,
+# G*a*h (2), two fmas into d(delta), dA fma, G*(delta*x), dx fma, G *= a).
+BWD_SLOTS_PER_ELEM = 15
 SCAN_KERNEL = "scan_stripe_kernel"
 STEP_KERNEL = "step_kernel"
 SSD_KERNEL = "ssd_kernel"
@@ -135,7 +139,9 @@ def bench_scan(args, name):
     # set 0: the seeded numpy streams (checked against the oracle below)
     sp = args.softplus  # delta handed over before its activation
     tr = args.trap  # exponential-trapezoidal rule
+    bw = args.backward  # the gradient (ssm_scan_bwd) in place of the forward scan
     inp = W.scan_inputs(cfg, raw_delta=sp, trap=tr) if name != "c3" else None
+    grads = W.grad_inputs(cfg) if (bw and inp is not None) else None
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
     whole = W.scan_inputs(cfg, 0, 0)
     A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
@@ -146,12 +152,29 @@ def bench_scan(args, name):
         if tr:
             keys += ("lam", "x_prev", "B_prev")
         sets.append({k: to_dev(inp[k]) for k in keys})
+        if bw:
+            sets[0]["dy"] = to_dev(grads["dy"])
     # further sets: same distributions, drawn on the GPU
     per_set = W.scan_bytes(cfg)
     nsets = max(1, min(args.rotate, int(60e9 // max(per_set, 1))))
     while len(sets) < nsets:
         sets.append(W.fill_scan_device(cfg, "cuda", seed=1000 + len(sets), raw_delta=sp, trap=tr))
+        if bw:
+            sets[-1]["dy"] = torch.randn(sets[-1]["x"].shape, device="cuda").to(sets[-1]["x"].dtype)
     ys = [torch.empty_like(s["x"]) for s in sets]
+    if bw:
+        f32 = torch.float32
+        ys = [{"dx": torch.empty_like(s["x"]), "ddelta": torch.empty_like(s["x"]),
+               "dz": torch.empty_like(s["x"]) if s["z"] is not None else None,
+               "dA": torch.empty((cfg.D, cfg.N), dtype=f32, device="cuda"),
+               "dBt": torch.empty((cfg.batch, cfg.L, cfg.N), dtype=f32, device="cuda"),
+               "dCt": torch.empty((cfg.batch, cfg.L, cfg.N), dtype=f32, device="cuda"),
+               "dDskip": torch.empty((cfg.D,), dtype=f32, device="cuda") if Dskip is not None else None,
+               "dstate_in": torch.empty((cfg.batch, cfg.D, cfg.N), dtype=f32, device="cuda")} for s in sets]
+        dstate = to_dev(W.grad_inputs(cfg, 0, 0)["dstate"])
+        bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
+                                                           0 if cfg.dtype == "f32" else 1),
+                          dtype=torch.uint8, device="cuda")
     ws_bytes = ssm.ssm_scan_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N, 0 if cfg.dtype == "f32" else 1)
     ws = ssm.new_workspace(ws_bytes)
     st_out = torch.empty((cfg.batch, cfg.D, cfg.N), dtype=torch.float32, device="cuda") \
@@ -160,7 +183,10 @@ def bench_scan(args, name):
 
     def step(i):
         s = sets[i % len(sets)]
-        if sp:
+        if bw:
+            ssm.ssm_scan_bwd(s["x"], s["delta"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip, z=s["z"],
+                             state_in=st_in, dstate=dstate, out=ys[i % len(sets)], workspace=bws, stream=stream)
+        elif sp:
             ssm.ssm_scan_fwd_dt(s["x"], s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"],
                                 state_in=st_in, state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
         elif tr:
@@ -181,6 +207,28 @@ def bench_scan(args, name):
            "bytes": W.scan_bytes(cfg, st_out is not None) + (cfg.D * 4 if sp else 0) +
                     (W.trap_extra_bytes(cfg) if tr else 0), "dtype": cfg.dtype,
            "parity": None, "cpu": None}
+    if bw:
+        out["bytes"] = W.scan_bwd_bytes(cfg)
+        if inp is not None and not args.no_cpu:
+            import oracle
+            torch.cuda.synchronize()
+            step(0)
+            torch.cuda.synchronize()
+            got = {k: (v.double().cpu().numpy() if v is not None else None) for k, v in ys[0].items()}
+            o = oracle.get()
+            reps, tot, ref = 0, 0.0, None
+            while reps == 0 or tot < args.cpu_seconds:
+                t = time.perf_counter()
+                ref = o.scan_bwd(inp, grads["dy"], grads["dstate"], cfg.dtype)
+                tot += time.perf_counter() - t
+                reps += 1
+            out["parity"] = {k: dict(zip(("relL2", "maxabs"), rel_l2(got[k], ref[k])))
+                             for k in ("dx", "ddelta", "dz", "dA", "dBt", "dCt", "dDskip", "dstate_in")
+                             if ref.get(k) is not None}
+            out["cpu"] = {"value": cfg.elems * reps / tot / 1e9, "unit": "G(B*L*D*N)-elem/s", "cores": 1,
+                          "kind": "oracle",
+                          "sample": f"whole workload, {reps} run(s), {tot:.1f}s, fp64 C oracle gradient, one thread"}
+        return out
     # parity of the timed configuration on set 0, and the CPU baseline
     if inp is not None and not args.no_cpu:
         import oracle
@@ -380,6 +428,8 @@ def main():
                     help="hand delta over before its activation (ssm_scan_fwd_dt / ssm_step_dt)")
     ap.add_argument("--trap", action="store_true",
                     help="the exponential-trapezoidal rule (ssm_scan_fwd_trap / ssm_step_trap)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the gradient of the scan (ssm_scan_bwd) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -400,6 +450,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
+    if args.backward and (args.softplus or args.trap or args.workload in ("c3", "c4", "ssd")):
+        ap.error("--backward times the gradient of the plain scan on c0, c1 or c2")
     if args.workload == "ssd" and (args.softplus or args.trap):
         ap.error("--softplus and --trap apply to the S6 scan and step")
     if args.workload == "ssd":
@@ -409,7 +461,7 @@ def main():
     cfg = r["cfg"]
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
-    traffic = None if (args.softplus or args.trap) else measured_traffic(args.workload)
+    traffic = None if (args.softplus or args.trap or args.backward) else measured_traffic(args.workload)
     kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL}.get(args.workload, SCAN_KERNEL)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": kernel,
@@ -422,6 +474,14 @@ def main():
                 "launch_us": launch_ms * 1e3}
     if args.workload in ("c4", "ssd"):
         roof = hbm  # the SSD layer needs more time at the HBM peak than at the matrix-core peak
+    elif args.backward:
+        # the whole gradient call (all its launches), against the VALU peak
+        slots = r["elems"] * BWD_SLOTS_PER_ELEM
+        tslots = slots / (launch_ms * 1e-3) / 1e12
+        hbm["kernel"] = "ssm_scan_bwd (all launches)"
+        roof = {"bound": "alu", "achieved": tslots, "peak": VALU_PEAK_TSLOTS, "unit": "T VALU-slots/s",
+                "frac": tslots / VALU_PEAK_TSLOTS, "traffic": None, "kernel": "ssm_scan_bwd (all launches)",
+                "algorithmic_slots_per_launch": slots, "launch_us": launch_ms * 1e3}
     else:
         # the scan needs more time at the VALU peak than at the HBM peak
         slots = r["elems"] * SCAN_SLOTS_PER_ELEM
@@ -449,6 +509,9 @@ def main():
         if args.trap:
             config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "selective-scan G(B*L*D*N)-elem/s"
+        if args.backward:
+            config["pass"] = "gradient (ssm_scan_bwd), dstate given"
+            metric = "selective-scan gradient G(B*L*D*N)-elem/s"
     line = {
         "metric": metric,
         "value": r["elems"] / (ms * 1e-3) / 1e9,

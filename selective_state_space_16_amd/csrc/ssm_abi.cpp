@@ -303,21 +303,21 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
     return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
-// Workspace of the gradient: [header | hst | dsum | gq | rsum | pdB | pdC | pdA | pdD].
+// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD].
 struct BwdLayout {
     int64_t K;
-    size_t off[8], bytes;
+    size_t off[7], bytes;
 };
 
 static BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N) {
     BwdLayout w{};
     w.K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
     const int64_t nDB = ssm::bwd_channel_blocks(D, N);
-    const size_t sz[8] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
-                          (size_t)(batch * w.K * D),     (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
+    const size_t sz[7] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
+                          (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
                           (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D)};
     size_t off = kHeader;
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 7; ++i) {
         w.off[i] = off;
         off += round_up256(sz[i] * sizeof(float));
     }
@@ -377,21 +377,6 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     const BwdLayout w = bwd_layout(batch, L, D, N);
     if (!workspace || workspace_bytes < w.bytes) return SSM_ERR_WORKSPACE;
     char *ws = (char *)workspace;
-    ssm::ScanArgs f{};
-    f.batch = batch;
-    f.L = L;
-    f.D = D;
-    f.x = x;
-    f.delta = delta;
-    f.Bt = Bt;
-    f.Ct = Ct;
-    f.A = A;
-    f.state_in = state_in;
-    f.K = w.K;
-    f.Lc = ssm::kBwdChunk;
-    f.ws_state = (float *)(ws + w.off[0]);
-    f.ws_dsum = (float *)(ws + w.off[1]);
-    if (ssm::launch_scan_states(f, (int)N, dtype, s) != hipSuccess) return SSM_ERR_HIP;
     ssm::BwdArgs a{};
     a.batch = batch;
     a.L = L;
@@ -415,14 +400,13 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.dCt = dCt;
     a.dDskip = Dskip ? dDskip : nullptr;
     a.dstate_in = dstate_in;
-    a.hst = f.ws_state;
-    a.dsum = f.ws_dsum;
+    a.hst = (float *)(ws + w.off[0]);
+    a.dsum = (float *)(ws + w.off[1]);
     a.gq = (float *)(ws + w.off[2]);
-    a.rsum = (float *)(ws + w.off[3]);
-    a.pdB = (float *)(ws + w.off[4]);
-    a.pdC = (float *)(ws + w.off[5]);
-    a.pdA = (float *)(ws + w.off[6]);
-    a.pdD = (float *)(ws + w.off[7]);
+    a.pdB = (float *)(ws + w.off[3]);
+    a.pdC = (float *)(ws + w.off[4]);
+    a.pdA = (float *)(ws + w.off[5]);
+    a.pdD = (float *)(ws + w.off[6]);
     return ssm::launch_scan_bwd(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

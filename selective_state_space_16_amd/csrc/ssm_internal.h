@@ -94,7 +94,6 @@ struct BwdArgs {
     float *hst;         // (batch, K, D, N) state entering each chunk
     float *dsum;        // (batch, K, D)    summed delta per chunk
     float *gq;          // (batch, K, D, N) gradient entering each chunk from its end
-    float *rsum;        // (batch, K, D)    summed delta per chunk (reverse pass)
     float *pdB, *pdC;   // (bwd_channel_blocks, batch, L, N) per-block partial sums
     float *pdA;         // (batch, K, D, N) per-chunk partial sums
     float *pdD;         // (batch, K, D)
@@ -106,9 +105,6 @@ inline int64_t bwd_channel_blocks(int64_t D, int64_t N) {
     const int64_t cpb = N > 8 ? 256 / (N / 8) : 256;
     return (D + cpb - 1) / cpb;
 }
-// Summary and carry launches of the chunked scan: the state entering every
-// chunk into a.ws_state (used by the gradient).
-hipError_t launch_scan_states(const ScanArgs &a, int N, int dtype, hipStream_t s);
 
 // Sequence split used for a scan of these sizes (deterministic).
 void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64_t *Lc);

@@ -237,35 +237,6 @@ hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s) {
     }
 }
 
-// The state entering every chunk (into a.ws_state), for the gradient: the
-// summary and carry launches alone; with K = 1 the carry copies state_in.
-template <int N, int DT>
-hipError_t launch_states_typed(const ScanArgs &a, hipStream_t s) {
-    const int64_t nb = (a.D + kWave - 1) / kWave;
-    if (a.K > 1)
-        hipLaunchKernelGGL((scan_chunk_kernel<N, DT, kSummary, false, false, false>),
-                           dim3((unsigned)(nb * (a.K - 1) * a.batch)), dim3(kWave), 0, s, a);
-    const int64_t total = a.batch * a.D * N;
-    hipLaunchKernelGGL((scan_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int N>
-hipError_t launch_states_dtype(const ScanArgs &a, int dtype, hipStream_t s) {
-    return dtype == 0 ? launch_states_typed<N, 0>(a, s) : launch_states_typed<N, 1>(a, s);
-}
-
-hipError_t launch_scan_states(const ScanArgs &a, int N, int dtype, hipStream_t s) {
-    switch (N) {
-        case 1: return launch_states_dtype<1>(a, dtype, s);
-        case 2: return launch_states_dtype<2>(a, dtype, s);
-        case 4: return launch_states_dtype<4>(a, dtype, s);
-        case 8: return launch_states_dtype<8>(a, dtype, s);
-        case 16: return launch_states_dtype<16>(a, dtype, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dst, n);

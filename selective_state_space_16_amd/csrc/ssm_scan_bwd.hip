@@ -11,13 +11,13 @@
 // hardware": the backward recomputes the intermediate states), so nothing of
 // size (batch, L, D, N) is written. The sequence is cut into chunks of 32
 // tokens:
-//   1. the forward chunk summaries and their carry give the state entering
-//      every chunk (the kernels of the forward scan, ssm_scan.hip);
-//   2. a reverse summary per chunk: G at the chunk's first token, times its
-//      a_t, from a zero gradient at the chunk's end, and the chunk's summed
-//      delta;
-//   3. a reverse carry per (b, d, n) over the chunks, from dstate at the end:
-//      the gradient entering every chunk from the tokens after it;
+//   1. forward summaries: each chunk's end state from a zero start;
+//   2. reverse summaries: the gradient each chunk sends into the state before
+//      it from a zero gradient at its end (both summaries in one pass, with
+//      each chunk's summed delta);
+//   3. carries per (b, d, n) over the chunks: from state_in, the state
+//      entering every chunk; from dstate, the gradient entering every chunk
+//      from the tokens after it;
 //   4. per chunk, from its entering state and gradient: the states again at
 //      8-token checkpoints, then token by token backwards, every gradient.
 //      dB and dC sum over the channels: exchanges within each wave, then LDS
@@ -41,6 +41,56 @@ __device__ __forceinline__ void silu_and_grad(float z, float &g, float &dg) {
     dg = sg * (1.0f + z * (1.0f - sg));
 }
 
+// v from lane (lane ^ BIT): DPP lane moves inside rows of 16 lanes for BIT <
+// 16 (quad permutes for 1 and 2; shifts by 4 within banks of 4 lanes for 4;
+// a rotation by 8 for 8), a swizzle inside 32 lanes for 16, a permute for 32.
+template <int BIT>
+__device__ __forceinline__ float xor_lane(float v) {
+    const int x = __float_as_int(v);
+    if constexpr (BIT == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    } else if constexpr (BIT == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    } else if constexpr (BIT == 4) {
+        // lanes 0-3 and 8-11 of a row read lane + 4 (row_shl:4), lanes 4-7 and 12-15 lane - 4 (row_shr:4)
+        const int lo = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0x5, false);
+        return __int_as_float(__builtin_amdgcn_update_dpp(lo, x, 0x114, 0xF, 0xA, false));
+    } else if constexpr (BIT == 8) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));  // row_ror:8
+    } else if constexpr (BIT == 16) {
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));  // and 31, xor 16
+    } else {
+        return __shfl_xor(v, BIT);
+    }
+}
+
+// One halving exchange of wave_sum_vec and the ones after it: lanes with bit
+// BIT set keep the upper HALF elements of the current vector, the others the
+// lower HALF, each adding its partner's (lane ^ BIT) copy of the kept half.
+// Recursion on constants keeps every array index a compile-time constant.
+template <int HALF, int BIT, int N>
+__device__ __forceinline__ void halve(float (&v)[N], int lane) {
+    if constexpr (HALF >= 1) {
+        const bool upper = (lane & BIT) != 0;
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            const float send = upper ? v[i] : v[i + HALF];
+            const float keep = upper ? v[i + HALF] : v[i];
+            v[i] = keep + xor_lane<BIT>(send);
+        }
+        halve<HALF / 2, BIT * 2>(v, lane);
+    }
+}
+
+template <int BIT, int SPAN>
+__device__ __forceinline__ float fold(float s) {
+    if constexpr (BIT < SPAN) {
+        return fold<BIT * 2, SPAN>(s + xor_lane<BIT>(s));
+    } else {
+        return s;
+    }
+}
+
 // Sum of v[0..N) over the lanes of a wave that share bit SPAN and above
 // (SPAN = 64: the whole wave). The halving exchanges leave lane l with the
 // sum, over N lanes, of one element, named by the bits of l below log2(N);
@@ -48,20 +98,8 @@ __device__ __forceinline__ void silu_and_grad(float z, float &g, float &dg) {
 // that sum.
 template <int N, int SPAN>
 __device__ __forceinline__ float wave_sum_vec(float (&v)[N], int lane) {
-#pragma unroll
-    for (int half = N / 2, bit = 1; half >= 1; half /= 2, bit *= 2) {
-        const bool upper = (lane & bit) != 0;  // keeps the upper half of the current vector
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float send = upper ? v[i] : v[i + half];
-            const float keep = upper ? v[i + half] : v[i];
-            v[i] = keep + __shfl_xor(send, bit);
-        }
-    }
-    float s = v[0];
-#pragma unroll
-    for (int bit = N; bit < SPAN; bit *= 2) s += __shfl_xor(s, bit);
-    return s;
+    halve<N / 2, 1>(v, lane);
+    return fold<N, SPAN>(v[0]);
 }
 
 // The element of v that wave_sum_vec<N, SPAN> leaves in lane `lane`.
@@ -69,71 +107,99 @@ template <int N>
 __device__ __forceinline__ int wave_sum_index(int lane) {
     int idx = 0;
 #pragma unroll
-    for (int half = N / 2, bit = 1; half >= 1; half /= 2, bit *= 2)
-        if (lane & bit) idx += half;
+    for (int s = 0; (N >> (s + 1)) >= 1; ++s)
+        if (lane & (1 << s)) idx += N >> (s + 1);
     return idx;
 }
 
-// 2. reverse summaries: per (b, chunk k >= 1, channel), G entering token t0 - 1
-// from a zero gradient at the chunk's end, and the chunk's summed delta.
+// 1+2. the summaries of every chunk k, in one forward pass over its tokens:
+// its end state from a zero start (S_k, for k < K - 1), the gradient it sends
+// into the state before it from a zero gradient at its end (R_k, for k >= 1),
+// and its summed delta. In token order, R_k is the sum of C_t ds_t times the
+// product of a_s over the chunk's tokens up to and including t, so the decay
+// a_t of each token serves both summaries.
 template <int N, int DT, bool GATE>
-__global__ __launch_bounds__(kBwdThreads) void bwd_rev_summary_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_summary_kernel(BwdArgs a) {
     using T = typename Act<DT>::T;
     const int64_t D = a.D, L = a.L, K = a.K;
-    // flat grid: block id = (b * (K - 1) + k - 1) * channel_blocks + channel_block
+    // flat grid: block id = (b * K + k) * channel_blocks + channel_block
     const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads, bid = blockIdx.x;
     const int64_t d = (bid % nb) * kBwdThreads + threadIdx.x;
-    const int64_t k = (bid / nb) % (K - 1) + 1, b = bid / (nb * (K - 1));
+    const int64_t k = (bid / nb) % K, b = bid / (nb * K);
     const bool valid = d < D;
     const int64_t dc = valid ? d : D - 1;
     const int64_t t0 = k * kBwdChunk, t1 = t0 + kBwdChunk < L ? t0 + kBwdChunk : L;
-    float A2[N], G[N];
+    float A2[N], h[N], P[N], R[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         A2[n] = a.A[dc * N + n] * kLog2e;
-        G[n] = 0.0f;
+        h[n] = 0.0f;
+        P[n] = 1.0f;
+        R[n] = 0.0f;
     }
-    const T *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
-    const T *Cp = (const T *)a.Ct;
+    const T *xp = (const T *)a.x, *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
+    const T *Bp = (const T *)a.Bt, *Cp = (const T *)a.Ct;
     float dsum = 0.0f;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
+    for (int64_t t = t0; t < t1; ++t) {
         const int64_t row = (b * L + t) * D + dc;
-        const float dt = ld_act(dp, row);
+        const float dt = ld_act(dp, row), dtx = dt * ld_act(xp, row);
         float ds = ld_act(gp, row);
         if (GATE) {
             float g, dg;
             silu_and_grad(ld_act(zp, row), g, dg);
             ds *= g;
         }
-        float Cv[N];
+        float Bv[N], Cv[N];
+        ld_row_uniform<N>(Bp, (b * L + t) * N, Bv);
         ld_row_uniform<N>(Cp, (b * L + t) * N, Cv);
         dsum += dt;
 #pragma unroll
-        for (int n = 0; n < N; ++n) G[n] = fast_exp2(dt * A2[n]) * __builtin_fmaf(Cv[n], ds, G[n]);
+        for (int n = 0; n < N; ++n) {
+            const float av = fast_exp2(dt * A2[n]);
+            h[n] = __builtin_fmaf(av, h[n], dtx * Bv[n]);
+            P[n] *= av;
+            R[n] = __builtin_fmaf(P[n] * Cv[n], ds, R[n]);
+        }
     }
     if (!valid) return;
-    float *dst = a.gq + ((b * K + k) * D + d) * N;
+    const int64_t o = ((b * K + k) * D + d) * N;
+    if (k + 1 < K) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) dst[n] = G[n];
-    a.rsum[(b * K + k) * D + d] = dsum;
+        for (int n = 0; n < N; ++n) a.hst[o + n] = h[n];
+    }
+    if (k > 0) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.gq[o + n] = R[n];
+    }
+    a.dsum[(b * K + k) * D + d] = dsum;
 }
 
-// 3. reverse carry: per (b, d, n), replace each chunk's reverse summary by the
-// gradient entering the chunk from the tokens after it; the gradient leaving
-// chunk 0 is dstate_in.
+// 3. the carries, per (b, d, n): in chunk order, the state entering each chunk
+// (from state_in: h <- exp(A sum delta_k) h + S_k); in reverse chunk order,
+// the gradient entering each chunk from its end (from dstate: q <- R_k +
+// exp(A sum delta_k) q). Each summary slot is replaced by its carry.
 template <int N>
-__global__ __launch_bounds__(256) void bwd_rev_carry_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t D = a.D, K = a.K;
     if (i >= a.batch * D * N) return;
     const int64_t n = i % N, d = (i / N) % D, b = i / ((int64_t)N * D);
     const float A2 = a.A[d * N + n] * kLog2e;
+    const int64_t base = (b * K * D + d) * N + n, kstride = D * N;
+    const float *ds = a.dsum + b * K * D + d;
+    float h = a.state_in ? a.state_in[i] : 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float *slot = a.hst + base + k * kstride;
+        const float s = k + 1 < K ? *slot : 0.0f;
+        *slot = h;
+        if (k + 1 < K) h = __builtin_fmaf(fast_exp2(A2 * ds[k * D]), h, s);
+    }
     float q = a.dstate ? a.dstate[i] : 0.0f;
     for (int64_t k = K - 1; k >= 0; --k) {
-        float *slot = a.gq + ((b * K + k) * D + d) * N + n;
+        float *slot = a.gq + base + k * kstride;
         const float r = k > 0 ? *slot : 0.0f;
         *slot = q;
-        if (k > 0) q = __builtin_fmaf(fast_exp2(A2 * a.rsum[(b * K + k) * D + d]), q, r);
+        if (k > 0) q = __builtin_fmaf(fast_exp2(A2 * ds[k * D]), q, r);
     }
 }
 
@@ -225,7 +291,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             float gate = 1.0f, dgate = 0.0f;
             if (GATE) silu_and_grad(ld_act(zp, row), gate, dgate);
             const float ds = valid ? dyv * gate : 0.0f;
-            float pre = 0.0f, gdt = 0.0f, gx = 0.0f, dCv[NP], dBv[NP];
+            const float dtx = valid ? dt * xv : 0.0f;
+            // gah = G a h_{t-1}: d(delta) takes sum(gah A) + x sum(G B), dx takes delta sum(G B)
+            float pre = 0.0f, gaa = 0.0f, gb = 0.0f, dCv[NP], dBv[NP];
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 const float Cv = sC[tl][n0 + i], Bv = sB[tl][n0 + i];
@@ -234,17 +302,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 dCv[i] = ds * hb[j + 1][i];
                 const float av = fast_exp2(dt * A2[i]);
                 const float gah = G[i] * av * hb[j][i];
-                gdt = __builtin_fmaf(gah * kLn2, A2[i], __builtin_fmaf(G[i] * Bv, xv, gdt));
+                gaa = __builtin_fmaf(gah, A2[i], gaa);
                 dA[i] = __builtin_fmaf(gah, dt, dA[i]);
-                dBv[i] = valid ? G[i] * dt * xv : 0.0f;
-                gx = __builtin_fmaf(G[i] * dt, Bv, gx);
+                dBv[i] = G[i] * dtx;
+                gb = __builtin_fmaf(G[i], Bv, gb);
                 G[i] *= av;
             }
             if (R == 2) {  // the other half of the channel's state elements
-                pre += __shfl_xor(pre, SPAN);
-                gdt += __shfl_xor(gdt, SPAN);
-                gx += __shfl_xor(gx, SPAN);
+                pre += xor_lane<SPAN>(pre);
+                gaa += xor_lane<SPAN>(gaa);
+                gb += xor_lane<SPAN>(gb);
             }
+            const float gdt = __builtin_fmaf(gaa, kLn2, gb * xv);
+            float gx = gb * dt;
             if (SKIP) {
                 pre = __builtin_fmaf(dsk, xv, pre);
                 gx = __builtin_fmaf(ds, dsk, gx);
@@ -286,13 +356,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
 }
 
-// 5. the sums of the partials, in a fixed order.
+// 5. the sums of the partials, in a fixed order (partial 0 first), eight
+// loads in flight per step.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part, int64_t nparts, int64_t stride,
                                                          float *out, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float s = 0.0f;
-    for (int64_t p = 0; p < nparts; ++p) s += part[p * stride + i];
+    int64_t p = 0;
+    for (; p + 8 <= nparts; p += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(p + u) * stride + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; p < nparts; ++p) s += part[p * stride + i];
     out[i] = s;
 }
 
@@ -301,17 +380,17 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
     const int64_t D = a.D, K = a.K;
     const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads;
     if (K > 1)
-        hipLaunchKernelGGL((bwd_rev_summary_kernel<N, DT, GATE>), dim3((unsigned)(nb * (K - 1) * a.batch)),
-                           dim3(kBwdThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_summary_kernel<N, DT, GATE>), dim3((unsigned)(nb * K * a.batch)), dim3(kBwdThreads),
+                           0, s, a);
     const int64_t total = a.batch * D * N;
-    hipLaunchKernelGGL((bwd_rev_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     const int64_t ncb = bwd_channel_blocks(D, N);
     hipLaunchKernelGGL((bwd_chunk_kernel<N, DT, GATE, SKIP>), dim3((unsigned)(ncb * K * a.batch)),
                        dim3(kBwdThreads), 0, s, a);
-    const int64_t nDB = ncb, bln = a.batch * a.L * N;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdB, nDB, bln,
+    const int64_t bln = a.batch * a.L * N;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdB, ncb, bln,
                        a.dBt, bln);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdC, nDB, bln,
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdC, ncb, bln,
                        a.dCt, bln);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D * N + 255) / 256)), dim3(256), 0, s, a.pdA,
                        a.batch * K, D * N, a.dA, D * N);

@@ -49,7 +49,7 @@ __all__ = [
     "fill_scan_device", "fill_step_device", "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
     "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
     "storage_to_f64", "scan_bytes", "step_bytes", "trap_extra_bytes", "trap_step_extra_bytes",
-    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes", "grad_inputs",
+    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes", "grad_inputs", "scan_bwd_bytes",
 ]
 
 DTYPES = ("f32", "bf16")
@@ -427,6 +427,20 @@ def scan_bytes(cfg: ScanConfig, state_out: bool = False) -> int:
         n += cfg.batch * cfg.D * cfg.N * 4
     if state_out:
         n += cfg.batch * cfg.D * cfg.N * 4
+    return n
+
+
+def scan_bwd_bytes(cfg: ScanConfig) -> int:
+    """Bytes the gradient must move: x, delta, dy, (z) read and dx, ddelta, (dz)
+    written once per (b,t,d); Bt, Ct read and dBt, dCt (float32) written once
+    per token; A, Dskip read and dA, dDskip written once; state_in (when used),
+    dstate and dstate_in once."""
+    e = _esize(cfg.dtype)
+    btd = cfg.batch * cfg.L * cfg.D
+    n = btd * e * (5 + (2 if cfg.gate else 0))
+    n += cfg.batch * cfg.L * cfg.N * (2 * e + 2 * 4)
+    n += 2 * (cfg.D * cfg.N * 4 + (cfg.D * 4 if cfg.dskip != "none" else 0))
+    n += cfg.batch * cfg.D * cfg.N * 4 * (3 if cfg.state_in is not None else 2)
     return n
 
 
