@@ -187,19 +187,42 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
     const float A2 = a.A[d * N + n] * kLog2e;
     const int64_t base = (b * K * D + d) * N + n, kstride = D * N;
     const float *ds = a.dsum + b * K * D + d;
+    // four chunks per step: their loads first, then the dependent chain
     float h = a.state_in ? a.state_in[i] : 0.0f;
-    for (int64_t k = 0; k < K; ++k) {
-        float *slot = a.hst + base + k * kstride;
-        const float s = k + 1 < K ? *slot : 0.0f;
-        *slot = h;
-        if (k + 1 < K) h = __builtin_fmaf(fast_exp2(A2 * ds[k * D]), h, s);
+    for (int64_t k0 = 0; k0 < K; k0 += 4) {
+        float sv[4], dv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 + u;
+            sv[u] = k + 1 < K ? a.hst[base + k * kstride] : 0.0f;
+            dv[u] = k + 1 < K ? ds[k * D] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 + u;
+            if (k < K) {
+                a.hst[base + k * kstride] = h;
+                h = __builtin_fmaf(fast_exp2(A2 * dv[u]), h, sv[u]);
+            }
+        }
     }
     float q = a.dstate ? a.dstate[i] : 0.0f;
-    for (int64_t k = K - 1; k >= 0; --k) {
-        float *slot = a.gq + base + k * kstride;
-        const float r = k > 0 ? *slot : 0.0f;
-        *slot = q;
-        if (k > 0) q = __builtin_fmaf(fast_exp2(A2 * ds[k * D]), q, r);
+    for (int64_t k0 = K - 1; k0 >= 0; k0 -= 4) {
+        float rv[4], dv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 - u;
+            rv[u] = k > 0 ? a.gq[base + k * kstride] : 0.0f;
+            dv[u] = k > 0 ? ds[k * D] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 - u;
+            if (k >= 0) {
+                a.gq[base + k * kstride] = q;
+                q = __builtin_fmaf(fast_exp2(A2 * dv[u]), q, rv[u]);
+            }
+        }
     }
 }
 
@@ -248,8 +271,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         G[i] = a.gq[((b * K + k) * D + dc) * N + n0 + i];
     }
     __syncthreads();
-    // forward through the chunk, keeping the state entering each block
-    for (int j = 0; j < cnt_chunk; ++j) {
+    // forward through the chunk up to its last block, keeping the state
+    // entering each block
+    const int nblk = (cnt_chunk + kSub - 1) / kSub;
+    for (int j = 0; j < (nblk - 1) * kSub; ++j) {
         if (j % kSub == 0) {
 #pragma unroll
             for (int i = 0; i < NP; ++i) ck[j / kSub][i][tid] = h[i];
@@ -259,12 +284,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NP; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), h[i], dx * sB[j][n0 + i]);
     }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) ck[nblk - 1][i][tid] = h[i];
     float dA[NP], dD = 0.0f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) dA[i] = 0.0f;
     const float dsk = SKIP ? a.Dskip[dc] : 0.0f;
     const int elem = n0 + wave_sum_index<NP>(cl);  // element this lane holds after the channel sums
-    const int nblk = (cnt_chunk + kSub - 1) / kSub;
     for (int blk = nblk - 1; blk >= 0; --blk) {
         const int s0 = blk * kSub;
         const int cnt = cnt_chunk - s0 < kSub ? cnt_chunk - s0 : kSub;
