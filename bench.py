@@ -461,7 +461,8 @@ def main():
     cfg = r["cfg"]
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
-    traffic = None if (args.softplus or args.trap or args.backward) else measured_traffic(args.workload)
+    traffic = None if (args.softplus or args.trap) else \
+        measured_traffic(args.workload + ("_grad" if args.backward else ""))
     kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL}.get(args.workload, SCAN_KERNEL)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": kernel,
@@ -480,7 +481,7 @@ def main():
         tslots = slots / (launch_ms * 1e-3) / 1e12
         hbm["kernel"] = "ssm_scan_bwd (all launches)"
         roof = {"bound": "alu", "achieved": tslots, "peak": VALU_PEAK_TSLOTS, "unit": "T VALU-slots/s",
-                "frac": tslots / VALU_PEAK_TSLOTS, "traffic": None, "kernel": "ssm_scan_bwd (all launches)",
+                "frac": tslots / VALU_PEAK_TSLOTS, "traffic": traffic, "kernel": "ssm_scan_bwd (all launches)",
                 "algorithmic_slots_per_launch": slots, "launch_us": launch_ms * 1e3}
     else:
         # the scan needs more time at the VALU peak than at the HBM peak

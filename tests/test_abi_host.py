@@ -214,3 +214,41 @@ def test_ssd_rejects(kw, code):
 
 def test_ssd_empty_ok_without_gpu():
     assert ssd(batch=0) == 0 and ssd(H=0) == 0 and ssd(L=0) == 0
+
+
+def bwd(**kw):
+    a = dict(batch=2, L=100, D=64, N=16, dtype=0, x=P, delta=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             state_in=None, dy=P, dstate=None, dx=P, ddelta=P, dA=P, dBt=P, dCt=P, dDskip=None, dz=None,
+             dstate_in=None, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_bwd(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["delta"], a["A"],
+                                  a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state_in"], a["dy"], a["dstate"],
+                                  a["dx"], a["ddelta"], a["dA"], a["dBt"], a["dCt"], a["dDskip"], a["dz"],
+                                  a["dstate_in"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(L=-1), -2), (dict(dtype=2), -3), (dict(N=3), -4), (dict(N=32), -4),
+    (dict(dA=None), -1), (dict(z=P, dz=None), -1), (dict(x=None), -1), (dict(dy=None), -1), (dict(dx=None), -1),
+    (dict(ddelta=None), -1), (dict(dBt=None), -1), (dict(dCt=None), -1), (dict(dz=MIS, z=P), -5),
+    (dict(dstate=MIS), -5), (dict(ws=None), -6), (dict(ws_bytes=100), -6), (dict(ws=MIS), -5),
+    (dict(batch=1 << 40, L=1 << 20), -2),
+])
+def test_scan_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_scan_bwd_workspace_bytes():
+    f = ssm.ssm_scan_bwd_workspace_bytes
+    assert f(0, 10, 64, 16, 0) == 0 and f(1, 0, 64, 16, 0) == 0 and f(1, 10, 0, 16, 0) == 0
+    assert f(1, 10, 64, 3, 0) == 0 and f(1, 10, 64, 16, 5) == 0 and f(-1, 10, 64, 16, 0) == 0
+    # 4 chunks of 32 tokens; every region a multiple of 256 bytes after a 256-byte header
+    n = f(2, 100, 64, 16, 0)
+    # states, gradients and dA partials per (batch, chunk, channel, n); dBt, dCt partials
+    assert n % 256 == 0 and n >= 256 + 3 * 2 * 4 * 64 * 16 * 4 + 2 * 2 * 100 * 16 * 4
+    assert f(2, 100, 64, 16, 1) == n  # the workspace is float32 whatever the activation dtype
+    assert f(2, 200, 64, 16, 0) > n
+
+
+def test_scan_bwd_empty_ok_without_gpu():
+    assert bwd(D=0) == 0
