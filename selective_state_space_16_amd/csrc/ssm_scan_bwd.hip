@@ -326,13 +326,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 pre = __builtin_fmaf(Cv, hb[j + 1][i], pre);
                 G[i] = __builtin_fmaf(Cv, ds, G[i]);
                 dCv[i] = ds * hb[j + 1][i];
-                const float av = fast_exp2(dt * A2[i]);
-                const float gah = G[i] * av * hb[j][i];
-                gaa = __builtin_fmaf(gah, A2[i], gaa);
-                dA[i] = __builtin_fmaf(gah, dt, dA[i]);
                 dBv[i] = G[i] * dtx;
                 gb = __builtin_fmaf(G[i], Bv, gb);
-                G[i] *= av;
+                G[i] *= fast_exp2(dt * A2[i]);  // the gradient of h_{t-1}
+                const float gah = G[i] * hb[j][i];
+                gaa = __builtin_fmaf(gah, A2[i], gaa);
+                dA[i] = __builtin_fmaf(gah, dt, dA[i]);
             }
             if (R == 2) {  // the other half of the channel's state elements
                 pre += xor_lane<SPAN>(pre);
