@@ -67,6 +67,8 @@ class Oracle:
         self.lib.oracle_ssd.restype = ci
         self.lib.oracle_scan_bwd.argtypes = [i64] * 4 + [_DP] * 18
         self.lib.oracle_scan_bwd.restype = ci
+        self.lib.oracle_softplus_grad.argtypes = [i64, i64] + [_DP] * 5
+        self.lib.oracle_softplus_grad.restype = ci
 
     def threads(self, nthreads: int = 0) -> int:
         return int(self.lib.oracle_threads(nthreads))
@@ -205,6 +207,24 @@ class Oracle:
             raise ValueError("oracle_scan_bwd rejected sizes")
         return out
 
+    def scan_bwd_dt64(self, x, delta_raw, dt_bias, A, Bt, Ct, Dskip, z, state_in, dy, dstate=None):
+        """Gradient of the scan whose step size is softplus(delta_raw + dt_bias):
+        scan_bwd64 on the activated step, then the chain rule through the
+        activation. Returns scan_bwd64's dict with ddelta replaced by
+        ddelta_raw, plus ddt_bias (D,)."""
+        d64 = self.softplus_bias64(delta_raw, dt_bias)
+        out = self.scan_bwd64(x, d64, A, Bt, Ct, Dskip, z, state_in, dy, dstate)
+        raw = _c64(delta_raw)
+        D = raw.shape[-1]
+        bias = None if dt_bias is None else _c64(dt_bias)
+        g = out.pop("ddelta")
+        graw, gbias = np.empty_like(raw), np.empty(D)
+        if self.lib.oracle_softplus_grad(raw.size // D if D else 0, D, _p(raw), _p(bias), _p(g), _p(graw),
+                                         _p(gbias)) != 0:
+            raise ValueError("oracle_softplus_grad rejected sizes")
+        out["ddelta_raw"], out["ddt_bias"] = graw, gbias
+        return out
+
     def softplus_bias64(self, raw, bias=None):
         """softplus(raw + bias[d]) over the last axis (D) of a float64 array."""
         raw = _c64(raw)
@@ -285,6 +305,14 @@ class Oracle:
         f32 = lambda a: None if a is None else upcast(a, "f32")
         return self.scan_bwd64(up(inp["x"]), up(inp["delta"]), f32(inp["A"]), up(inp["Bt"]), up(inp["Ct"]),
                                f32(inp.get("Dskip")), up(inp.get("z")), f32(inp.get("state_in")), up(dy), f32(dstate))
+
+    def scan_bwd_dt(self, inp: Dict[str, np.ndarray], dy, dstate, dtype: str):
+        """scan_bwd64_dt on stored inputs (delta_raw in the stored dtype, dt_bias float32 or None)."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        return self.scan_bwd_dt64(up(inp["x"]), up(inp["delta_raw"]), f32(inp.get("dt_bias")), f32(inp["A"]),
+                                  up(inp["Bt"]), up(inp["Ct"]), f32(inp.get("Dskip")), up(inp.get("z")),
+                                  f32(inp.get("state_in")), up(dy), f32(dstate))
 
     def step(self, tok: Dict[str, np.ndarray], A, Dskip, state64: np.ndarray, dtype: str,
              nthreads: int = 0):

@@ -153,6 +153,30 @@ int oracle_softplus_bias(int64_t rows, int64_t D, const double *raw, const doubl
 }
 
 /*
+ * Gradient through the step-size activation: with u = raw[r, d] + bias[d] and
+ * delta = softplus(u), d delta / d u = sigmoid(u) = 1 / (1 + exp(-u)), so for
+ * the gradient g of delta (rows, D):
+ *   graw[r, d] = g[r, d] * sigmoid(u)
+ *   gbias[d]   = sum over r of graw[r, d]          (gbias may be NULL)
+ * bias may be NULL (zero).
+ */
+int oracle_softplus_grad(int64_t rows, int64_t D, const double *raw, const double *bias, const double *g,
+                         double *graw, double *gbias)
+{
+    if (rows < 0 || D < 0) return -1;
+    if (gbias)
+        for (int64_t d = 0; d < D; ++d) gbias[d] = 0.0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d) {
+            double u = raw[r * D + d] + (bias ? bias[d] : 0.0);
+            double v = g[r * D + d] / (1.0 + exp(-u));
+            graw[r * D + d] = v;
+            if (gbias) gbias[d] += v;
+        }
+    return 0;
+}
+
+/*
  * One decode step: the loop body above with a single token, on a stored state
  * that is updated in place.
  *   x, delta, z, y : (batch, D)       z may be NULL

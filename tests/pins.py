@@ -609,6 +609,41 @@ def pin_bwd_finite_differences(o):
         assert np.allclose(g[gk], num, rtol=1e-6, atol=1e-7), (k, np.abs(g[gk] - num).max())
 
 
+def pin_bwd_dt_finite_differences(o):
+    """The gradient through the step-size activation (delta = softplus(delta_raw
+    + dt_bias)): ddelta_raw and ddt_bias against central differences of the
+    loss of the forward oracle run on the activated step, and dx against the
+    plain gradient at that step; at raw + bias = 0 the factor is sigmoid(0) = 1/2."""
+    rng = np.random.default_rng(43)
+    batch, L, D, N = 2, 5, 3, 4
+    p = _rand_problem(rng, batch, L, D, N)
+    raw = rng.normal(scale=1.5, size=(batch, L, D))
+    raw[0, 0, 0] = -0.25
+    bias = rng.normal(size=D)
+    bias[0] = 0.25  # raw + bias = 0 at (0, 0, 0)
+    dy, dstate = rng.normal(size=(batch, L, D)), rng.normal(size=(batch, D, N))
+
+    def loss(r, bv):
+        return _loss(o, dict(p, delta=o.softplus_bias64(r, bv)), dy, dstate)
+
+    g = o.scan_bwd_dt64(p["x"], raw, bias, p["A"], p["Bt"], p["Ct"], p["Dskip"], p["z"], p["state_in"], dy, dstate)
+    for name, base, gk in (("raw", raw, "ddelta_raw"), ("bias", bias, "ddt_bias")):
+        num = np.empty_like(base)
+        for i in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[i]))
+            a, b_ = base.copy(), base.copy()
+            a[i] += eps
+            b_[i] -= eps
+            up = loss(a, bias) if name == "raw" else loss(raw, a)
+            dn = loss(b_, bias) if name == "raw" else loss(raw, b_)
+            num[i] = (up - dn) / (2 * eps)
+        assert np.allclose(g[gk], num, rtol=1e-6, atol=1e-7), (name, np.abs(g[gk] - num).max())
+    plain = o.scan_bwd64(p["x"], o.softplus_bias64(raw, bias), p["A"], p["Bt"], p["Ct"], p["Dskip"], p["z"],
+                         p["state_in"], dy, dstate)
+    assert np.array_equal(g["dx"], plain["dx"]) and np.array_equal(g["dA"], plain["dA"])
+    assert g["ddelta_raw"][0, 0, 0] == plain["ddelta"][0, 0, 0] / 2.0
+
+
 def pin_bwd_adjoint_identities(o):
     """y is linear in x (zero carried-in state), and, without the skip term,
     in Bt, in Ct and in the carried-in state (x = 0 for the last): for each,
@@ -634,7 +669,7 @@ def pin_bwd_adjoint_identities(o):
     assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs)), (lhs, rhs)
 
 
-ALL_PINS = [pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
+ALL_PINS = [pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
             pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
