@@ -164,13 +164,16 @@ def bench_scan(args, name):
     ys = [torch.empty_like(s["x"]) for s in sets]
     if bw:
         f32 = torch.float32
-        ys = [{"dx": torch.empty_like(s["x"]), "ddelta": torch.empty_like(s["x"]),
+        ys = [{"dx": torch.empty_like(s["x"]), ("ddelta_raw" if sp else "ddelta"): torch.empty_like(s["x"]),
                "dz": torch.empty_like(s["x"]) if s["z"] is not None else None,
                "dA": torch.empty((cfg.D, cfg.N), dtype=f32, device="cuda"),
                "dBt": torch.empty((cfg.batch, cfg.L, cfg.N), dtype=f32, device="cuda"),
                "dCt": torch.empty((cfg.batch, cfg.L, cfg.N), dtype=f32, device="cuda"),
                "dDskip": torch.empty((cfg.D,), dtype=f32, device="cuda") if Dskip is not None else None,
                "dstate_in": torch.empty((cfg.batch, cfg.D, cfg.N), dtype=f32, device="cuda")} for s in sets]
+        if sp:
+            for o_ in ys:
+                o_["ddt_bias"] = torch.empty((cfg.D,), dtype=f32, device="cuda")
         dstate = to_dev(W.grad_inputs(cfg, 0, 0)["dstate"])
         bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
                                                            0 if cfg.dtype == "f32" else 1),
@@ -183,7 +186,11 @@ def bench_scan(args, name):
 
     def step(i):
         s = sets[i % len(sets)]
-        if bw:
+        if bw and sp:
+            ssm.ssm_scan_bwd_dt(s["x"], s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip,
+                                z=s["z"], state_in=st_in, dstate=dstate, out=ys[i % len(sets)], workspace=bws,
+                                stream=stream)
+        elif bw:
             ssm.ssm_scan_bwd(s["x"], s["delta"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip, z=s["z"],
                              state_in=st_in, dstate=dstate, out=ys[i % len(sets)], workspace=bws, stream=stream)
         elif sp:
@@ -208,7 +215,7 @@ def bench_scan(args, name):
                     (W.trap_extra_bytes(cfg) if tr else 0), "dtype": cfg.dtype,
            "parity": None, "cpu": None}
     if bw:
-        out["bytes"] = W.scan_bwd_bytes(cfg)
+        out["bytes"] = W.scan_bwd_bytes(cfg) + (2 * cfg.D * 4 if sp else 0)  # dt_bias read, ddt_bias written
         if inp is not None and not args.no_cpu:
             import oracle
             torch.cuda.synchronize()
@@ -219,11 +226,12 @@ def bench_scan(args, name):
             reps, tot, ref = 0, 0.0, None
             while reps == 0 or tot < args.cpu_seconds:
                 t = time.perf_counter()
-                ref = o.scan_bwd(inp, grads["dy"], grads["dstate"], cfg.dtype)
+                ref = (o.scan_bwd_dt if sp else o.scan_bwd)(inp, grads["dy"], grads["dstate"], cfg.dtype)
                 tot += time.perf_counter() - t
                 reps += 1
             out["parity"] = {k: dict(zip(("relL2", "maxabs"), rel_l2(got[k], ref[k])))
-                             for k in ("dx", "ddelta", "dz", "dA", "dBt", "dCt", "dDskip", "dstate_in")
+                             for k in ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dz", "dA", "dBt", "dCt", "dDskip",
+                                       "dstate_in")
                              if ref.get(k) is not None}
             out["cpu"] = {"value": cfg.elems * reps / tot / 1e9, "unit": "G(B*L*D*N)-elem/s", "cores": 1,
                           "kind": "oracle",
@@ -450,8 +458,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    if args.backward and (args.softplus or args.trap or args.workload in ("c3", "c4", "ssd")):
-        ap.error("--backward times the gradient of the plain scan on c0, c1 or c2")
+    if args.backward and (args.trap or args.workload in ("c3", "c4", "ssd")):
+        ap.error("--backward times the gradient of the scan (or, with --softplus, of the scan with its step "
+                 "activated) on c0, c1 or c2")
     if args.workload == "ssd" and (args.softplus or args.trap):
         ap.error("--softplus and --trap apply to the S6 scan and step")
     if args.workload == "ssd":
@@ -511,7 +520,7 @@ def main():
             config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "selective-scan G(B*L*D*N)-elem/s"
         if args.backward:
-            config["pass"] = "gradient (ssm_scan_bwd), dstate given"
+            config["pass"] = "gradient (ssm_scan_bwd%s), dstate given" % ("_dt" if args.softplus else "")
             metric = "selective-scan gradient G(B*L*D*N)-elem/s"
     line = {
         "metric": metric,

@@ -310,6 +310,30 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                  void *dx, void *ddelta, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
                  float *dstate_in, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * ssm_scan_bwd for ssm_scan_fwd_dt: the step size is given before its
+ * activation, delta = softplus(delta_raw + dt_bias[d]). The gradient of the
+ * raw step size is that of delta times sigmoid(delta_raw + dt_bias), the
+ * derivative of softplus; the gradient of dt_bias sums it over batch and
+ * tokens. For bfloat16 activations the forward rounds the activated step to
+ * bfloat16; the gradient takes that rounding as the identity.
+ *
+ *   delta_raw     (batch, L, D)  dtype      step size before its activation
+ *   dt_bias       (D)            float      NULL = zero bias
+ *   ddelta_raw    (batch, L, D)  dtype      written
+ *   ddt_bias      (D)            float      written; NULL = not written
+ *
+ * Every other argument, the workspace (ssm_scan_bwd_workspace_bytes) and the
+ * status codes are those of ssm_scan_bwd.
+ */
+int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                    const void *x, const void *delta_raw, const float *dt_bias, const float *A,
+                    const void *Bt, const void *Ct, const float *Dskip, const void *z, const float *state_in,
+                    const void *dy, const float *dstate,
+                    void *dx, void *ddelta_raw, float *ddt_bias, float *dA, float *dBt, float *dCt,
+                    float *dDskip, void *dz, float *dstate_in, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,8 @@ Functions (same names as the C ABI):
   ssm_scan_bwd(x, delta, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None,
                dstate=None) -> dict: the gradient of ssm_scan_fwd (dx, ddelta,
       dA, dBt, dCt, dDskip, dz, dstate_in)
+  ssm_scan_bwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, dy, ...) -> dict: the same for
+      ssm_scan_fwd_dt, with ddelta_raw and ddt_bias in place of ddelta
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_scan_bwd_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
@@ -31,7 +33,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_bwd", "ssm_scan_workspace_bytes",
+    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
@@ -47,7 +49,7 @@ lib_path = os.path.join(_HERE, "libssm.so")
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_bwd_workspace_bytes.restype = sz
     L.ssm_scan_bwd.argtypes = [i64, i64, i64, i64, ci] + [vp] * 18 + [vp, sz, vp]
     L.ssm_scan_bwd.restype = ci
+    L.ssm_scan_bwd_dt.argtypes = [i64, i64, i64, i64, ci] + [vp] * 20 + [vp, sz, vp]
+    L.ssm_scan_bwd_dt.restype = ci
     _lib = L
     return L
 
@@ -299,13 +303,7 @@ def ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None, 
     return y
 
 
-def ssm_scan_bwd(x, delta, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None, dstate=None, out=None,
-                 workspace=None, stream=None):
-    """Gradient of ssm_scan_fwd for the loss sum(dy * y) + sum(dstate * state_out).
-    Inputs as for ssm_scan_fwd; dy like x; dstate (batch, D, N) float32 or None.
-    Returns a dict: dx, ddelta, dz (like x; dz None without a gate), dA (D, N),
-    dBt, dCt (batch, L, N), dDskip (D,) or None, dstate_in (batch, D, N), all
-    float32 but the first three. `out` may hold preallocated outputs by those names."""
+def _scan_bwd(name, x, delta, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate, out, workspace, stream):
     import torch
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, D) and A (D, N)")
@@ -313,31 +311,60 @@ def ssm_scan_bwd(x, delta, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None, dst
     N = A.shape[1]
     act, f32 = x.dtype, torch.float32
     code = _dtype_code(x)
+    sp = name == "ssm_scan_bwd_dt"
+    dn = "ddelta_raw" if sp else "ddelta"
     o = dict(out or {})
     new = lambda shape, dt: torch.empty(shape, dtype=dt, device=x.device)
     o.setdefault("dx", torch.empty_like(x))
-    o.setdefault("ddelta", torch.empty_like(x))
+    o.setdefault(dn, torch.empty_like(x))
     o.setdefault("dz", None if z is None else torch.empty_like(x))
     o.setdefault("dA", new((D, N), f32))
     o.setdefault("dBt", new((batch, L, N), f32))
     o.setdefault("dCt", new((batch, L, N), f32))
     o.setdefault("dDskip", None if Dskip is None else new((D,), f32))
     o.setdefault("dstate_in", new((batch, D, N), f32))
+    if sp:
+        o.setdefault("ddt_bias", new((D,), f32))
     ws_bytes = ssm_scan_bwd_workspace_bytes(batch, L, D, N, code)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(A, "A", f32, (D, N)),
-            _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
-            _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
-            _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(dy, "dy", act, (batch, L, D)),
-            _ptr(dstate, "dstate", f32, (batch, D, N)),
-            _ptr(o["dx"], "dx", act, (batch, L, D)), _ptr(o["ddelta"], "ddelta", act, (batch, L, D)),
-            _ptr(o["dA"], "dA", f32, (D, N)), _ptr(o["dBt"], "dBt", f32, (batch, L, N)),
-            _ptr(o["dCt"], "dCt", f32, (batch, L, N)), _ptr(o["dDskip"], "dDskip", f32, (D,)),
-            _ptr(o["dz"], "dz", act, (batch, L, D)), _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
+    args = [_ptr(x, "x", act), _ptr(delta, "delta_raw" if sp else "delta", act, (batch, L, D))]
+    if sp:
+        args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
+    args += [_ptr(A, "A", f32, (D, N)),
+             _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
+             _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+             _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(dy, "dy", act, (batch, L, D)),
+             _ptr(dstate, "dstate", f32, (batch, D, N)),
+             _ptr(o["dx"], "dx", act, (batch, L, D)), _ptr(o[dn], dn, act, (batch, L, D))]
+    if sp:
+        args.append(_ptr(o["ddt_bias"], "ddt_bias", f32, (D,)))
+    args += [_ptr(o["dA"], "dA", f32, (D, N)), _ptr(o["dBt"], "dBt", f32, (batch, L, N)),
+             _ptr(o["dCt"], "dCt", f32, (batch, L, N)), _ptr(o["dDskip"], "dDskip", f32, (D,)),
+             _ptr(o["dz"], "dz", act, (batch, L, D)), _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
     ws_ptr = _ptr(workspace, "workspace")
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ssm_scan_bwd(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
+    st = getattr(lib(), name)(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
     if st != 0:
-        raise SSMError(st, "ssm_scan_bwd")
+        raise SSMError(st, name)
     return o
+
+
+def ssm_scan_bwd(x, delta, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None, dstate=None, out=None,
+                 workspace=None, stream=None):
+    """Gradient of ssm_scan_fwd for the loss sum(dy * y) + sum(dstate * state_out).
+    Inputs as for ssm_scan_fwd; dy like x; dstate (batch, D, N) float32 or None.
+    Returns a dict: dx, ddelta, dz (like x; dz None without a gate), dA (D, N),
+    dBt, dCt (batch, L, N), dDskip (D,) or None, dstate_in (batch, D, N), all
+    float32 but the first three. `out` may hold preallocated outputs by those names."""
+    return _scan_bwd("ssm_scan_bwd", x, delta, None, A, Bt, Ct, dy, Dskip, z, state_in, dstate, out, workspace,
+                     stream)
+
+
+def ssm_scan_bwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, dy, Dskip=None, z=None, state_in=None, dstate=None,
+                    out=None, workspace=None, stream=None):
+    """Gradient of ssm_scan_fwd_dt (step size softplus(delta_raw + dt_bias)).
+    As ssm_scan_bwd, with ddelta_raw (like x) in place of ddelta and ddt_bias
+    (D,) float32 (set out["ddt_bias"] = None to leave it out)."""
+    return _scan_bwd("ssm_scan_bwd_dt", x, delta_raw, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate, out,
+                     workspace, stream)

@@ -303,21 +303,21 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
     return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
-// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD].
+// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD | pdT].
 struct BwdLayout {
     int64_t K;
-    size_t off[7], bytes;
+    size_t off[8], bytes;
 };
 
 static BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N) {
     BwdLayout w{};
     w.K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
     const int64_t nDB = ssm::bwd_channel_blocks(D, N);
-    const size_t sz[7] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
+    const size_t sz[8] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
                           (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
-                          (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D)};
+                          (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D)};
     size_t off = kHeader;
-    for (int i = 0; i < 7; ++i) {
+    for (int i = 0; i < 8; ++i) {
         w.off[i] = off;
         off += round_up256(sz[i] * sizeof(float));
     }
@@ -345,12 +345,15 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t
     return bwd_layout(batch, L, D, N).bytes;
 }
 
-int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
-                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
-                 const float *Dskip, const void *z, const float *state_in,
-                 const void *dy, const float *dstate,
-                 void *dx, void *ddelta, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
-                 float *dstate_in, void *workspace, size_t workspace_bytes, void *stream) {
+// The gradient, for a step size given after its activation (softplus = 0) or
+// before it (softplus = 1: delta holds delta_raw, ddelta receives its
+// gradient, and ddt_bias, when given, the gradient of dt_bias).
+static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                    const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
+                    const void *Bt, const void *Ct, const float *Dskip, const void *z, const float *state_in,
+                    const void *dy, const float *dstate,
+                    void *dx, void *ddelta, float *ddt_bias, float *dA, float *dBt, float *dCt, float *dDskip,
+                    void *dz, float *dstate_in, void *workspace, size_t workspace_bytes, void *stream) {
     if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
@@ -358,7 +361,7 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     if (D > 0 && !dA) return SSM_ERR_NULL;
     if (z && !dz) return SSM_ERR_NULL;
     const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx, ddelta,
-                          dA, dBt, dCt, dDskip, dz, dstate_in, workspace};
+                          dA, dBt, dCt, dDskip, dz, dstate_in, workspace, dt_bias, ddt_bias};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
@@ -368,6 +371,7 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         // and the gradient of the entering state is that of the leaving one
         if (ssm::launch_state_copy(nullptr, dA, D * N, s) != hipSuccess) return SSM_ERR_HIP;
         if (Dskip && dDskip && ssm::launch_state_copy(nullptr, dDskip, D, s) != hipSuccess) return SSM_ERR_HIP;
+        if (ddt_bias && ssm::launch_state_copy(nullptr, ddt_bias, D, s) != hipSuccess) return SSM_ERR_HIP;
         if (dstate_in && dstate_in != dstate &&
             ssm::launch_state_copy(dstate, dstate_in, batch * D * N, s) != hipSuccess)
             return SSM_ERR_HIP;
@@ -400,6 +404,9 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.dCt = dCt;
     a.dDskip = Dskip ? dDskip : nullptr;
     a.dstate_in = dstate_in;
+    a.dt_bias = dt_bias;
+    a.delta_softplus = softplus;
+    a.ddt_bias = softplus ? ddt_bias : nullptr;
     a.hst = (float *)(ws + w.off[0]);
     a.dsum = (float *)(ws + w.off[1]);
     a.gq = (float *)(ws + w.off[2]);
@@ -407,7 +414,30 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.pdC = (float *)(ws + w.off[4]);
     a.pdA = (float *)(ws + w.off[5]);
     a.pdD = (float *)(ws + w.off[6]);
+    a.pdT = (float *)(ws + w.off[7]);
     return ssm::launch_scan_bwd(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                 const float *Dskip, const void *z, const float *state_in,
+                 const void *dy, const float *dstate,
+                 void *dx, void *ddelta, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
+                 float *dstate_in, void *workspace, size_t workspace_bytes, void *stream) {
+    return scan_bwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx,
+                    ddelta, nullptr, dA, dBt, dCt, dDskip, dz, dstate_in, workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                    const void *x, const void *delta_raw, const float *dt_bias, const float *A,
+                    const void *Bt, const void *Ct, const float *Dskip, const void *z, const float *state_in,
+                    const void *dy, const float *dstate,
+                    void *dx, void *ddelta_raw, float *ddt_bias, float *dA, float *dBt, float *dCt,
+                    float *dDskip, void *dz, float *dstate_in, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return scan_bwd(batch, L, D, N, dtype, x, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state_in, dy, dstate,
+                    dx, ddelta_raw, ddt_bias, dA, dBt, dCt, dDskip, dz, dstate_in, workspace, workspace_bytes,
+                    stream);
 }
 
 int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,

@@ -88,8 +88,11 @@ struct BwdArgs {
     int64_t batch, L, D, K;  // K = ceil(L / kBwdChunk) chunks
     const void *x, *delta, *Bt, *Ct, *z, *dy;
     const float *A, *Dskip, *state_in, *dstate;
-    void *dx, *ddelta, *dz;
+    const float *dt_bias;  // per-channel bias of the raw step size (NULL = 0)
+    int delta_softplus;    // delta holds the raw step size: the scan used softplus(delta + dt_bias)
+    void *dx, *ddelta, *dz;  // with delta_softplus, ddelta is the gradient of the raw step size
     float *dA, *dBt, *dCt, *dDskip, *dstate_in;
+    float *ddt_bias;       // gradient of dt_bias (NULL = not written)
     // workspace
     float *hst;         // (batch, K, D, N) state entering each chunk
     float *dsum;        // (batch, K, D)    summed delta per chunk
@@ -97,6 +100,7 @@ struct BwdArgs {
     float *pdB, *pdC;   // (bwd_channel_blocks, batch, L, N) per-block partial sums
     float *pdA;         // (batch, K, D, N) per-chunk partial sums
     float *pdD;         // (batch, K, D)
+    float *pdT;         // (batch, K, D)    partial sums of ddt_bias
 };
 hipError_t launch_scan_bwd(const BwdArgs &a, int N, int dtype, hipStream_t s);
 // Channel blocks of the gradient's chunk kernel (256 lanes; two lanes per

@@ -34,6 +34,14 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int kSub = 8;  // tokens per recomputed block
 
+// The step size of a token: given, or softplus(raw + bias) rounded to the
+// activation dtype, as the forward scan computes it.
+template <int DT, typename T>
+__device__ __forceinline__ float delta_at(const T *dp, int64_t row, bool sp, float dtb) {
+    const float v = ld_act(dp, row);
+    return sp ? act_round<DT>(softplus(v + dtb)) : v;
+}
+
 // silu(z) and its derivative sigmoid(z) (1 + z (1 - sigmoid(z))).
 __device__ __forceinline__ void silu_and_grad(float z, float &g, float &dg) {
     const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * kLog2e));
@@ -118,7 +126,7 @@ __device__ __forceinline__ int wave_sum_index(int lane) {
 // and its summed delta. In token order, R_k is the sum of C_t ds_t times the
 // product of a_s over the chunk's tokens up to and including t, so the decay
 // a_t of each token serves both summaries.
-template <int N, int DT, bool GATE>
+template <int N, int DT, bool GATE, bool SP>
 __global__ __launch_bounds__(kBwdThreads) void bwd_summary_kernel(BwdArgs a) {
     using T = typename Act<DT>::T;
     const int64_t D = a.D, L = a.L, K = a.K;
@@ -139,10 +147,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_summary_kernel(BwdArgs a) {
     }
     const T *xp = (const T *)a.x, *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
     const T *Bp = (const T *)a.Bt, *Cp = (const T *)a.Ct;
+    constexpr bool sp = SP;
+    const float dtb = (SP && a.dt_bias) ? a.dt_bias[dc] : 0.0f;
     float dsum = 0.0f;
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t row = (b * L + t) * D + dc;
-        const float dt = ld_act(dp, row), dtx = dt * ld_act(xp, row);
+        const float dt = delta_at<DT>(dp, row, sp, dtb), dtx = dt * ld_act(xp, row);
         float ds = ld_act(gp, row);
         if (GATE) {
             float g, dg;
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
 // own a channel, 8 elements each (lanes l and l + 32 of a wave), so that the
 // recomputed states of 8 tokens fit in registers; their per-channel sums meet
 // through one exchange. Bt and Ct of the chunk are staged in LDS.
-template <int N, int DT, bool GATE, bool SKIP>
+template <int N, int DT, bool GATE, bool SKIP, bool SP>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     using T = typename Act<DT>::T;
     constexpr int NP = N < 8 ? N : 8;        // state elements per lane
@@ -255,6 +265,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     const int64_t t0 = k * kBwdChunk, t1 = t0 + kBwdChunk < L ? t0 + kBwdChunk : L;
     const int cnt_chunk = (int)(t1 - t0);
     const T *xp = (const T *)a.x, *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
+    constexpr bool sp = SP;
+    const float dtb = (SP && a.dt_bias) ? a.dt_bias[dc] : 0.0f;
     for (int i = tid; i < kBwdChunk * N; i += kBwdThreads) {
         const int j = i / N, n = i % N;
         const bool in = j < cnt_chunk;
@@ -280,13 +292,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             for (int i = 0; i < NP; ++i) ck[j / kSub][i][tid] = h[i];
         }
         const int64_t row = (b * L + t0 + j) * D + dc;
-        const float dt = ld_act(dp, row), dx = dt * ld_act(xp, row);
+        const float dt = delta_at<DT>(dp, row, sp, dtb), dx = dt * ld_act(xp, row);
 #pragma unroll
         for (int i = 0; i < NP; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), h[i], dx * sB[j][n0 + i]);
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) ck[nblk - 1][i][tid] = h[i];
-    float dA[NP], dD = 0.0f;
+    float dA[NP], dD = 0.0f, dT = 0.0f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) dA[i] = 0.0f;
     const float dsk = SKIP ? a.Dskip[dc] : 0.0f;
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         for (int j = 0; j < kSub; ++j) {
             if (j < cnt) {
                 const int64_t row = (b * L + t0 + s0 + j) * D + dc;
-                const float dt = ld_act(dp, row), dx = dt * ld_act(xp, row);
+                const float dt = delta_at<DT>(dp, row, sp, dtb), dx = dt * ld_act(xp, row);
 #pragma unroll
                 for (int i = 0; i < NP; ++i)
                     hb[j + 1][i] = __builtin_fmaf(fast_exp2(dt * A2[i]), hb[j][i], dx * sB[s0 + j][n0 + i]);
@@ -313,7 +325,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             if (j >= cnt) continue;
             const int tl = s0 + j;
             const int64_t row = (b * L + t0 + tl) * D + dc;
-            const float dt = ld_act(dp, row), xv = ld_act(xp, row), dyv = ld_act(gp, row);
+            const float raw = ld_act(dp, row), xv = ld_act(xp, row), dyv = ld_act(gp, row);
+            const float dt = sp ? act_round<DT>(softplus(raw + dtb)) : raw;
             float gate = 1.0f, dgate = 0.0f;
             if (GATE) silu_and_grad(ld_act(zp, row), gate, dgate);
             const float ds = valid ? dyv * gate : 0.0f;
@@ -347,7 +360,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             dD = __builtin_fmaf(ds, xv, dD);
             if (valid && r == 0) {
                 st_act((T *)a.dx, row, gx);
-                st_act((T *)a.ddelta, row, gdt);
+                // through the activation: d softplus(u) / du = sigmoid(u)
+                const float g = sp ? gdt * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-(raw + dtb) * kLog2e)) : gdt;
+                dT += g;
+                st_act((T *)a.ddelta, row, g);
                 if (GATE) st_act((T *)a.dz, row, dyv * pre * dgate);
             }
             const float sc = wave_sum_vec<NP, SPAN>(dCv, lane);
@@ -374,7 +390,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     if (!valid) return;
 #pragma unroll
     for (int i = 0; i < NP; ++i) a.pdA[((b * K + k) * D + d) * N + n0 + i] = dA[i];
-    if (r == 0) a.pdD[(b * K + k) * D + d] = dD;
+    if (r == 0) {
+        a.pdD[(b * K + k) * D + d] = dD;
+        a.pdT[(b * K + k) * D + d] = dT;
+    }
     if (k == 0 && a.dstate_in) {
 #pragma unroll
         for (int i = 0; i < NP; ++i) a.dstate_in[(b * D + d) * N + n0 + i] = G[i];
@@ -400,17 +419,17 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part, int6
     out[i] = s;
 }
 
-template <int N, int DT, bool GATE, bool SKIP>
+template <int N, int DT, bool GATE, bool SKIP, bool SP>
 hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
     const int64_t D = a.D, K = a.K;
     const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads;
     if (K > 1)
-        hipLaunchKernelGGL((bwd_summary_kernel<N, DT, GATE>), dim3((unsigned)(nb * K * a.batch)), dim3(kBwdThreads),
+        hipLaunchKernelGGL((bwd_summary_kernel<N, DT, GATE, SP>), dim3((unsigned)(nb * K * a.batch)), dim3(kBwdThreads),
                            0, s, a);
     const int64_t total = a.batch * D * N;
     hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     const int64_t ncb = bwd_channel_blocks(D, N);
-    hipLaunchKernelGGL((bwd_chunk_kernel<N, DT, GATE, SKIP>), dim3((unsigned)(ncb * K * a.batch)),
+    hipLaunchKernelGGL((bwd_chunk_kernel<N, DT, GATE, SKIP, SP>), dim3((unsigned)(ncb * K * a.batch)),
                        dim3(kBwdThreads), 0, s, a);
     const int64_t bln = a.batch * a.L * N;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdB, ncb, bln,
@@ -422,21 +441,29 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
     if (a.dDskip)
         hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0, s, a.pdD, a.batch * K,
                            D, a.dDskip, D);
+    if (a.ddt_bias)
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0, s, a.pdT, a.batch * K,
+                           D, a.ddt_bias, D);
     return hipGetLastError();
 }
 
-template <int N, int DT>
+template <int N, int DT, bool SP>
 hipError_t launch_bwd_flags(const BwdArgs &a, hipStream_t s) {
     const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
-    if (gate && skip) return launch_bwd_typed<N, DT, true, true>(a, s);
-    if (gate) return launch_bwd_typed<N, DT, true, false>(a, s);
-    if (skip) return launch_bwd_typed<N, DT, false, true>(a, s);
-    return launch_bwd_typed<N, DT, false, false>(a, s);
+    if (gate && skip) return launch_bwd_typed<N, DT, true, true, SP>(a, s);
+    if (gate) return launch_bwd_typed<N, DT, true, false, SP>(a, s);
+    if (skip) return launch_bwd_typed<N, DT, false, true, SP>(a, s);
+    return launch_bwd_typed<N, DT, false, false, SP>(a, s);
+}
+
+template <int N, int DT>
+hipError_t launch_bwd_act(const BwdArgs &a, hipStream_t s) {
+    return a.delta_softplus ? launch_bwd_flags<N, DT, true>(a, s) : launch_bwd_flags<N, DT, false>(a, s);
 }
 
 template <int N>
 hipError_t launch_bwd_dtype(const BwdArgs &a, int dtype, hipStream_t s) {
-    return dtype == 0 ? launch_bwd_flags<N, 0>(a, s) : launch_bwd_flags<N, 1>(a, s);
+    return dtype == 0 ? launch_bwd_act<N, 0>(a, s) : launch_bwd_act<N, 1>(a, s);
 }
 
 }  // namespace

@@ -129,9 +129,10 @@ def gpu_ssd(inp, want_state=True):
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
 
 
-def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False):
-    """Run ssm_scan_bwd on stored inputs and upstream gradients; returns a dict
-    of float64 arrays with the oracle's keys (dDskip/dz None when absent)."""
+def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False, raw=False, want_dbias=True):
+    """Run ssm_scan_bwd (or, with raw, ssm_scan_bwd_dt on delta_raw and dt_bias)
+    on stored inputs and upstream gradients; returns a dict of float64 arrays
+    with the oracle's keys (dDskip/dz None when absent)."""
     import torch
     dev = {k: to_dev(v) for k, v in inp.items()}
     dy, dstate = to_dev(grads["dy"]), to_dev(grads.get("dstate"))
@@ -140,8 +141,14 @@ def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False):
         out["dstate_in"] = dstate
     if not want_dskip:
         out["dDskip"] = None
-    g = ssm.ssm_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], dy, Dskip=dev["Dskip"],
-                         z=dev["z"], state_in=dev["state_in"], dstate=dstate, out=out)
+    if raw:
+        if not want_dbias:
+            out["ddt_bias"] = None
+        g = ssm.ssm_scan_bwd_dt(dev["x"], dev["delta_raw"], dev.get("dt_bias"), dev["A"], dev["Bt"], dev["Ct"], dy,
+                                Dskip=dev["Dskip"], z=dev["z"], state_in=dev["state_in"], dstate=dstate, out=out)
+    else:
+        g = ssm.ssm_scan_bwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], dy, Dskip=dev["Dskip"],
+                             z=dev["z"], state_in=dev["state_in"], dstate=dstate, out=out)
     torch.cuda.synchronize()
     return {k: (None if v is None else to_f64(v)) for k, v in g.items()}
 
@@ -154,7 +161,7 @@ def check_grads(got, ref, dtype, keys=None):
     """Every gradient against the oracle's: relative L2 as for the outputs;
     for float32, max-abs 1e-4 scaled by the largest reference magnitude (the
     parameter gradients are sums over many tokens and channels)."""
-    for k in keys or ("dx", "ddelta", "dz", "dA", "dBt", "dCt", "dDskip", "dstate_in"):
+    for k in keys or ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dz", "dA", "dBt", "dCt", "dDskip", "dstate_in"):
         if ref.get(k) is None:
             assert got.get(k) is None, k + " written but not expected"
             continue

@@ -252,3 +252,27 @@ def test_scan_bwd_workspace_bytes():
 
 def test_scan_bwd_empty_ok_without_gpu():
     assert bwd(D=0) == 0
+
+
+def bwd_dt(**kw):
+    a = dict(batch=2, L=100, D=64, N=16, dtype=0, x=P, delta=P, dt_bias=None, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             state_in=None, dy=P, dstate=None, dx=P, ddelta=P, ddt_bias=None, dA=P, dBt=P, dCt=P, dDskip=None,
+             dz=None, dstate_in=None, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_bwd_dt(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["delta"],
+                                     a["dt_bias"], a["A"], a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state_in"],
+                                     a["dy"], a["dstate"], a["dx"], a["ddelta"], a["ddt_bias"], a["dA"], a["dBt"],
+                                     a["dCt"], a["dDskip"], a["dz"], a["dstate_in"], a["ws"], a["ws_bytes"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=5), -4), (dict(dA=None), -1), (dict(delta=None), -1),
+    (dict(ddelta=None), -1), (dict(dt_bias=MIS), -5), (dict(ddt_bias=MIS), -5), (dict(ws_bytes=1), -6),
+])
+def test_scan_bwd_dt_rejects(kw, code):
+    assert bwd_dt(**kw) == code
+
+
+def test_scan_bwd_dt_empty_ok_without_gpu():
+    assert bwd_dt(D=0) == 0

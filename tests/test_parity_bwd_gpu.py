@@ -143,3 +143,38 @@ def test_bwd_large_layer_sampled():
 def dataclass_replace(cfg, **kw):
     import dataclasses
     return dataclasses.replace(cfg, **kw)
+
+
+def _run_raw(cfg, bias=True, want_dbias=True):
+    say(f"case {cfg} raw delta, dt_bias={'given' if bias else 'NULL'}")
+    inp = W.scan_inputs(cfg, raw_delta=True)
+    if not bias:
+        inp["dt_bias"] = None
+    grads = W.grad_inputs(cfg)
+    got = gpu_scan_bwd(inp, grads, raw=True, want_dbias=want_dbias)
+    ref = oracle.get().scan_bwd_dt(inp, grads["dy"], grads["dstate"], cfg.dtype)
+    if not want_dbias:
+        assert got["ddt_bias"] is None
+        ref["ddt_bias"] = None
+    check_grads(got, ref, cfg.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bias", [True, False])
+def test_bwd_raw_delta(dtype, bias):
+    """ssm_scan_bwd_dt: the step size activated in the kernel, softplus(raw + bias)."""
+    _run_raw(_cfg("bwd_raw", 2, 100, 200, 16, dtype), bias=bias)
+
+
+@pytest.mark.parametrize("N", [1, 4, 8])
+def test_bwd_raw_delta_state_sizes(N):
+    _run_raw(_cfg(f"bwd_raw_N{N}", 1, 77, 130, N, "f32"))
+
+
+def test_bwd_raw_delta_without_bias_gradient():
+    _run_raw(_cfg("bwd_raw_nob", 1, 40, 64, 16, "bf16"), want_dbias=False)
+
+
+def test_bwd_raw_delta_small_layer_whole():
+    """The small-layer workload with its step size given before the activation."""
+    _run_raw(dataclass_replace(W.SCAN_CONFIGS["c1"], state_in=0.3))
