@@ -68,6 +68,8 @@ class Oracle:
         self.lib.oracle_scan_bwd.argtypes = [i64] * 4 + [_DP] * 18
         self.lib.oracle_scan_bwd.restype = ci
         self.lib.oracle_softplus_grad.argtypes = [i64, i64] + [_DP] * 5
+        self.lib.oracle_scan_bwd_trap.argtypes = [i64] * 4 + [_DP] * 24
+        self.lib.oracle_scan_bwd_trap.restype = ci
         self.lib.oracle_softplus_grad.restype = ci
 
     def threads(self, nthreads: int = 0) -> int:
@@ -207,6 +209,37 @@ class Oracle:
             raise ValueError("oracle_scan_bwd rejected sizes")
         return out
 
+    def scan_bwd_trap64(self, x, delta, lam, A, Bt, Ct, Dskip, z, x_prev, B_prev, state_in, dy, dstate=None):
+        """Gradient of scan_trap64 for the loss sum(dy * y) + sum(dstate * state_out).
+        Returns scan_bwd64's dict plus dlam, and dx_prev, dB_prev (None unless
+        x_prev and B_prev are given)."""
+        x = _c64(x)
+        batch, L, D = x.shape
+        A = _c64(A)
+        N = A.shape[1]
+        delta, lam, Bt, Ct, dy = _c64(delta), _c64(lam), _c64(Bt), _c64(Ct), _c64(dy)
+        assert delta.shape == x.shape and lam.shape == x.shape and dy.shape == x.shape
+        assert Bt.shape == (batch, L, N) and Ct.shape == Bt.shape
+        opt = lambda a, shape: None if a is None else _c64(a).reshape(shape)
+        Dskip, z = opt(Dskip, (D,)), opt(z, x.shape)
+        x_prev, B_prev = opt(x_prev, (batch, D)), opt(B_prev, (batch, N))
+        state_in, dstate = opt(state_in, (batch, D, N)), opt(dstate, (batch, D, N))
+        prev = x_prev is not None and B_prev is not None
+        out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dlam": np.empty_like(x), "dA": np.empty((D, N)),
+               "dBt": np.empty((batch, L, N)), "dCt": np.empty((batch, L, N)),
+               "dDskip": None if Dskip is None else np.empty(D), "dz": None if z is None else np.empty_like(x),
+               "dx_prev": np.empty((batch, D)) if prev else None, "dB_prev": np.empty((batch, N)) if prev else None,
+               "dstate_in": np.empty((batch, D, N))}
+        rc = self.lib.oracle_scan_bwd_trap(batch, L, D, N, _p(x), _p(delta), _p(lam), _p(A), _p(Bt), _p(Ct),
+                                           _p(Dskip), _p(z), _p(x_prev), _p(B_prev), _p(state_in), _p(dy),
+                                           _p(dstate), _p(out["dx"]), _p(out["ddelta"]), _p(out["dlam"]),
+                                           _p(out["dA"]), _p(out["dBt"]), _p(out["dCt"]), _p(out["dDskip"]),
+                                           _p(out["dz"]), _p(out["dx_prev"]), _p(out["dB_prev"]),
+                                           _p(out["dstate_in"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd_trap rejected sizes")
+        return out
+
     def scan_bwd_dt64(self, x, delta_raw, dt_bias, A, Bt, Ct, Dskip, z, state_in, dy, dstate=None):
         """Gradient of the scan whose step size is softplus(delta_raw + dt_bias):
         scan_bwd64 on the activated step, then the chain rule through the
@@ -305,6 +338,14 @@ class Oracle:
         f32 = lambda a: None if a is None else upcast(a, "f32")
         return self.scan_bwd64(up(inp["x"]), up(inp["delta"]), f32(inp["A"]), up(inp["Bt"]), up(inp["Ct"]),
                                f32(inp.get("Dskip")), up(inp.get("z")), f32(inp.get("state_in")), up(dy), f32(dstate))
+
+    def scan_bwd_trap(self, inp: Dict[str, np.ndarray], dy, dstate, dtype: str):
+        """scan_bwd_trap64 on stored inputs (lam, x_prev, B_prev in the stored dtype)."""
+        up = lambda a: None if a is None else upcast(a, dtype)
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        return self.scan_bwd_trap64(up(inp["x"]), up(inp["delta"]), up(inp["lam"]), f32(inp["A"]), up(inp["Bt"]),
+                                    up(inp["Ct"]), f32(inp.get("Dskip")), up(inp.get("z")), up(inp.get("x_prev")),
+                                    up(inp.get("B_prev")), f32(inp.get("state_in")), up(dy), f32(dstate))
 
     def scan_bwd_dt(self, inp: Dict[str, np.ndarray], dy, dstate, dtype: str):
         """scan_bwd64_dt on stored inputs (delta_raw in the stored dtype, dt_bias float32 or None)."""

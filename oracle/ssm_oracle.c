@@ -153,6 +153,114 @@ int oracle_softplus_bias(int64_t rows, int64_t D, const double *raw, const doubl
 }
 
 /*
+ * Gradient of oracle_scan_trap for the loss sum(dy * y) + sum(dstate *
+ * state_out), by the chain rule through its recurrence (reverse mode, by
+ * hand). With G_t the gradient of h_t (from the readout of token t and from
+ * h_{t+1} = alpha_{t+1} h_t + ...):
+ *   G_t      = Ct[t] ds_t + alpha_{t+1} G_{t+1},        ds_t = dy_t silu(z_t)
+ *   dv_t     = gamma_t G_t + beta_{t+1} G_{t+1}          (v_t feeds h_t and h_{t+1})
+ *   ddelta_t = sum_n G_t (A alpha (h_{t-1} + (1 - lam) delta v_{t-1})
+ *                         + (1 - lam) alpha v_{t-1} + lam v_t)
+ *   dlam_t   = sum_n G_t delta (v_t - alpha v_{t-1})
+ *   dA       = sum_t G_t delta alpha (h_{t-1} + (1 - lam) delta v_{t-1})
+ *   dx_t     = sum_n dv_t Bt[t] (+ Dskip ds_t), dBt[t] = sum_d dv_t x_t
+ * and dv_{-1} = beta_0 G_0 for the token before the first: dx_prev =
+ * sum_n dv_{-1} B_prev, dB_prev = sum_d dv_{-1} x_prev (written only when
+ * x_prev and B_prev are given). dstate_in = alpha_0 G_0.
+ * Outputs (all written): dx, ddelta, dlam (batch, L, D); dA (D, N); dBt, dCt
+ * (batch, L, N); dDskip (D) when Dskip; dz when z; dx_prev (batch, D) and
+ * dB_prev (batch, N) when x_prev and B_prev; dstate_in (batch, D, N).
+ */
+int oracle_scan_bwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N,
+                         const double *x, const double *delta, const double *lam, const double *A,
+                         const double *Bt, const double *Ct, const double *Dskip, const double *z,
+                         const double *x_prev, const double *B_prev, const double *state_in,
+                         const double *dy, const double *dstate,
+                         double *dx, double *ddelta, double *dlam, double *dA, double *dBt, double *dCt,
+                         double *dDskip, double *dz, double *dx_prev, double *dB_prev, double *dstate_in)
+{
+    if (batch < 0 || L < 0 || D < 0 || N < 1 || N > 4096) return -1;
+    const int prev = x_prev && B_prev;
+    double *H = (double *)malloc((size_t)((L + 1) * N) * sizeof(double));  /* H[(t + 1) N + n] = h_t */
+    if (!H) return -1;
+    for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
+    for (int64_t i = 0; i < batch * L * N; ++i) dBt[i] = dCt[i] = 0.0;
+    if (Dskip)
+        for (int64_t d = 0; d < D; ++d) dDskip[d] = 0.0;
+    if (prev)
+        for (int64_t i = 0; i < batch * N; ++i) dB_prev[i] = 0.0;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            /* the input of token t - 1 (token -1: the earlier token, or none) */
+#define VPREV(t, n) ((t) > 0 ? Bt[IDX3(b, (t) - 1, n, L, N)] * x[IDX3(b, (t) - 1, d, L, D)] \
+                             : (prev ? B_prev[b * N + (n)] * x_prev[b * D + d] : 0.0))
+            for (int64_t n = 0; n < N; ++n) H[n] = state_in ? state_in[IDX3(b, d, n, D, N)] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double dt = delta[IDX3(b, t, d, L, D)], lm = lam[IDX3(b, t, d, L, D)], u = x[IDX3(b, t, d, L, D)];
+                for (int64_t n = 0; n < N; ++n) {
+                    double alpha = exp(dt * A[d * N + n]);
+                    H[(t + 1) * N + n] = alpha * H[t * N + n] + (1.0 - lm) * dt * alpha * VPREV(t, n)
+                                         + lm * dt * Bt[IDX3(b, t, n, L, N)] * u;
+                }
+            }
+            double G[4096], Gb[4096];  /* G_t; beta_{t+1} G_{t+1} */
+            for (int64_t n = 0; n < N; ++n) {
+                G[n] = dstate ? dstate[IDX3(b, d, n, D, N)] : 0.0;
+                Gb[n] = 0.0;
+            }
+            for (int64_t t = L - 1; t >= 0; --t) {
+                int64_t r = IDX3(b, t, d, L, D);
+                double dt = delta[r], lm = lam[r], u = x[r];
+                double sum = 0.0;
+                for (int64_t n = 0; n < N; ++n) sum += Ct[IDX3(b, t, n, L, N)] * H[(t + 1) * N + n];
+                if (Dskip) sum += Dskip[d] * u;
+                double gate = 1.0, dgate = 0.0;
+                if (z) {
+                    double zz = z[r], sg = 1.0 / (1.0 + exp(-zz));
+                    gate = zz * sg;
+                    dgate = sg * (1.0 + zz * (1.0 - sg));
+                    dz[r] = dy[r] * sum * dgate;
+                }
+                double ds = dy[r] * gate;
+                double gx = Dskip ? ds * Dskip[d] : 0.0;
+                if (Dskip) dDskip[d] += ds * u;
+                double gd = 0.0, gl = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    int64_t bn = IDX3(b, t, n, L, N);
+                    G[n] += Ct[bn] * ds;
+                    dCt[bn] += ds * H[(t + 1) * N + n];
+                    double alpha = exp(dt * A[d * N + n]);
+                    double v = Bt[bn] * u, vp = VPREV(t, n);
+                    double p = H[t * N + n] + (1.0 - lm) * dt * vp;
+                    double dv = lm * dt * G[n] + Gb[n];
+                    gx += dv * Bt[bn];
+                    dBt[bn] += dv * u;
+                    gd += G[n] * (A[d * N + n] * alpha * p + (1.0 - lm) * alpha * vp + lm * v);
+                    gl += G[n] * dt * (v - alpha * vp);
+                    dA[d * N + n] += G[n] * dt * alpha * p;
+                    Gb[n] = (1.0 - lm) * dt * alpha * G[n];
+                    G[n] *= alpha;
+                }
+                ddelta[r] = gd;
+                dlam[r] = gl;
+                dx[r] = gx;
+            }
+            if (prev) {
+                double gp = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    gp += Gb[n] * B_prev[b * N + n];
+                    dB_prev[b * N + n] += Gb[n] * x_prev[b * D + d];
+                }
+                dx_prev[b * D + d] = gp;
+            }
+            for (int64_t n = 0; n < N; ++n) dstate_in[IDX3(b, d, n, D, N)] = G[n];
+#undef VPREV
+        }
+    free(H);
+    return 0;
+}
+
+/*
  * Gradient through the step-size activation: with u = raw[r, d] + bias[d] and
  * delta = softplus(u), d delta / d u = sigmoid(u) = 1 / (1 + exp(-u)), so for
  * the gradient g of delta (rows, D):

@@ -644,6 +644,50 @@ def pin_bwd_dt_finite_differences(o):
     assert g["ddelta_raw"][0, 0, 0] == plain["ddelta"][0, 0, 0] / 2.0
 
 
+def pin_bwd_trap_finite_differences(o):
+    """The trapezoidal rule's gradient: every element of every gradient (dlam,
+    dx_prev and dB_prev included) against central differences of the loss of
+    the trapezoidal forward oracle, on a tiny problem with every optional part
+    and an earlier token; with lam = 1 it equals the Euler gradient, and the
+    earlier token gets none."""
+    rng = np.random.default_rng(44)
+    batch, L, D, N = 2, 5, 3, 4
+    p = _rand_problem(rng, batch, L, D, N)
+    p["lam"] = rng.uniform(0.0, 1.0, size=(batch, L, D))
+    p["x_prev"], p["B_prev"] = rng.normal(size=(batch, D)), rng.normal(size=(batch, N))
+    dy, dstate = rng.normal(size=(batch, L, D)), rng.normal(size=(batch, D, N))
+
+    def loss(q):
+        y, st = o.scan_trap64(q["x"], q["delta"], q["lam"], q["A"], q["Bt"], q["Ct"], q["Dskip"], q["z"],
+                              q["x_prev"], q["B_prev"], q["state_in"])
+        return float(np.sum(y * dy) + np.sum(st * dstate))
+
+    def grads(q):
+        return o.scan_bwd_trap64(q["x"], q["delta"], q["lam"], q["A"], q["Bt"], q["Ct"], q["Dskip"], q["z"],
+                                 q["x_prev"], q["B_prev"], q["state_in"], dy, dstate)
+
+    g = grads(p)
+    names = {"x": "dx", "delta": "ddelta", "lam": "dlam", "A": "dA", "Bt": "dBt", "Ct": "dCt", "Dskip": "dDskip",
+             "z": "dz", "x_prev": "dx_prev", "B_prev": "dB_prev", "state_in": "dstate_in"}
+    for k, gk in names.items():
+        base = p[k]
+        num = np.empty_like(base)
+        for i in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[i]))
+            q = dict(p)
+            q[k] = base.copy()
+            q[k][i] = base[i] + eps
+            up = loss(q)
+            q[k][i] = base[i] - eps
+            num[i] = (up - loss(q)) / (2 * eps)
+        assert np.allclose(g[gk], num, rtol=1e-6, atol=1e-7), (k, np.abs(g[gk] - num).max())
+    one = grads(dict(p, lam=np.ones_like(p["lam"])))
+    euler = o.scan_bwd64(p["x"], p["delta"], p["A"], p["Bt"], p["Ct"], p["Dskip"], p["z"], p["state_in"], dy, dstate)
+    for k in ("dx", "ddelta", "dA", "dBt", "dCt", "dDskip", "dz", "dstate_in"):
+        assert np.allclose(one[k], euler[k], rtol=1e-12, atol=1e-12), k
+    assert not one["dx_prev"].any() and not one["dB_prev"].any()
+
+
 def pin_bwd_adjoint_identities(o):
     """y is linear in x (zero carried-in state), and, without the skip term,
     in Bt, in Ct and in the carried-in state (x = 0 for the last): for each,
@@ -669,7 +713,7 @@ def pin_bwd_adjoint_identities(o):
     assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs)), (lhs, rhs)
 
 
-ALL_PINS = [pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
+ALL_PINS = [pin_bwd_trap_finite_differences, pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
             pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
