@@ -174,6 +174,11 @@ def bench_scan(args, name):
         if sp:
             for o_ in ys:
                 o_["ddt_bias"] = torch.empty((cfg.D,), dtype=f32, device="cuda")
+        if tr:
+            for o_, s_ in zip(ys, sets):
+                o_["dlam"] = torch.empty_like(s_["x"])
+                o_["dx_prev"] = torch.empty((cfg.batch, cfg.D), dtype=s_["x"].dtype, device="cuda")
+                o_["dB_prev"] = torch.empty((cfg.batch, cfg.N), dtype=f32, device="cuda")
         dstate = to_dev(W.grad_inputs(cfg, 0, 0)["dstate"])
         bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
                                                            0 if cfg.dtype == "f32" else 1),
@@ -186,7 +191,11 @@ def bench_scan(args, name):
 
     def step(i):
         s = sets[i % len(sets)]
-        if bw and sp:
+        if bw and tr:
+            ssm.ssm_scan_bwd_trap(s["x"], s["delta"], s["lam"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip, z=s["z"],
+                                  x_prev=s["x_prev"], B_prev=s["B_prev"], state_in=st_in, dstate=dstate,
+                                  out=ys[i % len(sets)], workspace=bws, stream=stream)
+        elif bw and sp:
             ssm.ssm_scan_bwd_dt(s["x"], s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip,
                                 z=s["z"], state_in=st_in, dstate=dstate, out=ys[i % len(sets)], workspace=bws,
                                 stream=stream)
@@ -216,6 +225,9 @@ def bench_scan(args, name):
            "parity": None, "cpu": None}
     if bw:
         out["bytes"] = W.scan_bwd_bytes(cfg) + (2 * cfg.D * 4 if sp else 0)  # dt_bias read, ddt_bias written
+        if tr:  # lam read and dlam written; x_prev, B_prev read and their gradients written
+            out["bytes"] += 2 * cfg.batch * cfg.L * cfg.D * W._esize(cfg.dtype) + \
+                2 * cfg.batch * (cfg.D * W._esize(cfg.dtype) + cfg.N * 4)
         if inp is not None and not args.no_cpu:
             import oracle
             torch.cuda.synchronize()
@@ -226,12 +238,13 @@ def bench_scan(args, name):
             reps, tot, ref = 0, 0.0, None
             while reps == 0 or tot < args.cpu_seconds:
                 t = time.perf_counter()
-                ref = (o.scan_bwd_dt if sp else o.scan_bwd)(inp, grads["dy"], grads["dstate"], cfg.dtype)
+                ref = (o.scan_bwd_trap if tr else o.scan_bwd_dt if sp else o.scan_bwd)(inp, grads["dy"], grads["dstate"],
+                                                                                       cfg.dtype)
                 tot += time.perf_counter() - t
                 reps += 1
             out["parity"] = {k: dict(zip(("relL2", "maxabs"), rel_l2(got[k], ref[k])))
-                             for k in ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dz", "dA", "dBt", "dCt", "dDskip",
-                                       "dstate_in")
+                             for k in ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dlam", "dz", "dA", "dBt", "dCt",
+                                       "dDskip", "dx_prev", "dB_prev", "dstate_in")
                              if ref.get(k) is not None}
             out["cpu"] = {"value": cfg.elems * reps / tot / 1e9, "unit": "G(B*L*D*N)-elem/s", "cores": 1,
                           "kind": "oracle",
@@ -458,9 +471,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    if args.backward and (args.trap or args.workload in ("c3", "c4", "ssd")):
-        ap.error("--backward times the gradient of the scan (or, with --softplus, of the scan with its step "
-                 "activated) on c0, c1 or c2")
+    if args.backward and args.workload in ("c3", "c4", "ssd"):
+        ap.error("--backward times the gradient of the scan (plain, --softplus or --trap) on c0, c1 or c2")
     if args.workload == "ssd" and (args.softplus or args.trap):
         ap.error("--softplus and --trap apply to the S6 scan and step")
     if args.workload == "ssd":
@@ -520,7 +532,8 @@ def main():
             config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "selective-scan G(B*L*D*N)-elem/s"
         if args.backward:
-            config["pass"] = "gradient (ssm_scan_bwd%s), dstate given" % ("_dt" if args.softplus else "")
+            config["pass"] = "gradient (ssm_scan_bwd%s), dstate given" % (
+                "_dt" if args.softplus else "_trap" if args.trap else "")
             metric = "selective-scan gradient G(B*L*D*N)-elem/s"
     line = {
         "metric": metric,

@@ -334,6 +334,36 @@ int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     float *dDskip, void *dz, float *dstate_in, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * ssm_scan_bwd for ssm_scan_fwd_trap: the gradient of the exponential-
+ * trapezoidal rule ("Notas sobre Mamba", section "Recorrência trapezoidal").
+ * With v_t = Bt[t] x_t, the state's gradient G_t runs back as in ssm_scan_bwd
+ * (each token's update multiplies the state by dA_t in both rules); v_t enters
+ * h_t with weight lam_t delta_t and h_{t+1} with (1 - lam_{t+1}) delta_{t+1}
+ * dA_{t+1}, and its gradient collects both. lam's gradient is
+ * delta_t sum_n G_t (v_t - dA_t v_{t-1}).
+ *
+ *   lam, x_prev, B_prev   as passed to ssm_scan_fwd_trap
+ *   dlam          (batch, L, D)  dtype      written
+ *   dx_prev       (batch, D)     dtype      gradient of x_prev   } written when
+ *   dB_prev       (batch, N)     float      gradient of B_prev   } x_prev, B_prev,
+ *                                           (summed over channels) both given
+ *
+ * Passing exactly one of x_prev and B_prev, or of dx_prev and dB_prev, or a
+ * NULL lam with a non-empty input, returns SSM_ERR_NULL; L = 0 leaves dx_prev
+ * and dB_prev unwritten. Every other argument, the workspace
+ * (ssm_scan_bwd_workspace_bytes) and the status codes are those of
+ * ssm_scan_bwd.
+ */
+int ssm_scan_bwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x, const void *delta, const void *lam, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                      const void *x_prev, const void *B_prev, const float *state_in,
+                      const void *dy, const float *dstate,
+                      void *dx, void *ddelta, void *dlam, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
+                      void *dx_prev, float *dB_prev, float *dstate_in, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

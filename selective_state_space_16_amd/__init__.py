@@ -21,6 +21,8 @@ Functions (same names as the C ABI):
       dA, dBt, dCt, dDskip, dz, dstate_in)
   ssm_scan_bwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, dy, ...) -> dict: the same for
       ssm_scan_fwd_dt, with ddelta_raw and ddt_bias in place of ddelta
+  ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, ...) -> dict: the same for
+      ssm_scan_fwd_trap, with dlam, and dx_prev, dB_prev for the earlier token
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_scan_bwd_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
@@ -33,7 +35,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_workspace_bytes",
+    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
@@ -49,7 +51,7 @@ lib_path = os.path.join(_HERE, "libssm.so")
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -96,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_bwd.restype = ci
     L.ssm_scan_bwd_dt.argtypes = [i64, i64, i64, i64, ci] + [vp] * 20 + [vp, sz, vp]
     L.ssm_scan_bwd_dt.restype = ci
+    L.ssm_scan_bwd_trap.argtypes = [i64, i64, i64, i64, ci] + [vp] * 24 + [vp, sz, vp]
+    L.ssm_scan_bwd_trap.restype = ci
     _lib = L
     return L
 
@@ -368,3 +372,50 @@ def ssm_scan_bwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, dy, Dskip=None, z=None, st
     (D,) float32 (set out["ddt_bias"] = None to leave it out)."""
     return _scan_bwd("ssm_scan_bwd_dt", x, delta_raw, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate, out,
                      workspace, stream)
+
+
+def ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, Dskip=None, z=None, x_prev=None, B_prev=None, state_in=None,
+                      dstate=None, out=None, workspace=None, stream=None):
+    """Gradient of ssm_scan_fwd_trap. As ssm_scan_bwd, plus dlam (like x) and,
+    when x_prev and B_prev are given, dx_prev (batch, D) in x's dtype and
+    dB_prev (batch, N) float32."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and A (D, N)")
+    batch, L, D = x.shape
+    N = A.shape[1]
+    act, f32 = x.dtype, torch.float32
+    code = _dtype_code(x)
+    o = dict(out or {})
+    new = lambda shape, dt: torch.empty(shape, dtype=dt, device=x.device)
+    for k in ("dx", "ddelta", "dlam"):
+        o.setdefault(k, torch.empty_like(x))
+    o.setdefault("dz", None if z is None else torch.empty_like(x))
+    o.setdefault("dA", new((D, N), f32))
+    o.setdefault("dBt", new((batch, L, N), f32))
+    o.setdefault("dCt", new((batch, L, N), f32))
+    o.setdefault("dDskip", None if Dskip is None else new((D,), f32))
+    o.setdefault("dx_prev", None if x_prev is None else new((batch, D), act))
+    o.setdefault("dB_prev", None if x_prev is None else new((batch, N), f32))
+    o.setdefault("dstate_in", new((batch, D, N), f32))
+    ws_bytes = ssm_scan_bwd_workspace_bytes(batch, L, D, N, code)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(lam, "lam", act, (batch, L, D)),
+            _ptr(A, "A", f32, (D, N)), _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
+            _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+            _ptr(x_prev, "x_prev", act, (batch, D)), _ptr(B_prev, "B_prev", act, (batch, N)),
+            _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(dy, "dy", act, (batch, L, D)),
+            _ptr(dstate, "dstate", f32, (batch, D, N)),
+            _ptr(o["dx"], "dx", act, (batch, L, D)), _ptr(o["ddelta"], "ddelta", act, (batch, L, D)),
+            _ptr(o["dlam"], "dlam", act, (batch, L, D)), _ptr(o["dA"], "dA", f32, (D, N)),
+            _ptr(o["dBt"], "dBt", f32, (batch, L, N)), _ptr(o["dCt"], "dCt", f32, (batch, L, N)),
+            _ptr(o["dDskip"], "dDskip", f32, (D,)), _ptr(o["dz"], "dz", act, (batch, L, D)),
+            _ptr(o["dx_prev"], "dx_prev", act, (batch, D)), _ptr(o["dB_prev"], "dB_prev", f32, (batch, N)),
+            _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
+    ws_ptr = _ptr(workspace, "workspace")
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_scan_bwd_trap(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_scan_bwd_trap")
+    return o

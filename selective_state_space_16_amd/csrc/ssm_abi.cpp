@@ -303,21 +303,22 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
     return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
-// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD | pdT].
+// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD | pdT | pdBp].
 struct BwdLayout {
     int64_t K;
-    size_t off[8], bytes;
+    size_t off[9], bytes;
 };
 
 static BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N) {
     BwdLayout w{};
     w.K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
     const int64_t nDB = ssm::bwd_channel_blocks(D, N);
-    const size_t sz[8] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
+    const size_t sz[9] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
                           (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
-                          (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D)};
+                          (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D),
+                          (size_t)(nDB * batch * N)};
     size_t off = kHeader;
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 9; ++i) {
         w.off[i] = off;
         off += round_up256(sz[i] * sizeof(float));
     }
@@ -348,12 +349,20 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t
 // The gradient, for a step size given after its activation (softplus = 0) or
 // before it (softplus = 1: delta holds delta_raw, ddelta receives its
 // gradient, and ddt_bias, when given, the gradient of dt_bias).
+// The trapezoidal rule's extra inputs and outputs.
+struct TrapBwd {
+    const void *lam = nullptr, *x_prev = nullptr, *B_prev = nullptr;
+    void *dlam = nullptr, *dx_prev = nullptr;
+    float *dB_prev = nullptr;
+};
+
 static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
                     const void *Bt, const void *Ct, const float *Dskip, const void *z, const float *state_in,
                     const void *dy, const float *dstate,
                     void *dx, void *ddelta, float *ddt_bias, float *dA, float *dBt, float *dCt, float *dDskip,
-                    void *dz, float *dstate_in, void *workspace, size_t workspace_bytes, void *stream) {
+                    void *dz, float *dstate_in, void *workspace, size_t workspace_bytes, void *stream,
+                    TrapBwd tr = {}) {
     if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
@@ -361,7 +370,8 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     if (D > 0 && !dA) return SSM_ERR_NULL;
     if (z && !dz) return SSM_ERR_NULL;
     const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx, ddelta,
-                          dA, dBt, dCt, dDskip, dz, dstate_in, workspace, dt_bias, ddt_bias};
+                          dA, dBt, dCt, dDskip, dz, dstate_in, workspace, dt_bias, ddt_bias,
+                          tr.lam, tr.x_prev, tr.B_prev, tr.dlam, tr.dx_prev, tr.dB_prev};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
@@ -372,12 +382,14 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         if (ssm::launch_state_copy(nullptr, dA, D * N, s) != hipSuccess) return SSM_ERR_HIP;
         if (Dskip && dDskip && ssm::launch_state_copy(nullptr, dDskip, D, s) != hipSuccess) return SSM_ERR_HIP;
         if (ddt_bias && ssm::launch_state_copy(nullptr, ddt_bias, D, s) != hipSuccess) return SSM_ERR_HIP;
+
         if (dstate_in && dstate_in != dstate &&
             ssm::launch_state_copy(dstate, dstate_in, batch * D * N, s) != hipSuccess)
             return SSM_ERR_HIP;
         return SSM_OK;
     }
     if (!x || !delta || !A || !Bt || !Ct || !dy || !dx || !ddelta || !dBt || !dCt) return SSM_ERR_NULL;
+    if (tr.lam && !tr.dlam) return SSM_ERR_NULL;
     const BwdLayout w = bwd_layout(batch, L, D, N);
     if (!workspace || workspace_bytes < w.bytes) return SSM_ERR_WORKSPACE;
     char *ws = (char *)workspace;
@@ -407,6 +419,15 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.dt_bias = dt_bias;
     a.delta_softplus = softplus;
     a.ddt_bias = softplus ? ddt_bias : nullptr;
+    a.lam = tr.lam;
+    a.x_prev = tr.x_prev;
+    a.B_prev = tr.B_prev;
+    a.dlam = tr.dlam;
+    // the token before the first gets a gradient only when it is given, and
+    // both of its outputs are asked for
+    const bool prev_grad = tr.x_prev && tr.dx_prev && tr.dB_prev;
+    a.dx_prev = prev_grad ? tr.dx_prev : nullptr;
+    a.dB_prev = prev_grad ? tr.dB_prev : nullptr;
     a.hst = (float *)(ws + w.off[0]);
     a.dsum = (float *)(ws + w.off[1]);
     a.gq = (float *)(ws + w.off[2]);
@@ -415,6 +436,7 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.pdA = (float *)(ws + w.off[5]);
     a.pdD = (float *)(ws + w.off[6]);
     a.pdT = (float *)(ws + w.off[7]);
+    a.pdBp = (float *)(ws + w.off[8]);
     return ssm::launch_scan_bwd(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -426,6 +448,28 @@ int ssm_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                  float *dstate_in, void *workspace, size_t workspace_bytes, void *stream) {
     return scan_bwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx,
                     ddelta, nullptr, dA, dBt, dCt, dDskip, dz, dstate_in, workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_bwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x, const void *delta, const void *lam, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                      const void *x_prev, const void *B_prev, const float *state_in,
+                      const void *dy, const float *dstate,
+                      void *dx, void *ddelta, void *dlam, float *dA, float *dBt, float *dCt, float *dDskip, void *dz,
+                      void *dx_prev, float *dB_prev, float *dstate_in, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    if (!lam && batch > 0 && L > 0 && D > 0) return SSM_ERR_NULL;
+    if ((x_prev == nullptr) != (B_prev == nullptr)) return SSM_ERR_NULL;
+    if ((dx_prev == nullptr) != (dB_prev == nullptr)) return SSM_ERR_NULL;
+    TrapBwd tr;
+    tr.lam = lam;
+    tr.x_prev = x_prev;
+    tr.B_prev = B_prev;
+    tr.dlam = dlam;
+    tr.dx_prev = dx_prev;
+    tr.dB_prev = dB_prev;
+    return scan_bwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx,
+                    ddelta, nullptr, dA, dBt, dCt, dDskip, dz, dstate_in, workspace, workspace_bytes, stream, tr);
 }
 
 int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,

@@ -93,6 +93,13 @@ struct BwdArgs {
     void *dx, *ddelta, *dz;  // with delta_softplus, ddelta is the gradient of the raw step size
     float *dA, *dBt, *dCt, *dDskip, *dstate_in;
     float *ddt_bias;       // gradient of dt_bias (NULL = not written)
+    // exponential-trapezoidal rule: the weight lam (NULL = the Euler rule) and
+    // the token before the first (x_prev, B_prev; NULL = none); the gradients
+    // of lam (dtype) and of the token before (dx_prev dtype, dB_prev float;
+    // NULL = not written)
+    const void *lam, *x_prev, *B_prev;
+    void *dlam, *dx_prev;
+    float *dB_prev;
     // workspace
     float *hst;         // (batch, K, D, N) state entering each chunk
     float *dsum;        // (batch, K, D)    summed delta per chunk
@@ -101,8 +108,11 @@ struct BwdArgs {
     float *pdA;         // (batch, K, D, N) per-chunk partial sums
     float *pdD;         // (batch, K, D)
     float *pdT;         // (batch, K, D)    partial sums of ddt_bias
+    float *pdBp;        // (bwd_channel_blocks, batch, N) partial sums of dB_prev
 };
 hipError_t launch_scan_bwd(const BwdArgs &a, int N, int dtype, hipStream_t s);
+// The instances for the exponential-trapezoidal rule (called by launch_scan_bwd).
+hipError_t launch_scan_bwd_trap(const BwdArgs &a, int N, int dtype, hipStream_t s);
 // Channel blocks of the gradient's chunk kernel (256 lanes; two lanes per
 // channel when N = 16): the number of partials of dBt and dCt.
 inline int64_t bwd_channel_blocks(int64_t D, int64_t N) {

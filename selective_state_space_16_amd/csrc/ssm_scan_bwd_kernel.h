@@ -1,0 +1,609 @@
+#pragma once
+// Gradient of the selective scan (S6) for gfx950: the kernels.
+//
+// The loss is sum(dy * y) + sum(dstate * state_out). Per (batch row b,
+// channel d), with a_t = exp(delta_t A), h_t = a_t h_{t-1} + delta_t B_t x_t and
+// the gradient G_t = dLoss/dh_t, the chain rule gives
+//
+//   G_t = C_t ds_t + a_{t+1} G_{t+1},        ds_t = dy_t silu(z_t),
+//
+// a linear recurrence run backwards in t. The states are recomputed rather
+// than stored ("Notas sobre Mamba", section "A varredura paralela ciente do
+// hardware": the backward recomputes the intermediate states), so nothing of
+// size (batch, L, D, N) is written. The sequence is cut into chunks of 32
+// tokens:
+//   1. forward summaries: each chunk's end state from a zero start;
+//   2. reverse summaries: the gradient each chunk sends into the state before
+//      it from a zero gradient at its end (both summaries in one pass, with
+//      each chunk's summed delta);
+//   3. carries per (b, d, n) over the chunks: from state_in, the state
+//      entering every chunk; from dstate, the gradient entering every chunk
+//      from the tokens after it;
+//   4. per chunk, from its entering state and gradient: the states again at
+//      8-token checkpoints, then token by token backwards, every gradient.
+//      dB and dC sum over the channels: exchanges within each wave, then LDS
+//      across the block's waves, one partial per block of channels; dA and dD
+//      sum over (b, t): one partial per (b, chunk);
+//   5. the partials are summed, in a fixed order.
+//
+// TRAP: the exponential-trapezoidal rule ("Notas sobre Mamba", section
+// "Recorrência trapezoidal"), h_t = a_t (h_{t-1} + (1 - lam_t) delta_t v_{t-1})
+// + lam_t delta_t v_t with v_t = B_t x_t. The state's gradient runs as above;
+// v_t feeds h_t and h_{t+1}, so its gradient takes lam_t delta_t G_t plus
+// (1 - lam_{t+1}) delta_{t+1} a_{t+1} G_{t+1}, carried from token to token.
+#include "ssm_common.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kSub = 8;  // tokens per recomputed block
+
+// The recurrence the gradient goes through: the exponential-Euler rule with
+// the step size given, or given before its activation, or the
+// exponential-trapezoidal rule.
+enum BwdMode { kBwdEuler = 0, kBwdSoftplus = 1, kBwdTrap = 2 };
+
+// The step size of a token: given, or softplus(raw + bias) rounded to the
+// activation dtype, as the forward scan computes it.
+template <int DT, typename T>
+__device__ __forceinline__ float delta_at(const T *dp, int64_t row, bool sp, float dtb) {
+    const float v = ld_act(dp, row);
+    return sp ? act_round<DT>(softplus(v + dtb)) : v;
+}
+
+// silu(z) and its derivative sigmoid(z) (1 + z (1 - sigmoid(z))).
+__device__ __forceinline__ void silu_and_grad(float z, float &g, float &dg) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * kLog2e));
+    g = z * sg;
+    dg = sg * (1.0f + z * (1.0f - sg));
+}
+
+// v from lane (lane ^ BIT): DPP lane moves inside rows of 16 lanes for BIT <
+// 16 (quad permutes for 1 and 2; shifts by 4 within banks of 4 lanes for 4;
+// a rotation by 8 for 8), a swizzle inside 32 lanes for 16, a permute for 32.
+template <int BIT>
+__device__ __forceinline__ float xor_lane(float v) {
+    const int x = __float_as_int(v);
+    if constexpr (BIT == 1) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    } else if constexpr (BIT == 2) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    } else if constexpr (BIT == 4) {
+        // lanes 0-3 and 8-11 of a row read lane + 4 (row_shl:4), lanes 4-7 and 12-15 lane - 4 (row_shr:4)
+        const int lo = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0x5, false);
+        return __int_as_float(__builtin_amdgcn_update_dpp(lo, x, 0x114, 0xF, 0xA, false));
+    } else if constexpr (BIT == 8) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));  // row_ror:8
+    } else if constexpr (BIT == 16) {
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));  // and 31, xor 16
+    } else {
+        return __shfl_xor(v, BIT);
+    }
+}
+
+// One halving exchange of wave_sum_vec and the ones after it: lanes with bit
+// BIT set keep the upper HALF elements of the current vector, the others the
+// lower HALF, each adding its partner's (lane ^ BIT) copy of the kept half.
+// Recursion on constants keeps every array index a compile-time constant.
+template <int HALF, int BIT, int N>
+__device__ __forceinline__ void halve(float (&v)[N], int lane) {
+    if constexpr (HALF >= 1) {
+        const bool upper = (lane & BIT) != 0;
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            const float send = upper ? v[i] : v[i + HALF];
+            const float keep = upper ? v[i + HALF] : v[i];
+            v[i] = keep + xor_lane<BIT>(send);
+        }
+        halve<HALF / 2, BIT * 2>(v, lane);
+    }
+}
+
+template <int BIT, int SPAN>
+__device__ __forceinline__ float fold(float s) {
+    if constexpr (BIT < SPAN) {
+        return fold<BIT * 2, SPAN>(s + xor_lane<BIT>(s));
+    } else {
+        return s;
+    }
+}
+
+// Sum of v[0..N) over the lanes of a wave that share bit SPAN and above
+// (SPAN = 64: the whole wave). The halving exchanges leave lane l with the
+// sum, over N lanes, of one element, named by the bits of l below log2(N);
+// the remaining exchanges add the lanes that hold the same element. Returns
+// that sum.
+template <int N, int SPAN>
+__device__ __forceinline__ float wave_sum_vec(float (&v)[N], int lane) {
+    halve<N / 2, 1>(v, lane);
+    return fold<N, SPAN>(v[0]);
+}
+
+// The element of v that wave_sum_vec<N, SPAN> leaves in lane `lane`.
+template <int N>
+__device__ __forceinline__ int wave_sum_index(int lane) {
+    int idx = 0;
+#pragma unroll
+    for (int s = 0; (N >> (s + 1)) >= 1; ++s)
+        if (lane & (1 << s)) idx += N >> (s + 1);
+    return idx;
+}
+
+// 1+2. the summaries of every chunk k, in one forward pass over its tokens:
+// its end state from a zero start (S_k, for k < K - 1), the gradient it sends
+// into the state before it from a zero gradient at its end (R_k, for k >= 1),
+// and its summed delta. In token order, R_k is the sum of C_t ds_t times the
+// product of a_s over the chunk's tokens up to and including t, so the decay
+// a_t of each token serves both summaries.
+template <int N, int DT, bool GATE, int MODE>
+__global__ __launch_bounds__(kBwdThreads) void bwd_summary_kernel(BwdArgs a) {
+    using T = typename Act<DT>::T;
+    const int64_t D = a.D, L = a.L, K = a.K;
+    // flat grid: block id = (b * K + k) * channel_blocks + channel_block
+    const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads, bid = blockIdx.x;
+    const int64_t d = (bid % nb) * kBwdThreads + threadIdx.x;
+    const int64_t k = (bid / nb) % K, b = bid / (nb * K);
+    const bool valid = d < D;
+    const int64_t dc = valid ? d : D - 1;
+    const int64_t t0 = k * kBwdChunk, t1 = t0 + kBwdChunk < L ? t0 + kBwdChunk : L;
+    float A2[N], h[N], P[N], R[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[dc * N + n] * kLog2e;
+        h[n] = 0.0f;
+        P[n] = 1.0f;
+        R[n] = 0.0f;
+    }
+    const T *xp = (const T *)a.x, *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
+    const T *Bp = (const T *)a.Bt, *Cp = (const T *)a.Ct;
+    constexpr bool sp = MODE == kBwdSoftplus, TRAP = MODE == kBwdTrap;
+    const float dtb = (sp && a.dt_bias) ? a.dt_bias[dc] : 0.0f;
+    // TRAP: x and Bt of the token before the chunk (before token 0: x_prev, B_prev)
+    float xprev = 0.0f, Bprev[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Bprev[n] = 0.0f;
+    if constexpr (TRAP) {
+        if (t0 > 0) {
+            xprev = ld_act(xp, (b * L + t0 - 1) * D + dc);
+            ld_row_uniform<N>(Bp, (b * L + t0 - 1) * N, Bprev);
+        } else if (a.x_prev) {
+            xprev = ld_act((const T *)a.x_prev, b * D + dc);
+            ld_row_uniform<N>((const T *)a.B_prev, b * N, Bprev);
+        }
+    }
+    float dsum = 0.0f;
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t row = (b * L + t) * D + dc;
+        const float dt = delta_at<DT>(dp, row, sp, dtb), xv = ld_act(xp, row);
+        float dtx = dt * xv, mux = 0.0f;
+        if constexpr (TRAP) {  // h = a (h + (1 - lam) delta v_{t-1}) + lam delta v_t
+            const float lm = ld_act((const T *)a.lam, row);
+            mux = (dt - lm * dt) * xprev;
+            dtx = lm * dt * xv;
+            xprev = xv;
+        }
+        float ds = ld_act(gp, row);
+        if (GATE) {
+            float g, dg;
+            silu_and_grad(ld_act(zp, row), g, dg);
+            ds *= g;
+        }
+        float Bv[N], Cv[N];
+        ld_row_uniform<N>(Bp, (b * L + t) * N, Bv);
+        ld_row_uniform<N>(Cp, (b * L + t) * N, Cv);
+        dsum += dt;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float av = fast_exp2(dt * A2[n]);
+            if constexpr (TRAP) {
+                h[n] = __builtin_fmaf(av, __builtin_fmaf(mux, Bprev[n], h[n]), dtx * Bv[n]);
+                Bprev[n] = Bv[n];
+            } else {
+                h[n] = __builtin_fmaf(av, h[n], dtx * Bv[n]);
+            }
+            P[n] *= av;
+            R[n] = __builtin_fmaf(P[n] * Cv[n], ds, R[n]);
+        }
+    }
+    if (!valid) return;
+    const int64_t o = ((b * K + k) * D + d) * N;
+    if (k + 1 < K) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.hst[o + n] = h[n];
+    }
+    if (k > 0) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.gq[o + n] = R[n];
+    }
+    a.dsum[(b * K + k) * D + d] = dsum;
+}
+
+// 3. the carries, per (b, d, n): in chunk order, the state entering each chunk
+// (from state_in: h <- exp(A sum delta_k) h + S_k); in reverse chunk order,
+// the gradient entering each chunk from its end (from dstate: q <- R_k +
+// exp(A sum delta_k) q). Each summary slot is replaced by its carry.
+template <int N>
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t D = a.D, K = a.K;
+    if (i >= a.batch * D * N) return;
+    const int64_t n = i % N, d = (i / N) % D, b = i / ((int64_t)N * D);
+    const float A2 = a.A[d * N + n] * kLog2e;
+    const int64_t base = (b * K * D + d) * N + n, kstride = D * N;
+    const float *ds = a.dsum + b * K * D + d;
+    // four chunks per step: their loads first, then the dependent chain
+    float h = a.state_in ? a.state_in[i] : 0.0f;
+    for (int64_t k0 = 0; k0 < K; k0 += 4) {
+        float sv[4], dv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 + u;
+            sv[u] = k + 1 < K ? a.hst[base + k * kstride] : 0.0f;
+            dv[u] = k + 1 < K ? ds[k * D] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 + u;
+            if (k < K) {
+                a.hst[base + k * kstride] = h;
+                h = __builtin_fmaf(fast_exp2(A2 * dv[u]), h, sv[u]);
+            }
+        }
+    }
+    float q = a.dstate ? a.dstate[i] : 0.0f;
+    for (int64_t k0 = K - 1; k0 >= 0; k0 -= 4) {
+        float rv[4], dv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 - u;
+            rv[u] = k > 0 ? a.gq[base + k * kstride] : 0.0f;
+            dv[u] = k > 0 ? ds[k * D] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t k = k0 - u;
+            if (k >= 0) {
+                a.gq[base + k * kstride] = q;
+                q = __builtin_fmaf(fast_exp2(A2 * dv[u]), q, rv[u]);
+            }
+        }
+    }
+}
+
+// 4. the gradients of one chunk, for one batch row and a block of channels.
+// N <= 8: a lane owns a channel and its N state elements. N = 16: two lanes
+// own a channel, 8 elements each (lanes l and l + 32 of a wave), so that the
+// recomputed states of 8 tokens fit in registers; their per-channel sums meet
+// through one exchange. Bt and Ct of the chunk are staged in LDS.
+template <int N, int DT, bool GATE, bool SKIP, int MODE>
+__global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
+    using T = typename Act<DT>::T;
+    constexpr int NP = N < 8 ? N : 8;        // state elements per lane
+    constexpr int R = N / NP;                // lanes per channel
+    constexpr int SPAN = 64 / R;             // channels per wave
+    constexpr int CPB = kBwdThreads / R;     // channels per block
+    constexpr int NCK = kBwdChunk / kSub;    // checkpoints per chunk
+    constexpr int NW = kBwdThreads / 64;     // waves per block
+    // row j + 1: token t0 + j; row 0: the token before the chunk (TRAP)
+    __shared__ float sB[kBwdChunk + 1][N], sC[kBwdChunk + 1][N];
+    __shared__ float ck[NCK][NP][kBwdThreads];   // state entering each block of kSub tokens
+    __shared__ float red[2][NW][kSub][N];        // per-wave sums of dCt, dBt
+    const int64_t D = a.D, L = a.L, K = a.K;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = R == 1 ? 0 : lane / SPAN, cl = lane % SPAN;
+    // flat grid: block id = (b * K + k) * channel_blocks + channel_block
+    const int64_t nb = (D + CPB - 1) / CPB, bid = blockIdx.x;
+    const int64_t cb = bid % nb, k = (bid / nb) % K, b = bid / (nb * K);
+    const int64_t d = cb * CPB + w * SPAN + cl;
+    const bool valid = d < D;
+    const int64_t dc = valid ? d : D - 1;
+    const int64_t t0 = k * kBwdChunk, t1 = t0 + kBwdChunk < L ? t0 + kBwdChunk : L;
+    const int cnt_chunk = (int)(t1 - t0);
+    const T *xp = (const T *)a.x, *dp = (const T *)a.delta, *zp = (const T *)a.z, *gp = (const T *)a.dy;
+    constexpr bool sp = MODE == kBwdSoftplus, TRAP = MODE == kBwdTrap;
+    const float dtb = (sp && a.dt_bias) ? a.dt_bias[dc] : 0.0f;
+    const T *lp = (const T *)a.lam;
+    for (int i = tid; i < (kBwdChunk + 1) * N; i += kBwdThreads) {
+        const int jj = i / N, n = i % N;
+        float bv = 0.0f, cv = 0.0f;
+        if (jj >= 1 && jj - 1 < cnt_chunk) {
+            const int64_t o = (b * L + t0 + jj - 1) * N + n;
+            bv = ld_act((const T *)a.Bt, o);
+            cv = ld_act((const T *)a.Ct, o);
+        } else if (TRAP && jj == 0) {
+            if (t0 > 0) bv = ld_act((const T *)a.Bt, (b * L + t0 - 1) * N + n);
+            else if (a.B_prev) bv = ld_act((const T *)a.B_prev, b * N + n);
+        }
+        sB[jj][n] = bv;
+        sC[jj][n] = cv;
+    }
+    // TRAP: x of the token before token t (x_prev before token 0; none: 0)
+    auto x_before = [&](int64_t t) -> float {
+        if (t > 0) return ld_act(xp, (b * L + t - 1) * D + dc);
+        return a.x_prev ? ld_act((const T *)a.x_prev, b * D + dc) : 0.0f;
+    };
+    const int n0 = r * NP;  // first state element of this lane
+    float A2[NP], h[NP], G[NP], Gb[NP];
+    // TRAP: Gb = (1 - lam) delta a G of the token after: the gradient of this
+    // token's input through the next token's update; after the chunk, that of
+    // its first token, whose a G is the gradient entering from the end
+    float mu1 = 0.0f;
+    if (TRAP && t1 < L) {
+        const int64_t row1 = (b * L + t1) * D + dc;
+        const float dt1 = ld_act(dp, row1);
+        mu1 = dt1 - ld_act(lp, row1) * dt1;
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        A2[i] = a.A[dc * N + n0 + i] * kLog2e;
+        h[i] = a.hst[((b * K + k) * D + dc) * N + n0 + i];
+        G[i] = a.gq[((b * K + k) * D + dc) * N + n0 + i];
+        Gb[i] = mu1 * G[i];
+    }
+    __syncthreads();
+    // forward through the chunk up to its last block, keeping the state
+    // entering each block
+    const int nblk = (cnt_chunk + kSub - 1) / kSub;
+    float xprev = TRAP ? x_before(t0) : 0.0f;
+    for (int j = 0; j < (nblk - 1) * kSub; ++j) {
+        if (j % kSub == 0) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) ck[j / kSub][i][tid] = h[i];
+        }
+        const int64_t row = (b * L + t0 + j) * D + dc;
+        const float dt = delta_at<DT>(dp, row, sp, dtb), xv = ld_act(xp, row);
+        if constexpr (TRAP) {
+            const float lm = ld_act(lp, row), mux = (dt - lm * dt) * xprev, dx = lm * dt * xv;
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), __builtin_fmaf(mux, sB[j][n0 + i], h[i]),
+                                      dx * sB[j + 1][n0 + i]);
+            xprev = xv;
+        } else {
+            const float dx = dt * xv;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), h[i], dx * sB[j + 1][n0 + i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) ck[nblk - 1][i][tid] = h[i];
+    (void)xprev;
+    float dA[NP], dD = 0.0f, dT = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) dA[i] = 0.0f;
+    const float dsk = SKIP ? a.Dskip[dc] : 0.0f;
+    const int elem = n0 + wave_sum_index<NP>(cl);  // element this lane holds after the channel sums
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int s0 = blk * kSub;
+        const int cnt = cnt_chunk - s0 < kSub ? cnt_chunk - s0 : kSub;
+        // states of the block: hb[j] = state entering token s0 + j
+        float hb[kSub + 1][NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) hb[0][i] = ck[blk][i][tid];
+        float xpr = TRAP ? x_before(t0 + s0) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            if (j < cnt) {
+                const int64_t row = (b * L + t0 + s0 + j) * D + dc;
+                const float dt = delta_at<DT>(dp, row, sp, dtb), xv = ld_act(xp, row);
+                if constexpr (TRAP) {
+                    const float lm = ld_act(lp, row), mux = (dt - lm * dt) * xpr, dx = lm * dt * xv;
+#pragma unroll
+                    for (int i = 0; i < NP; ++i)
+                        hb[j + 1][i] = __builtin_fmaf(fast_exp2(dt * A2[i]),
+                                                      __builtin_fmaf(mux, sB[s0 + j][n0 + i], hb[j][i]),
+                                                      dx * sB[s0 + j + 1][n0 + i]);
+                    xpr = xv;
+                } else {
+                    const float dx = dt * xv;
+#pragma unroll
+                    for (int i = 0; i < NP; ++i)
+                        hb[j + 1][i] =
+                            __builtin_fmaf(fast_exp2(dt * A2[i]), hb[j][i], dx * sB[s0 + j + 1][n0 + i]);
+                }
+            }
+        }
+        (void)xpr;
+#pragma unroll
+        for (int j = kSub - 1; j >= 0; --j) {
+            if (j >= cnt) continue;
+            const int tl = s0 + j;
+            const int64_t row = (b * L + t0 + tl) * D + dc;
+            const float raw = ld_act(dp, row), xv = ld_act(xp, row), dyv = ld_act(gp, row);
+            const float dt = sp ? act_round<DT>(softplus(raw + dtb)) : raw;
+            float gate = 1.0f, dgate = 0.0f;
+            if (GATE) silu_and_grad(ld_act(zp, row), gate, dgate);
+            const float ds = valid ? dyv * gate : 0.0f;
+            const float xvv = valid ? xv : 0.0f;
+            // TRAP: the token before, its weight (1 - lam) delta, and this token's lam delta
+            float lm = 0.0f, xpv = 0.0f, mu = 0.0f, gam = dt;
+            if constexpr (TRAP) {
+                lm = ld_act(lp, row);
+                xpv = x_before(t0 + tl);
+                mu = dt - lm * dt;
+                gam = lm * dt;
+            }
+            const float mux = mu * xpv;
+            // Ga = a G is the gradient of h_{t-1}; gah = Ga (h_{t-1} + (1 - lam) delta v_{t-1});
+            // d(delta) takes sum(gah A), and x sum(G B) (Euler) or the trapezoid's terms
+            float pre = 0.0f, gaa = 0.0f, gb = 0.0f, gbb = 0.0f, gav = 0.0f, dCv[NP], dBv[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const float Cv = sC[tl + 1][n0 + i], Bv = sB[tl + 1][n0 + i];
+                pre = __builtin_fmaf(Cv, hb[j + 1][i], pre);
+                G[i] = __builtin_fmaf(Cv, ds, G[i]);
+                dCv[i] = ds * hb[j + 1][i];
+                gb = __builtin_fmaf(G[i], Bv, gb);
+                if constexpr (TRAP) {
+                    const float dv = __builtin_fmaf(gam, G[i], Gb[i]);  // gradient of v_t = B_t x_t
+                    dBv[i] = dv * xvv;
+                    gbb = __builtin_fmaf(Gb[i], Bv, gbb);
+                } else {
+                    dBv[i] = G[i] * (dt * xvv);
+                }
+                G[i] *= fast_exp2(dt * A2[i]);  // the gradient of h_{t-1}
+                float hp = hb[j][i];
+                if constexpr (TRAP) {
+                    const float Bp = sB[tl][n0 + i];
+                    hp = __builtin_fmaf(mux, Bp, hp);
+                    gav = __builtin_fmaf(G[i], Bp, gav);
+                    Gb[i] = mu * G[i];
+                }
+                const float gah = G[i] * hp;
+                gaa = __builtin_fmaf(gah, A2[i], gaa);
+                dA[i] = __builtin_fmaf(gah, dt, dA[i]);
+            }
+            if (R == 2) {  // the other half of the channel's state elements
+                pre += xor_lane<SPAN>(pre);
+                gaa += xor_lane<SPAN>(gaa);
+                gb += xor_lane<SPAN>(gb);
+                if constexpr (TRAP) {
+                    gbb += xor_lane<SPAN>(gbb);
+                    gav += xor_lane<SPAN>(gav);
+                }
+            }
+            float gdt, gx;
+            if constexpr (TRAP) {
+                // d(delta) = sum Ga A p + (1 - lam) x_{t-1} sum Ga B_{t-1} + lam x sum G B
+                gdt = __builtin_fmaf(gaa, kLn2, __builtin_fmaf((1.0f - lm) * xpv, gav, lm * xv * gb));
+                gx = __builtin_fmaf(gam, gb, gbb);
+            } else {
+                gdt = __builtin_fmaf(gaa, kLn2, gb * xv);
+                gx = gb * dt;
+            }
+            if (SKIP) {
+                pre = __builtin_fmaf(dsk, xv, pre);
+                gx = __builtin_fmaf(ds, dsk, gx);
+            }
+            dD = __builtin_fmaf(ds, xv, dD);
+            if (valid && r == 0) {
+                st_act((T *)a.dx, row, gx);
+                // through the activation: d softplus(u) / du = sigmoid(u)
+                const float g = sp ? gdt * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-(raw + dtb) * kLog2e)) : gdt;
+                dT += g;
+                st_act((T *)a.ddelta, row, g);
+                if (GATE) st_act((T *)a.dz, row, dyv * pre * dgate);
+                if (TRAP) st_act((T *)a.dlam, row, dt * (xv * gb - xpv * gav));
+            }
+            const float sc = wave_sum_vec<NP, SPAN>(dCv, lane);
+            const float sb = wave_sum_vec<NP, SPAN>(dBv, lane);
+            if (cl < NP) {
+                red[0][w][j][elem] = sc;
+                red[1][w][j][elem] = sb;
+            }
+        }
+        __syncthreads();
+        // the block's sums over its channels, one partial per channel block
+        for (int i = tid; i < 2 * kSub * N; i += kBwdThreads) {
+            const int which = i / (kSub * N), j = (i / N) % kSub, n = i % N;
+            if (j < cnt) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) sum += red[which][v][j][n];
+                float *dst = which == 0 ? a.pdC : a.pdB;
+                dst[((cb * a.batch + b) * L + t0 + s0 + j) * N + n] = sum;
+            }
+        }
+        __syncthreads();
+    }
+    if constexpr (TRAP) {
+        // the token before token 0: its input's gradient is Gb after token 0
+        if (k == 0 && a.dx_prev) {
+            const float xp0 = valid ? ld_act((const T *)a.x_prev, b * D + dc) : 0.0f;
+            float gp = 0.0f, dBp[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                gp = __builtin_fmaf(Gb[i], sB[0][n0 + i], gp);
+                dBp[i] = Gb[i] * xp0;
+            }
+            if (R == 2) gp += xor_lane<SPAN>(gp);
+            if (valid && r == 0) st_act((T *)a.dx_prev, b * D + d, gp);
+            const float sb = wave_sum_vec<NP, SPAN>(dBp, lane);
+            if (cl < NP) red[1][w][0][elem] = sb;
+            __syncthreads();
+            for (int n = tid; n < N; n += kBwdThreads) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) sum += red[1][v][0][n];
+                a.pdBp[(cb * a.batch + b) * N + n] = sum;
+            }
+        }
+    }
+    if (!valid) return;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) a.pdA[((b * K + k) * D + d) * N + n0 + i] = dA[i];
+    if (r == 0) {
+        a.pdD[(b * K + k) * D + d] = dD;
+        a.pdT[(b * K + k) * D + d] = dT;
+    }
+    if (k == 0 && a.dstate_in) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) a.dstate_in[(b * D + d) * N + n0 + i] = G[i];
+    }
+}
+
+// 5. the sums of the partials, in a fixed order (partial 0 first), eight
+// loads in flight per step.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *part, int64_t nparts, int64_t stride,
+                                                         float *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    int64_t p = 0;
+    for (; p + 8 <= nparts; p += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(p + u) * stride + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; p < nparts; ++p) s += part[p * stride + i];
+    out[i] = s;
+}
+
+template <int N, int DT, bool GATE, bool SKIP, int MODE>
+hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
+    const int64_t D = a.D, K = a.K;
+    const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads;
+    if (K > 1)
+        hipLaunchKernelGGL((bwd_summary_kernel<N, DT, GATE, MODE>), dim3((unsigned)(nb * K * a.batch)), dim3(kBwdThreads),
+                           0, s, a);
+    const int64_t total = a.batch * D * N;
+    hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    const int64_t ncb = bwd_channel_blocks(D, N);
+    hipLaunchKernelGGL((bwd_chunk_kernel<N, DT, GATE, SKIP, MODE>), dim3((unsigned)(ncb * K * a.batch)),
+                       dim3(kBwdThreads), 0, s, a);
+    const int64_t bln = a.batch * a.L * N;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdB, ncb, bln,
+                       a.dBt, bln);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((bln + 255) / 256)), dim3(256), 0, s, a.pdC, ncb, bln,
+                       a.dCt, bln);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D * N + 255) / 256)), dim3(256), 0, s, a.pdA,
+                       a.batch * K, D * N, a.dA, D * N);
+    if (a.dDskip)
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0, s, a.pdD, a.batch * K,
+                           D, a.dDskip, D);
+    if (a.ddt_bias)
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0, s, a.pdT, a.batch * K,
+                           D, a.ddt_bias, D);
+    if (MODE == kBwdTrap && a.dx_prev)
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((a.batch * N + 255) / 256)), dim3(256), 0, s, a.pdBp,
+                           ncb, a.batch * N, a.dB_prev, a.batch * N);
+    return hipGetLastError();
+}
+
+template <int N, int DT, int MODE>
+hipError_t launch_bwd_flags(const BwdArgs &a, hipStream_t s) {
+    const bool gate = a.z != nullptr, skip = a.Dskip != nullptr;
+    if (gate && skip) return launch_bwd_typed<N, DT, true, true, MODE>(a, s);
+    if (gate) return launch_bwd_typed<N, DT, true, false, MODE>(a, s);
+    if (skip) return launch_bwd_typed<N, DT, false, true, MODE>(a, s);
+    return launch_bwd_typed<N, DT, false, false, MODE>(a, s);
+}
+
+}  // namespace
+
+}  // namespace ssm

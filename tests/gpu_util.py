@@ -129,7 +129,7 @@ def gpu_ssd(inp, want_state=True):
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
 
 
-def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False, raw=False, want_dbias=True):
+def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False, raw=False, want_dbias=True, trap=False):
     """Run ssm_scan_bwd (or, with raw, ssm_scan_bwd_dt on delta_raw and dt_bias)
     on stored inputs and upstream gradients; returns a dict of float64 arrays
     with the oracle's keys (dDskip/dz None when absent)."""
@@ -141,7 +141,11 @@ def gpu_scan_bwd(inp, grads, want_dskip=True, dstate_alias=False, raw=False, wan
         out["dstate_in"] = dstate
     if not want_dskip:
         out["dDskip"] = None
-    if raw:
+    if trap:
+        g = ssm.ssm_scan_bwd_trap(dev["x"], dev["delta"], dev["lam"], dev["A"], dev["Bt"], dev["Ct"], dy,
+                                  Dskip=dev["Dskip"], z=dev["z"], x_prev=dev.get("x_prev"), B_prev=dev.get("B_prev"),
+                                  state_in=dev["state_in"], dstate=dstate, out=out)
+    elif raw:
         if not want_dbias:
             out["ddt_bias"] = None
         g = ssm.ssm_scan_bwd_dt(dev["x"], dev["delta_raw"], dev.get("dt_bias"), dev["A"], dev["Bt"], dev["Ct"], dy,
@@ -161,7 +165,8 @@ def check_grads(got, ref, dtype, keys=None):
     """Every gradient against the oracle's: relative L2 as for the outputs;
     for float32, max-abs 1e-4 scaled by the largest reference magnitude (the
     parameter gradients are sums over many tokens and channels)."""
-    for k in keys or ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dz", "dA", "dBt", "dCt", "dDskip", "dstate_in"):
+    for k in keys or ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dlam", "dz", "dA", "dBt", "dCt", "dDskip",
+                      "dx_prev", "dB_prev", "dstate_in"):
         if ref.get(k) is None:
             assert got.get(k) is None, k + " written but not expected"
             continue

@@ -276,3 +276,27 @@ def test_scan_bwd_dt_rejects(kw, code):
 
 def test_scan_bwd_dt_empty_ok_without_gpu():
     assert bwd_dt(D=0) == 0
+
+
+def bwd_trap(**kw):
+    a = dict(batch=2, L=100, D=64, N=16, dtype=0, x=P, delta=P, lam=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             x_prev=None, B_prev=None, state_in=None, dy=P, dstate=None, dx=P, ddelta=P, dlam=P, dA=P, dBt=P, dCt=P,
+             dDskip=None, dz=None, dx_prev=None, dB_prev=None, dstate_in=None, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_bwd_trap(*[a[k] for k in (
+        "batch", "L", "D", "N", "dtype", "x", "delta", "lam", "A", "Bt", "Ct", "Dskip", "z", "x_prev", "B_prev",
+        "state_in", "dy", "dstate", "dx", "ddelta", "dlam", "dA", "dBt", "dCt", "dDskip", "dz", "dx_prev",
+        "dB_prev", "dstate_in", "ws", "ws_bytes", "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lam=None), -1), (dict(dlam=None), -1), (dict(x_prev=P), -1), (dict(B_prev=P), -1),
+    (dict(dx_prev=P), -1), (dict(dB_prev=P), -1), (dict(lam=MIS), -5), (dict(dlam=MIS), -5),
+    (dict(x_prev=P, B_prev=MIS), -5), (dict(N=3), -4), (dict(ws=None), -6),
+])
+def test_scan_bwd_trap_rejects(kw, code):
+    assert bwd_trap(**kw) == code
+
+
+def test_scan_bwd_trap_empty_ok_without_gpu():
+    assert bwd_trap(D=0) == 0

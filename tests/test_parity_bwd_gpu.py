@@ -178,3 +178,41 @@ def test_bwd_raw_delta_without_bias_gradient():
 def test_bwd_raw_delta_small_layer_whole():
     """The small-layer workload with its step size given before the activation."""
     _run_raw(dataclass_replace(W.SCAN_CONFIGS["c1"], state_in=0.3))
+
+
+def _run_trap(cfg, prev=True):
+    say(f"case {cfg} trapezoidal, x_prev/B_prev={'given' if prev else 'NULL'}")
+    inp = W.scan_inputs(cfg, trap=True)
+    if not prev:
+        inp["x_prev"] = inp["B_prev"] = None
+    grads = W.grad_inputs(cfg)
+    got = gpu_scan_bwd(inp, grads, trap=True)
+    ref = oracle.get().scan_bwd_trap(inp, grads["dy"], grads["dstate"], cfg.dtype)
+    check_grads(got, ref, cfg.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("prev", [True, False])
+def test_bwd_trap(dtype, prev):
+    """ssm_scan_bwd_trap: 4 chunks with a ragged tail, a short channel block,
+    with and without the token before the first."""
+    _run_trap(_cfg("bwd_trap", 2, 100, 200, 16, dtype), prev=prev)
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_bwd_trap_state_sizes(N):
+    _run_trap(_cfg(f"bwd_trap_N{N}", 2, 77, 130, N, "f32"))
+
+
+@pytest.mark.parametrize("L", [1, 31, 33, 257])
+def test_bwd_trap_ragged_lengths(L):
+    _run_trap(_cfg(f"bwd_trap_L{L}", 1, L, 64, 16, "f32", seed=82))
+
+
+def test_bwd_trap_no_options():
+    _run_trap(_cfg("bwd_trap_plain", 1, 70, 64, 16, "f32", gate=False, dskip="none", state_in=None), prev=False)
+
+
+def test_bwd_trap_small_layer_whole():
+    """The small-layer workload with the trapezoidal rule, every gradient whole."""
+    _run_trap(dataclass_replace(W.SCAN_CONFIGS["c1"], state_in=0.3))
