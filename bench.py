@@ -50,9 +50,13 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """sha256 (first 16 hex) of the kernel sources: the .hip files and the
+    headers under csrc/ (the host-side C ABI in ssm_abi.cpp is left out)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_16_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -336,7 +336,11 @@ static bool bwd_sizes_ok(int64_t batch, int64_t L, int64_t D, int64_t N) {
     if (checked_mul3(checked_mul(batch, K), D, N) < 0 || checked_mul3(checked_mul(nDB, batch), L, N) < 0)
         return false;
     const int64_t blocks = checked_mul3(nDB, K, batch);
-    return blocks >= 0 && blocks < ((int64_t)1 << 24);
+    // the flat grids of the chunk kernels, the carry (batch * D * N lanes)
+    // and the sums of dBt, dCt (batch * L * N lanes), in 256-lane blocks
+    const int64_t lanes = checked_mul3(batch, D, N) > checked_mul3(batch, L, N) ? checked_mul3(batch, D, N)
+                                                                                : checked_mul3(batch, L, N);
+    return blocks >= 0 && blocks < ((int64_t)1 << 24) && lanes / 256 < ((int64_t)1 << 31);
 }
 
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
