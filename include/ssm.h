@@ -262,13 +262,14 @@ int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64
                 const float *Dskip, const float *state_in, float *state_out, void *y, void *stream);
 
 /*
- * Scratch bytes ssm_scan_bwd needs for these sizes (0 for empty or invalid
- * sizes). The gradient cuts the sequence into chunks of 32 tokens; the
- * workspace holds, per (batch row, chunk, channel), the state and the
- * gradient entering the chunk and the chunk's summed delta, and the partial
- * sums of dBt, dCt (per 64 channels), dA and dDskip (per chunk). It needs no
- * clearing: every word is written before it is read within one call. Calls
- * that share a workspace must not run at the same time.
+ * Scratch bytes ssm_scan_bwd, ssm_scan_bwd_dt and ssm_scan_bwd_trap need for
+ * these sizes (0 for empty or invalid sizes). The gradient cuts the sequence
+ * into chunks of 32 tokens; the workspace holds, per (batch row, chunk,
+ * channel), the state and the gradient entering the chunk and the chunk's
+ * summed delta, and the partial sums of dBt, dCt and dB_prev (per block of 256
+ * channels, 128 when N = 16) and of dA, dDskip and ddt_bias (per chunk). It
+ * needs no clearing: every word is written before it is read within one call.
+ * Calls that share a workspace must not run at the same time.
  */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
 
