@@ -356,6 +356,84 @@ def bench_ssd(args):
     return out
 
 
+def bench_ssd_step(args):
+    """The Mamba-2 SSD decode workload: K consecutive ssm_ssd_step calls, one
+    token each, on a (256, 80, 64, 128) float32 state resident in HBM, from a
+    captured graph as for the S6 decode step."""
+    import numpy as np
+    import torch
+    import dataclasses
+    import selective_state_space_16_amd as ssm
+    import workloads as W
+
+    cfg = W.SSD_CONFIGS["ssd_step"]
+    log(f"[bench] workload {cfg}")
+    nsteps = args.steps + args.warmup
+    tok = W.fill_ssd_device(dataclasses.replace(cfg, L=nsteps), "cuda")
+    # per-step tensors: (step, batch, ...) contiguous
+    tok = {k: v.transpose(0, 1).contiguous() for k, v in tok.items()}
+    whole = W.ssd_inputs(dataclasses.replace(cfg, L=0, state_in=None), batches=[0])
+    A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    state = torch.randn((cfg.batch, cfg.H, cfg.P, cfg.N), generator=g, device="cuda")
+    y = torch.empty((cfg.batch, cfg.H, cfg.P), dtype=tok["x"].dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(s):  # on the current stream (the capture stream inside the graph)
+        ssm.ssm_ssd_step(tok["x"][s], tok["delta"][s], A, tok["Bt"][s], tok["Ct"][s], state, Dskip=Dskip, y=y,
+                         stream=torch.cuda.current_stream())
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    graph.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} SSD decode steps from a graph, {ms * 1e3:.2f} us/step")
+    out = {"cfg": cfg, "ms": ms, "launch_ms": ms, "elems": cfg.batch * cfg.H * cfg.P * cfg.N,
+           "bytes": W.ssd_step_bytes(cfg), "dtype": cfg.dtype, "parity": None, "cpu": None}
+    if not args.no_cpu:
+        # parity and the oracle's rate on a bounded sample: 4 batch rows x 8
+        # heads, their inputs and state from the seeded streams, for T steps
+        import oracle
+        T = 16
+        bsel, hsel = np.array([0, 1, 128, 255]), np.arange(0, cfg.H, 10)
+        part = W.ssd_inputs(dataclasses.replace(cfg, L=T), batches=bsel, heads=hsel)
+        st = torch.zeros_like(state[:1]).expand(len(bsel), -1, -1, -1).contiguous()
+        st[:, torch.as_tensor(hsel, device="cuda")] = to_dev(part["state_in"])
+        d = {k: to_dev(v) for k, v in part.items()}
+        hs = torch.as_tensor(hsel, device="cuda")
+        ys = []
+        for t in range(T):
+            xs = torch.zeros((len(bsel), cfg.H, cfg.P), dtype=tok["x"].dtype, device="cuda")
+            ds = torch.ones((len(bsel), cfg.H), dtype=tok["x"].dtype, device="cuda")
+            xs[:, hs], ds[:, hs] = d["x"][:, t], d["delta"][:, t]
+            ys.append(ssm.ssm_ssd_step(xs, ds, A, d["Bt"][:, t].contiguous(), d["Ct"][:, t].contiguous(), st,
+                                       Dskip=Dskip)[:, hs])
+        torch.cuda.synchronize()
+        yg = torch.stack(ys, 1).double().cpu().numpy()
+        o = oracle.get()
+        t = time.perf_counter()
+        yr, _ = o.ssd(part, cfg.dtype, nthreads=1)
+        tot = time.perf_counter() - t
+        rel, mx = rel_l2(yg, yr)
+        out["parity"] = {"relL2": rel, "maxabs": mx}
+        out["cpu"] = {"value": len(bsel) * len(hsel) * T * cfg.P * cfg.N / tot / 1e9 / T,
+                      "unit": "G(B*H*P*N)-elem/s per step", "cores": 1, "kind": "oracle",
+                      "sample": f"{len(bsel)} batch rows x {len(hsel)} heads x {T} steps, {tot:.2f}s, fp64 C oracle"}
+    return out
+
+
 def bench_step(args):
     import numpy as np
     import torch
@@ -445,7 +523,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "ssd"])
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "ssd", "ssd_step"])
     ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -475,12 +553,14 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    if args.backward and args.workload in ("c3", "c4", "ssd"):
+    if args.backward and args.workload in ("c3", "c4", "ssd", "ssd_step"):
         ap.error("--backward times the gradient of the scan (plain, --softplus or --trap) on c0, c1 or c2")
-    if args.workload == "ssd" and (args.softplus or args.trap):
+    if args.workload in ("ssd", "ssd_step") and (args.softplus or args.trap):
         ap.error("--softplus and --trap apply to the S6 scan and step")
     if args.workload == "ssd":
         r = bench_ssd(args)
+    elif args.workload == "ssd_step":
+        r = bench_ssd_step(args)
     else:
         r = bench_step(args) if args.workload == "c4" else bench_scan(args, args.workload)
     cfg = r["cfg"]
@@ -488,7 +568,7 @@ def main():
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
     traffic = None if (args.softplus or args.trap) else \
         measured_traffic(args.workload + ("_grad" if args.backward else ""))
-    kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL}.get(args.workload, SCAN_KERNEL)
+    kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL, "ssd_step": "ssd_step_kernel"}.get(args.workload, SCAN_KERNEL)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": kernel,
            "algorithmic_bytes_per_launch": r["bytes"], "launch_us": launch_ms * 1e3}
@@ -498,7 +578,7 @@ def main():
         mfma = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tf / MFMA_BF16_PEAK_TFLOPS, "kernel": kernel, "algorithmic_flops_per_launch": r["flops"],
                 "launch_us": launch_ms * 1e3}
-    if args.workload in ("c4", "ssd"):
+    if args.workload in ("c4", "ssd", "ssd_step"):
         roof = hbm  # the SSD layer needs more time at the HBM peak than at the matrix-core peak
     elif args.backward:
         # the whole gradient call (all its launches), against the VALU peak
@@ -519,6 +599,10 @@ def main():
         config = {"workload": cfg.name, "batch": cfg.batch, "L": cfg.L, "H": cfg.H, "P": cfg.P, "G": cfg.G,
                   "N": cfg.N, "dtype": cfg.dtype, "chunk": 64}
         metric = "ssd-layer G(B*L*H*P*N)-elem/s"
+    elif args.workload == "ssd_step":
+        config = {"workload": cfg.name, "batch": cfg.batch, "H": cfg.H, "P": cfg.P, "G": cfg.G, "N": cfg.N,
+                  "dtype": cfg.dtype, "steps_timed": args.steps}
+        metric = "ssd-decode-step G(B*H*P*N)-elem/s"
     elif args.workload == "c4":
         config = {"workload": cfg.name, "batch": cfg.batch, "D": cfg.D, "N": cfg.N, "dtype": cfg.dtype,
                   "gate": cfg.gate, "steps_timed": args.steps}
@@ -542,7 +626,8 @@ def main():
     line = {
         "metric": metric,
         "value": r["elems"] / (ms * 1e-3) / 1e9,
-        "unit": {"c4": "G(B*D*N)-elem/s", "ssd": "G(B*L*H*P*N)-elem/s"}.get(args.workload, "G(B*L*D*N)-elem/s"),
+        "unit": {"c4": "G(B*D*N)-elem/s", "ssd": "G(B*L*H*P*N)-elem/s",
+                 "ssd_step": "G(B*H*P*N)-elem/s"}.get(args.workload, "G(B*L*D*N)-elem/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -262,6 +262,32 @@ int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64
                 const float *Dskip, const float *state_in, float *state_out, void *y, void *stream);
 
 /*
+ * Mamba-2 SSD decode step: one token per (batch row, head) on a stored state,
+ * updated in place, with the same transition, input rule and readout as
+ * ssm_ssd_fwd (its recurrent form, "A forma dual: atenção mascarada"):
+ *
+ *   a          = exp(delta[b,h] * A[h])
+ *   S[p][n]    = a * S[p][n] + delta[b,h] * x[b,h,p] * Bt[b,g,n]
+ *   y[b,h,p]   = sum_n Ct[b,g,n] * S[p][n]  (+ Dskip[h] * x[b,h,p])
+ *
+ * with g = h / (H / G). L calls, one per token, equal one ssm_ssd_fwd call
+ * over the L tokens (up to rounding).
+ *
+ *   x, y          (batch, H, P)     dtype
+ *   delta         (batch, H)        dtype      step after its activation
+ *   A, Dskip      (H)               float      Dskip NULL = no skip term
+ *   Bt, Ct        (batch, G, N)     dtype
+ *   state         (batch, H, P, N)  float      read and written in place
+ *
+ * Supported: P = 64 and N = 64 or 128, dtype SSM_F32 or SSM_BF16 (else
+ * SSM_ERR_UNSUPPORTED or SSM_ERR_DTYPE); H must be a multiple of G (else
+ * SSM_ERR_SHAPE). No workspace. Conventions otherwise as above.
+ */
+int ssm_ssd_step(int64_t batch, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                 const float *Dskip, float *state, void *y, void *stream);
+
+/*
  * Scratch bytes ssm_scan_bwd, ssm_scan_bwd_dt and ssm_scan_bwd_trap need for
  * these sizes (0 for empty or invalid sizes). The gradient cuts the sequence
  * into chunks of 32 tokens; the workspace holds, per (batch row, chunk,

@@ -23,6 +23,8 @@ Functions (same names as the C ABI):
       ssm_scan_fwd_dt, with ddelta_raw and ddt_bias in place of ddelta
   ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, ...) -> dict: the same for
       ssm_scan_fwd_trap, with dlam, and dx_prev, dB_prev for the earlier token
+  ssm_ssd_step(x, delta, A, Bt, Ct, state, Dskip=None, y=None) -> y: one SSD
+      decode token (x (batch, H, P), Bt/Ct (batch, G, N), state in place)
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_scan_bwd_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
@@ -35,7 +37,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
+    "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_ssd_step", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error",
 ]
@@ -51,7 +53,7 @@ lib_path = os.path.join(_HERE, "libssm.so")
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_step_trap.restype = ci
     L.ssm_ssd_fwd.argtypes = [i64] * 6 + [ci] + [vp] * 9 + [vp]
     L.ssm_ssd_fwd.restype = ci
+    L.ssm_ssd_step.argtypes = [i64] * 5 + [ci] + [vp] * 8 + [vp]
+    L.ssm_ssd_step.restype = ci
     L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
     L.ssm_scan_bwd_workspace_bytes.restype = sz
     L.ssm_scan_bwd.argtypes = [i64, i64, i64, i64, ci] + [vp] * 18 + [vp, sz, vp]
@@ -419,3 +423,25 @@ def ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, Dskip=None, z=None, x_prev=N
     if st != 0:
         raise SSMError(st, "ssm_scan_bwd_trap")
     return o
+
+
+def ssm_ssd_step(x, delta, A, Bt, Ct, state, Dskip=None, y=None, stream=None):
+    """One Mamba-2 SSD decode token. Shapes: x, y (batch, H, P) and delta
+    (batch, H) in the activation dtype; A, Dskip (H,) float32; Bt, Ct (batch,
+    G, N); state (batch, H, P, N) float32, updated in place."""
+    import torch
+    if x.dim() != 3 or Bt.dim() != 3:
+        raise ValueError("x must be (batch, H, P) and Bt (batch, G, N)")
+    batch, H, P = x.shape
+    G, N = Bt.shape[1], Bt.shape[2]
+    act, f32 = x.dtype, torch.float32
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, H)), _ptr(A, "A", f32, (H,)),
+            _ptr(Bt, "Bt", act, (batch, G, N)), _ptr(Ct, "Ct", act, (batch, G, N)), _ptr(Dskip, "Dskip", f32, (H,)),
+            _ptr(state, "state", f32, (batch, H, P, N)), _ptr(y, "y", act, (batch, H, P))]
+    st = lib().ssm_ssd_step(batch, H, P, G, N, code, *args, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_ssd_step")
+    return y

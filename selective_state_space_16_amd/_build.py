@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm.so")
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["ssm_scan_stripe_act.hip", "ssm_scan_stripe_trap.hip", "ssm_scan_stripe.hip", "ssm_scan.hip", "ssm_step.hip", "ssm_ssd.hip", "ssm_scan_bwd_trap.hip", "ssm_scan_bwd.hip", "ssm_abi.cpp"]
+SOURCES = ["ssm_scan_stripe_act.hip", "ssm_scan_stripe_trap.hip", "ssm_scan_stripe.hip", "ssm_scan.hip", "ssm_step.hip", "ssm_ssd.hip", "ssm_ssd_step.hip", "ssm_scan_bwd_trap.hip", "ssm_scan_bwd.hip", "ssm_abi.cpp"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.
 # The atomic optimizer is off: it rewrites a one-lane atomic with a returned

@@ -488,6 +488,36 @@ int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     stream);
 }
 
+int ssm_ssd_step(int64_t batch, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
+                 const float *Dskip, float *state, void *y, void *stream) {
+    if (batch < 0 || H < 0 || P < 0 || G < 0 || N < 0) return SSM_ERR_SHAPE;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (!ssm::ssd_step_supported(P, N)) return SSM_ERR_UNSUPPORTED;
+    if (H > 0 && (G < 1 || H % G != 0)) return SSM_ERR_SHAPE;
+    if (checked_mul3(checked_mul(batch, H), P, N) < 0 || checked_mul3(batch, G, N) < 0 ||
+        checked_mul(batch, H) >= ((int64_t)1 << 31))
+        return SSM_ERR_SHAPE;
+    if (batch == 0 || H == 0) return SSM_OK;
+    if (!x || !delta || !A || !Bt || !Ct || !state || !y) return SSM_ERR_NULL;
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, state, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+    ssm::SsdStepArgs a{};
+    a.batch = batch;
+    a.H = H;
+    a.G = G;
+    a.x = x;
+    a.delta = delta;
+    a.Bt = Bt;
+    a.Ct = Ct;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.state = state;
+    a.y = y;
+    return ssm::launch_ssd_step(a, (int)N, dtype, (hipStream_t)stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
                 const void *x, const void *delta, const float *A, const void *Bt, const void *Ct,
                 const float *Dskip, const float *state_in, float *state_out, void *y, void *stream) {

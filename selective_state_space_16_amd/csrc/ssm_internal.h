@@ -79,6 +79,18 @@ struct SsdArgs {
     void *y;
 };
 bool ssd_supported(int64_t P, int64_t N);
+
+// Mamba-2 SSD decode step: x, y (batch, H, P); delta (batch, H); Bt, Ct
+// (batch, G, N); A, Dskip (H); state (batch, H, P, N) float, in place.
+struct SsdStepArgs {
+    int64_t batch, H, G;
+    const void *x, *delta, *Bt, *Ct;
+    const float *A, *Dskip;
+    float *state;
+    void *y;
+};
+bool ssd_step_supported(int64_t P, int64_t N);
+hipError_t launch_ssd_step(const SsdStepArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_ssd(const SsdArgs &a, int N, hipStream_t s);
 
 // Gradient of the scan (Euler rule, delta after its activation). Pointers are

@@ -300,3 +300,23 @@ def test_scan_bwd_trap_rejects(kw, code):
 
 def test_scan_bwd_trap_empty_ok_without_gpu():
     assert bwd_trap(D=0) == 0
+
+
+def ssd_step(**kw):
+    a = dict(batch=2, H=4, P=64, G=1, N=128, dtype=1, x=P, delta=P, A=P, Bt=P, Ct=P, Dskip=None, state=P, y=P,
+             stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_ssd_step(*[a[k] for k in ("batch", "H", "P", "G", "N", "dtype", "x", "delta", "A", "Bt",
+                                                    "Ct", "Dskip", "state", "y", "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=4), -3), (dict(P=32), -4), (dict(N=16), -4), (dict(G=3), -2), (dict(G=0), -2),
+    (dict(x=None), -1), (dict(state=None), -1), (dict(y=None), -1), (dict(state=MIS), -5), (dict(Dskip=MIS), -5),
+])
+def test_ssd_step_rejects(kw, code):
+    assert ssd_step(**kw) == code
+
+
+def test_ssd_step_empty_ok_without_gpu():
+    assert ssd_step(batch=0) == 0 and ssd_step(H=0) == 0

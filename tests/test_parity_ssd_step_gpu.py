@@ -1,0 +1,104 @@
+"""The Mamba-2 SSD decode step (ssm_ssd_step) against the fp64 oracle (needs
+MI355X): T steps, one token each, on a state updated in place, equal the
+oracle's SSD layer over the T tokens (its y at every token and its final
+state); and they equal one ssm_ssd_fwd call over the same tokens."""
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_16_amd as ssm
+import workloads as W
+from gpu_util import check, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _steps(inp, state0):
+    """Run the tokens of `inp` one step at a time; returns (y (batch, T, H, P), state)."""
+    import torch
+    d = {k: to_dev(v) for k, v in inp.items()}
+    batch, T, H, P = d["x"].shape
+    N = d["Bt"].shape[3]
+    state = state0 if state0 is not None else torch.zeros((batch, H, P, N), dtype=torch.float32, device="cuda")
+    ys = []
+    for t in range(T):
+        ys.append(ssm.ssm_ssd_step(d["x"][:, t].contiguous(), d["delta"][:, t].contiguous(), d["A"],
+                                   d["Bt"][:, t].contiguous(), d["Ct"][:, t].contiguous(), state, Dskip=d["Dskip"]))
+    torch.cuda.synchronize()
+    return np.stack([to_f64(y) for y in ys], axis=1), to_f64(state)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_steps_equal_the_layer(dtype, N, G):
+    cfg = W.SsdConfig(f"ssd_step_{dtype}_{N}_{G}", 3, 40, 4, 64, G, N, dtype, dskip=True, state_in=0.5, seed=61)
+    say(f"case {cfg}")
+    inp = W.ssd_inputs(cfg)
+    y, st = _steps(inp, to_dev(inp["state_in"]).clone())
+    yr, sr = oracle.get().ssd(inp, dtype)
+    check(y, yr, dtype, "y")
+    check(st, sr, dtype, "state")
+
+
+def test_ssd_step_no_skip_zero_state():
+    cfg = W.SsdConfig("ssd_step_plain", 2, 9, 3, 64, 1, 128, "bf16", dskip=False, state_in=None, seed=62)
+    say(f"case {cfg}")
+    inp = W.ssd_inputs(cfg)
+    y, st = _steps(inp, None)
+    yr, sr = oracle.get().ssd(inp, "bf16")
+    check(y, yr, "bf16", "y")
+    check(st, sr, "bf16", "state")
+
+
+def test_ssd_steps_equal_one_layer_call():
+    """T GPU steps against one GPU ssm_ssd_fwd over the same tokens (bf16)."""
+    import torch
+    cfg = W.SsdConfig("ssd_step_vs_fwd", 2, 96, 4, 64, 1, 128, "bf16", dskip=True, state_in=0.5, seed=63)
+    say(f"case {cfg}")
+    inp = W.ssd_inputs(cfg)
+    y, st = _steps(inp, to_dev(inp["state_in"]).clone())
+    d = {k: to_dev(v) for k, v in inp.items()}
+    st2 = torch.empty_like(d["state_in"])
+    y2 = ssm.ssm_ssd_fwd(d["x"], d["delta"], d["A"], d["Bt"], d["Ct"], Dskip=d["Dskip"], state_in=d["state_in"],
+                         state_out=st2)
+    torch.cuda.synchronize()
+    check(y, to_f64(y2), "bf16", "y (steps vs layer)")
+    check(st, to_f64(st2), "bf16", "state (steps vs layer)")
+
+
+def test_ssd_step_decode_workload_sampled():
+    """The decode workload's full state (256 sequences, 80 heads of 64 x 128,
+    float32, 671 MB) for a few steps; sampled (batch row, head) pairs, whose
+    inputs and state are the seeded streams, checked against the oracle."""
+    import torch
+    cfg = W.SSD_CONFIGS["ssd_step"]
+    T, bsel, hsel = 3, np.array([0, 77, 255]), np.array([0, 41, 79])
+    say(f"case {cfg.name} full state, {T} steps, batch rows {list(bsel)}, heads {list(hsel)}")
+    fill = W.fill_ssd_device(dataclass_replace(cfg, L=T), "cuda")
+    state = torch.randn((cfg.batch, cfg.H, cfg.P, cfg.N), device="cuda")
+    part = W.ssd_inputs(dataclass_replace(cfg, L=T), batches=bsel, heads=hsel)
+    whole = W.ssd_inputs(dataclass_replace(cfg, L=T, state_in=None), 0, 0, batches=[0])  # A, Dskip of every head
+    bt, ht = torch.as_tensor(bsel, device="cuda"), torch.as_tensor(hsel, device="cuda")
+    for i, b in enumerate(bsel):
+        fill["x"][b, :, ht] = to_dev(part["x"][i])
+        fill["delta"][b, :, ht] = to_dev(part["delta"][i])
+        fill["Bt"][b] = to_dev(part["Bt"][i])
+        fill["Ct"][b] = to_dev(part["Ct"][i])
+        state[b, ht] = to_dev(part["state_in"][i])
+    A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
+    ys = []
+    for t in range(T):
+        ys.append(ssm.ssm_ssd_step(fill["x"][:, t].contiguous(), fill["delta"][:, t].contiguous(), A,
+                                   fill["Bt"][:, t].contiguous(), fill["Ct"][:, t].contiguous(), state, Dskip=Dskip))
+    torch.cuda.synchronize()
+    y = np.stack([to_f64(v[bt][:, ht]) for v in ys], axis=1)
+    st = to_f64(state[bt][:, ht])
+    yr, sr = oracle.get().ssd(part, cfg.dtype)
+    check(y, yr, cfg.dtype, "y")
+    check(st, sr, cfg.dtype, "state")
+
+
+def dataclass_replace(cfg, **kw):
+    import dataclasses
+    return dataclasses.replace(cfg, **kw)

@@ -49,7 +49,7 @@ __all__ = [
     "fill_scan_device", "fill_step_device", "ScanConfig", "StepConfig", "SCAN_CONFIGS", "STEP_CONFIG", "DTYPES",
     "scan_inputs", "step_inputs", "step_token_inputs", "bf16_bits_from_f64",
     "storage_to_f64", "scan_bytes", "step_bytes", "trap_extra_bytes", "trap_step_extra_bytes",
-    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes", "grad_inputs", "scan_bwd_bytes",
+    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "fill_ssd_device", "ssd_bytes", "grad_inputs", "scan_bwd_bytes", "ssd_step_bytes",
 ]
 
 DTYPES = ("f32", "bf16")
@@ -124,6 +124,9 @@ class SsdConfig:
 # (the pages: the SSD state can grow from 16 to 64, 128 or 256), one group.
 SSD_CONFIGS: Dict[str, SsdConfig] = {
     "ssd": SsdConfig("ssd_mamba2_layer_bf16", 8, 4096, 80, 64, 1, 128, "bf16", dskip=True, seed=5),
+    # decode: 256 sequences, one token per step, the same layer's heads and state
+    "ssd_step": SsdConfig("ssd_decode_step_bf16", 256, 1000, 80, 64, 1, 128, "bf16", dskip=True, state_in=1.0,
+                          seed=6),
 }
 
 
@@ -506,6 +509,15 @@ def fill_ssd_device(cfg: SsdConfig, device, seed: int = 777):
             "delta": torch.nn.functional.softplus(normal((cfg.batch, cfg.L, cfg.H)).mul_(0.5).add_(bias)).to(act),
             "Bt": normal((cfg.batch, cfg.L, cfg.G, cfg.N)).to(act),
             "Ct": normal((cfg.batch, cfg.L, cfg.G, cfg.N)).to(act)}
+
+
+def ssd_step_bytes(cfg: SsdConfig) -> int:
+    """Bytes one SSD decode step must move: the (batch, H, P, N) float32 state
+    read and written, x read and y written per (b, h, p), delta per (b, h), Bt
+    and Ct per (b, g, n), A and Dskip."""
+    e = _esize(cfg.dtype)
+    n = 2 * cfg.batch * cfg.H * cfg.P * cfg.N * 4 + 2 * cfg.batch * cfg.H * cfg.P * e + cfg.batch * cfg.H * e
+    return n + 2 * cfg.batch * cfg.G * cfg.N * e + cfg.H * 4 * (2 if cfg.dskip else 1)
 
 
 def ssd_bytes(cfg: SsdConfig, state_out: bool = False) -> int:
