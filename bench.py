@@ -49,14 +49,29 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix-core peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex) of the kernel sources: the .hip files and the
-    headers under csrc/ (the host-side C ABI in ssm_abi.cpp is left out)."""
+# The sources each measured kernel is built from (besides the shared headers).
+KERNEL_SOURCES = {
+    "scan": ("ssm_scan_stripe_kernel.h", "ssm_scan_stripe.hip", "ssm_scan_stripe_act.hip", "ssm_scan_stripe_trap.hip"),
+    "step": ("ssm_step.hip",),
+    "ssd": ("ssm_ssd.hip",),
+    "ssd_step": ("ssm_ssd_step.hip",),
+    "grad": ("ssm_scan_bwd_kernel.h", "ssm_scan_bwd.hip", "ssm_scan_bwd_trap.hip"),
+}
+SHARED_SOURCES = ("ssm_common.h", "ssm_device.h", "ssm_internal.h")
+
+
+def kernel_family(workload: str) -> str:
+    if workload.endswith("_grad"):
+        return "grad"
+    return {"c4": "step", "ssd": "ssd", "ssd_step": "ssd_step"}.get(workload, "scan")
+
+
+def kernel_source_hash(family: str) -> str:
+    """sha256 (first 16 hex) of the sources of one kernel family and the shared
+    device headers under csrc/."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_16_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if not name.endswith((".hip", ".h")):
-            continue
+    for name in sorted(KERNEL_SOURCES[family] + SHARED_SOURCES):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -70,7 +85,7 @@ def measured_traffic(workload: str):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_src_sha") != kernel_source_hash():
+    if not rec or rec.get("kernel_src_sha") != kernel_source_hash(kernel_family(workload)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
