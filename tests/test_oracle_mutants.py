@@ -70,6 +70,14 @@ MUTANTS = [
     ("bwd_gate_derivative_sigmoid_only", "dgate = sg * (1.0 + zz * (1.0 - sg));", "dgate = sg;"),
     ("bwd_skip_grad_missing", "double gx = Dskip ? ds * Dskip[d] : 0.0;", "double gx = 0.0;"),
     ("bwd_readout_grad_after_decay", "                    G[n] += Ct[bn] * ds;\n", ""),
+    ("bwdtrap_input_grad_misses_next_update", "double dv = lm * dt * G[n] + Gb[n];", "double dv = lm * dt * G[n];"),
+    ("bwdtrap_next_weight_not_decayed", "Gb[n] = (1.0 - lm) * dt * alpha * G[n];", "Gb[n] = (1.0 - lm) * dt * G[n];"),
+    ("bwdtrap_dlam_sign", "gl += G[n] * dt * (v - alpha * vp);", "gl += G[n] * dt * (v + alpha * vp);"),
+    ("bwdtrap_ddelta_misses_prev_term", "+ (1.0 - lm) * alpha * vp + lm * v);", "+ lm * v);"),
+    ("bwdtrap_decay_arg_without_prev", "double p = H[t * N + n] + (1.0 - lm) * dt * vp;", "double p = H[t * N + n];"),
+    ("bwdtrap_dx_prev_from_x", "gp += Gb[n] * B_prev[b * N + n];", "gp += Gb[n] * x_prev[b * D + d];"),
+    ("softplus_grad_sigmoid_sign", "g[r * D + d] / (1.0 + exp(-u))", "g[r * D + d] / (1.0 + exp(u))"),
+    ("softplus_grad_bias_sum_missing", "            if (gbias) gbias[d] += v;\n", ""),
     ("ssd_group_modulo", "g = h / (H / G);", "g = h % G;"),
     ("ssd_input_without_delta", "+ dt * xt[p] * Bg[n];", "+ xt[p] * Bg[n];"),
     ("ssd_decay_of_group", "double a = exp(dt * A[h]);", "double a = exp(dt * A[g]);"),
