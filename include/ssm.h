@@ -292,8 +292,8 @@ int ssm_ssd_step(int64_t batch, int64_t H, int64_t P, int64_t G, int64_t N, int 
  * these sizes (0 for empty or invalid sizes). The gradient cuts the sequence
  * into chunks of 32 tokens; the workspace holds, per (batch row, chunk,
  * channel), the state and the gradient entering the chunk and the chunk's
- * summed delta, and the partial sums of dBt, dCt and dB_prev (per block of 256
- * channels, 128 when N = 16) and of dA, dDskip and ddt_bias (per chunk). It
+ * summed delta, and the partial sums of dBt, dCt and dB_prev (per block of 64
+ * to 256 channels) and of dA, dDskip and ddt_bias (per chunk). It
  * needs no clearing: every word is written before it is read within one call.
  * Calls that share a workspace must not run at the same time.
  */

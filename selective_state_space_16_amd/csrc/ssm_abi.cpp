@@ -312,7 +312,7 @@ struct BwdLayout {
 static BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N) {
     BwdLayout w{};
     w.K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
-    const int64_t nDB = ssm::bwd_channel_blocks(D, N);
+    const int64_t nDB = ssm::bwd_channel_blocks(D, N, true);  // the most blocks: the trapezoidal rule
     const size_t sz[9] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
                           (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
                           (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D),
@@ -332,7 +332,7 @@ static bool bwd_sizes_ok(int64_t batch, int64_t L, int64_t D, int64_t N) {
     const int64_t K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
     if (checked_mul3(batch, L, D) < 0 || checked_mul3(batch, L, N) < 0 || checked_mul3(batch, D, N) < 0)
         return false;
-    const int64_t nDB = ssm::bwd_channel_blocks(D, N);
+    const int64_t nDB = ssm::bwd_channel_blocks(D, N, true);  // the most blocks: the trapezoidal rule
     if (checked_mul3(checked_mul(batch, K), D, N) < 0 || checked_mul3(checked_mul(nDB, batch), L, N) < 0)
         return false;
     const int64_t blocks = checked_mul3(nDB, K, batch);

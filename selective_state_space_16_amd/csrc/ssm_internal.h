@@ -96,6 +96,10 @@ hipError_t launch_ssd(const SsdArgs &a, int N, hipStream_t s);
 // Gradient of the scan (Euler rule, delta after its activation). Pointers are
 // device pointers; dx, ddelta, dz in the activation dtype, the rest float.
 constexpr int64_t kBwdChunk = 32;  // tokens per chunk of the gradient
+// State elements per lane in the gradient's chunk kernel: 8 (two lanes per
+// channel at N = 16), and 4 for the trapezoidal rule, whose reverse step
+// keeps one more vector per lane (measured faster with four lanes).
+constexpr int bwd_np(int64_t N, bool trap) { return (int)(N < (trap ? 4 : 8) ? N : (trap ? 4 : 8)); }
 struct BwdArgs {
     int64_t batch, L, D, K;  // K = ceil(L / kBwdChunk) chunks
     const void *x, *delta, *Bt, *Ct, *z, *dy;
@@ -125,10 +129,10 @@ struct BwdArgs {
 hipError_t launch_scan_bwd(const BwdArgs &a, int N, int dtype, hipStream_t s);
 // The instances for the exponential-trapezoidal rule (called by launch_scan_bwd).
 hipError_t launch_scan_bwd_trap(const BwdArgs &a, int N, int dtype, hipStream_t s);
-// Channel blocks of the gradient's chunk kernel (256 lanes; two lanes per
-// channel when N = 16): the number of partials of dBt and dCt.
-inline int64_t bwd_channel_blocks(int64_t D, int64_t N) {
-    const int64_t cpb = N > 8 ? 256 / (N / 8) : 256;
+// Channel blocks of the gradient's chunk kernel (256 lanes, N / bwd_np lanes
+// per channel): the number of partials of dBt and dCt.
+inline int64_t bwd_channel_blocks(int64_t D, int64_t N, bool trap) {
+    const int64_t cpb = 256 / (N / bwd_np(N, trap));
     return (D + cpb - 1) / cpb;
 }
 

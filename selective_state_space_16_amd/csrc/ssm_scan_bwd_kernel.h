@@ -274,14 +274,15 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
 }
 
 // 4. the gradients of one chunk, for one batch row and a block of channels.
-// N <= 8: a lane owns a channel and its N state elements. N = 16: two lanes
-// own a channel, 8 elements each (lanes l and l + 32 of a wave), so that the
-// recomputed states of 8 tokens fit in registers; their per-channel sums meet
-// through one exchange. Bt and Ct of the chunk are staged in LDS.
+// A lane owns NP = bwd_np(N) state elements of a channel: all of them when
+// N <= 8 (4 for the trapezoidal rule); otherwise N / NP lanes, SPAN lanes
+// apart in the wave, share a channel, so that the recomputed states of 8
+// tokens fit in registers, and their per-channel sums meet through lane
+// exchanges. Bt and Ct of the chunk are staged in LDS.
 template <int N, int DT, bool GATE, bool SKIP, int MODE>
 __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     using T = typename Act<DT>::T;
-    constexpr int NP = N < 8 ? N : 8;        // state elements per lane
+    constexpr int NP = bwd_np(N, MODE == kBwdTrap);  // state elements per lane
     constexpr int R = N / NP;                // lanes per channel
     constexpr int SPAN = 64 / R;             // channels per wave
     constexpr int CPB = kBwdThreads / R;     // channels per block
@@ -456,13 +457,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 gaa = __builtin_fmaf(gah, A2[i], gaa);
                 dA[i] = __builtin_fmaf(gah, dt, dA[i]);
             }
-            if (R == 2) {  // the other half of the channel's state elements
-                pre += xor_lane<SPAN>(pre);
-                gaa += xor_lane<SPAN>(gaa);
-                gb += xor_lane<SPAN>(gb);
+            if (R > 1) {  // the channel's other state elements, in the other lanes
+                pre = fold<SPAN, 64>(pre);
+                gaa = fold<SPAN, 64>(gaa);
+                gb = fold<SPAN, 64>(gb);
                 if constexpr (TRAP) {
-                    gbb += xor_lane<SPAN>(gbb);
-                    gav += xor_lane<SPAN>(gav);
+                    gbb = fold<SPAN, 64>(gbb);
+                    gav = fold<SPAN, 64>(gav);
                 }
             }
             float gdt, gx;
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 gp = __builtin_fmaf(Gb[i], sB[0][n0 + i], gp);
                 dBp[i] = Gb[i] * xp0;
             }
-            if (R == 2) gp += xor_lane<SPAN>(gp);
+            if (R > 1) gp = fold<SPAN, 64>(gp);
             if (valid && r == 0) st_act((T *)a.dx_prev, b * D + d, gp);
             const float sb = wave_sum_vec<NP, SPAN>(dBp, lane);
             if (cl < NP) red[1][w][0][elem] = sb;
@@ -573,7 +574,7 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
                            0, s, a);
     const int64_t total = a.batch * D * N;
     hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-    const int64_t ncb = bwd_channel_blocks(D, N);
+    const int64_t ncb = bwd_channel_blocks(D, N, MODE == kBwdTrap);
     hipLaunchKernelGGL((bwd_chunk_kernel<N, DT, GATE, SKIP, MODE>), dim3((unsigned)(ncb * K * a.batch)),
                        dim3(kBwdThreads), 0, s, a);
     const int64_t bln = a.batch * a.L * N;
