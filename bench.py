@@ -568,8 +568,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
 
-    if args.backward and args.workload in ("c3", "c4", "ssd", "ssd_step"):
-        ap.error("--backward times the gradient of the scan (plain, --softplus or --trap) on c0, c1 or c2")
+    if args.backward and args.workload in ("c4", "ssd", "ssd_step"):
+        ap.error("--backward times the gradient of the scan (plain, --softplus or --trap) on c0-c3")
     if args.workload in ("ssd", "ssd_step") and (args.softplus or args.trap):
         ap.error("--softplus and --trap apply to the S6 scan and step")
     if args.workload == "ssd":
