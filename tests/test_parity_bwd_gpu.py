@@ -248,3 +248,15 @@ def test_bwd_million_token_sampled():
            "dz": to_f64(g["dz"][:, :, sel_t]), "dA": to_f64(g["dA"][sel_t]), "dDskip": to_f64(g["dDskip"][sel_t]),
            "dstate_in": to_f64(g["dstate_in"][:, sel_t])}
     check_grads(got, ref, cfg.dtype, keys=("dx", "ddelta", "dz", "dA", "dDskip", "dstate_in"))
+
+
+@pytest.mark.parametrize("D,N", [(1, 16), (3, 16), (63, 16), (129, 2), (5, 1)])
+def test_bwd_ragged_channels(D, N):
+    """Channel counts that leave most lanes of the last block idle, including
+    whole waves past the last channel."""
+    _run(_cfg(f"bwd_D{D}_N{N}", 2, 45, D, N, "f32", seed=83))
+
+
+@pytest.mark.parametrize("D", [1, 63])
+def test_bwd_trap_ragged_channels(D):
+    _run_trap(_cfg(f"bwd_trap_D{D}", 2, 45, D, 16, "bf16", seed=84))
