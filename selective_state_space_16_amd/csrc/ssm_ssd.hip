@@ -202,7 +202,13 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_kernel(SsdArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
     const int lr = l & 15, lq = l >> 4;
     const int64_t H = a.H, L = a.L, G = a.G;
-    const int64_t b = blockIdx.x / H, h = blockIdx.x % H, g = h / (H / G);
+    // Workgroups are dealt to the 8 XCDs in turn (block id mod 8). When the
+    // count divides evenly, XCD x takes the x-th eighth of the (b, h) pairs in
+    // order, so the heads of a batch row, which read the same Bt and Ct,
+    // share one XCD's L2.
+    const int64_t nwg = (int64_t)gridDim.x;
+    const int64_t pair = nwg % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int64_t b = pair / H, h = pair % H, g = h / (H / G);
     const float A2 = a.A[h] * kLog2e;
     const float dsk = SKIP ? a.Dskip[h] : 0.0f;
     uint16_t *yp = (uint16_t *)a.y;
