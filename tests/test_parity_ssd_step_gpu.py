@@ -102,3 +102,37 @@ def test_ssd_step_decode_workload_sampled():
 def dataclass_replace(cfg, **kw):
     import dataclasses
     return dataclasses.replace(cfg, **kw)
+
+
+def test_ssd_step_graph_replay():
+    """SSD decode steps captured into a HIP graph (as the decode bench runs
+    them): every replay, with eager layer calls and synchronisations between
+    replays, equals the same steps launched eagerly, bit for bit."""
+    import torch
+    cfg = W.SsdConfig("ssd_step_graph", 2, 5, 4, 64, 1, 128, "bf16", dskip=True, state_in=0.5, seed=64)
+    say(f"case {cfg} graph replay")
+    inp = W.ssd_inputs(cfg)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    toks = [{k: d[k][:, t].contiguous() for k in ("x", "delta", "Bt", "Ct")} for t in range(cfg.L)]
+    st_g, st_e = d["state_in"].clone(), d["state_in"].clone()
+    y_g, y_e = torch.empty_like(toks[0]["x"]), torch.empty_like(toks[0]["x"])
+
+    def steps(state, y):
+        for tk in toks:
+            ssm.ssm_ssd_step(tk["x"], tk["delta"], d["A"], tk["Bt"], tk["Ct"], state, Dskip=d["Dskip"], y=y,
+                             stream=torch.cuda.current_stream())
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps(st_g, y_g)
+    torch.cuda.synchronize()
+    st_g.copy_(d["state_in"])
+    for rep in range(4):
+        graph.replay()
+        steps(st_e, y_e)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"y differs on replay {rep}"
+        assert torch.equal(st_g, st_e), f"state differs on replay {rep}"
+        ssm.ssm_ssd_fwd(d["x"], d["delta"], d["A"], d["Bt"], d["Ct"], Dskip=d["Dskip"])  # eager work between
+        torch.cuda.synchronize()
