@@ -303,22 +303,23 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
     return step(batch, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
-// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD | pdT | pdBp].
+// Workspace of the gradient: [header | hst | dsum | gq | pdB | pdC | pdA | pdD | pdT | pdBp | ckp | ckd].
 struct BwdLayout {
     int64_t K;
-    size_t off[9], bytes;
+    size_t off[11], bytes;
 };
 
 static BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N) {
     BwdLayout w{};
     w.K = (L + ssm::kBwdChunk - 1) / ssm::kBwdChunk;
     const int64_t nDB = ssm::bwd_channel_blocks(D, N, true);  // the most blocks: the trapezoidal rule
-    const size_t sz[9] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
-                          (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
-                          (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D),
-                          (size_t)(nDB * batch * N)};
+    const size_t sz[11] = {(size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D * N),
+                           (size_t)(nDB * batch * L * N), (size_t)(nDB * batch * L * N),
+                           (size_t)(batch * w.K * D * N), (size_t)(batch * w.K * D), (size_t)(batch * w.K * D),
+                           (size_t)(nDB * batch * N), (size_t)(batch * w.K * ssm::kBwdCk * D * N),
+                           (size_t)(batch * w.K * ssm::kBwdCk * D)};
     size_t off = kHeader;
-    for (int i = 0; i < 9; ++i) {
+    for (int i = 0; i < 11; ++i) {
         w.off[i] = off;
         off += round_up256(sz[i] * sizeof(float));
     }
@@ -441,6 +442,8 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.pdD = (float *)(ws + w.off[6]);
     a.pdT = (float *)(ws + w.off[7]);
     a.pdBp = (float *)(ws + w.off[8]);
+    a.ckp = (float *)(ws + w.off[9]);
+    a.ckd = (float *)(ws + w.off[10]);
     return ssm::launch_scan_bwd(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

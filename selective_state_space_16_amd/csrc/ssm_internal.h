@@ -96,6 +96,8 @@ hipError_t launch_ssd(const SsdArgs &a, int N, hipStream_t s);
 // Gradient of the scan (Euler rule, delta after its activation). Pointers are
 // device pointers; dx, ddelta, dz in the activation dtype, the rest float.
 constexpr int64_t kBwdChunk = 32;  // tokens per chunk of the gradient
+constexpr int kBwdSub = 8;         // tokens per recomputed block of a chunk
+constexpr int kBwdCk = (int)(kBwdChunk / kBwdSub) - 1;  // block entries inside a chunk
 // State elements per lane in the gradient's chunk kernel: 8 (two lanes per
 // channel at N = 16), and 4 for the trapezoidal rule, whose reverse step
 // keeps one more vector per lane (measured faster with four lanes).
@@ -125,6 +127,8 @@ struct BwdArgs {
     float *pdD;         // (batch, K, D)
     float *pdT;         // (batch, K, D)    partial sums of ddt_bias
     float *pdBp;        // (bwd_channel_blocks, batch, N) partial sums of dB_prev
+    float *ckp;         // (batch, K, kBwdCk, D, N) state at each block entry inside a chunk, from a zero chunk start
+    float *ckd;         // (batch, K, kBwdCk, D)    summed delta from the chunk start to each block entry
 };
 hipError_t launch_scan_bwd(const BwdArgs &a, int N, int dtype, hipStream_t s);
 // The instances for the exponential-trapezoidal rule (called by launch_scan_bwd).

@@ -39,7 +39,7 @@ namespace ssm {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kSub = 8;  // tokens per recomputed block
+constexpr int kSub = kBwdSub;  // tokens per recomputed block
 
 // The recurrence the gradient goes through: the exponential-Euler rule with
 // the step size given, or given before its activation, or the
@@ -176,6 +176,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_summary_kernel(BwdArgs a) {
     }
     float dsum = 0.0f;
     for (int64_t t = t0; t < t1; ++t) {
+        if (t > t0 && (t - t0) % kSub == 0 && valid) {
+            // a block entry inside the chunk: the state so far from a zero
+            // chunk start, and the delta summed so far
+            const int64_t j = (t - t0) / kSub - 1;
+            float *dst = a.ckp + (((b * K + k) * kBwdCk + j) * D + d) * N;
+#pragma unroll
+            for (int n = 0; n < N; ++n) dst[n] = h[n];
+            a.ckd[((b * K + k) * kBwdCk + j) * D + d] = dsum;
+        }
         const int64_t row = (b * L + t) * D + dc;
         const float dt = delta_at<DT>(dp, row, sp, dtb), xv = ld_act(xp, row);
         float dtx = dt * xv, mux = 0.0f;
@@ -347,31 +356,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
     // forward through the chunk up to its last block, keeping the state
     // entering each block
+    // the state entering each block: the chunk's entering state h carried
+    // through exp(A sum delta) plus the block entry's state from a zero chunk
+    // start (both from the summary pass: the recurrence is affine in h)
     const int nblk = (cnt_chunk + kSub - 1) / kSub;
-    float xprev = TRAP ? x_before(t0) : 0.0f;
-    for (int j = 0; j < (nblk - 1) * kSub; ++j) {
-        if (j % kSub == 0) {
 #pragma unroll
-            for (int i = 0; i < NP; ++i) ck[j / kSub][i][tid] = h[i];
-        }
-        const int64_t row = (b * L + t0 + j) * D + dc;
-        const float dt = delta_at<DT>(dp, row, sp, dtb), xv = ld_act(xp, row);
-        if constexpr (TRAP) {
-            const float lm = ld_act(lp, row), mux = (dt - lm * dt) * xprev, dx = lm * dt * xv;
+    for (int i = 0; i < NP; ++i) ck[0][i][tid] = h[i];
+    for (int j = 1; j < nblk; ++j) {
+        const int64_t o = ((b * K + k) * kBwdCk + j - 1) * D + dc;
+        const float cs = a.ckd[o];
 #pragma unroll
-            for (int i = 0; i < NP; ++i)
-                h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), __builtin_fmaf(mux, sB[j][n0 + i], h[i]),
-                                      dx * sB[j + 1][n0 + i]);
-            xprev = xv;
-        } else {
-            const float dx = dt * xv;
-#pragma unroll
-            for (int i = 0; i < NP; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * A2[i]), h[i], dx * sB[j + 1][n0 + i]);
-        }
+        for (int i = 0; i < NP; ++i)
+            ck[j][i][tid] = __builtin_fmaf(fast_exp2(cs * A2[i]), h[i], a.ckp[o * N + n0 + i]);
     }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) ck[nblk - 1][i][tid] = h[i];
-    (void)xprev;
     float dA[NP], dD = 0.0f, dT = 0.0f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) dA[i] = 0.0f;
@@ -569,9 +566,8 @@ template <int N, int DT, bool GATE, bool SKIP, int MODE>
 hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t s) {
     const int64_t D = a.D, K = a.K;
     const int64_t nb = (D + kBwdThreads - 1) / kBwdThreads;
-    if (K > 1)
-        hipLaunchKernelGGL((bwd_summary_kernel<N, DT, GATE, MODE>), dim3((unsigned)(nb * K * a.batch)), dim3(kBwdThreads),
-                           0, s, a);
+    hipLaunchKernelGGL((bwd_summary_kernel<N, DT, GATE, MODE>), dim3((unsigned)(nb * K * a.batch)), dim3(kBwdThreads),
+                       0, s, a);
     const int64_t total = a.batch * D * N;
     hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     const int64_t ncb = bwd_channel_blocks(D, N, MODE == kBwdTrap);
