@@ -291,9 +291,11 @@ int ssm_ssd_step(int64_t batch, int64_t H, int64_t P, int64_t G, int64_t N, int 
  * Scratch bytes ssm_scan_bwd, ssm_scan_bwd_dt and ssm_scan_bwd_trap need for
  * these sizes (0 for empty or invalid sizes). The gradient cuts the sequence
  * into chunks of 32 tokens; the workspace holds, per (batch row, chunk,
- * channel), the state and the gradient entering the chunk and the chunk's
- * summed delta, and the partial sums of dBt, dCt and dB_prev (per block of 64
- * to 256 channels) and of dA, dDskip and ddt_bias (per chunk). It
+ * channel), the state and the gradient entering the chunk, the chunk's summed
+ * delta and the states at its three inner 8-token block entries, and the
+ * partial sums of dBt, dCt and dB_prev (per block of 64 to 256 channels) and
+ * of dA, dDskip and ddt_bias (per chunk): about 0.75 bytes per (b, t, d, n)
+ * element in all. It
  * needs no clearing: every word is written before it is read within one call.
  * Calls that share a workspace must not run at the same time.
  */
