@@ -12,15 +12,17 @@
 // hardware": the backward recomputes the intermediate states), so nothing of
 // size (batch, L, D, N) is written. The sequence is cut into chunks of 32
 // tokens:
-//   1. forward summaries: each chunk's end state from a zero start;
+//   1. forward summaries: each chunk's end state from a zero start, and the
+//      same at its inner 8-token block entries;
 //   2. reverse summaries: the gradient each chunk sends into the state before
 //      it from a zero gradient at its end (both summaries in one pass, with
 //      each chunk's summed delta);
 //   3. carries per (b, d, n) over the chunks: from state_in, the state
 //      entering every chunk; from dstate, the gradient entering every chunk
 //      from the tokens after it;
-//   4. per chunk, from its entering state and gradient: the states again at
-//      8-token checkpoints, then token by token backwards, every gradient.
+//   4. per chunk, from its entering state and gradient: the state entering
+//      each block of 8 tokens (affine in the chunk's entering state), the
+//      block's states again, then token by token backwards, every gradient.
 //      dB and dC sum over the channels: exchanges within each wave, then LDS
 //      across the block's waves, one partial per block of channels; dA and dD
 //      sum over (b, t): one partial per (b, chunk);
