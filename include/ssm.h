@@ -26,9 +26,9 @@
  * Conventions for every entry point:
  *  - Pointers are device pointers (hipMalloc'd or equivalent), owned by the
  *    caller. The library allocates nothing and may be called from several
- *    host threads; its only state is a process-wide call counter (it marks the
- *    words a call publishes in the workspace) and, per device, the CU count
- *    and resident workgroups of each kernel, queried once.
+ *    host threads; its only state is, per device, the CU count and resident
+ *    workgroups of each kernel, queried once. What a scan needs from one call
+ *    to the next lives in the caller's workspace.
  *  - Tensors are dense, row-major, in the shapes listed; D (channels) is the
  *    fastest axis of x, delta, z and y; N is the fastest axis of Bt, Ct, A
  *    and the state. Every base pointer must be 16-byte aligned.
@@ -70,6 +70,8 @@ extern "C" {
 #define SSM_ERR_ALIGN (-5)       /* a pointer is not 16-byte aligned */
 #define SSM_ERR_WORKSPACE (-6)   /* workspace is NULL or smaller than required */
 #define SSM_ERR_HIP (-7)         /* a HIP launch or device query failed */
+#define SSM_ERR_TIMEOUT (-8)     /* reported by ssm_scan_workspace_status only: a wait of the
+                                    last scan for another workgroup's results gave up */
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *ssm_status_string(int status);
@@ -86,14 +88,35 @@ const char *ssm_version(void);
  *
  * The workspace must be zero-filled before its first use. After that it may
  * be reused by later calls of any size without clearing, as long as nothing
- * else writes to it in between: each call tags its words with a new value and
- * leaves its counters at zero.
- * Calls that share a workspace must not run at the same time. The tag is
- * fixed when a call is issued, so a scan that uses a workspace must not be
- * captured into a HIP graph and replayed: a replay would reuse the tag.
+ * else writes to it in between. Its first 256 bytes are a header that the
+ * kernels keep: a call reads the tag of the last finished call there, marks
+ * its own words with the next value, and its last workgroup stores that value
+ * back and leaves the unit counters at zero. The tag is therefore taken on the
+ * device when the call runs, so a scan captured into a HIP graph may be
+ * replayed any number of times, also between eager calls on the same
+ * workspace.
+ * Calls that share a workspace must not run at the same time (on the same
+ * stream, or ordered by events).
  * Returns 0 for invalid sizes.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
+
+/*
+ * Outcome of the last ssm_scan_fwd* call that used `workspace`: waits for
+ * `stream` (a hipStream_t; NULL = the null stream) to finish, then reads the
+ * workspace header. When a sequence is cut into stripes scanned at the same
+ * time, a stripe waits for the records of the stripes before it; that wait
+ * is bounded (about 4 million polls). A wait that gives up leaves the stripe's
+ * carried-in state NaN, so its y and final state, and those of every later
+ * stripe of its channels, come out NaN; it also marks the header, and every
+ * other wait of the same call then gives up at once. This function reports
+ * that as SSM_ERR_TIMEOUT (otherwise SSM_OK, also for a workspace no scan has
+ * used yet, or NULL). A timeout means the stripes could not all make progress,
+ * for instance because two calls shared the workspace at the same time. The
+ * next call on the workspace starts afresh. SSM_ERR_HIP: the copy or the
+ * synchronisation failed; SSM_ERR_ALIGN: workspace not 16-byte aligned.
+ */
+int ssm_scan_workspace_status(const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Selective scan forward over L tokens.

@@ -26,6 +26,9 @@ Functions (same names as the C ABI):
   ssm_ssd_step(x, delta, A, Bt, Ct, state, Dskip=None, y=None) -> y: one SSD
       decode token (x (batch, H, P), Bt/Ct (batch, G, N), state in place)
   ssm_scan_workspace_bytes(batch, L, D, N, dtype) -> int
+  ssm_scan_workspace_status(workspace, stream=None) -> int: SSM_OK, or
+      SSM_ERR_TIMEOUT when a wait of the last scan on that workspace gave up
+      (waits for the stream)
   ssm_scan_bwd_workspace_bytes(batch, L, D, N, dtype) -> int
   ssm_status_string(status) -> str, ssm_version() -> str
 """
@@ -39,13 +42,15 @@ __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
     "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_ssd_step", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
-    "workspace_error",
+    "workspace_error", "ssm_scan_workspace_status", "SSM_ERR_TIMEOUT",
 ]
 
 SSM_F32 = 0
 SSM_BF16 = 1
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE",
-          -4: "SSM_ERR_UNSUPPORTED", -5: "SSM_ERR_ALIGN", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
+          -4: "SSM_ERR_UNSUPPORTED", -5: "SSM_ERR_ALIGN", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP",
+          -8: "SSM_ERR_TIMEOUT"}
+SSM_ERR_TIMEOUT = -8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libssm.so")
@@ -53,7 +58,8 @@ lib_path = os.path.join(_HERE, "libssm.so")
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step",
+           "ssm_scan_workspace_status")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -80,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_version.restype = ctypes.c_char_p
     L.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
     L.ssm_scan_workspace_bytes.restype = sz
+    L.ssm_scan_workspace_status.argtypes = [vp, sz, vp]
+    L.ssm_scan_workspace_status.restype = ci
     L.ssm_scan_fwd.argtypes = [i64, i64, i64, i64, ci] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd.restype = ci
     L.ssm_step.argtypes = [i64, i64, i64, ci] + [vp] * 9 + [vp]
@@ -130,12 +138,19 @@ def new_workspace(nbytes: int, device="cuda"):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def workspace_error(workspace) -> int:
-    """Nonzero when a cross-workgroup wait of a scan that used this workspace
-    timed out (reads the workspace header; synchronises)."""
-    if workspace is None or workspace.numel() < 4:
+def ssm_scan_workspace_status(workspace, stream=None) -> int:
+    """Status of the last scan that used `workspace`: SSM_OK (0) or
+    SSM_ERR_TIMEOUT. Waits for `stream` (default: the current stream)."""
+    if workspace is None:
         return 0
-    return int(workspace[:4].view(__import__("torch").int32).item())
+    nbytes = workspace.numel() * workspace.element_size()
+    return int(lib().ssm_scan_workspace_status(_ptr(workspace, "workspace"), nbytes, _stream(stream)))
+
+
+def workspace_error(workspace, stream=None) -> int:
+    """Nonzero (the status code) when a wait of the last scan that used this
+    workspace gave up; waits for the stream."""
+    return ssm_scan_workspace_status(workspace, stream)
 
 
 def _dtype_code(t) -> int:
@@ -169,6 +184,25 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _order_after_alloc(stream, allocated):
+    """Tensors the binding allocates come from torch's caching allocator on the
+    current stream (torch.zeros also clears them there). A launch on another
+    stream first waits for the current one, and the tensors are recorded as in
+    use on the launch stream, so that their memory is not handed out again
+    while the kernel may still use it."""
+    import torch
+    allocated = [t for t in allocated if t is not None]
+    if stream is None or not allocated:
+        return
+    cur = torch.cuda.current_stream()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream))
+    if s.cuda_stream == cur.cuda_stream:
+        return
+    s.wait_stream(cur)
+    for t in allocated:
+        t.record_stream(s)
+
+
 def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream,
           lam=None, x_prev=None, B_prev=None):
     import torch
@@ -179,11 +213,15 @@ def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, 
     act = x.dtype
     code = _dtype_code(x)
     f32 = torch.float32
+    allocated = []
     if y is None:
         y = torch.empty_like(x)
+        allocated.append(y)
     ws_bytes = ssm_scan_workspace_bytes(batch, L, D, N, code)
-    if workspace is None and ws_bytes > 0:
+    own_ws = workspace is None and ws_bytes > 0
+    if own_ws:
         workspace = new_workspace(ws_bytes, x.device)
+        allocated.append(workspace)
     dname = "delta_raw" if name == "ssm_scan_fwd_dt" else "delta"
     args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, L, D))]
     if name == "ssm_scan_fwd_dt":
@@ -204,9 +242,17 @@ def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, 
     ]
     ws_ptr = _ptr(workspace, "workspace")
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _order_after_alloc(stream, allocated)
     st = getattr(lib(), name)(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
     if st != 0:
         raise SSMError(st, name)
+    if own_ws:
+        # The workspace is this call's alone, so its outcome can be read here;
+        # that waits for the stream. A caller that passes its own workspace
+        # reads it with ssm_scan_workspace_status when it chooses.
+        st = ssm_scan_workspace_status(workspace, stream)
+        if st != 0:
+            raise SSMError(st, name)
     return y
 
 
@@ -214,7 +260,9 @@ def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_o
                  y=None, workspace=None, stream=None):
     """Selective scan forward. Shapes: x, delta, z, y (batch, L, D); A (D, N);
     Bt, Ct (batch, L, N); Dskip (D,); state_in, state_out (batch, D, N) float32.
-    Allocates y and the workspace with torch when they are not given."""
+    Allocates y and the workspace with torch when they are not given; with a
+    workspace of its own the call waits for the stream and raises SSMError
+    (SSM_ERR_TIMEOUT) if a wait for another workgroup's results gave up."""
     return _scan("ssm_scan_fwd", x, delta, None, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream)
 
 
@@ -245,8 +293,10 @@ def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, lam=No
     act = x.dtype
     code = _dtype_code(x)
     f32 = torch.float32
+    allocated = []
     if y is None:
         y = torch.empty_like(x)
+        allocated.append(y)
     dname = "delta_raw" if name == "ssm_step_dt" else "delta"
     args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, D))]
     if name == "ssm_step_dt":
@@ -262,6 +312,7 @@ def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, lam=No
     if trap:
         args += [_ptr(x_prev, "x_prev", act, (batch, D)), _ptr(B_prev, "B_prev", act, (batch, N))]
     args += [_ptr(state, "state", f32, (batch, D, N)), _ptr(y, "y", act, (batch, D))]
+    _order_after_alloc(stream, allocated)
     st = getattr(lib(), name)(batch, D, N, code, *args, _stream(stream))
     if st != 0:
         raise SSMError(st, name)
@@ -299,12 +350,15 @@ def ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None, 
     G, N = Bt.shape[2], Bt.shape[3]
     act, f32 = x.dtype, torch.float32
     code = _dtype_code(x)
+    allocated = []
     if y is None:
         y = torch.empty_like(x)
+        allocated.append(y)
     args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, H)), _ptr(A, "A", f32, (H,)),
             _ptr(Bt, "Bt", act, (batch, L, G, N)), _ptr(Ct, "Ct", act, (batch, L, G, N)),
             _ptr(Dskip, "Dskip", f32, (H,)), _ptr(state_in, "state_in", f32, (batch, H, P, N)),
             _ptr(state_out, "state_out", f32, (batch, H, P, N)), _ptr(y, "y", act, (batch, L, H, P))]
+    _order_after_alloc(stream, allocated)
     st = lib().ssm_ssd_fwd(batch, L, H, P, G, N, code, *args, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_ssd_fwd")
@@ -322,6 +376,7 @@ def _scan_bwd(name, x, delta, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate
     sp = name == "ssm_scan_bwd_dt"
     dn = "ddelta_raw" if sp else "ddelta"
     o = dict(out or {})
+    given = set(o)
     new = lambda shape, dt: torch.empty(shape, dtype=dt, device=x.device)
     o.setdefault("dx", torch.empty_like(x))
     o.setdefault(dn, torch.empty_like(x))
@@ -334,8 +389,10 @@ def _scan_bwd(name, x, delta, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate
     if sp:
         o.setdefault("ddt_bias", new((D,), f32))
     ws_bytes = ssm_scan_bwd_workspace_bytes(batch, L, D, N, code)
+    allocated = [v for k, v in o.items() if k not in given]
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        allocated.append(workspace)
     args = [_ptr(x, "x", act), _ptr(delta, "delta_raw" if sp else "delta", act, (batch, L, D))]
     if sp:
         args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
@@ -352,6 +409,7 @@ def _scan_bwd(name, x, delta, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate
              _ptr(o["dz"], "dz", act, (batch, L, D)), _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
     ws_ptr = _ptr(workspace, "workspace")
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _order_after_alloc(stream, allocated)
     st = getattr(lib(), name)(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
     if st != 0:
         raise SSMError(st, name)
@@ -391,6 +449,7 @@ def ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, Dskip=None, z=None, x_prev=N
     act, f32 = x.dtype, torch.float32
     code = _dtype_code(x)
     o = dict(out or {})
+    given = set(o)
     new = lambda shape, dt: torch.empty(shape, dtype=dt, device=x.device)
     for k in ("dx", "ddelta", "dlam"):
         o.setdefault(k, torch.empty_like(x))
@@ -403,8 +462,10 @@ def ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, Dskip=None, z=None, x_prev=N
     o.setdefault("dB_prev", None if x_prev is None else new((batch, N), f32))
     o.setdefault("dstate_in", new((batch, D, N), f32))
     ws_bytes = ssm_scan_bwd_workspace_bytes(batch, L, D, N, code)
+    allocated = [v for k, v in o.items() if k not in given]
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        allocated.append(workspace)
     args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(lam, "lam", act, (batch, L, D)),
             _ptr(A, "A", f32, (D, N)), _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
             _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
@@ -419,6 +480,7 @@ def ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, Dskip=None, z=None, x_prev=N
             _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
     ws_ptr = _ptr(workspace, "workspace")
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _order_after_alloc(stream, allocated)
     st = lib().ssm_scan_bwd_trap(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_scan_bwd_trap")
@@ -436,11 +498,14 @@ def ssm_ssd_step(x, delta, A, Bt, Ct, state, Dskip=None, y=None, stream=None):
     G, N = Bt.shape[1], Bt.shape[2]
     act, f32 = x.dtype, torch.float32
     code = _dtype_code(x)
+    allocated = []
     if y is None:
         y = torch.empty_like(x)
+        allocated.append(y)
     args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, H)), _ptr(A, "A", f32, (H,)),
             _ptr(Bt, "Bt", act, (batch, G, N)), _ptr(Ct, "Ct", act, (batch, G, N)), _ptr(Dskip, "Dskip", f32, (H,)),
             _ptr(state, "state", f32, (batch, H, P, N)), _ptr(y, "y", act, (batch, H, P))]
+    _order_after_alloc(stream, allocated)
     st = lib().ssm_ssd_step(batch, H, P, G, N, code, *args, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_ssd_step")

@@ -5,8 +5,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <atomic>
-
 #include "../../include/ssm.h"
 #include "ssm_internal.h"
 
@@ -32,10 +30,9 @@ int64_t checked_mul3(int64_t a, int64_t b, int64_t c) {
 
 size_t round_up256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Both scans keep a 256-byte header at the start of the workspace: the first
-// word reports a timed-out wait for another workgroup's words; bytes 64..95
-// hold the stripe scan's eight unit counters.
-constexpr size_t kHeader = 256;
+// Both scans keep a header of ssm::kHdrBytes at the start of the workspace
+// (its words are described in ssm_internal.h); the chunked scan leaves it alone.
+constexpr size_t kHeader = ssm::kHdrBytes;
 
 // Workspace of the chunked three-launch scan:
 // [header | chunk states (batch,K,D,N) | summed deltas (batch,K,D)].
@@ -72,16 +69,6 @@ size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) 
                                                                : twopass_workspace(batch, L, D, N, &K, &Lc);
 }
 
-// Distinct nonzero value per call; marks the words a call publishes in the workspace.
-uint32_t next_epoch() {
-    static std::atomic<uint32_t> counter{0};
-    uint32_t e;
-    do {
-        e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-    } while (e == 0);
-    return e;
-}
-
 }  // namespace
 
 extern "C" {
@@ -96,11 +83,23 @@ const char *ssm_status_string(int status) {
         case SSM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case SSM_ERR_WORKSPACE: return "workspace is missing or too small";
         case SSM_ERR_HIP: return "a HIP launch failed";
+        case SSM_ERR_TIMEOUT: return "a wait for another workgroup's results gave up; the outputs that depend on them are NaN";
         default: return "unknown status";
     }
 }
 
 const char *ssm_version(void) { return "ssm-gfx950 0.1"; }
+
+int ssm_scan_workspace_status(const void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace || workspace_bytes < kHeader) return SSM_OK;  // no header: nothing can have failed
+    if (!aligned16(workspace)) return SSM_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t hdr[4] = {0, 0, 0, 0};
+    if (hipMemcpyAsync(hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess) return SSM_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SSM_ERR_HIP;
+    // the last call failed when the error word carries its tag
+    return hdr[ssm::kHdrError] != 0 && hdr[ssm::kHdrError] == hdr[ssm::kHdrEpoch] ? SSM_ERR_TIMEOUT : SSM_OK;
+}
 
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     if (batch < 0 || L < 0 || D < 0 || !supported_n(N)) return 0;
@@ -175,10 +174,8 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.n_whole = p.n_whole;
         a.S = p.S;
         a.SL = p.SL;
-        a.epoch = next_epoch();
         char *w = (char *)workspace;
-        a.error = (uint32_t *)w;
-        a.counters = (uint32_t *)(w + 64);
+        a.hdr = (uint32_t *)w;
         a.incl = (uint64_t *)(w + p.off_incl);
         a.agg = (uint64_t *)(w + p.off_agg);
         return ssm::launch_scan_stripe(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;

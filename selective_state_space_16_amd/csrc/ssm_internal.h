@@ -25,6 +25,21 @@ struct ScanArgs {
     int64_t Lc;        // tokens per chunk (the last chunk may be shorter)
 };
 
+// Header of a scan workspace: the first kHdrBytes bytes, as 32-bit words.
+// The kernels keep it consistent from call to call; it must be zero before the
+// workspace is first used.
+//  [kHdrError]    tag of the last call in which a wait for another workgroup's
+//                 words gave up (0: none)
+//  [kHdrEpoch]    tag of the last call that finished (0: none yet). A call tags
+//                 the words it publishes with this value plus one (skipping 0),
+//                 read on the device, so a launch replayed from a graph gets a
+//                 new tag like any other.
+//  [kHdrDone]     workgroups of the running call that have finished (0 between
+//                 calls); the last one advances kHdrEpoch and clears this word
+//  [kHdrCounters] eight unit counters (0 between calls)
+constexpr int kHdrError = 0, kHdrEpoch = 1, kHdrDone = 2, kHdrCounters = 16;
+constexpr size_t kHdrBytes = 256;
+
 // Stripe scan: every wave walks its channels along a stripe of the sequence.
 struct StripeArgs {
     int64_t batch, L, D;
@@ -43,9 +58,7 @@ struct StripeArgs {
     int64_t n_whole;        // columns per list run as one whole-sequence unit each
     int64_t S;              // stripes per remaining column
     int64_t SL;             // tokens per stripe (the last one may be shorter)
-    uint32_t epoch;         // value that marks this call's published words
-    uint32_t *error;        // set when a look-back wait timed out
-    uint32_t *counters;     // 8 unit counters, zero between calls
+    uint32_t *hdr;          // the workspace header (kHdr* words)
     uint64_t *incl;         // per (column, stripe, wave): end state, epoch-tagged words
     uint64_t *agg;          // per (column, stripe, wave): end state from zero and summed delta
 };

@@ -104,7 +104,8 @@ template <int N, int DT, bool TRAP = false>
 struct Shared {
     TileBuf<N, DT, TRAP> buf[2];
     float cb[TRAP ? Geo<N, DT>::TT : 1];  // TRAP, pass 2: sum_n Ct[t,n] Bt[t,n] per token of the current tile
-    int unit;  // the unit handed to this workgroup
+    int unit;      // the unit handed to this workgroup
+    uint32_t tag;  // this call's tag (see kHdrEpoch)
 };
 
 template <int N, int DT, bool TRAP>
@@ -467,7 +468,17 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
     const int64_t n_whole = a.n_whole, n_split = a.cols_per_list - a.n_whole;
 
     const int list = blockIdx.x % kLists;
-    uint32_t *const counter = a.counters + list;
+    uint32_t *const counter = a.hdr + kHdrCounters + list;
+    uint32_t *const err = a.hdr + kHdrError;
+    // This call's tag: one past that of the last finished call (skipping 0,
+    // the value of a cleared workspace). Every workgroup reads it before it
+    // counts itself finished, and only the last to finish advances it.
+    if (threadIdx.x == 0) {
+        const uint32_t e = ld_flag(a.hdr + kHdrEpoch) + 1u;
+        sh.tag = e == 0u ? 1u : e;
+    }
+    lds_barrier();
+    const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(sh.tag);
     const uint32_t units = (uint32_t)(n_whole + n_split * a.S);
     // every workgroup takes units until it is handed one past the end, so a
     // call makes exactly (units + workgroups of the list) takes; the last one
@@ -787,8 +798,8 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             prefetch(std::integral_constant<int, 1>{});
             walk(std::integral_constant<int, 1>{}, agg, dagg);
             uint64_t *ar = a.agg + rec * (64 * (NL + 1));
-            publish_state<NL>(ar, l, agg, a.epoch);
-            st_tagged(ar + 64 * NL + l, dagg, a.epoch);
+            publish_state<NL>(ar, l, agg, epoch);
+            st_tagged(ar + 64 * NL + l, dagg, epoch);
         } else if (has_next) {
             prefetch(std::integral_constant<int, 1>{});
             walk(std::integral_constant<int, 1>{}, agg, dagg);  // stripe 0: its end state goes out directly
@@ -814,18 +825,22 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
         } else {
             // Look back over the earlier stripes of this column: the nearest
             // one whose end state is out, with the aggregates of all stripes
-            // after it out.
+            // after it out. A wait that gives up (the spin limit, or another
+            // wait of this call gave up first: then this one does not wait at
+            // all) leaves a NaN state, so that every output depending on it
+            // is NaN, and marks the header's error word with this call's tag.
             int64_t j0 = -1;
             long spin = 0;
-            while (true) {
+            bool failed = (uint32_t)__builtin_amdgcn_readfirstlane(ld_flag(err)) == epoch;
+            while (!failed) {
                 const int64_t jj = j - 1 - l;  // stripe examined by this lane
                 bool inc = false, ag = false;
                 if (jj >= 0) {
                     // the first word of a record stands for all of it; the
                     // replay below still checks every word it reads
                     const int64_t r2 = rec_of(jj);
-                    inc = (uint32_t)(ld_tagged(a.incl + r2 * (64 * NL)) >> 32) == a.epoch;
-                    ag = inc || (uint32_t)(ld_tagged(a.agg + r2 * (64 * (NL + 1))) >> 32) == a.epoch;
+                    inc = (uint32_t)(ld_tagged(a.incl + r2 * (64 * NL)) >> 32) == epoch;
+                    ag = inc || (uint32_t)(ld_tagged(a.agg + r2 * (64 * (NL + 1))) >> 32) == epoch;
                 }
                 const uint64_t m_inc = __builtin_amdgcn_ballot_w64(inc);
                 const uint64_t m_agg = __builtin_amdgcn_ballot_w64(ag);
@@ -838,22 +853,25 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                     }
                 }
                 if (++spin > kSpinLimit ||
-                    (spin % 64 == 0 && __builtin_amdgcn_readfirstlane(ld_flag(a.error)) != 0)) {
-                    if (l == 0) __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    (spin % 64 == 0 && (uint32_t)__builtin_amdgcn_readfirstlane(ld_flag(err)) == epoch)) {
+                    failed = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(4);
             }
-            if (j0 < 0) {
-#pragma unroll
-                for (int q = 0; q < NL; ++q) h[q] = 0.0f;
-            } else {
+            if (!failed) {
                 // Replay forward from that state with the arithmetic each
                 // stripe uses for its own end state, kReplay records per
-                // round trip.
+                // round trip. A word still not of this call after its own
+                // bounded wait fails the replay.
+                bool bad = false;
+                auto value = [&](uint64_t v) {
+                    bad |= (uint32_t)(v >> 32) != epoch;
+                    return __uint_as_float((uint32_t)v);
+                };
                 const uint64_t *src = a.incl + rec_of(j0) * (64 * NL) + l;
 #pragma unroll
-                for (int q = 0; q < NL; ++q) h[q] = __uint_as_float((uint32_t)ld_valid(src + q * 64, a.epoch));
+                for (int q = 0; q < NL; ++q) h[q] = value(ld_valid(src + q * 64, epoch));
                 for (int64_t jj = j0 + 1; jj < j; jj += kReplay) {
                     uint64_t sv[kReplay][NL], dv2[kReplay];
 #pragma unroll
@@ -869,14 +887,20 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                     for (int r = 0; r < kReplay; ++r) {
                         if (jj + r < j) {
                             const uint64_t *ar = a.agg + rec_of(jj + r) * (64 * (NL + 1));
-                            const float dd = __uint_as_float((uint32_t)recheck(dv2[r], ar + 64 * NL + l, a.epoch));
+                            const float dd = value(recheck(dv2[r], ar + 64 * NL + l, epoch));
 #pragma unroll
                             for (int q = 0; q < NL; ++q)
                                 h[q] = __builtin_fmaf(fast_exp2(A2[q] * dd), h[q],
-                                                      __uint_as_float((uint32_t)recheck(sv[r][q], ar + q * 64 + l, a.epoch)));
+                                                      value(recheck(sv[r][q], ar + q * 64 + l, epoch)));
                         }
                     }
                 }
+                failed = __builtin_amdgcn_ballot_w64(bad) != 0;
+            }
+            if (failed) {
+                if (l == 0) __hip_atomic_store(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int q = 0; q < NL; ++q) h[q] = __builtin_nanf("");
             }
         }
         if (has_next) {
@@ -884,7 +908,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             float e[NL];
 #pragma unroll
             for (int q = 0; q < NL; ++q) e[q] = __builtin_fmaf(fast_exp2(A2[q] * dagg), h[q], agg[q]);
-            publish_state<NL>(a.incl + rec * (64 * NL), l, e, a.epoch);
+            publish_state<NL>(a.incl + rec * (64 * NL), l, e, epoch);
         }
 
         float unused = 0.0f;
@@ -893,6 +917,15 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             float *so = a.state_out + (b * D + d) * N + nstate0;
 #pragma unroll
             for (int q = 0; q < NL; ++q) so[q] = h[q];
+        }
+    }
+    // The last workgroup to finish publishes this call's tag as the last
+    // finished call's and clears the count for the next call.
+    if (threadIdx.x == 0) {
+        uint32_t *const done = a.hdr + kHdrDone;
+        if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+            __hip_atomic_store(a.hdr + kHdrEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

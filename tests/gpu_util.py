@@ -70,7 +70,7 @@ def gpu_scan(inp, want_state=True, state_alias=False):
     y = ssm.ssm_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], Dskip=dev["Dskip"],
                          z=dev["z"], state_in=dev["state_in"], state_out=st_out, workspace=ws)
     torch.cuda.synchronize()
-    assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
+    assert ssm.workspace_error(ws) == 0, "a look-back wait gave up"
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
 
 
@@ -92,7 +92,7 @@ def gpu_scan_dt(inp, dt_bias=True):
                             dev["Ct"], Dskip=dev["Dskip"], z=dev["z"], state_in=dev["state_in"], state_out=st_out,
                             workspace=ws)
     torch.cuda.synchronize()
-    assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
+    assert ssm.workspace_error(ws) == 0, "a look-back wait gave up"
     return to_f64(y), to_f64(st_out)
 
 
@@ -112,7 +112,7 @@ def gpu_scan_trap(inp, prev=True, want_state=True):
                               B_prev=dev["B_prev"] if prev else None, state_in=dev["state_in"], state_out=st_out,
                               workspace=ws)
     torch.cuda.synchronize()
-    assert ssm.workspace_error(ws) == 0, "a look-back wait timed out"
+    assert ssm.workspace_error(ws) == 0, "a look-back wait gave up"
     return to_f64(y), (to_f64(st_out) if st_out is not None else None)
 
 

@@ -37,10 +37,17 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert ssm.ssm_status_string(code) and ssm.ssm_status_string(code) != "unknown status"
     assert ssm.ssm_status_string(99) == "unknown status"
     assert "gfx950" in ssm.ssm_version()
+
+
+def test_workspace_status_without_a_workspace():
+    # no workspace, or one too small to hold a header: nothing to report, no HIP call
+    assert ssm.lib().ssm_scan_workspace_status(None, 0, None) == 0
+    assert ssm.lib().ssm_scan_workspace_status(P, 16, None) == 0
+    assert ssm.lib().ssm_scan_workspace_status(MIS, 4096, None) == -5
 
 
 def test_workspace_bytes():
