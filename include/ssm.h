@@ -145,6 +145,30 @@ int ssm_scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                  void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssm_scan_fwd for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace: the scan's workspace is a static device
+ * array of 12 MiB inside the library, one per GPU, held until the process
+ * ends. It covers every shape the tiled scan takes (its workspace is at most
+ * 9 MiB); a shape that needs more (the chunked scan of large inputs whose
+ * channel or Bt/Ct rows are not whole 16-byte pieces) returns
+ * SSM_ERR_WORKSPACE and launches nothing. The entry point calls no hipMalloc,
+ * hipFree or other allocating routine.
+ *
+ * Arguments, checks and status codes are those of ssm_scan_fwd without the
+ * workspace. The first call on a device looks the array up and clears it with
+ * a kernel on `stream`. Every call on a GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other host threads) race
+ * and must not be made. There is no status query for the array: a wait that
+ * gives up is seen only as NaN in the outputs that depend on it.
+ */
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                         const void *x, const void *delta, const float *A,
+                         const void *Bt, const void *Ct, const float *Dskip,
+                         const void *z, const float *state_in, float *state_out,
+                         void *y, void *stream);
+
+/*
  * ssm_scan_fwd with the step size given before its activation: the scan uses
  * delta = softplus(delta_raw + dt_bias[d]), softplus(u) = log(1 + exp(u)).
  * The pages make the step size the softplus of a projection of the input plus

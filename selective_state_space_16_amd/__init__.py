@@ -9,6 +9,8 @@ Functions (same names as the C ABI):
   ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None,
                state_out=None, y=None, workspace=None) -> y
   ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None) -> y
+  ssm_scan_fwd_noalloc(x, delta, A, Bt, Ct, y, ...) -> y: ssm_scan_fwd with the
+      library's static workspace, for callers that cannot allocate
   ssm_scan_fwd_dt / ssm_step_dt: the same with delta_raw and dt_bias in place
       of delta; the kernels use softplus(delta_raw + dt_bias) as the step size
   ssm_scan_fwd_trap / ssm_step_trap: the exponential-trapezoidal rule, with a
@@ -42,7 +44,7 @@ __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
     "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_ssd_step", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
-    "workspace_error", "ssm_scan_workspace_status", "SSM_ERR_TIMEOUT",
+    "workspace_error", "ssm_scan_workspace_status", "SSM_ERR_TIMEOUT", "ssm_scan_fwd_noalloc",
 ]
 
 SSM_F32 = 0
@@ -59,7 +61,7 @@ lib_path = os.path.join(_HERE, "libssm.so")
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step",
-           "ssm_scan_workspace_status")
+           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -90,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_workspace_status.restype = ci
     L.ssm_scan_fwd.argtypes = [i64, i64, i64, i64, ci] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd.restype = ci
+    L.ssm_scan_fwd_noalloc.argtypes = [i64, i64, i64, i64, ci] + [vp] * 10 + [vp]
+    L.ssm_scan_fwd_noalloc.restype = ci
     L.ssm_step.argtypes = [i64, i64, i64, ci] + [vp] * 9 + [vp]
     L.ssm_step.restype = ci
     L.ssm_scan_fwd_dt.argtypes = [i64, i64, i64, i64, ci] + [vp] * 11 + [vp, sz, vp]
@@ -264,6 +268,27 @@ def ssm_scan_fwd(x, delta, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_o
     workspace of its own the call waits for the stream and raises SSMError
     (SSM_ERR_TIMEOUT) if a wait for another workgroup's results gave up."""
     return _scan("ssm_scan_fwd", x, delta, None, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream)
+
+
+def ssm_scan_fwd_noalloc(x, delta, A, Bt, Ct, y, Dskip=None, z=None, state_in=None, state_out=None, stream=None):
+    """ssm_scan_fwd with the library's own static workspace (for callers that
+    cannot allocate): the same arguments, y required, nothing allocated."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, D) and A (D, N)")
+    batch, L, D = x.shape
+    N = A.shape[1]
+    act, f32 = x.dtype, torch.float32
+    code = _dtype_code(x)
+    args = [_ptr(x, "x", act), _ptr(delta, "delta", act, (batch, L, D)), _ptr(A, "A", f32, (D, N)),
+            _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
+            _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+            _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(state_out, "state_out", f32, (batch, D, N)),
+            _ptr(y, "y", act, (batch, L, D))]
+    st = lib().ssm_scan_fwd_noalloc(batch, L, D, N, code, *args, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_scan_fwd_noalloc")
+    return y
 
 
 def ssm_scan_fwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, Dskip=None, z=None, state_in=None, state_out=None,

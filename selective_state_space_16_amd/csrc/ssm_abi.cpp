@@ -119,7 +119,10 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     const void *x, const void *delta, const float *dt_bias, int softplus, const float *A,
                     const void *Bt, const void *Ct, const float *Dskip,
                     const void *z, const float *state_in, float *state_out,
-                    void *y, void *workspace, size_t workspace_bytes, void *stream, TrapIn tr = {}) {
+                    void *y, void *workspace, size_t workspace_bytes, void *stream, TrapIn tr = {},
+                    bool launch = true) {
+    // launch = false: check the arguments only (every check below precedes
+    // the first HIP call)
     if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
@@ -130,7 +133,7 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     if (L == 0) {
         if (!state_out) return SSM_OK;
         if (!aligned16(state_out) || (state_in && !aligned16(state_in))) return SSM_ERR_ALIGN;
-        if (state_in == state_out) return SSM_OK;
+        if (state_in == state_out || !launch) return SSM_OK;
         return ssm::launch_state_copy(state_in, state_out, batch * D * N, s) == hipSuccess ? SSM_OK
                                                                                           : SSM_ERR_HIP;
     }
@@ -145,6 +148,7 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SSM_ERR_ALIGN;
     }
+    if (!launch) return SSM_OK;
     const Impl impl = choose_impl(batch, L, D, N, dtype);
     if (impl == Impl::kStripe) {
         ssm::StripePlan p;
@@ -559,3 +563,15 @@ int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64
 }
 
 }  // extern "C"
+
+namespace ssm {
+
+int scan_fwd_euler(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, const void *x, const void *delta,
+                   const float *A, const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                   const float *state_in, float *state_out, void *y, void *workspace, size_t workspace_bytes,
+                   void *stream, bool launch) {
+    return scan_fwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, state_out, y,
+                    workspace, workspace_bytes, stream, TrapIn{}, launch);
+}
+
+}  // namespace ssm

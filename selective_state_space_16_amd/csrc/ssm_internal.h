@@ -165,6 +165,12 @@ hipError_t launch_scan_stripe_act(const StripeArgs &a, int N, int dtype, hipStre
 // The instances for the exponential-trapezoidal rule (called by launch_scan_stripe).
 hipError_t launch_scan_stripe_trap(const StripeArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);
+// ssm_scan_fwd's checks and launches (ssm_abi.cpp), for the entry points that
+// bring their own workspace; launch = false runs the checks only.
+int scan_fwd_euler(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, const void *x, const void *delta,
+                   const float *A, const void *Bt, const void *Ct, const float *Dskip, const void *z,
+                   const float *state_in, float *state_out, void *y, void *workspace, size_t workspace_bytes,
+                   void *stream, bool launch);
 hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
 hipError_t launch_step(const StepArgs &a, int N, int dtype, hipStream_t s);
 

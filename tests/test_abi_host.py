@@ -50,6 +50,32 @@ def test_workspace_status_without_a_workspace():
     assert ssm.lib().ssm_scan_workspace_status(MIS, 4096, None) == -5
 
 
+def noalloc(**kw):
+    a = dict(batch=1, L=8, D=64, N=16, dtype=0, x=P, delta=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
+             state_in=None, state_out=None, y=P, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_fwd_noalloc(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x"], a["delta"],
+                                          a["A"], a["Bt"], a["Ct"], a["Dskip"], a["z"], a["state_in"],
+                                          a["state_out"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=3), -4), (dict(x=None), -1), (dict(y=None), -1),
+    (dict(x=MIS), -5), (dict(state_out=MIS), -5),
+    # the chunked scan (channel rows not whole 16-byte pieces) of a large
+    # input needs more workspace than the library's static array
+    (dict(batch=64, L=1 << 16, D=63), -6),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, code):
+    assert noalloc(**kw) == code
+
+
+def test_noalloc_empty_is_ok_without_gpu():
+    assert noalloc(batch=0) == 0 and noalloc(D=0) == 0
+    # L = 0 with state_out aliasing state_in: nothing to copy
+    assert noalloc(L=0, state_in=P, state_out=P) == 0
+
+
 def test_workspace_bytes():
     assert ssm.ssm_scan_workspace_bytes(1, 256, 64, 16, ssm.SSM_F32) >= 0
     assert ssm.ssm_scan_workspace_bytes(-1, 256, 64, 16, ssm.SSM_F32) == 0
