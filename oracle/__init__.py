@@ -363,6 +363,54 @@ class Oracle:
                            up(tok.get("z")), state64, nthreads=nthreads)
 
 
+class ErrorSum:
+    """Relative L2 and max-abs error of a large output accumulated piece by
+    piece (sums of squares in float64), so that neither the whole reference
+    nor the whole device result needs to be held at once. A non-finite value
+    in the device result makes the relative error NaN."""
+
+    def __init__(self):
+        self.dd = 0.0
+        self.rr = 0.0
+        self.maxabs = 0.0
+        self.count = 0
+
+    def add(self, got: np.ndarray, ref: np.ndarray) -> None:
+        d = (np.asarray(got, dtype=np.float64) - ref).ravel()
+        r = np.asarray(ref, dtype=np.float64).ravel()
+        self.dd += float(np.dot(d, d))
+        self.rr += float(np.dot(r, r))
+        if d.size:
+            self.maxabs = max(self.maxabs, float(np.max(np.abs(d))))
+        self.count += r.size
+
+    @property
+    def rel(self) -> float:
+        return float(np.sqrt(self.dd) / (np.sqrt(self.rr) if self.rr > 0 else 1.0))
+
+
+def scan_compare(blocks, dtype: str, nthreads: int = 0, rule: str = "scan"):
+    """Compare a scan computed elsewhere with the oracle, block by block.
+    `blocks` yields (inp, y_got, state_got): `inp` the stored inputs of a part
+    of the workload that the oracle can run alone (some batch rows and channels
+    over the whole sequence, as Oracle.scan takes them), y_got and state_got
+    float64 (state_got None to skip it). `rule` names the oracle function:
+    "scan", "scan_dt" (step size before its activation) or "scan_trap".
+    Returns (ErrorSum of y, ErrorSum of the state, seconds spent in the
+    oracle)."""
+    o = get()
+    fn = {"scan": o.scan, "scan_dt": o.scan_dt, "scan_trap": o.scan_trap}[rule]
+    ey, es, secs = ErrorSum(), ErrorSum(), 0.0
+    for inp, y_got, st_got in blocks:
+        t = time.perf_counter()
+        yr, sr = fn(inp, dtype, nthreads=nthreads)
+        secs += time.perf_counter() - t
+        ey.add(y_got, yr)
+        if st_got is not None:
+            es.add(st_got, sr)
+    return ey, es, secs
+
+
 def upcast(a: np.ndarray, dtype: str) -> np.ndarray:
     """Exact float64 value of a stored array: float32, or bfloat16 bits (uint16)."""
     if dtype == "f32" or a.dtype == np.float32:

@@ -35,6 +35,45 @@ def to_f64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def to_host(t):
+    """A device tensor as the stored numpy array the oracle takes: float32 as
+    it is, bfloat16 as its uint16 bit patterns (exact)."""
+    import torch
+    if t is None:
+        return None
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def device_scan_blocks(dev, y, st_out, chans):
+    """Blocks of a scan run on the device, for oracle.scan_compare: for every
+    batch row and every `chans` channels, the stored inputs of those channels
+    over the whole sequence (copied back from the device), and the device's y
+    and final state for them in float64."""
+    batch, L, D = dev["x"].shape
+    for b in range(batch):
+        bt, ct = to_host(dev["Bt"][b:b + 1]), to_host(dev["Ct"][b:b + 1])
+        for c0 in range(0, D, chans):
+            sl = slice(c0, min(D, c0 + chans))
+            part = lambda k: None if dev.get(k) is None else to_host(dev[k][b:b + 1, :, sl])
+            inp = {"x": part("x"), "delta": part("delta"), "z": part("z"), "Bt": bt, "Ct": ct,
+                   "A": to_host(dev["A"][sl]), "Dskip": None if dev.get("Dskip") is None else to_host(dev["Dskip"][sl]),
+                   "state_in": None if dev.get("state_in") is None else to_host(dev["state_in"][b:b + 1, sl])}
+            yield inp, to_f64(y[b:b + 1, :, sl]), (None if st_out is None else to_f64(st_out[b:b + 1, sl]))
+
+
+def check_sum(acc, dtype, what):
+    """check() for an oracle.ErrorSum accumulated over a whole output."""
+    tol = TOL[dtype]
+    say(f"  {what}: relL2={acc.rel:.3e} maxabs={acc.maxabs:.3e} over {acc.count} values")
+    assert np.isfinite(acc.rel), what + ": non-finite output"
+    assert acc.rel <= tol["rel"], f"{what}: relL2 {acc.rel:.3e} > {tol['rel']}"
+    if tol["maxabs"] is not None:
+        assert acc.maxabs <= tol["maxabs"], f"{what}: maxabs {acc.maxabs:.3e} > {tol['maxabs']}"
+
+
 def errors(got: np.ndarray, ref: np.ndarray):
     diff = got - ref
     nref = float(np.sqrt(np.sum(ref * ref)))

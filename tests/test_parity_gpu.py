@@ -1,14 +1,16 @@
 """GPU path against the fp64 oracle on the same seeded inputs (needs MI355X).
 
-Small and medium cases compare every output; the full-size workloads compare
-sampled channels (all tokens, all batch rows) in the launch configuration the
-bench times, with the other channels filled by torch draws of the same
-distributions."""
+Small and medium cases compare every output on the seeded numpy streams; the
+full-size workloads (large layer, million tokens, 1000 decode steps) compare
+every output too, in the launch configuration the bench times, on inputs
+drawn on the device with the same recipe (seeded torch draws) and copied back
+as stored values for the oracle."""
 import numpy as np
 import pytest
 
 import workloads as W
-from gpu_util import TOL, check, errors, gpu_scan, oracle_scan, say, to_dev, to_f64
+from gpu_util import (TOL, check, check_sum, device_scan_blocks, errors, gpu_scan, oracle_scan, say,
+                      to_dev, to_f64, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,81 +86,74 @@ def test_c3_twin_bf16():
     _run_full(_cfg("c3_twin", 1, 131072, 128, 16, "bf16", gate=True, state_in=0.1, seed=3))
 
 
-def _run_sampled(cfg, sel):
-    """Full-size launch; compare the `sel` channels of y and of the final state."""
+def _run_full_size(cfg, chans, seed):
+    """The workload at full size, in the launch configuration the bench times
+    (one call, a workspace given, inputs resident on the device): inputs drawn
+    on the device with the workload's recipe (seeded), every output and every
+    final-state value compared with the oracle on the same stored values,
+    `chans` channels of one batch row at a time."""
     import torch
-    say(f"case {cfg.name} full size, sampled channels {list(sel)}")
-    part = W.scan_inputs(cfg, channels=sel)
-    fill = W.fill_scan_device(cfg, "cuda")
-    whole = W.scan_inputs(cfg, 0, 0)  # A, Dskip, state_in for every channel
-    sel_t = torch.as_tensor(sel, device="cuda")
-    for k in ("x", "delta", "z"):
-        if fill[k] is not None:
-            fill[k][:, :, sel_t] = to_dev(part[k])
-    fill["Bt"], fill["Ct"] = to_dev(part["Bt"]), to_dev(part["Ct"])
+    import oracle
     import selective_state_space_16_amd as ssm
-    A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
-    st_in = to_dev(whole["state_in"])
+    say(f"case {cfg.name} full size, every output (device-drawn inputs, seed {seed})")
+    dev = W.fill_scan_device(cfg, "cuda", seed=seed)
+    whole = W.scan_inputs(cfg, 0, 0)  # A, Dskip, state_in for every channel
+    dev["A"], dev["Dskip"], dev["state_in"] = to_dev(whole["A"]), to_dev(whole["Dskip"]), to_dev(whole["state_in"])
     st_out = torch.empty((cfg.batch, cfg.D, cfg.N), dtype=torch.float32, device="cuda")
-    y = ssm.ssm_scan_fwd(fill["x"], fill["delta"], A, fill["Bt"], fill["Ct"], Dskip=Dskip, z=fill["z"],
-                         state_in=st_in, state_out=st_out)
+    ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
+                                                        0 if cfg.dtype == "f32" else 1))
+    y = ssm.ssm_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["Bt"], dev["Ct"], Dskip=dev["Dskip"], z=dev["z"],
+                         state_in=dev["state_in"], state_out=st_out, workspace=ws)
     torch.cuda.synchronize()
-    yg = to_f64(y[:, :, sel_t])
-    sg = to_f64(st_out[:, sel_t])
-    del fill, y
-    yr, sr = oracle_scan(part, cfg.dtype)
-    check(yg, yr, cfg.dtype, "y (sampled)")
-    check(sg, sr, cfg.dtype, "state_out (sampled)")
+    assert ssm.ssm_scan_workspace_status(ws) == 0, "a look-back wait gave up"
+    ey, es, secs = oracle.scan_compare(device_scan_blocks(dev, y, st_out, chans), cfg.dtype)
+    say(f"  oracle: {secs:.1f}s on {oracle.get().threads()} threads")
+    assert ey.count == cfg.batch * cfg.L * cfg.D and es.count == cfg.batch * cfg.D * cfg.N
+    check_sum(ey, cfg.dtype, "y (every output)")
+    check_sum(es, cfg.dtype, "state_out (every value)")
 
 
-def test_c2_full_size_sampled():
-    cfg = W.SCAN_CONFIGS["c2"]
-    _run_sampled(cfg, np.array([0, 1, 37, 63, 64 * 40 + 5, 64 * 40 + 60, cfg.D - 2, cfg.D - 1]))
+def test_c2_full_size_every_output():
+    _run_full_size(W.SCAN_CONFIGS["c2"], chans=5120, seed=202)
 
 
-def test_c3_full_size_sampled():
-    cfg = W.SCAN_CONFIGS["c3"]
-    _run_sampled(cfg, np.array([64 * 7 + 0, 64 * 7 + 9, 64 * 7 + 33, 64 * 7 + 63]))
+def test_c3_full_size_every_output():
+    """The million-token workload: all 24 tile columns (cut into stripes that
+    run at the same time) and the final state of every channel."""
+    _run_full_size(W.SCAN_CONFIGS["c3"], chans=64, seed=303)
 
 
-def test_c4_decode_1000_steps_sampled():
+def test_c4_decode_1000_steps_every_channel():
     """The decode workload: (256, 5120, 16) float32 state updated in place for
-    1000 steps; sampled channels checked against 1000 oracle steps (y of
-    every step and the final state)."""
+    1000 steps with device-drawn tokens (seeded); y of every channel at every
+    step and the whole final state against 1000 oracle steps on the same
+    stored values."""
     import torch
     import oracle
     import selective_state_space_16_amd as ssm
     cfg = W.STEP_CONFIG
     steps = cfg.steps
-    sel = np.array([0, 5, 64 * 33 + 2, 64 * 33 + 61, cfg.D - 1])
-    say(f"case {cfg.name}: {steps} steps, sampled channels {list(sel)}")
+    say(f"case {cfg.name}: {steps} steps, every channel")
     base = W.step_inputs(cfg)
     state = to_dev(base["state"])
     A, Dskip = to_dev(base["A"]), to_dev(base["Dskip"])
-    fill = W.fill_step_device(cfg, steps, "cuda")
-    sel_t = torch.as_tensor(sel, device="cuda")
-    toks = []
-    for s in range(steps):
-        tk = W.step_token_inputs(cfg, s, channels=sel)
-        toks.append(tk)
-        for k in ("x", "delta", "z"):
-            fill[k][s][:, sel_t] = to_dev(tk[k])
-        fill["Bt"][s] = to_dev(tk["Bt"])
-        fill["Ct"][s] = to_dev(tk["Ct"])
-    ys = torch.empty((steps, cfg.batch, len(sel)), dtype=torch.float32, device="cuda")
-    y = torch.empty((cfg.batch, cfg.D), dtype=fill["x"].dtype, device="cuda")
+    fill = W.fill_step_device(cfg, steps, "cuda", seed=404)
+    ys = torch.empty((steps, cfg.batch, cfg.D), dtype=fill["x"].dtype, device="cuda")
     for s in range(steps):
         ssm.ssm_step(fill["x"][s], fill["delta"][s], A, fill["Bt"][s], fill["Ct"][s], state,
-                     Dskip=Dskip, z=fill["z"][s], y=y)
-        ys[s] = y[:, sel_t].float()
+                     Dskip=Dskip, z=fill["z"][s], y=ys[s])
     torch.cuda.synchronize()
     o = oracle.get()
-    st64 = np.ascontiguousarray(base["state"][:, sel], dtype=np.float64)
-    yref = np.empty((steps, cfg.batch, len(sel)))
+    st64 = np.ascontiguousarray(base["state"], dtype=np.float64)
+    ey = oracle.ErrorSum()
     for s in range(steps):
-        yref[s] = o.step(toks[s], base["A"][sel], base["Dskip"][sel], st64, cfg.dtype)
-    check(to_f64(ys), yref, cfg.dtype, "y, all steps (sampled)")
-    check(to_f64(state[:, sel_t]), st64, cfg.dtype, "final state (sampled)")
+        tk = {k: to_host(fill[k][s]) for k in ("x", "delta", "z", "Bt", "Ct")}
+        ey.add(to_f64(ys[s]), o.step(tk, base["A"], base["Dskip"], st64, cfg.dtype))
+    es = oracle.ErrorSum()
+    es.add(to_f64(state), st64)
+    assert ey.count == steps * cfg.batch * cfg.D
+    check_sum(ey, cfg.dtype, "y, every channel of every step")
+    check_sum(es, cfg.dtype, "final state, every value")
 
 
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
