@@ -194,6 +194,56 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
+def valu_calibration():
+    """Issue rates of v_exp_f32, v_fma_f32 and of the scan's mix (four
+    multiply-adds per exponential), from the calibration kernels of
+    libssm_calib.so at 1, 2, 4 and 8 waves per SIMD: lane instructions per
+    second, timed with events around each launch. This is the measurement the
+    VALU roofline's cost of two issue slots per exponential rests on."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "selective_state_space_16_amd", "libssm_calib.so"))
+    lib.ssm_calib_valu_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ssm_calib_valu_rate.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4096
+    stream = torch.cuda.current_stream()
+    rows = []
+    for op, name, per_step, exps in ((0, "v_exp_f32", 1, 1), (1, "v_fma_f32", 1, 0), (2, "4 fma + 1 exp", 5, 1)):
+        for wps in (1, 2, 4, 8):
+            blocks = cus * wps  # 4 waves per workgroup, one per SIMD
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            for _ in range(2):  # warm-up
+                assert lib.ssm_calib_valu_rate(op, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                               ctypes.c_void_p(stream.cuda_stream)) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                lib.ssm_calib_valu_rate(op, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                        ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 5 * 1e-3
+            lane_instr = blocks * 256.0 * iters * 8 * per_step
+            rate = lane_instr / sec / 1e12
+            rows.append({"op": name, "waves_per_simd": wps, "launch_us": sec * 1e6, "T_lane_instr_per_s": rate,
+                         "frac_of_issue_peak": rate / VALU_PEAK_TSLOTS,
+                         "slots_per_exp": (None if exps == 0 else None)})
+            log(f"[calib] {name:>14}  {wps} waves/SIMD  {sec * 1e6:8.1f} us  {rate:6.2f} T lane-instr/s "
+                f"({rate / VALU_PEAK_TSLOTS:.2f} of {VALU_PEAK_TSLOTS:.1f})")
+    # slots an exponential costs, from the best rates: issue peak / exp rate,
+    # and from the mix: time per step over the time of four fmas
+    best = {n: max(r["T_lane_instr_per_s"] for r in rows if r["op"] == n) for n in ("v_exp_f32", "v_fma_f32",
+                                                                                    "4 fma + 1 exp")}
+    exp_slots = best["v_fma_f32"] / best["v_exp_f32"]
+    mix_slots = 5 * best["v_fma_f32"] / best["4 fma + 1 exp"] - 4
+    for r in rows:
+        r.pop("slots_per_exp")
+    print(json.dumps({"valu_calibration": rows, "issue_peak_T_lane_instr_per_s": VALU_PEAK_TSLOTS,
+                      "cus": cus, "exp_cost_in_fma_slots_alone": exp_slots,
+                      "exp_cost_in_fma_slots_in_the_mix": mix_slots}), flush=True)
+
+
 def bench_scan(args, name):
     import numpy as np
     import torch
@@ -636,6 +686,8 @@ def main():
                     help="time the gradient of the scan (ssm_scan_bwd) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--valu-calibration", action="store_true",
+                    help="only measure the VALU issue rates of exp, fma and the scan's mix")
     args = ap.parse_args()
     if args.softplus and args.trap:
         ap.error("--softplus and --trap select different entry points; give one")
@@ -652,6 +704,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.valu_calibration:
+        valu_calibration()
         return
 
     if args.backward and args.workload in ("c4", "ssd", "ssd_step"):

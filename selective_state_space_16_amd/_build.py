@@ -10,6 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libssm.so")
+CALIB_LIB = os.path.join(PKG, "libssm_calib.so")
+CALIB_SOURCE = "ssm_calib.hip"
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["ssm_scan_stripe_act.hip", "ssm_scan_stripe_trap.hip", "ssm_scan_stripe.hip", "ssm_scan.hip", "ssm_step.hip", "ssm_ssd.hip", "ssm_ssd_step.hip", "ssm_scan_bwd_trap.hip", "ssm_scan_bwd.hip", "ssm_noalloc.hip", "ssm_abi.cpp"]
@@ -53,14 +55,23 @@ def build(out: str = LIB, verbose: bool = False) -> str:
         subprocess.run(cmd, check=True)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + [CALIB_SOURCE]))
+    calib_obj = objs.pop()
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    # the issue-rate calibration kernels, a library of their own (bench.py
+    # --valu-calibration); libssm does not contain or load them
+    tmp = CALIB_LIB + ".tmp%d" % os.getpid()
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, calib_obj]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, CALIB_LIB)
     return out
 
 
