@@ -55,7 +55,9 @@ STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTY
 SSM_ERR_TIMEOUT = -8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libssm.so")
+# The in-tree build; SSM_LIBRARY names another build of the same ABI (the host
+# tests use it to run against a sanitizer build of the argument checks).
+lib_path = os.environ.get("SSM_LIBRARY") or os.path.join(_HERE, "libssm.so")
 
 # The functions include/ssm.h declares.
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
