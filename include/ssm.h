@@ -298,10 +298,12 @@ int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,
  *   state_in      (batch, H, P, N)  float      NULL = zeros
  *   state_out     (batch, H, P, N)  float      NULL = not written; may equal state_in
  *
- * Supported: dtype SSM_BF16 (float accumulation; the chunk's masked matrix,
- * the weighted B and the state copy that meets C are rounded to bfloat16 on
- * the way into the matrix cores), P = 64, N = 64 or 128; anything else returns
- * SSM_ERR_UNSUPPORTED. H must be a multiple of G (else SSM_ERR_SHAPE). Uses no
+ * Supported: dtype SSM_BF16 (float accumulation; the chunk's masked matrix
+ * with Dskip on its diagonal, the weighted x and the state copy that meets C
+ * are rounded to bfloat16 on the way into the matrix cores), P = 64, N = 64
+ * or 128, H < 8192 * 64 and G * N < 2^25 (64 tokens of x and of Bt, Ct
+ * within 4 GiB); anything else returns SSM_ERR_UNSUPPORTED. H must be a
+ * multiple of G (else SSM_ERR_SHAPE). Uses no
  * workspace and keeps nothing between calls. Conventions otherwise as above.
  */
 int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,

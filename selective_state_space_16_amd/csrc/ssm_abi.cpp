@@ -529,6 +529,9 @@ int ssm_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (dtype != SSM_BF16 || !ssm::ssd_supported(P, N)) return SSM_ERR_UNSUPPORTED;
     if (H > 0 && (G < 1 || H % G != 0)) return SSM_ERR_SHAPE;
+    // 64 tokens of x and of Bt, Ct must span less than 4 GiB (32-bit offsets)
+    if (H > ((int64_t)UINT32_MAX / (64 * 2 * 64)) || G * N > ((int64_t)UINT32_MAX / (2 * 64)))
+        return SSM_ERR_UNSUPPORTED;
     if (checked_mul3(batch, L, H) < 0 || checked_mul3(checked_mul(batch, L), H, P) < 0 ||
         checked_mul3(checked_mul(batch, L), G, N) < 0 || checked_mul3(checked_mul(batch, H), P, N) < 0)
         return SSM_ERR_SHAPE;

@@ -240,6 +240,8 @@ def ssd(**kw):
     (dict(batch=-1), -2), (dict(dtype=3), -3), (dict(dtype=0), -4), (dict(P=32), -4), (dict(N=16), -4),
     (dict(G=3), -2), (dict(G=0), -2), (dict(x=None), -1), (dict(y=None), -1), (dict(Bt=MIS), -5),
     (dict(state_out=MIS), -5),
+    # 64 tokens of x or of Bt, Ct would span 4 GiB or more (the kernel's offsets are 32-bit)
+    (dict(H=8192 * 64, G=1), -4), (dict(H=1 << 18, G=1 << 18, N=128), -4),
 ])
 def test_ssd_rejects(kw, code):
     assert ssd(**kw) == code
@@ -247,6 +249,13 @@ def test_ssd_rejects(kw, code):
 
 def test_ssd_empty_ok_without_gpu():
     assert ssd(batch=0) == 0 and ssd(H=0) == 0 and ssd(L=0) == 0
+
+
+def test_ssd_largest_offsets_accepted():
+    """The largest H and G * N the 32-bit offsets allow pass the checks (an
+    empty batch, so nothing runs)."""
+    assert ssd(batch=0, H=8192 * 64 - 1, G=1) == 0
+    assert ssd(batch=0, H=(1 << 25) // 128 - 1, G=(1 << 25) // 128 - 1, N=128) == 0
 
 
 def bwd(**kw):

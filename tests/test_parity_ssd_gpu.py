@@ -3,13 +3,14 @@ dual: atenção mascarada", and "Mamba-2 e State Space Duality (SSD)") against
 the fp64 oracle's SSD recurrence (needs MI355X). The kernel computes by chunks
 of 64 tokens on the matrix cores; the cases cover several chunks and a ragged
 last chunk, both state sizes, heads sharing groups, a carried-in state,
-resumption, and the full-size layer on sampled heads."""
+resumption, and the full-size layer: sampled heads on the seeded streams, and
+every output on device-drawn inputs."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads as W
-from gpu_util import check, gpu_ssd, say, to_dev, to_f64
+from gpu_util import check, check_sum, gpu_ssd, say, to_dev, to_f64, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -80,3 +81,34 @@ def test_ssd_full_layer_sampled_heads():
         yr, sr = o.ssd(sub, cfg.dtype)
         check(to_f64(y[b, :, h]), yr[0, :, 0], cfg.dtype, f"y (b={b}, h={h})")
         check(to_f64(st_out[b, h]), sr[0, 0], cfg.dtype, f"state_out (b={b}, h={h})")
+
+
+@pytest.mark.parametrize("G", [1, 80])
+def test_ssd_full_layer_every_output(G):
+    """The full Mamba-2 layer workload (8 x 4096 tokens, 80 heads of 64, state
+    128), in the launch configuration the bench times: inputs drawn on the
+    device with the workload's recipe (seeded), copied back as stored values;
+    every y and every final-state value against the oracle, one batch row at a
+    time. G = 80 gives every head its own B and C."""
+    import dataclasses
+    import torch
+    import selective_state_space_16_amd as ssm
+    cfg = dataclasses.replace(W.SSD_CONFIGS["ssd"], G=G)
+    say(f"case {cfg}: every output (device-drawn inputs, seed {505 + G})")
+    dev = W.fill_ssd_device(cfg, "cuda", seed=505 + G)
+    whole = W.ssd_inputs(cfg, 0, 0)
+    A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
+    st_out = torch.empty((cfg.batch, cfg.H, cfg.P, cfg.N), dtype=torch.float32, device="cuda")
+    y = ssm.ssm_ssd_fwd(dev["x"], dev["delta"], A, dev["Bt"], dev["Ct"], Dskip=Dskip, state_out=st_out)
+    torch.cuda.synchronize()
+    o = oracle.get()
+    ey, es = oracle.ErrorSum(), oracle.ErrorSum()
+    for b in range(cfg.batch):
+        sub = {k: to_host(dev[k][b:b + 1]) for k in ("x", "delta", "Bt", "Ct")}
+        sub["A"], sub["Dskip"] = whole["A"], whole["Dskip"]
+        yr, sr = o.ssd(sub, cfg.dtype)
+        ey.add(to_f64(y[b:b + 1]), yr)
+        es.add(to_f64(st_out[b:b + 1]), sr)
+    assert ey.count == cfg.batch * cfg.L * cfg.H * cfg.P and es.count == cfg.batch * cfg.H * cfg.P * cfg.N
+    check_sum(ey, cfg.dtype, "y (every output)")
+    check_sum(es, cfg.dtype, "state_out (every value)")
