@@ -341,6 +341,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     __shared__ float sB[kBwdChunk + 1][N], sC[kBwdChunk + 1][N];
     __shared__ float ck[NCK][NP][kBwdThreads];   // state entering each block of kSub tokens
     __shared__ float red[2][NW][kSub][N];        // per-wave sums of dCt, dBt
+    // bfloat16: the chunk's x, delta, z, dy (and lam) of the block's channels,
+    // staged once with coalesced loads, so that the token loops read LDS rather
+    // than wait for a global load per token
+    constexpr bool STG = DT == 1;
+    constexpr int NA = MODE == kBwdTrap ? 5 : 4;
+    __shared__ T sA[STG ? NA : 1][STG ? kBwdChunk : 1][STG ? CPB : 1];
     const int64_t D = a.D, L = a.L, K = a.K;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = R == 1 ? 0 : lane / SPAN, cl = lane % SPAN;
@@ -370,6 +376,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         sB[jj][n] = bv;
         sC[jj][n] = cv;
     }
+    const int64_t ch0 = cb * CPB;  // first channel of the block
+    const int nch = (int)(D - ch0 < CPB ? D - ch0 : CPB);  // channels of the block that exist
+    if constexpr (STG) {
+        // thread (c, j0): channel c of the block (the last existing one past D),
+        // tokens j0, j0 + 256 / CPB, ...; a wave reads consecutive channels
+        const int c = tid % CPB, cc = c < nch ? c : nch - 1;
+        const int64_t col = ch0 + cc;
+        for (int j = tid / CPB; j < cnt_chunk; j += kBwdThreads / CPB) {
+            const int64_t row = (b * L + t0 + j) * D + col;
+            sA[0][j][c] = xp[row];
+            sA[1][j][c] = dp[row];
+            if (GATE) sA[2][j][c] = zp[row];
+            sA[3][j][c] = gp[row];
+            if constexpr (MODE == kBwdTrap) sA[NA - 1][j][c] = lp[row];
+        }
+    }
+    // this lane's channel in the staged rows (past D: the last existing one)
+    const int cws = valid ? w * SPAN + cl : nch - 1;
+    auto act = [&](int arr, int tl) -> float {
+        return STG ? __uint_as_float((uint32_t)sA[arr][tl][cws] << 16) : 0.0f;
+    };
     // TRAP: x of the token before token t (x_prev before token 0; none: 0)
     auto x_before = [&](int64_t t) -> float {
         if (t > 0) return ld_act(xp, (b * L + t - 1) * D + dc);
@@ -421,14 +448,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         float hb[kSub + 1][NP];
 #pragma unroll
         for (int i = 0; i < NP; ++i) hb[0][i] = ck[blk][i][tid];
-        float xpr = TRAP ? x_before(t0 + s0) : 0.0f;
+        float xpr = TRAP ? (STG && s0 > 0 ? act(0, s0 - 1) : x_before(t0 + s0)) : 0.0f;
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
             if (j < cnt) {
                 const int64_t row = (b * L + t0 + s0 + j) * D + dc;
-                const float dt = delta_at<DT>(dp, row, sp, dtb), xv = ld_act(xp, row);
+                float dt, xv;
+                if constexpr (STG) {
+                    const float rv = act(1, s0 + j);
+                    dt = sp ? act_round<DT>(softplus(rv + dtb)) : rv;
+                    xv = act(0, s0 + j);
+                } else {
+                    dt = delta_at<DT>(dp, row, sp, dtb);
+                    xv = ld_act(xp, row);
+                }
                 if constexpr (TRAP) {
-                    const float lm = ld_act(lp, row), mux = (dt - lm * dt) * xpr, dx = lm * dt * xv;
+                    const float lm = STG ? act(NA - 1, s0 + j) : ld_act(lp, row);
+                    const float mux = (dt - lm * dt) * xpr, dx = lm * dt * xv;
 #pragma unroll
                     for (int i = 0; i < NP; ++i)
                         hb[j + 1][i] = __builtin_fmaf(fast_exp2(dt * A2[i]),
@@ -450,17 +486,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             if (j >= cnt) continue;
             const int tl = s0 + j;
             const int64_t row = (b * L + t0 + tl) * D + dc;
-            const float raw = ld_act(dp, row), xv = ld_act(xp, row), dyv = ld_act(gp, row);
+            const float raw = STG ? act(1, tl) : ld_act(dp, row), xv = STG ? act(0, tl) : ld_act(xp, row);
+            const float dyv = STG ? act(3, tl) : ld_act(gp, row);
             const float dt = sp ? act_round<DT>(softplus(raw + dtb)) : raw;
             float gate = 1.0f, dgate = 0.0f;
-            if (GATE) silu_and_grad(ld_act(zp, row), gate, dgate);
+            if (GATE) silu_and_grad(STG ? act(2, tl) : ld_act(zp, row), gate, dgate);
             const float ds = valid ? dyv * gate : 0.0f;
             const float xvv = valid ? xv : 0.0f;
             // TRAP: the token before, its weight (1 - lam) delta, and this token's lam delta
             float lm = 0.0f, xpv = 0.0f, mu = 0.0f, gam = dt;
             if constexpr (TRAP) {
-                lm = ld_act(lp, row);
-                xpv = x_before(t0 + tl);
+                lm = STG ? act(NA - 1, tl) : ld_act(lp, row);
+                xpv = STG && tl > 0 ? act(0, tl - 1) : x_before(t0 + tl);
                 mu = dt - lm * dt;
                 gam = lm * dt;
             }
