@@ -695,7 +695,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the selective scan shards across channels and needs no "
-              f"collective on this path, and this build runs on a single MI355X (asked for --gpus "
+              f"collective on this path, so it is measured on a single MI355X (asked for --gpus "
               f"{args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
