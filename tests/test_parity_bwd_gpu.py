@@ -50,8 +50,11 @@ def test_bwd_no_options(dtype):
 
 
 @pytest.mark.parametrize("L", [1, 7, 31, 32, 33, 64, 257])
-def test_bwd_ragged_lengths(L):
-    _run(_cfg(f"bwd_L{L}", 1, L, 128, 16, "f32", seed=81))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_ragged_lengths(L, dtype):
+    """Chunks of 1 to 32 tokens and blocks of 1 to 8; with bfloat16 the
+    chunk's activations are staged in LDS only up to its last token."""
+    _run(_cfg(f"bwd_L{L}", 1, L, 128, 16, dtype, seed=81))
 
 
 def test_bwd_skip_without_its_gradient():
@@ -251,10 +254,12 @@ def test_bwd_million_token_sampled():
 
 
 @pytest.mark.parametrize("D,N", [(1, 16), (3, 16), (63, 16), (129, 2), (5, 1)])
-def test_bwd_ragged_channels(D, N):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_ragged_channels(D, N, dtype):
     """Channel counts that leave most lanes of the last block idle, including
-    whole waves past the last channel."""
-    _run(_cfg(f"bwd_D{D}_N{N}", 2, 45, D, N, "f32", seed=83))
+    whole waves past the last channel (with bfloat16 they read the staged rows
+    of the last existing channel)."""
+    _run(_cfg(f"bwd_D{D}_N{N}", 2, 45, D, N, dtype, seed=83))
 
 
 @pytest.mark.parametrize("D", [1, 63])
