@@ -23,6 +23,9 @@
 //   4. per chunk, from its entering state and gradient: the state entering
 //      each block of 8 tokens (affine in the chunk's entering state), the
 //      block's states again, then token by token backwards, every gradient.
+//      Bt and Ct of the chunk, and with bfloat16 activations its x, delta, z
+//      and dy of the block's channels, are staged in LDS first, so the token
+//      loops never wait for a global load.
 //      dB and dC sum over the channels: exchanges within each wave, then LDS
 //      across the block's waves, one partial per block of channels; dA and dD
 //      sum over (b, t): one partial per (b, chunk);
