@@ -341,7 +341,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     constexpr int NCK = kBwdChunk / kSub;    // checkpoints per chunk
     constexpr int NW = kBwdThreads / 64;     // waves per block
     // row j + 1: token t0 + j; row 0: the token before the chunk (TRAP)
-    __shared__ float sB[kBwdChunk + 1][N], sC[kBwdChunk + 1][N];
+    __shared__ float sBC[2][kBwdChunk + 1][N];  // Bt rows, then Ct rows
+    float(&sB)[kBwdChunk + 1][N] = sBC[0];
+    float(&sC)[kBwdChunk + 1][N] = sBC[1];
+    constexpr int kCt = (kBwdChunk + 1) * N;  // from a Bt element to the Ct element of its row
     __shared__ float ck[NCK][NP][kBwdThreads];   // state entering each block of kSub tokens
     __shared__ float red[2][NW][kSub][N];        // per-wave sums of dCt, dBt
     // bfloat16: the chunk's x, delta, z, dy (and lam) of the block's channels,
@@ -406,6 +409,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         return a.x_prev ? ld_act((const T *)a.x_prev, b * D + dc) : 0.0f;
     };
     const int n0 = r * NP;  // first state element of this lane
+    // With NP = 8, odd lanes hold their upper four elements first: position i
+    // of every per-lane state vector is element sx[i] = n0 + (i ^ own). Lanes
+    // l and l ^ 1 then hold the same element at positions i and i + 4, so the
+    // first halving of the channel sums adds the partner's upper half with no
+    // select.
+    constexpr bool SWQ = NP == 8;
+    const int own = SWQ ? (lane & 1) * 4 : 0;
+    int sx[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) sx[i] = n0 + (i ^ own);
     float A2[NP], h[NP], G[NP], Gb[NP];
     // TRAP: Gb = (1 - lam) delta a G of the token after: the gradient of this
     // token's input through the next token's update; after the chunk, that of
@@ -418,9 +431,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        A2[i] = a.A[dc * N + n0 + i] * kLog2e;
-        h[i] = a.hst[((b * K + k) * D + dc) * N + n0 + i];
-        G[i] = a.gq[((b * K + k) * D + dc) * N + n0 + i];
+        A2[i] = a.A[dc * N + sx[i]] * kLog2e;
+        h[i] = a.hst[((b * K + k) * D + dc) * N + sx[i]];
+        G[i] = a.gq[((b * K + k) * D + dc) * N + sx[i]];
         Gb[i] = mu1 * G[i];
     }
     __syncthreads();
@@ -437,21 +450,42 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         const float cs = a.ckd[o];
 #pragma unroll
         for (int i = 0; i < NP; ++i)
-            ck[j][i][tid] = __builtin_fmaf(fast_exp2(cs * A2[i]), h[i], a.ckp[o * N + n0 + i]);
+            ck[j][i][tid] = __builtin_fmaf(fast_exp2(cs * A2[i]), h[i], a.ckp[o * N + sx[i]]);
     }
     float dA[NP], dD = 0.0f, dT = 0.0f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) dA[i] = 0.0f;
     const float dsk = SKIP ? a.Dskip[dc] : 0.0f;
-    const int elem = n0 + wave_sum_index<NP>(cl);  // element this lane holds after the channel sums
+    // the element whose sum over the wave's channels chan_sum leaves in this lane
+    const int elem = SWQ ? n0 + own + wave_sum_index<4>(cl >> 1) : n0 + wave_sum_index<NP>(cl);
+    // sums over the wave's channels of a per-lane state vector (position order)
+    auto chan_sum = [&](float(&v)[NP]) -> float {
+        if constexpr (SWQ) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += xor_lane<1>(v[i + 4]);
+            float u[4] = {v[0], v[1], v[2], v[3]};
+            halve<2, 2>(u, lane);
+            return fold<8, SPAN>(u[0]);
+        } else {
+            return wave_sum_vec<NP, SPAN>(v, lane);
+        }
+    };
     for (int blk = nblk - 1; blk >= 0; --blk) {
         const int s0 = blk * kSub;
         const int cnt = cnt_chunk - s0 < kSub ? cnt_chunk - s0 : kSub;
-        // states of the block: hb[j] = state entering token s0 + j
-        float hb[kSub + 1][NP];
+        // states of the block: hb[j] = state entering token s0 + j; with
+        // bfloat16 activations also ea[j][i], the decay of token s0 + j, kept
+        // for the reverse walk (float32 recomputes it, and its lower register
+        // count keeps three waves per SIMD)
+        float hb[kSub + 1][NP], ea[STG ? kSub : 1][NP];
 #pragma unroll
         for (int i = 0; i < NP; ++i) hb[0][i] = ck[blk][i][tid];
         float xpr = TRAP ? (STG && s0 > 0 ? act(0, s0 - 1) : x_before(t0 + s0)) : 0.0f;
+        // Bt of row s0 + u at position i of the lane: brow(i, u * N); Ct: brow(i, kCt + u * N)
+        const float *bq[(NP + 3) / 4];
+#pragma unroll
+        for (int q = 0; q < (NP + 3) / 4; ++q) bq[q] = &sBC[0][0][0] + s0 * N + n0 + ((4 * q) ^ own);
+        auto brow = [&](int i, int off) -> float { return bq[i / 4][off + (i % 4)]; };
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
             if (j < cnt) {
@@ -469,17 +503,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                     const float lm = STG ? act(NA - 1, s0 + j) : ld_act(lp, row);
                     const float mux = (dt - lm * dt) * xpr, dx = lm * dt * xv;
 #pragma unroll
-                    for (int i = 0; i < NP; ++i)
-                        hb[j + 1][i] = __builtin_fmaf(fast_exp2(dt * A2[i]),
-                                                      __builtin_fmaf(mux, sB[s0 + j][n0 + i], hb[j][i]),
-                                                      dx * sB[s0 + j + 1][n0 + i]);
+                    for (int i = 0; i < NP; ++i) {
+                        const float e = fast_exp2(dt * A2[i]);
+                        if constexpr (STG) ea[j][i] = e;
+                        hb[j + 1][i] = __builtin_fmaf(e, __builtin_fmaf(mux, brow(i, j * N), hb[j][i]),
+                                                      dx * brow(i, (j + 1) * N));
+                    }
                     xpr = xv;
                 } else {
                     const float dx = dt * xv;
 #pragma unroll
-                    for (int i = 0; i < NP; ++i)
-                        hb[j + 1][i] =
-                            __builtin_fmaf(fast_exp2(dt * A2[i]), hb[j][i], dx * sB[s0 + j + 1][n0 + i]);
+                    for (int i = 0; i < NP; ++i) {
+                        const float e = fast_exp2(dt * A2[i]);
+                        if constexpr (STG) ea[j][i] = e;
+                        hb[j + 1][i] = __builtin_fmaf(e, hb[j][i], dx * brow(i, (j + 1) * N));
+                    }
                 }
             }
         }
@@ -510,7 +548,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             float pre = 0.0f, gaa = 0.0f, gb = 0.0f, gbb = 0.0f, gav = 0.0f, dCv[NP], dBv[NP];
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                const float Cv = sC[tl + 1][n0 + i], Bv = sB[tl + 1][n0 + i];
+                const float Cv = brow(i, kCt + (j + 1) * N), Bv = brow(i, (j + 1) * N);
                 pre = __builtin_fmaf(Cv, hb[j + 1][i], pre);
                 G[i] = __builtin_fmaf(Cv, ds, G[i]);
                 dCv[i] = ds * hb[j + 1][i];
@@ -522,10 +560,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 } else {
                     dBv[i] = G[i] * (dt * xvv);
                 }
-                G[i] *= fast_exp2(dt * A2[i]);  // the gradient of h_{t-1}
+                G[i] *= STG ? ea[STG ? j : 0][i] : fast_exp2(dt * A2[i]);  // the gradient of h_{t-1}
                 float hp = hb[j][i];
                 if constexpr (TRAP) {
-                    const float Bp = sB[tl][n0 + i];
+                    const float Bp = brow(i, j * N);
                     hp = __builtin_fmaf(mux, Bp, hp);
                     gav = __builtin_fmaf(G[i], Bp, gav);
                     Gb[i] = mu * G[i];
@@ -566,8 +604,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 if (GATE) st_act((T *)a.dz, row, dyv * pre * dgate);
                 if (TRAP) st_act((T *)a.dlam, row, dt * (xv * gb - xpv * gav));
             }
-            const float sc = wave_sum_vec<NP, SPAN>(dCv, lane);
-            const float sb = wave_sum_vec<NP, SPAN>(dBv, lane);
+            const float sc = chan_sum(dCv);
+            const float sb = chan_sum(dBv);
             if (cl < NP) {
                 red[0][w][j][elem] = sc;
                 red[1][w][j][elem] = sb;
@@ -594,12 +632,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             float gp = 0.0f, dBp[NP];
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                gp = __builtin_fmaf(Gb[i], sB[0][n0 + i], gp);
+                gp = __builtin_fmaf(Gb[i], sB[0][sx[i]], gp);
                 dBp[i] = Gb[i] * xp0;
             }
             if (R > 1) gp = fold<SPAN, 64>(gp);
             if (valid && r == 0) st_act((T *)a.dx_prev, b * D + d, gp);
-            const float sb = wave_sum_vec<NP, SPAN>(dBp, lane);
+            const float sb = chan_sum(dBp);
             if (cl < NP) red[1][w][0][elem] = sb;
             __syncthreads();
             for (int n = tid; n < N; n += kBwdThreads) {
@@ -612,14 +650,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     }
     if (!valid) return;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) a.pdA[((b * K + k) * D + d) * N + n0 + i] = dA[i];
+    for (int i = 0; i < NP; ++i) a.pdA[((b * K + k) * D + d) * N + sx[i]] = dA[i];
     if (r == 0) {
         a.pdD[(b * K + k) * D + d] = dD;
         a.pdT[(b * K + k) * D + d] = dT;
     }
     if (k == 0 && a.dstate_in) {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) a.dstate_in[(b * D + d) * N + n0 + i] = G[i];
+        for (int i = 0; i < NP; ++i) a.dstate_in[(b * D + d) * N + sx[i]] = G[i];
     }
 }
 
