@@ -66,27 +66,40 @@ __device__ __forceinline__ void silu_and_grad(float z, float &g, float &dg) {
     dg = sg * (1.0f + z * (1.0f - sg));
 }
 
-// v from lane (lane ^ BIT): DPP lane moves inside rows of 16 lanes for BIT <
-// 16 (quad permutes for 1 and 2; shifts by 4 within banks of 4 lanes for 4;
-// a rotation by 8 for 8), a swizzle inside 32 lanes for 16, a permute for 32.
+// v from lane (lane ^ BIT): DPP lane moves inside rows of 16 lanes for BIT 1,
+// 2 (quad permutes) and 8 (a rotation by 8), swizzles inside 32 lanes for 4
+// and 16, a permute for 32. Every lane has a source, so the DPP moves need no
+// initial value.
 template <int BIT>
 __device__ __forceinline__ float xor_lane(float v) {
     const int x = __float_as_int(v);
     if constexpr (BIT == 1) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+        return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
     } else if constexpr (BIT == 2) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+        return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
     } else if constexpr (BIT == 4) {
-        // lanes 0-3 and 8-11 of a row read lane + 4 (row_shl:4), lanes 4-7 and 12-15 lane - 4 (row_shr:4)
-        const int lo = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0x5, false);
-        return __int_as_float(__builtin_amdgcn_update_dpp(lo, x, 0x114, 0xF, 0xA, false));
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x101F));  // and 31, xor 4
     } else if constexpr (BIT == 8) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));  // row_ror:8
+        return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
     } else if constexpr (BIT == 16) {
         return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));  // and 31, xor 16
     } else {
         return __shfl_xor(v, BIT);
     }
+}
+
+// u[i] += fp * v[i + 4] of lane ^ 1 (i < 4): one DPP multiply-add each. The
+// s_nop covers the wait a DPP source written by the previous VALU instruction
+// needs (the compiler does not fold the move into a multiply-add itself).
+__device__ __forceinline__ void fmac_quad_neighbour(float (&u)[4], const float (&v)[8], float fp) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3])
+        : "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(fp));
 }
 
 // One halving exchange of wave_sum_vec and the ones after it: lanes with bit
@@ -458,16 +471,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
     const float dsk = SKIP ? a.Dskip[dc] : 0.0f;
     // the element whose sum over the wave's channels chan_sum leaves in this lane
     const int elem = SWQ ? n0 + own + wave_sum_index<4>(cl >> 1) : n0 + wave_sum_index<NP>(cl);
-    // sums over the wave's channels of a per-lane state vector (position order)
-    auto chan_sum = [&](float(&v)[NP]) -> float {
+    // sums over the wave's channels of f times a per-lane state vector v
+    // (position order). With SWQ the first halving takes the neighbour's
+    // upper half times its factor in one multiply-add each.
+    auto chan_sum = [&](const float(&v)[NP], float f) -> float {
         if constexpr (SWQ) {
+            float u[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] += xor_lane<1>(v[i + 4]);
-            float u[4] = {v[0], v[1], v[2], v[3]};
+            for (int i = 0; i < 4; ++i) u[i] = v[i] * f;
+            fmac_quad_neighbour(u, v, xor_lane<1>(f));
             halve<2, 2>(u, lane);
             return fold<8, SPAN>(u[0]);
         } else {
-            return wave_sum_vec<NP, SPAN>(v, lane);
+            float t[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) t[i] = v[i] * f;
+            return wave_sum_vec<NP, SPAN>(t, lane);
         }
     };
     for (int blk = nblk - 1; blk >= 0; --blk) {
@@ -545,20 +564,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
             const float mux = mu * xpv;
             // Ga = a G is the gradient of h_{t-1}; gah = Ga (h_{t-1} + (1 - lam) delta v_{t-1});
             // d(delta) takes sum(gah A), and x sum(G B) (Euler) or the trapezoid's terms
-            float pre = 0.0f, gaa = 0.0f, gb = 0.0f, gbb = 0.0f, gav = 0.0f, dCv[NP], dBv[NP];
+            // dCt takes ds times the state, dBt x times the input's gradient
+            // (Euler: delta x times G), summed over channels below
+            float pre = 0.0f, gaa = 0.0f, gb = 0.0f, gbb = 0.0f, gav = 0.0f, gin[NP];
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 const float Cv = brow(i, kCt + (j + 1) * N), Bv = brow(i, (j + 1) * N);
                 pre = __builtin_fmaf(Cv, hb[j + 1][i], pre);
                 G[i] = __builtin_fmaf(Cv, ds, G[i]);
-                dCv[i] = ds * hb[j + 1][i];
                 gb = __builtin_fmaf(G[i], Bv, gb);
                 if constexpr (TRAP) {
-                    const float dv = __builtin_fmaf(gam, G[i], Gb[i]);  // gradient of v_t = B_t x_t
-                    dBv[i] = dv * xvv;
+                    gin[i] = __builtin_fmaf(gam, G[i], Gb[i]);  // gradient of v_t = B_t x_t
                     gbb = __builtin_fmaf(Gb[i], Bv, gbb);
                 } else {
-                    dBv[i] = G[i] * (dt * xvv);
+                    gin[i] = G[i];
                 }
                 G[i] *= STG ? ea[STG ? j : 0][i] : fast_exp2(dt * A2[i]);  // the gradient of h_{t-1}
                 float hp = hb[j][i];
@@ -604,8 +623,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
                 if (GATE) st_act((T *)a.dz, row, dyv * pre * dgate);
                 if (TRAP) st_act((T *)a.dlam, row, dt * (xv * gb - xpv * gav));
             }
-            const float sc = chan_sum(dCv);
-            const float sb = chan_sum(dBv);
+            const float sc = chan_sum(hb[j + 1], ds);
+            const float sb = chan_sum(gin, TRAP ? xvv : dt * xvv);
             if (cl < NP) {
                 red[0][w][j][elem] = sc;
                 red[1][w][j][elem] = sb;
@@ -629,15 +648,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chunk_kernel(BwdArgs a) {
         // the token before token 0: its input's gradient is Gb after token 0
         if (k == 0 && a.dx_prev) {
             const float xp0 = valid ? ld_act((const T *)a.x_prev, b * D + dc) : 0.0f;
-            float gp = 0.0f, dBp[NP];
+            float gp = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                gp = __builtin_fmaf(Gb[i], sB[0][sx[i]], gp);
-                dBp[i] = Gb[i] * xp0;
-            }
+            for (int i = 0; i < NP; ++i) gp = __builtin_fmaf(Gb[i], sB[0][sx[i]], gp);
             if (R > 1) gp = fold<SPAN, 64>(gp);
             if (valid && r == 0) st_act((T *)a.dx_prev, b * D + d, gp);
-            const float sb = chan_sum(dBp);
+            const float sb = chan_sum(Gb, xp0);
             if (cl < NP) red[1][w][0][elem] = sb;
             __syncthreads();
             for (int n = tid; n < N; n += kBwdThreads) {
