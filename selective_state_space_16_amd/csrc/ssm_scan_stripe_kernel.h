@@ -59,6 +59,27 @@ constexpr int kLists = 8;   // unit lists (one per XCD of an MI355X)
 constexpr int kReplay = 4;  // stripe records loaded per round trip of a look-back replay
 constexpr int kSlotsPerList = 64;  // workgroups a list is planned for (2 per CU on 256 CUs)
 
+// dot_row for four states per lane when `c` came straight from an LDS read
+// (the high-half loads): a DPP read needs no wait states after an LDS read,
+// only after a VALU write, so the s_nop of dot_row is left out.
+template <int S0>
+__device__ __forceinline__ void dot_row_lds(float &acc, float c, const float (&h)[4]) {
+    asm volatile("v_mul_f32_dpp %0, %1, %2 row_newbcast:%6 row_mask:0xf bank_mask:0xf"
+                 "\n\tv_fmac_f32_dpp %0, %1, %3 row_newbcast:%7 row_mask:0xf bank_mask:0xf"
+                 "\n\tv_fmac_f32_dpp %0, %1, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf"
+                 "\n\tv_fmac_f32_dpp %0, %1, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
+                 : "=&v"(acc)
+                 : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "i"(S0), "i"(S0 + 1), "i"(S0 + 2),
+                   "i"(S0 + 3));
+}
+
+// swap_halves(a0, a2) and swap_halves(a1, a3) behind one pair of wait states
+// (the second swap's sources are older than the first's).
+__device__ __forceinline__ void swap_halves2(float &a0, float &a2, float &a1, float &a3) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3"
+                 : "+v"(a0), "+v"(a2), "+v"(a1), "+v"(a3));
+}
+
 template <int N, int DT>
 struct Geo {
     using T = typename Act<DT>::T;
@@ -743,7 +764,10 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                                 const float dA = fast_exp2(dv[t] * A2[q]);
                                 st[q] = __builtin_fmaf(dA, st[q], row_bcast<(t % TPV) * NL + q>(Bq[t / TPV]) * dx);
                             });
-                            dot_row<NL, (t % TPV) * NL>(yp[t], Cq[t / TPV], st);
+                            if constexpr (kHiLoads)
+                                dot_row_lds<(t % TPV) * NL>(yp[t], Cq[t / TPV], st);
+                            else
+                                dot_row<NL, (t % TPV) * NL>(yp[t], Cq[t / TPV], st);
                         });
                         // Sum the partial readouts over a channel's rows; afterwards
                         // row r holds the finished token NGR*q + (r % NGR) of group q.
@@ -752,8 +776,8 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
 #pragma unroll
                             for (int q = 0; q < GROUP / 4; ++q) {
                                 float a0 = yp[4 * q + 0], a2 = yp[4 * q + 2], a1 = yp[4 * q + 1], a3 = yp[4 * q + 3];
-                                swap_halves(a0, a2);  // rows 0,1: token 0 | rows 2,3: token 2
-                                swap_halves(a1, a3);  // rows 0,1: token 1 | rows 2,3: token 3
+                                // rows 0,1: token 0 | rows 2,3: token 2, and tokens 1 | 3
+                                swap_halves2(a0, a2, a1, a3);
                                 float s02 = a0 + a2, s13 = a1 + a3;
                                 swap_odd_even_rows(s02, s13);
                                 yo[q] = s02 + s13;
