@@ -59,6 +59,8 @@ class Oracle:
         self.lib.oracle_threads.restype = ci
         self.lib.oracle_softplus_bias.argtypes = [i64, i64, _DP, _DP, _DP]
         self.lib.oracle_softplus_bias.restype = ci
+        self.lib.oracle_conv_silu.argtypes = [i64, i64, i64] + [_DP] * 5
+        self.lib.oracle_conv_silu.restype = ci
         self.lib.oracle_scan_trap.argtypes = [i64, i64, i64, i64] + [_DP] * 13 + [ci]
         self.lib.oracle_scan_trap.restype = ci
         self.lib.oracle_step_trap.argtypes = [i64, i64, i64] + [_DP] * 12 + [ci]
@@ -271,6 +273,26 @@ class Oracle:
             raise ValueError("oracle_softplus_bias rejected sizes")
         return out
 
+    def conv_silu64(self, x, w, cb=None, state=None):
+        """The x branch ahead of the scan on float64 arrays: x (batch, L, D), taps
+        w (D, 4) (tap 3 on the token itself), bias cb (D,) or None, and the raw x
+        of the three tokens before token 0, state (batch, D, 3) oldest first, or
+        None (zeros). Returns silu(causal depthwise convolution), (batch, L, D)."""
+        x = _c64(x)
+        batch, L, D = x.shape
+        w = _c64(w)
+        assert w.shape == (D, 4)
+        cb = None if cb is None else _c64(cb)
+        state = None if state is None else _c64(state)
+        if cb is not None:
+            assert cb.shape == (D,)
+        if state is not None:
+            assert state.shape == (batch, D, 3)
+        out = np.empty_like(x)
+        if self.lib.oracle_conv_silu(batch, L, D, _p(x), _p(w), _p(cb), _p(state), _p(out)) != 0:
+            raise ValueError("oracle_conv_silu rejected sizes")
+        return out
+
     # -- stored-dtype entry points -------------------------------------------
     def scan(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
         """Scan on stored inputs (float32 arrays, or bfloat16 bit patterns as uint16).
@@ -293,6 +315,20 @@ class Oracle:
                            up(inp.get("z")),
                            None if inp.get("state_in") is None else upcast(inp["state_in"], "f32"),
                            nthreads=nthreads)
+
+    def scan_conv(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
+        """Scan behind the Mamba block's x branch: inp["x_raw"] (stored dtype)
+        goes through the causal convolution (inp["conv_w"] (D, 4), inp["conv_b"]
+        (D,) or None, float32) and SiLU, with inp["conv_state"] (batch, D, 3,
+        stored dtype) or None before token 0; the step size is given before its
+        activation, as in scan_dt."""
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        up = lambda a: None if a is None else upcast(a, dtype)
+        x64 = self.conv_silu64(upcast(inp["x_raw"], dtype), f32(inp["conv_w"]), f32(inp.get("conv_b")),
+                               up(inp.get("conv_state")))
+        d64 = self.softplus_bias64(upcast(inp["delta_raw"], dtype), f32(inp.get("dt_bias")))
+        return self.scan64(x64, d64, upcast(inp["A"], "f32"), up(inp["Bt"]), up(inp["Ct"]), f32(inp.get("Dskip")),
+                           up(inp.get("z")), f32(inp.get("state_in")), nthreads=nthreads)
 
     def step_dt(self, tok: Dict[str, np.ndarray], A, Dskip, dt_bias, state64: np.ndarray, dtype: str,
                 nthreads: int = 0):

@@ -153,6 +153,40 @@ int oracle_softplus_bias(int64_t rows, int64_t D, const double *raw, const doubl
 }
 
 /*
+ * The x branch of the Mamba block ahead of the scan: a short causal
+ * convolution over the tokens, separately per channel, then SiLU ("Notas
+ * sobre Mamba", section "O bloco Mamba": the projection, a short depthwise
+ * convolution that takes in local context, SiLU, then S6; the Mamba-2 layer
+ * configuration on the SSD production blog post gives its width, d_conv = 4).
+ * Per (b, t, d), with taps w[d, 0..3] (tap 3 on the token itself) and bias
+ * cb[d]:
+ *   u   = cb[d] + sum_{j=0..3} w[d, j] * xr(b, t - 3 + j, d)
+ *   out = u / (1 + exp(-u))                                       SiLU
+ * where xr is x for tokens 0..L-1 and, before token 0, the raw x of the
+ * three tokens before the call (state[b, d, 0..2], oldest first) or zero.
+ * cb and state may be NULL.
+ */
+int oracle_conv_silu(int64_t batch, int64_t L, int64_t D, const double *x, const double *w, const double *cb,
+                     const double *state, double *out)
+{
+    if (batch < 0 || L < 0 || D < 0) return -1;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < D; ++d)
+            for (int64_t t = 0; t < L; ++t) {
+                double u = cb ? cb[d] : 0.0;
+                for (int64_t j = 0; j < 4; ++j) {
+                    int64_t s = t - 3 + j;
+                    double v;
+                    if (s >= 0) v = x[IDX3(b, s, d, L, D)];
+                    else v = state ? state[IDX3(b, d, s + 3, D, 3)] : 0.0;
+                    u += w[d * 4 + j] * v;
+                }
+                out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(-u));
+            }
+    return 0;
+}
+
+/*
  * Gradient of oracle_scan_trap for the loss sum(dy * y) + sum(dstate *
  * state_out), by the chain rule through its recurrence (reverse mode, by
  * hand). With G_t the gradient of h_t (from the readout of token t and from

@@ -337,6 +337,53 @@ def pin_softplus_activation(o):
     assert np.allclose(y1, y2, rtol=1e-13, atol=1e-14) and np.allclose(s1, s2, rtol=1e-13, atol=1e-14)
 
 
+# --- the x branch ahead of the scan (NEXT-1's convolution) ------------------
+def pin_conv_silu(o):
+    """Short causal depthwise convolution (4 taps) and SiLU ahead of the scan
+    ("Notas sobre Mamba", section "O bloco Mamba"; d_conv = 4 in the Mamba-2
+    layer configuration of the SSD production blog post): against numpy's
+    convolution per channel, SiLU through the identity sigmoid(u) = (1 +
+    tanh(u / 2)) / 2 and printed values, causality with a support of exactly
+    4 tokens, and resumption from the raw x of the three tokens before."""
+    silu = lambda u: u * 0.5 * (1.0 + np.tanh(0.5 * u))
+    rng = np.random.default_rng(11)
+    batch, L, D = 2, 13, 5
+    x = rng.normal(size=(batch, L, D))
+    w = rng.uniform(-0.5, 0.5, size=(D, 4))
+    cb = rng.uniform(-0.5, 0.5, size=D)
+    st = rng.normal(size=(batch, D, 3))
+    for state in (None, st):
+        got = o.conv_silu64(x, w, cb, state)
+        for b in range(batch):
+            for d in range(D):
+                head = np.zeros(3) if state is None else state[b, d]
+                xpad = np.concatenate([head, x[b, :, d]])
+                # cross-correlation: tap 3 on the token itself, tap 0 three tokens back
+                u = np.convolve(xpad, w[d, ::-1], mode="valid") + cb[d]
+                assert u.shape == (L,)
+                assert np.allclose(got[b, :, d], silu(u), rtol=1e-14, atol=1e-15), (state is None, b, d)
+    # printed values of silu through the identity tap: silu(1), silu(-1), silu(0)
+    ident = np.zeros((1, 4))
+    ident[0, 3] = 1.0
+    v = o.conv_silu64(np.array([[[1.0], [-1.0], [0.0], [40.0]]]), ident)[0, :, 0]
+    assert abs(v[0] - 0.7310585786300049) <= 2e-16 and abs(v[1] + 0.2689414213699951) <= 2e-16
+    assert v[2] == 0.0 and abs(v[3] - 40.0) < 1e-15
+    # causality and support: a change at token t0 moves outputs t0..t0+3 only
+    base = o.conv_silu64(x, w, cb)
+    t0 = 5
+    x2 = x.copy()
+    x2[:, t0, :] += 1.0
+    moved = o.conv_silu64(x2, w, cb)
+    assert np.array_equal(moved[:, :t0], base[:, :t0]) and np.array_equal(moved[:, t0 + 4:], base[:, t0 + 4:])
+    assert np.all(moved[:, t0:t0 + 4] != base[:, t0:t0 + 4])
+    # resumption: the second part with the last three raw tokens of the first
+    L1 = 7
+    first = o.conv_silu64(x[:, :L1], w, cb, st)
+    second = o.conv_silu64(x[:, L1:], w, cb, np.ascontiguousarray(x[:, L1 - 3:L1].transpose(0, 2, 1)))
+    whole = o.conv_silu64(x, w, cb, st)
+    assert np.array_equal(np.concatenate([first, second], axis=1), whole)
+
+
 # --- the exponential-trapezoidal variant ------------------------------------
 def _trap(o, p, lam, **kw):
     return o.scan_trap64(p["x"], p["delta"], lam, p["A"], p["Bt"], p["Ct"], p.get("Dskip"), p.get("z"),
@@ -713,7 +760,7 @@ def pin_bwd_adjoint_identities(o):
     assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs)), (lhs, rhs)
 
 
-ALL_PINS = [pin_bwd_trap_finite_differences, pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
+ALL_PINS = [pin_conv_silu, pin_bwd_trap_finite_differences, pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
             pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,

@@ -87,6 +87,13 @@ MUTANTS = [
     ("trap_step_prev_uses_current_B", "B_prev[b * N + n] * x_prev[r]", "Bt[b * N + n] * x_prev[r]"),
     ("trap_step_beta_without_alpha", "            double beta = (1.0 - lm) * dt * alpha;\n            double gamma = lm * dt;\n            double vp",
      "            double beta = (1.0 - lm) * dt;\n            double gamma = lm * dt;\n            double vp"),
+    ("conv_taps_reversed", "u += w[d * 4 + j] * v;", "u += w[d * 4 + 3 - j] * v;"),
+    ("conv_three_taps", "for (int64_t j = 0; j < 4; ++j) {\n                    int64_t s", "for (int64_t j = 0; j < 3; ++j) {\n                    int64_t s"),
+    ("conv_state_newest_first", "state[IDX3(b, d, s + 3, D, 3)]", "state[IDX3(b, d, -s - 1, D, 3)]"),
+    ("conv_state_ignored", "else v = state ? state[IDX3(b, d, s + 3, D, 3)] : 0.0;", "else v = 0.0;"),
+    ("conv_drops_bias", "double u = cb ? cb[d] : 0.0;", "double u = 0.0;"),
+    ("conv_silu_sign", "out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(-u));", "out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(u));"),
+    ("conv_without_silu", "out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(-u));", "out[IDX3(b, t, d, L, D)] = u;"),
 ]
 
 

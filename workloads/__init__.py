@@ -26,6 +26,12 @@ as above, x, Bt, Ct ~ N(0, 1), Dskip ~ U(0.5, 1.5), bfloat16 activations.
 For the exponential-trapezoidal rule ("Recorrência trapezoidal"), the weight
 lam = sigmoid(u) with u ~ N(0, 1) per (b, t, d) (the sigmoid of a per-token
 projection), and the token before the first, x_prev and B_prev, ~ N(0, 1).
+For the x branch ahead of the scan ("O bloco Mamba": a short depthwise causal
+convolution of width 4, then SiLU), x_raw is the N(0, 1) draw that x is
+otherwise, and the taps (D, 4) and bias (D,) are U(-0.5, 0.5), float32 (the
+pages give no initialisation; this is PyTorch's default for a depthwise
+Conv1d of width 4, bound 1/sqrt(4)); the raw x of the three tokens before
+token 0 ~ N(0, 1).
 
 Random streams: ``numpy.random.default_rng(SeedSequence(seed, spawn_key=key))``
 with one key per (tensor kind, batch row, token chunk of 65536, block of 64
@@ -59,6 +65,7 @@ _CBLK = 64      # channels per random stream
 # stream keys (tensor kinds)
 _K_DT, _K_DNOISE, _K_X, _K_Z, _K_B, _K_C, _K_D, _K_STATE, _K_LAM, _K_XPREV, _K_BPREV, _K_AH, _K_DY, _K_DSTATE = \
     range(14)
+_K_CONVW, _K_CONVB, _K_CONVSTATE = range(14, 17)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -225,7 +232,7 @@ def _sigmoid(u: np.ndarray) -> np.ndarray:
 
 def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
                 channels: Optional[np.ndarray] = None, raw_delta: bool = False,
-                trap: bool = False) -> Dict[str, np.ndarray]:
+                trap: bool = False, conv: bool = False) -> Dict[str, np.ndarray]:
     """Inputs of `cfg` for tokens [t0, t1) (default: all), in storage dtypes.
 
     `channels` selects a subset of the D channels for x, delta, z, A and Dskip
@@ -242,6 +249,11 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
     the token before t0, x_prev (batch, D) and B_prev (batch, N): token t0 - 1
     of x and Bt when t0 > 0, else draws of their own (the last token of an
     earlier piece of the sequence).
+
+    With conv, also the x branch's inputs: x_raw (the same array as x, taken
+    as the convolution's input), conv_w (D, 4) and conv_b (D,) float32, and
+    conv_state (batch, D, 3) in the storage dtype, the raw x of tokens t0 - 3
+    .. t0 - 1, oldest first (draws of their own before token 0).
     """
     if t1 is None:
         t1 = cfg.L
@@ -287,6 +299,22 @@ def scan_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None,
                 xp[b] = _store(_token_block(cfg.seed, _K_XPREV, b, 0, 1, cfg.D, sel)[0], act)
                 bp[b] = _store(_token_block(cfg.seed, _K_BPREV, b, 0, 1, cfg.N)[0], act)
         out["lam"], out["x_prev"], out["B_prev"] = lam, xp, bp
+    if conv:
+        w = _rng(cfg.seed, _K_CONVW).uniform(-0.5, 0.5, size=(cfg.D, 4))
+        cb = _rng(cfg.seed, _K_CONVB).uniform(-0.5, 0.5, size=cfg.D)
+        cs = np.empty((cfg.batch, len(sel), 3), dtype=x.dtype)
+        for b in range(cfg.batch):
+            before = _token_block(cfg.seed, _K_CONVSTATE, b, 0, 3, cfg.D, sel)  # tokens -3 .. -1
+            for j in range(3):
+                s_tok = t0 - 3 + j
+                if s_tok >= 0:
+                    cs[b, :, j] = _store(_token_block(cfg.seed, _K_X, b, s_tok, s_tok + 1, cfg.D, sel)[0], act)
+                else:
+                    cs[b, :, j] = _store(before[s_tok + 3], act)
+        out["x_raw"] = x
+        out["conv_w"] = np.ascontiguousarray(w[sel].astype(np.float32))
+        out["conv_b"] = np.ascontiguousarray(cb[sel].astype(np.float32))
+        out["conv_state"] = cs
     return out
 
 
