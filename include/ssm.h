@@ -40,6 +40,9 @@
  *  - delta is the step AFTER the softplus (the pages apply softplus to a
  *    projection plus bias before the scan). The *_dt entry points take the
  *    step before it and apply softplus(delta_raw + dt_bias) themselves.
+ *  - x is the scan's input itself; ssm_scan_fwd_conv takes it one step
+ *    earlier, before the short causal convolution and SiLU of the block's x
+ *    branch, and applies both itself.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronise the host. Arguments are checked on the
  *    host before any HIP call; a failed check returns a negative status and
@@ -188,6 +191,50 @@ int ssm_scan_fwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     const void *Bt, const void *Ct, const float *Dskip,
                     const void *z, const float *state_in, float *state_out,
                     void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ssm_scan_fwd_dt behind the x branch of the Mamba block: the scan's x is
+ * SiLU of a short causal convolution of x_raw along the tokens, separately
+ * per channel ("Notas sobre Mamba", section "O bloco Mamba": projection,
+ * short depthwise convolution, SiLU, then S6; the Mamba-2 layer
+ * configuration on "Mamba-2 e State Space Duality (SSD)" gives its width,
+ * 4). Per (b, t, d):
+ *
+ *   u      = conv_b[d] + sum_{j=0..3} conv_w[d,j] * x_raw[b, t-3+j, d]
+ *   x[t]   = u / (1 + exp(-u))                                   (SiLU)
+ *
+ * where a token before token 0 takes its raw x from conv_state. That x feeds
+ * the input term and the D skip; the step size is softplus(delta_raw +
+ * dt_bias) as in ssm_scan_fwd_dt.
+ *
+ *   x_raw         (batch, L, D)  dtype      the convolution's input
+ *   conv_w        (D, 4)         float      taps; conv_w[d,3] multiplies the
+ *                                           token itself, conv_w[d,0] the
+ *                                           token three before it (the
+ *                                           layout of a depthwise Conv1d
+ *                                           weight (D, 1, 4) with left
+ *                                           padding 3)
+ *   conv_b        (D)            float      bias; NULL = zero
+ *   conv_state    (batch, D, 3)  dtype      raw x of the three tokens before
+ *                                           token 0, oldest first (to resume
+ *                                           a sequence cut after an earlier
+ *                                           call: that call's last three
+ *                                           x_raw tokens); NULL = zeros
+ *
+ * Every other argument, the workspace (ssm_scan_workspace_bytes) and the
+ * status codes are those of ssm_scan_fwd_dt; a NULL conv_w with a non-empty
+ * input returns SSM_ERR_NULL. The convolution and SiLU are computed in
+ * float32 once per (token, channel) and, for bfloat16 activations, held as
+ * bfloat16 (round to nearest even) before the scan uses them. The x_raw
+ * tokens the next piece of a sequence needs as conv_state are the caller's
+ * own input; nothing beyond y and state_out is written.
+ */
+int ssm_scan_fwd_conv(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x_raw, const float *conv_w, const float *conv_b, const void *conv_state,
+                      const void *delta_raw, const float *dt_bias, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip,
+                      const void *z, const float *state_in, float *state_out,
+                      void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * ssm_scan_fwd with the exponential-trapezoidal rule of "Notas sobre Mamba",

@@ -13,6 +13,9 @@ Functions (same names as the C ABI):
       library's static workspace, for callers that cannot allocate
   ssm_scan_fwd_dt / ssm_step_dt: the same with delta_raw and dt_bias in place
       of delta; the kernels use softplus(delta_raw + dt_bias) as the step size
+  ssm_scan_fwd_conv(x_raw, conv_w, delta_raw, dt_bias, A, Bt, Ct, conv_b=None,
+                    conv_state=None, ...) -> y: ssm_scan_fwd_dt behind the x
+      branch of the Mamba block (SiLU of a causal width-4 convolution of x_raw)
   ssm_scan_fwd_trap / ssm_step_trap: the exponential-trapezoidal rule, with a
       per-token weight lam and the token before the first (x_prev, B_prev)
   ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None,
@@ -42,6 +45,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
+    "ssm_scan_fwd_conv",
     "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_ssd_step", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error", "ssm_scan_workspace_status", "SSM_ERR_TIMEOUT", "ssm_scan_fwd_noalloc",
@@ -63,7 +67,7 @@ lib_path = os.environ.get("SSM_LIBRARY") or os.path.join(_HERE, "libssm.so")
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step",
-           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc")
+           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_conv")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -102,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_dt.restype = ci
     L.ssm_step_dt.argtypes = [i64, i64, i64, ci] + [vp] * 10 + [vp]
     L.ssm_step_dt.restype = ci
+    L.ssm_scan_fwd_conv.argtypes = [i64, i64, i64, i64, ci] + [vp] * 14 + [vp, sz, vp]
+    L.ssm_scan_fwd_conv.restype = ci
     L.ssm_scan_fwd_trap.argtypes = [i64, i64, i64, i64, ci] + [vp] * 13 + [vp, sz, vp]
     L.ssm_scan_fwd_trap.restype = ci
     L.ssm_step_trap.argtypes = [i64, i64, i64, ci] + [vp] * 12 + [vp]
@@ -210,7 +216,7 @@ def _order_after_alloc(stream, allocated):
 
 
 def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, workspace, stream,
-          lam=None, x_prev=None, B_prev=None):
+          lam=None, x_prev=None, B_prev=None, conv_w=None, conv_b=None, conv_state=None):
     import torch
     if x.dim() != 3 or A.dim() != 2:
         raise ValueError("x must be (batch, L, D) and A (D, N)")
@@ -228,9 +234,15 @@ def _scan(name, x, delta, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y, 
     if own_ws:
         workspace = new_workspace(ws_bytes, x.device)
         allocated.append(workspace)
-    dname = "delta_raw" if name == "ssm_scan_fwd_dt" else "delta"
-    args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, L, D))]
-    if name == "ssm_scan_fwd_dt":
+    raw = name in ("ssm_scan_fwd_dt", "ssm_scan_fwd_conv")
+    dname = "delta_raw" if raw else "delta"
+    if name == "ssm_scan_fwd_conv":
+        args = [_ptr(x, "x_raw", act), _ptr(conv_w, "conv_w", f32, (D, 4)), _ptr(conv_b, "conv_b", f32, (D,)),
+                _ptr(conv_state, "conv_state", act, (batch, D, 3))]
+    else:
+        args = [_ptr(x, "x", act)]
+    args.append(_ptr(delta, dname, act, (batch, L, D)))
+    if raw:
         args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
     trap = name == "ssm_scan_fwd_trap"
     if trap:
@@ -300,6 +312,18 @@ def ssm_scan_fwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, Dskip=None, z=None, state_
     or None (zero)."""
     return _scan("ssm_scan_fwd_dt", x, delta_raw, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y,
                  workspace, stream)
+
+
+def ssm_scan_fwd_conv(x_raw, conv_w, delta_raw, dt_bias, A, Bt, Ct, conv_b=None, conv_state=None, Dskip=None, z=None,
+                      state_in=None, state_out=None, y=None, workspace=None, stream=None):
+    """ssm_scan_fwd_dt behind the x branch of the Mamba block: the kernel's x is
+    SiLU of the causal width-4 convolution of x_raw (batch, L, D) along the
+    tokens, with taps conv_w (D, 4) float32 (tap 3 on the token itself), bias
+    conv_b (D,) float32 or None, and conv_state (batch, D, 3) in the activation
+    dtype, the raw x of the three tokens before token 0 (oldest first), or None
+    (zeros)."""
+    return _scan("ssm_scan_fwd_conv", x_raw, delta_raw, dt_bias, A, Bt, Ct, Dskip, z, state_in, state_out, y,
+                 workspace, stream, conv_w=conv_w, conv_b=conv_b, conv_state=conv_state)
 
 
 def ssm_scan_fwd_trap(x, delta, lam, A, Bt, Ct, Dskip=None, z=None, x_prev=None, B_prev=None, state_in=None,

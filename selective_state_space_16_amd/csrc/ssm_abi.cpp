@@ -110,9 +110,13 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, 
 }
 
 // Extra inputs of the exponential-trapezoidal rule: the per-token weight and
-// the token before the first (both of x_prev and B_prev, or neither).
+// the token before the first (both of x_prev and B_prev, or neither); and of
+// the x branch ahead of the scan: the taps, bias and earlier raw x of its
+// convolution (conv_w NULL: x is used as given).
 struct TrapIn {
     const void *lam = nullptr, *x_prev = nullptr, *B_prev = nullptr;
+    const float *conv_w = nullptr, *conv_b = nullptr;
+    const void *conv_state = nullptr;
 };
 
 static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
@@ -139,7 +143,7 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     }
     if (!x || !delta || !A || !Bt || !Ct || !y) return SSM_ERR_NULL;
     const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state_in, state_out, y, dt_bias, tr.lam, tr.x_prev,
-                          tr.B_prev};
+                          tr.B_prev, tr.conv_w, tr.conv_b, tr.conv_state};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
 
@@ -171,6 +175,9 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.lam = tr.lam;
         a.x_prev = tr.x_prev;
         a.B_prev = tr.B_prev;
+        a.conv_w = tr.conv_w;
+        a.conv_b = tr.conv_b;
+        a.conv_state = tr.conv_state;
         a.y = y;
         a.ntpb = p.ntpb;
         a.ncol = p.ncol;
@@ -201,6 +208,9 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.lam = tr.lam;
     a.x_prev = tr.x_prev;
     a.B_prev = tr.B_prev;
+    a.conv_w = tr.conv_w;
+    a.conv_b = tr.conv_b;
+    a.conv_state = tr.conv_state;
     a.state_out = state_out;
     a.y = y;
     if (twopass_workspace(batch, L, D, N, &a.K, &a.Lc) > 0) {
@@ -260,6 +270,21 @@ int ssm_scan_fwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     void *y, void *workspace, size_t workspace_bytes, void *stream) {
     return scan_fwd(batch, L, D, N, dtype, x, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state_in, state_out, y,
                     workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_conv(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x_raw, const float *conv_w, const float *conv_b, const void *conv_state,
+                      const void *delta_raw, const float *dt_bias, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip,
+                      const void *z, const float *state_in, float *state_out,
+                      void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!conv_w && batch > 0 && L > 0 && D > 0) return SSM_ERR_NULL;
+    TrapIn tr;
+    tr.conv_w = conv_w;
+    tr.conv_b = conv_b;
+    tr.conv_state = conv_state;
+    return scan_fwd(batch, L, D, N, dtype, x_raw, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state_in, state_out,
+                    y, workspace, workspace_bytes, stream, tr);
 }
 
 int ssm_scan_fwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,

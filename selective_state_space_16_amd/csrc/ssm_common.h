@@ -81,4 +81,17 @@ __device__ __forceinline__ float silu(float zv) {
     return zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
 }
 
+// The x branch ahead of the scan for one (token, channel): SiLU of the causal
+// width-4 convolution, bias + w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t,
+// summed in that order ("Notas sobre Mamba", section "O bloco Mamba": a short
+// depthwise convolution, then SiLU, ahead of S6).
+__device__ __forceinline__ float conv_silu(float w0, float w1, float w2, float w3, float bias, float xm3, float xm2,
+                                           float xm1, float x0) {
+    float u = __builtin_fmaf(w0, xm3, bias);
+    u = __builtin_fmaf(w1, xm2, u);
+    u = __builtin_fmaf(w2, xm1, u);
+    u = __builtin_fmaf(w3, x0, u);
+    return silu(u);
+}
+
 }  // namespace ssm

@@ -17,6 +17,13 @@ struct ScanArgs {
     // exponential-trapezoidal rule: per-token weight lam (NULL = the Euler
     // rule) and the token before the first (x_prev, B_prev; NULL = none)
     const void *lam, *x_prev, *B_prev;
+    // the x branch ahead of the scan: x holds the raw input of a causal
+    // depthwise convolution with taps conv_w (D, 4) (tap 3 on the token itself)
+    // and bias conv_b (D; NULL = 0), followed by SiLU; conv_state (batch, D, 3,
+    // activation dtype; NULL = zeros) is the raw x of the three tokens before
+    // token 0. conv_w NULL: x is used as given.
+    const float *conv_w, *conv_b;
+    const void *conv_state;
     float *state_out;
     void *y;
     float *ws_state;   // (batch, K, D, N) chunk end states, then carried-in states
@@ -50,6 +57,9 @@ struct StripeArgs {
     // exponential-trapezoidal rule: per-token weight lam (NULL = the Euler
     // rule) and the token before the first (x_prev, B_prev; NULL = none)
     const void *lam, *x_prev, *B_prev;
+    // the x branch ahead of the scan (as in ScanArgs)
+    const float *conv_w, *conv_b;
+    const void *conv_state;
     float *state_out;
     void *y;
     int64_t ntpb;           // tile columns per batch row
@@ -162,6 +172,9 @@ bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, Stri
 hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s);
 // The instances for a delta given before its activation (called by launch_scan_stripe).
 hipError_t launch_scan_stripe_act(const StripeArgs &a, int N, int dtype, hipStream_t s);
+// The instances for the x branch ahead of the scan, with a delta given before
+// its activation (called by launch_scan_stripe).
+hipError_t launch_scan_stripe_conv(const StripeArgs &a, int N, int dtype, hipStream_t s);
 // The instances for the exponential-trapezoidal rule (called by launch_scan_stripe).
 hipError_t launch_scan_stripe_trap(const StripeArgs &a, int N, int dtype, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, int N, int dtype, hipStream_t s);

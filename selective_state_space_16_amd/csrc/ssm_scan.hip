@@ -26,6 +26,11 @@
 // composition is unchanged (a = exp(delta A)); a chunk's summary includes its
 // first token's term in the input of the token before it, read from memory
 // (or x_prev, B_prev for token 0).
+//
+// With conv_w, x is the raw input of the x branch ahead of the scan ("Notas
+// sobre Mamba", section "O bloco Mamba"): each lane keeps the raw x of the
+// three tokens before the current one and uses SiLU of the causal width-4
+// convolution, rounded to the activation dtype, as x.
 #include "ssm_common.h"
 #include "ssm_internal.h"
 
@@ -96,13 +101,35 @@ __global__ __launch_bounds__(kWave) void scan_chunk_kernel(ScanArgs a) {
         }
     }
 
+    // the x branch: taps, bias and the raw x of the three tokens before t0
+    // (before token 0: conv_state, or zeros)
+    const bool conv = a.conv_w != nullptr;
+    float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbias = 0.0f, xm[3] = {0.0f, 0.0f, 0.0f};
+    if (conv) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cw[j] = a.conv_w[dc * 4 + j];
+        cbias = a.conv_b ? a.conv_b[dc] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int64_t s = t0 - 3 + j;
+            if (s >= 0) xm[j] = ld_act(xp, (b * L + s) * D + dc);
+            else if (a.conv_state) xm[j] = ld_act((const T *)a.conv_state, (b * D + dc) * 3 + (s + 3));
+        }
+    }
     float dsum = 0.0f;
 #pragma unroll 4
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t row = (b * L + t) * D + dc;
         float dt = ld_act(dp, row);
         if (a.delta_softplus) dt = act_round<DT>(softplus(dt + dtb));
-        const float xv = ld_act(xp, row);
+        float xv = ld_act(xp, row);
+        if (conv) {
+            const float raw = xv;
+            xv = act_round<DT>(conv_silu(cw[0], cw[1], cw[2], cw[3], cbias, xm[0], xm[1], xm[2], raw));
+            xm[0] = xm[1];
+            xm[1] = xm[2];
+            xm[2] = raw;
+        }
         float Bv[N];
         ld_row_uniform<N>(Bp, (b * L + t) * N, Bv);
         float dx = dt * xv;

@@ -103,9 +103,21 @@ struct Geo {
     static_assert(ACT_PIECES % 64 == 0, "activation tiles are loaded in whole waves of pieces");
 };
 
+// An LDS array of R rows of C elements that exists only when ON: otherwise
+// an empty member that takes no space, so that the buffers of the modes
+// without it keep their layout.
+template <class E, int R, int C, bool ON>
+struct OptRows {
+    alignas(16) E v[R][C];
+};
+template <class E, int R, int C>
+struct OptRows<E, R, C, false> {};
+
 // TRAP: the exponential-trapezoidal rule, which also needs the weight lam of
-// each token and the delta and lam of the token after the tile.
-template <int N, int DT, bool TRAP = false>
+// each token and the delta and lam of the token after the tile. CONV: the x
+// branch ahead of the scan; x holds the raw input and xc the tile's x after
+// the convolution and SiLU, which the scan reads.
+template <int N, int DT, bool TRAP = false, bool CONV = false>
 struct TileBuf {
     using G = Geo<N, DT>;
     using T = typename G::T;
@@ -119,18 +131,21 @@ struct TileBuf {
     alignas(16) T B[G::BC_SLOTS * G::VEC];  // Bt rows of the tile's tokens (padded to whole waves of pieces)
     alignas(16) T C[G::BC_SLOTS * G::VEC];
     alignas(16) T lam[TRAP ? G::TT + 1 : 1][TRAP ? G::TCH : G::VEC];  // TRAP: rows as dl (else a stub)
+    [[no_unique_address]] OptRows<T, G::TT, G::TCH, CONV> xc;  // CONV: rows as x
 };
 
-template <int N, int DT, bool TRAP = false>
+template <int N, int DT, bool TRAP = false, bool CONV = false>
 struct Shared {
-    TileBuf<N, DT, TRAP> buf[2];
+    TileBuf<N, DT, TRAP, CONV> buf[2];
     float cb[TRAP ? Geo<N, DT>::TT : 1];  // TRAP, pass 2: sum_n Ct[t,n] Bt[t,n] per token of the current tile
+    // CONV: the taps (rows 0..3) and the bias (row 4) of the unit's channels
+    [[no_unique_address]] OptRows<float, 5, Geo<N, DT>::TCH, CONV> cw;
     int unit;      // the unit handed to this workgroup
     uint32_t tag;  // this call's tag (see kHdrEpoch)
 };
 
-template <int N, int DT, bool TRAP>
-constexpr int stripe_min_blocks() { return 2 * sizeof(Shared<N, DT, TRAP>) <= 160 * 1024 ? 2 : 1; }
+template <int N, int DT, bool TRAP, bool CONV = false>
+constexpr int stripe_min_blocks() { return 2 * sizeof(Shared<N, DT, TRAP, CONV>) <= 160 * 1024 ? 2 : 1; }
 
 // An activation element of an LDS tile row, widened to float. A bfloat16 is
 // read as the 32-bit word holding it and its neighbour, and moved into the
@@ -303,8 +318,8 @@ __device__ __forceinline__ uint32_t take_unit(uint32_t *ctr) {
 }
 
 // The per-piece path of load_tile_w, with addresses clamped into the sequence.
-template <int N, int DT, int NACT, int NBC, bool HAS_Z, bool TRAP>
-__device__ __forceinline__ void load_tile_clamped(TileBuf<N, DT, TRAP> &tb, const StripeArgs &a, int64_t b,
+template <int N, int DT, int NACT, int NBC, bool HAS_Z, bool TRAP, class TB>
+__device__ __forceinline__ void load_tile_clamped(TB &tb, const StripeArgs &a, int64_t b,
                                                   int64_t ch0, int64_t tt0, int w, int lane) {
     using G = Geo<N, DT>;
     using T = typename G::T;
@@ -347,15 +362,14 @@ __device__ __forceinline__ void load_tile_clamped(TileBuf<N, DT, TRAP> &tb, cons
 // from the last whole piece of the row and never stored. TRAP adds lam, and
 // the delta (wave 1) and lam (wave 2) row of the token after the tile, read
 // from the last token when there is none.
-template <int N, int DT, bool GATE, int PASS, int WV, bool TRAP>
-__device__ __forceinline__ void load_tile_w(TileBuf<N, DT, TRAP> &tb, const StripeArgs &a, int64_t b, int64_t ch0,
+template <int N, int DT, bool GATE, int PASS, int WV, bool TRAP, class TB>
+__device__ __forceinline__ void load_tile_w(TB &tb, const StripeArgs &a, int64_t b, int64_t ch0,
                                             int64_t tt0, int lane, uint32_t act_off) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     constexpr bool HAS_Z = PASS == 2 && GATE;
     constexpr int NACT = 2 + (HAS_Z ? 1 : 0) + (TRAP ? 1 : 0);  // x, delta, [z], [lam]
     constexpr int NBC = PASS == 2 ? 2 : 1;
-    using TB = TileBuf<N, DT, TRAP>;
     const int64_t D = a.D, L = a.L;
     if (tt0 + G::TT <= L) {
         const uint32_t rowb = (uint32_t)(D * G::ESZ);
@@ -399,8 +413,8 @@ __device__ __forceinline__ void load_tile_w(TileBuf<N, DT, TRAP> &tb, const Stri
     }
 }
 
-template <int N, int DT, bool GATE, int PASS, bool TRAP>
-__device__ __forceinline__ void load_tile(TileBuf<N, DT, TRAP> &tb, const StripeArgs &a, int64_t b, int64_t ch0,
+template <int N, int DT, bool GATE, int PASS, bool TRAP, class TB>
+__device__ __forceinline__ void load_tile(TB &tb, const StripeArgs &a, int64_t b, int64_t ch0,
                                           int64_t tt0, int w, int lane, uint32_t act_off) {
     if (w == 1) load_tile_w<N, DT, GATE, PASS, 1, TRAP>(tb, a, b, ch0, tt0, lane, act_off);
     else if (w == 2) load_tile_w<N, DT, GATE, PASS, 2, TRAP>(tb, a, b, ch0, tt0, lane, act_off);
@@ -413,8 +427,8 @@ __device__ __forceinline__ void load_tile(TileBuf<N, DT, TRAP> &tb, const Stripe
 // (token, channel) is activated once. A thread's pieces all sit in the same
 // piece column (256 is a multiple of the pieces per row), so `dtb` holds the
 // bias of its VEC channels.
-template <int N, int DT>
-__device__ __forceinline__ void activate_delta(TileBuf<N, DT> &tb, const float (&dtb)[Geo<N, DT>::VEC]) {
+template <int N, int DT, class TB>
+__device__ __forceinline__ void activate_delta(TB &tb, const float (&dtb)[Geo<N, DT>::VEC]) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     using VT = uint32_t __attribute__((ext_vector_type(4)));
@@ -434,6 +448,61 @@ __device__ __forceinline__ void activate_delta(TileBuf<N, DT> &tb, const float (
         }
         __builtin_memcpy(&v, e, sizeof(v));
         *(VT *)__builtin_assume_aligned(p, 16) = v;
+    }
+}
+
+// The x branch ahead of the scan, once a tile has landed: xc = SiLU of the
+// causal width-4 convolution of the raw x rows, per channel. A thread takes
+// one 16-byte piece column (VEC channels) over RPT consecutive rows and reads
+// the three rows before them too; rows before the tile are the last three
+// raw rows of `prev`, the other buffer, which holds the previous tile (its
+// next load is issued only after the barrier that follows this) or, for the
+// first tile of a pass, the raw x of the three tokens before the stripe
+// (stage_halo). Writes go to xc only, so no thread overwrites a row another
+// still reads. `cw` holds the taps and bias of the tile column's channels.
+template <int N, int DT, class TB>
+__device__ __forceinline__ void conv_tile(TB &tb, const TB &prev, const float (&cw)[5][Geo<N, DT>::TCH]) {
+    using G = Geo<N, DT>;
+    using T = typename G::T;
+    using HT = uint32_t __attribute__((ext_vector_type(2)));  // half a piece
+    constexpr int VEC = G::VEC, HV = VEC / 2, PPR = G::PPR, TT = G::TT;
+    constexpr int RPT = G::ACT_PIECES / (64 * kWaves);  // rows per thread
+    static_assert(G::ACT_PIECES % (64 * kWaves) == 0 && (64 * kWaves) % PPR == 0, "whole rows per thread");
+    const int pc = threadIdx.x % PPR, r0 = (threadIdx.x / PPR) * RPT;
+    // the two halves of the piece one after the other, which halves the
+    // registers the raw rows and the taps hold at once
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int c0 = pc * VEC + hh * HV;
+        float raw[RPT + 3][HV], w[5][HV];
+#pragma unroll
+        for (int k = 0; k < RPT + 3; ++k) {
+            const int r = r0 - 3 + k;
+            const T *src = r >= 0 ? &tb.x[r][c0] : &prev.x[TT + r][c0];
+            const HT v = *(const HT *)__builtin_assume_aligned(src, 8);
+            T e[HV];
+            __builtin_memcpy(e, &v, sizeof(v));
+#pragma unroll
+            for (int q = 0; q < HV; ++q) raw[k][q] = ld_act(e, q);
+        }
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+#pragma unroll
+            for (int q = 0; q < HV; ++q) w[j][q] = cw[j][c0 + q];
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            T e[HV];
+#pragma unroll
+            for (int q = 0; q < HV; ++q) {
+                const float f = conv_silu(w[0][q], w[1][q], w[2][q], w[3][q], w[4][q], raw[k][q], raw[k + 1][q],
+                                          raw[k + 2][q], raw[k + 3][q]);
+                if constexpr (DT == 0) e[q] = f;
+                else e[q] = __builtin_bit_cast(uint16_t, (__bf16)f);
+            }
+            HT v;
+            __builtin_memcpy(&v, e, sizeof(v));
+            *(HT *)__builtin_assume_aligned(&tb.xc.v[r0 + k][c0], 8) = v;
+        }
     }
 }
 
@@ -463,19 +532,23 @@ __device__ __forceinline__ void publish_state(uint64_t *rec, int l, const float 
 //      y_t = C_t . k_t - mu_{t+1} x_t (C_t . B_t) + D x_t   (before the gate),
 //    k starts from h_in + mu_0 v_{-1}, and mu_L = 0 (no token after the call)
 //    makes the final k the final h.
-enum ScanMode { kEuler = 0, kSoftplus = 1, kTrap = 2 };
+//  kConv: as kSoftplus, and x holds the raw input of the x branch ahead of
+//    the scan ("Notas sobre Mamba", section "O bloco Mamba"): the scan uses
+//    SiLU of its causal width-4 convolution per channel (conv_tile), rounded
+//    to the activation dtype, in both passes and in the D skip.
+enum ScanMode { kEuler = 0, kSoftplus = 1, kTrap = 2, kConv = 3 };
 
 template <int N, int DT, bool GATE, bool SKIP, int MODE>
-__global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTrap>())) void scan_stripe_kernel(
+__global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTrap, MODE == kConv>())) void scan_stripe_kernel(
     StripeArgs a) {
     using G = Geo<N, DT>;
     using T = typename G::T;
     constexpr int NL = G::NL, NGR = G::NGR, CPW = G::CPW, TCH = G::TCH, TPV = G::TPV, BREGS = G::BREGS;
     constexpr int TT = G::TT, GROUP = G::GROUP;
-    constexpr bool SP = MODE == kSoftplus, TRAP = MODE == kTrap;
-    using TBT = TileBuf<N, DT, TRAP>;
+    constexpr bool CONV = MODE == kConv, SP = MODE == kSoftplus || CONV, TRAP = MODE == kTrap;
+    using TBT = TileBuf<N, DT, TRAP, CONV>;
 
-    __shared__ Shared<N, DT, TRAP> sh;
+    __shared__ Shared<N, DT, TRAP, CONV> sh;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
     const int l = threadIdx.x & 63;
@@ -540,6 +613,15 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
 #pragma unroll
         for (int k = 0; k < G::VEC; ++k) dtb[k] = (SP && a.dt_bias) ? a.dt_bias[lane_ch + k] : 0.0f;
         const int64_t dc = valid ? d : D - 1;
+        if constexpr (CONV) {
+            // taps and bias of the tile column's channels (past D: the last
+            // channel's; those results are never stored)
+            for (int q = threadIdx.x; q < 5 * TCH; q += 64 * kWaves) {
+                const int jj = q / TCH, c = q % TCH;
+                const int64_t ch = ch0 + c < D ? ch0 + c : D - 1;
+                sh.cw.v[jj][c] = jj < 4 ? a.conv_w[ch * 4 + jj] : (a.conv_b ? a.conv_b[ch] : 0.0f);
+            }
+        }
         const int64_t t0 = j * SL;
         const int64_t t1 = t0 + SL < L ? t0 + SL : L;
         const int ntiles = (int)((t1 - t0 + TT - 1) / TT);
@@ -620,6 +702,21 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             for (int q = 0; q < BREGS; ++q) Bq[q] = Cq[q] = 0.0f;
 #pragma unroll
             for (int q = 0; q < G::OWN; ++q) xo[q] = zo[q] = 0.0f;
+            if constexpr (CONV) {
+                // the raw x of the three tokens before the stripe, as the last
+                // rows of the buffer the first tile's convolution takes as the
+                // previous one (before token 0: conv_state, or zeros); the
+                // prefetch fills the other buffer
+                for (int q = threadIdx.x; q < 3 * TCH; q += 64 * kWaves) {
+                    const int jj = q / TCH, c = q % TCH;
+                    const int64_t ch = ch0 + c < D ? ch0 + c : D - 1;
+                    const int64_t t = t0 - 3 + jj;
+                    T v = T(0);
+                    if (t >= 0) v = ((const T *)a.x)[(b * L + t) * D + ch];
+                    else if (a.conv_state) v = ((const T *)a.conv_state)[(b * D + ch) * 3 + (t + 3)];
+                    sh.buf[1].x[TT - 3 + jj][c] = v;
+                }
+            }
             if (w > 0) vm_wait();  // the first tile (prefetch) has landed
             lds_barrier();
             for (int i = 0; i < ntiles; ++i) {
@@ -630,7 +727,8 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                     // complete behind this tile's scan; its buffer is loaded next
                     if (i > 0) store_y(sh.buf[(i - 1) & 1], i - 1);
                 }
-                if constexpr (SP) activate_delta(tb, dtb);  // this tile has landed for every wave
+                if constexpr (SP) activate_delta<N, DT>(tb, dtb);  // this tile has landed for every wave
+                if constexpr (CONV) conv_tile<N, DT>(tb, sh.buf[(i + 1) & 1], sh.cw.v);
                 if constexpr (TRAP && PASS == 2) tile_cb(tb);
                 if (SP || (PASS == 2 && (TRAP || i > 0))) lds_barrier();
                 if (w > 0 && i + 1 < ntiles)
@@ -662,10 +760,16 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                 constexpr int ROWB = TCH * G::ESZ, BCB = N * G::ESZ;
                 constexpr int OFF_DL = offsetof(TB, dl), OFF_Z = offsetof(TB, z), OFF_LAM = offsetof(TB, lam);
                 constexpr int OFF_B = offsetof(TB, B), OFF_C = offsetof(TB, C);
+                constexpr int OFF_X = CONV ? offsetof(TB, xc) : offsetof(TB, x);  // the x the scan reads
                 const uint32_t a_ch = lds_addr(&tb) + cl * G::ESZ;
                 const uint32_t a_bc = lds_addr(&tb) + OFF_B + ((k16 / NL) * N + nstate0 + (k16 % NL)) * G::ESZ;
                 const uint32_t a_own = a_ch + g * ROWB;
                 const uint32_t a_cb = lds_addr(&sh.cb[0]) + g * 4;  // TRAP: C . B of the lane's first finished token
+                // row r of the x the scan reads (generic loads)
+                [[maybe_unused]] auto xrow = [&](int r) -> const T * {
+                    if constexpr (CONV) return &tb.xc.v[r][0];
+                    else return &tb.x[r][0];
+                };
                 static_for<0, TT / GROUP>([&](auto gc) {
                     constexpr int tg = decltype(gc)::value * GROUP;
                     // Keep the groups in order: the previous group's state
@@ -678,9 +782,9 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                     if constexpr (kHiLoads) {
                         // bfloat16: loads into the high halves of the registers
                         // that held the previous group's values, one wait per group
-                        constexpr int OX = tg * ROWB, OD = OFF_DL + tg * ROWB, OL = OFF_LAM + tg * ROWB;
+                        constexpr int OX = OFF_X + tg * ROWB, OD = OFF_DL + tg * ROWB, OL = OFF_LAM + tg * ROWB;
                         constexpr int SB = TPV * BCB, OB = tg * BCB, OC = OFF_C - OFF_B + tg * BCB;
-                        constexpr int SO = NGR * ROWB, OXO = tg * ROWB, OZO = OFF_Z + tg * ROWB;
+                        constexpr int SO = NGR * ROWB, OXO = OFF_X + tg * ROWB, OZO = OFF_Z + tg * ROWB;
                         if constexpr (TRAP && PASS == 2)
                             lds_bf16_t2<ROWB, OX, OD, OL, SB, OB, OC, SO, OXO, OZO, OFF_DL + (tg + 1) * ROWB,
                                         OFF_LAM + (tg + 1) * ROWB, NGR * 4, tg * 4>(
@@ -695,7 +799,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                     } else {
 #pragma unroll
                         for (int t = 0; t < GROUP; ++t) {
-                            xv[t] = lds_act(&tb.x[tg + t][0], cl, sel_ch);
+                            xv[t] = lds_act(xrow(tg + t), cl, sel_ch);
                             dv[t] = lds_act(&tb.dl[tg + t][0], cl, sel_ch);
                             if constexpr (TRAP) lv[t] = lds_act(&tb.lam[tg + t][0], cl, sel_ch);
                         }
@@ -714,7 +818,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
 #pragma unroll
                             for (int q = 0; q < G::OWN; ++q) {
                                 const int tw = tg + NGR * q + g;
-                                xo[q] = (SKIP || TRAP) ? lds_act(&tb.x[tw][0], cl, sel_ch) : 0.0f;
+                                xo[q] = (SKIP || TRAP) ? lds_act(xrow(tw), cl, sel_ch) : 0.0f;
                                 zo[q] = GATE ? lds_act(&tb.z[tw][0], cl, sel_ch) : 0.0f;
                                 if constexpr (TRAP) {
                                     dno[q] = lds_act(&tb.dl[tw + 1][0], cl, sel_ch);

@@ -186,6 +186,30 @@ def test_dt_entry_points_empty_ok_without_gpu():
     assert step_dt(batch=0) == 0 and step_dt(D=0) == 0
 
 
+def scan_conv(**kw):
+    a = dict(batch=1, L=8, D=64, N=16, dtype=0, x_raw=P, conv_w=P, conv_b=None, conv_state=None, delta_raw=P,
+             dt_bias=None, A=P, Bt=P, Ct=P, Dskip=None, z=None, state_in=None, state_out=None, y=P, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_fwd_conv(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x_raw"], a["conv_w"],
+                                       a["conv_b"], a["conv_state"], a["delta_raw"], a["dt_bias"], a["A"], a["Bt"],
+                                       a["Ct"], a["Dskip"], a["z"], a["state_in"], a["state_out"], a["y"], a["ws"],
+                                       a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=3), -4), (dict(conv_w=None), -1), (dict(x_raw=None), -1),
+    (dict(delta_raw=None), -1), (dict(y=None), -1), (dict(conv_w=MIS), -5), (dict(conv_b=MIS), -5),
+    (dict(conv_state=MIS), -5), (dict(x_raw=MIS), -5), (dict(L=1 << 20, D=64), -6),
+])
+def test_scan_conv_rejects(kw, code):
+    assert scan_conv(**kw) == code
+
+
+def test_conv_entry_point_empty_ok_without_gpu():
+    assert scan_conv(batch=0) == 0 and scan_conv(D=0) == 0 and scan_conv(conv_w=None, L=0) == 0
+
+
 def scan_trap(**kw):
     a = dict(batch=1, L=8, D=64, N=16, dtype=0, x=P, delta=P, lam=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
              x_prev=None, B_prev=None, state_in=None, state_out=None, y=P, ws=None, wsb=0, stream=None)

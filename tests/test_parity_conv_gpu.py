@@ -1,0 +1,154 @@
+"""ssm_scan_fwd_conv (the scan behind the Mamba block's x branch: SiLU of a
+causal width-4 convolution of x_raw per channel, with the step size given
+before its activation) against the fp64 oracle's convolution, activation and
+scan (needs MI355X). Shapes cover the LDS-tiled scan (the convolution runs on
+each landed tile, with the previous tile's raw rows as its halo), the fallback
+scan (a per-lane window), ragged lengths and channel counts, cut columns
+(stripes whose halo comes from the tokens before them), resumption from the
+raw x of an earlier piece, and the optional parts."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_16_amd as ssm
+import workloads as W
+from gpu_util import check, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(name, batch, L, D, N=16, dtype="f32", gate=True, dskip="uniform", state_in=None, seed=91):
+    return W.ScanConfig(name, batch, L, D, N, dtype, gate=gate, dskip=dskip, state_in=state_in, seed=seed)
+
+
+def gpu_scan_conv(inp, state_out=True):
+    """ssm_scan_fwd_conv on stored inputs; returns (y64, state64 or None)."""
+    import torch
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    batch, L, D = dev["x_raw"].shape
+    N = dev["A"].shape[1]
+    st = torch.empty((batch, D, N), dtype=torch.float32, device="cuda") if state_out else None
+    ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(batch, L, D, N,
+                                                        0 if dev["x_raw"].dtype == torch.float32 else 1))
+    y = ssm.ssm_scan_fwd_conv(dev["x_raw"], dev["conv_w"], dev["delta_raw"], dev.get("dt_bias"), dev["A"], dev["Bt"],
+                              dev["Ct"], conv_b=dev.get("conv_b"), conv_state=dev.get("conv_state"),
+                              Dskip=dev.get("Dskip"), z=dev.get("z"), state_in=dev.get("state_in"), state_out=st,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0, "a look-back wait gave up"
+    return to_f64(y), None if st is None else to_f64(st)
+
+
+def _inputs(cfg, t0=0, t1=None, conv_state=True, conv_b=True):
+    inp = W.scan_inputs(cfg, t0, t1, raw_delta=True, conv=True)
+    if not conv_state:
+        inp["conv_state"] = None
+    if not conv_b:
+        inp["conv_b"] = None
+    return inp
+
+
+def _run(cfg, **kw):
+    say(f"case {cfg} {kw}")
+    inp = _inputs(cfg, **kw)
+    y, st = gpu_scan_conv(inp)
+    yr, sr = oracle.get().scan_conv(inp, cfg.dtype)
+    check(y, yr, cfg.dtype, "y")
+    check(st, sr, cfg.dtype, "state_out")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [96, 200])
+def test_scan_conv_tiled(dtype, D):
+    _run(_cfg(f"conv_{D}", 2, 777, D, 16, dtype, state_in=0.3))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_conv_no_state_no_bias(dtype):
+    """conv_state NULL (zeros before token 0) and conv_b NULL (zero bias)."""
+    _run(_cfg("conv_bare", 2, 300, 64, 16, dtype, state_in=0.2), conv_state=False, conv_b=False)
+
+
+@pytest.mark.parametrize("D,dtype", [(63, "f32"), (100, "bf16"), (130, "bf16")])
+def test_scan_conv_fallback_shapes(D, dtype):
+    """Channel counts that are not whole 16-byte pieces take the fallback scan."""
+    _run(_cfg(f"conv_fb{D}", 2, 500, D, 16, dtype, state_in=0.3))
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_conv_state_sizes(N, dtype):
+    _run(_cfg(f"conv_N{N}", 2, 333, 128, N, dtype, state_in=0.5))
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 65, 4097])
+def test_scan_conv_ragged_lengths_bf16(L):
+    """Lengths shorter than the window, one past a tile, and a ragged tail."""
+    _run(_cfg(f"conv_L{L}", 1, L, 96, 16, "bf16", state_in=0.3))
+
+
+@pytest.mark.parametrize("gate,dskip", [(False, "uniform"), (True, "none"), (False, "none")])
+def test_scan_conv_optional_parts(gate, dskip):
+    _run(_cfg("conv_opt", 2, 400, 128, 16, "bf16", gate=gate, dskip=dskip, state_in=0.2))
+
+
+def test_scan_conv_cut_columns_bf16():
+    """Few channel columns and a long sequence: every column is cut into
+    stripes, and each stripe's first tile takes its halo from the three tokens
+    before the stripe, in both passes."""
+    _run(_cfg("conv_c3twin", 1, 131072, 128, 16, "bf16", state_in=0.1, seed=3))
+
+
+def test_scan_conv_c1_layer_f32():
+    _run(W.SCAN_CONFIGS["c1"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_conv_fallback_chunks(dtype, monkeypatch):
+    """The fallback scan cut into chunks: each chunk starts its window from the
+    three tokens before it."""
+    monkeypatch.setenv("SSM_SCAN_IMPL", "twopass")
+    _run(_cfg("conv_twopass", 2, 3000, 128, 16, dtype, state_in=0.3))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_conv_resume(dtype):
+    """Two calls, the second given the first's final state and its last three
+    raw tokens as conv_state, match the oracle over the whole sequence."""
+    cfg = _cfg("conv_resume", 2, 1500, 128, 16, dtype, state_in=0.3)
+    say(f"case {cfg} resume at 700")
+    whole = _inputs(cfg)
+    first = _inputs(cfg, 0, 700)
+    y1, s1 = gpu_scan_conv(first)
+    second = _inputs(cfg, 700, 1500)
+    assert np.array_equal(second["conv_state"], np.ascontiguousarray(first["x_raw"][:, -3:].transpose(0, 2, 1)))
+    second["state_in"] = s1.astype(np.float32)
+    y2, s2 = gpu_scan_conv(second)
+    yr, sr = oracle.get().scan_conv(whole, dtype)
+    check(np.concatenate([y1, y2], axis=1), yr, dtype, "y")
+    check(s2, sr, dtype, "state_out")
+
+
+def test_scan_conv_deterministic():
+    """Two calls on the same inputs give the same bits."""
+    cfg = _cfg("conv_det", 1, 20000, 128, 16, "bf16", state_in=0.1)
+    inp = _inputs(cfg)
+    ya, sa = gpu_scan_conv(inp)
+    yb, sb = gpu_scan_conv(inp)
+    assert np.array_equal(ya, yb) and np.array_equal(sa, sb)
+
+
+def test_scan_conv_stripe_and_fallback_agree():
+    """The tiled scan and the fallback round the convolved x the same way: on
+    float32 inputs they agree to float32 rounding of the recurrence."""
+    cfg = _cfg("conv_paths", 1, 600, 128, 16, "f32", state_in=0.3)
+    inp = _inputs(cfg)
+    y1, s1 = gpu_scan_conv(inp)
+    os.environ["SSM_SCAN_IMPL"] = "twopass"
+    try:
+        y2, s2 = gpu_scan_conv(inp)
+    finally:
+        del os.environ["SSM_SCAN_IMPL"]
+    assert np.allclose(y1, y2, rtol=1e-5, atol=1e-5) and np.allclose(s1, s2, rtol=1e-5, atol=1e-5)
