@@ -66,7 +66,8 @@ PAGE_CLAIMS = {
 
 # The sources each measured kernel is built from (besides the shared headers).
 KERNEL_SOURCES = {
-    "scan": ("ssm_scan_stripe_kernel.h", "ssm_scan_stripe.hip", "ssm_scan_stripe_act.hip", "ssm_scan_stripe_trap.hip"),
+    "scan": ("ssm_scan_stripe_kernel.h", "ssm_scan_stripe.hip", "ssm_scan_stripe_act.hip", "ssm_scan_stripe_trap.hip",
+             "ssm_scan_stripe_conv.hip"),
     "step": ("ssm_step.hip",),
     "ssd": ("ssm_ssd.hip",),
     "ssd_step": ("ssm_ssd_step.hip",),
@@ -146,6 +147,10 @@ def device_blocks(dev, y, st_out, order, chans):
                "z": part("z"), "Bt": bt, "Ct": ct, "A": to_host(dev["A"][sl]),
                "Dskip": None if dev.get("Dskip") is None else to_host(dev["Dskip"][sl]),
                "dt_bias": None if dev.get("dt_bias") is None else to_host(dev["dt_bias"][sl]),
+               "x_raw": part("x") if dev.get("conv_w") is not None else None,
+               "conv_w": None if dev.get("conv_w") is None else to_host(dev["conv_w"][sl]),
+               "conv_b": None if dev.get("conv_b") is None else to_host(dev["conv_b"][sl]),
+               "conv_state": None if dev.get("conv_state") is None else to_host(dev["conv_state"][0:1, sl]),
                "x_prev": None if dev.get("x_prev") is None else to_host(dev["x_prev"][0:1, sl]),
                "B_prev": None if dev.get("B_prev") is None else to_host(dev["B_prev"][0:1]),
                "state_in": None if dev.get("state_in") is None else to_host(dev["state_in"][0:1, sl])}
@@ -254,15 +259,19 @@ def bench_scan(args, name):
     log(f"[bench] workload {cfg}")
     t0 = time.time()
     # set 0: the seeded numpy streams (checked against the oracle below)
-    sp = args.softplus  # delta handed over before its activation
+    cv = args.conv  # x before the block's short convolution and SiLU (ssm_scan_fwd_conv)
+    sp = args.softplus or cv  # delta handed over before its activation
     tr = args.trap  # exponential-trapezoidal rule
     bw = args.backward  # the gradient (ssm_scan_bwd) in place of the forward scan
-    inp = W.scan_inputs(cfg, raw_delta=sp, trap=tr) if name != "c3" else None
+    inp = W.scan_inputs(cfg, raw_delta=sp, trap=tr, conv=cv) if name != "c3" else None
     grads = W.grad_inputs(cfg) if (bw and inp is not None) else None
     log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
-    whole = W.scan_inputs(cfg, 0, 0)
+    whole = W.scan_inputs(cfg, 0, 0, conv=cv)
     A, Dskip = to_dev(whole["A"]), to_dev(whole["Dskip"])
     st_in = to_dev(whole["state_in"])
+    # the convolution's taps, bias and earlier raw tokens (per channel: shared by every set)
+    cw, cb, cs = (to_dev(whole["conv_w"]), to_dev(whole["conv_b"]), to_dev(whole["conv_state"])) if cv else \
+        (None, None, None)
     sets = []
     if inp is not None:
         keys = ("x", "delta_raw", "dt_bias", "z", "Bt", "Ct") if sp else ("x", "delta", "z", "Bt", "Ct")
@@ -319,6 +328,10 @@ def bench_scan(args, name):
         elif bw:
             ssm.ssm_scan_bwd(s["x"], s["delta"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip, z=s["z"],
                              state_in=st_in, dstate=dstate, out=ys[i % len(sets)], workspace=bws, stream=stream)
+        elif cv:
+            ssm.ssm_scan_fwd_conv(s["x"], cw, s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], conv_b=cb,
+                                  conv_state=cs, Dskip=Dskip, z=s["z"], state_in=st_in, state_out=st_out,
+                                  y=ys[i % len(sets)], workspace=ws, stream=stream)
         elif sp:
             ssm.ssm_scan_fwd_dt(s["x"], s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], Dskip=Dskip, z=s["z"],
                                 state_in=st_in, state_out=st_out, y=ys[i % len(sets)], workspace=ws, stream=stream)
@@ -338,7 +351,8 @@ def bench_scan(args, name):
         f"over {len(sets)} rotating sets")
     out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems,
            "bytes": W.scan_bytes(cfg, st_out is not None) + (cfg.D * 4 if sp else 0) +
-                    (W.trap_extra_bytes(cfg) if tr else 0), "dtype": cfg.dtype,
+                    (W.trap_extra_bytes(cfg) if tr else 0) +
+                    (cfg.D * 5 * 4 + cfg.batch * cfg.D * 3 * W._esize(cfg.dtype) if cv else 0), "dtype": cfg.dtype,
            "parity": None, "cpu": None}
     if bw:
         out["bytes"] = W.scan_bwd_bytes(cfg) + (2 * cfg.D * 4 if sp else 0)  # dt_bias read, ddt_bias written
@@ -377,11 +391,11 @@ def bench_scan(args, name):
         torch.cuda.synchronize()
         step(0)
         torch.cuda.synchronize()
-        dev = dict(sets[0], A=A, Dskip=Dskip, state_in=st_in)
+        dev = dict(sets[0], A=A, Dskip=Dskip, state_in=st_in, conv_w=cw, conv_b=cb, conv_state=cs)
         nblk = (cfg.D + 63) // 64
         stride = next(k for k in (7, 5, 3, 1) if np.gcd(k, nblk) == 1)
         order = [(k * stride) % nblk for k in range(nblk)]
-        rule = "scan_dt" if sp else "scan_trap" if tr else "scan"
+        rule = "scan_conv" if cv else "scan_dt" if sp else "scan_trap" if tr else "scan"
 
         def bounded():
             spent = 0.0
@@ -415,7 +429,8 @@ def bench_scan(args, name):
         reps, tot, yr = 0, 0.0, None
         while reps == 0 or tot < args.cpu_seconds:
             t = time.perf_counter()
-            yr, _ = o.scan_dt(inp, cfg.dtype) if sp else o.scan_trap(inp, cfg.dtype) if tr else o.scan(inp, cfg.dtype)
+            yr, _ = o.scan_conv(inp, cfg.dtype) if cv else o.scan_dt(inp, cfg.dtype) if sp else \
+                o.scan_trap(inp, cfg.dtype) if tr else o.scan(inp, cfg.dtype)
             tot += time.perf_counter() - t
             reps += 1
         rel, mx = rel_l2(y0, yr)
@@ -682,6 +697,9 @@ def main():
                     help="hand delta over before its activation (ssm_scan_fwd_dt / ssm_step_dt)")
     ap.add_argument("--trap", action="store_true",
                     help="the exponential-trapezoidal rule (ssm_scan_fwd_trap / ssm_step_trap)")
+    ap.add_argument("--conv", action="store_true",
+                    help="x before the Mamba block's short convolution and SiLU, delta before its activation "
+                         "(ssm_scan_fwd_conv)")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradient of the scan (ssm_scan_bwd) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -689,8 +707,10 @@ def main():
     ap.add_argument("--valu-calibration", action="store_true",
                     help="only measure the VALU issue rates of exp, fma and the scan's mix")
     args = ap.parse_args()
-    if args.softplus and args.trap:
-        ap.error("--softplus and --trap select different entry points; give one")
+    if sum((args.softplus, args.trap, args.conv)) > 1:
+        ap.error("--softplus, --trap and --conv select different entry points; give one")
+    if args.conv and (args.backward or args.workload in ("c4", "ssd", "ssd_step")):
+        ap.error("--conv applies to the forward scan (c0-c3)")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -723,7 +743,7 @@ def main():
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
     traffic = None if (args.softplus or args.trap) else \
-        measured_traffic(args.workload + ("_grad" if args.backward else ""))
+        measured_traffic(args.workload + ("_grad" if args.backward else "_conv" if args.conv else ""))
     kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL, "ssd_step": "ssd_step_kernel"}.get(args.workload, SCAN_KERNEL)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": kernel,
@@ -774,8 +794,10 @@ def main():
     else:
         config = {"workload": cfg.name, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                   "dtype": cfg.dtype, "gate": cfg.gate, "state_in": cfg.state_in is not None}
-        if args.softplus:
+        if args.softplus or args.conv:
             config["delta"] = "raw: softplus(delta_raw + dt_bias) in the kernel"
+        if args.conv:
+            config["x"] = "raw: SiLU of the causal width-4 depthwise convolution in the kernel"
         if args.trap:
             config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "selective-scan G(B*L*D*N)-elem/s"

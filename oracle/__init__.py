@@ -431,11 +431,12 @@ def scan_compare(blocks, dtype: str, nthreads: int = 0, rule: str = "scan"):
     of the workload that the oracle can run alone (some batch rows and channels
     over the whole sequence, as Oracle.scan takes them), y_got and state_got
     float64 (state_got None to skip it). `rule` names the oracle function:
-    "scan", "scan_dt" (step size before its activation) or "scan_trap".
+    "scan", "scan_dt" (step size before its activation), "scan_conv" (also x
+    before the block's convolution and SiLU) or "scan_trap".
     Returns (ErrorSum of y, ErrorSum of the state, seconds spent in the
     oracle)."""
     o = get()
-    fn = {"scan": o.scan, "scan_dt": o.scan_dt, "scan_trap": o.scan_trap}[rule]
+    fn = {"scan": o.scan, "scan_dt": o.scan_dt, "scan_conv": o.scan_conv, "scan_trap": o.scan_trap}[rule]
     ey, es, secs = ErrorSum(), ErrorSum(), 0.0
     for inp, y_got, st_got in blocks:
         t = time.perf_counter()

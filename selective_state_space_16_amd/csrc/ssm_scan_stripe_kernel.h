@@ -453,57 +453,32 @@ __device__ __forceinline__ void activate_delta(TB &tb, const float (&dtb)[Geo<N,
 
 // The x branch ahead of the scan, once a tile has landed: xc = SiLU of the
 // causal width-4 convolution of the raw x rows, per channel. A thread takes
-// one 16-byte piece column (VEC channels) over RPT consecutive rows and reads
-// the three rows before them too; rows before the tile are the last three
-// raw rows of `prev`, the other buffer, which holds the previous tile (its
-// next load is issued only after the barrier that follows this) or, for the
-// first tile of a pass, the raw x of the three tokens before the stripe
-// (stage_halo). Writes go to xc only, so no thread overwrites a row another
+// one channel over RPT consecutive rows, so every LDS access of a wave covers
+// one row of 64 channels (no bank conflicts); it reads the three rows before
+// its own too, all in one round. Rows before the tile are the last three raw
+// rows of `prev`, the other buffer, which holds the previous tile (its next
+// load is issued only after the barrier that follows this) or, for the first
+// tile of a pass, the raw x of the three tokens before the stripe (staged by
+// the walk). Writes go to xc only, so no thread overwrites a row another
 // still reads. `cw` holds the taps and bias of the tile column's channels.
 template <int N, int DT, class TB>
 __device__ __forceinline__ void conv_tile(TB &tb, const TB &prev, const float (&cw)[5][Geo<N, DT>::TCH]) {
     using G = Geo<N, DT>;
-    using T = typename G::T;
-    using HT = uint32_t __attribute__((ext_vector_type(2)));  // half a piece
-    constexpr int VEC = G::VEC, HV = VEC / 2, PPR = G::PPR, TT = G::TT;
-    constexpr int RPT = G::ACT_PIECES / (64 * kWaves);  // rows per thread
-    static_assert(G::ACT_PIECES % (64 * kWaves) == 0 && (64 * kWaves) % PPR == 0, "whole rows per thread");
-    const int pc = threadIdx.x % PPR, r0 = (threadIdx.x / PPR) * RPT;
-    // the two halves of the piece one after the other, which halves the
-    // registers the raw rows and the taps hold at once
+    constexpr int TCH = G::TCH, TT = G::TT;
+    constexpr int TPC = 64 * kWaves / TCH;  // threads per channel
+    constexpr int RPT = TT / TPC;           // rows per thread
+    static_assert((64 * kWaves) % TCH == 0 && TT % TPC == 0, "whole rows per thread");
+    const int c = threadIdx.x % TCH, r0 = (threadIdx.x / TCH) * RPT;
+    float raw[RPT + 3];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int c0 = pc * VEC + hh * HV;
-        float raw[RPT + 3][HV], w[5][HV];
-#pragma unroll
-        for (int k = 0; k < RPT + 3; ++k) {
-            const int r = r0 - 3 + k;
-            const T *src = r >= 0 ? &tb.x[r][c0] : &prev.x[TT + r][c0];
-            const HT v = *(const HT *)__builtin_assume_aligned(src, 8);
-            T e[HV];
-            __builtin_memcpy(e, &v, sizeof(v));
-#pragma unroll
-            for (int q = 0; q < HV; ++q) raw[k][q] = ld_act(e, q);
-        }
-#pragma unroll
-        for (int j = 0; j < 5; ++j)
-#pragma unroll
-            for (int q = 0; q < HV; ++q) w[j][q] = cw[j][c0 + q];
-#pragma unroll
-        for (int k = 0; k < RPT; ++k) {
-            T e[HV];
-#pragma unroll
-            for (int q = 0; q < HV; ++q) {
-                const float f = conv_silu(w[0][q], w[1][q], w[2][q], w[3][q], w[4][q], raw[k][q], raw[k + 1][q],
-                                          raw[k + 2][q], raw[k + 3][q]);
-                if constexpr (DT == 0) e[q] = f;
-                else e[q] = __builtin_bit_cast(uint16_t, (__bf16)f);
-            }
-            HT v;
-            __builtin_memcpy(&v, e, sizeof(v));
-            *(HT *)__builtin_assume_aligned(&tb.xc.v[r0 + k][c0], 8) = v;
-        }
+    for (int k = 0; k < RPT + 3; ++k) {
+        const int r = r0 - 3 + k;
+        raw[k] = ld_act(r >= 0 ? &tb.x[r][0] : &prev.x[TT + r][0], c);
     }
+    const float w0 = cw[0][c], w1 = cw[1][c], w2 = cw[2][c], w3 = cw[3][c], bias = cw[4][c];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)
+        st_act(&tb.xc.v[r0 + k][0], c, conv_silu(w0, w1, w2, w3, bias, raw[k], raw[k + 1], raw[k + 2], raw[k + 3]));
 }
 
 // One stripe record: NL state words per lane (and, for an aggregate, one
