@@ -40,9 +40,9 @@
  *  - delta is the step AFTER the softplus (the pages apply softplus to a
  *    projection plus bias before the scan). The *_dt entry points take the
  *    step before it and apply softplus(delta_raw + dt_bias) themselves.
- *  - x is the scan's input itself; ssm_scan_fwd_conv takes it one step
- *    earlier, before the short causal convolution and SiLU of the block's x
- *    branch, and applies both itself.
+ *  - x is the scan's input itself; ssm_scan_fwd_conv and ssm_step_conv take
+ *    it one step earlier, before the short causal convolution and SiLU of the
+ *    block's x branch, and apply both themselves.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronise the host. Arguments are checked on the
  *    host before any HIP call; a failed check returns a negative status and
@@ -304,6 +304,34 @@ int ssm_step_dt(int64_t batch, int64_t D, int64_t N, int dtype,
                 const void *x, const void *delta_raw, const float *dt_bias, const float *A,
                 const void *Bt, const void *Ct, const float *Dskip,
                 const void *z, float *state, void *y, void *stream);
+
+/*
+ * ssm_step_dt behind the x branch of the Mamba block, as in
+ * ssm_scan_fwd_conv: x of this token is SiLU of conv_b + the taps times the
+ * raw x of the three tokens before it (conv_state) and of this token
+ * (x_raw); conv_state is then shifted in place to hold the raw x of the last
+ * three tokens, this one last ("Notas sobre Mamba", section "O bloco Mamba";
+ * the constant-size state a decode step carries is the scan state plus this
+ * window).
+ *
+ *   x_raw         (batch, D)     dtype      the convolution's input
+ *   conv_w        (D, 4)         float      taps (as in ssm_scan_fwd_conv)
+ *   conv_b        (D)            float      bias; NULL = zero
+ *   conv_state    (batch, D, 3)  dtype      raw x of the three tokens before,
+ *                                           oldest first; read, then
+ *                                           overwritten with the window that
+ *                                           ends with this token
+ *
+ * Every other argument is that of ssm_step_dt; a NULL conv_w or conv_state
+ * with a non-empty input returns SSM_ERR_NULL. T calls on tokens 0..T-1,
+ * starting from a scan's conv_state and state_in, give ssm_scan_fwd_conv's y
+ * and final state over those tokens.
+ */
+int ssm_step_conv(int64_t batch, int64_t D, int64_t N, int dtype,
+                  const void *x_raw, const float *conv_w, const float *conv_b, void *conv_state,
+                  const void *delta_raw, const float *dt_bias, const float *A,
+                  const void *Bt, const void *Ct, const float *Dskip,
+                  const void *z, float *state, void *y, void *stream);
 
 /*
  * One decode step with the exponential-trapezoidal rule (see

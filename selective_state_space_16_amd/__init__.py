@@ -15,7 +15,8 @@ Functions (same names as the C ABI):
       of delta; the kernels use softplus(delta_raw + dt_bias) as the step size
   ssm_scan_fwd_conv(x_raw, conv_w, delta_raw, dt_bias, A, Bt, Ct, conv_b=None,
                     conv_state=None, ...) -> y: ssm_scan_fwd_dt behind the x
-      branch of the Mamba block (SiLU of a causal width-4 convolution of x_raw)
+      branch of the Mamba block (SiLU of a causal width-4 convolution of x_raw);
+      ssm_step_conv, its decode step, shifts conv_state in place
   ssm_scan_fwd_trap / ssm_step_trap: the exponential-trapezoidal rule, with a
       per-token weight lam and the token before the first (x_prev, B_prev)
   ssm_ssd_fwd(x, delta, A, Bt, Ct, Dskip=None, state_in=None, state_out=None,
@@ -45,7 +46,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_conv",
+    "ssm_scan_fwd_conv", "ssm_step_conv",
     "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_ssd_step", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error", "ssm_scan_workspace_status", "SSM_ERR_TIMEOUT", "ssm_scan_fwd_noalloc",
@@ -67,7 +68,7 @@ lib_path = os.environ.get("SSM_LIBRARY") or os.path.join(_HERE, "libssm.so")
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step",
-           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_conv")
+           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_conv", "ssm_step_conv")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_conv.restype = ci
     L.ssm_scan_fwd_trap.argtypes = [i64, i64, i64, i64, ci] + [vp] * 13 + [vp, sz, vp]
     L.ssm_scan_fwd_trap.restype = ci
+    L.ssm_step_conv.argtypes = [i64, i64, i64, ci] + [vp] * 13 + [vp]
+    L.ssm_step_conv.restype = ci
     L.ssm_step_trap.argtypes = [i64, i64, i64, ci] + [vp] * 12 + [vp]
     L.ssm_step_trap.restype = ci
     L.ssm_ssd_fwd.argtypes = [i64] * 6 + [ci] + [vp] * 9 + [vp]
@@ -335,7 +338,8 @@ def ssm_scan_fwd_trap(x, delta, lam, A, Bt, Ct, Dskip=None, z=None, x_prev=None,
                  stream, lam=lam, x_prev=x_prev, B_prev=B_prev)
 
 
-def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, lam=None, x_prev=None, B_prev=None):
+def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, lam=None, x_prev=None, B_prev=None,
+          conv_w=None, conv_b=None, conv_state=None):
     import torch
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, D) and A (D, N)")
@@ -348,9 +352,15 @@ def _step(name, x, delta, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, lam=No
     if y is None:
         y = torch.empty_like(x)
         allocated.append(y)
-    dname = "delta_raw" if name == "ssm_step_dt" else "delta"
-    args = [_ptr(x, "x", act), _ptr(delta, dname, act, (batch, D))]
-    if name == "ssm_step_dt":
+    raw = name in ("ssm_step_dt", "ssm_step_conv")
+    dname = "delta_raw" if raw else "delta"
+    if name == "ssm_step_conv":
+        args = [_ptr(x, "x_raw", act), _ptr(conv_w, "conv_w", f32, (D, 4)), _ptr(conv_b, "conv_b", f32, (D,)),
+                _ptr(conv_state, "conv_state", act, (batch, D, 3))]
+    else:
+        args = [_ptr(x, "x", act)]
+    args.append(_ptr(delta, dname, act, (batch, D)))
+    if raw:
         args.append(_ptr(dt_bias, "dt_bias", f32, (D,)))
     trap = name == "ssm_step_trap"
     if trap:
@@ -379,6 +389,16 @@ def ssm_step(x, delta, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None
 def ssm_step_dt(x, delta_raw, dt_bias, A, Bt, Ct, state, Dskip=None, z=None, y=None, stream=None):
     """ssm_step with the step size before its activation (see ssm_scan_fwd_dt)."""
     return _step("ssm_step_dt", x, delta_raw, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream)
+
+
+def ssm_step_conv(x_raw, conv_w, conv_state, delta_raw, dt_bias, A, Bt, Ct, state, conv_b=None, Dskip=None, z=None,
+                  y=None, stream=None):
+    """ssm_step_dt behind the Mamba block's x branch (see ssm_scan_fwd_conv):
+    x_raw (batch, D), conv_w (D, 4), conv_b (D,) or None, and conv_state
+    (batch, D, 3) in the activation dtype, the raw x of the three tokens
+    before, shifted in place to end with this token's."""
+    return _step("ssm_step_conv", x_raw, delta_raw, dt_bias, A, Bt, Ct, state, Dskip, z, y, stream, conv_w=conv_w,
+                 conv_b=conv_b, conv_state=conv_state)
 
 
 def ssm_step_trap(x, delta, lam, A, Bt, Ct, state, Dskip=None, z=None, x_prev=None, B_prev=None, y=None,

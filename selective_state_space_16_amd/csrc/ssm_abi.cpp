@@ -231,7 +231,8 @@ static int step(int64_t batch, int64_t D, int64_t N, int dtype,
     if (checked_mul3(batch, D, N) < 0) return SSM_ERR_SHAPE;
     if (batch == 0 || D == 0) return SSM_OK;
     if (!x || !delta || !A || !Bt || !Ct || !state || !y) return SSM_ERR_NULL;
-    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y, dt_bias, tr.lam, tr.x_prev, tr.B_prev};
+    const void *ptrs[] = {x, delta, A, Bt, Ct, Dskip, z, state, y, dt_bias, tr.lam, tr.x_prev, tr.B_prev,
+                          tr.conv_w, tr.conv_b, tr.conv_state};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return SSM_ERR_ALIGN;
     ssm::StepArgs a{};
@@ -251,6 +252,9 @@ static int step(int64_t batch, int64_t D, int64_t N, int dtype,
     a.lam = tr.lam;
     a.x_prev = tr.x_prev;
     a.B_prev = tr.B_prev;
+    a.conv_w = tr.conv_w;
+    a.conv_b = tr.conv_b;
+    a.conv_state = const_cast<void *>(tr.conv_state);
     return ssm::launch_step(a, (int)N, dtype, (hipStream_t)stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -314,6 +318,19 @@ int ssm_step_dt(int64_t batch, int64_t D, int64_t N, int dtype,
                 const void *Bt, const void *Ct, const float *Dskip,
                 const void *z, float *state, void *y, void *stream) {
     return step(batch, D, N, dtype, x, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state, y, stream);
+}
+
+int ssm_step_conv(int64_t batch, int64_t D, int64_t N, int dtype,
+                  const void *x_raw, const float *conv_w, const float *conv_b, void *conv_state,
+                  const void *delta_raw, const float *dt_bias, const float *A,
+                  const void *Bt, const void *Ct, const float *Dskip,
+                  const void *z, float *state, void *y, void *stream) {
+    if ((!conv_w || !conv_state) && batch > 0 && D > 0) return SSM_ERR_NULL;
+    TrapIn tr;
+    tr.conv_w = conv_w;
+    tr.conv_b = conv_b;
+    tr.conv_state = conv_state;
+    return step(batch, D, N, dtype, x_raw, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip, z, state, y, stream, tr);
 }
 
 int ssm_step_trap(int64_t batch, int64_t D, int64_t N, int dtype,

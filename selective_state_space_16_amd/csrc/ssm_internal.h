@@ -88,6 +88,13 @@ struct StepArgs {
     // exponential-trapezoidal rule: per-token weight lam (NULL = the Euler
     // rule) and the token before the first (x_prev, B_prev; NULL = none)
     const void *lam, *x_prev, *B_prev;
+    // the x branch ahead of the step (as in ScanArgs): taps conv_w (D, 4),
+    // bias conv_b (D; NULL = 0) and conv_state (batch, D, 3, activation
+    // dtype), the raw x of the three tokens before this one, which the step
+    // shifts in place to end with this token's raw x. conv_w NULL: x is used
+    // as given.
+    const float *conv_w, *conv_b;
+    void *conv_state;
     float *state;
     void *y;
 };

@@ -14,6 +14,11 @@
 // and the channel's readout, summed over its LPC lanes with DPP quad
 // permutes, comes back the same way. A is read once for the kRows rows, and
 // every load of a row group is issued before the first use.
+//
+// MODE kConv adds the x branch ahead of the step ("Notas sobre Mamba",
+// section "O bloco Mamba"): the lane that moves a channel's x reads the raw x
+// of the three tokens before it from conv_state, uses SiLU of the causal
+// width-4 convolution as x, and shifts this token's raw x into conv_state.
 #include "ssm_common.h"
 #include "ssm_internal.h"
 
@@ -85,7 +90,7 @@ __device__ __forceinline__ float from_lane(int src, float v) {
 
 // What the step computes besides the exponential-Euler update on an
 // activated step size.
-enum StepMode { kEuler = 0, kSoftplus = 1, kTrap = 2 };
+enum StepMode { kEuler = 0, kSoftplus = 1, kTrap = 2, kConv = 3 };
 
 // Grid: x = block of kBlockCh channels, y = group of kRows batch rows
 // (strided by gridDim.y when the groups outnumber kMaxGridY).
@@ -96,9 +101,10 @@ enum StepMode { kEuler = 0, kSoftplus = 1, kTrap = 2 };
 // with v = B x of this token and v_prev = B_prev x_prev of the previous one
 // (zero when x_prev and B_prev are not given), taken as
 //   h = a (h + ((1 - lam) delta x_prev) B_prev) + (lam delta x) B.
+// MODE kConv: as kSoftplus, with x before the block's convolution and SiLU.
 template <int N, int DT, bool GATE, bool SKIP, int MODE>
 __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
-    constexpr bool SP = MODE == kSoftplus, TRAP = MODE == kTrap;
+    constexpr bool CONV = MODE == kConv, SP = MODE == kSoftplus || CONV, TRAP = MODE == kTrap;
     using T = typename Act<DT>::T;
     constexpr int NPL = N < 4 ? N : 4;
     constexpr int LPC = N / NPL;        // lanes per channel = accesses per row
@@ -130,6 +136,12 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
     for (int q = 0; q < LPC; ++q) ld_vec<NPL>(a.A + chq[q] * N + n0, A2[q]);
     const float ds = SKIP ? a.Dskip[own] : 0.0f;
     const float dtb = (SP && a.dt_bias) ? a.dt_bias[own] : 0.0f;  // bias of a raw step size
+    // taps and bias of the convolution for the channel this lane moves
+    float cwv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbias = 0.0f;
+    if constexpr (CONV) {
+        ld_vec<4>(a.conv_w + own * 4, cwv);
+        cbias = a.conv_b ? a.conv_b[own] : 0.0f;
+    }
 #pragma unroll
     for (int q = 0; q < LPC; ++q)
 #pragma unroll
@@ -144,7 +156,7 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
             bok[r] = b < a.batch;
             bc[r] = bok[r] ? b : a.batch - 1;
         }
-        float h[kRows][LPC][NPL], xo[kRows], dto[kRows], zo[kRows], lo[kRows], xpo[kRows];
+        float h[kRows][LPC][NPL], xo[kRows], dto[kRows], zo[kRows], lo[kRows], xpo[kRows], cso[kRows][3];
         typename BC::T braw[kRows], craw[kRows], bpraw[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; ++r)
@@ -159,6 +171,10 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
             if (GATE) zo[r] = ld_act((const T *)a.z, row);
             braw[r] = BC::load(Bp + bc[r] * N + n0);
             craw[r] = BC::load(Cp + bc[r] * N + n0);
+            if constexpr (CONV) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) cso[r][j] = ld_act((const T *)a.conv_state, row * 3 + j);
+            }
             if constexpr (TRAP) {
                 lo[r] = ld_act((const T *)a.lam, row);
                 if (a.x_prev) {
@@ -168,6 +184,22 @@ __global__ __launch_bounds__(kStepBlock) void step_kernel(StepArgs a) {
             }
         }
 
+        if constexpr (CONV) {
+            // x of this token from the branch's convolution; the raw x moves
+            // into the window
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const float raw = xo[r];
+                xo[r] = act_round<DT>(conv_silu(cwv[0], cwv[1], cwv[2], cwv[3], cbias, cso[r][0], cso[r][1],
+                                                cso[r][2], raw));
+                if (bok[r] && own_ok) {
+                    T *cs = (T *)a.conv_state + (bc[r] * D + own) * 3;
+                    st_act(cs, 0, cso[r][1]);
+                    st_act(cs, 1, cso[r][2]);
+                    st_act(cs, 2, raw);
+                }
+            }
+        }
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             float Bv[NPL], Cv[NPL], Bpv[NPL], acc[LPC];
@@ -245,6 +277,7 @@ hipError_t launch_step_mode(const StepArgs &a, hipStream_t s) {
 template <int N, int DT>
 hipError_t launch_step_flags(const StepArgs &a, hipStream_t s) {
     if (a.lam) return launch_step_mode<N, DT, kTrap>(a, s);
+    if (a.conv_w) return launch_step_mode<N, DT, kConv>(a, s);
     if (a.delta_softplus) return launch_step_mode<N, DT, kSoftplus>(a, s);
     return launch_step_mode<N, DT, kEuler>(a, s);
 }

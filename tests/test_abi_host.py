@@ -206,8 +206,27 @@ def test_scan_conv_rejects(kw, code):
     assert scan_conv(**kw) == code
 
 
+def step_conv(**kw):
+    a = dict(batch=1, D=64, N=16, dtype=0, x_raw=P, conv_w=P, conv_b=None, conv_state=P, delta_raw=P, dt_bias=None,
+             A=P, Bt=P, Ct=P, Dskip=None, z=None, state=P, y=P, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_step_conv(a["batch"], a["D"], a["N"], a["dtype"], a["x_raw"], a["conv_w"], a["conv_b"],
+                                   a["conv_state"], a["delta_raw"], a["dt_bias"], a["A"], a["Bt"], a["Ct"],
+                                   a["Dskip"], a["z"], a["state"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=5), -4), (dict(conv_w=None), -1), (dict(conv_state=None), -1),
+    (dict(x_raw=None), -1), (dict(state=None), -1), (dict(conv_w=MIS), -5), (dict(conv_b=MIS), -5),
+    (dict(conv_state=MIS), -5),
+])
+def test_step_conv_rejects(kw, code):
+    assert step_conv(**kw) == code
+
+
 def test_conv_entry_point_empty_ok_without_gpu():
     assert scan_conv(batch=0) == 0 and scan_conv(D=0) == 0 and scan_conv(conv_w=None, L=0) == 0
+    assert step_conv(batch=0) == 0 and step_conv(D=0) == 0 and step_conv(conv_state=None, batch=0) == 0
 
 
 def scan_trap(**kw):

@@ -152,3 +152,57 @@ def test_scan_conv_stripe_and_fallback_agree():
     finally:
         del os.environ["SSM_SCAN_IMPL"]
     assert np.allclose(y1, y2, rtol=1e-5, atol=1e-5) and np.allclose(s1, s2, rtol=1e-5, atol=1e-5)
+
+
+# -- the decode step ----------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [37, 300])
+def test_step_conv_every_output(N, dtype, D):
+    """One step of five sequences against the oracle's scan over that one
+    token (y and state), and the window it leaves: the last two earlier raw
+    tokens and this token's raw x, bit for bit."""
+    import torch
+    cfg = _cfg(f"step_conv_{N}_{D}", 5, 1, D, N, dtype, state_in=1.0)
+    say(f"case {cfg}")
+    inp = _inputs(cfg)
+    yr, sr = oracle.get().scan_conv(inp, dtype)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    state = dev["state_in"].clone()
+    window = dev["conv_state"].clone()
+    y = ssm.ssm_step_conv(dev["x_raw"][:, 0].contiguous(), dev["conv_w"], window, dev["delta_raw"][:, 0].contiguous(),
+                          dev["dt_bias"], dev["A"], dev["Bt"][:, 0].contiguous(), dev["Ct"][:, 0].contiguous(), state,
+                          conv_b=dev["conv_b"], Dskip=dev["Dskip"], z=dev["z"][:, 0].contiguous())
+    torch.cuda.synchronize()
+    check(to_f64(y)[:, None, :], yr, dtype, "y")
+    check(to_f64(state), sr, dtype, "state")
+    want = np.concatenate([inp["conv_state"][:, :, 1:], inp["x_raw"][:, 0][:, :, None]], axis=2)
+    got = window.cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+    assert np.array_equal(got, want), "conv_state after the step"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_conv_fold_equals_scan_conv(dtype):
+    """T decode steps from the scan's conv_state and state_in give the scan's
+    y and final state, and leave the last three raw tokens as the window."""
+    import torch
+    cfg = _cfg("fold_conv", 2, 150, 70, 16, dtype, state_in=0.4)
+    say(f"case {cfg}")
+    inp = _inputs(cfg)
+    y, st = gpu_scan_conv(inp)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    state = dev["state_in"].clone()
+    window = dev["conv_state"].clone()
+    ys = []
+    for t in range(cfg.L):
+        yt = ssm.ssm_step_conv(dev["x_raw"][:, t].contiguous(), dev["conv_w"], window,
+                               dev["delta_raw"][:, t].contiguous(), dev["dt_bias"], dev["A"],
+                               dev["Bt"][:, t].contiguous(), dev["Ct"][:, t].contiguous(), state, conv_b=dev["conv_b"],
+                               Dskip=dev["Dskip"], z=dev["z"][:, t].contiguous())
+        ys.append(to_f64(yt))
+    torch.cuda.synchronize()
+    check(np.stack(ys, 1), y, dtype, "fold of steps vs scan (y)")
+    check(to_f64(state), st, dtype, "fold of steps vs scan (state)")
+    assert torch.equal(window, dev["x_raw"][:, -3:].transpose(1, 2).contiguous()), "window after the steps"
