@@ -79,7 +79,8 @@ SHARED_SOURCES = ("ssm_common.h", "ssm_device.h", "ssm_internal.h")
 def kernel_family(workload: str) -> str:
     if workload.endswith("_grad"):
         return "grad"
-    return {"c4": "step", "ssd": "ssd", "ssd_step": "ssd_step"}.get(workload, "scan")
+    base = workload[:-len("_conv")] if workload.endswith("_conv") else workload
+    return {"c4": "step", "ssd": "ssd", "ssd_step": "ssd_step"}.get(base, "scan")
 
 
 def kernel_source_hash(family: str) -> str:
@@ -608,10 +609,13 @@ def bench_step(args):
     cfg = W.STEP_CONFIG
     log(f"[bench] workload {cfg}")
     nsteps = args.steps + args.warmup
-    base = W.step_inputs(cfg)
+    cv = args.conv  # x before the block's convolution and SiLU (ssm_step_conv)
+    base = W.step_inputs(cfg, conv=cv)
     state = to_dev(base["state"])
     A, Dskip = to_dev(base["A"]), to_dev(base["Dskip"])
-    sp = args.softplus  # delta handed over before its activation
+    cw, cb, window = (to_dev(base["conv_w"]), to_dev(base["conv_b"]), to_dev(base["conv_state"])) if cv else \
+        (None, None, None)
+    sp = args.softplus or cv  # delta handed over before its activation
     tr = args.trap  # exponential-trapezoidal rule; step s gets token s - 1 as the earlier token
     fill = W.fill_step_device(cfg, nsteps, "cuda", raw_delta=sp, trap=tr)
     bias = to_dev(base["dt_bias"])
@@ -619,7 +623,10 @@ def bench_step(args):
     stream = torch.cuda.current_stream()
 
     def step(s):
-        if sp:
+        if cv:
+            ssm.ssm_step_conv(fill["x"][s], cw, window, fill["delta_raw"][s], bias, A, fill["Bt"][s], fill["Ct"][s],
+                              state, conv_b=cb, Dskip=Dskip, z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
+        elif sp:
             ssm.ssm_step_dt(fill["x"][s], fill["delta_raw"][s], bias, A, fill["Bt"][s], fill["Ct"][s], state,
                             Dskip=Dskip, z=fill["z"][s], y=y, stream=torch.cuda.current_stream())
         elif tr:
@@ -655,18 +662,23 @@ def bench_step(args):
     log(f"[bench] {args.steps} decode steps from a graph, {ms * 1e3:.2f} us/step "
         f"(eager launches from Python: {eager_ms * 1e3:.2f} us/step)")
     out = {"cfg": cfg, "ms": ms, "launch_ms": launch_ms, "elems": cfg.elems_per_step,
-           "bytes": W.step_bytes(cfg) + (cfg.D * 4 if sp else 0) + (W.trap_step_extra_bytes(cfg) if tr else 0),
+           "bytes": W.step_bytes(cfg) + (cfg.D * 4 if sp else 0) + (W.trap_step_extra_bytes(cfg) if tr else 0) +
+                    (cfg.D * 5 * 4 + 2 * cfg.batch * cfg.D * 3 * W._esize(cfg.dtype) if cv else 0),
            "dtype": cfg.dtype, "parity": None, "cpu": None}
     if not args.no_cpu:
         import oracle
         o = oracle.get()
         sel = np.arange(0, cfg.D, 16)  # a bounded sample: every 16th channel
         st64 = np.ascontiguousarray(base["state"][:, sel], dtype=np.float64)
+        win64 = W.storage_to_f64(base["conv_state"][:, sel], cfg.dtype) if cv else None
         reps, tot, prev = 0, 0.0, None
         while reps == 0 or (tot < args.cpu_seconds and reps < cfg.steps):
             tk = W.step_token_inputs(cfg, reps, channels=sel, raw_delta=sp, trap=tr)
             t = time.perf_counter()
-            if sp:
+            if cv:
+                o.step_conv(tk, base["A"][sel], base["Dskip"][sel], base["dt_bias"][sel], base["conv_w"][sel],
+                            base["conv_b"][sel], win64, st64, cfg.dtype)
+            elif sp:
                 o.step_dt(tk, base["A"][sel], base["Dskip"][sel], base["dt_bias"][sel], st64, cfg.dtype)
             elif tr:
                 o.step_trap(dict(tk, x_prev=None if prev is None else prev["x"],
@@ -709,8 +721,8 @@ def main():
     args = ap.parse_args()
     if sum((args.softplus, args.trap, args.conv)) > 1:
         ap.error("--softplus, --trap and --conv select different entry points; give one")
-    if args.conv and (args.backward or args.workload in ("c4", "ssd", "ssd_step")):
-        ap.error("--conv applies to the forward scan (c0-c3)")
+    if args.conv and (args.backward or args.workload in ("ssd", "ssd_step")):
+        ap.error("--conv applies to the forward scan (c0-c3) and the decode step (c4)")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -786,8 +798,10 @@ def main():
     elif args.workload == "c4":
         config = {"workload": cfg.name, "batch": cfg.batch, "D": cfg.D, "N": cfg.N, "dtype": cfg.dtype,
                   "gate": cfg.gate, "steps_timed": args.steps}
-        if args.softplus:
+        if args.softplus or args.conv:
             config["delta"] = "raw: softplus(delta_raw + dt_bias) in the kernel"
+        if args.conv:
+            config["x"] = "raw: SiLU of the causal width-4 depthwise convolution in the kernel, window updated in place"
         if args.trap:
             config["rule"] = "exponential-trapezoidal, lam per token and channel"
         metric = "decode-step G(B*D*N)-elem/s"

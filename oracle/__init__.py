@@ -340,6 +340,24 @@ class Oracle:
                            up(tok["Ct"]), None if Dskip is None else upcast(Dskip, "f32"),
                            up(tok.get("z")), state64, nthreads=nthreads)
 
+    def step_conv(self, tok: Dict[str, np.ndarray], A, Dskip, dt_bias, conv_w, conv_b, window64: np.ndarray,
+                  state64: np.ndarray, dtype: str, nthreads: int = 0):
+        """Decode step behind the x branch: tok["x"] is the token's raw x,
+        window64 (batch, D, 3) float64 the raw x of the three tokens before it
+        (oldest first). x is the branch's convolution and SiLU (conv_silu64 over
+        that one token); window64 is shifted in place to end with this token's
+        raw x; the step runs as step_dt."""
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        raw = upcast(tok["x"], dtype)
+        x64 = self.conv_silu64(raw[:, None, :], f32(conv_w), f32(conv_b), window64)[:, 0, :]
+        window64[:, :, :2] = window64[:, :, 1:].copy()
+        window64[:, :, 2] = raw
+        bias = None if dt_bias is None else upcast(dt_bias, "f32")
+        d64 = self.softplus_bias64(upcast(tok["delta_raw"], dtype), bias)
+        up = lambda a: None if a is None else upcast(a, dtype)
+        return self.step64(x64, d64, upcast(A, "f32"), up(tok["Bt"]), up(tok["Ct"]), f32(Dskip), up(tok.get("z")),
+                           state64, nthreads=nthreads)
+
     def scan_trap(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
         """Exponential-trapezoidal scan on stored inputs: inp["lam"] (stored dtype)
         and optional inp["x_prev"], inp["B_prev"] (stored dtype)."""

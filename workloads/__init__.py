@@ -336,16 +336,26 @@ def grad_inputs(cfg: ScanConfig, t0: int = 0, t1: Optional[int] = None, channels
     return out
 
 
-def step_inputs(cfg: StepConfig, channels: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+def step_inputs(cfg: StepConfig, channels: Optional[np.ndarray] = None, conv: bool = False) -> Dict[str, np.ndarray]:
     """Per-workload tensors of a decode run: A, Dskip, dt_bias (float32) and
-    the initial state."""
+    the initial state; with conv also the x branch's taps conv_w (D, 4) and
+    bias conv_b (D,) (float32) and its initial window conv_state (batch, D, 3)
+    in the storage dtype, drawn as in scan_inputs."""
     A, dt_bias, Dskip = _channel_params(cfg.seed, cfg.D, cfg.N, cfg.dskip)
     sel = np.arange(cfg.D) if channels is None else np.asarray(channels)
     st = _rng(cfg.seed, _K_STATE).standard_normal((cfg.batch, cfg.D, cfg.N)) * cfg.state_std
-    return {"A": np.ascontiguousarray(A[sel]),
-            "Dskip": None if Dskip is None else np.ascontiguousarray(Dskip[sel]),
-            "dt_bias": np.ascontiguousarray(dt_bias[sel].astype(np.float32)),
-            "state": np.ascontiguousarray(st[:, sel, :].astype(np.float32))}
+    out = {"A": np.ascontiguousarray(A[sel]),
+           "Dskip": None if Dskip is None else np.ascontiguousarray(Dskip[sel]),
+           "dt_bias": np.ascontiguousarray(dt_bias[sel].astype(np.float32)),
+           "state": np.ascontiguousarray(st[:, sel, :].astype(np.float32))}
+    if conv:
+        w = _rng(cfg.seed, _K_CONVW).uniform(-0.5, 0.5, size=(cfg.D, 4))
+        cb = _rng(cfg.seed, _K_CONVB).uniform(-0.5, 0.5, size=cfg.D)
+        cs = _rng(cfg.seed, _K_CONVSTATE).standard_normal((cfg.batch, cfg.D, 3))
+        out["conv_w"] = np.ascontiguousarray(w[sel].astype(np.float32))
+        out["conv_b"] = np.ascontiguousarray(cb[sel].astype(np.float32))
+        out["conv_state"] = np.ascontiguousarray(_store(cs[:, sel, :], cfg.dtype))
+    return out
 
 
 def step_token_inputs(cfg: StepConfig, step: int, channels: Optional[np.ndarray] = None,
