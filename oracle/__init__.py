@@ -61,6 +61,8 @@ class Oracle:
         self.lib.oracle_softplus_bias.restype = ci
         self.lib.oracle_conv_silu.argtypes = [i64, i64, i64] + [_DP] * 5
         self.lib.oracle_conv_silu.restype = ci
+        self.lib.oracle_conv_silu_bwd.argtypes = [i64, i64, i64] + [_DP] * 9
+        self.lib.oracle_conv_silu_bwd.restype = ci
         self.lib.oracle_scan_trap.argtypes = [i64, i64, i64, i64] + [_DP] * 13 + [ci]
         self.lib.oracle_scan_trap.restype = ci
         self.lib.oracle_step_trap.argtypes = [i64, i64, i64] + [_DP] * 12 + [ci]
@@ -293,6 +295,21 @@ class Oracle:
             raise ValueError("oracle_conv_silu rejected sizes")
         return out
 
+    def conv_silu_bwd64(self, x, w, cb, state, gout):
+        """Gradient of conv_silu64 for a loss with d loss / d out = gout (float64
+        arrays shaped as in conv_silu64). Returns dict gx (batch, L, D), gw (D, 4),
+        gb (D,) and gstate (batch, D, 3)."""
+        x = _c64(x)
+        batch, L, D = x.shape
+        w, gout = _c64(w), _c64(gout)
+        cb = None if cb is None else _c64(cb)
+        state = None if state is None else _c64(state)
+        out = {"gx": np.empty_like(x), "gw": np.empty((D, 4)), "gb": np.empty(D), "gstate": np.empty((batch, D, 3))}
+        if self.lib.oracle_conv_silu_bwd(batch, L, D, _p(x), _p(w), _p(cb), _p(state), _p(gout), _p(out["gx"]),
+                                         _p(out["gw"]), _p(out["gb"]), _p(out["gstate"])) != 0:
+            raise ValueError("oracle_conv_silu_bwd rejected sizes")
+        return out
+
     # -- stored-dtype entry points -------------------------------------------
     def scan(self, inp: Dict[str, np.ndarray], dtype: str, nthreads: int = 0):
         """Scan on stored inputs (float32 arrays, or bfloat16 bit patterns as uint16).
@@ -400,6 +417,22 @@ class Oracle:
         return self.scan_bwd_trap64(up(inp["x"]), up(inp["delta"]), up(inp["lam"]), f32(inp["A"]), up(inp["Bt"]),
                                     up(inp["Ct"]), f32(inp.get("Dskip")), up(inp.get("z")), up(inp.get("x_prev")),
                                     up(inp.get("B_prev")), f32(inp.get("state_in")), up(dy), f32(dstate))
+
+    def scan_bwd_conv(self, inp: Dict[str, np.ndarray], dy, dstate, dtype: str):
+        """Gradient of scan_conv: the scan's gradient on the branch's output x
+        (with the step size before its activation), then back through SiLU and
+        the convolution. Keys as scan_bwd_dt's with dx replaced by dx_raw, plus
+        dconv_w, dconv_b and dconv_state."""
+        f32 = lambda a: None if a is None else upcast(a, "f32")
+        up = lambda a: None if a is None else upcast(a, dtype)
+        xr, w, cb, cs = up(inp["x_raw"]), f32(inp["conv_w"]), f32(inp.get("conv_b")), up(inp.get("conv_state"))
+        x64 = self.conv_silu64(xr, w, cb, cs)
+        g = self.scan_bwd_dt64(x64, up(inp["delta_raw"]), f32(inp.get("dt_bias")), f32(inp["A"]), up(inp["Bt"]),
+                               up(inp["Ct"]), f32(inp.get("Dskip")), up(inp.get("z")), f32(inp.get("state_in")),
+                               upcast(dy, dtype), None if dstate is None else upcast(dstate, "f32"))
+        c = self.conv_silu_bwd64(xr, w, cb, cs, g.pop("dx"))
+        g["dx_raw"], g["dconv_w"], g["dconv_b"], g["dconv_state"] = c["gx"], c["gw"], c["gb"], c["gstate"]
+        return g
 
     def scan_bwd_dt(self, inp: Dict[str, np.ndarray], dy, dstate, dtype: str):
         """scan_bwd64_dt on stored inputs (delta_raw in the stored dtype, dt_bias float32 or None)."""

@@ -187,6 +187,72 @@ int oracle_conv_silu(int64_t batch, int64_t L, int64_t D, const double *x, const
 }
 
 /*
+ * Gradient of oracle_conv_silu for a loss whose gradient with respect to its
+ * output is gout (batch, L, D), by the chain rule (reverse mode, by hand).
+ * With u and the window xr as in oracle_conv_silu and
+ *   du[t]     = gout[t] * sigmoid(u[t]) * (1 + u[t] * (1 - sigmoid(u[t])))    (SiLU')
+ * the gradients are
+ *   gx[s]     = sum_j w[d, j] * du[s + 3 - j]     over tokens s + 3 - j in 0..L-1
+ *   gw[d, j]  = sum_{b, t} du[t] * xr(b, t - 3 + j, d)
+ *   gb[d]     = sum_{b, t} du[t]
+ *   gstate[b, d, k] (the raw x of token k - 3) = sum_j w[d, j] * du[k - j], k - j >= 0
+ * gw and gb are overwritten (not accumulated); gb, state and gstate may be
+ * NULL.
+ */
+int oracle_conv_silu_bwd(int64_t batch, int64_t L, int64_t D, const double *x, const double *w, const double *cb,
+                         const double *state, const double *gout, double *gx, double *gw, double *gb,
+                         double *gstate)
+{
+    if (batch < 0 || L < 0 || D < 0) return -1;
+    double *du = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!du) return -1;
+    for (int64_t d = 0; d < D; ++d) {
+        for (int64_t j = 0; j < 4; ++j) gw[d * 4 + j] = 0.0;
+        if (gb) gb[d] = 0.0;
+    }
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            for (int64_t t = 0; t < L; ++t) {
+                double u = cb ? cb[d] : 0.0;
+                for (int64_t j = 0; j < 4; ++j) {
+                    int64_t s = t - 3 + j;
+                    double v;
+                    if (s >= 0) v = x[IDX3(b, s, d, L, D)];
+                    else v = state ? state[IDX3(b, d, s + 3, D, 3)] : 0.0;
+                    u += w[d * 4 + j] * v;
+                }
+                double sg = 1.0 / (1.0 + exp(-u));
+                du[t] = gout[IDX3(b, t, d, L, D)] * sg * (1.0 + u * (1.0 - sg));
+                for (int64_t j = 0; j < 4; ++j) {
+                    int64_t s = t - 3 + j;
+                    double v;
+                    if (s >= 0) v = x[IDX3(b, s, d, L, D)];
+                    else v = state ? state[IDX3(b, d, s + 3, D, 3)] : 0.0;
+                    gw[d * 4 + j] += du[t] * v;
+                }
+                if (gb) gb[d] += du[t];
+            }
+            for (int64_t s = 0; s < L; ++s) {
+                double g = 0.0;
+                for (int64_t j = 0; j < 4; ++j) {
+                    int64_t t = s + 3 - j;
+                    if (t < L) g += w[d * 4 + j] * du[t];
+                }
+                gx[IDX3(b, s, d, L, D)] = g;
+            }
+            if (gstate)
+                for (int64_t k = 0; k < 3; ++k) {
+                    double g = 0.0;
+                    for (int64_t j = 0; j <= k; ++j)
+                        if (k - j < L) g += w[d * 4 + j] * du[k - j];
+                    gstate[IDX3(b, d, k, D, 3)] = g;
+                }
+        }
+    free(du);
+    return 0;
+}
+
+/*
  * Gradient of oracle_scan_trap for the loss sum(dy * y) + sum(dstate *
  * state_out), by the chain rule through its recurrence (reverse mode, by
  * hand). With G_t the gradient of h_t (from the readout of token t and from

@@ -384,6 +384,59 @@ def pin_conv_silu(o):
     assert np.array_equal(np.concatenate([first, second], axis=1), whole)
 
 
+def pin_conv_silu_bwd(o):
+    """Gradient of the x branch: every element of the gradients of the raw x,
+    the taps, the bias and the earlier raw tokens against central differences
+    of the loss sum(g * conv_silu(...)), and, through the whole scan, the
+    gradients of x_raw and the taps against central differences of the scan's
+    loss."""
+    rng = np.random.default_rng(12)
+    batch, L, D = 2, 7, 3
+    x = rng.normal(size=(batch, L, D))
+    w = rng.uniform(-0.5, 0.5, size=(D, 4))
+    cb = rng.uniform(-0.5, 0.5, size=D)
+    st = rng.normal(size=(batch, D, 3))
+    g = rng.normal(size=(batch, L, D))
+    got = o.conv_silu_bwd64(x, w, cb, st, g)
+    loss = lambda xx, ww, bb, ss: float(np.sum(g * o.conv_silu64(xx, ww, bb, ss)))
+    eps = 1e-6
+    for name, arr, key in (("x", x, "gx"), ("w", w, "gw"), ("b", cb, "gb"), ("state", st, "gstate")):
+        for idx in np.ndindex(arr.shape):
+            args = {"x": x, "w": w, "b": cb, "state": st}
+            hi = {k: v.copy() for k, v in args.items()}
+            lo = {k: v.copy() for k, v in args.items()}
+            hi[name][idx] += eps
+            lo[name][idx] -= eps
+            fd = (loss(hi["x"], hi["w"], hi["b"], hi["state"]) - loss(lo["x"], lo["w"], lo["b"], lo["state"])) / (2 * eps)
+            assert abs(fd - got[key][idx]) <= 1e-7 * (1 + abs(fd)), (name, idx, fd, got[key][idx])
+    # through the scan: inputs as the stored-dtype entry points take them (float32 arrays)
+    p = _rand_problem(rng, 1, 6, 3, 4)
+    inp = {"x_raw": x[:1, :6].astype(np.float32), "conv_w": w.astype(np.float32), "conv_b": cb.astype(np.float32),
+           "conv_state": st[:1].astype(np.float32), "delta_raw": (0.5 * rng.normal(size=(1, 6, 3))).astype(np.float32),
+           "dt_bias": rng.normal(size=3).astype(np.float32) * 0.1, "A": p["A"].astype(np.float32),
+           "Bt": p["Bt"].astype(np.float32), "Ct": p["Ct"].astype(np.float32),
+           "Dskip": p["Dskip"].astype(np.float32), "z": p["z"].astype(np.float32),
+           "state_in": p["state_in"].astype(np.float32)}
+    dy = rng.normal(size=(1, 6, 3)).astype(np.float32)
+    dst = rng.normal(size=(1, 3, 4)).astype(np.float32)
+    gr = o.scan_bwd_conv(inp, dy, dst, "f32")
+
+    def scan_loss(q):
+        y, sfin = o.scan_conv(q, "f32")
+        return float(np.sum(dy.astype(np.float64) * y) + np.sum(dst.astype(np.float64) * sfin))
+    for key, gkey in (("x_raw", "dx_raw"), ("conv_w", "dconv_w"), ("conv_state", "dconv_state")):
+        for idx in list(np.ndindex(inp[key].shape))[::3]:
+            base = inp[key][idx]
+            h = 1e-3 * max(1.0, abs(float(base)))
+            qa, qb = dict(inp), dict(inp)
+            qa[key], qb[key] = inp[key].copy(), inp[key].copy()
+            qa[key][idx] = np.float32(base + h)
+            qb[key][idx] = np.float32(base - h)
+            step = float(qa[key][idx]) - float(qb[key][idx])
+            fd = (scan_loss(qa) - scan_loss(qb)) / step
+            assert abs(fd - gr[gkey][idx]) <= 1e-4 * (1 + abs(fd)), (key, idx, fd, gr[gkey][idx])
+
+
 # --- the exponential-trapezoidal variant ------------------------------------
 def _trap(o, p, lam, **kw):
     return o.scan_trap64(p["x"], p["delta"], lam, p["A"], p["Bt"], p["Ct"], p.get("Dskip"), p.get("z"),
@@ -760,7 +813,7 @@ def pin_bwd_adjoint_identities(o):
     assert abs(lhs - rhs) <= 1e-10 * (1 + abs(lhs)), (lhs, rhs)
 
 
-ALL_PINS = [pin_conv_silu, pin_bwd_trap_finite_differences, pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
+ALL_PINS = [pin_conv_silu, pin_conv_silu_bwd, pin_bwd_trap_finite_differences, pin_bwd_dt_finite_differences, pin_bwd_finite_differences, pin_bwd_adjoint_identities, pin_ssd_pages_dual, pin_ssd_is_scalar_a_s6, pin_ssd_brute_force, pin_ssd_resume,
             pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,

@@ -94,6 +94,11 @@ MUTANTS = [
     ("conv_drops_bias", "double u = cb ? cb[d] : 0.0;", "double u = 0.0;"),
     ("conv_silu_sign", "out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(-u));", "out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(u));"),
     ("conv_without_silu", "out[IDX3(b, t, d, L, D)] = u / (1.0 + exp(-u));", "out[IDX3(b, t, d, L, D)] = u;"),
+    ("convbwd_silu_grad_sigmoid_only", "du[t] = gout[IDX3(b, t, d, L, D)] * sg * (1.0 + u * (1.0 - sg));",
+     "du[t] = gout[IDX3(b, t, d, L, D)] * sg;"),
+    ("convbwd_taps_not_flipped", "if (t < L) g += w[d * 4 + j] * du[t];", "if (t < L) g += w[d * 4 + 3 - j] * du[t];"),
+    ("convbwd_bias_grad_missing", "                if (gb) gb[d] += du[t];\n", ""),
+    ("convbwd_state_grad_drops_a_tap", "for (int64_t j = 0; j <= k; ++j)", "for (int64_t j = 0; j < k; ++j)"),
 ]
 
 
