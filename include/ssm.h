@@ -488,6 +488,53 @@ int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     void *stream);
 
 /*
+ * Scratch bytes ssm_scan_bwd_conv needs for these sizes (0 for invalid or
+ * empty sizes): ssm_scan_bwd's, then the branch's output and its gradient
+ * (two (batch, L, D) arrays of the activation dtype) and the partial sums of
+ * the taps' and bias' gradients. No clearing is needed.
+ */
+size_t ssm_scan_bwd_conv_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype);
+
+/*
+ * ssm_scan_bwd for ssm_scan_fwd_conv: the gradient through the scan, then back
+ * through SiLU and the causal width-4 convolution of the x branch ("Notas
+ * sobre Mamba", section "O bloco Mamba"; the pages give the forward only, and
+ * this is its chain rule). With u and x as in ssm_scan_fwd_conv and dx the
+ * gradient of the scan's x,
+ *
+ *   du[t]          = dx[t] * s(u[t]) * (1 + u[t] * (1 - s(u[t]))),  s = sigmoid
+ *   dx_raw[t]      = sum_j conv_w[d,j] * du[t+3-j]           (tokens < L)
+ *   dconv_w[d,j]   = sum_{b,t} du[t] * x_raw[t-3+j]           (conv_state before 0)
+ *   dconv_b[d]     = sum_{b,t} du[t]
+ *   dconv_state[b,d,k] = sum_{j<=k} conv_w[d,j] * du[k-j]     (the raw x of token k-3)
+ *
+ * The forward rounds x to the activation dtype; the gradient takes that
+ * rounding as the identity, as it does for the activated step size.
+ *
+ *   x_raw, conv_w, conv_b, conv_state, delta_raw, dt_bias   as passed to
+ *                                           ssm_scan_fwd_conv
+ *   dx_raw        (batch, L, D)  dtype      written
+ *   dconv_w       (D, 4)         float      written
+ *   dconv_b       (D)            float      written when conv_b is given
+ *   dconv_state   (batch, D, 3)  dtype      written; NULL = not written
+ *   ddelta_raw, ddt_bias          as in ssm_scan_bwd_dt
+ *   workspace     ssm_scan_bwd_conv_workspace_bytes() bytes
+ *
+ * Every other argument and the status codes are those of ssm_scan_bwd_dt; a
+ * NULL conv_w or dconv_w returns SSM_ERR_NULL. All sums over tokens and
+ * channels run in a fixed order: the result is bitwise reproducible.
+ */
+int ssm_scan_bwd_conv(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x_raw, const float *conv_w, const float *conv_b, const void *conv_state,
+                      const void *delta_raw, const float *dt_bias, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip, const void *z, const float *state_in,
+                      const void *dy, const float *dstate,
+                      void *dx_raw, float *dconv_w, float *dconv_b, void *dconv_state,
+                      void *ddelta_raw, float *ddt_bias, float *dA, float *dBt, float *dCt,
+                      float *dDskip, void *dz, float *dstate_in, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
  * ssm_scan_bwd for ssm_scan_fwd_trap: the gradient of the exponential-
  * trapezoidal rule ("Notas sobre Mamba", section "Recorrência trapezoidal").
  * With v_t = Bt[t] x_t, the state's gradient G_t runs back as in ssm_scan_bwd

@@ -27,6 +27,8 @@ Functions (same names as the C ABI):
       dA, dBt, dCt, dDskip, dz, dstate_in)
   ssm_scan_bwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, dy, ...) -> dict: the same for
       ssm_scan_fwd_dt, with ddelta_raw and ddt_bias in place of ddelta
+  ssm_scan_bwd_conv(x_raw, conv_w, delta_raw, dt_bias, A, Bt, Ct, dy, ...) -> dict:
+      the same for ssm_scan_fwd_conv, with dx_raw, dconv_w, dconv_b, dconv_state
   ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, ...) -> dict: the same for
       ssm_scan_fwd_trap, with dlam, and dx_prev, dB_prev for the earlier token
   ssm_ssd_step(x, delta, A, Bt, Ct, state, Dskip=None, y=None) -> y: one SSD
@@ -46,7 +48,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSMError", "lib", "lib_path", "ssm_scan_fwd", "ssm_step", "ssm_scan_fwd_dt", "ssm_step_dt",
-    "ssm_scan_fwd_conv", "ssm_step_conv",
+    "ssm_scan_fwd_conv", "ssm_step_conv", "ssm_scan_bwd_conv",
     "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd", "ssm_ssd_step", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_scan_workspace_bytes",
     "ssm_scan_bwd_workspace_bytes", "ssm_status_string", "ssm_version", "EXPORTS", "new_workspace",
     "workspace_error", "ssm_scan_workspace_status", "SSM_ERR_TIMEOUT", "ssm_scan_fwd_noalloc",
@@ -68,7 +70,8 @@ lib_path = os.environ.get("SSM_LIBRARY") or os.path.join(_HERE, "libssm.so")
 EXPORTS = ("ssm_status_string", "ssm_version", "ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_step",
            "ssm_scan_fwd_dt", "ssm_step_dt", "ssm_scan_fwd_trap", "ssm_step_trap", "ssm_ssd_fwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_dt", "ssm_scan_bwd_trap", "ssm_ssd_step",
-           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_conv", "ssm_step_conv")
+           "ssm_scan_workspace_status", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_conv", "ssm_step_conv",
+           "ssm_scan_bwd_conv_workspace_bytes", "ssm_scan_bwd_conv")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -125,6 +128,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_bwd.restype = ci
     L.ssm_scan_bwd_dt.argtypes = [i64, i64, i64, i64, ci] + [vp] * 20 + [vp, sz, vp]
     L.ssm_scan_bwd_dt.restype = ci
+    L.ssm_scan_bwd_conv_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    L.ssm_scan_bwd_conv_workspace_bytes.restype = sz
+    L.ssm_scan_bwd_conv.argtypes = [i64, i64, i64, i64, ci] + [vp] * 26 + [vp, sz, vp]
+    L.ssm_scan_bwd_conv.restype = ci
     L.ssm_scan_bwd_trap.argtypes = [i64, i64, i64, i64, ci] + [vp] * 24 + [vp, sz, vp]
     L.ssm_scan_bwd_trap.restype = ci
     _lib = L
@@ -505,6 +512,61 @@ def ssm_scan_bwd_dt(x, delta_raw, dt_bias, A, Bt, Ct, dy, Dskip=None, z=None, st
     (D,) float32 (set out["ddt_bias"] = None to leave it out)."""
     return _scan_bwd("ssm_scan_bwd_dt", x, delta_raw, dt_bias, A, Bt, Ct, dy, Dskip, z, state_in, dstate, out,
                      workspace, stream)
+
+
+def ssm_scan_bwd_conv(x_raw, conv_w, delta_raw, dt_bias, A, Bt, Ct, dy, conv_b=None, conv_state=None, Dskip=None,
+                      z=None, state_in=None, dstate=None, out=None, workspace=None, stream=None):
+    """Gradient of ssm_scan_fwd_conv. As ssm_scan_bwd_dt, with dx_raw (like x_raw)
+    in place of dx, and dconv_w (D, 4), dconv_b (D,) (None without conv_b) float32
+    and dconv_state (batch, D, 3) in x_raw's dtype (None without conv_state;
+    set out["dconv_state"] to ask for it anyway)."""
+    import torch
+    if x_raw.dim() != 3 or A.dim() != 2:
+        raise ValueError("x_raw must be (batch, L, D) and A (D, N)")
+    batch, L, D = x_raw.shape
+    N = A.shape[1]
+    act, f32 = x_raw.dtype, torch.float32
+    code = _dtype_code(x_raw)
+    o = dict(out or {})
+    given = set(o)
+    new = lambda shape, dt: torch.empty(shape, dtype=dt, device=x_raw.device)
+    o.setdefault("dx_raw", torch.empty_like(x_raw))
+    o.setdefault("dconv_w", new((D, 4), f32))
+    o.setdefault("dconv_b", None if conv_b is None else new((D,), f32))
+    o.setdefault("dconv_state", None if conv_state is None else new((batch, D, 3), act))
+    o.setdefault("ddelta_raw", torch.empty_like(x_raw))
+    o.setdefault("ddt_bias", new((D,), f32))
+    o.setdefault("dA", new((D, N), f32))
+    o.setdefault("dBt", new((batch, L, N), f32))
+    o.setdefault("dCt", new((batch, L, N), f32))
+    o.setdefault("dDskip", None if Dskip is None else new((D,), f32))
+    o.setdefault("dz", None if z is None else torch.empty_like(x_raw))
+    o.setdefault("dstate_in", new((batch, D, N), f32))
+    ws_bytes = lib().ssm_scan_bwd_conv_workspace_bytes(batch, L, D, N, code)
+    allocated = [v for k, v in o.items() if k not in given and v is not None]
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x_raw.device)
+        allocated.append(workspace)
+    args = [_ptr(x_raw, "x_raw", act), _ptr(conv_w, "conv_w", f32, (D, 4)), _ptr(conv_b, "conv_b", f32, (D,)),
+            _ptr(conv_state, "conv_state", act, (batch, D, 3)), _ptr(delta_raw, "delta_raw", act, (batch, L, D)),
+            _ptr(dt_bias, "dt_bias", f32, (D,)), _ptr(A, "A", f32, (D, N)),
+            _ptr(Bt, "Bt", act, (batch, L, N)), _ptr(Ct, "Ct", act, (batch, L, N)),
+            _ptr(Dskip, "Dskip", f32, (D,)), _ptr(z, "z", act, (batch, L, D)),
+            _ptr(state_in, "state_in", f32, (batch, D, N)), _ptr(dy, "dy", act, (batch, L, D)),
+            _ptr(dstate, "dstate", f32, (batch, D, N)),
+            _ptr(o["dx_raw"], "dx_raw", act, (batch, L, D)), _ptr(o["dconv_w"], "dconv_w", f32, (D, 4)),
+            _ptr(o["dconv_b"], "dconv_b", f32, (D,)), _ptr(o["dconv_state"], "dconv_state", act, (batch, D, 3)),
+            _ptr(o["ddelta_raw"], "ddelta_raw", act, (batch, L, D)), _ptr(o["ddt_bias"], "ddt_bias", f32, (D,)),
+            _ptr(o["dA"], "dA", f32, (D, N)), _ptr(o["dBt"], "dBt", f32, (batch, L, N)),
+            _ptr(o["dCt"], "dCt", f32, (batch, L, N)), _ptr(o["dDskip"], "dDskip", f32, (D,)),
+            _ptr(o["dz"], "dz", act, (batch, L, D)), _ptr(o["dstate_in"], "dstate_in", f32, (batch, D, N))]
+    ws_ptr = _ptr(workspace, "workspace")
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _order_after_alloc(stream, allocated)
+    st = lib().ssm_scan_bwd_conv(batch, L, D, N, code, *args, ws_ptr, ws_len, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_scan_bwd_conv")
+    return o
 
 
 def ssm_scan_bwd_trap(x, delta, lam, A, Bt, Ct, dy, Dskip=None, z=None, x_prev=None, B_prev=None, state_in=None,

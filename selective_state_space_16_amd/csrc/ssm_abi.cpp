@@ -410,7 +410,9 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
                     const void *dy, const float *dstate,
                     void *dx, void *ddelta, float *ddt_bias, float *dA, float *dBt, float *dCt, float *dDskip,
                     void *dz, float *dstate_in, void *workspace, size_t workspace_bytes, void *stream,
-                    TrapBwd tr = {}) {
+                    TrapBwd tr = {}, bool launch = true) {
+    // launch = false: check the arguments only (every check below precedes
+    // the first HIP call)
     if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
     if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
@@ -425,6 +427,7 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     hipStream_t s = (hipStream_t)stream;
     if (D == 0) return SSM_OK;
     if (batch == 0 || L == 0) {
+        if (!launch) return SSM_OK;
         // nothing flows through the tokens: the parameter gradients are zero
         // and the gradient of the entering state is that of the leaving one
         if (ssm::launch_state_copy(nullptr, dA, D * N, s) != hipSuccess) return SSM_ERR_HIP;
@@ -487,6 +490,7 @@ static int scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     a.pdBp = (float *)(ws + w.off[8]);
     a.ckp = (float *)(ws + w.off[9]);
     a.ckd = (float *)(ws + w.off[10]);
+    if (!launch) return SSM_OK;
     return ssm::launch_scan_bwd(a, (int)N, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -520,6 +524,92 @@ int ssm_scan_bwd_trap(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
     tr.dB_prev = dB_prev;
     return scan_bwd(batch, L, D, N, dtype, x, delta, nullptr, 0, A, Bt, Ct, Dskip, z, state_in, dy, dstate, dx,
                     ddelta, nullptr, dA, dBt, dCt, dDskip, dz, dstate_in, workspace, workspace_bytes, stream, tr);
+}
+
+// Workspace of the gradient through the x branch: the scan gradient's, then
+// the branch's output and its gradient (activation dtype) and the partial
+// sums of the taps' and bias' gradients.
+struct ConvBwdLayout {
+    int64_t chunk, nchunk;
+    size_t bwd, off_xc, off_gx, off_part, bytes;
+};
+
+static ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
+    ConvBwdLayout w{};
+    ssm::conv_bwd_plan(L, &w.chunk, &w.nchunk);
+    w.bwd = bwd_layout(batch, L, D, N).bytes;
+    const size_t act = (size_t)(batch * L * D) * (dtype == SSM_BF16 ? 2 : 4);
+    w.off_xc = w.bwd;
+    w.off_gx = w.off_xc + round_up256(act);
+    w.off_part = w.off_gx + round_up256(act);
+    w.bytes = w.off_part + round_up256((size_t)(batch * w.nchunk * D * 5) * sizeof(float));
+    return w;
+}
+
+size_t ssm_scan_bwd_conv_workspace_bytes(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
+    if (batch <= 0 || L <= 0 || D <= 0 || !supported_n(N)) return 0;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+    if (!bwd_sizes_ok(batch, L, D, N)) return 0;
+    return conv_bwd_layout(batch, L, D, N, dtype).bytes;
+}
+
+int ssm_scan_bwd_conv(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
+                      const void *x_raw, const float *conv_w, const float *conv_b, const void *conv_state,
+                      const void *delta_raw, const float *dt_bias, const float *A,
+                      const void *Bt, const void *Ct, const float *Dskip, const void *z, const float *state_in,
+                      const void *dy, const float *dstate,
+                      void *dx_raw, float *dconv_w, float *dconv_b, void *dconv_state,
+                      void *ddelta_raw, float *ddt_bias, float *dA, float *dBt, float *dCt,
+                      float *dDskip, void *dz, float *dstate_in, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_SHAPE;
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+    if (!supported_n(N)) return SSM_ERR_UNSUPPORTED;
+    if (!bwd_sizes_ok(batch, L, D, N)) return SSM_ERR_SHAPE;
+    if (D > 0 && (!conv_w || !dconv_w)) return SSM_ERR_NULL;
+    const void *ptrs[] = {conv_w, conv_b, conv_state, dconv_w, dconv_b, dconv_state};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSM_ERR_ALIGN;
+    const bool tokens = batch > 0 && L > 0 && D > 0;
+    if (tokens && (!x_raw || !dx_raw)) return SSM_ERR_NULL;
+    if (x_raw && !aligned16(x_raw)) return SSM_ERR_ALIGN;
+    if (dx_raw && !aligned16(dx_raw)) return SSM_ERR_ALIGN;
+    const ConvBwdLayout w = tokens ? conv_bwd_layout(batch, L, D, N, dtype) : ConvBwdLayout{};
+    if (tokens && (!workspace || workspace_bytes < w.bytes)) return SSM_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return SSM_ERR_ALIGN;
+    char *ws = (char *)workspace;
+    ssm::ConvBwdArgs c{};
+    c.batch = batch;
+    c.L = L;
+    c.D = D;
+    c.chunk = w.chunk;
+    c.nchunk = w.nchunk;
+    c.x_raw = x_raw;
+    c.conv_state = conv_state;
+    c.conv_w = conv_w;
+    c.conv_b = conv_b;
+    c.xc = tokens ? ws + w.off_xc : nullptr;
+    c.gx = tokens ? ws + w.off_gx : nullptr;
+    c.dx_raw = dx_raw;
+    c.dconv_state = dconv_state;
+    c.dconv_w = dconv_w;
+    c.dconv_b = conv_b ? dconv_b : nullptr;
+    c.part = tokens ? (float *)(ws + w.off_part) : nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    // check the scan gradient's own arguments before launching anything: the
+    // branch's output stands in for x (any aligned address passes the checks)
+    const int chk = scan_bwd(batch, L, D, N, dtype, tokens ? c.xc : x_raw, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip,
+                             z, state_in, dy, dstate, tokens ? ws + w.off_gx : dx_raw, ddelta_raw, ddt_bias, dA,
+                             dBt, dCt, dDskip, dz, dstate_in, workspace, tokens ? w.bwd : workspace_bytes, stream,
+                             TrapBwd{}, /*launch=*/false);
+    if (chk != SSM_OK) return chk;
+    if (D == 0) return SSM_OK;
+    if (ssm::launch_conv_fwd(c, dtype, s) != hipSuccess) return SSM_ERR_HIP;
+    const int rc = scan_bwd(batch, L, D, N, dtype, tokens ? c.xc : x_raw, delta_raw, dt_bias, 1, A, Bt, Ct, Dskip,
+                            z, state_in, dy, dstate, tokens ? ws + w.off_gx : dx_raw, ddelta_raw, ddt_bias, dA, dBt,
+                            dCt, dDskip, dz, dstate_in, workspace, tokens ? w.bwd : workspace_bytes, stream);
+    if (rc != SSM_OK) return rc;
+    return ssm::launch_conv_bwd(c, dtype, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int ssm_scan_bwd_dt(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,

@@ -175,7 +175,25 @@ void scan_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int64_t *K, int64
 
 bool stripe_plan(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype, StripePlan *p);
 
-// Launchers; return hipSuccess or the launch error.
+// The gradient through the x branch ahead of the scan (ssm_conv_bwd.hip).
+// Pointers are device pointers; x_raw, conv_state, xc, gx, dx_raw and
+// dconv_state in the activation dtype, the rest float.
+struct ConvBwdArgs {
+    int64_t batch, L, D;
+    int64_t chunk, nchunk;  // tokens per chunk of conv_bwd_kernel, chunks per batch row
+    const void *x_raw, *conv_state;  // the branch's input; the raw x of the three tokens before (NULL = 0)
+    const float *conv_w, *conv_b;    // taps (D, 4), bias (D; NULL = 0)
+    void *xc;                        // (batch, L, D) the branch's output (conv_fwd_kernel)
+    const void *gx;                  // (batch, L, D) the gradient of that output
+    void *dx_raw, *dconv_state;      // gradients of x_raw and conv_state (NULL: not written)
+    float *dconv_w, *dconv_b;        // gradients of the taps and bias (dconv_b NULL: not written)
+    float *part;                     // (batch * nchunk, D, 5) partial sums of the taps' and bias' gradients
+};
+void conv_bwd_plan(int64_t L, int64_t *chunk, int64_t *nchunk);
+hipError_t launch_conv_fwd(const ConvBwdArgs &a, int dtype, hipStream_t s);
+hipError_t launch_conv_bwd(const ConvBwdArgs &a, int dtype, hipStream_t s);
+
+// Launchers; return hipSuccess or the launch error.// Launchers; return hipSuccess or the launch error.
 hipError_t launch_scan_stripe(const StripeArgs &a, int N, int dtype, hipStream_t s);
 // The instances for a delta given before its activation (called by launch_scan_stripe).
 hipError_t launch_scan_stripe_act(const StripeArgs &a, int N, int dtype, hipStream_t s);

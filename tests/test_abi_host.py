@@ -363,6 +363,42 @@ def test_scan_bwd_dt_empty_ok_without_gpu():
     assert bwd_dt(D=0) == 0
 
 
+def bwd_conv(**kw):
+    a = dict(batch=2, L=100, D=64, N=16, dtype=0, x_raw=P, conv_w=P, conv_b=None, conv_state=None, delta=P,
+             dt_bias=None, A=P, Bt=P, Ct=P, Dskip=None, z=None, state_in=None, dy=P, dstate=None, dx_raw=P,
+             dconv_w=P, dconv_b=None, dconv_state=None, ddelta=P, ddt_bias=None, dA=P, dBt=P, dCt=P, dDskip=None,
+             dz=None, dstate_in=None, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_bwd_conv(a["batch"], a["L"], a["D"], a["N"], a["dtype"], a["x_raw"], a["conv_w"],
+                                       a["conv_b"], a["conv_state"], a["delta"], a["dt_bias"], a["A"], a["Bt"],
+                                       a["Ct"], a["Dskip"], a["z"], a["state_in"], a["dy"], a["dstate"], a["dx_raw"],
+                                       a["dconv_w"], a["dconv_b"], a["dconv_state"], a["ddelta"], a["ddt_bias"],
+                                       a["dA"], a["dBt"], a["dCt"], a["dDskip"], a["dz"], a["dstate_in"], a["ws"],
+                                       a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dtype=2), -3), (dict(N=5), -4), (dict(conv_w=None), -1), (dict(dconv_w=None), -1),
+    (dict(x_raw=None), -1), (dict(dx_raw=None), -1), (dict(delta=None), -1), (dict(dy=None), -1),
+    (dict(dA=None), -1), (dict(conv_w=MIS), -5), (dict(conv_state=MIS), -5), (dict(dconv_state=MIS), -5),
+    (dict(x_raw=MIS), -5), (dict(dt_bias=MIS), -5), (dict(ws_bytes=1), -6), (dict(ws=None), -6),
+])
+def test_scan_bwd_conv_rejects(kw, code):
+    assert bwd_conv(**kw) == code
+
+
+def test_scan_bwd_conv_workspace_bytes():
+    f = ssm.lib().ssm_scan_bwd_conv_workspace_bytes
+    base = ssm.lib().ssm_scan_bwd_workspace_bytes(2, 100, 64, 16, 1)
+    # the scan gradient's, the branch's output and its gradient (bf16), the partial sums
+    assert f(2, 100, 64, 16, 1) >= base + 2 * 2 * 100 * 64 * 2
+    assert f(0, 100, 64, 16, 1) == 0 and f(2, 0, 64, 16, 1) == 0 and f(2, 100, 64, 3, 1) == 0
+
+
+def test_scan_bwd_conv_empty_ok_without_gpu():
+    assert bwd_conv(D=0) == 0
+
+
 def bwd_trap(**kw):
     a = dict(batch=2, L=100, D=64, N=16, dtype=0, x=P, delta=P, lam=P, A=P, Bt=P, Ct=P, Dskip=None, z=None,
              x_prev=None, B_prev=None, state_in=None, dy=P, dstate=None, dx=P, ddelta=P, dlam=P, dA=P, dBt=P, dCt=P,
