@@ -72,11 +72,14 @@ KERNEL_SOURCES = {
     "ssd": ("ssm_ssd.hip",),
     "ssd_step": ("ssm_ssd_step.hip",),
     "grad": ("ssm_scan_bwd_kernel.h", "ssm_scan_bwd.hip", "ssm_scan_bwd_trap.hip"),
+    "conv_grad": ("ssm_scan_bwd_kernel.h", "ssm_scan_bwd.hip", "ssm_scan_bwd_trap.hip", "ssm_conv_bwd.hip"),
 }
 SHARED_SOURCES = ("ssm_common.h", "ssm_device.h", "ssm_internal.h")
 
 
 def kernel_family(workload: str) -> str:
+    if workload.endswith("_conv_grad"):
+        return "conv_grad"
     if workload.endswith("_grad"):
         return "grad"
     base = workload[:-len("_conv")] if workload.endswith("_conv") else workload
@@ -291,7 +294,8 @@ def bench_scan(args, name):
     ys = [torch.empty_like(s["x"]) for s in sets]
     if bw:
         f32 = torch.float32
-        ys = [{"dx": torch.empty_like(s["x"]), ("ddelta_raw" if sp else "ddelta"): torch.empty_like(s["x"]),
+        ys = [{("dx_raw" if cv else "dx"): torch.empty_like(s["x"]),
+               ("ddelta_raw" if sp else "ddelta"): torch.empty_like(s["x"]),
                "dz": torch.empty_like(s["x"]) if s["z"] is not None else None,
                "dA": torch.empty((cfg.D, cfg.N), dtype=f32, device="cuda"),
                "dBt": torch.empty((cfg.batch, cfg.L, cfg.N), dtype=f32, device="cuda"),
@@ -301,14 +305,19 @@ def bench_scan(args, name):
         if sp:
             for o_ in ys:
                 o_["ddt_bias"] = torch.empty((cfg.D,), dtype=f32, device="cuda")
+        if cv:
+            for o_, s_ in zip(ys, sets):
+                o_["dconv_w"] = torch.empty((cfg.D, 4), dtype=f32, device="cuda")
+                o_["dconv_b"] = torch.empty((cfg.D,), dtype=f32, device="cuda")
+                o_["dconv_state"] = torch.empty((cfg.batch, cfg.D, 3), dtype=s_["x"].dtype, device="cuda")
         if tr:
             for o_, s_ in zip(ys, sets):
                 o_["dlam"] = torch.empty_like(s_["x"])
                 o_["dx_prev"] = torch.empty((cfg.batch, cfg.D), dtype=s_["x"].dtype, device="cuda")
                 o_["dB_prev"] = torch.empty((cfg.batch, cfg.N), dtype=f32, device="cuda")
         dstate = to_dev(W.grad_inputs(cfg, 0, 0)["dstate"])
-        bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
-                                                           0 if cfg.dtype == "f32" else 1),
+        bws_fn = ssm.lib().ssm_scan_bwd_conv_workspace_bytes if cv else ssm.ssm_scan_bwd_workspace_bytes
+        bws = torch.empty(bws_fn(cfg.batch, cfg.L, cfg.D, cfg.N, 0 if cfg.dtype == "f32" else 1),
                           dtype=torch.uint8, device="cuda")
     ws_bytes = ssm.ssm_scan_workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N, 0 if cfg.dtype == "f32" else 1)
     ws = ssm.new_workspace(ws_bytes)
@@ -318,7 +327,11 @@ def bench_scan(args, name):
 
     def step(i):
         s = sets[i % len(sets)]
-        if bw and tr:
+        if bw and cv:
+            ssm.ssm_scan_bwd_conv(s["x"], cw, s["delta_raw"], s["dt_bias"], A, s["Bt"], s["Ct"], s["dy"], conv_b=cb,
+                                  conv_state=cs, Dskip=Dskip, z=s["z"], state_in=st_in, dstate=dstate,
+                                  out=ys[i % len(sets)], workspace=bws, stream=stream)
+        elif bw and tr:
             ssm.ssm_scan_bwd_trap(s["x"], s["delta"], s["lam"], A, s["Bt"], s["Ct"], s["dy"], Dskip=Dskip, z=s["z"],
                                   x_prev=s["x_prev"], B_prev=s["B_prev"], state_in=st_in, dstate=dstate,
                                   out=ys[i % len(sets)], workspace=bws, stream=stream)
@@ -357,6 +370,8 @@ def bench_scan(args, name):
            "parity": None, "cpu": None}
     if bw:
         out["bytes"] = W.scan_bwd_bytes(cfg) + (2 * cfg.D * 4 if sp else 0)  # dt_bias read, ddt_bias written
+        if cv:  # taps and bias read and their gradients written; the earlier raw tokens and their gradient
+            out["bytes"] += 2 * cfg.D * 5 * 4 + 2 * cfg.batch * cfg.D * 3 * W._esize(cfg.dtype)
         if tr:  # lam read and dlam written; x_prev, B_prev read and their gradients written
             out["bytes"] += 2 * cfg.batch * cfg.L * cfg.D * W._esize(cfg.dtype) + \
                 2 * cfg.batch * (cfg.D * W._esize(cfg.dtype) + cfg.N * 4)
@@ -370,13 +385,14 @@ def bench_scan(args, name):
             reps, tot, ref = 0, 0.0, None
             while reps == 0 or tot < args.cpu_seconds:
                 t = time.perf_counter()
-                ref = (o.scan_bwd_trap if tr else o.scan_bwd_dt if sp else o.scan_bwd)(inp, grads["dy"], grads["dstate"],
-                                                                                       cfg.dtype)
+                ref = (o.scan_bwd_conv if cv else o.scan_bwd_trap if tr else o.scan_bwd_dt if sp else o.scan_bwd)(
+                    inp, grads["dy"], grads["dstate"], cfg.dtype)
                 tot += time.perf_counter() - t
                 reps += 1
             out["parity"] = {k: dict(zip(("relL2", "maxabs"), rel_l2(got[k], ref[k])))
-                             for k in ("dx", "ddelta", "ddelta_raw", "ddt_bias", "dlam", "dz", "dA", "dBt", "dCt",
-                                       "dDskip", "dx_prev", "dB_prev", "dstate_in")
+                             for k in ("dx", "dx_raw", "dconv_w", "dconv_b", "dconv_state", "ddelta", "ddelta_raw",
+                                       "ddt_bias", "dlam", "dz", "dA", "dBt", "dCt", "dDskip", "dx_prev", "dB_prev",
+                                       "dstate_in")
                              if ref.get(k) is not None}
             out["cpu"] = {"value": cfg.elems * reps / tot / 1e9, "unit": "G(B*L*D*N)-elem/s", "cores": 1,
                           "kind": "oracle",
@@ -721,8 +737,8 @@ def main():
     args = ap.parse_args()
     if sum((args.softplus, args.trap, args.conv)) > 1:
         ap.error("--softplus, --trap and --conv select different entry points; give one")
-    if args.conv and (args.backward or args.workload in ("ssd", "ssd_step")):
-        ap.error("--conv applies to the forward scan (c0-c3) and the decode step (c4)")
+    if args.conv and (args.workload in ("ssd", "ssd_step") or (args.backward and args.workload == "c4")):
+        ap.error("--conv applies to the scan (c0-c3, forward or --backward) and the decode step (c4)")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -755,7 +771,7 @@ def main():
     ms, launch_ms = r["ms"], r["launch_ms"]
     gbs = r["bytes"] / (launch_ms * 1e-3) / 1e9
     traffic = None if (args.softplus or args.trap) else \
-        measured_traffic(args.workload + ("_grad" if args.backward else "_conv" if args.conv else ""))
+        measured_traffic(args.workload + ("_conv" if args.conv else "") + ("_grad" if args.backward else ""))
     kernel = {"c4": STEP_KERNEL, "ssd": SSD_KERNEL, "ssd_step": "ssd_step_kernel"}.get(args.workload, SCAN_KERNEL)
     hbm = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
            "traffic": traffic, "kernel": kernel,
@@ -817,7 +833,7 @@ def main():
         metric = "selective-scan G(B*L*D*N)-elem/s"
         if args.backward:
             config["pass"] = "gradient (ssm_scan_bwd%s), dstate given" % (
-                "_dt" if args.softplus else "_trap" if args.trap else "")
+                "_conv" if args.conv else "_dt" if args.softplus else "_trap" if args.trap else "")
             metric = "selective-scan gradient G(B*L*D*N)-elem/s"
     line = {
         "metric": metric,

@@ -536,7 +536,7 @@ struct ConvBwdLayout {
 
 static ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     ConvBwdLayout w{};
-    ssm::conv_bwd_plan(L, &w.chunk, &w.nchunk);
+    ssm::conv_bwd_plan(batch, L, D, &w.chunk, &w.nchunk);
     w.bwd = bwd_layout(batch, L, D, N).bytes;
     const size_t act = (size_t)(batch * L * D) * (dtype == SSM_BF16 ? 2 : 4);
     w.off_xc = w.bwd;

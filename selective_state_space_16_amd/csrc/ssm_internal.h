@@ -189,7 +189,7 @@ struct ConvBwdArgs {
     float *dconv_w, *dconv_b;        // gradients of the taps and bias (dconv_b NULL: not written)
     float *part;                     // (batch * nchunk, D, 5) partial sums of the taps' and bias' gradients
 };
-void conv_bwd_plan(int64_t L, int64_t *chunk, int64_t *nchunk);
+void conv_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t *chunk, int64_t *nchunk);
 hipError_t launch_conv_fwd(const ConvBwdArgs &a, int dtype, hipStream_t s);
 hipError_t launch_conv_bwd(const ConvBwdArgs &a, int dtype, hipStream_t s);
 
