@@ -206,3 +206,91 @@ def test_step_conv_fold_equals_scan_conv(dtype):
     check(np.stack(ys, 1), y, dtype, "fold of steps vs scan (y)")
     check(to_f64(state), st, dtype, "fold of steps vs scan (state)")
     assert torch.equal(window, dev["x_raw"][:, -3:].transpose(1, 2).contiguous()), "window after the steps"
+
+
+# -- capture into a HIP graph -------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_conv_graph_replay(dtype):
+    """ssm_scan_fwd_conv with a workspace, captured into a graph on a shape
+    whose columns are cut into stripes: four replays, each followed by eager
+    calls of another size on the same workspace, equal the eager call bit for
+    bit (y and final state)."""
+    import torch
+    cfg = _cfg("conv_graph", 2, 2048, 1536, 16, dtype, state_in=0.3, seed=94)
+    say(f"case {cfg} graph replay")
+    d = {k: to_dev(v) for k, v in _inputs(cfg).items()}
+    other = _cfg("conv_graph_other", 2, 700, 96, 16, dtype, state_in=0.3, seed=95)
+    o = {k: to_dev(v) for k, v in _inputs(other).items()}
+    code = 0 if dtype == "f32" else 1
+    ws = ssm.new_workspace(max(ssm.ssm_scan_workspace_bytes(2, 2048, 1536, 16, code),
+                               ssm.ssm_scan_workspace_bytes(2, 700, 96, 16, code)))
+
+    def run(inp, y=None, st=None, stream=None):
+        if y is None:
+            y = torch.empty_like(inp["x_raw"])
+        if st is None:
+            st = torch.empty_like(inp["state_in"])
+        ssm.ssm_scan_fwd_conv(inp["x_raw"], inp["conv_w"], inp["delta_raw"], inp["dt_bias"], inp["A"], inp["Bt"],
+                              inp["Ct"], conv_b=inp["conv_b"], conv_state=inp["conv_state"], Dskip=inp["Dskip"],
+                              z=inp["z"], state_in=inp["state_in"], state_out=st, y=y, workspace=ws, stream=stream)
+        return y, st
+
+    y_ref, st_ref = run(d)
+    torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0
+    y_g, st_g = torch.empty_like(y_ref), torch.empty_like(st_ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(d, y_g, st_g, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y_g.fill_(float("nan"))
+        st_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert ssm.workspace_error(ws) == 0
+        assert torch.equal(y_g, y_ref), f"y differs on replay {rep}"
+        assert torch.equal(st_g, st_ref), f"state differs on replay {rep}"
+        run(o)  # eager work of another size on the same workspace
+        run(d)
+        torch.cuda.synchronize()
+        assert ssm.workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_conv_graph_replay(dtype):
+    """Decode steps with the x branch captured into a graph: every replay (with
+    eager scans between replays) equals the same steps launched eagerly, bit
+    for bit, in y, the state and the window of raw tokens."""
+    import torch
+    cfg = _cfg("step_conv_graph", 3, 6, 200, 16, dtype, state_in=0.5, seed=96)
+    say(f"case {cfg} graph replay")
+    dev = {k: to_dev(v) for k, v in _inputs(cfg).items()}
+    toks = [{k: dev[k][:, t].contiguous() for k in ("x_raw", "delta_raw", "Bt", "Ct", "z")} for t in range(cfg.L)]
+    st_g, st_e = dev["state_in"].clone(), dev["state_in"].clone()
+    win_g, win_e = dev["conv_state"].clone(), dev["conv_state"].clone()
+    y_g, y_e = torch.empty_like(toks[0]["x_raw"]), torch.empty_like(toks[0]["x_raw"])
+
+    def steps(state, window, y):
+        for tk in toks:
+            ssm.ssm_step_conv(tk["x_raw"], dev["conv_w"], window, tk["delta_raw"], dev["dt_bias"], dev["A"], tk["Bt"],
+                              tk["Ct"], state, conv_b=dev["conv_b"], Dskip=dev["Dskip"], z=tk["z"], y=y,
+                              stream=torch.cuda.current_stream())
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps(st_g, win_g, y_g)
+    torch.cuda.synchronize()
+    st_g.copy_(dev["state_in"])
+    win_g.copy_(dev["conv_state"])
+    for rep in range(4):
+        graph.replay()
+        steps(st_e, win_e, y_e)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"y differs on replay {rep}"
+        assert torch.equal(st_g, st_e), f"state differs on replay {rep}"
+        assert torch.equal(win_g, win_e), f"window differs on replay {rep}"
+        gpu_scan_conv(_inputs(_cfg("conv_between", 1, 50, 40, 16, dtype, seed=97 + rep)))
+        torch.cuda.synchronize()
