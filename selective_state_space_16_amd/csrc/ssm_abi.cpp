@@ -62,6 +62,14 @@ Impl choose_impl(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     return stripe_ok ? Impl::kStripe : Impl::kTwopass;
 }
 
+// Whether cut stripes take early mode: by their length, or as
+// SSM_STRIPE_EARLY=0/1 says (for comparison and tests).
+int stripe_early(const ssm::StripePlan &p) {
+    const char *e = getenv("SSM_STRIPE_EARLY");
+    if (e && (strcmp(e, "0") == 0 || strcmp(e, "1") == 0)) return e[0] == '1';
+    return p.early ? 1 : 0;
+}
+
 size_t workspace_for(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype) {
     int64_t K, Lc;
     ssm::StripePlan sp;
@@ -185,6 +193,7 @@ static int scan_fwd(int64_t batch, int64_t L, int64_t D, int64_t N, int dtype,
         a.n_whole = p.n_whole;
         a.S = p.S;
         a.SL = p.SL;
+        a.early = stripe_early(p);
         char *w = (char *)workspace;
         a.hdr = (uint32_t *)w;
         a.incl = (uint64_t *)(w + p.off_incl);

@@ -68,6 +68,7 @@ struct StripeArgs {
     int64_t n_whole;        // columns per list run as one whole-sequence unit each
     int64_t S;              // stripes per remaining column
     int64_t SL;             // tokens per stripe (the last one may be shorter)
+    int early;              // cut stripes take early mode (scan from zero first, then a pass 2 that may stop early)
     uint32_t *hdr;          // the workspace header (kHdr* words)
     uint64_t *incl;         // per (column, stripe, wave): end state, epoch-tagged words
     uint64_t *agg;          // per (column, stripe, wave): end state from zero and summed delta
@@ -75,6 +76,7 @@ struct StripeArgs {
 
 struct StripePlan {
     int64_t nl, tch, tt, vec, ntpb, ncol, cols_per_list, n_whole, S, SL;
+    bool early;         // stripes are long enough for early mode
     bool supported;     // shape meets the tile-load requirements
     size_t off_incl, off_agg, bytes;
 };

@@ -27,6 +27,19 @@
 // completion waits. The replay uses the same arithmetic each stripe uses for
 // its own end state, so results do not depend on timing.
 //
+// Long stripes take another order (early mode). The carried-in state enters
+// the stripe's states only as exp(A * summed delta) * h_in, which shrinks
+// token by token when A <= 0 and delta >= 0 (as the method draws them: A the
+// negative exponential of a parameter, delta a softplus). So pass 1 runs the
+// whole scan from a zero start, writing y and the (sum delta, S) pair; after
+// the look-back, pass 2 walks again from the carried-in state only until, at
+// the end of a tile, every lane's decayed carried-in state is below the
+// output's rounding unit (2^-24 for float32, 2^-16 for bfloat16) times the
+// largest of its states; from there on pass 1's y stands. The test is taken
+// from the data alone, so the results do not depend on timing either; a lane
+// whose A or delta has the other sign, or whose carried-in state is not
+// finite, never passes it.
+//
 // Memory. Tiles of TT tokens x TCH channels of x, delta (and z, for pass 2),
 // and the TT tokens of Bt (and Ct) are loaded into LDS with global_load_lds,
 // double-buffered so that the next tile streams in while this one is scanned;
@@ -58,6 +71,9 @@ constexpr int kWaves = 4;   // waves per workgroup (one per channel group)
 constexpr int kLists = 8;   // unit lists (one per XCD of an MI355X)
 constexpr int kReplay = 4;  // stripe records loaded per round trip of a look-back replay
 constexpr int kSlotsPerList = 64;  // workgroups a list is planned for (2 per CU on 256 CUs)
+constexpr int64_t kEarlyMinTokens = 16384;  // stripes at least this long take early mode
+// options of a stripe walk: sum delta, track its minimum, stop early
+constexpr int kSum = 1, kMin = 2, kStop = 4;
 
 // dot_row for four states per lane when `c` came straight from an LDS read
 // (the high-half loads): a DPP read needs no wait states after an LDS read,
@@ -142,6 +158,7 @@ struct Shared {
     [[no_unique_address]] OptRows<float, 5, Geo<N, DT>::TCH, CONV> cw;
     int unit;      // the unit handed to this workgroup
     uint32_t tag;  // this call's tag (see kHdrEpoch)
+    int stop[2][kWaves];  // early mode, pass 2: each wave's vote to stop, by tile parity
 };
 
 template <int N, int DT, bool TRAP, bool CONV = false>
@@ -660,8 +677,16 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                 sh.cb[threadIdx.x] = cbv;
             }
         };
-        auto walk = [&](auto pass_c, float (&st)[NL], float &dsum) {
+        // Early mode, pass 2: the carried-in state, and whether this lane may
+        // vote to stop (see the file comment).
+        float hin[NL];
+        bool lane_ok = false;
+        // OPT (kSum, kMin, kStop): pass 2 also sums delta into dsum, tracks its
+        // minimum in dmin, or stops at the first tile end where every lane of
+        // the workgroup votes to (pass 1 always sums).
+        auto walk = [&](auto pass_c, auto opt_c, float (&st)[NL], float &dsum, float &dmin) {
             constexpr int PASS = decltype(pass_c)::value;
+            constexpr int OPT = decltype(opt_c)::value;
             // bfloat16 groups of 8 tokens with two broadcast registers and two
             // finished tokens per lane take the high-half loads
             constexpr bool kHiLoads = DT == 1 && GROUP == 8 && BREGS == 2 && G::OWN == 2;
@@ -694,6 +719,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
             }
             if (w > 0) vm_wait();  // the first tile (prefetch) has landed
             lds_barrier();
+            int last = ntiles - 1;  // the last tile walked
             for (int i = 0; i < ntiles; ++i) {
                 TBT &tb = sh.buf[i & 1];
                 const int64_t tt0 = t0 + (int64_t)i * TT;
@@ -838,6 +864,8 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                         static_for<0, GROUP>([&](auto tc) {
                             constexpr int t = decltype(tc)::value;
                             const float dx = in_x(tc);
+                            if constexpr ((OPT & kSum) != 0) dsum += dv[t];
+                            if constexpr ((OPT & kMin) != 0) dmin = __builtin_fminf(dmin, dv[t]);
                             static_for<0, NL>([&](auto jc) {
                                 constexpr int q = decltype(jc)::value;
                                 const float dA = fast_exp2(dv[t] * A2[q]);
@@ -888,26 +916,63 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                         }
                     }
                 });
+                if constexpr ((OPT & kStop) != 0) {
+                    // this lane's vote: its carried-in state, decayed to the
+                    // end of this tile, below the rounding unit of its states
+                    constexpr float kRel = DT == 0 ? 0x1p-24f : 0x1p-16f;
+                    float em = 0.0f, hm = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < NL; ++q) {
+                        em = __builtin_fmaxf(em, __builtin_fabsf(hin[q]) * fast_exp2(A2[q] * dsum));
+                        hm = __builtin_fmaxf(hm, __builtin_fabsf(st[q]));
+                    }
+                    const bool ok = lane_ok && em <= kRel * hm;
+                    const uint64_t against = __builtin_amdgcn_ballot_w64(!ok);  // every lane, before the branch
+                    if (l == 0) sh.stop[i & 1][w] = against == 0 ? 1 : 0;
+                }
                 vm_wait();  // the next tile has landed (and this wave's earlier y stores are out)
                 lds_barrier();
+                if constexpr ((OPT & kStop) != 0) {
+                    int all = 1;
+#pragma unroll
+                    for (int v = 0; v < kWaves; ++v) all &= sh.stop[i & 1][v];
+                    if (__builtin_amdgcn_readfirstlane(all)) {
+                        last = i;
+                        break;
+                    }
+                }
             }
-            if constexpr (PASS == 2) store_y(sh.buf[(ntiles - 1) & 1], ntiles - 1);
+            if constexpr (PASS == 2) store_y(sh.buf[last & 1], last);
         };
 
-        float agg[NL], dagg = 0.0f;
+        using P1 = std::integral_constant<int, 1>;
+        using P2 = std::integral_constant<int, 2>;
+        float agg[NL], dagg = 0.0f, dmin = __builtin_inff(), unused = 0.0f;
 #pragma unroll
         for (int q = 0; q < NL; ++q) agg[q] = 0.0f;
-        if (has_next && j > 0) {
-            prefetch(std::integral_constant<int, 1>{});
-            walk(std::integral_constant<int, 1>{}, agg, dagg);
-            uint64_t *ar = a.agg + rec * (64 * (NL + 1));
-            publish_state<NL>(ar, l, agg, epoch);
-            st_tagged(ar + 64 * NL + l, dagg, epoch);
-        } else if (has_next) {
-            prefetch(std::integral_constant<int, 1>{});
-            walk(std::integral_constant<int, 1>{}, agg, dagg);  // stripe 0: its end state goes out directly
+        // early mode: stripe 0 walks once from its known state; every later
+        // stripe runs the scan from zero first (fold), then the short pass 2
+        const bool early = a.early != 0 && S > 1;
+        const bool fold = early && j > 0;
+        if (fold) {
+            prefetch(P2{});
+            walk(P2{}, std::integral_constant<int, kSum | (SP ? 0 : kMin)>{}, agg, dagg, dmin);
+            if (has_next) {
+                uint64_t *ar = a.agg + rec * (64 * (NL + 1));
+                publish_state<NL>(ar, l, agg, epoch);
+                st_tagged(ar + 64 * NL + l, dagg, epoch);
+            }
+            lds_barrier();  // every wave has read its share of the last y tile before the prefetch lands
+        } else if (!early && has_next) {
+            prefetch(P1{});
+            walk(P1{}, std::integral_constant<int, 0>{}, agg, dagg, unused);
+            if (j > 0) {  // (stripe 0: its end state goes out directly)
+                uint64_t *ar = a.agg + rec * (64 * (NL + 1));
+                publish_state<NL>(ar, l, agg, epoch);
+                st_tagged(ar + 64 * NL + l, dagg, epoch);
+            }
         }
-        prefetch(std::integral_constant<int, 2>{});  // lands during the look-back
+        prefetch(P2{});  // lands during the look-back
 
         // Carried-in state of this stripe.
         if (j == 0) {
@@ -1006,18 +1071,34 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
                 for (int q = 0; q < NL; ++q) h[q] = __builtin_nanf("");
             }
         }
-        if (has_next) {
-            // this stripe's end state, for the stripes after it
-            float e[NL];
+        // this stripe's end state, from the pair (for the stripes after it,
+        // and the final state of a folded last stripe)
+        float e[NL];
 #pragma unroll
-            for (int q = 0; q < NL; ++q) e[q] = __builtin_fmaf(fast_exp2(A2[q] * dagg), h[q], agg[q]);
-            publish_state<NL>(a.incl + rec * (64 * NL), l, e, epoch);
+        for (int q = 0; q < NL; ++q) e[q] = __builtin_fmaf(fast_exp2(A2[q] * dagg), h[q], agg[q]);
+        if (has_next && !(early && j == 0)) publish_state<NL>(a.incl + rec * (64 * NL), l, e, epoch);
+        const bool final_state = !has_next && a.state_out && valid;
+        float *so = a.state_out + (b * D + dc) * N + nstate0;
+        if (fold && final_state) {
+#pragma unroll
+            for (int q = 0; q < NL; ++q) so[q] = e[q];
         }
 
-        float unused = 0.0f;
-        walk(std::integral_constant<int, 2>{}, h, unused);
-        if (!has_next && a.state_out && valid) {
-            float *so = a.state_out + (b * D + d) * N + nstate0;
+        if (fold) {
+            bool ok = SP || dmin >= 0.0f;
+#pragma unroll
+            for (int q = 0; q < NL; ++q) {
+                hin[q] = h[q];
+                ok = ok && __builtin_isfinite(h[q]) && A2[q] <= 0.0f;
+            }
+            lane_ok = ok;
+            float dsum = 0.0f;
+            walk(P2{}, std::integral_constant<int, kSum | kStop>{}, h, dsum, unused);
+        } else {
+            walk(P2{}, std::integral_constant<int, 0>{}, h, unused, unused);
+            if (early && has_next) publish_state<NL>(a.incl + rec * (64 * NL), l, h, epoch);  // stripe 0
+        }
+        if (!fold && final_state) {
 #pragma unroll
             for (int q = 0; q < NL; ++q) so[q] = h[q];
         }
@@ -1112,6 +1193,7 @@ void stripe_geometry(int64_t batch, int64_t L, int64_t D, StripePlan *p) {
     S = tiles > 0 ? (tiles + tiles_per_stripe - 1) / tiles_per_stripe : 1;
     p->SL = tiles_per_stripe * G::TT;
     p->S = S;
+    p->early = S > 1 && p->SL >= kEarlyMinTokens;
     p->n_whole = S > 1 ? C - rem : C;
 }
 

@@ -75,13 +75,17 @@ def test_scan_graph_replay(dtype):
         assert ssm.ssm_scan_workspace_status(ws) == 0
 
 
-def test_giveup_poisons_and_is_reported():
+@pytest.mark.parametrize("early", ["0", "1"])
+def test_giveup_poisons_and_is_reported(early, monkeypatch):
     """A call whose waits give up: the first stripe of every column (which
     waits for nothing) is exact, every later token is NaN, the final state is
     NaN, the status reports SSM_ERR_TIMEOUT; the next call on the same
-    workspace is exact and reports SSM_OK."""
+    workspace is exact and reports SSM_OK. In early mode too, where the later
+    stripes have written y from a zero start before their wait: the walk from
+    the NaN state never stops early, so it overwrites all of it."""
     import torch
-    say("case forced give-up")
+    monkeypatch.setenv("SSM_STRIPE_EARLY", early)
+    say(f"case forced give-up early={early}")
     d = _inputs("f32")
     ws = ssm.new_workspace(ssm.ssm_scan_workspace_bytes(2, 2048, 1536, 16, 0))
     y_ref, st_ref = _run(d, ws)
