@@ -102,10 +102,11 @@ const char *ssm_version(void);
  * Order of work on long stripes (16384 tokens or more): every stripe but the
  * first scans from a zero start first, writing y, and after its entering
  * state is known walks again only until that state, decayed by exp(A * summed
- * delta), is below the output's rounding unit (2^-24 for float32, 2^-16 for
- * bfloat16) times every lane's largest state ("Notas sobre Mamba", section "O
- * mecanismo de seleção (S6)": the recurrence is linear in the state). The
- * stop is decided on the data only, so results stay bitwise reproducible; it
+ * delta), is below 2^-24 (float32 outputs, their unit roundoff) or 2^-16
+ * (bfloat16 outputs, 1/256 of theirs) times every lane's largest state
+ * ("Notas sobre Mamba", section "O mecanismo de seleção (S6)": the
+ * recurrence is linear in the state). The stop is decided on the data only,
+ * so results stay bitwise reproducible; it
  * is never taken where A > 0, delta < 0 or the entering state is not finite.
  * The environment variable SSM_STRIPE_EARLY=0 or 1, read at each call, forces
  * the two-pass order or this one (for comparison and tests).

@@ -33,12 +33,12 @@
 // negative exponential of a parameter, delta a softplus). So pass 1 runs the
 // whole scan from a zero start, writing y and the (sum delta, S) pair; after
 // the look-back, pass 2 walks again from the carried-in state only until, at
-// the end of a tile, every lane's decayed carried-in state is below the
-// output's rounding unit (2^-24 for float32, 2^-16 for bfloat16) times the
-// largest of its states; from there on pass 1's y stands. The test is taken
-// from the data alone, so the results do not depend on timing either; a lane
-// whose A or delta has the other sign, or whose carried-in state is not
-// finite, never passes it.
+// the end of a tile, every lane's decayed carried-in state is below 2^-24
+// (float32 outputs: their unit roundoff) or 2^-16 (bfloat16 outputs: 1/256 of
+// theirs) times the largest of its states; from there on pass 1's y stands.
+// The test is taken from the data alone, so the results do not depend on
+// timing either; a lane whose A or delta has the other sign, or whose
+// carried-in state is not finite, never passes it.
 //
 // Memory. Tiles of TT tokens x TCH channels of x, delta (and z, for pass 2),
 // and the TT tokens of Bt (and Ct) are loaded into LDS with global_load_lds,

@@ -1,7 +1,7 @@
 """Early mode of the tiled scan on cut columns (needs MI355X). Long stripes (or
 any, with SSM_STRIPE_EARLY=1) run the scan from a zero start first, writing y;
 after the look-back a second walk from the carried-in state rewrites y only
-until that state's decayed contribution is below the output's rounding unit.
+until that state's decayed contribution is below the output's rounding.
 Against the fp64 oracle: stops that come after a tile or two (fast decays),
 never (slow decays), each form of the step size and the x branch, the
 trapezoidal rule, and inputs where the stop must not be taken (a positive A, a
@@ -168,3 +168,55 @@ def test_early_deterministic(early):
     ya, sa = gpu_scan(inp)
     yb, sb = gpu_scan(inp)
     assert np.array_equal(ya, yb) and np.array_equal(sa, sb)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_early_ragged_shapes(dtype, monkeypatch):
+    """Two batch rows, a channel count that leaves the last tile column part
+    empty (its lanes past D vote on clamped data), and a length that leaves a
+    ragged last tile in the last stripe."""
+    cfg = _cfg(f"early_ragged_{dtype}", L=24000 - 37, D=200, dtype=dtype, seed=79, batch=2)
+    say(f"case {cfg} delta x30")
+    inp = W.scan_inputs(cfg)
+    _scale_delta(inp, dtype, 30.0)
+    _both_orders(gpu_scan, inp, oracle_scan(inp, dtype), dtype, monkeypatch)
+
+
+def test_early_graph_replay(early):
+    """Early mode captured into a graph: replays, with eager calls of another
+    size between them, equal the eager call bit for bit."""
+    import torch
+    cfg = _cfg("early_graph", seed=80)
+    say(f"case {cfg} graph replay, delta x30")
+    inp = W.scan_inputs(cfg)
+    _scale_delta(inp, "bf16", 30.0)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    other = {k: to_dev(v) for k, v in W.scan_inputs(_cfg("early_graph_other", L=5000, D=64, seed=81)).items()}
+    ws = ssm.new_workspace(max(ssm.ssm_scan_workspace_bytes(1, cfg.L, cfg.D, 16, 1),
+                               ssm.ssm_scan_workspace_bytes(1, 5000, 64, 16, 1)))
+
+    def run(v, y=None, st=None, stream=None):
+        y = torch.empty_like(v["x"]) if y is None else y
+        st = torch.empty_like(v["state_in"]) if st is None else st
+        ssm.ssm_scan_fwd(v["x"], v["delta"], v["A"], v["Bt"], v["Ct"], Dskip=v["Dskip"], z=v["z"],
+                         state_in=v["state_in"], state_out=st, y=y, workspace=ws, stream=stream)
+        return y, st
+
+    y_ref, st_ref = run(d)
+    torch.cuda.synchronize()
+    assert ssm.workspace_error(ws) == 0
+    y_g, st_g = torch.empty_like(y_ref), torch.empty_like(st_ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(d, y_g, st_g, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y_g.fill_(float("nan"))
+        st_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert ssm.workspace_error(ws) == 0
+        assert torch.equal(y_g, y_ref), f"y differs on replay {rep}"
+        assert torch.equal(st_g, st_ref), f"state differs on replay {rep}"
+        run(other)
+        torch.cuda.synchronize()
