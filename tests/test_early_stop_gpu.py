@@ -220,3 +220,14 @@ def test_early_graph_replay(early):
         assert torch.equal(st_g, st_ref), f"state differs on replay {rep}"
         run(other)
         torch.cuda.synchronize()
+
+
+def test_early_two_stripes(monkeypatch):
+    """The fewest stripes a cut column has: 256 tile columns (32 per list) are
+    cut into two, so the last stripe's look-back reads stripe 0's end state
+    directly, with no pairs in between."""
+    cfg = _cfg("early_two_stripes", L=1024, D=16384, dtype="bf16", seed=82)
+    say(f"case {cfg} delta x30")
+    inp = W.scan_inputs(cfg)
+    _scale_delta(inp, "bf16", 30.0)
+    _both_orders(gpu_scan, inp, oracle_scan(inp, "bf16"), "bf16", monkeypatch)
