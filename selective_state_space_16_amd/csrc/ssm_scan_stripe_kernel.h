@@ -1078,7 +1078,7 @@ __global__ __launch_bounds__(64 * kWaves, (stripe_min_blocks<N, DT, MODE == kTra
         for (int q = 0; q < NL; ++q) e[q] = __builtin_fmaf(fast_exp2(A2[q] * dagg), h[q], agg[q]);
         if (has_next && !(early && j == 0)) publish_state<NL>(a.incl + rec * (64 * NL), l, e, epoch);
         const bool final_state = !has_next && a.state_out && valid;
-        float *so = a.state_out + (b * D + dc) * N + nstate0;
+        float *const so = final_state ? a.state_out + (b * D + d) * N + nstate0 : nullptr;
         if (fold && final_state) {
 #pragma unroll
             for (int q = 0; q < NL; ++q) so[q] = e[q];
