@@ -307,6 +307,32 @@ def pin_linearity_causality(o):
         assert not np.array_equal(yk[:, t0 + 1:], y0[:, t0 + 1:]), k
 
 
+def pin_entering_state_decay(o):
+    """The scan's dependence on its entering state in closed form ("Notas sobre
+    Mamba", "O mecanismo de seleção (S6)": each update multiplies the state by
+    exp(delta_t A) before adding the input, so the map is affine in h_0). With
+    the same inputs, y from h_in minus y from a zero start is, at token t,
+    silu(z_t) * sum_n Ct[t, n] exp(A[d, n] * sum_{s<=t} delta_s[d]) h_in[d, n]
+    (the readout sees the state after token t's update), and the final states
+    differ by exp(A * sum delta) h_in. The stripe scan's early stop (a walk from
+    zero whose y stands once this term is below rounding) rests on it."""
+    rng = np.random.default_rng(17)
+    p = _rand_problem(rng, 2, 300, 5, 16, s4d=True)  # A = -(n+1); gate, skip and entering state on
+    q = dict(p)
+    q["state_in"] = None
+    yp, sp = _scan(o, p)
+    yq, sq = _scan(o, q)
+    cum = np.cumsum(p["delta"], axis=1)  # inclusive: token t's own step counts
+    decay = np.exp(cum[..., None] * p["A"][None, None])  # (batch, L, D, N)
+    carried = decay * p["state_in"][:, None]
+    z = p["z"]
+    want = np.einsum("bln,bldn->bld", p["Ct"], carried) * (z / (1.0 + np.exp(-z)))
+    assert np.allclose(yp - yq, want, rtol=1e-9, atol=1e-12)
+    assert np.allclose(sp - sq, carried[:, -1], rtol=1e-9, atol=1e-12)
+    # and it vanishes: far enough into the sequence the two runs agree to rounding
+    assert np.max(np.abs(want[:, -1])) < 1e-3 * np.max(np.abs(want[:, 0]))
+
+
 def pin_softplus_activation(o):
     """Step-size activation delta = softplus(raw + dt_bias[d]) ("Notas sobre
     Mamba", section "O mecanismo de seleção (S6)"): against closed forms, the
@@ -817,4 +843,4 @@ ALL_PINS = [pin_conv_silu, pin_conv_silu_bwd, pin_bwd_trap_finite_differences, p
             pin_trap_pages_example, pin_trap_lambda_one_is_euler, pin_trap_classic_convolution,
             pin_trap_second_order, pin_trap_brute_force, pin_trap_composition, pin_softplus_activation, pin_step_example, pin_lti_convolution, pin_geometric, pin_delta_limits,
             pin_semiseparable, pin_scalar_a_dual, pin_composition, pin_skip_gate,
-            pin_linearity_causality]
+            pin_linearity_causality, pin_entering_state_decay]
