@@ -231,3 +231,17 @@ def test_early_two_stripes(monkeypatch):
     inp = W.scan_inputs(cfg)
     _scale_delta(inp, "bf16", 30.0)
     _both_orders(gpu_scan, inp, oracle_scan(inp, "bf16"), "bf16", monkeypatch)
+
+
+def test_early_state_in_place(early):
+    """state_out given as state_in's own memory: the last stripe writes the
+    final state (before its second walk) only after its look-back, which
+    follows stripe 0's read of state_in through the records."""
+    cfg = _cfg("early_inplace", seed=83)
+    say(f"case {cfg} state_out = state_in, delta x30")
+    inp = W.scan_inputs(cfg)
+    _scale_delta(inp, "bf16", 30.0)
+    y, st = gpu_scan(inp, state_alias=True)
+    yr, sr = oracle_scan(inp, "bf16")
+    check(y, yr, "bf16", "y")
+    check(st, sr, "bf16", "state_out (in place)")
